@@ -1,0 +1,327 @@
+"""Pins of the CPU oracle against facts fixed outside it.
+
+Each test checks the oracle against a closed form, a brute-force enumeration,
+an invariant the pages state, a hand-worked example, or an independent library
+routine (torch's scaled-dot-product attention on the CPU in float64), chosen
+so that a dropped term, a wrong sign or index, or a transposed operand in the
+oracle fails at least one of them.
+"""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_attention_softmax_amd.workloads import (WORKLOADS, f64_to_bf16_bits,
+                                                          generate)
+from oracle import sparge_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hybrid_mask_examples.txt")
+
+
+# ----------------------------------------------------------------- decoding
+def test_bf16_decode_known_patterns():
+    bits = np.array([0x3F80, 0xC000, 0x3F81, 0x0000, 0x8000, 0x4049, 0x7F7F], np.uint16)
+    want = [1.0, -2.0, 1.0 + 2.0 ** -7, 0.0, -0.0, 3.140625, 3.3895313892515355e38]
+    assert O.bf16_to_f64(bits).tolist() == want
+
+
+def test_bf16_rounding_of_generator_is_nearest_even():
+    # halfway cases round to the even neighbour; others to the nearest
+    x = np.array([1.0, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -1.0 - 2.0 ** -9,
+                  1.0 + 2.0 ** -8 + 2.0 ** -20])
+    got = O.bf16_to_f64(f64_to_bf16_bits(x))
+    assert got.tolist() == [1.0, 1.0, 1.0 + 2.0 ** -6, -1.0, 1.0 + 2.0 ** -7]
+
+
+# ----------------------------------------------------------------- pooling
+def test_pool_constant_blocks_give_the_constant():
+    rng = np.random.default_rng(5)
+    N, d, blk = 200, 8, 64
+    consts = rng.standard_normal((4, d))
+    X = np.concatenate([np.repeat(consts[j:j + 1], e - s, axis=0)
+                        for j, (s, e) in enumerate(O.block_bounds(N, blk))])
+    np.testing.assert_allclose(O.pool_mean(X, blk), consts, rtol=1e-14, atol=0)
+
+
+def test_pool_arange_means_are_arithmetic_series_midpoints():
+    N, blk = 200, 64
+    X = np.arange(N, dtype=np.float64)[:, None] * np.array([1.0, -2.0])[None, :]
+    got = O.pool_mean(X, blk)
+    mids = [31.5, 95.5, 159.5, 195.5]  # (first + last) / 2; last block holds 192..199
+    np.testing.assert_array_equal(got[:, 0], mids)
+    np.testing.assert_array_equal(got[:, 1], [-2 * m for m in mids])
+
+
+def test_block_logits_orientation_and_scale():
+    Qbar = np.array([[1.0, 0.0], [0.0, 2.0], [1.0, 1.0]])
+    Kbar = np.array([[3.0, 0.0], [0.0, 5.0]])
+    s = O.block_logits(Qbar, Kbar, 0.5)
+    np.testing.assert_array_equal(s, [[1.5, 0.0], [0.0, 5.0], [1.5, 2.5]])
+
+
+# ----------------------------------------------------------------- softmax
+def test_softmax_rows_sum_to_one_and_shift_invariant():
+    rng = np.random.default_rng(1)
+    s = rng.standard_normal((7, 33)) * 3
+    P = O.row_softmax(s)
+    np.testing.assert_allclose(P.sum(axis=1), 1.0, atol=1e-15)
+    np.testing.assert_allclose(O.row_softmax(s + 17.25), P, atol=1e-15)
+    assert (np.diff(P[0][np.argsort(s[0])]) >= 0).all()  # monotone in the logit
+
+
+def test_zero_pooled_query_gives_exactly_uniform_row():
+    s = O.block_logits(np.zeros((1, 16)), np.random.default_rng(2).standard_normal((24, 16)), 0.25)
+    assert (O.row_softmax(s) == 1.0 / 24).all()
+
+
+# --------------------------------------------------------------- Top-k size
+@pytest.mark.parametrize("k,n_k,want", [
+    (0.10, 16, 2), (0.05, 512, 26), (0.03, 512, 16), (0.05, 1182, 60),
+    (0.10, 10, 1), (1.0, 37, 37), (1e-9, 100, 1), (0.5, 3, 2), (0.25, 4, 1)])
+def test_topk_size_is_ceiling_of_k_times_nk(k, n_k, want):
+    assert O.topk_size(k, n_k) == want
+    assert O.topk_size(k, n_k) >= float(np.float32(k)) * n_k - 1e-6
+
+
+# ------------------------------------------------------- brute-force selection
+def _mass(P, subset):
+    return sum(P[j] for j in subset)
+
+
+def _rows_with_ties(rng, rows, n_k):
+    # integer-valued logits on a coarse grid make exact ties common
+    return rng.integers(-3, 4, size=(rows, n_k)).astype(np.float64) * 0.7
+
+
+@pytest.mark.parametrize("n_k", [5, 9, 12])
+def test_topk_prefix_is_max_mass_and_lowest_index_among_maximisers(n_k):
+    rng = np.random.default_rng(n_k)
+    s = np.concatenate([_rows_with_ties(rng, 6, n_k), rng.standard_normal((6, n_k))])
+    P = O.row_softmax(s)
+    for k in (1.0 / n_k, 0.3, 0.5):
+        sel = O.hybrid_select(s, k, 0.0)  # p = 0: Top-k alone
+        K = O.topk_size(k, n_k)
+        for r in range(s.shape[0]):
+            best = max(_mass(P[r], c) for c in itertools.combinations(range(n_k), K))
+            maximisers = [c for c in itertools.combinations(range(n_k), K)
+                          if _mass(P[r], c) >= best - 1e-12]
+            want = min(maximisers)  # combinations are sorted tuples
+            got = tuple(np.nonzero(sel.kept[r])[0])
+            assert got == want, (r, s[r], got, want)
+
+
+@pytest.mark.parametrize("n_k", [6, 10, 12])
+def test_topp_prefix_has_minimum_cardinality_over_all_subsets(n_k):
+    rng = np.random.default_rng(100 + n_k)
+    s = rng.standard_normal((10, n_k)) * 1.5
+    P = O.row_softmax(s)
+    for p in (0.3, 0.62, 0.9, 0.999):
+        sel = O.hybrid_select(s, 1.0 / n_k, p)
+        for r in range(s.shape[0]):
+            min_card = min(len(c) for m in range(n_k + 1)
+                           for c in itertools.combinations(range(n_k), m)
+                           if _mass(P[r], c) >= float(np.float32(p)))
+            assert sel.m_p[r] == min_card
+            prefix = sel.order[r, :sel.m_p[r]]
+            assert P[r, prefix].sum() >= float(np.float32(p))
+
+
+def test_union_contains_both_sets_and_meets_the_stated_invariants():
+    rng = np.random.default_rng(7)
+    for n_k in (16, 57, 300):
+        s = rng.standard_normal((40, n_k)) * rng.uniform(0.1, 6, size=(40, 1))
+        P = O.row_softmax(s)
+        for k, p in ((0.05, 0.9), (0.3, 0.5), (0.01, 0.99)):
+            sel = O.hybrid_select(s, k, p)
+            K = O.topk_size(k, n_k)
+            for r in range(s.shape[0]):
+                topk = set(sel.order[r, :K])
+                topp = set(sel.order[r, :sel.m_p[r]])
+                kept = set(np.nonzero(sel.kept[r])[0])
+                assert kept == topk | topp
+                assert len(kept) == max(K, sel.m_p[r]) == sel.count[r]
+                assert P[r, list(kept)].sum() >= float(np.float32(p))  # mass >= p
+                assert len(kept) >= float(np.float32(k)) * n_k - 1e-6   # count >= k n_k
+                # every kept block scores at least as high as every dropped block
+                if len(kept) < n_k:
+                    dropped = [j for j in range(n_k) if j not in kept]
+                    assert s[r, list(kept)].min() >= s[r, dropped].max()
+
+
+def test_p_at_least_one_keeps_everything_and_p_zero_is_topk():
+    s = np.random.default_rng(3).standard_normal((5, 20))
+    assert O.hybrid_select(s, 0.1, 1.0).kept.all()
+    sel = O.hybrid_select(s, 0.1, 0.0)
+    assert (sel.count == 2).all()
+
+
+def _load_golden():
+    cases = []
+    with open(GOLDEN) as f:
+        for line in f:
+            if not line.strip() or line.startswith("#"):
+                continue
+            name, n_k, k, p, logits, kept = [x.strip() for x in line.split("|")]
+            vals = []
+            for tok in logits.split(","):
+                v, _, rep = tok.partition("*")
+                vals += [float(v)] * (int(rep) if rep else 1)
+            idx = []
+            for tok in kept.split(","):
+                a, _, b = tok.partition("-")
+                idx += list(range(int(a), int(b) + 1)) if b else [int(a)]
+            assert len(vals) == int(n_k)
+            cases.append((name, np.array(vals), float(k), float(p), idx))
+    return cases
+
+
+@pytest.mark.parametrize("case", _load_golden(), ids=lambda c: c[0])
+def test_golden_hand_examples(case):
+    name, s, k, p, want = case
+    sel = O.hybrid_select(s[None, :], k, p)
+    assert list(np.nonzero(sel.kept[0])[0]) == want
+
+
+def test_near_tie_margin_measures_the_boundary_gaps():
+    s = np.array([[3.0, 2.0, 1.0 + 2e-6, 1.0, -5.0]])
+    sel = O.hybrid_select(s, 0.6, 0.0)  # K_k = 3: boundary between 1+2e-6 and 1.0
+    assert sel.count[0] == 3
+    assert abs(sel.margin[0] - 2e-6) < 1e-12
+    s2 = np.array([[3.0, 2.0, 0.0, -1.0, -5.0]])
+    sel2 = O.hybrid_select(s2, 0.2, 0.0)
+    assert sel2.margin[0] == 1.0
+
+
+# ----------------------------------------------------------- mask emission
+def test_bits_and_index_list_encode_the_kept_set():
+    rng = np.random.default_rng(4)
+    kept = rng.random((3, 70)) < 0.3
+    bits = O.kept_to_bits(kept)
+    assert bits.shape == (3, 3)
+    for r in range(3):
+        for j in range(70):
+            assert bool((int(bits[r, j // 32]) >> (j % 32)) & 1) == kept[r, j]
+    idx, cnt = O.kept_to_index_list(kept)
+    for r in range(3):
+        assert list(idx[r, :cnt[r]]) == list(np.nonzero(kept[r])[0])
+        assert (idx[r, cnt[r]:] == -1).all()
+
+
+def test_tiny_workload_mask_meets_invariants():
+    wl = WORKLOADS["tiny"]
+    Q, K, _ = generate(wl)
+    m = O.predict_mask(Q, K, wl.block_q, wl.block_k, wl.k_frac, wl.p_mass, wl.scale)
+    P = O.row_softmax(m.logits)
+    mass = (P * m.kept).sum(-1)
+    assert (mass >= np.float32(wl.p_mass)).all()
+    assert (m.cnt >= 2).all() and (m.cnt == m.kept.sum(-1)).all()
+    # the sink block (keys 0..63 carry +4c, every query carries +4c) is always kept
+    assert m.kept[..., 0].all()
+
+
+# ------------------------------------------------------------- attention
+def _sdpa(q, k, v, scale):
+    return torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(k)[None], torch.from_numpy(v)[None],
+        scale=scale)[0].numpy()
+
+
+@pytest.mark.parametrize("N,d,bq,bk", [(200, 16, 64, 64), (300, 32, 128, 64)])
+def test_all_blocks_kept_equals_textbook_attention(N, d, bq, bk):
+    rng = np.random.default_rng(N)
+    q, k, v = (rng.standard_normal((N, d)) for _ in range(3))
+    kept = np.ones((-(-N // bq), -(-N // bk)), bool)
+    scale = 1 / math.sqrt(d)
+    got = O.masked_attention_head(q, k, v, kept, bq, bk, scale)
+    np.testing.assert_allclose(got, _sdpa(q, k, v, scale), atol=1e-12)
+
+
+def test_single_kept_block_equals_attention_over_that_block():
+    rng = np.random.default_rng(9)
+    N, d, bq, bk = 260, 16, 64, 64
+    q, k, v = (rng.standard_normal((N, d)) for _ in range(3))
+    kept = np.zeros((5, 5), bool)
+    kept[np.arange(5), [3, 0, 4, 4, 1]] = True  # block 4 is the short one (4 keys)
+    got = O.masked_attention_head(q, k, v, kept, bq, bk, 0.3)
+    for i, j in enumerate([3, 0, 4, 4, 1]):
+        qs, ks = slice(i * 64, min(N, i * 64 + 64)), slice(j * 64, min(N, j * 64 + 64))
+        np.testing.assert_allclose(got[qs], _sdpa(q[qs], k[ks], v[ks], 0.3), atol=1e-12)
+
+
+def test_constant_values_and_zero_queries():
+    rng = np.random.default_rng(11)
+    N, d = 256, 8
+    q, k = rng.standard_normal((N, d)), rng.standard_normal((N, d))
+    kept = rng.random((4, 4)) < 0.5
+    kept[:, 2] = True
+    ones = np.ones((N, d))
+    np.testing.assert_allclose(O.masked_attention_head(q, k, ones, kept, 64, 64, 0.5), 1.0,
+                               atol=1e-14)
+    v = rng.standard_normal((N, d))
+    got = O.masked_attention_head(np.zeros((N, d)), k, v, kept, 64, 64, 0.5)
+    for i in range(4):
+        toks = np.concatenate([np.arange(j * 64, j * 64 + 64) for j in np.nonzero(kept[i])[0]])
+        np.testing.assert_allclose(got[i * 64:(i + 1) * 64], np.broadcast_to(
+            v[toks].mean(0), (64, d)), atol=1e-14)
+
+
+def test_empty_kept_row_gives_zero():
+    rng = np.random.default_rng(12)
+    q, k, v = (rng.standard_normal((128, 8)) for _ in range(3))
+    kept = np.array([[True, False], [False, False]])
+    out = O.masked_attention_head(q, k, v, kept, 64, 64, 0.5)
+    assert (out[64:] == 0).all() and np.isfinite(out[:64]).all()
+
+
+# ----------------------------------------------------------- linear branch
+def test_elu_plus_one_values():
+    x = np.array([-2.0, -1e-3, 0.0, 0.5, 3.0])
+    np.testing.assert_allclose(O.elu_plus_one(x), [math.exp(-2), math.exp(-1e-3), 1.0, 1.5, 4.0],
+                               rtol=1e-15)
+
+
+def test_linear_branch_zero_inputs_average_the_dropped_values():
+    rng = np.random.default_rng(13)
+    N, d = 250, 8
+    v = rng.standard_normal((N, d))
+    kept = np.array([[True, False, False, True], [False] * 3 + [True], [True] * 4, [False] * 4])
+    z = np.zeros((N, d))
+    got = O.linear_branch_head(z, z, v, kept, 64, 64)
+    bounds = O.block_bounds(N, 64)
+    for i, (s, e) in enumerate(bounds):
+        toks = [t for j, (a, b) in enumerate(bounds) if not kept[i, j] for t in range(a, b)]
+        want = v[toks].mean(0) if toks else np.zeros(d)
+        np.testing.assert_allclose(got[s:e], np.broadcast_to(want, (e - s, d)), atol=1e-14)
+
+
+def test_linear_branch_equals_its_associative_form():
+    rng = np.random.default_rng(14)
+    N, d = 300, 16
+    q, k, v = (rng.standard_normal((N, d)) for _ in range(3))
+    kept = rng.random((3, 5)) < 0.4
+    got = O.linear_branch_head(q, k, v, kept, 128, 64)
+    for i, (s, e) in enumerate(O.block_bounds(N, 128)):
+        D = [t for j, (a, b) in enumerate(O.block_bounds(N, 64)) if not kept[i, j]
+             for t in range(a, b)]
+        fq = np.where(q[s:e] > 0, q[s:e] + 1, np.exp(q[s:e]))
+        fk = np.where(k[D] > 0, k[D] + 1, np.exp(k[D]))
+        Hm, zv = fk.T @ v[D], fk.sum(0)          # d x d summary and normaliser
+        np.testing.assert_allclose(got[s:e], (fq @ Hm) / (fq @ zv)[:, None], rtol=1e-12,
+                                   atol=1e-14)
+
+
+def test_linear_branch_constant_values_and_full_keep():
+    rng = np.random.default_rng(15)
+    N, d = 256, 8
+    q, k = rng.standard_normal((N, d)), rng.standard_normal((N, d))
+    kept = np.array([[True, False, True, False]] * 4)
+    v = np.full((N, d), -0.75)
+    np.testing.assert_allclose(O.linear_branch_head(q, k, v, kept, 64, 64), -0.75, atol=1e-14)
+    vv = rng.standard_normal((N, d))
+    full = np.ones((4, 4), bool)
+    np.testing.assert_array_equal(
+        O.sparse_linear_attention_head(q, k, vv, full, 64, 64, 0.5, 0.1),
+        O.masked_attention_head(q, k, vv, full, 64, 64, 0.5))
