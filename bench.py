@@ -1,0 +1,188 @@
+"""Benchmark of the hybrid Top-k + Top-p block-sparse attention path on one MI355X.
+
+One step = the whole path on one batch of synthetic input: mask prediction
+(pool Q and K, float64 block scores, hybrid selection, index list) followed
+by the block-sparse attention forward over the kept key blocks. Inputs are
+resident in HBM before the timed region starts.
+
+Default workload: the Wan2.1-1.3B-shaped grid (B=1, H=12, N=32760 =
+21x30x52, d=128, blocks 128x64, k=5%, p=0.9). `value` is dense-equivalent
+throughput: 4*B*H*N^2*d floating-point operations per step divided by the
+step time (TFLOP/s). Next to it the line reports the attention kernel against
+the bf16 MFMA roofline at the kept-block count, the same path at the Top-k
+operating points of 90% and 95% block sparsity (p = 0, k = 10% / 5%), and the
+CPU oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse attn ms + dense-equiv TFLOPS (% bf16 MFMA peak) at 90/95% sparsity"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+
+def kept_flops(cnt: np.ndarray, idx: np.ndarray, N: int, d: int, block_q: int,
+               block_k: int) -> float:
+    """Algorithmic FLOPs of the attention over the kept tiles: for every kept
+    (query block i, key block j), 4 * d * |I_i| * |J_j| with true token counts."""
+    B, H, n_q = cnt.shape
+    qrows = np.minimum(block_q, N - np.arange(n_q) * block_q).astype(np.float64)
+    n_k = idx.shape[-1]
+    krows = np.minimum(block_k, N - np.arange(n_k) * block_k).astype(np.float64)
+    total = 0.0
+    flat_c = cnt.reshape(-1, n_q)
+    flat_i = idx.reshape(-1, n_q, n_k)
+    for bh in range(flat_c.shape[0]):
+        for i in range(n_q):
+            c = flat_c[bh, i]
+            total += qrows[i] * krows[flat_i[bh, i, :c]].sum()
+    return 4.0 * d * total
+
+
+def cpu_baseline(wl, Q, K, V, blocks: int):
+    """The oracle, as it stands, on a bounded sample: the mask of head 0 and the
+    masked attention of its first `blocks` query blocks."""
+    from oracle import sparge_oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    q, k, v = (O.bf16_to_f64(X[0, 0]) for X in (Q, K, V))
+    t0 = time.perf_counter()
+    sel, _ = O.predict_mask_head(q, k, wl.block_q, wl.block_k, wl.k_frac, wl.p_mass, wl.scale)
+    t_mask = time.perf_counter() - t0
+    blocks = min(blocks, wl.n_q)
+    t0 = time.perf_counter()
+    O.masked_attention_head(q, k, v, sel.kept, wl.block_q, wl.block_k, wl.scale,
+                            q_blocks=range(blocks))
+    t_attn = time.perf_counter() - t0
+    rows = min(blocks * wl.block_q, wl.N)
+    t = t_attn + t_mask * rows / wl.N  # the mask's share for the sampled rows
+    dense = 4.0 * rows * wl.N * wl.d
+    return {"value": dense / t / 1e12, "unit": "TFLOPS (dense-equivalent)", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{wl.name} head 0: mask of all {wl.n_q} query blocks ({t_mask:.2f} s, "
+                      f"charged pro rata) + attention of the first {blocks} query blocks "
+                      f"({t_attn:.2f} s), float64 NumPy"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="wan1.3b")
+    ap.add_argument("--cpu-blocks", type=int, default=256,
+                    help="query blocks of the oracle's CPU sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
+              "(heads shard across GPUs with no exchange, see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from block_sparse_attention_softmax_amd import binding as S
+    from block_sparse_attention_softmax_amd.workloads import WORKLOADS, generate
+
+    wl = WORKLOADS[args.workload]
+    Q, K, V = generate(wl)
+    dev = torch.device("cuda:0")
+    g = lambda a: torch.from_numpy(a).view(torch.bfloat16).to(dev)
+    q, k, v = g(Q), g(K), g(V)
+    B, H, N, d = q.shape
+    n_q, n_k = wl.n_q, wl.n_k
+    bits = torch.empty((B, H, n_q, -(-n_k // 32)), dtype=torch.int32, device=dev)
+    idx = torch.empty((B, H, n_q, n_k), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, H, n_q), dtype=torch.int32, device=dev)
+    ws = torch.empty(S.mask_workspace_bytes(B, H, N, d, wl.block_q, wl.block_k),
+                     dtype=torch.uint8, device=dev)
+    o = torch.empty_like(q)
+
+    def step(k_frac, p_mass, ev=None):
+        if ev is not None:
+            ev[0].record()
+        S.sparge_mask_predict(q, k, wl.block_q, wl.block_k, k_frac, p_mass, wl.scale,
+                              workspace=ws, out=(bits, idx, cnt))
+        if ev is not None:
+            ev[1].record()
+        S.sparge_attn_fwd(q, k, v, idx, cnt, wl.block_q, wl.block_k, wl.scale, out=o)
+        if ev is not None:
+            ev[2].record()
+
+    def timed(k_frac, p_mass, steps, warmup):
+        for _ in range(warmup):
+            step(k_frac, p_mass)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(k_frac, p_mass, evs[i])
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / steps
+        mask_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+        attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+        c_np, i_np = cnt.cpu().numpy(), idx.cpu().numpy()
+        kf = kept_flops(c_np, i_np, N, d, wl.block_q, wl.block_k)
+        kept_frac = float(c_np.sum()) / (B * H * n_q * n_k)
+        return wall, mask_ms, attn_ms, kf, kept_frac
+
+    dense = 4.0 * B * H * float(N) * N * d
+    wall, mask_ms, attn_ms, kf, kept_frac = timed(wl.k_frac, wl.p_mass, args.steps, args.warmup)
+    achieved = kf / (attn_ms * 1e-3) / 1e12
+
+    points = {}
+    for kfrac in (0.10, 0.05):
+        w2, m2, a2, kf2, frac2 = timed(kfrac, 0.0, max(5, args.steps // 2), 2)
+        points[f"p0_k{int(kfrac * 100)}"] = {
+            "k": kfrac, "p": 0.0, "block_sparsity": round(1 - frac2, 4),
+            "ms_per_step": round(w2 * 1e3, 4), "mask_ms": round(m2, 4),
+            "attn_ms": round(a2, 4),
+            "dense_equiv_tflops": round(dense / w2 / 1e12, 2),
+            "attn_dense_equiv_tflops": round(dense / (a2 * 1e-3) / 1e12, 2),
+            "attn_kept_tflops": round(kf2 / (a2 * 1e-3) / 1e12, 2),
+            "attn_frac_bf16_peak": round(kf2 / (a2 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(wl, Q, K, V, args.cpu_blocks)
+
+    line = {
+        "metric": METRIC,
+        "value": round(dense / wall / 1e12, 3),
+        "unit": "TFLOPS (dense-equivalent)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{wl.name}: B={B} H={H} N={N} (grid {'x'.join(map(str, wl.grid))})"
+                               f" d={d} blocks {wl.block_q}x{wl.block_k} k={wl.k_frac} "
+                               f"p={wl.p_mass}",
+                   "global_batch": B, "seq_len": N, "parallelism": "single GPU",
+                   "block_sparsity": round(1 - kept_frac, 4)},
+        "mask_ms": round(mask_ms, 4), "attn_ms": round(attn_ms, 4),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel": "sparse_attn_fwd_kernel<128,128>",
+                     "flops_per_launch": kf},
+        "operating_points": points,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,153 @@
+"""ctypes binding of libsparge.so with the C ABI's names.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI. torch supplies device memory and the current HIP
+stream. Importing this module does not need a GPU; calling an entry point
+needs the built library (it raises if libsparge.so is missing) and
+bfloat16 CUDA tensors.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsparge.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP = 0, -1, -2, -3
+
+# every symbol the public header declares
+EXPORTS = ("sparge_mask_workspace_bytes", "sparge_mask_predict", "sparge_attn_fwd",
+           "sparse_linear_workspace_bytes", "sparse_linear_attn_fwd", "sparge_last_error")
+
+_lib = None
+
+
+class SpargeError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"sparge error {code}: {msg}")
+        self.code = code
+
+
+def lib() -> ctypes.CDLL:
+    """Load libsparge.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m block_sparse_attention_softmax_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        c_int, c_float, c_size, vp = ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+        L.sparge_mask_workspace_bytes.argtypes = [c_int] * 6
+        L.sparge_mask_workspace_bytes.restype = c_size
+        L.sparge_mask_predict.argtypes = [vp, vp] + [c_int] * 6 + [c_float] * 3 + [vp] * 5 + [
+            c_size, vp]
+        L.sparge_mask_predict.restype = c_int
+        L.sparge_attn_fwd.argtypes = [vp] * 5 + [c_int] * 6 + [c_float, vp, vp]
+        L.sparge_attn_fwd.restype = c_int
+        L.sparse_linear_workspace_bytes.argtypes = [c_int] * 4
+        L.sparse_linear_workspace_bytes.restype = c_size
+        L.sparse_linear_attn_fwd.argtypes = [vp] * 6 + [c_int] * 6 + [c_float, vp, vp, c_size,
+                                                                       vp]
+        L.sparse_linear_attn_fwd.restype = c_int
+        L.sparge_last_error.argtypes = []
+        L.sparge_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(rc: int):
+    if rc != OK:
+        raise SpargeError(rc, lib().sparge_last_error().decode())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _qkv(*ts):
+    shape = ts[0].shape
+    for t in ts:
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("Q, K, V must be contiguous bfloat16 GPU tensors")
+        if t.dim() != 4 or t.shape != shape:
+            raise ValueError("Q, K, V must share one [B, H, N, d] shape")
+    return shape
+
+
+def default_scale(d: int) -> float:
+    return float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def mask_workspace_bytes(B, H, N, d, block_q, block_k) -> int:
+    return lib().sparge_mask_workspace_bytes(B, H, N, d, block_q, block_k)
+
+
+def sparge_mask_predict(q, k, block_q=128, block_k=64, k_frac=0.05, p_mass=0.9, scale=None,
+                        return_logits=False, workspace=None, out=None):
+    """Hybrid Top-k + Top-p block mask.
+
+    Returns (mask_bits int32-viewed uint32 [B,H,n_q,ceil(n_k/32)], kv_idx int32
+    [B,H,n_q,n_k], kv_cnt int32 [B,H,n_q][, logits float64 [B,H,n_q,n_k]]).
+    """
+    B, H, N, d = _qkv(q, k)
+    n_q, n_k = -(-N // block_q), -(-N // block_k)
+    dev = q.device
+    if out is None:
+        bits = torch.empty((B, H, n_q, -(-n_k // 32)), dtype=torch.int32, device=dev)
+        idx = torch.empty((B, H, n_q, n_k), dtype=torch.int32, device=dev)
+        cnt = torch.empty((B, H, n_q), dtype=torch.int32, device=dev)
+    else:
+        bits, idx, cnt = out
+    logits = (torch.empty((B, H, n_q, n_k), dtype=torch.float64, device=dev)
+              if return_logits else None)
+    ws_bytes = mask_workspace_bytes(B, H, N, d, block_q, block_k)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    if scale is None:
+        scale = default_scale(d)
+    _check(lib().sparge_mask_predict(
+        _ptr(q), _ptr(k), B, H, N, d, block_q, block_k, k_frac, p_mass, scale,
+        _ptr(bits), _ptr(idx), _ptr(cnt), _ptr(logits), _ptr(workspace),
+        workspace.numel(), _stream(q)))
+    return (bits, idx, cnt, logits) if return_logits else (bits, idx, cnt)
+
+
+def sparge_attn_fwd(q, k, v, kv_idx, kv_cnt, block_q=128, block_k=64, scale=None, out=None):
+    """Block-sparse attention over the key blocks listed in kv_idx/kv_cnt."""
+    B, H, N, d = _qkv(q, k, v)
+    o = torch.empty_like(q) if out is None else out
+    if scale is None:
+        scale = default_scale(d)
+    _check(lib().sparge_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_idx), _ptr(kv_cnt), B, H,
+                                 N, d, block_q, block_k, scale, _ptr(o), _stream(q)))
+    return o
+
+
+def linear_workspace_bytes(B, H, N, d) -> int:
+    return lib().sparse_linear_workspace_bytes(B, H, N, d)
+
+
+def sparse_linear_attn_fwd(q, k, v, kv_idx, kv_cnt, alpha, block_q=128, block_k=64,
+                           scale=None, workspace=None, out=None):
+    """Sparse attention plus alpha[h] times elu+1 linear attention over dropped blocks."""
+    B, H, N, d = _qkv(q, k, v)
+    if alpha.dtype != torch.float32 or not alpha.is_cuda or alpha.numel() != H:
+        raise ValueError("alpha must be a float32 GPU tensor of H values")
+    o = torch.empty_like(q) if out is None else out
+    if scale is None:
+        scale = default_scale(d)
+    ws_bytes = linear_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    _check(lib().sparse_linear_attn_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(kv_idx), _ptr(kv_cnt), _ptr(alpha.contiguous()), B, H,
+        N, d, block_q, block_k, scale, _ptr(o), _ptr(workspace), workspace.numel(),
+        _stream(q)))
+    return o

@@ -1,0 +1,197 @@
+// C ABI of libsparge.so (declared in include/sparge.h): argument checks on
+// the host, sizes, and dispatch to the kernels on the caller's stream.
+#include <math.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "../../include/sparge.h"
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* msg) {
+  g_last_error = msg;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  char buf[256];
+  snprintf(buf, sizeof buf, "%s: %s", where, hipGetErrorString(e));
+  g_last_error = buf;
+  return SPARGE_ERR_HIP;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Shape checks common to every entry point. Returns SPARGE_OK or an error.
+int check_shape(int B, int H, int N, int d, int block_q, int block_k) {
+  if (B < 1 || H < 1 || N < 1) return fail(SPARGE_ERR_INVALID_ARG, "B, H and N must be >= 1");
+  if (d != 64 && d != 128) return fail(SPARGE_ERR_UNSUPPORTED, "d must be 64 or 128");
+  if (block_q != 64 && block_q != 128)
+    return fail(SPARGE_ERR_UNSUPPORTED, "block_q must be 64 or 128");
+  if (block_k != 64) return fail(SPARGE_ERR_UNSUPPORTED, "block_k must be 64");
+  // every element offset must fit comfortably in 64-bit arithmetic and
+  // every workgroup count in a 32-bit grid dimension
+  const double elems = (double)B * H * (double)N * d;
+  if (elems > 9.0e15) return fail(SPARGE_ERR_INVALID_ARG, "tensor too large");
+  const double tiles = (double)B * H * ceil_div(N, block_q);
+  if (tiles > 2.0e9) return fail(SPARGE_ERR_INVALID_ARG, "too many query blocks");
+  return SPARGE_OK;
+}
+
+int next_pow2(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+constexpr int kMaxKeyBlocks = 4096;  // sort capacity of the selection kernel
+
+size_t mask_ws(int B, int H, int N, int d, int block_q, int block_k) {
+  const size_t BH = (size_t)B * H;
+  const size_t n_q = ceil_div(N, block_q), n_k = ceil_div(N, block_k);
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  return up(BH * n_q * d * sizeof(double)) + up(BH * n_k * d * sizeof(double)) +
+         up(BH * n_q * n_k * sizeof(double));
+}
+
+int check_attn_args(const void* q, const void* k, const void* v, const int32_t* kv_idx,
+                    const int32_t* kv_cnt, int B, int H, int N, int d, int block_q,
+                    int block_k, float scale, const void* o) {
+  int rc = check_shape(B, H, N, d, block_q, block_k);
+  if (rc != SPARGE_OK) return rc;
+  if (!q || !k || !v || !o || !kv_idx || !kv_cnt)
+    return fail(SPARGE_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+    return fail(SPARGE_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
+  if (!aligned(kv_idx, 4) || !aligned(kv_cnt, 4))
+    return fail(SPARGE_ERR_INVALID_ARG, "kv_idx and kv_cnt must be 4-byte aligned");
+  if (!(scale > 0.0f) || !isfinite(scale))
+    return fail(SPARGE_ERR_INVALID_ARG, "scale must be finite and > 0");
+  return SPARGE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sparge_last_error(void) { return g_last_error.c_str(); }
+
+size_t sparge_mask_workspace_bytes(int B, int H, int N, int d, int block_q, int block_k) {
+  const std::string saved = g_last_error;
+  const int rc = check_shape(B, H, N, d, block_q, block_k);
+  g_last_error = saved;
+  if (rc != SPARGE_OK || ceil_div(N, block_k) > kMaxKeyBlocks) return 0;
+  return mask_ws(B, H, N, d, block_q, block_k);
+}
+
+int sparge_mask_predict(const void* q, const void* k, int B, int H, int N, int d, int block_q,
+                        int block_k, float k_frac, float p_mass, float scale,
+                        uint32_t* mask_bits, int32_t* kv_idx, int32_t* kv_cnt,
+                        double* block_logits, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  g_last_error.clear();
+  int rc = check_shape(B, H, N, d, block_q, block_k);
+  if (rc != SPARGE_OK) return rc;
+  const int n_q = ceil_div(N, block_q), n_k = ceil_div(N, block_k);
+  if (n_k > kMaxKeyBlocks)
+    return fail(SPARGE_ERR_UNSUPPORTED, "more than 4096 key blocks (N > 262144)");
+  if (!(k_frac > 0.0f) || !(k_frac <= 1.0f))
+    return fail(SPARGE_ERR_INVALID_ARG, "k_frac must satisfy 0 < k_frac <= 1");
+  if (!(p_mass >= 0.0f) || !isfinite(p_mass))
+    return fail(SPARGE_ERR_INVALID_ARG, "p_mass must be finite and >= 0");
+  if (!(scale > 0.0f) || !isfinite(scale))
+    return fail(SPARGE_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (!q || !k || !mask_bits || !kv_idx || !kv_cnt || !workspace)
+    return fail(SPARGE_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(workspace, 16))
+    return fail(SPARGE_ERR_INVALID_ARG, "q, k and workspace must be 16-byte aligned");
+  if (!aligned(mask_bits, 4) || !aligned(kv_idx, 4) || !aligned(kv_cnt, 4))
+    return fail(SPARGE_ERR_INVALID_ARG, "mask_bits, kv_idx, kv_cnt must be 4-byte aligned");
+  if (block_logits && !aligned(block_logits, 8))
+    return fail(SPARGE_ERR_INVALID_ARG, "block_logits must be 8-byte aligned");
+  const size_t need = mask_ws(B, H, N, d, block_q, block_k);
+  if (workspace_bytes < need) return fail(SPARGE_ERR_INVALID_ARG, "workspace too small");
+
+  sparge::MaskLaunch a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.B = B; a.H = H; a.N = N; a.d = d; a.block_q = block_q; a.block_k = block_k;
+  a.n_q = n_q; a.n_k = n_k;
+  a.npad = next_pow2(n_k < 64 ? 64 : n_k);
+  a.words = ceil_div(n_k, 32);
+  // Top-k size from the float32 fraction, evaluated in double
+  const double kk = ceil((double)k_frac * n_k - 1e-6);
+  a.K_k = (int)fmin((double)n_k, fmax(1.0, kk));
+  a.keep_all = p_mass >= 1.0f;
+  a.p = (double)p_mass;
+  a.scale = (double)scale;
+  const size_t BH = (size_t)B * H;
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  a.qbar = reinterpret_cast<double*>(ws);
+  a.kbar = reinterpret_cast<double*>(ws + up(BH * n_q * d * sizeof(double)));
+  a.logits = block_logits
+                 ? block_logits
+                 : reinterpret_cast<double*>(ws + up(BH * n_q * d * sizeof(double)) +
+                                             up(BH * n_k * d * sizeof(double)));
+  a.bits = mask_bits;
+  a.idx = kv_idx;
+  a.cnt = kv_cnt;
+  const hipError_t e = sparge::launch_mask(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "sparge_mask_predict launch");
+  return SPARGE_OK;
+}
+
+int sparge_attn_fwd(const void* q, const void* k, const void* v, const int32_t* kv_idx,
+                    const int32_t* kv_cnt, int B, int H, int N, int d, int block_q,
+                    int block_k, float scale, void* o, void* stream) {
+  g_last_error.clear();
+  int rc = check_attn_args(q, k, v, kv_idx, kv_cnt, B, H, N, d, block_q, block_k, scale, o);
+  if (rc != SPARGE_OK) return rc;
+  sparge::AttnLaunch a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.idx = kv_idx;
+  a.cnt = kv_cnt;
+  a.o = static_cast<uint16_t*>(o);
+  a.B = B; a.H = H; a.N = N; a.d = d; a.block_q = block_q;
+  a.n_q = ceil_div(N, block_q);
+  a.n_k = ceil_div(N, block_k);
+  a.scale = scale;
+  const hipError_t e = sparge::launch_attn(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "sparge_attn_fwd launch");
+  return SPARGE_OK;
+}
+
+size_t sparse_linear_workspace_bytes(int B, int H, int N, int d) {
+  const std::string saved = g_last_error;
+  const int rc = check_shape(B, H, N, d, 128, 64);
+  g_last_error = saved;
+  if (rc != SPARGE_OK) return 0;
+  const size_t BH = (size_t)B * H;
+  return BH * (size_t)d * d * sizeof(float) + BH * (size_t)d * sizeof(float);
+}
+
+int sparse_linear_attn_fwd(const void* q, const void* k, const void* v,
+                           const int32_t* kv_idx, const int32_t* kv_cnt, const float* alpha,
+                           int B, int H, int N, int d, int block_q, int block_k, float scale,
+                           void* o, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  int rc = check_attn_args(q, k, v, kv_idx, kv_cnt, B, H, N, d, block_q, block_k, scale, o);
+  if (rc != SPARGE_OK) return rc;
+  if (!alpha || !workspace) return fail(SPARGE_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned(alpha, 4) || !aligned(workspace, 16))
+    return fail(SPARGE_ERR_INVALID_ARG, "alpha / workspace misaligned");
+  if (workspace_bytes < sparse_linear_workspace_bytes(B, H, N, d))
+    return fail(SPARGE_ERR_INVALID_ARG, "workspace too small");
+  return fail(SPARGE_ERR_UNSUPPORTED, "linear branch not built yet");
+}
+
+}  // extern "C"

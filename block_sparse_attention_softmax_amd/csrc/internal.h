@@ -1,0 +1,72 @@
+// Internal declarations shared by the HIP translation units of libsparge.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sparge {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// bf16 bit pattern -> float (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// float -> bf16 bit pattern, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Workgroup id -> tile id such that the tiles of one XCD are contiguous.
+// Workgroups are dispatched round-robin over the 8 XCDs (wg % 8), so the
+// remap gives each XCD a contiguous, head-major range of tiles and the
+// query blocks of one head share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int wg, int total) {
+  constexpr int XCDS = 8;
+  const int per = total / XCDS, rem = total % XCDS;
+  const int x = wg % XCDS, pos = wg / XCDS;
+  const int base = x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per;
+  return base + pos;
+}
+
+// ---- launchers (each returns the hipError_t of its launches) ----
+struct MaskLaunch {
+  const uint16_t* q;
+  const uint16_t* k;
+  int B, H, N, d, block_q, block_k, n_q, n_k, npad, words;
+  int K_k;        // Top-k size
+  int keep_all;   // p_mass >= 1
+  double p;       // Top-p mass
+  double scale;
+  double* qbar;   // [B*H, n_q, d]
+  double* kbar;   // [B*H, n_k, d]
+  double* logits; // [B*H, n_q, n_k]
+  uint32_t* bits;
+  int32_t* idx;
+  int32_t* cnt;
+};
+hipError_t launch_mask(const MaskLaunch& a, hipStream_t s);
+
+struct AttnLaunch {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* idx;
+  const int32_t* cnt;
+  uint16_t* o;
+  int B, H, N, d, block_q, n_q, n_k;
+  float scale;
+  // linear branch (null alpha = plain sparse attention)
+  const float* alpha;
+  float* lin_h;  // [B*H, d, d]  sum_u phi(K_u)^T V_u
+  float* lin_z;  // [B*H, d]     sum_u phi(K_u)
+};
+hipError_t launch_attn(const AttnLaunch& a, hipStream_t s);
+
+}  // namespace sparge

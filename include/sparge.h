@@ -1,0 +1,154 @@
+/*
+ * sparge.h - C ABI of libsparge.so: hybrid Top-k + Top-p block-sparse
+ * attention for AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one described on the page "SpargeAttention2: Trainable
+ * Sparse Attention via Hybrid Top-k+Top-p Masking and Distillation
+ * Fine-Tuning": a per-row mask that is the union of a Top-k and a Top-p
+ * selection (section 2A), applied at the level of blocks by a block-sparse
+ * FlashAttention kernel that skips the masked tiles (section 2C). The scores
+ * that pick the blocks come from mean-pooled queries and keys ("SLA2:
+ * Sparse-Linear Attention with Learnable Routing and QAT", section 2B: the
+ * router compresses Q and K by pooling adjacent tokens and scores the pooled
+ * pairs, never V). The optional linear branch over the dropped blocks is the
+ * sparse + linear split of the SLA2 page (section 1) with a static per-head
+ * down-scaling of the linear part, as the SALAD page describes it.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Q, K, V and O are device pointers to contiguous bfloat16 tensors of
+ *    shape [B, H, N, d] (row-major; d fastest), passed as raw 16-bit
+ *    patterns. They must be 16-byte aligned. The caller owns every buffer;
+ *    the library allocates nothing.
+ *  - Blocks: query block i covers tokens [i*block_q, min((i+1)*block_q, N)),
+ *    key block j covers [j*block_k, min((j+1)*block_k, N)). n_q =
+ *    ceil(N/block_q), n_k = ceil(N/block_k). The last block may be short.
+ *  - Supported shapes: d in {64, 128}; block_q in {64, 128}; block_k = 64;
+ *    B, H, N >= 1; n_k <= 4096 for the mask (N <= 262144).
+ *  - `stream` is a hipStream_t cast to void* (NULL = the default stream).
+ *    Every call only enqueues work on that stream and returns; outputs are
+ *    valid once the stream reaches that point.
+ *  - Return value: SPARGE_OK, or a negative sparge_status. Arguments are
+ *    checked on the host before anything is enqueued; on a failed check
+ *    nothing is launched and sparge_last_error() says why. A failed launch
+ *    returns SPARGE_ERR_HIP. No call throws.
+ *  - Calls are thread-safe; the library keeps no state besides the
+ *    per-thread error message.
+ */
+#ifndef SPARGE_H
+#define SPARGE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SPARGE_OK = 0,
+  SPARGE_ERR_INVALID_ARG = -1, /* a bad size, value, pointer or workspace  */
+  SPARGE_ERR_UNSUPPORTED = -2, /* valid request outside the built shapes   */
+  SPARGE_ERR_HIP = -3          /* the HIP runtime reported an error        */
+} sparge_status;
+
+/* Device workspace (bytes) that sparge_mask_predict needs: the pooled
+ * queries and keys and the block scores, all float64. Returns 0 for
+ * arguments that sparge_mask_predict would reject. */
+size_t sparge_mask_workspace_bytes(int B, int H, int N, int d, int block_q,
+                                   int block_k);
+
+/* Block mask by the hybrid Top-k + Top-p rule (SpargeAttention2 page,
+ * sections 1 and 2A; pooled scores as on the SLA2 page, section 2B).
+ *
+ * For every (b, h) and query block i:
+ *   Qbar_i, Kbar_j = means of the valid rows of query block i / key block j;
+ *   s_ij  = scale * <Qbar_i, Kbar_j>, P_i = softmax over j of s_i;
+ *   order = key blocks by s_ij descending, equal scores by lower j first;
+ *   K_k   = min(n_k, max(1, ceil(k_frac * n_k - 1e-6)))   (Top-k size);
+ *   m_p   = least m with P mass of the first m blocks >= p_mass, summed in
+ *           that order (Top-p size); n_k if p_mass >= 1 or never reached;
+ *   kept  = the first max(K_k, m_p) blocks of the order (the union of the
+ *           Top-k and the Top-p sets, both prefixes of one order).
+ * Pooling, scores, softmax and prefix sums are evaluated in float64.
+ *
+ *  q, k        : bf16 [B, H, N, d], device, 16-byte aligned.
+ *  k_frac      : Top-k fraction, 0 < k_frac <= 1.
+ *  p_mass      : Top-p mass, p_mass >= 0 (0 = Top-k alone; >= 1 = keep all).
+ *  scale       : score scale, finite and > 0 (normally 1/sqrt(d)).
+ *  mask_bits   : out uint32 [B, H, n_q, ceil(n_k/32)]; bit j%32 of word
+ *                j/32 is set iff key block j is kept. 4-byte aligned.
+ *  kv_idx      : out int32 [B, H, n_q, n_k]; the first kv_cnt entries of a
+ *                row list the kept key blocks in ascending order; the rest
+ *                of the row is left untouched. 4-byte aligned.
+ *  kv_cnt      : out int32 [B, H, n_q], number of kept blocks per row.
+ *  block_logits: optional out float64 [B, H, n_q, n_k] (the scores s), or
+ *                NULL. 8-byte aligned.
+ *  workspace   : device scratch of at least sparge_mask_workspace_bytes(),
+ *                16-byte aligned; contents on entry do not matter.
+ */
+int sparge_mask_predict(const void* q, const void* k, int B, int H, int N, int d,
+                        int block_q, int block_k, float k_frac, float p_mass,
+                        float scale, uint32_t* mask_bits, int32_t* kv_idx,
+                        int32_t* kv_cnt, double* block_logits, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* Block-sparse attention forward (SpargeAttention2 page, section 2C): for
+ * every query t of query block i,
+ *   O_t = sum_u softmax_u(scale * <Q_t, K_u>) V_u
+ * where u runs over the valid keys of the key blocks listed in row i of
+ * kv_idx / kv_cnt only; blocks not listed are skipped entirely. A row with
+ * kv_cnt = 0 yields zeros. Products use bf16 inputs with float32
+ * accumulation; the softmax runs online in float32; O is rounded to bf16
+ * (nearest even).
+ *
+ *  q, k, v : bf16 [B, H, N, d], device, 16-byte aligned.
+ *  kv_idx  : int32 [B, H, n_q, n_k]; first kv_cnt entries of each row are
+ *            key block indices in [0, n_k). Any such list is accepted (for
+ *            example the output of sparge_mask_predict, or a fixed local
+ *            window). Counts are clamped to [0, n_k] and indices to
+ *            [0, n_k - 1], so a corrupt list cannot read out of bounds.
+ *  kv_cnt  : int32 [B, H, n_q].
+ *  o       : out bf16 [B, H, N, d], device, 16-byte aligned; must not
+ *            overlap the inputs.
+ */
+int sparge_attn_fwd(const void* q, const void* k, const void* v,
+                    const int32_t* kv_idx, const int32_t* kv_cnt, int B, int H,
+                    int N, int d, int block_q, int block_k, float scale, void* o,
+                    void* stream);
+
+/* Device workspace (bytes) of sparse_linear_attn_fwd: per (b, h) the float32
+ * summaries sum_u phi(K_u)^T V_u (d x d) and sum_u phi(K_u) (d). Returns 0
+ * for arguments that sparse_linear_attn_fwd would reject. */
+size_t sparse_linear_workspace_bytes(int B, int H, int N, int d);
+
+/* Sparse attention plus a linear-attention branch over the dropped blocks
+ * (sparse / linear split of the SLA2 page, section 1; static down-scaling of
+ * the linear branch as on the SALAD page):
+ *   O_t = O_s,t + alpha[h] * O_l,t,
+ * O_s as in sparge_attn_fwd, and with phi(x) = elu(x) + 1 elementwise and D_i
+ * the valid keys of the blocks NOT listed in row i,
+ *   O_l,t = sum_{u in D_i} (phi(Q_t).phi(K_u)) V_u / sum_{u in D_i} phi(Q_t).phi(K_u),
+ * and O_l,t = 0 when D_i is empty. phi is applied to the unscaled Q and K.
+ * The linear branch accumulates in float32. Setting alpha[h] = 0 still
+ * evaluates the branch; callers that drop it should call sparge_attn_fwd.
+ *
+ *  alpha     : float32 [H], device.
+ *  workspace : device scratch of at least sparse_linear_workspace_bytes(),
+ *              16-byte aligned; contents on entry do not matter.
+ *  Other arguments as for sparge_attn_fwd. */
+int sparse_linear_attn_fwd(const void* q, const void* k, const void* v,
+                           const int32_t* kv_idx, const int32_t* kv_cnt,
+                           const float* alpha, int B, int H, int N, int d,
+                           int block_q, int block_k, float scale, void* o,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Message for the last non-OK return on the calling thread ("" if none).
+ * The pointer stays valid until the next library call on that thread. */
+const char* sparge_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARGE_H */

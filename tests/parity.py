@@ -1,0 +1,83 @@
+"""Comparison helpers shared by the GPU parity tests (not a test module).
+
+Masks: rows whose oracle margin is at least 1e-5 must match bit for bit
+(bitmask, count, index list). Rows under that margin may legitimately differ;
+such a GPU row is accepted if it is admissible: (i) it keeps at least K_k
+blocks, (ii) its oracle probability mass is at least p - 1e-5 (or it keeps
+all blocks when p >= 1), (iii) no kept block scores more than 1e-5 below a
+dropped block, and (iv) it is minimal: without its lowest-scoring block it
+would hold fewer than K_k blocks or less than p + 1e-5 mass.
+
+Outputs: max |O_gpu - O_oracle| <= 2e-2 and mean <= 2e-3 over valid rows.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import sparge_oracle as O
+
+MAX_ABS, MEAN_ABS, TIE = 2e-2, 2e-3, 1e-5
+
+
+def to_gpu(bits_u16: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits_u16)).view(torch.bfloat16).cuda()
+
+
+def gpu_bits_to_bool(bits_i32: torch.Tensor, n_k: int) -> np.ndarray:
+    w = bits_i32.cpu().numpy().view(np.uint32)
+    j = np.arange(n_k)
+    return ((w[..., j // 32] >> (j % 32).astype(np.uint32)) & 1).astype(bool)
+
+
+def check_index_list(kept: np.ndarray, idx: np.ndarray, cnt: np.ndarray):
+    """GPU idx/cnt must list exactly the set bits, ascending."""
+    flat_k = kept.reshape(-1, kept.shape[-1])
+    flat_i = idx.reshape(-1, idx.shape[-1])
+    flat_c = cnt.reshape(-1)
+    assert (flat_c == flat_k.sum(1)).all(), "count differs from popcount of the bitmask"
+    for r in range(flat_k.shape[0]):
+        want = np.nonzero(flat_k[r])[0]
+        got = flat_i[r, : flat_c[r]]
+        if not np.array_equal(got, want):
+            raise AssertionError(f"row {r}: idx {got[:8]}... != bits {want[:8]}...")
+
+
+def compare_masks(m: O.MaskResult, gpu_kept: np.ndarray, k_frac: float, p_mass: float):
+    """Returns (n_near_tie_rows, n_near_tie_rows_that_differ). Raises on failure."""
+    n_k = gpu_kept.shape[-1]
+    p = float(np.float32(p_mass))
+    tie = m.margin < TIE
+    same = (gpu_kept == m.kept).all(-1)
+    bad = ~same & ~tie
+    if bad.any():
+        r = np.argwhere(bad)[0]
+        raise AssertionError(f"mask differs on a row with margin {m.margin[tuple(r)]:.3e} "
+                             f"at {tuple(r)}: gpu cnt {gpu_kept[tuple(r)].sum()} "
+                             f"oracle cnt {m.cnt[tuple(r)]}; {bad.sum()} such rows")
+    P = O.row_softmax(m.logits)
+    for r in np.argwhere(tie & ~same):
+        r = tuple(r)
+        keep = gpu_kept[r]
+        s, Pr = m.logits[r], P[r]
+        assert keep.sum() >= m.K_k
+        if p >= 1:
+            assert keep.all()
+            continue
+        assert Pr[keep].sum() >= p - TIE
+        if not keep.all():
+            assert s[keep].min() >= s[~keep].max() - TIE
+        low = np.argmin(np.where(keep, s, np.inf))
+        rest = keep.copy()
+        rest[low] = False
+        assert rest.sum() < m.K_k or Pr[rest].sum() < p + TIE
+    return int(tie.sum()), int((tie & ~same).sum())
+
+
+def compare_outputs(o_gpu: np.ndarray, o_ref: np.ndarray):
+    """o_gpu, o_ref: float64 arrays over the same valid rows."""
+    err = np.abs(o_gpu - o_ref)
+    assert np.isfinite(o_gpu).all(), "non-finite GPU output"
+    mx, mean = float(err.max()), float(err.mean())
+    assert mx <= MAX_ABS and mean <= MEAN_ABS, f"max {mx:.3e} mean {mean:.3e}"
+    return mx, mean

@@ -1,0 +1,107 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol,
+sizes its workspaces, and rejects bad arguments before it touches HIP."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from block_sparse_attention_softmax_amd import binding
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "sparge.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(binding.LIB_PATH),
+                                reason="libsparge.so not built")
+
+A = ctypes.c_void_p(0x10000)      # aligned, never dereferenced: checks fail first
+MIS = ctypes.c_void_p(0x10002)    # misaligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_bound_symbols():
+    assert declared_functions() == sorted(binding.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = binding.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_mask_workspace_bytes():
+    L = binding.lib()
+    up = lambda x: (x + 255) // 256 * 256
+    B, H, N, d = 1, 12, 32760, 128
+    n_q, n_k = math.ceil(N / 128), math.ceil(N / 64)
+    want = up(B * H * n_q * d * 8) + up(B * H * n_k * d * 8) + up(B * H * n_q * n_k * 8)
+    assert L.sparge_mask_workspace_bytes(B, H, N, d, 128, 64) == want
+    assert L.sparge_mask_workspace_bytes(1, 1, 100, 96, 128, 64) == 0       # bad d
+    assert L.sparge_mask_workspace_bytes(1, 1, 64 * 4097, 64, 64, 64) == 0  # > 4096 blocks
+    assert L.sparse_linear_workspace_bytes(1, 40, 75600, 128) == 40 * (128 * 128 + 128) * 4
+
+
+def _mask(**kw):
+    args = dict(q=A, k=A, B=1, H=2, N=1024, d=64, bq=64, bk=64, kf=0.1, p=0.9, sc=0.125,
+                bits=A, idx=A, cnt=A, logits=None, ws=A, wsb=1 << 30, st=None)
+    args.update(kw)
+    L = binding.lib()
+    return L.sparge_mask_predict(*args.values())
+
+
+def _attn(**kw):
+    args = dict(q=A, k=A, v=A, idx=A, cnt=A, B=1, H=2, N=1024, d=64, bq=64, bk=64, sc=0.125,
+                o=A, st=None)
+    args.update(kw)
+    return binding.lib().sparge_attn_fwd(*args.values())
+
+
+def _lin(**kw):
+    args = dict(q=A, k=A, v=A, idx=A, cnt=A, alpha=A, B=1, H=2, N=1024, d=64, bq=64, bk=64,
+                sc=0.125, o=A, ws=A, wsb=1 << 30, st=None)
+    args.update(kw)
+    return binding.lib().sparse_linear_attn_fwd(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(bits=None), -1), (dict(ws=None), -1),
+    (dict(q=MIS), -1), (dict(idx=ctypes.c_void_p(0x10001)), -1),
+    (dict(logits=ctypes.c_void_p(0x10004)), -1),
+    (dict(d=96), -2), (dict(bq=32), -2), (dict(bk=128), -2),
+    (dict(B=0), -1), (dict(H=-1), -1), (dict(N=0), -1),
+    (dict(kf=0.0), -1), (dict(kf=1.5), -1), (dict(kf=float("nan")), -1),
+    (dict(p=-0.1), -1), (dict(p=float("inf")), -1), (dict(p=float("nan")), -1),
+    (dict(sc=0.0), -1), (dict(sc=float("nan")), -1),
+    (dict(wsb=100), -1), (dict(N=64 * 4097), -2),
+])
+def test_mask_rejects_bad_arguments(kw, code):
+    assert _mask(**kw) == code
+    assert binding.lib().sparge_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(o=None), -1), (dict(cnt=None), -1), (dict(v=MIS), -1),
+    (dict(d=80), -2), (dict(bq=256), -2), (dict(bk=32), -2), (dict(N=0), -1),
+    (dict(sc=-1.0), -1), (dict(sc=float("inf")), -1),
+])
+def test_attn_rejects_bad_arguments(kw, code):
+    assert _attn(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(alpha=None), -1), (dict(ws=None), -1), (dict(wsb=16), -1), (dict(q=None), -1),
+    (dict(d=32), -2), (dict(alpha=ctypes.c_void_p(0x10001)), -1),
+])
+def test_linear_rejects_bad_arguments(kw, code):
+    assert _lin(**kw) == code
+
+
+def test_error_message_is_per_call():
+    assert _attn(d=80) == -2
+    assert "d must be" in binding.lib().sparge_last_error().decode()
+    assert _mask(kf=0.0) == -1
+    assert "k_frac" in binding.lib().sparge_last_error().decode()

@@ -1,0 +1,154 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Masks are compared bit for bit outside near-tie rows (see parity.py);
+outputs within max-abs 2e-2 and mean-abs 2e-3 of the float64 oracle. Small
+shapes are compared in full (several tiles and a ragged tail in both the
+query and the key direction); the full-size workloads compare every mask row
+and a seeded sample of query blocks of the output, in the launch
+configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_attention_softmax_amd import binding as S
+from block_sparse_attention_softmax_amd.workloads import WORKLOADS, generate
+from oracle import sparge_oracle as O
+from parity import (check_index_list, compare_masks, compare_outputs, gpu_bits_to_bool,
+                    to_gpu)
+
+pytestmark = pytest.mark.gpu
+
+_CACHE = {}
+
+
+def workload_tensors(name):
+    if name not in _CACHE:
+        _CACHE.clear()
+        wl = WORKLOADS[name]
+        Q, K, V = generate(wl)
+        _CACHE[name] = (wl, Q, K, V, to_gpu(Q), to_gpu(K), to_gpu(V))
+    return _CACHE[name]
+
+
+def run_mask(wl, q, k, k_frac=None, p_mass=None):
+    k_frac = wl.k_frac if k_frac is None else k_frac
+    p_mass = wl.p_mass if p_mass is None else p_mass
+    bits, idx, cnt, logits = S.sparge_mask_predict(q, k, wl.block_q, wl.block_k, k_frac, p_mass,
+                                                   wl.scale, return_logits=True)
+    torch.cuda.synchronize()
+    n_k = wl.n_k
+    kept = gpu_bits_to_bool(bits, n_k)
+    idx_np, cnt_np = idx.cpu().numpy(), cnt.cpu().numpy()
+    check_index_list(kept, idx_np, cnt_np)
+    return kept, idx, cnt, logits.cpu().numpy()
+
+
+@pytest.mark.parametrize("name", ["tiny", "wan1.3b", "wan1.3b_s95", "wan14b_720p"])
+def test_mask_matches_oracle(name):
+    wl, Q, K, V, q, k, v = workload_tensors(name)
+    print(f"\n[mask] {name} B={wl.B} H={wl.H} N={wl.N} d={wl.d}", flush=True)
+    kept, idx, cnt, logits = run_mask(wl, q, k)
+    m = O.predict_mask(Q, K, wl.block_q, wl.block_k, wl.k_frac, wl.p_mass, wl.scale)
+    np.testing.assert_allclose(logits, m.logits, rtol=1e-12, atol=1e-12)
+    ties, differ = compare_masks(m, kept, wl.k_frac, wl.p_mass)
+    sparsity = 1 - kept.sum() / kept.size
+    print(f"[mask] {name}: sparsity {sparsity:.4f} near-tie rows {ties} differing {differ}",
+          flush=True)
+
+
+@pytest.mark.parametrize("k_frac", [0.10, 0.05])
+def test_mask_topk_only_operating_points(k_frac):
+    """p = 0 (Top-k alone): the 90% and 95% block-sparsity points on wan1.3b inputs."""
+    wl, Q, K, V, q, k, v = workload_tensors("wan1.3b")
+    kept, idx, cnt, logits = run_mask(wl, q, k, k_frac=k_frac, p_mass=0.0)
+    m = O.predict_mask(Q, K, wl.block_q, wl.block_k, k_frac, 0.0, wl.scale)
+    compare_masks(m, kept, k_frac, 0.0)
+    assert (cnt.cpu().numpy() == O.topk_size(k_frac, wl.n_k)).all()
+
+
+def test_uniform_rows_keep_lowest_indices():
+    """Q = 0 gives exactly equal block scores: Top-p(0.9) keeps 15 of 16 blocks, ties to the
+    lower index (the uniform-row case of the SpargeAttention2 page, section 1)."""
+    B, H, N, d = 1, 2, 1024, 64
+    g = torch.Generator().manual_seed(0)
+    q = torch.zeros(B, H, N, d, dtype=torch.bfloat16).cuda()
+    k = torch.randn(B, H, N, d, generator=g).to(torch.bfloat16).cuda()
+    bits, idx, cnt = S.sparge_mask_predict(q, k, 64, 64, 0.1, 0.9)
+    assert (cnt.cpu() == 15).all()
+    assert (idx.cpu()[..., :15] == torch.arange(15, dtype=torch.int32)).all()
+    bits, idx, cnt = S.sparge_mask_predict(q, k, 64, 64, 0.1, 0.0)
+    assert (cnt.cpu() == 2).all()
+    assert (idx.cpu()[..., :2] == torch.tensor([0, 1], dtype=torch.int32)).all()
+
+
+# --------------------------------------------------------------- attention
+def _random_lists(rng, B, H, n_q, n_k):
+    kept = rng.random((B, H, n_q, n_k)) < rng.uniform(0.05, 0.7)
+    flat = kept.reshape(-1, n_k)
+    flat[0] = False                      # an empty row -> zeros
+    if flat.shape[0] > 1:
+        flat[1] = True                   # a dense row
+    if flat.shape[0] > 2:
+        flat[2] = False
+        flat[2, n_k - 1] = True          # only the short last block
+    return kept
+
+
+@pytest.mark.parametrize("B,H,N,d,bq", [
+    (1, 2, 1000, 128, 128), (2, 1, 1000, 64, 64), (1, 3, 777, 128, 64),
+    (1, 2, 300, 64, 128), (1, 1, 50, 128, 128), (2, 2, 1, 64, 64), (1, 1, 4096, 128, 128)])
+def test_attention_small_shapes_in_full(B, H, N, d, bq):
+    rng = np.random.default_rng(N + d + bq)
+    from block_sparse_attention_softmax_amd.workloads import f64_to_bf16_bits
+    Q, K, V = (f64_to_bf16_bits(rng.standard_normal((B, H, N, d)) * 1.5) for _ in range(3))
+    n_q, n_k = -(-N // bq), -(-N // 64)
+    kept = _random_lists(rng, B, H, n_q, n_k)
+    idx, cnt = O.kept_to_index_list(kept)
+    print(f"\n[attn] B={B} H={H} N={N} d={d} bq={bq}", flush=True)
+    o = S.sparge_attn_fwd(to_gpu(Q), to_gpu(K), to_gpu(V), torch.from_numpy(idx).cuda(),
+                          torch.from_numpy(cnt).cuda(), bq, 64, None)
+    torch.cuda.synchronize()
+    got = O.bf16_to_f64(o.cpu().view(torch.uint16).numpy())
+    scale = S.default_scale(d)
+    for b in range(B):
+        for h in range(H):
+            ref = O.masked_attention_head(O.bf16_to_f64(Q[b, h]), O.bf16_to_f64(K[b, h]),
+                                          O.bf16_to_f64(V[b, h]), kept[b, h], bq, 64, scale)
+            compare_outputs(got[b, h], ref)
+
+
+def test_attention_is_deterministic():
+    wl, Q, K, V, q, k, v = workload_tensors("tiny")
+    bits, idx, cnt = S.sparge_mask_predict(q, k, wl.block_q, wl.block_k, wl.k_frac, wl.p_mass)
+    o1 = S.sparge_attn_fwd(q, k, v, idx, cnt, wl.block_q, wl.block_k)
+    o2 = S.sparge_attn_fwd(q, k, v, idx, cnt, wl.block_q, wl.block_k)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+@pytest.mark.parametrize("name,samples", [("tiny", None), ("wan1.3b", 6), ("wan1.3b_s95", 6),
+                                          ("wan14b_720p", 4)])
+def test_attention_matches_oracle_on_workloads(name, samples):
+    """Mask and attention as the benchmark runs them; the oracle uses the GPU's mask."""
+    wl, Q, K, V, q, k, v = workload_tensors(name)
+    print(f"\n[attn] {name}", flush=True)
+    bits, idx, cnt = S.sparge_mask_predict(q, k, wl.block_q, wl.block_k, wl.k_frac, wl.p_mass)
+    o = S.sparge_attn_fwd(q, k, v, idx, cnt, wl.block_q, wl.block_k)
+    torch.cuda.synchronize()
+    kept = gpu_bits_to_bool(bits, wl.n_k)
+    got = O.bf16_to_f64(o.cpu().view(torch.uint16).numpy())
+    rng = np.random.default_rng(2024)
+    for b in range(wl.B):
+        heads = range(wl.H) if samples is None else rng.choice(wl.H, size=2, replace=False)
+        for h in heads:
+            if samples is None:
+                blocks = None
+            else:  # always the first and the short last block, plus a seeded sample
+                blocks = sorted({0, wl.n_q - 1, *rng.choice(wl.n_q, samples - 2, replace=False)})
+            ref = O.masked_attention_head(O.bf16_to_f64(Q[b, h]), O.bf16_to_f64(K[b, h]),
+                                          O.bf16_to_f64(V[b, h]), kept[b, h], wl.block_q,
+                                          wl.block_k, wl.scale, q_blocks=blocks)
+            rows = ~np.isnan(ref[:, 0])
+            mx, mean = compare_outputs(got[b, h][rows], ref[rows])
+            print(f"[attn] {name} b={b} h={h}: max {mx:.2e} mean {mean:.2e}", flush=True)
