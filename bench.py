@@ -88,6 +88,9 @@ def main():
     ap.add_argument("--cpu-blocks", type=int, default=256,
                     help="query blocks of the oracle's CPU sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one device-to-device copy of this many MiB first, as a "
+                         "known-size reference for hardware byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
@@ -113,6 +116,14 @@ def main():
     ws = torch.empty(S.mask_workspace_bytes(B, H, N, d, wl.block_q, wl.block_k),
                      dtype=torch.uint8, device=dev)
     o = torch.empty_like(q)
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step(k_frac, p_mass, ev=None):
         if ev is not None:

@@ -55,6 +55,9 @@ def build(verbose: bool = True) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
+    # resolve every symbol now: a missing kernel stub fails here, not at first use
+    import ctypes
+    ctypes.CDLL(tmp, mode=os.RTLD_NOW)
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

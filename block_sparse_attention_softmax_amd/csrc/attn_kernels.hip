@@ -26,17 +26,50 @@ namespace {
 
 constexpr int BK = 64;
 
+// LDS holds K and V tiles row-major ([64 keys][D] bf16), 16-byte chunks of
+// each row XOR-swizzled with the row index so that the MFMA operand reads
+// below hit distinct banks: chunk c of row r lives at chunk c ^ (r & SWZ).
 template <int D>
-struct Lds {
-  static constexpr int KS = D * 2 + 16;  // K row pitch (bytes), 16 B pad
-  static constexpr int VS = BK * 2 + 16; // V^T row pitch (bytes), 16 B pad
-  static constexpr int KBUF = BK * KS;
-  static constexpr int VBUF = D * VS;
-  static constexpr int STAGE = KBUF + VBUF;
+struct Tile {
+  static constexpr int ROWB = D * 2;              // bytes per row
+  static constexpr int CPR = D / 8;               // 16-byte chunks per row
+  static constexpr int SWZ = CPR - 1;             // 15 (D=128) or 7 (D=64)
+  static constexpr int BYTES = BK * ROWB;         // one K or V tile
+  static constexpr int STAGE = 2 * BYTES;         // K + V
+  __device__ static constexpr int off(int row, int chunk) {
+    return row * ROWB + ((chunk ^ (row & SWZ)) << 4);
+  }
 };
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// 16-byte global -> LDS copy without a register round trip (global_load_lds
+// dwordx4). `lds` must be the same for the whole wave: lane i's 16 bytes land
+// at lds + 16 * i. (Kept out of the kernel templates: the host pass drops a
+// template kernel's launch stub when its body names this builtin.)
+__device__ __forceinline__ void dma16(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+}
 
 __device__ __forceinline__ bf16x8 lds_read16(const unsigned char* p) {
   return *reinterpret_cast<const bf16x8*>(p);
+}
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16). Within each group of 16
+// lanes, lane i receives element (i & 3) of the 4-element rows addressed by
+// lanes 4e + (i >> 2), e = 0..3. When four lanes address the 16 consecutive
+// d-values of one key row and the group covers four key rows, every lane
+// gets the four keys at its own d.
+__device__ __forceinline__ v4i16 lds_read_tr(const unsigned char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_v4i16*)(reinterpret_cast<uintptr_t>(p)));
+}
+
+__device__ __forceinline__ bf16x8 join(v4i16 lo, v4i16 hi) {
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  const v8i16 r = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, r);
 }
 
 __device__ __forceinline__ bf16x8 pack_bf16x8(const floatx16& x, int base) {
@@ -46,14 +79,23 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(const floatx16& x, int base) {
   return r;
 }
 
-// Slot (in bf16 units, within a 64-key row of V^T) of the first of the four
-// consecutive keys 4*kg .. 4*kg+3. Inside each group of 16 keys, slots
-// 8*h + e (h = lane / 32, e = 0..7) hold key 8*(e/4) + 4*h + e%4, which is
-// the key that register 8*hk + e of the S^T accumulator holds for that lane.
-__device__ __forceinline__ int vt_slot(int kg) {
-  const int m = kg & 3;
-  return 16 * (kg >> 2) + 8 * (m & 1) + 4 * (m >> 1);
+// max over the two half-waves (lane l and lane l ^ 32): the swap returns
+// both values of the pair in its two results
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// A kept row's running maximum is only raised (and O rescaled) when a block
+// raises it by more than 2^8 in the exponent; until then P <= 2^8, which
+// float32 sums and bf16 products carry without loss of relative precision.
+constexpr float kRescaleLog2 = 8.0f;
 
 template <int D, int BQ>
 __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void sparse_attn_fwd_kernel(
@@ -61,22 +103,18 @@ __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void sparse
     const uint16_t* __restrict__ v, const int32_t* __restrict__ kv_idx,
     const int32_t* __restrict__ kv_cnt, uint16_t* __restrict__ o, int N, int n_q,
     int n_k, int total, float c) {
-  constexpr int NT = BQ * 2;               // threads (BQ/32 waves)
-  constexpr int KCH = D / 8;               // 16-byte chunks per row
-  constexpr int KUNITS = BK * KCH;         // K chunks per block
-  constexpr int KPT = KUNITS / NT;         // K chunks per thread
-  constexpr int VUNITS = 16 * KCH;         // (4 keys x 8 d) V units per block
-  constexpr int VPT = (VUNITS + NT - 1) / NT;
-  constexpr int DT = D / 32;               // O^T tiles per wave
-  constexpr int KSTEPS = D / 16;           // k-steps of the QK product
-  using L = Lds<D>;
-  static_assert(KUNITS % NT == 0, "K staging must divide evenly");
+  constexpr int NW = BQ / 32;               // waves, 32 query rows each
+  using T = Tile<D>;
+  constexpr int LOADS = BK * T::CPR / 64 / NW;  // 16-byte DMA loads per lane per tile
+  constexpr int DT = D / 32;                // O^T tiles per wave
+  constexpr int KSTEPS = D / 16;            // k-steps of the QK product
 
-  __shared__ __align__(16) unsigned char smem[2 * L::STAGE];
+  __shared__ __align__(16) unsigned char smem[2 * T::STAGE];
 
   const int tile = xcd_remap(blockIdx.x, total);
   const int bh = tile / n_q, qi = tile % n_q;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int h2 = lane >> 5, l32 = lane & 31;
   const size_t head = (size_t)bh * N * D;
 
@@ -84,16 +122,9 @@ __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void sparse
   const int qrow = qi * BQ + wave * 32 + l32;
   bf16x8 qf[KSTEPS];
   {
-    const uint16_t* qp = q + head + (size_t)qrow * D + 8 * h2;
+    const uint16_t* qp = q + head + (size_t)min(qrow, N - 1) * D + 8 * h2;
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-      if (qrow < N) {
-        qf[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qf[s][e] = (__bf16)0.0f;
-      }
-    }
+    for (int s = 0; s < KSTEPS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
   }
 
   const int count = min(max(kv_cnt[tile], 0), n_k);
@@ -101,66 +132,58 @@ __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void sparse
   const uint16_t* kh = k + head;
   const uint16_t* vh = v + head;
 
-  uint4 kreg[KPT];
-  uint4 vreg[VPT][4];
-
-  auto gload = [&](int j) {
+  // ---- DMA staging: wave w, load u fills LDS chunks [64*(u*NW+w), +64),
+  // lane-linear; each lane fetches the global chunk that the swizzle maps
+  // there. Per-lane element offsets within a tile are loop invariant.
+  int src_row[LOADS], src_off[LOADS];
+#pragma unroll
+  for (int u = 0; u < LOADS; ++u) {
+    const int p = 64 * (u * NW + wave) + lane;   // LDS chunk index
+    const int row = p / T::CPR;
+    const int ch = (p % T::CPR) ^ (row & T::SWZ);
+    src_row[u] = row;
+    src_off[u] = row * D + ch * 8;
+  }
+  auto stage = [&](int j, int buf) {
+    unsigned char* kb = smem + buf * T::STAGE;
+    unsigned char* vb = kb + T::BYTES;
     const int key0 = j * BK;
+    const uint16_t* kt = kh + (size_t)key0 * D;
+    const uint16_t* vt = vh + (size_t)key0 * D;
+    if (key0 + BK <= N) {
 #pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int cu = t + NT * u, row = cu / KCH, ch = cu % KCH;
-      const int key = key0 + row;
-      kreg[u] = key < N ? *reinterpret_cast<const uint4*>(kh + (size_t)key * D + ch * 8)
-                        : make_uint4(0, 0, 0, 0);
-    }
+      for (int u = 0; u < LOADS; ++u) {
+        const int dst = 1024 * (u * NW + wave);
+        dma16(kt + src_off[u], kb + dst);
+        dma16(vt + src_off[u], vb + dst);
+      }
+    } else {  // short last block: rows past N repeat row N-1 (masked below)
 #pragma unroll
-    for (int u = 0; u < VPT; ++u) {
-      const int vu = t + NT * u;
-      if (vu < VUNITS) {
-        const int kg = vu & 15, ch = vu >> 4;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = key0 + 4 * kg + r;
-          vreg[u][r] = key < N
-                           ? *reinterpret_cast<const uint4*>(vh + (size_t)key * D + ch * 8)
-                           : make_uint4(0, 0, 0, 0);
-        }
+      for (int u = 0; u < LOADS; ++u) {
+        const int dst = 1024 * (u * NW + wave);
+        const int shift = max(key0 + src_row[u] - (N - 1), 0) * D;
+        dma16(kt + src_off[u] - shift, kb + dst);
+        dma16(vt + src_off[u] - shift, vb + dst);
       }
     }
   };
 
-  auto swrite = [&](int buf) {
-    unsigned char* ks = smem + buf * L::STAGE;
-    unsigned char* vt = ks + L::KBUF;
+  // ---- per-lane LDS read offsets (loop invariant)
+  int koff[KSTEPS];  // K rows l32 (+32 tau), chunk 2s + h2
 #pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int cu = t + NT * u, row = cu / KCH, ch = cu % KCH;
-      *reinterpret_cast<uint4*>(ks + row * L::KS + ch * 16) = kreg[u];
+  for (int s = 0; s < KSTEPS; ++s) koff[s] = T::off(l32, 2 * s + h2);
+  // V^T operand: group of 16 lanes gq, lane li within it; read r covers keys
+  // 16G + 8r + 4*h2 + (li >> 2), d = 32i + 16*(gq & 1) + 4*(li & 3)
+  const int gq = lane >> 4, li = lane & 15;
+  int voff[2][DT];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int i = 0; i < DT; ++i) {
+      const int key = 8 * r + 4 * h2 + (li >> 2);
+      const int d = 32 * i + 16 * (gq & 1) + 4 * (li & 3);
+      voff[r][i] = T::off(key, d >> 3) + (d & 7) * 2;
     }
-#pragma unroll
-    for (int u = 0; u < VPT; ++u) {
-      const int vu = t + NT * u;
-      if (vu < VUNITS) {
-        const int kg = vu & 15, ch = vu >> 4;
-        unsigned char* dst = vt + (ch * 8) * L::VS + vt_slot(kg) * 2;
-        const uint32_t w0[4] = {vreg[u][0].x, vreg[u][0].y, vreg[u][0].z, vreg[u][0].w};
-        const uint32_t w1[4] = {vreg[u][1].x, vreg[u][1].y, vreg[u][1].z, vreg[u][1].w};
-        const uint32_t w2[4] = {vreg[u][2].x, vreg[u][2].y, vreg[u][2].z, vreg[u][2].w};
-        const uint32_t w3[4] = {vreg[u][3].x, vreg[u][3].y, vreg[u][3].z, vreg[u][3].w};
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          // d = 8*ch + 2w (low halves) and 8*ch + 2w + 1 (high halves)
-          uint2 lo, hi;
-          lo.x = (w0[w] & 0xFFFFu) | (w1[w] << 16);
-          lo.y = (w2[w] & 0xFFFFu) | (w3[w] << 16);
-          hi.x = (w0[w] >> 16) | (w1[w] & 0xFFFF0000u);
-          hi.y = (w2[w] >> 16) | (w3[w] & 0xFFFF0000u);
-          *reinterpret_cast<uint2*>(dst + (2 * w) * L::VS) = lo;
-          *reinterpret_cast<uint2*>(dst + (2 * w + 1) * L::VS) = hi;
-        }
-      }
-    }
-  };
 
   floatx16 oacc[DT];
 #pragma unroll
@@ -169,20 +192,16 @@ __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void sparse
     for (int r = 0; r < 16; ++r) oacc[i][r] = 0.0f;
   float m = -INFINITY, lsum = 0.0f;
 
-  int jcur = count > 0 ? min(max(ids[0], 0), n_k - 1) : 0;
-  if (count > 0) gload(jcur);
+  if (count > 0) stage(min(max(ids[0], 0), n_k - 1), 0);
 
   for (int it = 0; it < count; ++it) {
     const int buf = it & 1;
-    swrite(buf);
-    __syncthreads();
-    const int j = jcur;
-    if (it + 1 < count) {
-      jcur = min(max(ids[it + 1], 0), n_k - 1);
-      gload(jcur);
-    }
-    const unsigned char* ks = smem + buf * L::STAGE;
-    const unsigned char* vt = ks + L::KBUF;
+    const int j = min(max(ids[it], 0), n_k - 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this lane's DMA for buf landed
+    __syncthreads();                     // all lanes' DMA landed; buf^1 is free
+    if (it + 1 < count) stage(min(max(ids[it + 1], 0), n_k - 1), buf ^ 1);
+    const unsigned char* kb = smem + buf * T::STAGE;
+    const unsigned char* vb = kb + T::BYTES;
 
     // ---- S^T = K_j Q^T : two 32-key tiles
     floatx16 st[2];
@@ -194,7 +213,7 @@ __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void sparse
     for (int s = 0; s < KSTEPS; ++s) {
 #pragma unroll
       for (int tau = 0; tau < 2; ++tau) {
-        const bf16x8 a = lds_read16(ks + (32 * tau + l32) * L::KS + (16 * s + 8 * h2) * 2);
+        const bf16x8 a = lds_read16(kb + tau * 32 * T::ROWB + koff[s]);
         st[tau] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], st[tau], 0, 0, 0);
       }
     }
@@ -211,22 +230,24 @@ __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void sparse
         }
     }
 
-    // ---- online softmax (one query per lane; halves hold disjoint keys)
+    // ---- online softmax (one query per lane; the two halves hold disjoint keys)
     float mloc = -INFINITY;
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, st[tau][r]);
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m, mloc);
-    const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c);
-    m = m_new;
-    const float mc = m_new * c;
-    lsum *= alpha;
+    mloc = pair_max(mloc);
+    if (__any((mloc - m) * c > kRescaleLog2)) {
+      const float m_new = fmaxf(m, mloc);
+      const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c);
+      m = m_new;
+      lsum *= alpha;
 #pragma unroll
-    for (int i = 0; i < DT; ++i)
+      for (int i = 0; i < DT; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+        for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+    }
+    const float mc = m * c;
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
@@ -241,11 +262,12 @@ __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void sparse
     for (int tau = 0; tau < 2; ++tau) {
 #pragma unroll
       for (int hk = 0; hk < 2; ++hk) {
+        const int G = 2 * tau + hk;
         const bf16x8 pb = pack_bf16x8(st[tau], 8 * hk);
 #pragma unroll
         for (int i = 0; i < DT; ++i) {
-          const bf16x8 a =
-              lds_read16(vt + (32 * i + l32) * L::VS + (32 * tau + 16 * hk + 8 * h2) * 2);
+          const unsigned char* base = vb + G * 16 * T::ROWB;
+          const bf16x8 a = join(lds_read_tr(base + voff[0][i]), lds_read_tr(base + voff[1][i]));
           oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[i], 0, 0, 0);
         }
       }
@@ -253,7 +275,7 @@ __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void sparse
   }
 
   // ---- epilogue: O = O^T / l, bf16, rows < N only
-  const float ltot = lsum + __shfl_xor(lsum, 32);
+  const float ltot = pair_sum(lsum);
   const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
   if (qrow < N) {
     uint16_t* orow = o + head + (size_t)qrow * D;
