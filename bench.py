@@ -116,6 +116,7 @@ def main():
     ws = torch.empty(S.mask_workspace_bytes(B, H, N, d, wl.block_q, wl.block_k),
                      dtype=torch.uint8, device=dev)
     o = torch.empty_like(q)
+    aws = torch.empty(S.attn_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 20
         src = torch.ones(n, dtype=torch.uint8, device=dev)
@@ -132,7 +133,8 @@ def main():
                               workspace=ws, out=(bits, idx, cnt))
         if ev is not None:
             ev[1].record()
-        S.sparge_attn_fwd(q, k, v, idx, cnt, wl.block_q, wl.block_k, wl.scale, out=o)
+        S.sparge_attn_fwd(q, k, v, idx, cnt, wl.block_q, wl.block_k, wl.scale, out=o,
+                          workspace=aws)
         if ev is not None:
             ev[2].record()
 

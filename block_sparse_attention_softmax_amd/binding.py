@@ -19,7 +19,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsparge.s
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP = 0, -1, -2, -3
 
 # every symbol the public header declares
-EXPORTS = ("sparge_mask_workspace_bytes", "sparge_mask_predict", "sparge_attn_fwd",
+EXPORTS = ("sparge_mask_workspace_bytes", "sparge_mask_predict", "sparge_attn_workspace_bytes",
+           "sparge_attn_fwd",
            "sparse_linear_workspace_bytes", "sparse_linear_attn_fwd", "sparge_last_error")
 
 _lib = None
@@ -45,7 +46,9 @@ def lib() -> ctypes.CDLL:
         L.sparge_mask_predict.argtypes = [vp, vp] + [c_int] * 6 + [c_float] * 3 + [vp] * 5 + [
             c_size, vp]
         L.sparge_mask_predict.restype = c_int
-        L.sparge_attn_fwd.argtypes = [vp] * 5 + [c_int] * 6 + [c_float, vp, vp]
+        L.sparge_attn_workspace_bytes.argtypes = [c_int] * 4
+        L.sparge_attn_workspace_bytes.restype = c_size
+        L.sparge_attn_fwd.argtypes = [vp] * 5 + [c_int] * 6 + [c_float, vp, vp, c_size, vp]
         L.sparge_attn_fwd.restype = c_int
         L.sparse_linear_workspace_bytes.argtypes = [c_int] * 4
         L.sparse_linear_workspace_bytes.restype = c_size
@@ -119,14 +122,23 @@ def sparge_mask_predict(q, k, block_q=128, block_k=64, k_frac=0.05, p_mass=0.9, 
     return (bits, idx, cnt, logits) if return_logits else (bits, idx, cnt)
 
 
-def sparge_attn_fwd(q, k, v, kv_idx, kv_cnt, block_q=128, block_k=64, scale=None, out=None):
+def attn_workspace_bytes(B, H, N, d) -> int:
+    return lib().sparge_attn_workspace_bytes(B, H, N, d)
+
+
+def sparge_attn_fwd(q, k, v, kv_idx, kv_cnt, block_q=128, block_k=64, scale=None, out=None,
+                    workspace=None):
     """Block-sparse attention over the key blocks listed in kv_idx/kv_cnt."""
     B, H, N, d = _qkv(q, k, v)
     o = torch.empty_like(q) if out is None else out
     if scale is None:
         scale = default_scale(d)
+    if workspace is None:
+        workspace = torch.empty(max(attn_workspace_bytes(B, H, N, d), 16), dtype=torch.uint8,
+                                device=q.device)
     _check(lib().sparge_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_idx), _ptr(kv_cnt), B, H,
-                                 N, d, block_q, block_k, scale, _ptr(o), _stream(q)))
+                                 N, d, block_q, block_k, scale, _ptr(o), _ptr(workspace),
+                                 workspace.numel(), _stream(q)))
     return o
 
 

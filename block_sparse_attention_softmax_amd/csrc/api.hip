@@ -148,12 +148,26 @@ int sparge_mask_predict(const void* q, const void* k, int B, int H, int N, int d
   return SPARGE_OK;
 }
 
+size_t sparge_attn_workspace_bytes(int B, int H, int N, int d) {
+  const std::string saved = g_last_error;
+  const int rc = check_shape(B, H, N, d, 128, 64);
+  g_last_error = saved;
+  if (rc != SPARGE_OK) return 0;
+  return sparge::attn_workspace_bytes(B, H, N, d);
+}
+
 int sparge_attn_fwd(const void* q, const void* k, const void* v, const int32_t* kv_idx,
                     const int32_t* kv_cnt, int B, int H, int N, int d, int block_q,
-                    int block_k, float scale, void* o, void* stream) {
+                    int block_k, float scale, void* o, void* workspace, size_t workspace_bytes,
+                    void* stream) {
   g_last_error.clear();
   int rc = check_attn_args(q, k, v, kv_idx, kv_cnt, B, H, N, d, block_q, block_k, scale, o);
   if (rc != SPARGE_OK) return rc;
+  if (!workspace) return fail(SPARGE_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned(workspace, 16))
+    return fail(SPARGE_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  if (workspace_bytes < sparge::attn_workspace_bytes(B, H, N, d))
+    return fail(SPARGE_ERR_INVALID_ARG, "workspace too small");
   sparge::AttnLaunch a{};
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -161,6 +175,7 @@ int sparge_attn_fwd(const void* q, const void* k, const void* v, const int32_t* 
   a.idx = kv_idx;
   a.cnt = kv_cnt;
   a.o = static_cast<uint16_t*>(o);
+  a.vt = static_cast<uint16_t*>(workspace);
   a.B = B; a.H = H; a.N = N; a.d = d; a.block_q = block_q;
   a.n_q = ceil_div(N, block_q);
   a.n_k = ceil_div(N, block_k);
@@ -176,7 +191,8 @@ size_t sparse_linear_workspace_bytes(int B, int H, int N, int d) {
   g_last_error = saved;
   if (rc != SPARGE_OK) return 0;
   const size_t BH = (size_t)B * H;
-  return BH * (size_t)d * d * sizeof(float) + BH * (size_t)d * sizeof(float);
+  return sparge::attn_workspace_bytes(B, H, N, d) + BH * (size_t)d * d * sizeof(float) +
+         BH * (size_t)d * sizeof(float);
 }
 
 int sparse_linear_attn_fwd(const void* q, const void* k, const void* v,

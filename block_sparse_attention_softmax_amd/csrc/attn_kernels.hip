@@ -13,12 +13,13 @@
 // the MFMA output layout, so row maxima and sums need only one exchange
 // between the two half-waves, and the rescaling of O uses the lane's own
 // factor. The P^T accumulator registers are fed back as the B operand of the
-// second product unchanged: the key order they imply inside each 16-key step
-// is matched by the order in which V^T is laid out in LDS.
+// second product unchanged; V is pre-packed once per call (vt_pack_kernel)
+// into key-contiguous tiles in the key order those registers imply, so both
+// MFMA A operands are plain 16-byte LDS reads.
 //
-// K_j and V_j are staged in LDS, double-buffered: the global loads of block
-// j+1 are issued before the products of block j and written to the other
-// buffer at the top of the next iteration, so one barrier per block suffices.
+// K_j and packed V_j tiles are copied global -> LDS by direct-to-LDS loads,
+// double-buffered: the copies of block j+1 are issued right after the
+// barrier that opens block j and overlap all of block j's work.
 #include "internal.h"
 
 namespace sparge {
@@ -26,23 +27,69 @@ namespace {
 
 constexpr int BK = 64;
 
-// LDS holds K and V tiles row-major ([64 keys][D] bf16), 16-byte chunks of
-// each row XOR-swizzled with the row index so that the MFMA operand reads
-// below hit distinct banks: chunk c of row r lives at chunk c ^ (r & SWZ).
+// ------------------------------------------------------------- V packing
+// Slot of a key inside its 16-key group in a packed V^T row: slots 8*h + e
+// (h = lane / 32, e = 0..7) hold key 8*(e/4) + 4*h + e%4, the key that
+// register 8*hk + e of an S^T accumulator holds for that lane.
+__device__ __forceinline__ int packed_key(int slot) {
+  const int g = slot >> 4, h = (slot >> 3) & 1, e = slot & 7;
+  return 16 * g + 8 * (e >> 2) + 4 * h + (e & 3);
+}
+
+// vt[bh][j][d][slot] = V[bh][64*j + packed_key(slot)][d], zero past N.
+// grid (n_k, B*H), 256 threads; one 64-key block per workgroup.
+template <int D>
+__global__ __launch_bounds__(256) void vt_pack_kernel(const uint16_t* __restrict__ v,
+                                                      uint16_t* __restrict__ vt, int N,
+                                                      int n_k) {
+  __shared__ uint16_t tile[BK][D + 2];  // +2: odd 32-bit word pitch, conflict-free columns
+  const int j = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+  const uint16_t* src = v + ((size_t)bh * N + (size_t)j * BK) * D;
+  constexpr int CPR = D / 8;
+  for (int c = t; c < BK * CPR; c += 256) {
+    const int row = c / CPR, ch = c % CPR;
+    uint4 w = make_uint4(0, 0, 0, 0);
+    if (j * BK + row < N) w = *reinterpret_cast<const uint4*>(src + (size_t)row * D + ch * 8);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      tile[row][ch * 8 + 2 * e] = (uint16_t)(ws[e] & 0xFFFFu);
+      tile[row][ch * 8 + 2 * e + 1] = (uint16_t)(ws[e] >> 16);
+    }
+  }
+  __syncthreads();
+  uint16_t* dst = vt + ((size_t)bh * n_k + j) * (size_t)D * BK;
+  for (int c = t; c < D * (BK / 8); c += 256) {  // output chunk: row d, slots 8*g8..+8
+    const int d = c / (BK / 8), g8 = c % (BK / 8);
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = (uint32_t)tile[packed_key(8 * g8 + 2 * e)][d] |
+             ((uint32_t)tile[packed_key(8 * g8 + 2 * e + 1)][d] << 16);
+    *reinterpret_cast<uint4*>(dst + (size_t)d * BK + 8 * g8) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// ------------------------------------------------------------ LDS tiles
+// K tile: [64 keys][D] row-major; V tile: packed V^T, [D][64 slots]. The
+// 16-byte chunks of every row are XOR-swizzled with the row index so that
+// the MFMA operand reads (32 rows at one chunk) hit distinct banks: chunk c
+// of row r is stored at chunk c ^ (r mod chunks-per-row).
 template <int D>
 struct Tile {
-  static constexpr int ROWB = D * 2;              // bytes per row
-  static constexpr int CPR = D / 8;               // 16-byte chunks per row
-  static constexpr int SWZ = CPR - 1;             // 15 (D=128) or 7 (D=64)
-  static constexpr int BYTES = BK * ROWB;         // one K or V tile
-  static constexpr int STAGE = 2 * BYTES;         // K + V
-  __device__ static constexpr int off(int row, int chunk) {
-    return row * ROWB + ((chunk ^ (row & SWZ)) << 4);
-  }
+  static constexpr int KROWB = D * 2;   // bytes per K row
+  static constexpr int KCPR = D / 8;    // 16-byte chunks per K row
+  static constexpr int VROWB = BK * 2;  // bytes per V^T row (128)
+  static constexpr int VCPR = BK / 8;   // 8
+  static constexpr int BYTES = BK * D * 2;  // one K or V tile
+  static constexpr int STAGE = 2 * BYTES;   // K + V
+  __device__ static constexpr int kchunk(int row, int chunk) { return chunk ^ (row & (KCPR - 1)); }
+  __device__ static constexpr int vchunk(int row, int chunk) { return chunk ^ (row & (VCPR - 1)); }
 };
 
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+__device__ __forceinline__ bf16x8 lds_read16(const unsigned char* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
 
 // 16-byte global -> LDS copy without a register round trip (global_load_lds
 // dwordx4). `lds` must be the same for the whole wave: lane i's 16 bytes land
@@ -52,26 +99,6 @@ __device__ __forceinline__ void dma16(const void* src, void* lds) {
   __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
 }
 
-__device__ __forceinline__ bf16x8 lds_read16(const unsigned char* p) {
-  return *reinterpret_cast<const bf16x8*>(p);
-}
-
-// Transposing LDS read (gfx950 ds_read_b64_tr_b16). Within each group of 16
-// lanes, lane i receives element (i & 3) of the 4-element rows addressed by
-// lanes 4e + (i >> 2), e = 0..3. When four lanes address the 16 consecutive
-// d-values of one key row and the group covers four key rows, every lane
-// gets the four keys at its own d.
-__device__ __forceinline__ v4i16 lds_read_tr(const unsigned char* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_v4i16*)(reinterpret_cast<uintptr_t>(p)));
-}
-
-__device__ __forceinline__ bf16x8 join(v4i16 lo, v4i16 hi) {
-  typedef short v8i16 __attribute__((ext_vector_type(8)));
-  const v8i16 r = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, r);
-}
-
 __device__ __forceinline__ bf16x8 pack_bf16x8(const floatx16& x, int base) {
   bf16x8 r;
 #pragma unroll
@@ -79,8 +106,8 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(const floatx16& x, int base) {
   return r;
 }
 
-// max over the two half-waves (lane l and lane l ^ 32): the swap returns
-// both values of the pair in its two results
+// max / sum over the two half-waves (lane l and lane l ^ 32): the swap
+// returns both values of the pair in its two results
 __device__ __forceinline__ float pair_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
                                                   false, false);
@@ -92,7 +119,7 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// A kept row's running maximum is only raised (and O rescaled) when a block
+// A row's running maximum is only raised (and O rescaled) when a block
 // raises it by more than 2^8 in the exponent; until then P <= 2^8, which
 // float32 sums and bf16 products carry without loss of relative precision.
 constexpr float kRescaleLog2 = 8.0f;
@@ -100,12 +127,12 @@ constexpr float kRescaleLog2 = 8.0f;
 template <int D, int BQ>
 __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void sparse_attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const int32_t* __restrict__ kv_idx,
+    const uint16_t* __restrict__ vt, const int32_t* __restrict__ kv_idx,
     const int32_t* __restrict__ kv_cnt, uint16_t* __restrict__ o, int N, int n_q,
     int n_k, int total, float c) {
   constexpr int NW = BQ / 32;               // waves, 32 query rows each
   using T = Tile<D>;
-  constexpr int LOADS = BK * T::CPR / 64 / NW;  // 16-byte DMA loads per lane per tile
+  constexpr int LOADS = BK * D / 8 / 64 / NW;  // 16-byte DMA loads per lane per tile
   constexpr int DT = D / 32;                // O^T tiles per wave
   constexpr int KSTEPS = D / 16;            // k-steps of the QK product
 
@@ -130,60 +157,45 @@ __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void sparse
   const int count = min(max(kv_cnt[tile], 0), n_k);
   const int32_t* ids = kv_idx + (size_t)tile * n_k;
   const uint16_t* kh = k + head;
-  const uint16_t* vh = v + head;
+  const uint16_t* vth = vt + (size_t)bh * n_k * D * BK;
 
   // ---- DMA staging: wave w, load u fills LDS chunks [64*(u*NW+w), +64),
   // lane-linear; each lane fetches the global chunk that the swizzle maps
-  // there. Per-lane element offsets within a tile are loop invariant.
-  int src_row[LOADS], src_off[LOADS];
+  // there (the swizzles are involutions). Offsets are loop invariant.
+  int krow[LOADS], ksrc[LOADS], vsrc[LOADS];
 #pragma unroll
   for (int u = 0; u < LOADS; ++u) {
     const int p = 64 * (u * NW + wave) + lane;   // LDS chunk index
-    const int row = p / T::CPR;
-    const int ch = (p % T::CPR) ^ (row & T::SWZ);
-    src_row[u] = row;
-    src_off[u] = row * D + ch * 8;
+    const int kr = p / T::KCPR, vr = p / T::VCPR;
+    krow[u] = kr;
+    ksrc[u] = kr * D + T::kchunk(kr, p % T::KCPR) * 8;
+    vsrc[u] = vr * BK + T::vchunk(vr, p % T::VCPR) * 8;
   }
   auto stage = [&](int j, int buf) {
     unsigned char* kb = smem + buf * T::STAGE;
     unsigned char* vb = kb + T::BYTES;
     const int key0 = j * BK;
     const uint16_t* kt = kh + (size_t)key0 * D;
-    const uint16_t* vt = vh + (size_t)key0 * D;
-    if (key0 + BK <= N) {
+    const uint16_t* vtt = vth + (size_t)j * D * BK;
+    const bool full = key0 + BK <= N;
 #pragma unroll
-      for (int u = 0; u < LOADS; ++u) {
-        const int dst = 1024 * (u * NW + wave);
-        dma16(kt + src_off[u], kb + dst);
-        dma16(vt + src_off[u], vb + dst);
-      }
-    } else {  // short last block: rows past N repeat row N-1 (masked below)
-#pragma unroll
-      for (int u = 0; u < LOADS; ++u) {
-        const int dst = 1024 * (u * NW + wave);
-        const int shift = max(key0 + src_row[u] - (N - 1), 0) * D;
-        dma16(kt + src_off[u] - shift, kb + dst);
-        dma16(vt + src_off[u] - shift, vb + dst);
-      }
+    for (int u = 0; u < LOADS; ++u) {
+      const int dst = 1024 * (u * NW + wave);
+      // short last block: K rows past N repeat row N-1 (their scores are
+      // masked); packed V is zero there
+      const int shift = full ? 0 : max(key0 + krow[u] - (N - 1), 0) * D;
+      dma16(kt + ksrc[u] - shift, kb + dst);
+      dma16(vtt + vsrc[u], vb + dst);
     }
   };
 
   // ---- per-lane LDS read offsets (loop invariant)
   int koff[KSTEPS];  // K rows l32 (+32 tau), chunk 2s + h2
 #pragma unroll
-  for (int s = 0; s < KSTEPS; ++s) koff[s] = T::off(l32, 2 * s + h2);
-  // V^T operand: group of 16 lanes gq, lane li within it; read r covers keys
-  // 16G + 8r + 4*h2 + (li >> 2), d = 32i + 16*(gq & 1) + 4*(li & 3)
-  const int gq = lane >> 4, li = lane & 15;
-  int voff[2][DT];
+  for (int s = 0; s < KSTEPS; ++s) koff[s] = l32 * T::KROWB + (T::kchunk(l32, 2 * s + h2) << 4);
+  int voff[4];       // V^T rows l32 (+32 i), chunk 2G + h2 (slots 16G + 8h2 .. +8)
 #pragma unroll
-  for (int r = 0; r < 2; ++r)
-#pragma unroll
-    for (int i = 0; i < DT; ++i) {
-      const int key = 8 * r + 4 * h2 + (li >> 2);
-      const int d = 32 * i + 16 * (gq & 1) + 4 * (li & 3);
-      voff[r][i] = T::off(key, d >> 3) + (d & 7) * 2;
-    }
+  for (int g = 0; g < 4; ++g) voff[g] = l32 * T::VROWB + (T::vchunk(l32, 2 * g + h2) << 4);
 
   floatx16 oacc[DT];
 #pragma unroll
@@ -198,7 +210,7 @@ __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void sparse
     const int buf = it & 1;
     const int j = min(max(ids[it], 0), n_k - 1);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this lane's DMA for buf landed
-    __syncthreads();                     // all lanes' DMA landed; buf^1 is free
+    __syncthreads();                     // every lane's DMA landed; buf^1 is free
     if (it + 1 < count) stage(min(max(ids[it + 1], 0), n_k - 1), buf ^ 1);
     const unsigned char* kb = smem + buf * T::STAGE;
     const unsigned char* vb = kb + T::BYTES;
@@ -213,7 +225,7 @@ __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void sparse
     for (int s = 0; s < KSTEPS; ++s) {
 #pragma unroll
       for (int tau = 0; tau < 2; ++tau) {
-        const bf16x8 a = lds_read16(kb + tau * 32 * T::ROWB + koff[s]);
+        const bf16x8 a = lds_read16(kb + tau * 32 * T::KROWB + koff[s]);
         st[tau] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], st[tau], 0, 0, 0);
       }
     }
@@ -266,8 +278,7 @@ __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void sparse
         const bf16x8 pb = pack_bf16x8(st[tau], 8 * hk);
 #pragma unroll
         for (int i = 0; i < DT; ++i) {
-          const unsigned char* base = vb + G * 16 * T::ROWB;
-          const bf16x8 a = join(lds_read_tr(base + voff[0][i]), lds_read_tr(base + voff[1][i]));
+          const bf16x8 a = lds_read16(vb + i * 32 * T::VROWB + voff[G]);
           oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[i], 0, 0, 0);
         }
       }
@@ -298,12 +309,19 @@ template <int D, int BQ>
 hipError_t launch_sparse(const AttnLaunch& a, hipStream_t s) {
   const int total = a.B * a.H * a.n_q;
   const float c = a.scale * 1.4426950408889634f;  // scale * log2(e)
+  hipLaunchKernelGGL((vt_pack_kernel<D>), dim3(a.n_k, a.B * a.H), dim3(256), 0, s, a.v, a.vt,
+                     a.N, a.n_k);
   hipLaunchKernelGGL((sparse_attn_fwd_kernel<D, BQ>), dim3(total), dim3(BQ * 2), 0, s, a.q,
-                     a.k, a.v, a.idx, a.cnt, a.o, a.N, a.n_q, a.n_k, total, c);
+                     a.k, a.vt, a.idx, a.cnt, a.o, a.N, a.n_q, a.n_k, total, c);
   return hipGetLastError();
 }
 
 }  // namespace
+
+size_t attn_workspace_bytes(int B, int H, int N, int d) {
+  const size_t n_k = (N + BK - 1) / BK;
+  return (size_t)B * H * n_k * BK * d * sizeof(uint16_t);
+}
 
 hipError_t launch_attn(const AttnLaunch& a, hipStream_t s) {
   if (a.d == 128 && a.block_q == 128) return launch_sparse<128, 128>(a, s);

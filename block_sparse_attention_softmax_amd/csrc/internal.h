@@ -60,6 +60,7 @@ struct AttnLaunch {
   const int32_t* idx;
   const int32_t* cnt;
   uint16_t* o;
+  uint16_t* vt;  // workspace: V packed key-contiguous per block, [B*H, n_k, d, 64]
   int B, H, N, d, block_q, n_q, n_k;
   float scale;
   // linear branch (null alpha = plain sparse attention)
@@ -68,5 +69,6 @@ struct AttnLaunch {
   float* lin_z;  // [B*H, d]     sum_u phi(K_u)
 };
 hipError_t launch_attn(const AttnLaunch& a, hipStream_t s);
+size_t attn_workspace_bytes(int B, int H, int N, int d);  // packed V
 
 }  // namespace sparge

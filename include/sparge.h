@@ -93,6 +93,11 @@ int sparge_mask_predict(const void* q, const void* k, int B, int H, int N, int d
                         int32_t* kv_cnt, double* block_logits, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/* Device workspace (bytes) that sparge_attn_fwd needs: V re-packed per
+ * 64-key block into key-contiguous rows (bf16, B*H*ceil(N/64)*64*d values).
+ * Returns 0 for arguments that sparge_attn_fwd would reject. */
+size_t sparge_attn_workspace_bytes(int B, int H, int N, int d);
+
 /* Block-sparse attention forward (SpargeAttention2 page, section 2C): for
  * every query t of query block i,
  *   O_t = sum_u softmax_u(scale * <Q_t, K_u>) V_u
@@ -102,24 +107,27 @@ int sparge_mask_predict(const void* q, const void* k, int B, int H, int N, int d
  * accumulation; the softmax runs online in float32; O is rounded to bf16
  * (nearest even).
  *
- *  q, k, v : bf16 [B, H, N, d], device, 16-byte aligned.
- *  kv_idx  : int32 [B, H, n_q, n_k]; first kv_cnt entries of each row are
- *            key block indices in [0, n_k). Any such list is accepted (for
- *            example the output of sparge_mask_predict, or a fixed local
- *            window). Counts are clamped to [0, n_k] and indices to
- *            [0, n_k - 1], so a corrupt list cannot read out of bounds.
- *  kv_cnt  : int32 [B, H, n_q].
- *  o       : out bf16 [B, H, N, d], device, 16-byte aligned; must not
- *            overlap the inputs.
+ *  q, k, v   : bf16 [B, H, N, d], device, 16-byte aligned.
+ *  kv_idx    : int32 [B, H, n_q, n_k]; first kv_cnt entries of each row are
+ *              key block indices in [0, n_k). Any such list is accepted (for
+ *              example the output of sparge_mask_predict, or a fixed local
+ *              window). Counts are clamped to [0, n_k] and indices to
+ *              [0, n_k - 1], so a corrupt list cannot read out of bounds.
+ *  kv_cnt    : int32 [B, H, n_q].
+ *  o         : out bf16 [B, H, N, d], device, 16-byte aligned; must not
+ *              overlap the inputs.
+ *  workspace : device scratch of at least sparge_attn_workspace_bytes(),
+ *              16-byte aligned; contents on entry do not matter.
  */
 int sparge_attn_fwd(const void* q, const void* k, const void* v,
                     const int32_t* kv_idx, const int32_t* kv_cnt, int B, int H,
                     int N, int d, int block_q, int block_k, float scale, void* o,
-                    void* stream);
+                    void* workspace, size_t workspace_bytes, void* stream);
 
-/* Device workspace (bytes) of sparse_linear_attn_fwd: per (b, h) the float32
- * summaries sum_u phi(K_u)^T V_u (d x d) and sum_u phi(K_u) (d). Returns 0
- * for arguments that sparse_linear_attn_fwd would reject. */
+/* Device workspace (bytes) of sparse_linear_attn_fwd: the packed V of
+ * sparge_attn_fwd plus, per (b, h), the float32 summaries
+ * sum_u phi(K_u)^T V_u (d x d) and sum_u phi(K_u) (d). Returns 0 for
+ * arguments that sparse_linear_attn_fwd would reject. */
 size_t sparse_linear_workspace_bytes(int B, int H, int N, int d);
 
 /* Sparse attention plus a linear-attention branch over the dropped blocks

@@ -42,7 +42,10 @@ def test_mask_workspace_bytes():
     assert L.sparge_mask_workspace_bytes(B, H, N, d, 128, 64) == want
     assert L.sparge_mask_workspace_bytes(1, 1, 100, 96, 128, 64) == 0       # bad d
     assert L.sparge_mask_workspace_bytes(1, 1, 64 * 4097, 64, 64, 64) == 0  # > 4096 blocks
-    assert L.sparse_linear_workspace_bytes(1, 40, 75600, 128) == 40 * (128 * 128 + 128) * 4
+    packed_v = 40 * math.ceil(75600 / 64) * 64 * 128 * 2
+    assert L.sparge_attn_workspace_bytes(1, 40, 75600, 128) == packed_v
+    assert L.sparge_attn_workspace_bytes(1, 40, 75600, 96) == 0
+    assert L.sparse_linear_workspace_bytes(1, 40, 75600, 128) == packed_v + 40 * (128 * 128 + 128) * 4
 
 
 def _mask(**kw):
@@ -55,7 +58,7 @@ def _mask(**kw):
 
 def _attn(**kw):
     args = dict(q=A, k=A, v=A, idx=A, cnt=A, B=1, H=2, N=1024, d=64, bq=64, bk=64, sc=0.125,
-                o=A, st=None)
+                o=A, ws=A, wsb=1 << 30, st=None)
     args.update(kw)
     return binding.lib().sparge_attn_fwd(*args.values())
 
@@ -87,6 +90,7 @@ def test_mask_rejects_bad_arguments(kw, code):
     (dict(q=None), -1), (dict(o=None), -1), (dict(cnt=None), -1), (dict(v=MIS), -1),
     (dict(d=80), -2), (dict(bq=256), -2), (dict(bk=32), -2), (dict(N=0), -1),
     (dict(sc=-1.0), -1), (dict(sc=float("inf")), -1),
+    (dict(ws=None), -1), (dict(ws=MIS), -1), (dict(wsb=1024 * 64 * 2 * 2 - 1), -1),
 ])
 def test_attn_rejects_bad_arguments(kw, code):
     assert _attn(**kw) == code
