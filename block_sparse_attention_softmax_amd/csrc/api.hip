@@ -190,9 +190,7 @@ size_t sparse_linear_workspace_bytes(int B, int H, int N, int d) {
   const int rc = check_shape(B, H, N, d, 128, 64);
   g_last_error = saved;
   if (rc != SPARGE_OK) return 0;
-  const size_t BH = (size_t)B * H;
-  return sparge::attn_workspace_bytes(B, H, N, d) + BH * (size_t)d * d * sizeof(float) +
-         BH * (size_t)d * sizeof(float);
+  return sparge::linear_workspace_bytes(B, H, N, d);
 }
 
 int sparse_linear_attn_fwd(const void* q, const void* k, const void* v,
@@ -205,9 +203,34 @@ int sparse_linear_attn_fwd(const void* q, const void* k, const void* v,
   if (!alpha || !workspace) return fail(SPARGE_ERR_INVALID_ARG, "null pointer argument");
   if (!aligned(alpha, 4) || !aligned(workspace, 16))
     return fail(SPARGE_ERR_INVALID_ARG, "alpha / workspace misaligned");
-  if (workspace_bytes < sparse_linear_workspace_bytes(B, H, N, d))
+  if (workspace_bytes < sparge::linear_workspace_bytes(B, H, N, d))
     return fail(SPARGE_ERR_INVALID_ARG, "workspace too small");
-  return fail(SPARGE_ERR_UNSUPPORTED, "linear branch not built yet");
+  if (block_q != d)
+    return fail(SPARGE_ERR_UNSUPPORTED, "the linear branch is built for block_q == d (64 or 128)");
+  sparge::AttnLaunch a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.idx = kv_idx;
+  a.cnt = kv_cnt;
+  a.o = static_cast<uint16_t*>(o);
+  a.B = B; a.H = H; a.N = N; a.d = d; a.block_q = block_q;
+  a.n_q = ceil_div(N, block_q);
+  a.n_k = ceil_div(N, block_k);
+  a.scale = scale;
+  a.alpha = alpha;
+  const size_t BH = (size_t)B * H, packed = sparge::attn_workspace_bytes(B, H, N, d);
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  a.vt = reinterpret_cast<uint16_t*>(ws);
+  a.phikt = reinterpret_cast<uint16_t*>(ws + packed);
+  float* f = reinterpret_cast<float*>(ws + 2 * packed);
+  a.lin_h = f;
+  a.lin_z = a.lin_h + BH * d * d;
+  a.part_h = a.lin_z + BH * d;
+  a.part_z = a.part_h + BH * sparge::kLinSplit * d * d;
+  const hipError_t e = sparge::launch_attn(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "sparse_linear_attn_fwd launch");
+  return SPARGE_OK;
 }
 
 }  // extern "C"

@@ -36,37 +36,56 @@ __device__ __forceinline__ int packed_key(int slot) {
   return 16 * g + 8 * (e >> 2) + 4 * h + (e & 3);
 }
 
-// vt[bh][j][d][slot] = V[bh][64*j + packed_key(slot)][d], zero past N.
+// phi(x) = elu(x) + 1, the feature map of the linear branch
+__device__ __forceinline__ float elu1(float x) { return x > 0.0f ? x + 1.0f : expf(x); }
+
+// vt[bh][j][d][slot] = V[bh][64*j + packed_key(slot)][d], zero past N; with
+// LIN also phikt[...] = bf16(phi(K[...])) in the same layout.
 // grid (n_k, B*H), 256 threads; one 64-key block per workgroup.
-template <int D>
-__global__ __launch_bounds__(256) void vt_pack_kernel(const uint16_t* __restrict__ v,
-                                                      uint16_t* __restrict__ vt, int N,
-                                                      int n_k) {
-  __shared__ uint16_t tile[BK][D + 2];  // +2: odd 32-bit word pitch, conflict-free columns
+template <int D, bool LIN>
+__global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ v,
+                                                   const uint16_t* __restrict__ k,
+                                                   uint16_t* __restrict__ vt,
+                                                   uint16_t* __restrict__ phikt, int N,
+                                                   int n_k) {
+  constexpr int NT = LIN ? 2 : 1;
+  // +2: odd 32-bit word pitch, so the column reads below are conflict-free
+  __shared__ uint16_t tile[NT][BK][D + 2];
   const int j = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
-  const uint16_t* src = v + ((size_t)bh * N + (size_t)j * BK) * D;
   constexpr int CPR = D / 8;
-  for (int c = t; c < BK * CPR; c += 256) {
-    const int row = c / CPR, ch = c % CPR;
-    uint4 w = make_uint4(0, 0, 0, 0);
-    if (j * BK + row < N) w = *reinterpret_cast<const uint4*>(src + (size_t)row * D + ch * 8);
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      tile[row][ch * 8 + 2 * e] = (uint16_t)(ws[e] & 0xFFFFu);
-      tile[row][ch * 8 + 2 * e + 1] = (uint16_t)(ws[e] >> 16);
+  for (int w = 0; w < NT; ++w) {
+    const uint16_t* src = (w == 0 ? v : k) + ((size_t)bh * N + (size_t)j * BK) * D;
+    for (int c = t; c < BK * CPR; c += 256) {
+      const int row = c / CPR, ch = c % CPR;
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (j * BK + row < N) x = *reinterpret_cast<const uint4*>(src + (size_t)row * D + ch * 8);
+      const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        uint16_t lo = (uint16_t)(xs[e] & 0xFFFFu), hi = (uint16_t)(xs[e] >> 16);
+        if (w == 1 && j * BK + row < N) {
+          lo = (uint16_t)f32_to_bf16_rne(elu1(bf16_lo(xs[e])));
+          hi = (uint16_t)f32_to_bf16_rne(elu1(bf16_hi(xs[e])));
+        }
+        tile[w][row][ch * 8 + 2 * e] = lo;
+        tile[w][row][ch * 8 + 2 * e + 1] = hi;
+      }
     }
   }
   __syncthreads();
-  uint16_t* dst = vt + ((size_t)bh * n_k + j) * (size_t)D * BK;
-  for (int c = t; c < D * (BK / 8); c += 256) {  // output chunk: row d, slots 8*g8..+8
-    const int d = c / (BK / 8), g8 = c % (BK / 8);
-    uint32_t w[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      w[e] = (uint32_t)tile[packed_key(8 * g8 + 2 * e)][d] |
-             ((uint32_t)tile[packed_key(8 * g8 + 2 * e + 1)][d] << 16);
-    *reinterpret_cast<uint4*>(dst + (size_t)d * BK + 8 * g8) = make_uint4(w[0], w[1], w[2], w[3]);
+  for (int w = 0; w < NT; ++w) {
+    uint16_t* dst = (w == 0 ? vt : phikt) + ((size_t)bh * n_k + j) * (size_t)D * BK;
+    for (int c = t; c < D * (BK / 8); c += 256) {  // output chunk: row d, slots 8*g8..+8
+      const int d = c / (BK / 8), g8 = c % (BK / 8);
+      uint32_t x[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        x[e] = (uint32_t)tile[w][packed_key(8 * g8 + 2 * e)][d] |
+               ((uint32_t)tile[w][packed_key(8 * g8 + 2 * e + 1)][d] << 16);
+      *reinterpret_cast<uint4*>(dst + (size_t)d * BK + 8 * g8) = make_uint4(x[0], x[1], x[2], x[3]);
+    }
   }
 }
 
@@ -75,14 +94,14 @@ __global__ __launch_bounds__(256) void vt_pack_kernel(const uint16_t* __restrict
 // 16-byte chunks of every row are XOR-swizzled with the row index so that
 // the MFMA operand reads (32 rows at one chunk) hit distinct banks: chunk c
 // of row r is stored at chunk c ^ (r mod chunks-per-row).
-template <int D>
+template <int D, bool LIN>
 struct Tile {
+  static constexpr int STAGE = (LIN ? 3 : 2) * BK * D * 2;  // K + V^T (+ phi(K)^T)
   static constexpr int KROWB = D * 2;   // bytes per K row
   static constexpr int KCPR = D / 8;    // 16-byte chunks per K row
   static constexpr int VROWB = BK * 2;  // bytes per V^T row (128)
   static constexpr int VCPR = BK / 8;   // 8
-  static constexpr int BYTES = BK * D * 2;  // one K or V tile
-  static constexpr int STAGE = 2 * BYTES;   // K + V
+  static constexpr int BYTES = BK * D * 2;  // one K, V^T or phi(K)^T tile
   __device__ static constexpr int kchunk(int row, int chunk) { return chunk ^ (row & (KCPR - 1)); }
   __device__ static constexpr int vchunk(int row, int chunk) { return chunk ^ (row & (VCPR - 1)); }
 };
@@ -124,17 +143,97 @@ __device__ __forceinline__ float pair_sum(float x) {
 // float32 sums and bf16 products carry without loss of relative precision.
 constexpr float kRescaleLog2 = 8.0f;
 
-template <int D, int BQ>
-__global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void sparse_attn_fwd_kernel(
+// ------------------------------------------------- linear-branch totals
+// Split-K partials of H_tot = sum_u phi(K_u)^T V_u (d x d, row = phi index)
+// and z_tot = sum_u phi(K_u) from the packed tiles: workgroup (split, bh)
+// covers blocks j = split, split + kLinSplit, ...; D/32 waves, wave w owns
+// rows 32w..32w+31. Operands come straight from the packed global tiles.
+template <int D>
+__global__ __launch_bounds__(D * 2) void linear_total_kernel(const uint16_t* __restrict__ phikt,
+                                                             const uint16_t* __restrict__ vt,
+                                                             float* __restrict__ part_h,
+                                                             float* __restrict__ part_z,
+                                                             int n_k) {
+  constexpr int DT = D / 32;
+  const int split = blockIdx.x, bh = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h2 = lane >> 5, l32 = lane & 31;
+  floatx16 hacc[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) hacc[i][r] = 0.0f;
+  float zp = 0.0f;
+  const size_t tile = (size_t)D * BK;
+  for (int j = split; j < n_k; j += kLinSplit) {
+    const uint16_t* pk = phikt + ((size_t)bh * n_k + j) * tile + (size_t)(32 * wave + l32) * BK;
+    const uint16_t* vv = vt + ((size_t)bh * n_k + j) * tile + (size_t)l32 * BK;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(pk + 16 * g + 8 * h2);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) zp += (float)a[e];
+#pragma unroll
+      for (int i = 0; i < DT; ++i) {
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(vv + (size_t)32 * i * BK + 16 * g + 8 * h2);
+        hacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, hacc[i], 0, 0, 0);
+      }
+    }
+  }
+  float* ph = part_h + ((size_t)bh * kLinSplit + split) * D * D;
+#pragma unroll
+  for (int i = 0; i < DT; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int a = 32 * wave + 8 * (r >> 2) + 4 * h2 + (r & 3);
+      ph[(size_t)a * D + 32 * i + l32] = hacc[i][r];
+    }
+  zp += __shfl_xor(zp, 32);
+  if (h2 == 0) part_z[((size_t)bh * kLinSplit + split) * D + 32 * wave + l32] = zp;
+}
+
+// H_tot, z_tot = sums of the kLinSplit partials, in split order.
+template <int D>
+__global__ __launch_bounds__(256) void linear_reduce_kernel(const float* __restrict__ part_h,
+                                                            const float* __restrict__ part_z,
+                                                            float* __restrict__ lin_h,
+                                                            float* __restrict__ lin_z) {
+  const int bh = blockIdx.x;
+  for (int e = threadIdx.x; e < D * D + D; e += 256) {
+    float acc = 0.0f;
+    if (e < D * D) {
+      for (int sp = 0; sp < kLinSplit; ++sp) acc += part_h[((size_t)bh * kLinSplit + sp) * D * D + e];
+      lin_h[(size_t)bh * D * D + e] = acc;
+    } else {
+      const int a = e - D * D;
+      for (int sp = 0; sp < kLinSplit; ++sp) acc += part_z[((size_t)bh * kLinSplit + sp) * D + a];
+      lin_z[(size_t)bh * D + a] = acc;
+    }
+  }
+}
+
+// ------------------------------------------------------ attention kernel
+// LIN adds the linear branch over the dropped blocks: each kept block also
+// accumulates H_kept += phi(K_j)^T V_j (wave w owns rows 32w..32w+31 of the
+// d x d product, reusing the V^T fragments of the PV product as its B
+// operand) and z_kept += sum phi(K_j); the epilogue forms H_D = H_tot -
+// H_kept, z_D = z_tot - z_kept and O_l = phi(Q) H_D / (phi(Q) . z_D) with a
+// three-term split-bf16 MFMA product (about 16 significant bits per
+// operand), and writes O = O_s + alpha[h] * O_l.
+template <int D, int BQ, bool LIN>
+__global__ __launch_bounds__(BQ * 2, (LIN || (D == 128 && BQ == 64)) ? 1 : 2) void sparse_attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ vt, const int32_t* __restrict__ kv_idx,
-    const int32_t* __restrict__ kv_cnt, uint16_t* __restrict__ o, int N, int n_q,
-    int n_k, int total, float c) {
+    const int32_t* __restrict__ kv_cnt, uint16_t* __restrict__ o, int H, int N, int n_q,
+    int n_k, int total, float c, const float* __restrict__ alpha,
+    const uint16_t* __restrict__ phikt, const float* __restrict__ lin_h,
+    const float* __restrict__ lin_z) {
   constexpr int NW = BQ / 32;               // waves, 32 query rows each
-  using T = Tile<D>;
+  using T = Tile<D, LIN>;
   constexpr int LOADS = BK * D / 8 / 64 / NW;  // 16-byte DMA loads per lane per tile
   constexpr int DT = D / 32;                // O^T tiles per wave
   constexpr int KSTEPS = D / 16;            // k-steps of the QK product
+  static_assert(!LIN || NW == DT, "the linear branch needs one wave per 32 rows of d");
 
   __shared__ __align__(16) unsigned char smem[2 * T::STAGE];
 
@@ -157,7 +256,9 @@ __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void sparse
   const int count = min(max(kv_cnt[tile], 0), n_k);
   const int32_t* ids = kv_idx + (size_t)tile * n_k;
   const uint16_t* kh = k + head;
-  const uint16_t* vth = vt + (size_t)bh * n_k * D * BK;
+  const size_t vtile = (size_t)D * BK;
+  const uint16_t* vth = vt + (size_t)bh * n_k * vtile;
+  const uint16_t* pkh = LIN ? phikt + (size_t)bh * n_k * vtile : nullptr;
 
   // ---- DMA staging: wave w, load u fills LDS chunks [64*(u*NW+w), +64),
   // lane-linear; each lane fetches the global chunk that the swizzle maps
@@ -176,16 +277,17 @@ __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void sparse
     unsigned char* vb = kb + T::BYTES;
     const int key0 = j * BK;
     const uint16_t* kt = kh + (size_t)key0 * D;
-    const uint16_t* vtt = vth + (size_t)j * D * BK;
+    const uint16_t* vtt = vth + (size_t)j * vtile;
     const bool full = key0 + BK <= N;
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
       const int dst = 1024 * (u * NW + wave);
       // short last block: K rows past N repeat row N-1 (their scores are
-      // masked); packed V is zero there
+      // masked); the packed tiles are zero there
       const int shift = full ? 0 : max(key0 + krow[u] - (N - 1), 0) * D;
       dma16(kt + ksrc[u] - shift, kb + dst);
       dma16(vtt + vsrc[u], vb + dst);
+      if constexpr (LIN) dma16(pkh + (size_t)j * vtile + vsrc[u], vb + T::BYTES + dst);
     }
   };
 
@@ -198,11 +300,18 @@ __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void sparse
   for (int g = 0; g < 4; ++g) voff[g] = l32 * T::VROWB + (T::vchunk(l32, 2 * g + h2) << 4);
 
   floatx16 oacc[DT];
+  floatx16 hacc[LIN ? DT : 1];
 #pragma unroll
   for (int i = 0; i < DT; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[i][r] = 0.0f;
-  float m = -INFINITY, lsum = 0.0f;
+  if constexpr (LIN) {
+#pragma unroll
+    for (int i = 0; i < DT; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) hacc[i][r] = 0.0f;
+  }
+  float m = -INFINITY, lsum = 0.0f, zk = 0.0f;
 
   if (count > 0) stage(min(max(ids[0], 0), n_k - 1), 0);
 
@@ -251,13 +360,13 @@ __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void sparse
     mloc = pair_max(mloc);
     if (__any((mloc - m) * c > kRescaleLog2)) {
       const float m_new = fmaxf(m, mloc);
-      const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c);
+      const float alpha_r = __builtin_amdgcn_exp2f((m - m_new) * c);
       m = m_new;
-      lsum *= alpha;
+      lsum *= alpha_r;
 #pragma unroll
       for (int i = 0; i < DT; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+        for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha_r;
     }
     const float mc = m * c;
 #pragma unroll
@@ -269,25 +378,99 @@ __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void sparse
         lsum += pr;
       }
 
-    // ---- O^T += V_j^T P^T : 4 k-steps of 16 keys
+    // ---- O^T += V_j^T P^T : 4 k-steps of 16 keys (LIN: H_kept += phi(K_j)^T V_j)
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
 #pragma unroll
       for (int hk = 0; hk < 2; ++hk) {
         const int G = 2 * tau + hk;
         const bf16x8 pb = pack_bf16x8(st[tau], 8 * hk);
+        bf16x8 pkf;
+        if constexpr (LIN) {
+          pkf = lds_read16(vb + T::BYTES + wave * 32 * T::VROWB + voff[G]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) zk += (float)pkf[e];
+        }
 #pragma unroll
         for (int i = 0; i < DT; ++i) {
           const bf16x8 a = lds_read16(vb + i * 32 * T::VROWB + voff[G]);
           oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[i], 0, 0, 0);
+          if constexpr (LIN)
+            hacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pkf, a, hacc[i], 0, 0, 0);
         }
       }
     }
   }
 
-  // ---- epilogue: O = O^T / l, bf16, rows < N only
+  // ---- epilogue: O = O^T / l (+ alpha * O_l), bf16, rows < N only
   const float ltot = pair_sum(lsum);
   const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
+  float lin_scale = 0.0f;  // alpha[h] / (phi(Q_t) . z_D), 0 when nothing was dropped
+  if constexpr (LIN) {
+    // the staging buffers become H_D^T [D][D+4] fp32 and z_D [D]
+    constexpr int HP = D + 4;
+    float* ht = reinterpret_cast<float*>(smem);
+    float* zd = ht + D * HP;
+    static_assert(D * HP * 4 + D * 4 <= 2 * T::STAGE, "H_D must fit the staging buffers");
+    const bool dropped = count < n_k;  // D_i is empty when every block is kept
+    zk = pair_sum(zk);
+    __syncthreads();                   // every wave is done with the staging buffers
+    if (dropped) {
+      const float* Ht = lin_h + (size_t)bh * D * D;
+#pragma unroll
+      for (int i = 0; i < DT; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int a0 = 32 * wave + 8 * g + 4 * h2, b = 32 * i + l32;
+          float4 x;
+          x.x = Ht[(size_t)(a0 + 0) * D + b] - hacc[i][4 * g + 0];
+          x.y = Ht[(size_t)(a0 + 1) * D + b] - hacc[i][4 * g + 1];
+          x.z = Ht[(size_t)(a0 + 2) * D + b] - hacc[i][4 * g + 2];
+          x.w = Ht[(size_t)(a0 + 3) * D + b] - hacc[i][4 * g + 3];
+          *reinterpret_cast<float4*>(ht + b * HP + a0) = x;
+        }
+      if (h2 == 0) zd[32 * wave + l32] = lin_z[(size_t)bh * D + 32 * wave + l32] - zk;
+    }
+    __syncthreads();
+    if (dropped) {
+      // O_l^T (d x 32 queries) = H_D^T phi(Q)^T; phi(Q) in the qf layout
+      floatx16* lacc = hacc;
+#pragma unroll
+      for (int i = 0; i < DT; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) lacc[i][r] = 0.0f;
+      float den = 0.0f;
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) {
+        bf16x8 qhi, qlo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float fq = elu1((float)qf[s][e]);
+          den = fmaf(fq, zd[16 * s + 8 * h2 + e], den);
+          qhi[e] = (__bf16)fq;
+          qlo[e] = (__bf16)(fq - (float)qhi[e]);
+        }
+#pragma unroll
+        for (int i = 0; i < DT; ++i) {
+          const float* hp = ht + (32 * i + l32) * HP + 16 * s + 8 * h2;
+          const float4 h0 = *reinterpret_cast<const float4*>(hp);
+          const float4 h1 = *reinterpret_cast<const float4*>(hp + 4);
+          const float hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+          bf16x8 hhi, hlo;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            hhi[e] = (__bf16)hv[e];
+            hlo[e] = (__bf16)(hv[e] - (float)hhi[e]);
+          }
+          lacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hhi, qhi, lacc[i], 0, 0, 0);
+          lacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hhi, qlo, lacc[i], 0, 0, 0);
+          lacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hlo, qhi, lacc[i], 0, 0, 0);
+        }
+      }
+      den = pair_sum(den);
+      lin_scale = den > 0.0f ? alpha[bh % H] / den : 0.0f;
+    }
+  }
   if (qrow < N) {
     uint16_t* orow = o + head + (size_t)qrow * D;
 #pragma unroll
@@ -295,24 +478,36 @@ __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void sparse
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = 32 * i + 8 * g + 4 * h2;
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          y[e] = oacc[i][4 * g + e] * inv;
+          if constexpr (LIN) y[e] = fmaf(hacc[i][4 * g + e], lin_scale, y[e]);
+        }
         uint2 pk;
-        pk.x = f32_to_bf16_rne(oacc[i][4 * g] * inv) |
-               (f32_to_bf16_rne(oacc[i][4 * g + 1] * inv) << 16);
-        pk.y = f32_to_bf16_rne(oacc[i][4 * g + 2] * inv) |
-               (f32_to_bf16_rne(oacc[i][4 * g + 3] * inv) << 16);
+        pk.x = f32_to_bf16_rne(y[0]) | (f32_to_bf16_rne(y[1]) << 16);
+        pk.y = f32_to_bf16_rne(y[2]) | (f32_to_bf16_rne(y[3]) << 16);
         *reinterpret_cast<uint2*>(orow + d0) = pk;
       }
   }
 }
 
-template <int D, int BQ>
+template <int D, int BQ, bool LIN>
 hipError_t launch_sparse(const AttnLaunch& a, hipStream_t s) {
   const int total = a.B * a.H * a.n_q;
   const float c = a.scale * 1.4426950408889634f;  // scale * log2(e)
-  hipLaunchKernelGGL((vt_pack_kernel<D>), dim3(a.n_k, a.B * a.H), dim3(256), 0, s, a.v, a.vt,
-                     a.N, a.n_k);
-  hipLaunchKernelGGL((sparse_attn_fwd_kernel<D, BQ>), dim3(total), dim3(BQ * 2), 0, s, a.q,
-                     a.k, a.vt, a.idx, a.cnt, a.o, a.N, a.n_q, a.n_k, total, c);
+  const int BH = a.B * a.H;
+  hipLaunchKernelGGL((pack_kernel<D, LIN>), dim3(a.n_k, BH), dim3(256), 0, s, a.v, a.k, a.vt,
+                     a.phikt, a.N, a.n_k);
+  if constexpr (LIN) {
+    hipLaunchKernelGGL((linear_total_kernel<D>), dim3(kLinSplit, BH), dim3(D * 2), 0, s,
+                       a.phikt, a.vt, a.part_h, a.part_z, a.n_k);
+    hipLaunchKernelGGL((linear_reduce_kernel<D>), dim3(BH), dim3(256), 0, s, a.part_h,
+                       a.part_z, a.lin_h, a.lin_z);
+  }
+  hipLaunchKernelGGL((sparse_attn_fwd_kernel<D, BQ, LIN>), dim3(total), dim3(BQ * 2), 0, s,
+                     a.q, a.k, a.vt, a.idx, a.cnt, a.o, a.H, a.N, a.n_q, a.n_k, total, c,
+                     a.alpha, a.phikt, a.lin_h, a.lin_z);
   return hipGetLastError();
 }
 
@@ -323,11 +518,21 @@ size_t attn_workspace_bytes(int B, int H, int N, int d) {
   return (size_t)B * H * n_k * BK * d * sizeof(uint16_t);
 }
 
+size_t linear_workspace_bytes(int B, int H, int N, int d) {
+  const size_t BH = (size_t)B * H;
+  return 2 * attn_workspace_bytes(B, H, N, d) +                // packed V, packed phi(K)
+         BH * ((size_t)d * d + d) * (1 + kLinSplit) * sizeof(float);  // totals + partials
+}
+
 hipError_t launch_attn(const AttnLaunch& a, hipStream_t s) {
-  if (a.d == 128 && a.block_q == 128) return launch_sparse<128, 128>(a, s);
-  if (a.d == 128 && a.block_q == 64) return launch_sparse<128, 64>(a, s);
-  if (a.d == 64 && a.block_q == 128) return launch_sparse<64, 128>(a, s);
-  return launch_sparse<64, 64>(a, s);
+  if (a.alpha) {
+    if (a.d == 128) return launch_sparse<128, 128, true>(a, s);
+    return launch_sparse<64, 64, true>(a, s);
+  }
+  if (a.d == 128 && a.block_q == 128) return launch_sparse<128, 128, false>(a, s);
+  if (a.d == 128 && a.block_q == 64) return launch_sparse<128, 64, false>(a, s);
+  if (a.d == 64 && a.block_q == 128) return launch_sparse<64, 128, false>(a, s);
+  return launch_sparse<64, 64, false>(a, s);
 }
 
 }  // namespace sparge

@@ -60,15 +60,21 @@ struct AttnLaunch {
   const int32_t* idx;
   const int32_t* cnt;
   uint16_t* o;
-  uint16_t* vt;  // workspace: V packed key-contiguous per block, [B*H, n_k, d, 64]
   int B, H, N, d, block_q, n_q, n_k;
   float scale;
-  // linear branch (null alpha = plain sparse attention)
-  const float* alpha;
-  float* lin_h;  // [B*H, d, d]  sum_u phi(K_u)^T V_u
-  float* lin_z;  // [B*H, d]     sum_u phi(K_u)
+  // workspace: V packed key-contiguous per block, [B*H, n_k, d, 64]
+  uint16_t* vt;
+  // linear branch (alpha == nullptr: plain sparse attention)
+  const float* alpha;  // [H]
+  uint16_t* phikt;     // phi(K) packed like vt, bf16
+  float* lin_h;        // [B*H, d, d]  sum_u phi(K_u)^T V_u  (row = phi(K) index)
+  float* lin_z;        // [B*H, d]     sum_u phi(K_u)
+  float* part_h;       // [B*H, kLinSplit, d, d] split-K partials of lin_h
+  float* part_z;       // [B*H, kLinSplit, d]
 };
+constexpr int kLinSplit = 16;
 hipError_t launch_attn(const AttnLaunch& a, hipStream_t s);
-size_t attn_workspace_bytes(int B, int H, int N, int d);  // packed V
+size_t attn_workspace_bytes(int B, int H, int N, int d);    // packed V
+size_t linear_workspace_bytes(int B, int H, int N, int d);  // packed V + linear branch
 
 }  // namespace sparge

@@ -125,9 +125,10 @@ int sparge_attn_fwd(const void* q, const void* k, const void* v,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* Device workspace (bytes) of sparse_linear_attn_fwd: the packed V of
- * sparge_attn_fwd plus, per (b, h), the float32 summaries
- * sum_u phi(K_u)^T V_u (d x d) and sum_u phi(K_u) (d). Returns 0 for
- * arguments that sparse_linear_attn_fwd would reject. */
+ * sparge_attn_fwd, phi(K) packed the same way, and per (b, h) the float32
+ * summaries sum_u phi(K_u)^T V_u (d x d) and sum_u phi(K_u) (d) with 16
+ * split-K partials of each. Returns 0 for arguments that
+ * sparse_linear_attn_fwd would reject. */
 size_t sparse_linear_workspace_bytes(int B, int H, int N, int d);
 
 /* Sparse attention plus a linear-attention branch over the dropped blocks
@@ -138,8 +139,11 @@ size_t sparse_linear_workspace_bytes(int B, int H, int N, int d);
  * the valid keys of the blocks NOT listed in row i,
  *   O_l,t = sum_{u in D_i} (phi(Q_t).phi(K_u)) V_u / sum_{u in D_i} phi(Q_t).phi(K_u),
  * and O_l,t = 0 when D_i is empty. phi is applied to the unscaled Q and K.
- * The linear branch accumulates in float32. Setting alpha[h] = 0 still
- * evaluates the branch; callers that drop it should call sparge_attn_fwd.
+ * The linear branch accumulates in float32 from bf16-rounded phi(K) and V;
+ * its final product phi(Q) . (sum over D_i) carries about 16 significant
+ * bits per operand. Built for block_q == d (64 or 128); other block sizes
+ * return SPARGE_ERR_UNSUPPORTED. Setting alpha[h] = 0 still evaluates the
+ * branch; callers that drop it should call sparge_attn_fwd.
  *
  *  alpha     : float32 [H], device.
  *  workspace : device scratch of at least sparse_linear_workspace_bytes(),

@@ -45,7 +45,8 @@ def test_mask_workspace_bytes():
     packed_v = 40 * math.ceil(75600 / 64) * 64 * 128 * 2
     assert L.sparge_attn_workspace_bytes(1, 40, 75600, 128) == packed_v
     assert L.sparge_attn_workspace_bytes(1, 40, 75600, 96) == 0
-    assert L.sparse_linear_workspace_bytes(1, 40, 75600, 128) == packed_v + 40 * (128 * 128 + 128) * 4
+    lin = 2 * packed_v + 40 * (128 * 128 + 128) * 4 * (1 + 16)  # totals + 16 split partials
+    assert L.sparse_linear_workspace_bytes(1, 40, 75600, 128) == lin
 
 
 def _mask(**kw):
@@ -99,6 +100,7 @@ def test_attn_rejects_bad_arguments(kw, code):
 @pytest.mark.parametrize("kw,code", [
     (dict(alpha=None), -1), (dict(ws=None), -1), (dict(wsb=16), -1), (dict(q=None), -1),
     (dict(d=32), -2), (dict(alpha=ctypes.c_void_p(0x10001)), -1),
+    (dict(bq=128), -2),  # the linear branch is built for block_q == d
 ])
 def test_linear_rejects_bad_arguments(kw, code):
     assert _lin(**kw) == code

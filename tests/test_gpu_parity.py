@@ -152,3 +152,73 @@ def test_attention_matches_oracle_on_workloads(name, samples):
             rows = ~np.isnan(ref[:, 0])
             mx, mean = compare_outputs(got[b, h][rows], ref[rows])
             print(f"[attn] {name} b={b} h={h}: max {mx:.2e} mean {mean:.2e}", flush=True)
+
+
+# ------------------------------------------------------------ linear branch
+@pytest.mark.parametrize("B,H,N,d,bq", [(1, 2, 1000, 128, 128), (2, 1, 777, 64, 64),
+                                         (1, 3, 300, 128, 128), (1, 1, 64, 64, 64)])
+def test_sparse_linear_small_shapes_in_full(B, H, N, d, bq):
+    rng = np.random.default_rng(7 * N + d)
+    from block_sparse_attention_softmax_amd.workloads import f64_to_bf16_bits
+    Q, K, V = (f64_to_bf16_bits(rng.standard_normal((B, H, N, d))) for _ in range(3))
+    n_q, n_k = -(-N // bq), -(-N // 64)
+    kept = _random_lists(rng, B, H, n_q, n_k)  # includes an empty and a full row
+    idx, cnt = O.kept_to_index_list(kept)
+    alpha = rng.uniform(0.05, 0.8, size=H).astype(np.float32)
+    print(f"\n[linear] B={B} H={H} N={N} d={d} bq={bq}", flush=True)
+    o = S.sparse_linear_attn_fwd(to_gpu(Q), to_gpu(K), to_gpu(V), torch.from_numpy(idx).cuda(),
+                                 torch.from_numpy(cnt).cuda(), torch.from_numpy(alpha).cuda(),
+                                 bq, 64)
+    torch.cuda.synchronize()
+    got = O.bf16_to_f64(o.cpu().view(torch.uint16).numpy())
+    scale = S.default_scale(d)
+    for b in range(B):
+        for h in range(H):
+            ref = O.sparse_linear_attention_head(O.bf16_to_f64(Q[b, h]), O.bf16_to_f64(K[b, h]),
+                                                 O.bf16_to_f64(V[b, h]), kept[b, h], bq, 64,
+                                                 scale, float(alpha[h]))
+            mx, mean = compare_outputs(got[b, h], ref)
+            print(f"[linear] b={b} h={h}: max {mx:.2e} mean {mean:.2e}", flush=True)
+
+
+def test_sparse_linear_matches_oracle_on_workload():
+    """The sparse-linear workload: wan1.3b inputs and mask, alpha = 0.1 per head."""
+    wl, Q, K, V, q, k, v = workload_tensors("wan1.3b_linear")
+    bits, idx, cnt = S.sparge_mask_predict(q, k, wl.block_q, wl.block_k, wl.k_frac, wl.p_mass)
+    alpha = torch.full((wl.H,), wl.linear_alpha, dtype=torch.float32, device="cuda")
+    o = S.sparse_linear_attn_fwd(q, k, v, idx, cnt, alpha, wl.block_q, wl.block_k)
+    torch.cuda.synchronize()
+    kept = gpu_bits_to_bool(bits, wl.n_k)
+    got = O.bf16_to_f64(o.cpu().view(torch.uint16).numpy())
+    rng = np.random.default_rng(99)
+    for h in rng.choice(wl.H, size=3, replace=False):
+        blocks = sorted({0, wl.n_q - 1, *rng.choice(wl.n_q, 4, replace=False)})
+        ref = O.sparse_linear_attention_head(O.bf16_to_f64(Q[0, h]), O.bf16_to_f64(K[0, h]),
+                                             O.bf16_to_f64(V[0, h]), kept[0, h], wl.block_q,
+                                             wl.block_k, wl.scale, wl.linear_alpha,
+                                             q_blocks=blocks)
+        rows = ~np.isnan(ref[:, 0])
+        mx, mean = compare_outputs(got[0, h][rows], ref[rows])
+        print(f"[linear] wan1.3b_linear h={h}: max {mx:.2e} mean {mean:.2e}", flush=True)
+
+
+def test_sparse_linear_branch_contributes():
+    """The linear term is really added: with alpha = 0 the output equals sparse attention,
+    and with alpha > 0 it differs exactly on rows that dropped blocks."""
+    rng = np.random.default_rng(5)
+    from block_sparse_attention_softmax_amd.workloads import f64_to_bf16_bits
+    B, H, N, d = 1, 2, 512, 128
+    Q, K, V = (to_gpu(f64_to_bf16_bits(rng.standard_normal((B, H, N, d)))) for _ in range(3))
+    kept = np.zeros((B, H, 4, 8), bool)
+    kept[..., :3] = True
+    kept[:, :, 2, :] = True  # query block 2 keeps everything -> no linear term
+    idx, cnt = (torch.from_numpy(x).cuda() for x in O.kept_to_index_list(kept))
+    o_s = S.sparge_attn_fwd(Q, K, V, idx, cnt, 128, 64)
+    zero = S.sparse_linear_attn_fwd(Q, K, V, idx, cnt, torch.zeros(H, device="cuda"), 128, 64)
+    half = S.sparse_linear_attn_fwd(Q, K, V, idx, cnt, torch.full((H,), 0.5, device="cuda"),
+                                    128, 64)
+    torch.cuda.synchronize()
+    assert torch.equal(zero.view(torch.int16), o_s.view(torch.int16))
+    diff = (half.float() - o_s.float()).abs().amax(dim=-1)  # [B, H, N]
+    assert (diff[..., 256:384] == 0).all()
+    assert (diff[..., :256] > 0).all() and (diff[..., 384:] > 0).all()
