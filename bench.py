@@ -30,6 +30,24 @@ sys.path.insert(0, ROOT)
 
 METRIC = "sparse attn ms + dense-equiv TFLOPS (% bf16 MFMA peak) at 90/95% sparsity"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+KERNEL_SRC = os.path.join(ROOT, "block_sparse_attention_softmax_amd", "csrc", "attn_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_attn_fwd_wan1.3b_traffic.txt")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the attention kernel from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary, or None if the kernel source changed since."""
+    import hashlib
+    try:
+        kv = dict(line.split("=", 1) for line in open(TRAFFIC_FILE)
+                  if "=" in line and not line.startswith("#"))
+        kv = {k.strip(): v.strip() for k, v in kv.items()}
+        src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+        if kv.get("kernel_source_sha256") != src:
+            return None
+        return float(kv["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def kept_flops(cnt: np.ndarray, idx: np.ndarray, N: int, d: int, block_q: int,
@@ -117,6 +135,8 @@ def main():
                      dtype=torch.uint8, device=dev)
     o = torch.empty_like(q)
     aws = torch.empty(S.attn_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+    lws = torch.empty(S.linear_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+    alpha = torch.full((H,), 0.1, dtype=torch.float32, device=dev)
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 20
         src = torch.ones(n, dtype=torch.uint8, device=dev)
@@ -126,26 +146,30 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    def step(k_frac, p_mass, ev=None):
+    def step(k_frac, p_mass, ev=None, linear=False):
         if ev is not None:
             ev[0].record()
         S.sparge_mask_predict(q, k, wl.block_q, wl.block_k, k_frac, p_mass, wl.scale,
                               workspace=ws, out=(bits, idx, cnt))
         if ev is not None:
             ev[1].record()
-        S.sparge_attn_fwd(q, k, v, idx, cnt, wl.block_q, wl.block_k, wl.scale, out=o,
-                          workspace=aws)
+        if linear:
+            S.sparse_linear_attn_fwd(q, k, v, idx, cnt, alpha, wl.block_q, wl.block_k, wl.scale,
+                                     workspace=lws, out=o)
+        else:
+            S.sparge_attn_fwd(q, k, v, idx, cnt, wl.block_q, wl.block_k, wl.scale, out=o,
+                              workspace=aws)
         if ev is not None:
             ev[2].record()
 
-    def timed(k_frac, p_mass, steps, warmup):
+    def timed(k_frac, p_mass, steps, warmup, linear=False):
         for _ in range(warmup):
-            step(k_frac, p_mass)
+            step(k_frac, p_mass, linear=linear)
         torch.cuda.synchronize()
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
         t0 = time.perf_counter()
         for i in range(steps):
-            step(k_frac, p_mass, evs[i])
+            step(k_frac, p_mass, evs[i], linear=linear)
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) / steps
         mask_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
@@ -155,21 +179,47 @@ def main():
         kept_frac = float(c_np.sum()) / (B * H * n_q * n_k)
         return wall, mask_ms, attn_ms, kf, kept_frac
 
+    def pack_only_ms(reps=20):
+        """sparge_attn_fwd with every list empty: the V pack plus a launch whose
+        workgroups exit at once. Subtracted from the call to time the kernel."""
+        zero = torch.zeros_like(cnt)
+        for _ in range(3):
+            S.sparge_attn_fwd(q, k, v, idx, zero, wl.block_q, wl.block_k, wl.scale, out=o,
+                              workspace=aws)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            S.sparge_attn_fwd(q, k, v, idx, zero, wl.block_q, wl.block_k, wl.scale, out=o,
+                              workspace=aws)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
     dense = 4.0 * B * H * float(N) * N * d
     wall, mask_ms, attn_ms, kf, kept_frac = timed(wl.k_frac, wl.p_mass, args.steps, args.warmup)
-    achieved = kf / (attn_ms * 1e-3) / 1e12
+    pack_ms = pack_only_ms()
+    kern_ms = attn_ms - pack_ms
+    achieved = kf / (kern_ms * 1e-3) / 1e12
 
     points = {}
     for kfrac in (0.10, 0.05):
         w2, m2, a2, kf2, frac2 = timed(kfrac, 0.0, max(5, args.steps // 2), 2)
+        k2 = a2 - pack_ms
         points[f"p0_k{int(kfrac * 100)}"] = {
             "k": kfrac, "p": 0.0, "block_sparsity": round(1 - frac2, 4),
             "ms_per_step": round(w2 * 1e3, 4), "mask_ms": round(m2, 4),
-            "attn_ms": round(a2, 4),
+            "attn_ms": round(a2, 4), "attn_kernel_ms": round(k2, 4),
             "dense_equiv_tflops": round(dense / w2 / 1e12, 2),
             "attn_dense_equiv_tflops": round(dense / (a2 * 1e-3) / 1e12, 2),
-            "attn_kept_tflops": round(kf2 / (a2 * 1e-3) / 1e12, 2),
-            "attn_frac_bf16_peak": round(kf2 / (a2 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+            "attn_kept_tflops": round(kf2 / (k2 * 1e-3) / 1e12, 2),
+            "attn_frac_bf16_peak": round(kf2 / (k2 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+    # the sparse-linear workload: same inputs and mask, plus alpha = 0.1 elu+1 linear branch
+    w3, m3, a3, kf3, frac3 = timed(wl.k_frac, wl.p_mass, max(5, args.steps // 2), 2, linear=True)
+    linear = {"workload": "wan1.3b_linear (alpha = 0.1, phi = elu + 1)",
+              "ms_per_step": round(w3 * 1e3, 4), "mask_ms": round(m3, 4),
+              "sparse_linear_ms": round(a3, 4),
+              "dense_equiv_tflops": round(dense / w3 / 1e12, 2)}
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl, Q, K, V, args.cpu_blocks)
 
@@ -187,11 +237,14 @@ def main():
                    "global_batch": B, "seq_len": N, "parallelism": "single GPU",
                    "block_sparsity": round(1 - kept_frac, 4)},
         "mask_ms": round(mask_ms, 4), "attn_ms": round(attn_ms, 4),
+        "pack_ms": round(pack_ms, 4), "attn_kernel_ms": round(kern_ms, 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "kernel": "sparse_attn_fwd_kernel<128,128>",
+                     "traffic": measured_traffic(),
+                     "kernel": "sparse_attn_fwd_kernel<128,128,false>",
                      "flops_per_launch": kf},
         "operating_points": points,
+        "sparse_linear": linear,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -41,50 +41,52 @@ __device__ __forceinline__ float elu1(float x) { return x > 0.0f ? x + 1.0f : ex
 
 // vt[bh][j][d][slot] = V[bh][64*j + packed_key(slot)][d], zero past N; with
 // LIN also phikt[...] = bf16(phi(K[...])) in the same layout.
-// grid (n_k, B*H), 256 threads; one 64-key block per workgroup.
+// grid (n_k, B*H), 2*D threads; one 64-key block per workgroup. Thread t
+// takes keys 4q..4q+3 (q = t % 16) at d = 8c..8c+7 (c = t / 16): four 16-byte
+// rows in, transposed in registers, eight 8-byte pieces out. The four keys
+// occupy four consecutive slots, and the 16 lanes sharing c write whole
+// 128-byte rows of the packed block.
 template <int D, bool LIN>
-__global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ v,
-                                                   const uint16_t* __restrict__ k,
-                                                   uint16_t* __restrict__ vt,
-                                                   uint16_t* __restrict__ phikt, int N,
-                                                   int n_k) {
-  constexpr int NT = LIN ? 2 : 1;
-  // +2: odd 32-bit word pitch, so the column reads below are conflict-free
-  __shared__ uint16_t tile[NT][BK][D + 2];
+__global__ __launch_bounds__(2 * D) void pack_kernel(const uint16_t* __restrict__ v,
+                                                     const uint16_t* __restrict__ k,
+                                                     uint16_t* __restrict__ vt,
+                                                     uint16_t* __restrict__ phikt, int N,
+                                                     int n_k) {
   const int j = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
-  constexpr int CPR = D / 8;
+  const int q = t & 15, c = t >> 4;
+  // slot of key 4q: group q/4, then the inverse of packed_key within it
+  const int slot0 = 16 * (q >> 2) + 8 * (q & 1) + 4 * ((q >> 1) & 1);
 #pragma unroll
-  for (int w = 0; w < NT; ++w) {
-    const uint16_t* src = (w == 0 ? v : k) + ((size_t)bh * N + (size_t)j * BK) * D;
-    for (int c = t; c < BK * CPR; c += 256) {
-      const int row = c / CPR, ch = c % CPR;
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (j * BK + row < N) x = *reinterpret_cast<const uint4*>(src + (size_t)row * D + ch * 8);
-      const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+  for (int w = 0; w < (LIN ? 2 : 1); ++w) {
+    const uint16_t* src = (w == 0 ? v : k) + ((size_t)bh * N + (size_t)j * BK) * D + c * 8;
+    uint32_t x[4][4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        uint16_t lo = (uint16_t)(xs[e] & 0xFFFFu), hi = (uint16_t)(xs[e] >> 16);
-        if (w == 1 && j * BK + row < N) {
-          lo = (uint16_t)f32_to_bf16_rne(elu1(bf16_lo(xs[e])));
-          hi = (uint16_t)f32_to_bf16_rne(elu1(bf16_hi(xs[e])));
+    for (int r = 0; r < 4; ++r) {
+      const int key = 4 * q + r;
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (j * BK + key < N) {
+        u = *reinterpret_cast<const uint4*>(src + (size_t)key * D);
+        if (w == 1) {  // phi(K), rounded to bf16
+          uint32_t* p = &u.x;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            p[e] = f32_to_bf16_rne(elu1(bf16_lo(p[e]))) |
+                   (f32_to_bf16_rne(elu1(bf16_hi(p[e]))) << 16);
         }
-        tile[w][row][ch * 8 + 2 * e] = lo;
-        tile[w][row][ch * 8 + 2 * e + 1] = hi;
       }
+      x[r][0] = u.x; x[r][1] = u.y; x[r][2] = u.z; x[r][3] = u.w;
     }
-  }
-  __syncthreads();
+    uint16_t* dst = (w == 0 ? vt : phikt) + ((size_t)bh * n_k + j) * (size_t)D * BK +
+                    (size_t)(8 * c) * BK + slot0;
 #pragma unroll
-  for (int w = 0; w < NT; ++w) {
-    uint16_t* dst = (w == 0 ? vt : phikt) + ((size_t)bh * n_k + j) * (size_t)D * BK;
-    for (int c = t; c < D * (BK / 8); c += 256) {  // output chunk: row d, slots 8*g8..+8
-      const int d = c / (BK / 8), g8 = c % (BK / 8);
-      uint32_t x[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        x[e] = (uint32_t)tile[w][packed_key(8 * g8 + 2 * e)][d] |
-               ((uint32_t)tile[w][packed_key(8 * g8 + 2 * e + 1)][d] << 16);
-      *reinterpret_cast<uint4*>(dst + (size_t)d * BK + 8 * g8) = make_uint4(x[0], x[1], x[2], x[3]);
+    for (int e = 0; e < 4; ++e) {  // d = 8c + 2e (low halves) and 8c + 2e + 1 (high)
+      uint2 lo, hi;
+      lo.x = (x[0][e] & 0xFFFFu) | (x[1][e] << 16);
+      lo.y = (x[2][e] & 0xFFFFu) | (x[3][e] << 16);
+      hi.x = (x[0][e] >> 16) | (x[1][e] & 0xFFFF0000u);
+      hi.y = (x[2][e] >> 16) | (x[3][e] & 0xFFFF0000u);
+      *reinterpret_cast<uint2*>(dst + (size_t)(2 * e) * BK) = lo;
+      *reinterpret_cast<uint2*>(dst + (size_t)(2 * e + 1) * BK) = hi;
     }
   }
 }
@@ -92,8 +94,10 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ 
 // ------------------------------------------------------------ LDS tiles
 // K tile: [64 keys][D] row-major; V tile: packed V^T, [D][64 slots]. The
 // 16-byte chunks of every row are XOR-swizzled with the row index so that
-// the MFMA operand reads (32 rows at one chunk) hit distinct banks: chunk c
-// of row r is stored at chunk c ^ (r mod chunks-per-row).
+// the MFMA operand reads (16 lanes per cycle, 16 consecutive rows at one
+// logical chunk) cover all 64 banks: K rows are 256 bytes, so chunk c of row
+// r goes to c ^ (r mod 16); V^T rows are 128 bytes, two per bank window, so
+// chunk c goes to c ^ ((r / 2) mod 8).
 template <int D, bool LIN>
 struct Tile {
   static constexpr int STAGE = (LIN ? 3 : 2) * BK * D * 2;  // K + V^T (+ phi(K)^T)
@@ -103,7 +107,7 @@ struct Tile {
   static constexpr int VCPR = BK / 8;   // 8
   static constexpr int BYTES = BK * D * 2;  // one K, V^T or phi(K)^T tile
   __device__ static constexpr int kchunk(int row, int chunk) { return chunk ^ (row & (KCPR - 1)); }
-  __device__ static constexpr int vchunk(int row, int chunk) { return chunk ^ (row & (VCPR - 1)); }
+  __device__ static constexpr int vchunk(int row, int chunk) { return chunk ^ ((row >> 1) & (VCPR - 1)); }
 };
 
 __device__ __forceinline__ bf16x8 lds_read16(const unsigned char* p) {
@@ -123,6 +127,18 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(const floatx16& x, int base) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) r[e] = (__bf16)x[base + e];
   return r;
+}
+
+// acc + sum of the 8 bf16 values (v_dot2 against ones, float32 accumulate)
+__device__ __forceinline__ float row_sum_bf16x8(const bf16x8& p, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    const bf16x2 pr = {p[e], p[e + 1]};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc, false);
+  }
+  return acc;
 }
 
 // max / sum over the two half-waves (lane l and lane l ^ 32): the swap
@@ -263,31 +279,41 @@ __global__ __launch_bounds__(BQ * 2, (LIN || (D == 128 && BQ == 64)) ? 1 : 2) vo
   // ---- DMA staging: wave w, load u fills LDS chunks [64*(u*NW+w), +64),
   // lane-linear; each lane fetches the global chunk that the swizzle maps
   // there (the swizzles are involutions). Offsets are loop invariant.
-  int krow[LOADS], ksrc[LOADS], vsrc[LOADS];
+  int krow[LOADS];
+  uint32_t kbyte[LOADS], vbyte[LOADS];  // byte offsets within a tile
 #pragma unroll
   for (int u = 0; u < LOADS; ++u) {
     const int p = 64 * (u * NW + wave) + lane;   // LDS chunk index
     const int kr = p / T::KCPR, vr = p / T::VCPR;
     krow[u] = kr;
-    ksrc[u] = kr * D + T::kchunk(kr, p % T::KCPR) * 8;
-    vsrc[u] = vr * BK + T::vchunk(vr, p % T::VCPR) * 8;
+    kbyte[u] = (uint32_t)(kr * D + T::kchunk(kr, p % T::KCPR) * 8) * 2u;
+    vbyte[u] = (uint32_t)(vr * BK + T::vchunk(vr, p % T::VCPR) * 8) * 2u;
   }
   auto stage = [&](int j, int buf) {
     unsigned char* kb = smem + buf * T::STAGE;
     unsigned char* vb = kb + T::BYTES;
     const int key0 = j * BK;
-    const uint16_t* kt = kh + (size_t)key0 * D;
-    const uint16_t* vtt = vth + (size_t)j * vtile;
-    const bool full = key0 + BK <= N;
+    const char* kt = reinterpret_cast<const char*>(kh + (size_t)key0 * D);
+    const char* vtt = reinterpret_cast<const char*>(vth + (size_t)j * vtile);
+    const char* ptt = LIN ? reinterpret_cast<const char*>(pkh + (size_t)j * vtile) : nullptr;
+    if (key0 + BK <= N) {
 #pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      const int dst = 1024 * (u * NW + wave);
-      // short last block: K rows past N repeat row N-1 (their scores are
-      // masked); the packed tiles are zero there
-      const int shift = full ? 0 : max(key0 + krow[u] - (N - 1), 0) * D;
-      dma16(kt + ksrc[u] - shift, kb + dst);
-      dma16(vtt + vsrc[u], vb + dst);
-      if constexpr (LIN) dma16(pkh + (size_t)j * vtile + vsrc[u], vb + T::BYTES + dst);
+      for (int u = 0; u < LOADS; ++u) {
+        const int dst = 1024 * (u * NW + wave);
+        dma16(kt + kbyte[u], kb + dst);
+        dma16(vtt + vbyte[u], vb + dst);
+        if constexpr (LIN) dma16(ptt + vbyte[u], vb + T::BYTES + dst);
+      }
+    } else {  // short last block: K rows past N repeat row N-1 (their scores
+              // are masked); the packed tiles are zero there
+#pragma unroll
+      for (int u = 0; u < LOADS; ++u) {
+        const int dst = 1024 * (u * NW + wave);
+        const uint32_t shift = (uint32_t)max(key0 + krow[u] - (N - 1), 0) * D * 2u;
+        dma16(kt + (kbyte[u] - shift), kb + dst);
+        dma16(vtt + vbyte[u], vb + dst);
+        if constexpr (LIN) dma16(ptt + vbyte[u], vb + T::BYTES + dst);
+      }
     }
   };
 
@@ -372,11 +398,7 @@ __global__ __launch_bounds__(BQ * 2, (LIN || (D == 128 && BQ == 64)) ? 1 : 2) vo
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pr = __builtin_amdgcn_exp2f(fmaf(st[tau][r], c, -mc));
-        st[tau][r] = pr;
-        lsum += pr;
-      }
+      for (int r = 0; r < 16; ++r) st[tau][r] = __builtin_amdgcn_exp2f(fmaf(st[tau][r], c, -mc));
 
     // ---- O^T += V_j^T P^T : 4 k-steps of 16 keys (LIN: H_kept += phi(K_j)^T V_j)
 #pragma unroll
@@ -385,6 +407,7 @@ __global__ __launch_bounds__(BQ * 2, (LIN || (D == 128 && BQ == 64)) ? 1 : 2) vo
       for (int hk = 0; hk < 2; ++hk) {
         const int G = 2 * tau + hk;
         const bf16x8 pb = pack_bf16x8(st[tau], 8 * hk);
+        lsum = row_sum_bf16x8(pb, lsum);  // l sums the same bf16 P that meets V
         bf16x8 pkf;
         if constexpr (LIN) {
           pkf = lds_read16(vb + T::BYTES + wave * 32 * T::VROWB + voff[G]);
@@ -497,7 +520,7 @@ hipError_t launch_sparse(const AttnLaunch& a, hipStream_t s) {
   const int total = a.B * a.H * a.n_q;
   const float c = a.scale * 1.4426950408889634f;  // scale * log2(e)
   const int BH = a.B * a.H;
-  hipLaunchKernelGGL((pack_kernel<D, LIN>), dim3(a.n_k, BH), dim3(256), 0, s, a.v, a.k, a.vt,
+  hipLaunchKernelGGL((pack_kernel<D, LIN>), dim3(a.n_k, BH), dim3(2 * D), 0, s, a.v, a.k, a.vt,
                      a.phikt, a.N, a.n_k);
   if constexpr (LIN) {
     hipLaunchKernelGGL((linear_total_kernel<D>), dim3(kLinSplit, BH), dim3(D * 2), 0, s,
