@@ -147,6 +147,7 @@ def main():
         del src, dst
 
     def step(k_frac, p_mass, ev=None, linear=False):
+        """mask -> [events] -> V pack -> attention (the two halves of sparge_attn_fwd)."""
         if ev is not None:
             ev[0].record()
         S.sparge_mask_predict(q, k, wl.block_q, wl.block_k, k_frac, p_mass, wl.scale,
@@ -156,69 +157,58 @@ def main():
         if linear:
             S.sparse_linear_attn_fwd(q, k, v, idx, cnt, alpha, wl.block_q, wl.block_k, wl.scale,
                                      workspace=lws, out=o)
+            if ev is not None:
+                ev[2].record()
         else:
-            S.sparge_attn_fwd(q, k, v, idx, cnt, wl.block_q, wl.block_k, wl.scale, out=o,
-                              workspace=aws)
+            S.sparge_attn_pack(v, workspace=aws)
+            if ev is not None:
+                ev[2].record()
+            S.sparge_attn_fwd_packed(q, k, idx, cnt, aws, wl.block_q, wl.block_k, wl.scale,
+                                     out=o)
         if ev is not None:
-            ev[2].record()
+            ev[3].record()
 
     def timed(k_frac, p_mass, steps, warmup, linear=False):
         for _ in range(warmup):
             step(k_frac, p_mass, linear=linear)
         torch.cuda.synchronize()
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
         t0 = time.perf_counter()
         for i in range(steps):
             step(k_frac, p_mass, evs[i], linear=linear)
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) / steps
         mask_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-        attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+        pack_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+        attn_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
         c_np, i_np = cnt.cpu().numpy(), idx.cpu().numpy()
         kf = kept_flops(c_np, i_np, N, d, wl.block_q, wl.block_k)
         kept_frac = float(c_np.sum()) / (B * H * n_q * n_k)
-        return wall, mask_ms, attn_ms, kf, kept_frac
-
-    def pack_only_ms(reps=20):
-        """sparge_attn_fwd with every list empty: the V pack plus a launch whose
-        workgroups exit at once. Subtracted from the call to time the kernel."""
-        zero = torch.zeros_like(cnt)
-        for _ in range(3):
-            S.sparge_attn_fwd(q, k, v, idx, zero, wl.block_q, wl.block_k, wl.scale, out=o,
-                              workspace=aws)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            S.sparge_attn_fwd(q, k, v, idx, zero, wl.block_q, wl.block_k, wl.scale, out=o,
-                              workspace=aws)
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps
+        return wall, mask_ms, pack_ms, attn_ms, kf, kept_frac
 
     dense = 4.0 * B * H * float(N) * N * d
-    wall, mask_ms, attn_ms, kf, kept_frac = timed(wl.k_frac, wl.p_mass, args.steps, args.warmup)
-    pack_ms = pack_only_ms()
-    kern_ms = attn_ms - pack_ms
+    wall, mask_ms, pack_ms, kern_ms, kf, kept_frac = timed(wl.k_frac, wl.p_mass, args.steps,
+                                                            args.warmup)
     achieved = kf / (kern_ms * 1e-3) / 1e12
 
     points = {}
     for kfrac in (0.10, 0.05):
-        w2, m2, a2, kf2, frac2 = timed(kfrac, 0.0, max(5, args.steps // 2), 2)
-        k2 = a2 - pack_ms
+        w2, m2, p2, k2, kf2, frac2 = timed(kfrac, 0.0, max(5, args.steps // 2), 2)
         points[f"p0_k{int(kfrac * 100)}"] = {
             "k": kfrac, "p": 0.0, "block_sparsity": round(1 - frac2, 4),
             "ms_per_step": round(w2 * 1e3, 4), "mask_ms": round(m2, 4),
-            "attn_ms": round(a2, 4), "attn_kernel_ms": round(k2, 4),
+            "pack_ms": round(p2, 4), "attn_kernel_ms": round(k2, 4),
             "dense_equiv_tflops": round(dense / w2 / 1e12, 2),
-            "attn_dense_equiv_tflops": round(dense / (a2 * 1e-3) / 1e12, 2),
+            "attn_dense_equiv_tflops": round(dense / (k2 * 1e-3) / 1e12, 2),
             "attn_kept_tflops": round(kf2 / (k2 * 1e-3) / 1e12, 2),
             "attn_frac_bf16_peak": round(kf2 / (k2 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
     # the sparse-linear workload: same inputs and mask, plus alpha = 0.1 elu+1 linear branch
-    w3, m3, a3, kf3, frac3 = timed(wl.k_frac, wl.p_mass, max(5, args.steps // 2), 2, linear=True)
+    w3, m3, l3, _, kf3, frac3 = timed(wl.k_frac, wl.p_mass, max(5, args.steps // 2), 2,
+                                      linear=True)
     linear = {"workload": "wan1.3b_linear (alpha = 0.1, phi = elu + 1)",
               "ms_per_step": round(w3 * 1e3, 4), "mask_ms": round(m3, 4),
-              "sparse_linear_ms": round(a3, 4),
+              "sparse_linear_ms": round(l3, 4),
               "dense_equiv_tflops": round(dense / w3 / 1e12, 2)}
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl, Q, K, V, args.cpu_blocks)
@@ -236,8 +226,8 @@ def main():
                                f"p={wl.p_mass}",
                    "global_batch": B, "seq_len": N, "parallelism": "single GPU",
                    "block_sparsity": round(1 - kept_frac, 4)},
-        "mask_ms": round(mask_ms, 4), "attn_ms": round(attn_ms, 4),
-        "pack_ms": round(pack_ms, 4), "attn_kernel_ms": round(kern_ms, 4),
+        "mask_ms": round(mask_ms, 4), "pack_ms": round(pack_ms, 4),
+        "attn_kernel_ms": round(kern_ms, 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(),

@@ -20,7 +20,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP = 0, -1, -2, -3
 
 # every symbol the public header declares
 EXPORTS = ("sparge_mask_workspace_bytes", "sparge_mask_predict", "sparge_attn_workspace_bytes",
-           "sparge_attn_fwd",
+           "sparge_attn_fwd", "sparge_attn_pack", "sparge_attn_fwd_packed",
            "sparse_linear_workspace_bytes", "sparse_linear_attn_fwd", "sparge_last_error")
 
 _lib = None
@@ -50,6 +50,10 @@ def lib() -> ctypes.CDLL:
         L.sparge_attn_workspace_bytes.restype = c_size
         L.sparge_attn_fwd.argtypes = [vp] * 5 + [c_int] * 6 + [c_float, vp, vp, c_size, vp]
         L.sparge_attn_fwd.restype = c_int
+        L.sparge_attn_pack.argtypes = [vp] + [c_int] * 4 + [vp, c_size, vp]
+        L.sparge_attn_pack.restype = c_int
+        L.sparge_attn_fwd_packed.argtypes = [vp] * 4 + [c_int] * 6 + [c_float, vp, vp, c_size, vp]
+        L.sparge_attn_fwd_packed.restype = c_int
         L.sparse_linear_workspace_bytes.argtypes = [c_int] * 4
         L.sparse_linear_workspace_bytes.restype = c_size
         L.sparse_linear_attn_fwd.argtypes = [vp] * 6 + [c_int] * 6 + [c_float, vp, vp, c_size,
@@ -139,6 +143,30 @@ def sparge_attn_fwd(q, k, v, kv_idx, kv_cnt, block_q=128, block_k=64, scale=None
     _check(lib().sparge_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_idx), _ptr(kv_cnt), B, H,
                                  N, d, block_q, block_k, scale, _ptr(o), _ptr(workspace),
                                  workspace.numel(), _stream(q)))
+    return o
+
+
+def sparge_attn_pack(v, workspace=None):
+    """Pack V for sparge_attn_fwd_packed; returns the workspace holding it."""
+    B, H, N, d = _qkv(v)
+    if workspace is None:
+        workspace = torch.empty(max(attn_workspace_bytes(B, H, N, d), 16), dtype=torch.uint8,
+                                device=v.device)
+    _check(lib().sparge_attn_pack(_ptr(v), B, H, N, d, _ptr(workspace), workspace.numel(),
+                                  _stream(v)))
+    return workspace
+
+
+def sparge_attn_fwd_packed(q, k, kv_idx, kv_cnt, workspace, block_q=128, block_k=64, scale=None,
+                           out=None):
+    """Block-sparse attention with V already packed into `workspace`."""
+    B, H, N, d = _qkv(q, k)
+    o = torch.empty_like(q) if out is None else out
+    if scale is None:
+        scale = default_scale(d)
+    _check(lib().sparge_attn_fwd_packed(_ptr(q), _ptr(k), _ptr(kv_idx), _ptr(kv_cnt), B, H, N, d,
+                                        block_q, block_k, scale, _ptr(o), _ptr(workspace),
+                                        workspace.numel(), _stream(q)))
     return o
 
 

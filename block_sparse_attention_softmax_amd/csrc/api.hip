@@ -156,18 +156,10 @@ size_t sparge_attn_workspace_bytes(int B, int H, int N, int d) {
   return sparge::attn_workspace_bytes(B, H, N, d);
 }
 
-int sparge_attn_fwd(const void* q, const void* k, const void* v, const int32_t* kv_idx,
-                    const int32_t* kv_cnt, int B, int H, int N, int d, int block_q,
-                    int block_k, float scale, void* o, void* workspace, size_t workspace_bytes,
-                    void* stream) {
-  g_last_error.clear();
-  int rc = check_attn_args(q, k, v, kv_idx, kv_cnt, B, H, N, d, block_q, block_k, scale, o);
-  if (rc != SPARGE_OK) return rc;
-  if (!workspace) return fail(SPARGE_ERR_INVALID_ARG, "null pointer argument");
-  if (!aligned(workspace, 16))
-    return fail(SPARGE_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-  if (workspace_bytes < sparge::attn_workspace_bytes(B, H, N, d))
-    return fail(SPARGE_ERR_INVALID_ARG, "workspace too small");
+namespace {
+sparge::AttnLaunch attn_args(const void* q, const void* k, const void* v, const int32_t* kv_idx,
+                             const int32_t* kv_cnt, int B, int H, int N, int d, int block_q,
+                             int block_k, float scale, void* o, void* workspace) {
   sparge::AttnLaunch a{};
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -180,8 +172,66 @@ int sparge_attn_fwd(const void* q, const void* k, const void* v, const int32_t* 
   a.n_q = ceil_div(N, block_q);
   a.n_k = ceil_div(N, block_k);
   a.scale = scale;
+  return a;
+}
+
+int check_attn_workspace(const void* workspace, size_t workspace_bytes, int B, int H, int N,
+                         int d) {
+  if (!workspace) return fail(SPARGE_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned(workspace, 16))
+    return fail(SPARGE_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  if (workspace_bytes < sparge::attn_workspace_bytes(B, H, N, d))
+    return fail(SPARGE_ERR_INVALID_ARG, "workspace too small");
+  return SPARGE_OK;
+}
+}  // namespace
+
+int sparge_attn_fwd(const void* q, const void* k, const void* v, const int32_t* kv_idx,
+                    const int32_t* kv_cnt, int B, int H, int N, int d, int block_q,
+                    int block_k, float scale, void* o, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  g_last_error.clear();
+  int rc = check_attn_args(q, k, v, kv_idx, kv_cnt, B, H, N, d, block_q, block_k, scale, o);
+  if (rc == SPARGE_OK) rc = check_attn_workspace(workspace, workspace_bytes, B, H, N, d);
+  if (rc != SPARGE_OK) return rc;
+  const sparge::AttnLaunch a =
+      attn_args(q, k, v, kv_idx, kv_cnt, B, H, N, d, block_q, block_k, scale, o, workspace);
   const hipError_t e = sparge::launch_attn(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "sparge_attn_fwd launch");
+  return SPARGE_OK;
+}
+
+int sparge_attn_pack(const void* v, int B, int H, int N, int d, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  int rc = check_shape(B, H, N, d, 128, 64);
+  if (rc != SPARGE_OK) return rc;
+  if (!v) return fail(SPARGE_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned(v, 16)) return fail(SPARGE_ERR_INVALID_ARG, "v must be 16-byte aligned");
+  rc = check_attn_workspace(workspace, workspace_bytes, B, H, N, d);
+  if (rc != SPARGE_OK) return rc;
+  const sparge::AttnLaunch a =
+      attn_args(nullptr, nullptr, v, nullptr, nullptr, B, H, N, d, 128, 64, 1.0f, nullptr,
+                workspace);
+  const hipError_t e = sparge::launch_attn(a, static_cast<hipStream_t>(stream), sparge::kPackOnly);
+  if (e != hipSuccess) return hip_fail(e, "sparge_attn_pack launch");
+  return SPARGE_OK;
+}
+
+int sparge_attn_fwd_packed(const void* q, const void* k, const int32_t* kv_idx,
+                           const int32_t* kv_cnt, int B, int H, int N, int d, int block_q,
+                           int block_k, float scale, void* o, const void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  // v is not read here; q stands in for it in the shared pointer checks
+  int rc = check_attn_args(q, k, q, kv_idx, kv_cnt, B, H, N, d, block_q, block_k, scale, o);
+  if (rc == SPARGE_OK) rc = check_attn_workspace(workspace, workspace_bytes, B, H, N, d);
+  if (rc != SPARGE_OK) return rc;
+  const sparge::AttnLaunch a = attn_args(q, k, nullptr, kv_idx, kv_cnt, B, H, N, d, block_q,
+                                         block_k, scale, o, const_cast<void*>(workspace));
+  const hipError_t e =
+      sparge::launch_attn(a, static_cast<hipStream_t>(stream), sparge::kAttendOnly);
+  if (e != hipSuccess) return hip_fail(e, "sparge_attn_fwd_packed launch");
   return SPARGE_OK;
 }
 

@@ -516,21 +516,24 @@ __global__ __launch_bounds__(BQ * 2, (LIN || (D == 128 && BQ == 64)) ? 1 : 2) vo
 }
 
 template <int D, int BQ, bool LIN>
-hipError_t launch_sparse(const AttnLaunch& a, hipStream_t s) {
+hipError_t launch_sparse(const AttnLaunch& a, hipStream_t s, AttnPhase phase) {
   const int total = a.B * a.H * a.n_q;
   const float c = a.scale * 1.4426950408889634f;  // scale * log2(e)
   const int BH = a.B * a.H;
-  hipLaunchKernelGGL((pack_kernel<D, LIN>), dim3(a.n_k, BH), dim3(2 * D), 0, s, a.v, a.k, a.vt,
-                     a.phikt, a.N, a.n_k);
-  if constexpr (LIN) {
-    hipLaunchKernelGGL((linear_total_kernel<D>), dim3(kLinSplit, BH), dim3(D * 2), 0, s,
-                       a.phikt, a.vt, a.part_h, a.part_z, a.n_k);
-    hipLaunchKernelGGL((linear_reduce_kernel<D>), dim3(BH), dim3(256), 0, s, a.part_h,
-                       a.part_z, a.lin_h, a.lin_z);
+  if (phase != kAttendOnly) {
+    hipLaunchKernelGGL((pack_kernel<D, LIN>), dim3(a.n_k, BH), dim3(2 * D), 0, s, a.v, a.k,
+                       a.vt, a.phikt, a.N, a.n_k);
+    if constexpr (LIN) {
+      hipLaunchKernelGGL((linear_total_kernel<D>), dim3(kLinSplit, BH), dim3(D * 2), 0, s,
+                         a.phikt, a.vt, a.part_h, a.part_z, a.n_k);
+      hipLaunchKernelGGL((linear_reduce_kernel<D>), dim3(BH), dim3(256), 0, s, a.part_h,
+                         a.part_z, a.lin_h, a.lin_z);
+    }
   }
-  hipLaunchKernelGGL((sparse_attn_fwd_kernel<D, BQ, LIN>), dim3(total), dim3(BQ * 2), 0, s,
-                     a.q, a.k, a.vt, a.idx, a.cnt, a.o, a.H, a.N, a.n_q, a.n_k, total, c,
-                     a.alpha, a.phikt, a.lin_h, a.lin_z);
+  if (phase != kPackOnly)
+    hipLaunchKernelGGL((sparse_attn_fwd_kernel<D, BQ, LIN>), dim3(total), dim3(BQ * 2), 0, s,
+                       a.q, a.k, a.vt, a.idx, a.cnt, a.o, a.H, a.N, a.n_q, a.n_k, total, c,
+                       a.alpha, a.phikt, a.lin_h, a.lin_z);
   return hipGetLastError();
 }
 
@@ -547,15 +550,15 @@ size_t linear_workspace_bytes(int B, int H, int N, int d) {
          BH * ((size_t)d * d + d) * (1 + kLinSplit) * sizeof(float);  // totals + partials
 }
 
-hipError_t launch_attn(const AttnLaunch& a, hipStream_t s) {
+hipError_t launch_attn(const AttnLaunch& a, hipStream_t s, AttnPhase phase) {
   if (a.alpha) {
-    if (a.d == 128) return launch_sparse<128, 128, true>(a, s);
-    return launch_sparse<64, 64, true>(a, s);
+    if (a.d == 128) return launch_sparse<128, 128, true>(a, s, phase);
+    return launch_sparse<64, 64, true>(a, s, phase);
   }
-  if (a.d == 128 && a.block_q == 128) return launch_sparse<128, 128, false>(a, s);
-  if (a.d == 128 && a.block_q == 64) return launch_sparse<128, 64, false>(a, s);
-  if (a.d == 64 && a.block_q == 128) return launch_sparse<64, 128, false>(a, s);
-  return launch_sparse<64, 64, false>(a, s);
+  if (a.d == 128 && a.block_q == 128) return launch_sparse<128, 128, false>(a, s, phase);
+  if (a.d == 128 && a.block_q == 64) return launch_sparse<128, 64, false>(a, s, phase);
+  if (a.d == 64 && a.block_q == 128) return launch_sparse<64, 128, false>(a, s, phase);
+  return launch_sparse<64, 64, false>(a, s, phase);
 }
 
 }  // namespace sparge

@@ -73,7 +73,9 @@ struct AttnLaunch {
   float* part_z;       // [B*H, kLinSplit, d]
 };
 constexpr int kLinSplit = 16;
-hipError_t launch_attn(const AttnLaunch& a, hipStream_t s);
+// pack (V, and phi(K) for the linear branch) then attend; or either half alone
+enum AttnPhase { kPackAndAttend = 0, kPackOnly = 1, kAttendOnly = 2 };
+hipError_t launch_attn(const AttnLaunch& a, hipStream_t s, AttnPhase phase = kPackAndAttend);
 size_t attn_workspace_bytes(int B, int H, int N, int d);    // packed V
 size_t linear_workspace_bytes(int B, int H, int N, int d);  // packed V + linear branch
 

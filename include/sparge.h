@@ -124,6 +124,26 @@ int sparge_attn_fwd(const void* q, const void* k, const void* v,
                     int N, int d, int block_q, int block_k, float scale, void* o,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* The two halves of sparge_attn_fwd, for callers that pack V once and attend
+ * several times (different query sets or lists over the same K and V), or
+ * that pack V on another stream while sparge_mask_predict runs (the mask
+ * reads only Q and K). sparge_attn_fwd(...) == sparge_attn_pack(v, ...)
+ * followed by sparge_attn_fwd_packed(...) on one stream, bit for bit.
+ *
+ * sparge_attn_pack writes the packed V into `workspace` (at least
+ * sparge_attn_workspace_bytes(B, H, N, d), 16-byte aligned). v: bf16
+ * [B, H, N, d], device, 16-byte aligned.
+ *
+ * sparge_attn_fwd_packed reads that workspace (it must hold the pack of the
+ * V that goes with q and k, and must not be modified while the call runs);
+ * other arguments as for sparge_attn_fwd. */
+int sparge_attn_pack(const void* v, int B, int H, int N, int d, void* workspace,
+                     size_t workspace_bytes, void* stream);
+int sparge_attn_fwd_packed(const void* q, const void* k, const int32_t* kv_idx,
+                           const int32_t* kv_cnt, int B, int H, int N, int d,
+                           int block_q, int block_k, float scale, void* o,
+                           const void* workspace, size_t workspace_bytes, void* stream);
+
 /* Device workspace (bytes) of sparse_linear_attn_fwd: the packed V of
  * sparge_attn_fwd, phi(K) packed the same way, and per (b, h) the float32
  * summaries sum_u phi(K_u)^T V_u (d x d) and sum_u phi(K_u) (d) with 16

@@ -64,6 +64,33 @@ def _attn(**kw):
     return binding.lib().sparge_attn_fwd(*args.values())
 
 
+def _pack(**kw):
+    args = dict(v=A, B=1, H=2, N=1024, d=64, ws=A, wsb=1 << 30, st=None)
+    args.update(kw)
+    return binding.lib().sparge_attn_pack(*args.values())
+
+
+def _packed(**kw):
+    args = dict(q=A, k=A, idx=A, cnt=A, B=1, H=2, N=1024, d=64, bq=64, bk=64, sc=0.125, o=A,
+                ws=A, wsb=1 << 30, st=None)
+    args.update(kw)
+    return binding.lib().sparge_attn_fwd_packed(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(v=None), -1), (dict(v=MIS), -1), (dict(ws=None), -1), (dict(wsb=1000), -1),
+    (dict(d=32), -2), (dict(N=0), -1)])
+def test_pack_rejects_bad_arguments(kw, code):
+    assert _pack(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(k=MIS), -1), (dict(o=None), -1), (dict(idx=None), -1),
+    (dict(ws=None), -1), (dict(wsb=1000), -1), (dict(bk=16), -2), (dict(sc=0.0), -1)])
+def test_packed_attn_rejects_bad_arguments(kw, code):
+    assert _packed(**kw) == code
+
+
 def _lin(**kw):
     args = dict(q=A, k=A, v=A, idx=A, cnt=A, alpha=A, B=1, H=2, N=1024, d=64, bq=64, bk=64,
                 sc=0.125, o=A, ws=A, wsb=1 << 30, st=None)

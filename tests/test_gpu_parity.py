@@ -118,6 +118,18 @@ def test_attention_small_shapes_in_full(B, H, N, d, bq):
             compare_outputs(got[b, h], ref)
 
 
+def test_pack_then_packed_equals_one_call():
+    wl, Q, K, V, q, k, v = workload_tensors("tiny")
+    bits, idx, cnt = S.sparge_mask_predict(q, k, wl.block_q, wl.block_k, wl.k_frac, wl.p_mass)
+    o1 = S.sparge_attn_fwd(q, k, v, idx, cnt, wl.block_q, wl.block_k)
+    ws = S.sparge_attn_pack(v)
+    o2 = S.sparge_attn_fwd_packed(q, k, idx, cnt, ws, wl.block_q, wl.block_k)
+    o3 = S.sparge_attn_fwd_packed(q, k, idx, cnt, ws, wl.block_q, wl.block_k)  # reuse
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(o1.view(torch.int16), o3.view(torch.int16))
+
+
 def test_attention_is_deterministic():
     wl, Q, K, V, q, k, v = workload_tensors("tiny")
     bits, idx, cnt = S.sparge_mask_predict(q, k, wl.block_q, wl.block_k, wl.k_frac, wl.p_mass)
