@@ -279,16 +279,26 @@ __global__ __launch_bounds__(BQ * 2, (LIN || (D == 128 && BQ == 64)) ? 1 : 2) vo
   // ---- DMA staging: wave w, load u fills LDS chunks [64*(u*NW+w), +64),
   // lane-linear; each lane fetches the global chunk that the swizzle maps
   // there (the swizzles are involutions). Offsets are loop invariant.
-  int krow[LOADS];
-  uint32_t kbyte[LOADS], vbyte[LOADS];  // byte offsets within a tile
+  // Load u covers rows 64*NW*u/CPR further down the tile; when that step is
+  // a multiple of the swizzle period the lane's chunk is the same for every
+  // u and its source offset is u0's plus a constant (fewer live registers).
+  constexpr int KROWS_U = 64 * NW / T::KCPR, VROWS_U = 64 * NW / T::VCPR;
+  constexpr bool KCONST = KROWS_U % T::KCPR == 0, VCONST = VROWS_U % (2 * T::VCPR) == 0;
+  uint32_t kbyte[KCONST ? 1 : LOADS], vbyte[VCONST ? 1 : LOADS];  // byte offsets in a tile
 #pragma unroll
-  for (int u = 0; u < LOADS; ++u) {
+  for (int u = 0; u < (KCONST ? 1 : LOADS); ++u) {
     const int p = 64 * (u * NW + wave) + lane;   // LDS chunk index
-    const int kr = p / T::KCPR, vr = p / T::VCPR;
-    krow[u] = kr;
+    const int kr = p / T::KCPR;
     kbyte[u] = (uint32_t)(kr * D + T::kchunk(kr, p % T::KCPR) * 8) * 2u;
+  }
+#pragma unroll
+  for (int u = 0; u < (VCONST ? 1 : LOADS); ++u) {
+    const int p = 64 * (u * NW + wave) + lane;
+    const int vr = p / T::VCPR;
     vbyte[u] = (uint32_t)(vr * BK + T::vchunk(vr, p % T::VCPR) * 8) * 2u;
   }
+  auto kofs = [&](int u) { return KCONST ? kbyte[0] + (uint32_t)(u * KROWS_U * D * 2) : kbyte[u]; };
+  auto vofs = [&](int u) { return VCONST ? vbyte[0] + (uint32_t)(u * VROWS_U * BK * 2) : vbyte[u]; };
   auto stage = [&](int j, int buf) {
     unsigned char* kb = smem + buf * T::STAGE;
     unsigned char* vb = kb + T::BYTES;
@@ -300,19 +310,20 @@ __global__ __launch_bounds__(BQ * 2, (LIN || (D == 128 && BQ == 64)) ? 1 : 2) vo
 #pragma unroll
       for (int u = 0; u < LOADS; ++u) {
         const int dst = 1024 * (u * NW + wave);
-        dma16(kt + kbyte[u], kb + dst);
-        dma16(vtt + vbyte[u], vb + dst);
-        if constexpr (LIN) dma16(ptt + vbyte[u], vb + T::BYTES + dst);
+        dma16(kt + kofs(u), kb + dst);
+        dma16(vtt + vofs(u), vb + dst);
+        if constexpr (LIN) dma16(ptt + vofs(u), vb + T::BYTES + dst);
       }
     } else {  // short last block: K rows past N repeat row N-1 (their scores
               // are masked); the packed tiles are zero there
 #pragma unroll
       for (int u = 0; u < LOADS; ++u) {
         const int dst = 1024 * (u * NW + wave);
-        const uint32_t shift = (uint32_t)max(key0 + krow[u] - (N - 1), 0) * D * 2u;
-        dma16(kt + (kbyte[u] - shift), kb + dst);
-        dma16(vtt + vbyte[u], vb + dst);
-        if constexpr (LIN) dma16(ptt + vbyte[u], vb + T::BYTES + dst);
+        const int krow = (64 * (u * NW + wave) + lane) / T::KCPR;
+        const uint32_t shift = (uint32_t)max(key0 + krow - (N - 1), 0) * D * 2u;
+        dma16(kt + (kofs(u) - shift), kb + dst);
+        dma16(vtt + vofs(u), vb + dst);
+        if constexpr (LIN) dma16(ptt + vofs(u), vb + T::BYTES + dst);
       }
     }
   };
@@ -356,13 +367,19 @@ __global__ __launch_bounds__(BQ * 2, (LIN || (D == 128 && BQ == 64)) ? 1 : 2) vo
     for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
       for (int r = 0; r < 16; ++r) st[tau][r] = 0.0f;
+    // operands for k-step s+1 are read while the MFMAs of step s run
+    bf16x8 ka[2] = {lds_read16(kb + koff[0]), lds_read16(kb + 32 * T::KROWB + koff[0])};
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
-#pragma unroll
-      for (int tau = 0; tau < 2; ++tau) {
-        const bf16x8 a = lds_read16(kb + tau * 32 * T::KROWB + koff[s]);
-        st[tau] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], st[tau], 0, 0, 0);
+      bf16x8 kn[2];
+      if (s + 1 < KSTEPS) {
+        kn[0] = lds_read16(kb + koff[s + 1]);
+        kn[1] = lds_read16(kb + 32 * T::KROWB + koff[s + 1]);
       }
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau)
+        st[tau] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[tau], qf[s], st[tau], 0, 0, 0);
+      if (s + 1 < KSTEPS) { ka[0] = kn[0]; ka[1] = kn[1]; }
     }
 
     // ---- keys past N in a short last block get -inf
@@ -400,27 +417,35 @@ __global__ __launch_bounds__(BQ * 2, (LIN || (D == 128 && BQ == 64)) ? 1 : 2) vo
 #pragma unroll
       for (int r = 0; r < 16; ++r) st[tau][r] = __builtin_amdgcn_exp2f(fmaf(st[tau][r], c, -mc));
 
-    // ---- O^T += V_j^T P^T : 4 k-steps of 16 keys (LIN: H_kept += phi(K_j)^T V_j)
+    // ---- O^T += V_j^T P^T : 4 k-steps of 16 keys (LIN: H_kept += phi(K_j)^T V_j);
+    //      the V^T operands of step G+1 are read while the MFMAs of step G run
+    bf16x8 va[DT];
 #pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
+    for (int i = 0; i < DT; ++i) va[i] = lds_read16(vb + i * 32 * T::VROWB + voff[0]);
 #pragma unroll
-      for (int hk = 0; hk < 2; ++hk) {
-        const int G = 2 * tau + hk;
-        const bf16x8 pb = pack_bf16x8(st[tau], 8 * hk);
-        lsum = row_sum_bf16x8(pb, lsum);  // l sums the same bf16 P that meets V
-        bf16x8 pkf;
-        if constexpr (LIN) {
-          pkf = lds_read16(vb + T::BYTES + wave * 32 * T::VROWB + voff[G]);
+    for (int G = 0; G < 4; ++G) {
+      const int tau = G >> 1, hk = G & 1;
+      const bf16x8 pb = pack_bf16x8(st[tau], 8 * hk);
+      lsum = row_sum_bf16x8(pb, lsum);  // l sums the same bf16 P that meets V
+      bf16x8 vn[DT], pkf;
+      if (G + 1 < 4) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) zk += (float)pkf[e];
-        }
+        for (int i = 0; i < DT; ++i) vn[i] = lds_read16(vb + i * 32 * T::VROWB + voff[G + 1]);
+      }
+      if constexpr (LIN) {
+        pkf = lds_read16(vb + T::BYTES + wave * 32 * T::VROWB + voff[G]);
 #pragma unroll
-        for (int i = 0; i < DT; ++i) {
-          const bf16x8 a = lds_read16(vb + i * 32 * T::VROWB + voff[G]);
-          oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[i], 0, 0, 0);
-          if constexpr (LIN)
-            hacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pkf, a, hacc[i], 0, 0, 0);
-        }
+        for (int e = 0; e < 8; ++e) zk += (float)pkf[e];
+      }
+#pragma unroll
+      for (int i = 0; i < DT; ++i) {
+        oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], pb, oacc[i], 0, 0, 0);
+        if constexpr (LIN)
+          hacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pkf, va[i], hacc[i], 0, 0, 0);
+      }
+      if (G + 1 < 4) {
+#pragma unroll
+        for (int i = 0; i < DT; ++i) va[i] = vn[i];
       }
     }
   }

@@ -14,6 +14,9 @@
 //
 // Everything that decides the mask is float64, so the selection is the one a
 // float64 evaluation of the definition gives, up to summation order.
+#include <algorithm>
+#include <mutex>
+
 #include "internal.h"
 
 namespace sparge {
@@ -22,16 +25,23 @@ namespace {
 constexpr int kThreads = 256;
 
 // ----------------------------------------------------------------- pooling
-// grid (nblk, B*H); one workgroup per block of `block` rows.
+// One workgroup per block of Q (blockIdx.x < nq) or K (the rest); grid.y =
+// B*H. Thread t owns 16-byte column chunk t % CH and rows t / CH + RSTEP*i.
 template <int D>
 __global__ __launch_bounds__(kThreads) void pool_mean_kernel(
-    const uint16_t* __restrict__ x, double* __restrict__ out, int N, int block,
-    int nblk) {
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, double* __restrict__ qbar,
+    double* __restrict__ kbar, int N, int block_q, int block_k, int nq, int nk) {
   constexpr int CH = D / 8;              // 16-byte chunks per row
   constexpr int RSTEP = kThreads / CH;   // rows handled per pass
   __shared__ double red[kThreads][9];    // +1 pad against bank conflicts
 
-  const int bh = blockIdx.y, blk = blockIdx.x, t = threadIdx.x;
+  const bool isq = (int)blockIdx.x < nq;
+  const int blk = isq ? blockIdx.x : blockIdx.x - nq;
+  const int block = isq ? block_q : block_k;
+  const int nblk = isq ? nq : nk;
+  const uint16_t* x = isq ? q : k;
+  double* out = isq ? qbar : kbar;
+  const int bh = blockIdx.y, t = threadIdx.x;
   const int c = t % CH, r0 = t / CH;
   const int start = blk * block;
   const int rows = min(block, N - start);
@@ -41,9 +51,17 @@ __global__ __launch_bounds__(kThreads) void pool_mean_kernel(
   double acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.0;
-  for (int r = r0; r < rows; r += RSTEP) {
-    const uint4 w = src[(size_t)r * CH];
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  // at most 128 rows per block: up to 8 (D=128) or 4 (D=64) loads per thread
+  constexpr int MAXIT = 128 / RSTEP;
+  uint4 w[MAXIT];
+#pragma unroll
+  for (int i = 0; i < MAXIT; ++i) {
+    const int r = r0 + RSTEP * i;
+    w[i] = r < rows ? src[(size_t)r * CH] : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < MAXIT; ++i) {
+    const uint32_t ws[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       acc[2 * e] += (double)bf16_lo(ws[e]);
@@ -62,61 +80,66 @@ __global__ __launch_bounds__(kThreads) void pool_mean_kernel(
 }
 
 // ------------------------------------------------------------ block scores
-// s[bh][i][j] = scale * sum_c qbar[bh][i][c] * kbar[bh][j][c]
-// grid (ceil(n_k/64), ceil(n_q/32), B*H); 256 threads, 2x4 outputs each.
-constexpr int LQ = 32, LK = 64, LC = 16;
+// s[bh][i][j] = scale * sum_c qbar[bh][i][c] * kbar[bh][j][c], float64 on the
+// matrix cores (v_mfma_f64_16x16x4_f64: lane l supplies A[l&15][l>>4] and
+// B[l>>4][l&15] and holds D[4e + (l>>4)][l&15], e = 0..3). One wave per
+// 32 x 32 output tile (2 x 2 MFMA tiles); each lane's 16-byte loads of Qbar and
+// Kbar rows feed two k-steps (the same c order on both sides). Rows and
+// columns past n_q / n_k read a valid row and are not stored.
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 template <int D>
 __global__ __launch_bounds__(kThreads) void block_logits_kernel(
     const double* __restrict__ qbar, const double* __restrict__ kbar,
-    double* __restrict__ s, int n_q, int n_k, double scale) {
-  __shared__ double qs[LQ][LC + 1];
-  __shared__ double ks[LK][LC + 1];
-  const int bh = blockIdx.z, i0 = blockIdx.y * LQ, j0 = blockIdx.x * LK;
-  const int t = threadIdx.x, ty = t / 16, tx = t % 16;
-  const double* qh = qbar + (size_t)bh * n_q * D;
-  const double* kh = kbar + (size_t)bh * n_k * D;
-  double acc[2][4] = {};
-  for (int c0 = 0; c0 < D; c0 += LC) {
-    for (int u = t; u < LQ * LC; u += kThreads) {
-      const int r = u / LC, cc = u % LC;
-      qs[r][cc] = (i0 + r < n_q) ? qh[(size_t)(i0 + r) * D + c0 + cc] : 0.0;
-    }
-    for (int u = t; u < LK * LC; u += kThreads) {
-      const int r = u / LC, cc = u % LC;
-      ks[r][cc] = (j0 + r < n_k) ? kh[(size_t)(j0 + r) * D + c0 + cc] : 0.0;
-    }
-    __syncthreads();
+    double* __restrict__ s, int n_q, int n_k, int tq, int tk, int tiles, double scale) {
+  const int lane = threadIdx.x & 63;
+  const int tile = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (tile >= tiles) return;
+  const int bh = tile / (tq * tk), rem = tile % (tq * tk);
+  const int i0 = (rem / tk) * 32, j0 = (rem % tk) * 32;
+  const int r = lane & 15, g = lane >> 4;
+  const double* qa = qbar + ((size_t)bh * n_q + min(i0 + r, n_q - 1)) * D + 2 * g;
+  const double* qb = qbar + ((size_t)bh * n_q + min(i0 + 16 + r, n_q - 1)) * D + 2 * g;
+  const double* ka = kbar + ((size_t)bh * n_k + min(j0 + r, n_k - 1)) * D + 2 * g;
+  const double* kb = kbar + ((size_t)bh * n_k + min(j0 + 16 + r, n_k - 1)) * D + 2 * g;
+  f64x4 acc[2][2];
 #pragma unroll
-    for (int cc = 0; cc < LC; ++cc) {
-      const double a0 = qs[2 * ty][cc], a1 = qs[2 * ty + 1][cc];
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const double b = ks[tx + 16 * u][cc];
-        acc[0][u] = fma(a0, b, acc[0][u]);
-        acc[1][u] = fma(a1, b, acc[1][u]);
+    for (int b = 0; b < 2; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll 4
+  for (int c0 = 0; c0 < D; c0 += 8) {
+    const double2 xa = *reinterpret_cast<const double2*>(qa + c0);
+    const double2 xb = *reinterpret_cast<const double2*>(qb + c0);
+    const double2 ya = *reinterpret_cast<const double2*>(ka + c0);
+    const double2 yb = *reinterpret_cast<const double2*>(kb + c0);
+    acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(xa.x, ya.x, acc[0][0], 0, 0, 0);
+    acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(xa.x, yb.x, acc[0][1], 0, 0, 0);
+    acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(xb.x, ya.x, acc[1][0], 0, 0, 0);
+    acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(xb.x, yb.x, acc[1][1], 0, 0, 0);
+    acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(xa.y, ya.y, acc[0][0], 0, 0, 0);
+    acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(xa.y, yb.y, acc[0][1], 0, 0, 0);
+    acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(xb.y, ya.y, acc[1][0], 0, 0, 0);
+    acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(xb.y, yb.y, acc[1][1], 0, 0, 0);
+  }
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = i0 + 16 * a + 4 * e + g, j = j0 + 16 * b + r;
+        if (i < n_q && j < n_k) s[((size_t)bh * n_q + i) * n_k + j] = scale * acc[a][b][e];
       }
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int rr = 0; rr < 2; ++rr) {
-    const int i = i0 + 2 * ty + rr;
-    if (i >= n_q) continue;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int j = j0 + tx + 16 * u;
-      if (j < n_k) s[((size_t)bh * n_q + i) * n_k + j] = scale * acc[rr][u];
-    }
-  }
 }
 
-// ------------------------------------------------- workgroup scan helpers
+// ------------------------------------------------------- wave-level helpers
 __device__ __forceinline__ double wave_max(double v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o));
   return v;
 }
-__device__ __forceinline__ double wave_sum(double v) {
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
   return v;
@@ -131,153 +154,199 @@ __device__ __forceinline__ T wave_incl_scan(T v, int lane) {
   }
   return v;
 }
-
-// Exclusive scan of one value per thread over the 256-thread workgroup.
-template <typename T>
-__device__ __forceinline__ T block_excl_scan(T v, T* wtot) {
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const T incl = wave_incl_scan(v, lane);
-  if (lane == 63) wtot[w] = incl;
-  __syncthreads();
-  T base = 0;
-  for (int u = 0; u < w; ++u) base += wtot[u];
-  __syncthreads();
-  return base + incl - v;
+// make this wave's LDS writes visible to its other lanes
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // ----------------------------------------------------------- selection
-// One workgroup per query-block row. Dynamic LDS: sv[npad] doubles,
-// si[npad] ints, bits[words] uint32.
+// LDS bytes one wave of the selection kernel needs for npad sorted entries
+__host__ __device__ constexpr size_t select_lds_bytes(int npad) {
+  return (((size_t)npad * (2 * sizeof(double) + sizeof(uint16_t)) + 128 * sizeof(uint32_t)) + 15) &
+         ~(size_t)15;
+}
+
+// One wave per query-block row (rows_per_wg waves per workgroup, each with
+// its own LDS region: sv[npad] doubles (scores, sorted in place), ev[npad]
+// doubles (exp(s - max) by original index), si[npad] uint16, wb[words]
+// uint32).
+// Every step is wave-local, so the 45-66 stages of the bitonic sort need no
+// workgroup barrier.
+template <int NPAD>
 __global__ __launch_bounds__(kThreads) void hybrid_select_kernel(
-    const double* __restrict__ s, int n_k, int npad, int words, int K_k,
+    const double* __restrict__ s, int rows, int n_k, int words, int K_k,
     int keep_all, double p, uint32_t* __restrict__ bits_out,
     int32_t* __restrict__ idx_out, int32_t* __restrict__ cnt_out) {
   extern __shared__ __align__(16) unsigned char smem[];
-  double* sv = reinterpret_cast<double*>(smem);
-  int* si = reinterpret_cast<int*>(sv + npad);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int npad = NPAD;
+  const size_t per_wave = select_lds_bytes(npad);
+  unsigned char* base = smem + wave * per_wave;
+  double* sv = reinterpret_cast<double*>(base);
+  double* ev = sv + npad;
+  uint16_t* si = reinterpret_cast<uint16_t*>(ev + npad);
   uint32_t* wb = reinterpret_cast<uint32_t*>(si + npad);
-  __shared__ double dred[4];
-  __shared__ int ired[4];
-  __shared__ int first_hit;
-
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const size_t row = blockIdx.x;
+  const size_t row = (size_t)blockIdx.x * (blockDim.x >> 6) + wave;
+  if (row >= (size_t)rows) return;  // whole wave leaves together
   const double* srow = s + row * (size_t)n_k;
 
-  // 1. load scores, padding with -inf past n_k; row maximum
+  // 1. load scores, padding with -inf past n_k; row maximum and exp sum
   double mx = -INFINITY;
-  for (int j = t; j < npad; j += kThreads) {
+  for (int j = lane; j < npad; j += 64) {
     const double v = j < n_k ? srow[j] : -INFINITY;
     sv[j] = v;
-    si[j] = j;
+    si[j] = (uint16_t)j;
     mx = fmax(mx, v);
   }
-  if (t < words) wb[t] = 0u;
-  if (t == 0) first_hit = INT32_MAX;
+  for (int w = lane; w < words; w += 64) wb[w] = 0u;
   mx = wave_max(mx);
-  if (lane == 0) dred[w] = mx;
-  __syncthreads();
-  mx = fmax(fmax(dred[0], dred[1]), fmax(dred[2], dred[3]));
-  __syncthreads();
-
-  // 2. softmax normaliser
   double tot = 0.0;
-  for (int j = t; j < n_k; j += kThreads) tot += exp(sv[j] - mx);
+  for (int j = lane; j < n_k; j += 64) {
+    const double e = exp(sv[j] - mx);  // this lane wrote sv[j] itself
+    ev[j] = e;
+    tot += e;
+  }
   tot = wave_sum(tot);
-  if (lane == 0) dred[w] = tot;
-  __syncthreads();
-  tot = (dred[0] + dred[1]) + (dred[2] + dred[3]);
+  wave_lds_sync();
 
-  // 3. bitonic sort: position 0 = highest score, equal scores lower index
+  // 2. bitonic sort: position 0 = highest score, equal scores lower index
   //    first. All (score, index) pairs are distinct, so the order is total.
-  for (int kk = 2; kk <= npad; kk <<= 1) {
+  //    Each stage issues all of a lane's reads before any compare.
+  constexpr int PAIRS = NPAD / 2, C = PAIRS >= 64 ? PAIRS / 64 : 1;
+#pragma unroll 1
+  for (int kk = 2; kk <= NPAD; kk <<= 1) {
+#pragma unroll 1
     for (int jj = kk >> 1; jj > 0; jj >>= 1) {
-      for (int pi = t; pi < (npad >> 1); pi += kThreads) {
-        const int i = 2 * pi - (pi & (jj - 1));
-        const int l = i + jj;
-        const double a = sv[i], b = sv[l];
-        const int ia = si[i], ib = si[l];
-        const bool l_first = (b > a) || (b == a && ib < ia);
-        const bool up = (i & kk) == 0;
-        if (l_first == up) {
-          sv[i] = b; sv[l] = a;
-          si[i] = ib; si[l] = ia;
+      double a[C], b[C];
+      int ia[C], ib[C], ii[C];
+#pragma unroll
+      for (int u = 0; u < C; ++u) {
+        const int pi = lane + 64 * u;
+        ii[u] = 2 * pi - (pi & (jj - 1));
+        if (pi < PAIRS) {
+          a[u] = sv[ii[u]];
+          b[u] = sv[ii[u] + jj];
+          ia[u] = si[ii[u]];
+          ib[u] = si[ii[u] + jj];
         }
       }
-      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < C; ++u) {
+        const int pi = lane + 64 * u, i = ii[u];
+        if (pi < PAIRS) {
+          const bool l_first = (b[u] > a[u]) || (b[u] == a[u] && ib[u] < ia[u]);
+          if (l_first == ((i & kk) == 0)) {
+            sv[i] = b[u]; sv[i + jj] = a[u];
+            si[i] = (uint16_t)ib[u]; si[i + jj] = (uint16_t)ia[u];
+          }
+        }
+      }
+      wave_lds_sync();
     }
   }
 
-  // 4. Top-p: cumulative probability in sorted order; first prefix >= p
+  // 3. Top-p: cumulative probability in sorted order; first prefix >= p.
+  //    Lane L owns sorted positions [L*per, (L+1)*per).
   int m_p = n_k;
   if (!keep_all) {
     if (p <= 0.0) {
       m_p = 0;
     } else {
-      const int per = npad / kThreads > 0 ? npad / kThreads : 1;
-      const int r0 = t * per;
+      const int per = npad / 64 > 0 ? npad / 64 : 1;
+      const int r0 = lane * per;
       double local = 0.0;
-      for (int r = r0; r < r0 + per && r < n_k; ++r) local += exp(sv[r] - mx) / tot;
-      double base = block_excl_scan(local, dred);
+      for (int r = r0; r < r0 + per && r < n_k; ++r) local += ev[si[r]] / tot;
+      double run = wave_incl_scan(local, lane) - local;
+      int hit = INT32_MAX;
       for (int r = r0; r < r0 + per && r < n_k; ++r) {
-        base += exp(sv[r] - mx) / tot;
-        if (base >= p) { atomicMin(&first_hit, r + 1); break; }
+        run += ev[si[r]] / tot;
+        if (run >= p) { hit = r + 1; break; }
       }
-      __syncthreads();
-      if (first_hit != INT32_MAX) m_p = first_hit;
+      const unsigned long long any = __ballot(hit != INT32_MAX);
+      if (any) m_p = __shfl(hit, __ffsll((long long)any) - 1);
     }
   }
   const int count = max(K_k, m_p);
 
-  // 5. union = first `count` of the order -> bitmask
-  for (int r = t; r < count; r += kThreads) {
+  // 4. union = first `count` of the order -> bitmask
+  for (int r = lane; r < count; r += 64) {
     const int j = si[r];
     if (j < n_k) atomicOr(&wb[j >> 5], 1u << (j & 31));  // (only non-finite scores reach j >= n_k)
   }
-  __syncthreads();
+  wave_lds_sync();
 
-  // 6. emit bitmask, ascending index list and count
-  uint32_t word = t < words ? wb[t] : 0u;
-  if (t < words) bits_out[row * words + t] = word;
-  const int off = block_excl_scan((int)__popc(word), ired);
+  // 5. emit bitmask, ascending index list and count (words <= 128: two per lane)
+  const uint32_t w0 = lane < words ? wb[lane] : 0u;
+  const uint32_t w1 = lane + 64 < words ? wb[lane + 64] : 0u;
+  if (lane < words) bits_out[row * words + lane] = w0;
+  if (lane + 64 < words) bits_out[row * words + lane + 64] = w1;
+  const int c0 = __popc(w0), c1 = __popc(w1);
+  const int e0 = wave_incl_scan(c0, lane) - c0;
+  const int e1 = wave_sum(c0) + wave_incl_scan(c1, lane) - c1;
   int32_t* irow = idx_out + row * (size_t)n_k;
-  int pos = off;
+  uint32_t word = w0;
+  int pos = e0;
   while (word) {
-    const int b = __ffs(word) - 1;
-    irow[pos++] = t * 32 + b;
+    irow[pos++] = lane * 32 + __ffs(word) - 1;
     word &= word - 1;
   }
-  if (t == 0) cnt_out[row] = count;
+  word = w1;
+  pos = e1;
+  while (word) {
+    irow[pos++] = (lane + 64) * 32 + __ffs(word) - 1;
+    word &= word - 1;
+  }
+  if (lane == 0) cnt_out[row] = count;
+}
+
+// up to 4 rows (one per wave) per workgroup within the CU's 160 KiB of LDS;
+// the kernel's dynamic-LDS limit is raised once per instantiation
+template <int NPAD>
+hipError_t launch_select(const MaskLaunch& a, hipStream_t st) {
+  constexpr size_t kLdsMax = 160 * 1024;
+  static std::once_flag lds_once;
+  static hipError_t lds_err = hipSuccess;
+  std::call_once(lds_once, [] {
+    lds_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&hybrid_select_kernel<NPAD>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMax);
+  });
+  if (lds_err != hipSuccess) return lds_err;
+  const size_t per_wave = select_lds_bytes(NPAD);
+  const int waves = (int)std::max<size_t>(1, std::min<size_t>(4, kLdsMax / per_wave));
+  const int rows = a.B * a.H * a.n_q;
+  hipLaunchKernelGGL(hybrid_select_kernel<NPAD>, dim3((rows + waves - 1) / waves),
+                     dim3(64 * waves), per_wave * waves, st, a.logits, rows, a.n_k, a.words,
+                     a.K_k, a.keep_all, a.p, a.bits, a.idx, a.cnt);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_mask(const MaskLaunch& a, hipStream_t st) {
   const int BH = a.B * a.H;
+  const int tq = (a.n_q + 31) / 32, tk = (a.n_k + 31) / 32, tiles = BH * tq * tk;
   if (a.d == 128) {
-    hipLaunchKernelGGL(pool_mean_kernel<128>, dim3(a.n_q, BH), dim3(kThreads), 0, st,
-                       a.q, a.qbar, a.N, a.block_q, a.n_q);
-    hipLaunchKernelGGL(pool_mean_kernel<128>, dim3(a.n_k, BH), dim3(kThreads), 0, st,
-                       a.k, a.kbar, a.N, a.block_k, a.n_k);
-    hipLaunchKernelGGL(block_logits_kernel<128>,
-                       dim3((a.n_k + LK - 1) / LK, (a.n_q + LQ - 1) / LQ, BH),
-                       dim3(kThreads), 0, st, a.qbar, a.kbar, a.logits, a.n_q, a.n_k,
-                       a.scale);
+    hipLaunchKernelGGL(pool_mean_kernel<128>, dim3(a.n_q + a.n_k, BH), dim3(kThreads), 0, st,
+                       a.q, a.k, a.qbar, a.kbar, a.N, a.block_q, a.block_k, a.n_q, a.n_k);
+    hipLaunchKernelGGL(block_logits_kernel<128>, dim3((tiles + 3) / 4), dim3(kThreads), 0, st,
+                       a.qbar, a.kbar, a.logits, a.n_q, a.n_k, tq, tk, tiles, a.scale);
   } else {
-    hipLaunchKernelGGL(pool_mean_kernel<64>, dim3(a.n_q, BH), dim3(kThreads), 0, st,
-                       a.q, a.qbar, a.N, a.block_q, a.n_q);
-    hipLaunchKernelGGL(pool_mean_kernel<64>, dim3(a.n_k, BH), dim3(kThreads), 0, st,
-                       a.k, a.kbar, a.N, a.block_k, a.n_k);
-    hipLaunchKernelGGL(block_logits_kernel<64>,
-                       dim3((a.n_k + LK - 1) / LK, (a.n_q + LQ - 1) / LQ, BH),
-                       dim3(kThreads), 0, st, a.qbar, a.kbar, a.logits, a.n_q, a.n_k,
-                       a.scale);
+    hipLaunchKernelGGL(pool_mean_kernel<64>, dim3(a.n_q + a.n_k, BH), dim3(kThreads), 0, st,
+                       a.q, a.k, a.qbar, a.kbar, a.N, a.block_q, a.block_k, a.n_q, a.n_k);
+    hipLaunchKernelGGL(block_logits_kernel<64>, dim3((tiles + 3) / 4), dim3(kThreads), 0, st,
+                       a.qbar, a.kbar, a.logits, a.n_q, a.n_k, tq, tk, tiles, a.scale);
   }
-  const size_t lds = (size_t)a.npad * (sizeof(double) + sizeof(int)) +
-                     (size_t)a.words * sizeof(uint32_t);
-  hipLaunchKernelGGL(hybrid_select_kernel, dim3(BH * a.n_q), dim3(kThreads), lds, st,
-                     a.logits, a.n_k, a.npad, a.words, a.K_k, a.keep_all, a.p, a.bits,
-                     a.idx, a.cnt);
+  switch (a.npad) {
+    case 64: return launch_select<64>(a, st);
+    case 128: return launch_select<128>(a, st);
+    case 256: return launch_select<256>(a, st);
+    case 512: return launch_select<512>(a, st);
+    case 1024: return launch_select<1024>(a, st);
+    case 2048: return launch_select<2048>(a, st);
+    default: return launch_select<4096>(a, st);
+  }
   return hipGetLastError();
 }
 

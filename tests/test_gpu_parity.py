@@ -57,6 +57,33 @@ def test_mask_matches_oracle(name):
           flush=True)
 
 
+@pytest.mark.parametrize("B,H,N,d,bq,k_frac,p_mass", [
+    (1, 2, 5000, 128, 128, 0.1, 0.5),      # n_k 79   -> sort width 128
+    (2, 1, 12345, 64, 64, 0.02, 0.95),     # n_k 193  -> 256
+    (1, 1, 60000, 64, 128, 0.05, 0.0),     # n_k 938  -> 1024, Top-k alone
+    (1, 1, 200000, 64, 128, 0.01, 0.7),    # n_k 3125 -> 4096 (the largest supported width)
+    (1, 3, 777, 128, 64, 1.0, 0.9),        # k = 100% keeps everything
+    (1, 2, 3000, 64, 64, 0.2, 1.0)])       # p >= 1 keeps everything
+def test_mask_matches_oracle_across_sort_widths(B, H, N, d, bq, k_frac, p_mass):
+    rng = np.random.default_rng(N)
+    from block_sparse_attention_softmax_amd.workloads import f64_to_bf16_bits
+    # a smooth trend along the sequence makes the rows far from uniform
+    trend = np.sin(np.arange(N) / 700.0)[None, None, :, None] * rng.standard_normal(d)
+    Q, K = (f64_to_bf16_bits(rng.standard_normal((B, H, N, d)) + 3 * trend) for _ in range(2))
+    scale = S.default_scale(d)
+    print(f"\n[mask] B={B} H={H} N={N} d={d} bq={bq} k={k_frac} p={p_mass}", flush=True)
+    bits, idx, cnt, logits = S.sparge_mask_predict(to_gpu(Q), to_gpu(K), bq, 64, k_frac, p_mass,
+                                                   scale, return_logits=True)
+    torch.cuda.synchronize()
+    n_k = -(-N // 64)
+    kept = gpu_bits_to_bool(bits, n_k)
+    check_index_list(kept, idx.cpu().numpy(), cnt.cpu().numpy())
+    m = O.predict_mask(Q, K, bq, 64, k_frac, p_mass, scale)
+    np.testing.assert_allclose(logits.cpu().numpy(), m.logits, rtol=1e-12, atol=1e-12)
+    ties, differ = compare_masks(m, kept, k_frac, p_mass)
+    print(f"[mask] kept {kept.mean():.4f} near-tie rows {ties} differing {differ}", flush=True)
+
+
 @pytest.mark.parametrize("k_frac", [0.10, 0.05])
 def test_mask_topk_only_operating_points(k_frac):
     """p = 0 (Top-k alone): the 90% and 95% block-sparsity points on wan1.3b inputs."""
