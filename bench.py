@@ -231,7 +231,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(),
-                     "kernel": "sparse_attn_fwd_kernel<128,128,false>",
+                     "kernel": "sparse_attn_fwd_kernel<128,128>",
                      "flops_per_launch": kf},
         "operating_points": points,
         "sparse_linear": linear,

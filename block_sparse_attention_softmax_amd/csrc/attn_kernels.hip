@@ -13,14 +13,16 @@
 // the MFMA output layout, so row maxima and sums need only one exchange
 // between the two half-waves, and the rescaling of O uses the lane's own
 // factor. The P^T accumulator registers are fed back as the B operand of the
-// second product unchanged; V is pre-packed once per call (vt_pack_kernel)
+// second product unchanged; V is pre-packed once per call (pack_kernel)
 // into key-contiguous tiles in the key order those registers imply, so both
 // MFMA A operands are plain 16-byte LDS reads.
 //
-// K_j and packed V_j tiles are copied global -> LDS by direct-to-LDS loads,
-// double-buffered: the copies of block j+1 are issued right after the
-// barrier that opens block j and overlap all of block j's work.
+// K_j and packed V_j tiles are copied global -> LDS by direct-to-LDS loads
+// (no register round trip), double-buffered so the copies overlap the
+// products of earlier blocks.
 #include "internal.h"
+
+#include <type_traits>
 
 namespace sparge {
 namespace {
@@ -229,21 +231,300 @@ __global__ __launch_bounds__(256) void linear_reduce_kernel(const float* __restr
 }
 
 // ------------------------------------------------------ attention kernel
-// LIN adds the linear branch over the dropped blocks: each kept block also
+// Software-pipelined over the listed blocks: the S^T product of block it+1
+// is issued while the softmax and the P V product of block it run, so the
+// matrix cores have independent work during the softmax. K tiles and packed
+// V^T tiles are double-buffered separately, one block apart: during step
+// `it` K buffer (it+1)&1 holds K of block it+1 and V buffer it&1 holds V^T
+// of block it; the copies issued during step `it` (K of block it+2, V^T of
+// block it+1) fill the buffers that step it-1 finished with. They are
+// spread one per k-step over the S^T product instead of issued together,
+// so the waves of a CU do not queue behind each other's copies.
+template <int D, int BQ>
+__global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void sparse_attn_fwd_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ vt, const int32_t* __restrict__ kv_idx,
+    const int32_t* __restrict__ kv_cnt, uint16_t* __restrict__ o, int N, int n_q, int n_k,
+    int total, float c) {
+  constexpr int NW = BQ / 32;
+  using T = Tile<D, false>;
+  constexpr int LOADS = BK * D / 8 / 64 / NW;
+  constexpr int DT = D / 32;
+  constexpr int KSTEPS = D / 16;
+
+  __shared__ __align__(16) unsigned char smem[4 * T::BYTES];  // K0 K1 V0 V1
+  unsigned char* const kbuf = smem;
+  unsigned char* const vbuf = smem + 2 * T::BYTES;
+
+  const int tile = xcd_remap(blockIdx.x, total);
+  const int bh = tile / n_q, qi = tile % n_q;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int h2 = lane >> 5, l32 = lane & 31;
+  const size_t head = (size_t)bh * N * D;
+
+  const int qrow = qi * BQ + wave * 32 + l32;
+  bf16x8 qf[KSTEPS];
+  {
+    const uint16_t* qp = q + head + (size_t)min(qrow, N - 1) * D + 8 * h2;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
+  }
+
+  const int count = min(max(kv_cnt[tile], 0), n_k);
+  const int32_t* ids = kv_idx + (size_t)tile * n_k;
+  const uint16_t* kh = k + head;
+  const size_t vtile = (size_t)D * BK;
+  const uint16_t* vth = vt + (size_t)bh * n_k * vtile;
+  auto jat = [&](int i) { return min(max(ids[i], 0), n_k - 1); };
+
+  constexpr int KROWS_U = 64 * NW / T::KCPR, VROWS_U = 64 * NW / T::VCPR;
+  constexpr bool KCONST = KROWS_U % T::KCPR == 0, VCONST = VROWS_U % (2 * T::VCPR) == 0;
+  uint32_t kbyte[KCONST ? 1 : LOADS], vbyte[VCONST ? 1 : LOADS];
+#pragma unroll
+  for (int u = 0; u < (KCONST ? 1 : LOADS); ++u) {
+    const int p = 64 * (u * NW + wave) + lane;
+    const int kr = p / T::KCPR;
+    kbyte[u] = (uint32_t)(kr * D + T::kchunk(kr, p % T::KCPR) * 8) * 2u;
+  }
+#pragma unroll
+  for (int u = 0; u < (VCONST ? 1 : LOADS); ++u) {
+    const int p = 64 * (u * NW + wave) + lane;
+    const int vr = p / T::VCPR;
+    vbyte[u] = (uint32_t)(vr * BK + T::vchunk(vr, p % T::VCPR) * 8) * 2u;
+  }
+  auto kofs = [&](int u) { return KCONST ? kbyte[0] + (uint32_t)(u * KROWS_U * D * 2) : kbyte[u]; };
+  auto vofs = [&](int u) { return VCONST ? vbyte[0] + (uint32_t)(u * VROWS_U * BK * 2) : vbyte[u]; };
+  auto stageK = [&](int j, int b) {
+    unsigned char* kb = kbuf + b * T::BYTES;
+    const int key0 = j * BK;
+    const char* kt = reinterpret_cast<const char*>(kh + (size_t)key0 * D);
+    if (key0 + BK <= N) {
+#pragma unroll
+      for (int u = 0; u < LOADS; ++u) dma16(kt + kofs(u), kb + 1024 * (u * NW + wave));
+    } else {  // short last block: K rows past N repeat row N-1 (their scores are masked)
+#pragma unroll
+      for (int u = 0; u < LOADS; ++u) {
+        const int krow = (64 * (u * NW + wave) + lane) / T::KCPR;
+        const uint32_t shift = (uint32_t)max(key0 + krow - (N - 1), 0) * D * 2u;
+        dma16(kt + (kofs(u) - shift), kb + 1024 * (u * NW + wave));
+      }
+    }
+  };
+  auto stageV = [&](int j, int b) {
+    unsigned char* vb = vbuf + b * T::BYTES;
+    const char* vtt = reinterpret_cast<const char*>(vth + (size_t)j * vtile);
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) dma16(vtt + vofs(u), vb + 1024 * (u * NW + wave));
+  };
+
+  int koff[KSTEPS];
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) koff[s] = l32 * T::KROWB + (T::kchunk(l32, 2 * s + h2) << 4);
+  int voff[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) voff[g] = l32 * T::VROWB + (T::vchunk(l32, 2 * g + h2) << 4);
+
+  // k-steps [S0, S1) of S^T = K Q^T from the K tile at kb
+  auto qk = [&](const unsigned char* kb, floatx16(&st)[2], auto s0_tag, auto s1_tag, auto&& hook) {
+    constexpr int S0 = decltype(s0_tag)::value, S1 = decltype(s1_tag)::value;
+    bf16x8 ka[2] = {lds_read16(kb + koff[S0]), lds_read16(kb + 32 * T::KROWB + koff[S0])};
+#pragma unroll
+    for (int s = S0; s < S1; ++s) {
+      hook(s - S0);
+      bf16x8 kn[2];
+      if (s + 1 < S1) {
+        kn[0] = lds_read16(kb + koff[s + 1]);
+        kn[1] = lds_read16(kb + 32 * T::KROWB + koff[s + 1]);
+      }
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau)
+        st[tau] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[tau], qf[s], st[tau], 0, 0, 0);
+      if (s + 1 < S1) { ka[0] = kn[0]; ka[1] = kn[1]; }
+    }
+  };
+  using Zero = std::integral_constant<int, 0>;
+  using Half = std::integral_constant<int, KSTEPS / 2>;
+  using Full = std::integral_constant<int, KSTEPS>;
+
+  floatx16 oacc[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[i][r] = 0.0f;
+  float m = -INFINITY, lsum = 0.0f;
+  floatx16 sc[2];  // S^T of the current block
+#pragma unroll
+  for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sc[tau][r] = 0.0f;
+  int jcur = 0;
+
+  if (count > 0) {
+    jcur = jat(0);
+    stageK(jcur, 0);
+    stageV(jcur, 0);
+    if (count > 1) stageK(jat(1), 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    qk(kbuf, sc, Zero{}, Full{}, [](int) {});
+  }
+
+  // one listed block: softmax and P V of block `it` (S^T in sc), and with
+  // NEXT the S^T of block it+1 into sn, interleaved
+  auto step = [&](int it, auto next_tag) {
+    constexpr bool NEXT = decltype(next_tag)::value;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K of it+1 and V^T of it landed
+    __syncthreads();                     // and every wave is done with step it-1's buffers
+    int jn = jcur;
+    // copies for later steps, spread one per k-step over the S^T product of
+    // block it+1: K of block it+2 (a repeat of it+1 when there is none; that
+    // buffer is not read again) and V^T of block it+1
+    const char* ksrc = nullptr;
+    const char* vsrc = nullptr;
+    uint32_t ko[LOADS];
+    if constexpr (NEXT) {
+      jn = jat(it + 1);
+      const int jk = it + 2 < count ? jat(it + 2) : jn;
+      const int key0 = jk * BK;
+      ksrc = reinterpret_cast<const char*>(kh + (size_t)key0 * D);
+      vsrc = reinterpret_cast<const char*>(vth + (size_t)jn * vtile);
+      if (key0 + BK <= N) {
+#pragma unroll
+        for (int u = 0; u < LOADS; ++u) ko[u] = kofs(u);
+      } else {
+#pragma unroll
+        for (int u = 0; u < LOADS; ++u) {
+          const int krow = (64 * (u * NW + wave) + lane) / T::KCPR;
+          ko[u] = kofs(u) - (uint32_t)max(key0 + krow - (N - 1), 0) * D * 2u;
+        }
+      }
+    }
+    unsigned char* kdst = kbuf + (it & 1) * T::BYTES;
+    unsigned char* vdst = vbuf + ((it + 1) & 1) * T::BYTES;
+    constexpr int HALF = KSTEPS / 2;
+    auto kdma = [&](int sl) {
+#pragma unroll
+      for (int u = 0; u < LOADS; ++u)
+        if (u * HALF / LOADS == sl) dma16(ksrc + ko[u], kdst + 1024 * (u * NW + wave));
+    };
+    auto vdma = [&](int sl) {
+#pragma unroll
+      for (int u = 0; u < LOADS; ++u)
+        if (u * HALF / LOADS == sl) dma16(vsrc + vofs(u), vdst + 1024 * (u * NW + wave));
+    };
+    const unsigned char* kn = kbuf + ((it + 1) & 1) * T::BYTES;
+    const unsigned char* vb = vbuf + (it & 1) * T::BYTES;
+
+    const int nvalid = N - jcur * BK;  // keys past N in a short last block get -inf
+    if (nvalid < BK) {
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 32 * tau + 8 * (r >> 2) + 4 * h2 + (r & 3);
+          if (key >= nvalid) sc[tau][r] = -INFINITY;
+        }
+    }
+
+    floatx16 sn[2];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sn[tau][r] = 0.0f;
+    if constexpr (NEXT) qk(kn, sn, Zero{}, Half{}, kdma);
+
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sc[tau][r]);
+    mloc = pair_max(mloc);
+    if (__any((mloc - m) * c > kRescaleLog2)) {
+      const float m_new = fmaxf(m, mloc);
+      const float alpha_r = __builtin_amdgcn_exp2f((m - m_new) * c);
+      m = m_new;
+      lsum *= alpha_r;
+#pragma unroll
+      for (int i = 0; i < DT; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha_r;
+    }
+
+    if constexpr (NEXT) qk(kn, sn, Half{}, Full{}, vdma);
+    const float mc = m * c;
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[tau][r] = __builtin_amdgcn_exp2f(fmaf(sc[tau][r], c, -mc));
+
+    bf16x8 va[DT];
+#pragma unroll
+    for (int i = 0; i < DT; ++i) va[i] = lds_read16(vb + i * 32 * T::VROWB + voff[0]);
+#pragma unroll
+    for (int G = 0; G < 4; ++G) {
+      const int tau = G >> 1, hk = G & 1;
+      const bf16x8 pb = pack_bf16x8(sc[tau], 8 * hk);
+      lsum = row_sum_bf16x8(pb, lsum);
+      bf16x8 vn[DT];
+      if (G + 1 < 4) {
+#pragma unroll
+        for (int i = 0; i < DT; ++i) vn[i] = lds_read16(vb + i * 32 * T::VROWB + voff[G + 1]);
+      }
+#pragma unroll
+      for (int i = 0; i < DT; ++i)
+        oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], pb, oacc[i], 0, 0, 0);
+      if (G + 1 < 4) {
+#pragma unroll
+        for (int i = 0; i < DT; ++i) va[i] = vn[i];
+      }
+    }
+    if constexpr (NEXT) {
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau) sc[tau] = sn[tau];
+      jcur = jn;
+    }
+  };
+  int it = 0;
+  for (; it + 1 < count; ++it) step(it, std::true_type{});
+  if (count > 0) step(it, std::false_type{});
+
+  const float ltot = pair_sum(lsum);
+  const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
+  if (qrow < N) {
+    uint16_t* orow = o + head + (size_t)qrow * D;
+#pragma unroll
+    for (int i = 0; i < DT; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * i + 8 * g + 4 * h2;
+        uint2 pk;
+        pk.x = f32_to_bf16_rne(oacc[i][4 * g + 0] * inv) | (f32_to_bf16_rne(oacc[i][4 * g + 1] * inv) << 16);
+        pk.y = f32_to_bf16_rne(oacc[i][4 * g + 2] * inv) | (f32_to_bf16_rne(oacc[i][4 * g + 3] * inv) << 16);
+        *reinterpret_cast<uint2*>(orow + d0) = pk;
+      }
+  }
+}
+
+// ----------------------------------------- attention + linear branch kernel
+// The block loop of the sparse product with double-buffered K / V^T / phi(K)^T
+// stages (copies of block j+1 issued after the barrier that opens block j),
+// plus the linear branch over the dropped blocks: each kept block also
 // accumulates H_kept += phi(K_j)^T V_j (wave w owns rows 32w..32w+31 of the
 // d x d product, reusing the V^T fragments of the PV product as its B
 // operand) and z_kept += sum phi(K_j); the epilogue forms H_D = H_tot -
 // H_kept, z_D = z_tot - z_kept and O_l = phi(Q) H_D / (phi(Q) . z_D) with a
 // three-term split-bf16 MFMA product (about 16 significant bits per
 // operand), and writes O = O_s + alpha[h] * O_l.
-template <int D, int BQ, bool LIN>
-__global__ __launch_bounds__(BQ * 2, (LIN || (D == 128 && BQ == 64)) ? 1 : 2) void sparse_attn_fwd_kernel(
+template <int D, int BQ>
+__global__ __launch_bounds__(BQ * 2, 1) void sparse_linear_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ vt, const int32_t* __restrict__ kv_idx,
     const int32_t* __restrict__ kv_cnt, uint16_t* __restrict__ o, int H, int N, int n_q,
     int n_k, int total, float c, const float* __restrict__ alpha,
     const uint16_t* __restrict__ phikt, const float* __restrict__ lin_h,
     const float* __restrict__ lin_z) {
+  constexpr bool LIN = true;
   constexpr int NW = BQ / 32;               // waves, 32 query rows each
   using T = Tile<D, LIN>;
   constexpr int LOADS = BK * D / 8 / 64 / NW;  // 16-byte DMA loads per lane per tile
@@ -555,10 +836,15 @@ hipError_t launch_sparse(const AttnLaunch& a, hipStream_t s, AttnPhase phase) {
                          a.part_z, a.lin_h, a.lin_z);
     }
   }
-  if (phase != kPackOnly)
-    hipLaunchKernelGGL((sparse_attn_fwd_kernel<D, BQ, LIN>), dim3(total), dim3(BQ * 2), 0, s,
-                       a.q, a.k, a.vt, a.idx, a.cnt, a.o, a.H, a.N, a.n_q, a.n_k, total, c,
-                       a.alpha, a.phikt, a.lin_h, a.lin_z);
+  if (phase != kPackOnly) {
+    if constexpr (LIN)
+      hipLaunchKernelGGL((sparse_linear_attn_kernel<D, BQ>), dim3(total), dim3(BQ * 2), 0, s,
+                         a.q, a.k, a.vt, a.idx, a.cnt, a.o, a.H, a.N, a.n_q, a.n_k, total, c,
+                         a.alpha, a.phikt, a.lin_h, a.lin_z);
+    else
+      hipLaunchKernelGGL((sparse_attn_fwd_kernel<D, BQ>), dim3(total), dim3(BQ * 2), 0, s,
+                         a.q, a.k, a.vt, a.idx, a.cnt, a.o, a.N, a.n_q, a.n_k, total, c);
+  }
   return hipGetLastError();
 }
 
