@@ -124,6 +124,13 @@ __device__ __forceinline__ void dma16(const void* src, void* lds) {
   __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
 }
 
+// two floats -> two bf16 (round to nearest even) in one dword, low half first
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 __device__ __forceinline__ bf16x8 pack_bf16x8(const floatx16& x, int base) {
   bf16x8 r;
 #pragma unroll
@@ -499,8 +506,8 @@ __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void sparse
       for (int g = 0; g < 4; ++g) {
         const int d0 = 32 * i + 8 * g + 4 * h2;
         uint2 pk;
-        pk.x = f32_to_bf16_rne(oacc[i][4 * g + 0] * inv) | (f32_to_bf16_rne(oacc[i][4 * g + 1] * inv) << 16);
-        pk.y = f32_to_bf16_rne(oacc[i][4 * g + 2] * inv) | (f32_to_bf16_rne(oacc[i][4 * g + 3] * inv) << 16);
+        pk.x = pack2_bf16(oacc[i][4 * g + 0] * inv, oacc[i][4 * g + 1] * inv);
+        pk.y = pack2_bf16(oacc[i][4 * g + 2] * inv, oacc[i][4 * g + 3] * inv);
         *reinterpret_cast<uint2*>(orow + d0) = pk;
       }
   }
@@ -814,8 +821,8 @@ __global__ __launch_bounds__(BQ * 2, 1) void sparse_linear_attn_kernel(
           if constexpr (LIN) y[e] = fmaf(hacc[i][4 * g + e], lin_scale, y[e]);
         }
         uint2 pk;
-        pk.x = f32_to_bf16_rne(y[0]) | (f32_to_bf16_rne(y[1]) << 16);
-        pk.y = f32_to_bf16_rne(y[2]) | (f32_to_bf16_rne(y[3]) << 16);
+        pk.x = pack2_bf16(y[0], y[1]);
+        pk.y = pack2_bf16(y[2], y[3]);
         *reinterpret_cast<uint2*>(orow + d0) = pk;
       }
   }
