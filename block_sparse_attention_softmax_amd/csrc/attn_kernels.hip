@@ -100,9 +100,8 @@ __global__ __launch_bounds__(2 * D) void pack_kernel(const uint16_t* __restrict_
 // logical chunk) cover all 64 banks: K rows are 256 bytes, so chunk c of row
 // r goes to c ^ (r mod 16); V^T rows are 128 bytes, two per bank window, so
 // chunk c goes to c ^ ((r / 2) mod 8).
-template <int D, bool LIN>
+template <int D>
 struct Tile {
-  static constexpr int STAGE = (LIN ? 3 : 2) * BK * D * 2;  // K + V^T (+ phi(K)^T)
   static constexpr int KROWB = D * 2;   // bytes per K row
   static constexpr int KCPR = D / 8;    // 16-byte chunks per K row
   static constexpr int VROWB = BK * 2;  // bytes per V^T row (128)
@@ -247,21 +246,35 @@ __global__ __launch_bounds__(256) void linear_reduce_kernel(const float* __restr
 // block it+1) fill the buffers that step it-1 finished with. They are
 // spread one per k-step over the S^T product instead of issued together,
 // so the waves of a CU do not queue behind each other's copies.
-template <int D, int BQ>
-__global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void sparse_attn_fwd_kernel(
+//
+// LIN adds the linear branch over the dropped blocks: each kept block also
+// accumulates H_kept += phi(K_j)^T V_j (wave w owns rows 32w..32w+31 of the
+// d x d product, reusing the V^T fragments of the P V product as its B
+// operand; phi(K)^T tiles are staged beside the V^T tiles) and z_kept +=
+// sum phi(K_j); the epilogue forms H_D = H_tot - H_kept, z_D = z_tot -
+// z_kept and O_l = phi(Q) H_D / (phi(Q) . z_D) with a three-term split-bf16
+// MFMA product (about 16 significant bits per operand), and writes
+// O = O_s + alpha[h] * O_l.
+template <int D, int BQ, bool LIN>
+__global__ __launch_bounds__(BQ * 2, (LIN || (D == 128 && BQ == 64)) ? 1 : 2) void sparse_attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ vt, const int32_t* __restrict__ kv_idx,
-    const int32_t* __restrict__ kv_cnt, uint16_t* __restrict__ o, int N, int n_q, int n_k,
-    int total, float c) {
+    const int32_t* __restrict__ kv_cnt, uint16_t* __restrict__ o, int H, int N, int n_q,
+    int n_k, int total, float c, const float* __restrict__ alpha,
+    const uint16_t* __restrict__ phikt, const float* __restrict__ lin_h,
+    const float* __restrict__ lin_z) {
   constexpr int NW = BQ / 32;
-  using T = Tile<D, false>;
+  using T = Tile<D>;
   constexpr int LOADS = BK * D / 8 / 64 / NW;
   constexpr int DT = D / 32;
   constexpr int KSTEPS = D / 16;
+  static_assert(!LIN || NW == DT, "the linear branch needs one wave per 32 rows of d");
 
-  __shared__ __align__(16) unsigned char smem[4 * T::BYTES];  // K0 K1 V0 V1
+  // K0 K1 V0 V1 (LIN: phi(K)^T 0, 1); buffer b of block i is (i + ...) & 1 as below
+  __shared__ __align__(16) unsigned char smem[(LIN ? 6 : 4) * T::BYTES];
   unsigned char* const kbuf = smem;
   unsigned char* const vbuf = smem + 2 * T::BYTES;
+  unsigned char* const pbuf = smem + 4 * T::BYTES;
 
   const int tile = xcd_remap(blockIdx.x, total);
   const int bh = tile / n_q, qi = tile % n_q;
@@ -283,6 +296,7 @@ __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void sparse
   const uint16_t* kh = k + head;
   const size_t vtile = (size_t)D * BK;
   const uint16_t* vth = vt + (size_t)bh * n_k * vtile;
+  const uint16_t* pkh = LIN ? phikt + (size_t)bh * n_k * vtile : nullptr;
   auto jat = [&](int i) { return min(max(ids[i], 0), n_k - 1); };
 
   constexpr int KROWS_U = 64 * NW / T::KCPR, VROWS_U = 64 * NW / T::VCPR;
@@ -318,11 +332,15 @@ __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void sparse
       }
     }
   };
-  auto stageV = [&](int j, int b) {
-    unsigned char* vb = vbuf + b * T::BYTES;
+  auto stageV = [&](int j, int b) {  // V^T tile (LIN: and the phi(K)^T tile)
     const char* vtt = reinterpret_cast<const char*>(vth + (size_t)j * vtile);
 #pragma unroll
-    for (int u = 0; u < LOADS; ++u) dma16(vtt + vofs(u), vb + 1024 * (u * NW + wave));
+    for (int u = 0; u < LOADS; ++u) dma16(vtt + vofs(u), vbuf + b * T::BYTES + 1024 * (u * NW + wave));
+    if constexpr (LIN) {
+      const char* ptt = reinterpret_cast<const char*>(pkh + (size_t)j * vtile);
+#pragma unroll
+      for (int u = 0; u < LOADS; ++u) dma16(ptt + vofs(u), pbuf + b * T::BYTES + 1024 * (u * NW + wave));
+    }
   };
 
   int koff[KSTEPS];
@@ -360,6 +378,14 @@ __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void sparse
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[i][r] = 0.0f;
   float m = -INFINITY, lsum = 0.0f;
+  floatx16 hacc[LIN ? DT : 1];  // H_kept rows 32*wave.. (LIN)
+  float zk = 0.0f;              // z_kept entry 32*wave + l32 (LIN; split over the half-waves)
+  if constexpr (LIN) {
+#pragma unroll
+    for (int i = 0; i < DT; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) hacc[i][r] = 0.0f;
+  }
   floatx16 sc[2];  // S^T of the current block
 #pragma unroll
   for (int tau = 0; tau < 2; ++tau)
@@ -389,6 +415,7 @@ __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void sparse
     // buffer is not read again) and V^T of block it+1
     const char* ksrc = nullptr;
     const char* vsrc = nullptr;
+    const char* psrc = nullptr;
     uint32_t ko[LOADS];
     if constexpr (NEXT) {
       jn = jat(it + 1);
@@ -396,6 +423,7 @@ __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void sparse
       const int key0 = jk * BK;
       ksrc = reinterpret_cast<const char*>(kh + (size_t)key0 * D);
       vsrc = reinterpret_cast<const char*>(vth + (size_t)jn * vtile);
+      if constexpr (LIN) psrc = reinterpret_cast<const char*>(pkh + (size_t)jn * vtile);
       if (key0 + BK <= N) {
 #pragma unroll
         for (int u = 0; u < LOADS; ++u) ko[u] = kofs(u);
@@ -409,6 +437,7 @@ __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void sparse
     }
     unsigned char* kdst = kbuf + (it & 1) * T::BYTES;
     unsigned char* vdst = vbuf + ((it + 1) & 1) * T::BYTES;
+    unsigned char* pdst = pbuf + ((it + 1) & 1) * T::BYTES;
     constexpr int HALF = KSTEPS / 2;
     auto kdma = [&](int sl) {
 #pragma unroll
@@ -418,10 +447,14 @@ __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void sparse
     auto vdma = [&](int sl) {
 #pragma unroll
       for (int u = 0; u < LOADS; ++u)
-        if (u * HALF / LOADS == sl) dma16(vsrc + vofs(u), vdst + 1024 * (u * NW + wave));
+        if (u * HALF / LOADS == sl) {
+          dma16(vsrc + vofs(u), vdst + 1024 * (u * NW + wave));
+          if constexpr (LIN) dma16(psrc + vofs(u), pdst + 1024 * (u * NW + wave));
+        }
     };
     const unsigned char* kn = kbuf + ((it + 1) & 1) * T::BYTES;
     const unsigned char* vb = vbuf + (it & 1) * T::BYTES;
+    const unsigned char* pb_ = pbuf + (it & 1) * T::BYTES;
 
     const int nvalid = N - jcur * BK;  // keys past N in a short last block get -inf
     if (nvalid < BK) {
@@ -473,14 +506,22 @@ __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void sparse
       const int tau = G >> 1, hk = G & 1;
       const bf16x8 pb = pack_bf16x8(sc[tau], 8 * hk);
       lsum = row_sum_bf16x8(pb, lsum);
-      bf16x8 vn[DT];
+      bf16x8 vn[DT], pkf;
       if (G + 1 < 4) {
 #pragma unroll
         for (int i = 0; i < DT; ++i) vn[i] = lds_read16(vb + i * 32 * T::VROWB + voff[G + 1]);
       }
+      if constexpr (LIN) {  // phi(K_j)^T rows 32*wave.., keys of k-step G
+        pkf = lds_read16(pb_ + wave * 32 * T::VROWB + voff[G]);
 #pragma unroll
-      for (int i = 0; i < DT; ++i)
+        for (int e = 0; e < 8; ++e) zk += (float)pkf[e];
+      }
+#pragma unroll
+      for (int i = 0; i < DT; ++i) {
         oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], pb, oacc[i], 0, 0, 0);
+        if constexpr (LIN)
+          hacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pkf, va[i], hacc[i], 0, 0, 0);
+      }
       if (G + 1 < 4) {
 #pragma unroll
         for (int i = 0; i < DT; ++i) va[i] = vn[i];
@@ -496,248 +537,6 @@ __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void sparse
   for (; it + 1 < count; ++it) step(it, std::true_type{});
   if (count > 0) step(it, std::false_type{});
 
-  const float ltot = pair_sum(lsum);
-  const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
-  if (qrow < N) {
-    uint16_t* orow = o + head + (size_t)qrow * D;
-#pragma unroll
-    for (int i = 0; i < DT; ++i)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * i + 8 * g + 4 * h2;
-        uint2 pk;
-        pk.x = pack2_bf16(oacc[i][4 * g + 0] * inv, oacc[i][4 * g + 1] * inv);
-        pk.y = pack2_bf16(oacc[i][4 * g + 2] * inv, oacc[i][4 * g + 3] * inv);
-        *reinterpret_cast<uint2*>(orow + d0) = pk;
-      }
-  }
-}
-
-// ----------------------------------------- attention + linear branch kernel
-// The block loop of the sparse product with double-buffered K / V^T / phi(K)^T
-// stages (copies of block j+1 issued after the barrier that opens block j),
-// plus the linear branch over the dropped blocks: each kept block also
-// accumulates H_kept += phi(K_j)^T V_j (wave w owns rows 32w..32w+31 of the
-// d x d product, reusing the V^T fragments of the PV product as its B
-// operand) and z_kept += sum phi(K_j); the epilogue forms H_D = H_tot -
-// H_kept, z_D = z_tot - z_kept and O_l = phi(Q) H_D / (phi(Q) . z_D) with a
-// three-term split-bf16 MFMA product (about 16 significant bits per
-// operand), and writes O = O_s + alpha[h] * O_l.
-template <int D, int BQ>
-__global__ __launch_bounds__(BQ * 2, 1) void sparse_linear_attn_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ vt, const int32_t* __restrict__ kv_idx,
-    const int32_t* __restrict__ kv_cnt, uint16_t* __restrict__ o, int H, int N, int n_q,
-    int n_k, int total, float c, const float* __restrict__ alpha,
-    const uint16_t* __restrict__ phikt, const float* __restrict__ lin_h,
-    const float* __restrict__ lin_z) {
-  constexpr bool LIN = true;
-  constexpr int NW = BQ / 32;               // waves, 32 query rows each
-  using T = Tile<D, LIN>;
-  constexpr int LOADS = BK * D / 8 / 64 / NW;  // 16-byte DMA loads per lane per tile
-  constexpr int DT = D / 32;                // O^T tiles per wave
-  constexpr int KSTEPS = D / 16;            // k-steps of the QK product
-  static_assert(!LIN || NW == DT, "the linear branch needs one wave per 32 rows of d");
-
-  __shared__ __align__(16) unsigned char smem[2 * T::STAGE];
-
-  const int tile = xcd_remap(blockIdx.x, total);
-  const int bh = tile / n_q, qi = tile % n_q;
-  const int t = threadIdx.x, lane = t & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int h2 = lane >> 5, l32 = lane & 31;
-  const size_t head = (size_t)bh * N * D;
-
-  // ---- Q fragments (B operand of S^T = K Q^T): query row, 8 d-values
-  const int qrow = qi * BQ + wave * 32 + l32;
-  bf16x8 qf[KSTEPS];
-  {
-    const uint16_t* qp = q + head + (size_t)min(qrow, N - 1) * D + 8 * h2;
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
-  }
-
-  const int count = min(max(kv_cnt[tile], 0), n_k);
-  const int32_t* ids = kv_idx + (size_t)tile * n_k;
-  const uint16_t* kh = k + head;
-  const size_t vtile = (size_t)D * BK;
-  const uint16_t* vth = vt + (size_t)bh * n_k * vtile;
-  const uint16_t* pkh = LIN ? phikt + (size_t)bh * n_k * vtile : nullptr;
-
-  // ---- DMA staging: wave w, load u fills LDS chunks [64*(u*NW+w), +64),
-  // lane-linear; each lane fetches the global chunk that the swizzle maps
-  // there (the swizzles are involutions). Offsets are loop invariant.
-  // Load u covers rows 64*NW*u/CPR further down the tile; when that step is
-  // a multiple of the swizzle period the lane's chunk is the same for every
-  // u and its source offset is u0's plus a constant (fewer live registers).
-  constexpr int KROWS_U = 64 * NW / T::KCPR, VROWS_U = 64 * NW / T::VCPR;
-  constexpr bool KCONST = KROWS_U % T::KCPR == 0, VCONST = VROWS_U % (2 * T::VCPR) == 0;
-  uint32_t kbyte[KCONST ? 1 : LOADS], vbyte[VCONST ? 1 : LOADS];  // byte offsets in a tile
-#pragma unroll
-  for (int u = 0; u < (KCONST ? 1 : LOADS); ++u) {
-    const int p = 64 * (u * NW + wave) + lane;   // LDS chunk index
-    const int kr = p / T::KCPR;
-    kbyte[u] = (uint32_t)(kr * D + T::kchunk(kr, p % T::KCPR) * 8) * 2u;
-  }
-#pragma unroll
-  for (int u = 0; u < (VCONST ? 1 : LOADS); ++u) {
-    const int p = 64 * (u * NW + wave) + lane;
-    const int vr = p / T::VCPR;
-    vbyte[u] = (uint32_t)(vr * BK + T::vchunk(vr, p % T::VCPR) * 8) * 2u;
-  }
-  auto kofs = [&](int u) { return KCONST ? kbyte[0] + (uint32_t)(u * KROWS_U * D * 2) : kbyte[u]; };
-  auto vofs = [&](int u) { return VCONST ? vbyte[0] + (uint32_t)(u * VROWS_U * BK * 2) : vbyte[u]; };
-  auto stage = [&](int j, int buf) {
-    unsigned char* kb = smem + buf * T::STAGE;
-    unsigned char* vb = kb + T::BYTES;
-    const int key0 = j * BK;
-    const char* kt = reinterpret_cast<const char*>(kh + (size_t)key0 * D);
-    const char* vtt = reinterpret_cast<const char*>(vth + (size_t)j * vtile);
-    const char* ptt = LIN ? reinterpret_cast<const char*>(pkh + (size_t)j * vtile) : nullptr;
-    if (key0 + BK <= N) {
-#pragma unroll
-      for (int u = 0; u < LOADS; ++u) {
-        const int dst = 1024 * (u * NW + wave);
-        dma16(kt + kofs(u), kb + dst);
-        dma16(vtt + vofs(u), vb + dst);
-        if constexpr (LIN) dma16(ptt + vofs(u), vb + T::BYTES + dst);
-      }
-    } else {  // short last block: K rows past N repeat row N-1 (their scores
-              // are masked); the packed tiles are zero there
-#pragma unroll
-      for (int u = 0; u < LOADS; ++u) {
-        const int dst = 1024 * (u * NW + wave);
-        const int krow = (64 * (u * NW + wave) + lane) / T::KCPR;
-        const uint32_t shift = (uint32_t)max(key0 + krow - (N - 1), 0) * D * 2u;
-        dma16(kt + (kofs(u) - shift), kb + dst);
-        dma16(vtt + vofs(u), vb + dst);
-        if constexpr (LIN) dma16(ptt + vofs(u), vb + T::BYTES + dst);
-      }
-    }
-  };
-
-  // ---- per-lane LDS read offsets (loop invariant)
-  int koff[KSTEPS];  // K rows l32 (+32 tau), chunk 2s + h2
-#pragma unroll
-  for (int s = 0; s < KSTEPS; ++s) koff[s] = l32 * T::KROWB + (T::kchunk(l32, 2 * s + h2) << 4);
-  int voff[4];       // V^T rows l32 (+32 i), chunk 2G + h2 (slots 16G + 8h2 .. +8)
-#pragma unroll
-  for (int g = 0; g < 4; ++g) voff[g] = l32 * T::VROWB + (T::vchunk(l32, 2 * g + h2) << 4);
-
-  floatx16 oacc[DT];
-  floatx16 hacc[LIN ? DT : 1];
-#pragma unroll
-  for (int i = 0; i < DT; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[i][r] = 0.0f;
-  if constexpr (LIN) {
-#pragma unroll
-    for (int i = 0; i < DT; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) hacc[i][r] = 0.0f;
-  }
-  float m = -INFINITY, lsum = 0.0f, zk = 0.0f;
-
-  if (count > 0) stage(min(max(ids[0], 0), n_k - 1), 0);
-
-  for (int it = 0; it < count; ++it) {
-    const int buf = it & 1;
-    const int j = min(max(ids[it], 0), n_k - 1);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this lane's DMA for buf landed
-    __syncthreads();                     // every lane's DMA landed; buf^1 is free
-    if (it + 1 < count) stage(min(max(ids[it + 1], 0), n_k - 1), buf ^ 1);
-    const unsigned char* kb = smem + buf * T::STAGE;
-    const unsigned char* vb = kb + T::BYTES;
-
-    // ---- S^T = K_j Q^T : two 32-key tiles
-    floatx16 st[2];
-#pragma unroll
-    for (int tau = 0; tau < 2; ++tau)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st[tau][r] = 0.0f;
-    // operands for k-step s+1 are read while the MFMAs of step s run
-    bf16x8 ka[2] = {lds_read16(kb + koff[0]), lds_read16(kb + 32 * T::KROWB + koff[0])};
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-      bf16x8 kn[2];
-      if (s + 1 < KSTEPS) {
-        kn[0] = lds_read16(kb + koff[s + 1]);
-        kn[1] = lds_read16(kb + 32 * T::KROWB + koff[s + 1]);
-      }
-#pragma unroll
-      for (int tau = 0; tau < 2; ++tau)
-        st[tau] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[tau], qf[s], st[tau], 0, 0, 0);
-      if (s + 1 < KSTEPS) { ka[0] = kn[0]; ka[1] = kn[1]; }
-    }
-
-    // ---- keys past N in a short last block get -inf
-    const int nvalid = N - j * BK;
-    if (nvalid < BK) {
-#pragma unroll
-      for (int tau = 0; tau < 2; ++tau)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = 32 * tau + 8 * (r >> 2) + 4 * h2 + (r & 3);
-          if (key >= nvalid) st[tau][r] = -INFINITY;
-        }
-    }
-
-    // ---- online softmax (one query per lane; the two halves hold disjoint keys)
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int tau = 0; tau < 2; ++tau)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, st[tau][r]);
-    mloc = pair_max(mloc);
-    if (__any((mloc - m) * c > kRescaleLog2)) {
-      const float m_new = fmaxf(m, mloc);
-      const float alpha_r = __builtin_amdgcn_exp2f((m - m_new) * c);
-      m = m_new;
-      lsum *= alpha_r;
-#pragma unroll
-      for (int i = 0; i < DT; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha_r;
-    }
-    const float mc = m * c;
-#pragma unroll
-    for (int tau = 0; tau < 2; ++tau)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st[tau][r] = __builtin_amdgcn_exp2f(fmaf(st[tau][r], c, -mc));
-
-    // ---- O^T += V_j^T P^T : 4 k-steps of 16 keys (LIN: H_kept += phi(K_j)^T V_j);
-    //      the V^T operands of step G+1 are read while the MFMAs of step G run
-    bf16x8 va[DT];
-#pragma unroll
-    for (int i = 0; i < DT; ++i) va[i] = lds_read16(vb + i * 32 * T::VROWB + voff[0]);
-#pragma unroll
-    for (int G = 0; G < 4; ++G) {
-      const int tau = G >> 1, hk = G & 1;
-      const bf16x8 pb = pack_bf16x8(st[tau], 8 * hk);
-      lsum = row_sum_bf16x8(pb, lsum);  // l sums the same bf16 P that meets V
-      bf16x8 vn[DT], pkf;
-      if (G + 1 < 4) {
-#pragma unroll
-        for (int i = 0; i < DT; ++i) vn[i] = lds_read16(vb + i * 32 * T::VROWB + voff[G + 1]);
-      }
-      if constexpr (LIN) {
-        pkf = lds_read16(vb + T::BYTES + wave * 32 * T::VROWB + voff[G]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) zk += (float)pkf[e];
-      }
-#pragma unroll
-      for (int i = 0; i < DT; ++i) {
-        oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], pb, oacc[i], 0, 0, 0);
-        if constexpr (LIN)
-          hacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pkf, va[i], hacc[i], 0, 0, 0);
-      }
-      if (G + 1 < 4) {
-#pragma unroll
-        for (int i = 0; i < DT; ++i) va[i] = vn[i];
-      }
-    }
-  }
-
   // ---- epilogue: O = O^T / l (+ alpha * O_l), bf16, rows < N only
   const float ltot = pair_sum(lsum);
   const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
@@ -747,7 +546,7 @@ __global__ __launch_bounds__(BQ * 2, 1) void sparse_linear_attn_kernel(
     constexpr int HP = D + 4;
     float* ht = reinterpret_cast<float*>(smem);
     float* zd = ht + D * HP;
-    static_assert(D * HP * 4 + D * 4 <= 2 * T::STAGE, "H_D must fit the staging buffers");
+    static_assert(D * HP * 4 + D * 4 <= 6 * T::BYTES, "H_D must fit the staging buffers");
     const bool dropped = count < n_k;  // D_i is empty when every block is kept
     zk = pair_sum(zk);
     __syncthreads();                   // every wave is done with the staging buffers
@@ -843,15 +642,10 @@ hipError_t launch_sparse(const AttnLaunch& a, hipStream_t s, AttnPhase phase) {
                          a.part_z, a.lin_h, a.lin_z);
     }
   }
-  if (phase != kPackOnly) {
-    if constexpr (LIN)
-      hipLaunchKernelGGL((sparse_linear_attn_kernel<D, BQ>), dim3(total), dim3(BQ * 2), 0, s,
-                         a.q, a.k, a.vt, a.idx, a.cnt, a.o, a.H, a.N, a.n_q, a.n_k, total, c,
-                         a.alpha, a.phikt, a.lin_h, a.lin_z);
-    else
-      hipLaunchKernelGGL((sparse_attn_fwd_kernel<D, BQ>), dim3(total), dim3(BQ * 2), 0, s,
-                         a.q, a.k, a.vt, a.idx, a.cnt, a.o, a.N, a.n_q, a.n_k, total, c);
-  }
+  if (phase != kPackOnly)
+    hipLaunchKernelGGL((sparse_attn_fwd_kernel<D, BQ, LIN>), dim3(total), dim3(BQ * 2), 0, s,
+                       a.q, a.k, a.vt, a.idx, a.cnt, a.o, a.H, a.N, a.n_q, a.n_k, total, c,
+                       a.alpha, a.phikt, a.lin_h, a.lin_z);
   return hipGetLastError();
 }
 
