@@ -1,16 +1,20 @@
-// Block mask of the hybrid Top-k + Top-p rule, three kernels:
+// Block mask of the hybrid Top-k + Top-p rule, three steps:
 //
 //   pool_mean_kernel    Qbar, Kbar = means of the valid rows of every block
 //                       (pooled queries and keys as on the SLA2 page,
 //                       section 2B; mean pooling of blocks as the Sparse
 //                       VideoGen2 page, section 1, names it). HBM-bound: it
 //                       reads Q and K once.
-//   block_logits_kernel s = scale * Qbar Kbar^T per head, float64, LDS-tiled.
-//   hybrid_select_kernel one workgroup per query-block row: softmax of s,
-//                       bitonic sort of (score desc, index asc) in LDS,
-//                       float64 prefix sum for Top-p, union with Top-k
-//                       (SpargeAttention2 page, sections 1 and 2A), then the
-//                       bitmask and the ascending index list.
+//   block_logits_kernel s = scale * Qbar Kbar^T per head, float64 on the
+//                       matrix cores.
+//   selection           per query-block row: softmax of s, sort of (score
+//                       desc, index asc), float64 prefix sum for Top-p, union
+//                       with Top-k (SpargeAttention2 page, sections 1 and 2A),
+//                       then the bitmask and the ascending index list.
+//                       hybrid_select_reg_kernel: rows of up to 512 blocks, one
+//                       wave per row, the sort in registers and lane shuffles;
+//                       hybrid_select_kernel: wider rows, one workgroup per row,
+//                       the sort in LDS.
 //
 // Everything that decides the mask is float64, so the selection is the one a
 // float64 evaluation of the definition gives, up to summation order.
@@ -162,59 +166,62 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 // ----------------------------------------------------------- selection
-// LDS bytes one wave of the selection kernel needs for npad sorted entries
+// LDS bytes of one row of the selection kernel with npad sorted entries
 __host__ __device__ constexpr size_t select_lds_bytes(int npad) {
   return (((size_t)npad * (2 * sizeof(double) + sizeof(uint16_t)) + 128 * sizeof(uint32_t)) + 15) &
          ~(size_t)15;
 }
+// threads per row: one compare-exchange pair each per sorting stage, at most 256
+__host__ __device__ constexpr int select_threads(int npad) { return npad / 2 < 256 ? (npad / 2 < 64 ? 64 : npad / 2) : 256; }
 
-// One wave per query-block row (rows_per_wg waves per workgroup, each with
-// its own LDS region: sv[npad] doubles (scores, sorted in place), ev[npad]
-// doubles (exp(s - max) by original index), si[npad] uint16, wb[words]
-// uint32).
-// Every step is wave-local, so the 45-66 stages of the bitonic sort need no
-// workgroup barrier.
+// One workgroup per query-block row. LDS: sv[npad] doubles (scores, sorted in
+// place), ev[npad] doubles (exp(s - max) by original index), si[npad] uint16,
+// wb[words] uint32. Wave 0 loads the row, forms the softmax terms, takes the
+// Top-p prefix and emits the outputs; all waves sort. A sorting stage whose
+// compare distance keeps every pair of a wave inside that wave's 128 entries
+// needs only a wave-local fence; the others take a workgroup barrier.
 template <int NPAD>
-__global__ __launch_bounds__(kThreads) void hybrid_select_kernel(
+__global__ __launch_bounds__(256) void hybrid_select_kernel(
     const double* __restrict__ s, int rows, int n_k, int words, int K_k,
     int keep_all, double p, uint32_t* __restrict__ bits_out,
     int32_t* __restrict__ idx_out, int32_t* __restrict__ cnt_out) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int npad = NPAD;
-  const size_t per_wave = select_lds_bytes(npad);
-  unsigned char* base = smem + wave * per_wave;
-  double* sv = reinterpret_cast<double*>(base);
+  constexpr int TH = select_threads(NPAD);
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  double* sv = reinterpret_cast<double*>(smem);
   double* ev = sv + npad;
   uint16_t* si = reinterpret_cast<uint16_t*>(ev + npad);
   uint32_t* wb = reinterpret_cast<uint32_t*>(si + npad);
-  const size_t row = (size_t)blockIdx.x * (blockDim.x >> 6) + wave;
-  if (row >= (size_t)rows) return;  // whole wave leaves together
+  __shared__ double tot_s;
+  const size_t row = blockIdx.x;
   const double* srow = s + row * (size_t)n_k;
 
-  // 1. load scores, padding with -inf past n_k; row maximum and exp sum
-  double mx = -INFINITY;
-  for (int j = lane; j < npad; j += 64) {
-    const double v = j < n_k ? srow[j] : -INFINITY;
-    sv[j] = v;
-    si[j] = (uint16_t)j;
-    mx = fmax(mx, v);
+  // 1. load scores (padding with -inf past n_k); row maximum and exp sum (wave 0)
+  if (wave == 0) {
+    double mx = -INFINITY;
+    for (int j = lane; j < npad; j += 64) {
+      const double v = j < n_k ? srow[j] : -INFINITY;
+      sv[j] = v;
+      si[j] = (uint16_t)j;
+      mx = fmax(mx, v);
+    }
+    for (int w = lane; w < words; w += 64) wb[w] = 0u;
+    mx = wave_max(mx);
+    double tot = 0.0;
+    for (int j = lane; j < n_k; j += 64) {
+      const double e = exp(sv[j] - mx);  // this lane wrote sv[j] itself
+      ev[j] = e;
+      tot += e;
+    }
+    tot = wave_sum(tot);
+    if (lane == 0) tot_s = tot;
   }
-  for (int w = lane; w < words; w += 64) wb[w] = 0u;
-  mx = wave_max(mx);
-  double tot = 0.0;
-  for (int j = lane; j < n_k; j += 64) {
-    const double e = exp(sv[j] - mx);  // this lane wrote sv[j] itself
-    ev[j] = e;
-    tot += e;
-  }
-  tot = wave_sum(tot);
-  wave_lds_sync();
+  __syncthreads();
 
   // 2. bitonic sort: position 0 = highest score, equal scores lower index
   //    first. All (score, index) pairs are distinct, so the order is total.
-  //    Each stage issues all of a lane's reads before any compare.
-  constexpr int PAIRS = NPAD / 2, C = PAIRS >= 64 ? PAIRS / 64 : 1;
+  constexpr int PAIRS = NPAD / 2, C = PAIRS / TH > 0 ? PAIRS / TH : 1;
 #pragma unroll 1
   for (int kk = 2; kk <= NPAD; kk <<= 1) {
 #pragma unroll 1
@@ -223,7 +230,7 @@ __global__ __launch_bounds__(kThreads) void hybrid_select_kernel(
       int ia[C], ib[C], ii[C];
 #pragma unroll
       for (int u = 0; u < C; ++u) {
-        const int pi = lane + 64 * u;
+        const int pi = (wave * C + u) * 64 + lane;  // each wave owns 64*C consecutive pairs
         ii[u] = 2 * pi - (pi & (jj - 1));
         if (pi < PAIRS) {
           a[u] = sv[ii[u]];
@@ -234,7 +241,7 @@ __global__ __launch_bounds__(kThreads) void hybrid_select_kernel(
       }
 #pragma unroll
       for (int u = 0; u < C; ++u) {
-        const int pi = lane + 64 * u, i = ii[u];
+        const int pi = (wave * C + u) * 64 + lane, i = ii[u];
         if (pi < PAIRS) {
           const bool l_first = (b[u] > a[u]) || (b[u] == a[u] && ib[u] < ia[u]);
           if (l_first == ((i & kk) == 0)) {
@@ -243,9 +250,16 @@ __global__ __launch_bounds__(kThreads) void hybrid_select_kernel(
           }
         }
       }
-      wave_lds_sync();
+      // a wave's pairs cover its own 128*C consecutive entries whenever the
+      // distance is at most 64*C, so between two such stages a wave-local
+      // fence suffices
+      const int jn = jj > 1 ? jj >> 1 : kk;  // next stage's distance
+      if (jj <= 64 * C && jn <= 64 * C) wave_lds_sync();
+      else __syncthreads();
     }
   }
+  if (wave != 0) return;  // no barrier follows
+  const double tot = tot_s;
 
   // 3. Top-p: cumulative probability in sorted order; first prefix >= p.
   //    Lane L owns sorted positions [L*per, (L+1)*per).
@@ -301,24 +315,156 @@ __global__ __launch_bounds__(kThreads) void hybrid_select_kernel(
   if (lane == 0) cnt_out[row] = count;
 }
 
-// up to 4 rows (one per wave) per workgroup within the CU's 160 KiB of LDS;
-// the kernel's dynamic-LDS limit is raised once per instantiation
+// Rows of up to 512 padded entries: one wave per row, entries in registers.
+// Lane L holds sorted positions L*E .. L*E+E-1 (E = NPAD/64) once the bitonic
+// network has run; a compare distance below E pairs two registers of one
+// lane, a larger one pairs the same register of lanes L and L ^ (jj/E),
+// exchanged with shuffles. The softmax total, the probabilities and the
+// Top-p prefix sums are formed exactly as by the LDS variant above.
+template <int NPAD>
+__global__ __launch_bounds__(256) void hybrid_select_reg_kernel(
+    const double* __restrict__ s, int rows, int n_k, int words, int K_k,
+    int keep_all, double p, uint32_t* __restrict__ bits_out,
+    int32_t* __restrict__ idx_out, int32_t* __restrict__ cnt_out) {
+  constexpr int E = NPAD / 64;
+  static_assert(E >= 1 && E <= 8, "register rows hold 64 .. 512 entries");
+  __shared__ uint32_t wbs[4][NPAD / 32 > 0 ? NPAD / 32 : 1];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const size_t row = (size_t)blockIdx.x * 4 + wave;
+  if (row >= (size_t)rows) return;  // whole wave leaves together
+  uint32_t* wb = wbs[wave];
+  const double* srow = s + row * (size_t)n_k;
+
+  // 1. load (entry j = lane + 64e in register e), row maximum, exp sum in
+  //    index order per lane
+  double sc[E];
+  int ix[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = lane + 64 * e;
+    sc[e] = j < n_k ? srow[j] : -INFINITY;
+    ix[e] = j;
+  }
+  for (int w = lane; w < words; w += 64) wb[w] = 0u;
+  double mx = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < E; ++e) mx = fmax(mx, sc[e]);
+  mx = wave_max(mx);
+  double tot = 0.0;
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (lane + 64 * e < n_k) tot += exp(sc[e] - mx);
+  tot = wave_sum(tot);
+
+  // 2. bitonic sort: position 0 = highest score, equal scores lower index first
+#pragma unroll
+  for (int kk = 2; kk <= NPAD; kk <<= 1) {
+#pragma unroll
+    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+      if (jj < E) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          if (e & jj) continue;
+          const int f = e ^ jj;
+          const bool desc = ((lane * E + e) & kk) == 0;
+          const bool b_first = (sc[f] > sc[e]) || (sc[f] == sc[e] && ix[f] < ix[e]);
+          if (b_first == desc) {
+            const double ts = sc[e]; sc[e] = sc[f]; sc[f] = ts;
+            const int ti = ix[e]; ix[e] = ix[f]; ix[f] = ti;
+          }
+        }
+      } else {
+        const int m = jj / E;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const double os = __shfl_xor(sc[e], m);
+          const int oi = __shfl_xor(ix[e], m);
+          const int pos = lane * E + e;
+          const bool lower = (pos & jj) == 0, desc = (pos & kk) == 0;
+          const double as = lower ? sc[e] : os, bs = lower ? os : sc[e];
+          const int ai = lower ? ix[e] : oi, bi = lower ? oi : ix[e];
+          const bool b_first = (bs > as) || (bs == as && bi < ai);
+          if (b_first == desc) { sc[e] = os; ix[e] = oi; }
+        }
+      }
+    }
+  }
+
+  // 3. Top-p: cumulative probability in sorted order; first prefix >= p
+  int m_p = n_k;
+  if (!keep_all) {
+    if (p <= 0.0) {
+      m_p = 0;
+    } else {
+      double pr[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) pr[e] = exp(sc[e] - mx) / tot;
+      double local = 0.0;
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (lane * E + e < n_k) local += pr[e];
+      double run = wave_incl_scan(local, lane) - local;
+      int hit = INT32_MAX;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        if (lane * E + e < n_k && hit == INT32_MAX) {
+          run += pr[e];
+          if (run >= p) hit = lane * E + e + 1;
+        }
+      }
+      const unsigned long long any = __ballot(hit != INT32_MAX);
+      if (any) m_p = __shfl(hit, __ffsll((long long)any) - 1);
+    }
+  }
+  const int count = max(K_k, m_p);
+
+  // 4. union = first `count` of the order -> bitmask
+  wave_lds_sync();  // wb cleared by every lane
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (lane * E + e < count && ix[e] < n_k) atomicOr(&wb[ix[e] >> 5], 1u << (ix[e] & 31));
+  wave_lds_sync();
+
+  // 5. emit bitmask, ascending index list and count (words <= 64: one per lane)
+  const uint32_t w0 = lane < words ? wb[lane] : 0u;
+  if (lane < words) bits_out[row * words + lane] = w0;
+  const int c0 = __popc(w0);
+  const int e0 = wave_incl_scan(c0, lane) - c0;
+  int32_t* irow = idx_out + row * (size_t)n_k;
+  uint32_t word = w0;
+  int pos = e0;
+  while (word) {
+    irow[pos++] = lane * 32 + __ffs(word) - 1;
+    word &= word - 1;
+  }
+  if (lane == 0) cnt_out[row] = count;
+}
+
+template <int NPAD>
+hipError_t launch_select_reg(const MaskLaunch& a, hipStream_t st) {
+  const int rows = a.B * a.H * a.n_q;
+  hipLaunchKernelGGL(hybrid_select_reg_kernel<NPAD>, dim3((rows + 3) / 4), dim3(256), 0, st,
+                     a.logits, rows, a.n_k, a.words, a.K_k, a.keep_all, a.p, a.bits, a.idx,
+                     a.cnt);
+  return hipGetLastError();
+}
+
+// one row per workgroup; the kernel's dynamic-LDS limit is raised once per
+// instantiation (the 4096-entry rows need 73 KiB)
 template <int NPAD>
 hipError_t launch_select(const MaskLaunch& a, hipStream_t st) {
-  constexpr size_t kLdsMax = 160 * 1024;
   static std::once_flag lds_once;
   static hipError_t lds_err = hipSuccess;
   std::call_once(lds_once, [] {
     lds_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&hybrid_select_kernel<NPAD>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMax);
+                                  hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)select_lds_bytes(NPAD));
   });
   if (lds_err != hipSuccess) return lds_err;
-  const size_t per_wave = select_lds_bytes(NPAD);
-  const int waves = (int)std::max<size_t>(1, std::min<size_t>(4, kLdsMax / per_wave));
   const int rows = a.B * a.H * a.n_q;
-  hipLaunchKernelGGL(hybrid_select_kernel<NPAD>, dim3((rows + waves - 1) / waves),
-                     dim3(64 * waves), per_wave * waves, st, a.logits, rows, a.n_k, a.words,
-                     a.K_k, a.keep_all, a.p, a.bits, a.idx, a.cnt);
+  hipLaunchKernelGGL(hybrid_select_kernel<NPAD>, dim3(rows), dim3(select_threads(NPAD)),
+                     select_lds_bytes(NPAD), st, a.logits, rows, a.n_k, a.words, a.K_k,
+                     a.keep_all, a.p, a.bits, a.idx, a.cnt);
   return hipGetLastError();
 }
 
@@ -339,10 +485,10 @@ hipError_t launch_mask(const MaskLaunch& a, hipStream_t st) {
                        a.qbar, a.kbar, a.logits, a.n_q, a.n_k, tq, tk, tiles, a.scale);
   }
   switch (a.npad) {
-    case 64: return launch_select<64>(a, st);
-    case 128: return launch_select<128>(a, st);
-    case 256: return launch_select<256>(a, st);
-    case 512: return launch_select<512>(a, st);
+    case 64: return launch_select_reg<64>(a, st);
+    case 128: return launch_select_reg<128>(a, st);
+    case 256: return launch_select_reg<256>(a, st);
+    case 512: return launch_select_reg<512>(a, st);
     case 1024: return launch_select<1024>(a, st);
     case 2048: return launch_select<2048>(a, st);
     default: return launch_select<4096>(a, st);
@@ -351,3 +497,4 @@ hipError_t launch_mask(const MaskLaunch& a, hipStream_t st) {
 }
 
 }  // namespace sparge
+

@@ -111,8 +111,9 @@ size_t sparge_attn_workspace_bytes(int B, int H, int N, int d);
  *  kv_idx    : int32 [B, H, n_q, n_k]; first kv_cnt entries of each row are
  *              key block indices in [0, n_k). Any such list is accepted (for
  *              example the output of sparge_mask_predict, or a fixed local
- *              window). Counts are clamped to [0, n_k] and indices to
- *              [0, n_k - 1], so a corrupt list cannot read out of bounds.
+ *              window), in any order; a block listed twice is attended twice.
+ *              Counts are clamped to [0, n_k] and indices to [0, n_k - 1], so
+ *              a corrupt list cannot read out of bounds.
  *  kv_cnt    : int32 [B, H, n_q].
  *  o         : out bf16 [B, H, N, d], device, 16-byte aligned; must not
  *              overlap the inputs.

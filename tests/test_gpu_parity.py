@@ -193,6 +193,50 @@ def test_attention_matches_oracle_on_workloads(name, samples):
             print(f"[attn] {name} b={b} h={h}: max {mx:.2e} mean {mean:.2e}", flush=True)
 
 
+@pytest.mark.parametrize("k_frac", [0.10, 0.05])
+def test_attention_matches_oracle_at_topk_operating_points(k_frac):
+    """The 90% / 95% block-sparsity points the benchmark times (p = 0, Top-k alone),
+    sampled query blocks of two heads against the oracle."""
+    wl, Q, K, V, q, k, v = workload_tensors("wan1.3b")
+    bits, idx, cnt = S.sparge_mask_predict(q, k, wl.block_q, wl.block_k, k_frac, 0.0)
+    ws = S.sparge_attn_pack(v)
+    o = S.sparge_attn_fwd_packed(q, k, idx, cnt, ws, wl.block_q, wl.block_k)
+    torch.cuda.synchronize()
+    kept = gpu_bits_to_bool(bits, wl.n_k)
+    got = O.bf16_to_f64(o.cpu().view(torch.uint16).numpy())
+    rng = np.random.default_rng(int(k_frac * 1000))
+    for h in rng.choice(wl.H, size=2, replace=False):
+        blocks = sorted({0, wl.n_q - 1, *rng.choice(wl.n_q, 4, replace=False)})
+        ref = O.masked_attention_head(O.bf16_to_f64(Q[0, h]), O.bf16_to_f64(K[0, h]),
+                                      O.bf16_to_f64(V[0, h]), kept[0, h], wl.block_q,
+                                      wl.block_k, wl.scale, q_blocks=blocks)
+        rows = ~np.isnan(ref[:, 0])
+        mx, mean = compare_outputs(got[0, h][rows], ref[rows])
+        print(f"[attn k={k_frac}] h={h}: max {mx:.2e} mean {mean:.2e}", flush=True)
+
+
+def test_attention_accepts_lists_in_any_order():
+    """kv_idx rows need not be sorted: a permuted list gives the oracle's result."""
+    B, H, N, d, bq = 1, 2, 2000, 128, 128
+    rng = np.random.default_rng(99)
+    from block_sparse_attention_softmax_amd.workloads import f64_to_bf16_bits
+    Q, K, V = (f64_to_bf16_bits(rng.standard_normal((B, H, N, d)) * 1.5) for _ in range(3))
+    n_q, n_k = -(-N // bq), -(-N // 64)
+    kept = _random_lists(rng, B, H, n_q, n_k)
+    idx, cnt = O.kept_to_index_list(kept)
+    for row in np.ndindex(B, H, n_q):
+        idx[row][: cnt[row]] = rng.permutation(idx[row][: cnt[row]])
+    o = S.sparge_attn_fwd(to_gpu(Q), to_gpu(K), to_gpu(V), torch.from_numpy(idx).cuda(),
+                          torch.from_numpy(cnt).cuda(), bq, 64, None)
+    torch.cuda.synchronize()
+    got = O.bf16_to_f64(o.cpu().view(torch.uint16).numpy())
+    for h in range(H):
+        ref = O.masked_attention_head(O.bf16_to_f64(Q[0, h]), O.bf16_to_f64(K[0, h]),
+                                      O.bf16_to_f64(V[0, h]), kept[0, h], bq, 64,
+                                      S.default_scale(d))
+        compare_outputs(got[0, h], ref)
+
+
 # ------------------------------------------------------------ linear branch
 @pytest.mark.parametrize("B,H,N,d,bq", [(1, 2, 1000, 128, 128), (2, 1, 777, 64, 64),
                                          (1, 3, 300, 128, 128), (1, 1, 64, 64, 64)])
