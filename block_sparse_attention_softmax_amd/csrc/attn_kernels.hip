@@ -247,16 +247,21 @@ __global__ __launch_bounds__(256) void linear_reduce_kernel(const float* __restr
 // spread one per k-step over the S^T product instead of issued together,
 // so the waves of a CU do not queue behind each other's copies.
 //
-// LIN adds the linear branch over the dropped blocks: each kept block also
-// accumulates H_kept += phi(K_j)^T V_j (wave w owns rows 32w..32w+31 of the
-// d x d product, reusing the V^T fragments of the P V product as its B
-// operand; phi(K)^T tiles are staged beside the V^T tiles) and z_kept +=
-// sum phi(K_j); the epilogue forms H_D = H_tot - H_kept, z_D = z_tot -
-// z_kept and O_l = phi(Q) H_D / (phi(Q) . z_D) with a three-term split-bf16
-// MFMA product (about 16 significant bits per operand), and writes
-// O = O_s + alpha[h] * O_l.
+// LIN adds the linear branch over the dropped blocks with a second set of
+// BQ/32 waves in the workgroup (H waves). phi(K)^T tiles are staged beside
+// the V^T tiles; per listed block, H wave w accumulates rows 32w..32w+31 of
+// H_kept += phi(K_j)^T V_j and its share of z_kept += sum phi(K_j), with one
+// barrier per block like the attention waves, whose loop is the plain one.
+// The H waves' matrix products fill the attention waves' softmax gaps on the
+// same SIMDs, and the attention waves carry no extra accumulator. At the end
+// the H waves form H_D = H_tot - H_kept and z_D = z_tot - z_kept in LDS, then
+// O_l = phi(Q) H_D / (phi(Q) . z_D) for the queries of the attention wave of
+// the same index (three-term split-bf16 MFMA product, about 16 significant
+// bits per operand), and hand O_l and the scale alpha[h] / (phi(Q) . z_D)
+// over through LDS in the attention wave's own register layout; the
+// attention wave writes O = O_s + alpha[h] * O_l.
 template <int D, int BQ, bool LIN>
-__global__ __launch_bounds__(BQ * 2, (LIN || (D == 128 && BQ == 64)) ? 1 : 2) void sparse_attn_fwd_kernel(
+__global__ __launch_bounds__(BQ * (LIN ? 4 : 2), (LIN || (D == 128 && BQ == 64)) ? 1 : 2) void sparse_attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ vt, const int32_t* __restrict__ kv_idx,
     const int32_t* __restrict__ kv_cnt, uint16_t* __restrict__ o, int H, int N, int n_q,
@@ -279,12 +284,16 @@ __global__ __launch_bounds__(BQ * 2, (LIN || (D == 128 && BQ == 64)) ? 1 : 2) vo
   const int tile = xcd_remap(blockIdx.x, total);
   const int bh = tile / n_q, qi = tile % n_q;
   const int t = threadIdx.x, lane = t & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wave_id = __builtin_amdgcn_readfirstlane(t >> 6);
+  // LIN: waves NW.. are H waves (H_kept and z_kept for the d rows 32*wave..);
+  // the first NW waves run the attention itself and issue every copy
+  const bool hwave = LIN && wave_id >= NW;
+  const int wave = hwave ? wave_id - NW : wave_id;
   const int h2 = lane >> 5, l32 = lane & 31;
   const size_t head = (size_t)bh * N * D;
 
   const int qrow = qi * BQ + wave * 32 + l32;
-  bf16x8 qf[KSTEPS];
+  bf16x8 qf[KSTEPS];  // (H waves load the rows of their attention wave, for phi(Q))
   {
     const uint16_t* qp = q + head + (size_t)min(qrow, N - 1) * D + 8 * h2;
 #pragma unroll
@@ -378,14 +387,8 @@ __global__ __launch_bounds__(BQ * 2, (LIN || (D == 128 && BQ == 64)) ? 1 : 2) vo
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[i][r] = 0.0f;
   float m = -INFINITY, lsum = 0.0f;
-  floatx16 hacc[LIN ? DT : 1];  // H_kept rows 32*wave.. (LIN)
-  float zk = 0.0f;              // z_kept entry 32*wave + l32 (LIN; split over the half-waves)
-  if constexpr (LIN) {
-#pragma unroll
-    for (int i = 0; i < DT; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) hacc[i][r] = 0.0f;
-  }
+  // H waves accumulate H_kept (rows 32*wave..) in oacc and their share of
+  // z_kept (entry 32*wave + l32, split over the half-waves) in lsum
   floatx16 sc[2];  // S^T of the current block
 #pragma unroll
   for (int tau = 0; tau < 2; ++tau)
@@ -394,13 +397,15 @@ __global__ __launch_bounds__(BQ * 2, (LIN || (D == 128 && BQ == 64)) ? 1 : 2) vo
   int jcur = 0;
 
   if (count > 0) {
-    jcur = jat(0);
-    stageK(jcur, 0);
-    stageV(jcur, 0);
-    if (count > 1) stageK(jat(1), 1);
+    if (!hwave) {
+      jcur = jat(0);
+      stageK(jcur, 0);
+      stageV(jcur, 0);
+      if (count > 1) stageK(jat(1), 1);
+    }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
-    qk(kbuf, sc, Zero{}, Full{}, [](int) {});
+    if (!hwave) qk(kbuf, sc, Zero{}, Full{}, [](int) {});
   }
 
   // one listed block: softmax and P V of block `it` (S^T in sc), and with
@@ -454,7 +459,6 @@ __global__ __launch_bounds__(BQ * 2, (LIN || (D == 128 && BQ == 64)) ? 1 : 2) vo
     };
     const unsigned char* kn = kbuf + ((it + 1) & 1) * T::BYTES;
     const unsigned char* vb = vbuf + (it & 1) * T::BYTES;
-    const unsigned char* pb_ = pbuf + (it & 1) * T::BYTES;
 
     const int nvalid = N - jcur * BK;  // keys past N in a short last block get -inf
     if (nvalid < BK) {
@@ -506,22 +510,14 @@ __global__ __launch_bounds__(BQ * 2, (LIN || (D == 128 && BQ == 64)) ? 1 : 2) vo
       const int tau = G >> 1, hk = G & 1;
       const bf16x8 pb = pack_bf16x8(sc[tau], 8 * hk);
       lsum = row_sum_bf16x8(pb, lsum);
-      bf16x8 vn[DT], pkf;
+      bf16x8 vn[DT];
       if (G + 1 < 4) {
 #pragma unroll
         for (int i = 0; i < DT; ++i) vn[i] = lds_read16(vb + i * 32 * T::VROWB + voff[G + 1]);
       }
-      if constexpr (LIN) {  // phi(K_j)^T rows 32*wave.., keys of k-step G
-        pkf = lds_read16(pb_ + wave * 32 * T::VROWB + voff[G]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) zk += (float)pkf[e];
-      }
-#pragma unroll
-      for (int i = 0; i < DT; ++i) {
+      for (int i = 0; i < DT; ++i)
         oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], pb, oacc[i], 0, 0, 0);
-        if constexpr (LIN)
-          hacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pkf, va[i], hacc[i], 0, 0, 0);
-      }
       if (G + 1 < 4) {
 #pragma unroll
         for (int i = 0; i < DT; ++i) va[i] = vn[i];
@@ -533,24 +529,54 @@ __global__ __launch_bounds__(BQ * 2, (LIN || (D == 128 && BQ == 64)) ? 1 : 2) vo
       jcur = jn;
     }
   };
-  int it = 0;
-  for (; it + 1 < count; ++it) step(it, std::true_type{});
-  if (count > 0) step(it, std::false_type{});
+  if (hwave) {
+    // H waves: one barrier per listed block, like the attention waves' steps;
+    // H_kept += phi(K_it)^T V_it and z_kept += sum phi(K_it) from the tiles
+    // of block it (V^T and phi(K)^T buffers it & 1)
+    for (int it = 0; it < count; ++it) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+      const unsigned char* vbh = vbuf + (it & 1) * T::BYTES;
+      const unsigned char* pbh = pbuf + (it & 1) * T::BYTES;
+#pragma unroll
+      for (int G = 0; G < 4; ++G) {
+        const bf16x8 pkf = lds_read16(pbh + wave * 32 * T::VROWB + voff[G]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) lsum += (float)pkf[e];
+#pragma unroll
+        for (int i = 0; i < DT; ++i)
+          oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              pkf, lds_read16(vbh + i * 32 * T::VROWB + voff[G]), oacc[i], 0, 0, 0);
+      }
+    }
+  } else {
+    int it = 0;
+    for (; it + 1 < count; ++it) step(it, std::true_type{});
+    if (count > 0) step(it, std::false_type{});
+  }
 
   // ---- epilogue: O = O^T / l (+ alpha * O_l), bf16, rows < N only
-  const float ltot = pair_sum(lsum);
+  const float ltot = pair_sum(lsum);  // (H waves: z_kept entry 32*wave + l32)
   const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
-  float lin_scale = 0.0f;  // alpha[h] / (phi(Q_t) . z_D), 0 when nothing was dropped
+  // LIN: O_l for this lane's (d, query) entries, in the oacc layout, and
+  // alpha[h] / (phi(Q_t) . z_D) for its query, handed over through LDS by the
+  // H wave of the same index
+  const float4* yl = nullptr;
+  const float* ys = nullptr;
   if constexpr (LIN) {
-    // the staging buffers become H_D^T [D][D+4] fp32 and z_D [D]
+    // the staging buffers become H_D^T [D][D+4] fp32 and z_D [D], then the
+    // per-lane O_l fragments [NW][DT*4][64 lanes] float4 and scales [NW][64]
     constexpr int HP = D + 4;
     float* ht = reinterpret_cast<float*>(smem);
     float* zd = ht + D * HP;
     static_assert(D * HP * 4 + D * 4 <= 6 * T::BYTES, "H_D must fit the staging buffers");
+    static_assert(NW * DT * 4 * 64 * 16 + NW * 64 * 4 <= 6 * T::BYTES,
+                  "O_l must fit the staging buffers");
+    float4* ylds = reinterpret_cast<float4*>(smem);
+    float* ysds = reinterpret_cast<float*>(ylds + NW * DT * 4 * 64);
     const bool dropped = count < n_k;  // D_i is empty when every block is kept
-    zk = pair_sum(zk);
     __syncthreads();                   // every wave is done with the staging buffers
-    if (dropped) {
+    if (dropped && hwave) {
       const float* Ht = lin_h + (size_t)bh * D * D;
 #pragma unroll
       for (int i = 0; i < DT; ++i)
@@ -558,22 +584,22 @@ __global__ __launch_bounds__(BQ * 2, (LIN || (D == 128 && BQ == 64)) ? 1 : 2) vo
         for (int g = 0; g < 4; ++g) {
           const int a0 = 32 * wave + 8 * g + 4 * h2, b = 32 * i + l32;
           float4 x;
-          x.x = Ht[(size_t)(a0 + 0) * D + b] - hacc[i][4 * g + 0];
-          x.y = Ht[(size_t)(a0 + 1) * D + b] - hacc[i][4 * g + 1];
-          x.z = Ht[(size_t)(a0 + 2) * D + b] - hacc[i][4 * g + 2];
-          x.w = Ht[(size_t)(a0 + 3) * D + b] - hacc[i][4 * g + 3];
+          x.x = Ht[(size_t)(a0 + 0) * D + b] - oacc[i][4 * g + 0];
+          x.y = Ht[(size_t)(a0 + 1) * D + b] - oacc[i][4 * g + 1];
+          x.z = Ht[(size_t)(a0 + 2) * D + b] - oacc[i][4 * g + 2];
+          x.w = Ht[(size_t)(a0 + 3) * D + b] - oacc[i][4 * g + 3];
           *reinterpret_cast<float4*>(ht + b * HP + a0) = x;
         }
-      if (h2 == 0) zd[32 * wave + l32] = lin_z[(size_t)bh * D + 32 * wave + l32] - zk;
+      if (h2 == 0) zd[32 * wave + l32] = lin_z[(size_t)bh * D + 32 * wave + l32] - ltot;
     }
     __syncthreads();
-    if (dropped) {
+    float lin_scale = 0.0f;  // alpha[h] / (phi(Q_t) . z_D)
+    if (dropped && hwave) {
       // O_l^T (d x 32 queries) = H_D^T phi(Q)^T; phi(Q) in the qf layout
-      floatx16* lacc = hacc;
 #pragma unroll
       for (int i = 0; i < DT; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) lacc[i][r] = 0.0f;
+        for (int r = 0; r < 16; ++r) oacc[i][r] = 0.0f;
       float den = 0.0f;
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) {
@@ -597,16 +623,32 @@ __global__ __launch_bounds__(BQ * 2, (LIN || (D == 128 && BQ == 64)) ? 1 : 2) vo
             hhi[e] = (__bf16)hv[e];
             hlo[e] = (__bf16)(hv[e] - (float)hhi[e]);
           }
-          lacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hhi, qhi, lacc[i], 0, 0, 0);
-          lacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hhi, qlo, lacc[i], 0, 0, 0);
-          lacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hlo, qhi, lacc[i], 0, 0, 0);
+          oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hhi, qhi, oacc[i], 0, 0, 0);
+          oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hhi, qlo, oacc[i], 0, 0, 0);
+          oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hlo, qhi, oacc[i], 0, 0, 0);
         }
       }
       den = pair_sum(den);
       lin_scale = den > 0.0f ? alpha[bh % H] / den : 0.0f;
     }
+    __syncthreads();  // every H wave is done reading H_D^T
+    if (dropped && hwave) {
+#pragma unroll
+      for (int i = 0; i < DT; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          ylds[((wave * DT + i) * 4 + g) * 64 + lane] =
+              make_float4(oacc[i][4 * g + 0], oacc[i][4 * g + 1], oacc[i][4 * g + 2],
+                          oacc[i][4 * g + 3]);
+      ysds[wave * 64 + lane] = lin_scale;
+    }
+    __syncthreads();
+    if (dropped) {
+      yl = ylds;
+      ys = ysds;
+    }
   }
-  if (qrow < N) {
+  if (!hwave && qrow < N) {
     uint16_t* orow = o + head + (size_t)qrow * D;
 #pragma unroll
     for (int i = 0; i < DT; ++i)
@@ -615,9 +657,16 @@ __global__ __launch_bounds__(BQ * 2, (LIN || (D == 128 && BQ == 64)) ? 1 : 2) vo
         const int d0 = 32 * i + 8 * g + 4 * h2;
         float y[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          y[e] = oacc[i][4 * g + e] * inv;
-          if constexpr (LIN) y[e] = fmaf(hacc[i][4 * g + e], lin_scale, y[e]);
+        for (int e = 0; e < 4; ++e) y[e] = oacc[i][4 * g + e] * inv;
+        if constexpr (LIN) {
+          if (yl) {
+            const float4 l = yl[((wave * DT + i) * 4 + g) * 64 + lane];
+            const float sl = ys[wave * 64 + lane];
+            y[0] = fmaf(l.x, sl, y[0]);
+            y[1] = fmaf(l.y, sl, y[1]);
+            y[2] = fmaf(l.z, sl, y[2]);
+            y[3] = fmaf(l.w, sl, y[3]);
+          }
         }
         uint2 pk;
         pk.x = pack2_bf16(y[0], y[1]);
@@ -643,7 +692,7 @@ hipError_t launch_sparse(const AttnLaunch& a, hipStream_t s, AttnPhase phase) {
     }
   }
   if (phase != kPackOnly)
-    hipLaunchKernelGGL((sparse_attn_fwd_kernel<D, BQ, LIN>), dim3(total), dim3(BQ * 2), 0, s,
+    hipLaunchKernelGGL((sparse_attn_fwd_kernel<D, BQ, LIN>), dim3(total), dim3(BQ * (LIN ? 4 : 2)), 0, s,
                        a.q, a.k, a.vt, a.idx, a.cnt, a.o, a.H, a.N, a.n_q, a.n_k, total, c,
                        a.alpha, a.phikt, a.lin_h, a.lin_z);
   return hipGetLastError();
