@@ -306,7 +306,17 @@ __global__ __launch_bounds__(BQ * (LIN ? 4 : 2), (LIN || (D == 128 && BQ == 64))
   const size_t vtile = (size_t)D * BK;
   const uint16_t* vth = vt + (size_t)bh * n_k * vtile;
   const uint16_t* pkh = LIN ? phikt + (size_t)bh * n_k * vtile : nullptr;
-  auto jat = [&](int i) { return min(max(ids[i], 0), n_k - 1); };
+  // the list is read through two 64-entry windows held one entry per lane
+  // (entries w0 .. w0+127), so the block loop issues no scalar memory loads
+  auto load_win = [&](int base) { return base + lane < n_k ? ids[base + lane] : 0; };
+  int w0 = 0;
+  int win0 = load_win(0), win1 = load_win(64);
+  auto jat = [&](int i) {  // i in [w0, w0 + 128)
+    const int r = i - w0;
+    const int a = __builtin_amdgcn_readlane(win0, r & 63);
+    const int b = __builtin_amdgcn_readlane(win1, r & 63);
+    return min(max(r < 64 ? a : b, 0), n_k - 1);
+  };
 
   constexpr int KROWS_U = 64 * NW / T::KCPR, VROWS_U = 64 * NW / T::VCPR;
   constexpr bool KCONST = KROWS_U % T::KCPR == 0, VCONST = VROWS_U % (2 * T::VCPR) == 0;
@@ -389,7 +399,7 @@ __global__ __launch_bounds__(BQ * (LIN ? 4 : 2), (LIN || (D == 128 && BQ == 64))
   float m = -INFINITY, lsum = 0.0f;
   // H waves accumulate H_kept (rows 32*wave..) in oacc and their share of
   // z_kept (entry 32*wave + l32, split over the half-waves) in lsum
-  floatx16 sc[2];  // S^T of the current block
+  floatx16 sc[2], sn[2];  // S^T of the current and the next block (roles swap each step)
 #pragma unroll
   for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
@@ -410,7 +420,7 @@ __global__ __launch_bounds__(BQ * (LIN ? 4 : 2), (LIN || (D == 128 && BQ == 64))
 
   // one listed block: softmax and P V of block `it` (S^T in sc), and with
   // NEXT the S^T of block it+1 into sn, interleaved
-  auto step = [&](int it, auto next_tag) {
+  auto step = [&](int it, auto next_tag, floatx16(&sc)[2], floatx16(&sn)[2]) {
     constexpr bool NEXT = decltype(next_tag)::value;
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K of it+1 and V^T of it landed
     __syncthreads();                     // and every wave is done with step it-1's buffers
@@ -423,6 +433,11 @@ __global__ __launch_bounds__(BQ * (LIN ? 4 : 2), (LIN || (D == 128 && BQ == 64))
     const char* psrc = nullptr;
     uint32_t ko[LOADS];
     if constexpr (NEXT) {
+      if (it + 1 == w0 + 64) {  // slide the windows; the load lands with this step's copies
+        win0 = win1;
+        w0 += 64;
+        win1 = load_win(w0 + 64);
+      }
       jn = jat(it + 1);
       const int jk = it + 2 < count ? jat(it + 2) : jn;
       const int key0 = jk * BK;
@@ -471,7 +486,6 @@ __global__ __launch_bounds__(BQ * (LIN ? 4 : 2), (LIN || (D == 128 && BQ == 64))
         }
     }
 
-    floatx16 sn[2];
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
@@ -523,11 +537,7 @@ __global__ __launch_bounds__(BQ * (LIN ? 4 : 2), (LIN || (D == 128 && BQ == 64))
         for (int i = 0; i < DT; ++i) va[i] = vn[i];
       }
     }
-    if constexpr (NEXT) {
-#pragma unroll
-      for (int tau = 0; tau < 2; ++tau) sc[tau] = sn[tau];
-      jcur = jn;
-    }
+    if constexpr (NEXT) jcur = jn;
   };
   if (hwave) {
     // H waves: one barrier per listed block, like the attention waves' steps;
@@ -551,8 +561,25 @@ __global__ __launch_bounds__(BQ * (LIN ? 4 : 2), (LIN || (D == 128 && BQ == 64))
     }
   } else {
     int it = 0;
-    for (; it + 1 < count; ++it) step(it, std::true_type{});
-    if (count > 0) step(it, std::false_type{});
+    if constexpr (LIN) {  // (two steps per iteration need more registers than LIN has left)
+      for (; it + 1 < count; ++it) {
+        step(it, std::true_type{}, sc, sn);
+        sc[0] = sn[0];
+        sc[1] = sn[1];
+      }
+      if (count > 0) step(it, std::false_type{}, sc, sn);
+    } else {  // two steps per iteration, the S^T arrays swapping roles
+      for (; it + 2 < count; it += 2) {
+        step(it, std::true_type{}, sc, sn);
+        step(it + 1, std::true_type{}, sn, sc);
+      }
+      if (it + 1 < count) {
+        step(it, std::true_type{}, sc, sn);
+        step(it + 1, std::false_type{}, sn, sc);
+      } else if (it < count) {
+        step(it, std::false_type{}, sc, sn);
+      }
+    }
   }
 
   // ---- epilogue: O = O^T / l (+ alpha * O_l), bf16, rows < N only
