@@ -237,6 +237,33 @@ def test_attention_accepts_lists_in_any_order():
         compare_outputs(got[0, h], ref)
 
 
+def test_attention_long_rows_sampled():
+    """N = 200000 (3125 key blocks): rows listing up to every block, so the kernel
+    walks lists far longer than its 128-entry index windows; sampled query
+    blocks against the oracle."""
+    B, H, N, d, bq = 1, 1, 200000, 128, 128
+    rng = np.random.default_rng(200000)
+    from block_sparse_attention_softmax_amd.workloads import f64_to_bf16_bits
+    Q, K, V = (f64_to_bf16_bits(rng.standard_normal((B, H, N, d))) for _ in range(3))
+    n_q, n_k = -(-N // bq), -(-N // 64)
+    kept = rng.random((B, H, n_q, n_k)) < 0.3
+    kept[0, 0, 0] = True                   # every block
+    kept[0, 0, n_q - 1] = False
+    kept[0, 0, n_q - 1, n_k - 1] = True    # only the short last key block
+    idx, cnt = O.kept_to_index_list(kept)
+    o = S.sparge_attn_fwd(to_gpu(Q), to_gpu(K), to_gpu(V), torch.from_numpy(idx).cuda(),
+                          torch.from_numpy(cnt).cuda(), bq, 64, None)
+    torch.cuda.synchronize()
+    got = O.bf16_to_f64(o[0, 0].cpu().view(torch.uint16).numpy())
+    blocks = sorted({0, 1, n_q // 2, n_q - 1})
+    ref = O.masked_attention_head(O.bf16_to_f64(Q[0, 0]), O.bf16_to_f64(K[0, 0]),
+                                  O.bf16_to_f64(V[0, 0]), kept[0, 0], bq, 64,
+                                  S.default_scale(d), q_blocks=blocks)
+    rows = ~np.isnan(ref[:, 0])
+    mx, mean = compare_outputs(got[rows], ref[rows])
+    print(f"[attn long rows] max {mx:.2e} mean {mean:.2e}", flush=True)
+
+
 # ------------------------------------------------------------ linear branch
 @pytest.mark.parametrize("B,H,N,d,bq", [(1, 2, 1000, 128, 128), (2, 1, 777, 64, 64),
                                          (1, 3, 300, 128, 128), (1, 1, 64, 64, 64)])
