@@ -27,7 +27,11 @@ What it computes, step by step, in float64 with NumPy, written from the pages:
    only skips work that the mask removes, so its result is this);
 8. optional linear branch over the dropped keys with phi = elu + 1, added to
    the sparse output with a per-head weight alpha (the SLA2 page, section 1,
-   and the SALAD page's static scaling of the linear branch).
+   and the SALAD page's static scaling of the linear branch);
+9. the SLA2 variants: the router's learnable linear projections of the pooled
+   queries and keys before the compressed score (SLA2 page, section 2B; hard
+   Top-k at inference, section 2D), and the faithful mix O = alpha (*) O_s +
+   (1 - alpha) (*) O_l with a learned vector alpha in [0, 1] (section 2A).
 
 Readings of points the pages leave open (each also listed in the design
 notes): mean pooling over the valid tokens of a partial last block; no
@@ -181,6 +185,47 @@ def predict_mask(Qb: np.ndarray, Kb: np.ndarray, block_q: int, block_k: int,
     return MaskResult(kept, cnt, logits, margin, K_k, m_p)
 
 
+# ------------------------------------------------------------ SLA2 router
+def router_project(Xbar: np.ndarray, W: np.ndarray) -> np.ndarray:
+    """The router's learnable linear projection of pooled rows (SLA2 page,
+    section 2B: proj_q, proj_k applied to the pooled Q and K): Xbar [n, d] @ W
+    [d, d_out], W given as the float32 values of the weights."""
+    return Xbar @ np.asarray(W, np.float32).astype(np.float64)
+
+
+def predict_mask_routed_head(q: np.ndarray, k: np.ndarray, wq: np.ndarray, wk: np.ndarray,
+                             block_q: int, block_k: int, k_frac: float, p_mass: float,
+                             scale: float) -> tuple:
+    """Mask of one head whose compressed score is taken between the projected
+    pooled queries and keys: s = scale * (Qbar Wq)(Kbar Wk)^T, then the hybrid
+    selection as before (p = 0 gives the router's hard Top-k)."""
+    s = block_logits(router_project(pool_mean(q, block_q), wq),
+                     router_project(pool_mean(k, block_k), wk), scale)
+    return hybrid_select(s, k_frac, p_mass), s
+
+
+def predict_mask_routed(Qb: np.ndarray, Kb: np.ndarray, Wq: np.ndarray, Wk: np.ndarray,
+                        block_q: int, block_k: int, k_frac: float, p_mass: float,
+                        scale: float) -> MaskResult:
+    """Routed mask of every (batch, head); Wq, Wk [H, d, d] float32 (per head)."""
+    B, H, N, _ = Qb.shape
+    n_q, n_k = -(-N // block_q), -(-N // block_k)
+    kept = np.zeros((B, H, n_q, n_k), bool)
+    cnt = np.zeros((B, H, n_q), np.int64)
+    logits = np.zeros((B, H, n_q, n_k))
+    margin = np.zeros((B, H, n_q))
+    m_p = np.zeros((B, H, n_q), np.int64)
+    K_k = topk_size(k_frac, n_k)
+    for b in range(B):
+        for h in range(H):
+            sel, s = predict_mask_routed_head(bf16_to_f64(Qb[b, h]), bf16_to_f64(Kb[b, h]),
+                                              Wq[h], Wk[h], block_q, block_k, k_frac, p_mass,
+                                              scale)
+            kept[b, h], cnt[b, h], logits[b, h] = sel.kept, sel.count, s
+            margin[b, h], m_p[b, h] = sel.margin, sel.m_p
+    return MaskResult(kept, cnt, logits, margin, K_k, m_p)
+
+
 def kept_to_bits(kept: np.ndarray) -> np.ndarray:
     """bool [..., n_k] -> uint32 [..., ceil(n_k/32)]: bit j%32 of word j//32."""
     n_k = kept.shape[-1]
@@ -264,3 +309,16 @@ def sparse_linear_attention_head(q, k, v, kept, block_q: int, block_k: int,
     o_s = masked_attention_head(q, k, v, kept, block_q, block_k, scale, q_blocks)
     o_l = linear_branch_head(q, k, v, kept, block_q, block_k, q_blocks)
     return o_s + float(np.float32(alpha)) * o_l
+
+
+def sla2_mix_attention_head(q, k, v, kept, block_q: int, block_k: int, scale: float,
+                            alpha, q_blocks=None):
+    """SLA2's faithful sparse-linear output for one head (SLA2 page, section 2A):
+    O = alpha (*) O_s + (1 - alpha) (*) O_l, alpha [d] (float32 values in [0, 1],
+    one per output channel, the same for every row); O_s the block-sparse
+    softmax attention, O_l the elu + 1 linear attention over the dropped keys
+    (zero when no block was dropped)."""
+    o_s = masked_attention_head(q, k, v, kept, block_q, block_k, scale, q_blocks)
+    o_l = linear_branch_head(q, k, v, kept, block_q, block_k, q_blocks)
+    a = np.asarray(alpha, np.float32).astype(np.float64)
+    return a * o_s + (1.0 - a) * o_l

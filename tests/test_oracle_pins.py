@@ -325,3 +325,94 @@ def test_linear_branch_constant_values_and_full_keep():
     np.testing.assert_array_equal(
         O.sparse_linear_attention_head(q, k, vv, full, 64, 64, 0.5, 0.1),
         O.masked_attention_head(q, k, vv, full, 64, 64, 0.5))
+
+
+# ------------------------------------------------ SLA2 router (section 2B)
+def test_router_identity_weights_give_the_plain_mask():
+    rng = np.random.default_rng(31)
+    q, k = rng.standard_normal((700, 32)), rng.standard_normal((700, 32))
+    eye = np.eye(32, dtype=np.float32)
+    sel_r, s_r = O.predict_mask_routed_head(q, k, eye, eye, 64, 64, 0.1, 0.8, 32 ** -0.5)
+    sel, s = O.predict_mask_head(q, k, 64, 64, 0.1, 0.8, 32 ** -0.5)
+    assert np.array_equal(s_r, s)          # x @ I is exact in float64
+    assert np.array_equal(sel_r.kept, sel.kept)
+
+
+def test_router_permutation_weights_keep_the_scores():
+    # Wq = Wk = P (a permutation): (Qbar P)(Kbar P)^T = Qbar Kbar^T, summed in
+    # another order; the mask is unchanged away from near ties
+    rng = np.random.default_rng(32)
+    q, k = rng.standard_normal((900, 16)), rng.standard_normal((900, 16))
+    P = np.eye(16, dtype=np.float32)[rng.permutation(16)]
+    sel_r, s_r = O.predict_mask_routed_head(q, k, P, P, 64, 64, 0.2, 0.6, 0.25)
+    sel, s = O.predict_mask_head(q, k, 64, 64, 0.2, 0.6, 0.25)
+    np.testing.assert_allclose(s_r, s, rtol=0, atol=1e-14)
+    far = sel.margin > 1e-9
+    assert far.all() and np.array_equal(sel_r.kept, sel.kept)
+
+
+def test_router_positive_scaling_keeps_the_hard_topk_set():
+    # Wq = 2I, Wk = 3I multiply every score by 6: the order, hence the hard
+    # Top-k set the router uses at inference (SLA2 section 2D), is unchanged
+    rng = np.random.default_rng(33)
+    q, k = rng.standard_normal((640, 8)), rng.standard_normal((640, 8))
+    wq, wk = 2 * np.eye(8, dtype=np.float32), 3 * np.eye(8, dtype=np.float32)
+    sel_r, s_r = O.predict_mask_routed_head(q, k, wq, wk, 64, 64, 0.3, 0.0, 0.5)
+    sel, s = O.predict_mask_head(q, k, 64, 64, 0.3, 0.0, 0.5)
+    np.testing.assert_allclose(s_r, 6 * s, rtol=0, atol=1e-13)
+    assert np.array_equal(sel_r.kept, sel.kept)
+
+
+def test_router_projection_hand_example():
+    # one query block, three key blocks of one token each, d = 2.
+    # Qbar = (1, 0); Kbar = (1, 0), (0, 1), (0.5, 0.5).
+    # unprojected: s = scale * (1, 0, 0.5) -> hard Top-1 keeps block 0.
+    # Wq swaps the two channels, Wk = I: Qbar Wq = (0, 1) -> s = scale * (0, 1, 0.5)
+    # -> Top-1 keeps block 1, Top-2 keeps {1, 2}.
+    q = np.array([[1.0, 0.0]])
+    k = np.array([[1.0, 0.0], [0.0, 1.0], [0.5, 0.5]])
+    swap = np.array([[0, 1], [1, 0]], np.float32)
+    eye = np.eye(2, dtype=np.float32)
+    sel, s = O.predict_mask_routed_head(q, k, swap, eye, 1, 1, 1 / 3, 0.0, 0.5)
+    assert s.tolist() == [[0.0, 0.5, 0.25]]
+    assert sel.kept.tolist() == [[False, True, False]]
+    sel2, _ = O.predict_mask_routed_head(q, k, swap, eye, 1, 1, 2 / 3, 0.0, 0.5)
+    assert sel2.kept.tolist() == [[False, True, True]]
+    plain, _ = O.predict_mask_head(q, k, 1, 1, 1 / 3, 0.0, 0.5)
+    assert plain.kept.tolist() == [[True, False, False]]
+
+
+# ---------------------------------------------- SLA2 faithful mix (section 2A)
+def _mix_case(seed, N=300, d=16, bq=64, bk=64):
+    rng = np.random.default_rng(seed)
+    q, k, v = (rng.standard_normal((N, d)) for _ in range(3))
+    n_q, n_k = -(-N // bq), -(-N // bk)
+    kept = rng.random((n_q, n_k)) < 0.5
+    kept[0] = True          # a row with nothing dropped
+    kept[1] = False
+    kept[1, 0] = True       # a row with one kept block
+    return q, k, v, kept
+
+
+def test_mix_extremes_are_the_two_branches():
+    q, k, v, kept = _mix_case(41)
+    o_s = O.masked_attention_head(q, k, v, kept, 64, 64, 0.25)
+    o_l = O.linear_branch_head(q, k, v, kept, 64, 64)
+    ones, zeros = np.ones(16), np.zeros(16)
+    assert np.array_equal(O.sla2_mix_attention_head(q, k, v, kept, 64, 64, 0.25, ones), o_s)
+    assert np.array_equal(O.sla2_mix_attention_head(q, k, v, kept, 64, 64, 0.25, zeros), o_l)
+
+
+def test_mix_keeps_rows_normalised():
+    # SLA2 section 2A: the mix keeps the output row-normalised. With V = 1 both
+    # branches give 1 on every row that dropped a block, so O = 1 for any alpha
+    # in [0, 1], per channel; a row that dropped nothing gives alpha (O_l = 0).
+    q, k, v, kept = _mix_case(42)
+    v = np.ones_like(v)
+    alpha = np.random.default_rng(43).random(16).astype(np.float32)
+    o = O.sla2_mix_attention_head(q, k, v, kept, 64, 64, 0.25, alpha)
+    full = kept.all(axis=1)
+    rows = np.repeat(~full, 64)[: o.shape[0]]
+    np.testing.assert_allclose(o[rows], 1.0, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(o[~rows], np.broadcast_to(alpha.astype(np.float64),
+                                                         o[~rows].shape), atol=1e-14)
