@@ -19,9 +19,11 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsparge.s
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP = 0, -1, -2, -3
 
 # every symbol the public header declares
-EXPORTS = ("sparge_mask_workspace_bytes", "sparge_mask_predict", "sparge_attn_workspace_bytes",
-           "sparge_attn_fwd", "sparge_attn_pack", "sparge_attn_fwd_packed",
-           "sparse_linear_workspace_bytes", "sparse_linear_attn_fwd", "sparge_last_error")
+EXPORTS = ("sparge_mask_workspace_bytes", "sparge_mask_predict",
+           "sparge_mask_routed_workspace_bytes", "sparge_mask_predict_routed",
+           "sparge_attn_workspace_bytes", "sparge_attn_fwd", "sparge_attn_pack",
+           "sparge_attn_fwd_packed", "sparse_linear_workspace_bytes", "sparse_linear_attn_fwd",
+           "sparge_last_error")
 
 _lib = None
 
@@ -46,6 +48,11 @@ def lib() -> ctypes.CDLL:
         L.sparge_mask_predict.argtypes = [vp, vp] + [c_int] * 6 + [c_float] * 3 + [vp] * 5 + [
             c_size, vp]
         L.sparge_mask_predict.restype = c_int
+        L.sparge_mask_routed_workspace_bytes.argtypes = [c_int] * 6
+        L.sparge_mask_routed_workspace_bytes.restype = c_size
+        L.sparge_mask_predict_routed.argtypes = [vp] * 4 + [c_int] * 6 + [c_float] * 3 + [
+            vp] * 5 + [c_size, vp]
+        L.sparge_mask_predict_routed.restype = c_int
         L.sparge_attn_workspace_bytes.argtypes = [c_int] * 4
         L.sparge_attn_workspace_bytes.restype = c_size
         L.sparge_attn_fwd.argtypes = [vp] * 5 + [c_int] * 6 + [c_float, vp, vp, c_size, vp]
@@ -122,6 +129,42 @@ def sparge_mask_predict(q, k, block_q=128, block_k=64, k_frac=0.05, p_mass=0.9, 
     _check(lib().sparge_mask_predict(
         _ptr(q), _ptr(k), B, H, N, d, block_q, block_k, k_frac, p_mass, scale,
         _ptr(bits), _ptr(idx), _ptr(cnt), _ptr(logits), _ptr(workspace),
+        workspace.numel(), _stream(q)))
+    return (bits, idx, cnt, logits) if return_logits else (bits, idx, cnt)
+
+
+def mask_routed_workspace_bytes(B, H, N, d, block_q, block_k) -> int:
+    return lib().sparge_mask_routed_workspace_bytes(B, H, N, d, block_q, block_k)
+
+
+def sparge_mask_predict_routed(q, k, w_q, w_k, block_q=128, block_k=64, k_frac=0.05,
+                               p_mass=0.0, scale=None, return_logits=False, workspace=None,
+                               out=None):
+    """Block mask scored through the router's projections (w_q, w_k float32 GPU
+    tensors [H, d, d]); outputs as sparge_mask_predict."""
+    B, H, N, d = _qkv(q, k)
+    for w in (w_q, w_k):
+        if w.dtype != torch.float32 or not w.is_cuda or tuple(w.shape) != (H, d, d):
+            raise ValueError("w_q, w_k must be float32 GPU tensors [H, d, d]")
+    w_q, w_k = w_q.contiguous(), w_k.contiguous()
+    n_q, n_k = -(-N // block_q), -(-N // block_k)
+    dev = q.device
+    if out is None:
+        bits = torch.empty((B, H, n_q, -(-n_k // 32)), dtype=torch.int32, device=dev)
+        idx = torch.empty((B, H, n_q, n_k), dtype=torch.int32, device=dev)
+        cnt = torch.empty((B, H, n_q), dtype=torch.int32, device=dev)
+    else:
+        bits, idx, cnt = out
+    logits = (torch.empty((B, H, n_q, n_k), dtype=torch.float64, device=dev)
+              if return_logits else None)
+    if workspace is None:
+        workspace = torch.empty(max(mask_routed_workspace_bytes(B, H, N, d, block_q, block_k),
+                                    16), dtype=torch.uint8, device=dev)
+    if scale is None:
+        scale = default_scale(d)
+    _check(lib().sparge_mask_predict_routed(
+        _ptr(q), _ptr(k), _ptr(w_q), _ptr(w_k), B, H, N, d, block_q, block_k, k_frac, p_mass,
+        scale, _ptr(bits), _ptr(idx), _ptr(cnt), _ptr(logits), _ptr(workspace),
         workspace.numel(), _stream(q)))
     return (bits, idx, cnt, logits) if return_logits else (bits, idx, cnt)
 

@@ -60,6 +60,15 @@ size_t mask_ws(int B, int H, int N, int d, int block_q, int block_k) {
          up(BH * n_q * n_k * sizeof(double));
 }
 
+// the routed mask adds the transposed float64 weights and the projected means
+size_t routed_mask_ws(int B, int H, int N, int d, int block_q, int block_k) {
+  const size_t BH = (size_t)B * H;
+  const size_t n_q = ceil_div(N, block_q), n_k = ceil_div(N, block_k);
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  return mask_ws(B, H, N, d, block_q, block_k) + 2 * up(BH * d * d * sizeof(double)) +
+         up(BH * n_q * d * sizeof(double)) + up(BH * n_k * d * sizeof(double));
+}
+
 int check_attn_args(const void* q, const void* k, const void* v, const int32_t* kv_idx,
                     const int32_t* kv_cnt, int B, int H, int N, int d, int block_q,
                     int block_k, float scale, const void* o) {
@@ -90,12 +99,14 @@ size_t sparge_mask_workspace_bytes(int B, int H, int N, int d, int block_q, int 
   return mask_ws(B, H, N, d, block_q, block_k);
 }
 
-int sparge_mask_predict(const void* q, const void* k, int B, int H, int N, int d, int block_q,
-                        int block_k, float k_frac, float p_mass, float scale,
-                        uint32_t* mask_bits, int32_t* kv_idx, int32_t* kv_cnt,
-                        double* block_logits, void* workspace, size_t workspace_bytes,
-                        void* stream) {
-  g_last_error.clear();
+}  // extern "C"
+
+namespace {
+// the mask, optionally with the router's projections (wq, wk both set)
+int mask_impl(const void* q, const void* k, const float* wq, const float* wk, int B, int H,
+              int N, int d, int block_q, int block_k, float k_frac, float p_mass, float scale,
+              uint32_t* mask_bits, int32_t* kv_idx, int32_t* kv_cnt, double* block_logits,
+              void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_shape(B, H, N, d, block_q, block_k);
   if (rc != SPARGE_OK) return rc;
   const int n_q = ceil_div(N, block_q), n_k = ceil_div(N, block_k);
@@ -115,7 +126,11 @@ int sparge_mask_predict(const void* q, const void* k, int B, int H, int N, int d
     return fail(SPARGE_ERR_INVALID_ARG, "mask_bits, kv_idx, kv_cnt must be 4-byte aligned");
   if (block_logits && !aligned(block_logits, 8))
     return fail(SPARGE_ERR_INVALID_ARG, "block_logits must be 8-byte aligned");
-  const size_t need = mask_ws(B, H, N, d, block_q, block_k);
+  const bool routed = wq != nullptr;
+  if (routed && (!aligned(wq, 4) || !aligned(wk, 4)))
+    return fail(SPARGE_ERR_INVALID_ARG, "w_q and w_k must be 4-byte aligned");
+  const size_t need = routed ? routed_mask_ws(B, H, N, d, block_q, block_k)
+                             : mask_ws(B, H, N, d, block_q, block_k);
   if (workspace_bytes < need) return fail(SPARGE_ERR_INVALID_ARG, "workspace too small");
 
   sparge::MaskLaunch a{};
@@ -140,12 +155,54 @@ int sparge_mask_predict(const void* q, const void* k, int B, int H, int N, int d
                  ? block_logits
                  : reinterpret_cast<double*>(ws + up(BH * n_q * d * sizeof(double)) +
                                              up(BH * n_k * d * sizeof(double)));
+  if (routed) {  // after the plain layout: W_q^T, W_k^T, projected Qbar, Kbar
+    unsigned char* r = ws + mask_ws(B, H, N, d, block_q, block_k);
+    a.wq = wq;
+    a.wk = wk;
+    a.wqT = reinterpret_cast<double*>(r);
+    a.wkT = reinterpret_cast<double*>(r + up(BH * d * d * sizeof(double)));
+    a.qbar_p = reinterpret_cast<double*>(r + 2 * up(BH * d * d * sizeof(double)));
+    a.kbar_p = reinterpret_cast<double*>(r + 2 * up(BH * d * d * sizeof(double)) +
+                                         up(BH * n_q * d * sizeof(double)));
+  }
   a.bits = mask_bits;
   a.idx = kv_idx;
   a.cnt = kv_cnt;
   const hipError_t e = sparge::launch_mask(a, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "sparge_mask_predict launch");
+  if (e != hipSuccess) return hip_fail(e, "mask prediction launch");
   return SPARGE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int sparge_mask_predict(const void* q, const void* k, int B, int H, int N, int d, int block_q,
+                        int block_k, float k_frac, float p_mass, float scale,
+                        uint32_t* mask_bits, int32_t* kv_idx, int32_t* kv_cnt,
+                        double* block_logits, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  g_last_error.clear();
+  return mask_impl(q, k, nullptr, nullptr, B, H, N, d, block_q, block_k, k_frac, p_mass, scale,
+                   mask_bits, kv_idx, kv_cnt, block_logits, workspace, workspace_bytes, stream);
+}
+
+size_t sparge_mask_routed_workspace_bytes(int B, int H, int N, int d, int block_q, int block_k) {
+  const std::string saved = g_last_error;
+  const int rc = check_shape(B, H, N, d, block_q, block_k);
+  g_last_error = saved;
+  if (rc != SPARGE_OK || ceil_div(N, block_k) > kMaxKeyBlocks) return 0;
+  return routed_mask_ws(B, H, N, d, block_q, block_k);
+}
+
+int sparge_mask_predict_routed(const void* q, const void* k, const float* w_q, const float* w_k,
+                               int B, int H, int N, int d, int block_q, int block_k,
+                               float k_frac, float p_mass, float scale, uint32_t* mask_bits,
+                               int32_t* kv_idx, int32_t* kv_cnt, double* block_logits,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (!w_q || !w_k) return fail(SPARGE_ERR_INVALID_ARG, "null pointer argument");
+  return mask_impl(q, k, w_q, w_k, B, H, N, d, block_q, block_k, k_frac, p_mass, scale,
+                   mask_bits, kv_idx, kv_cnt, block_logits, workspace, workspace_bytes, stream);
 }
 
 size_t sparge_attn_workspace_bytes(int B, int H, int N, int d) {

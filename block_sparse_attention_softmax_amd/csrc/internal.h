@@ -47,6 +47,13 @@ struct MaskLaunch {
   double* qbar;   // [B*H, n_q, d]
   double* kbar;   // [B*H, n_k, d]
   double* logits; // [B*H, n_q, n_k]
+  // router (optional): scores between Qbar Wq and Kbar Wk
+  const float* wq;  // [H, d, d] float32, row = input channel; nullptr: no router
+  const float* wk;
+  double* wqT;      // [B*H, d, d] float64, W transposed (row = output channel)
+  double* wkT;
+  double* qbar_p;   // [B*H, n_q, d] projected pooled queries
+  double* kbar_p;   // [B*H, n_k, d]
   uint32_t* bits;
   int32_t* idx;
   int32_t* cnt;

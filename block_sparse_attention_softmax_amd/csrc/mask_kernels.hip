@@ -136,6 +136,23 @@ __global__ __launch_bounds__(kThreads) void block_logits_kernel(
       }
 }
 
+// ----------------------------------------------------------- router weights
+// The router's projection weights (SLA2 page, section 2B: proj_q, proj_k on
+// the pooled queries and keys), float32 [H][d][d] with row = input channel,
+// as float64 W^T for every (b, h): wt[bh][j][c] = W[h][c][j]. The projection
+// Xbar W is then the same "rows of A against rows of B" product as the block
+// scores and runs in block_logits_kernel with scale 1.
+__global__ __launch_bounds__(kThreads) void router_weights_kernel(const float* __restrict__ w,
+                                                                  double* __restrict__ wt,
+                                                                  int H, int d) {
+  const int bh = blockIdx.y, h = bh % H;
+  const int dd = d * d;
+  for (int e = blockIdx.x * kThreads + threadIdx.x; e < dd; e += gridDim.x * kThreads) {
+    const int j = e / d, c = e % d;
+    wt[(size_t)bh * dd + e] = (double)w[(size_t)h * dd + (size_t)c * d + j];
+  }
+}
+
 // ------------------------------------------------------- wave-level helpers
 __device__ __forceinline__ double wave_max(double v) {
 #pragma unroll
@@ -472,18 +489,33 @@ hipError_t launch_select(const MaskLaunch& a, hipStream_t st) {
 
 hipError_t launch_mask(const MaskLaunch& a, hipStream_t st) {
   const int BH = a.B * a.H;
-  const int tq = (a.n_q + 31) / 32, tk = (a.n_k + 31) / 32, tiles = BH * tq * tk;
-  if (a.d == 128) {
+  auto scores = [&](const double* x, const double* y, double* out, int nx, int ny, double sc) {
+    const int tq = (nx + 31) / 32, tk = (ny + 31) / 32, tiles = BH * tq * tk;
+    if (a.d == 128)
+      hipLaunchKernelGGL(block_logits_kernel<128>, dim3((tiles + 3) / 4), dim3(kThreads), 0, st,
+                         x, y, out, nx, ny, tq, tk, tiles, sc);
+    else
+      hipLaunchKernelGGL(block_logits_kernel<64>, dim3((tiles + 3) / 4), dim3(kThreads), 0, st,
+                         x, y, out, nx, ny, tq, tk, tiles, sc);
+  };
+  if (a.d == 128)
     hipLaunchKernelGGL(pool_mean_kernel<128>, dim3(a.n_q + a.n_k, BH), dim3(kThreads), 0, st,
                        a.q, a.k, a.qbar, a.kbar, a.N, a.block_q, a.block_k, a.n_q, a.n_k);
-    hipLaunchKernelGGL(block_logits_kernel<128>, dim3((tiles + 3) / 4), dim3(kThreads), 0, st,
-                       a.qbar, a.kbar, a.logits, a.n_q, a.n_k, tq, tk, tiles, a.scale);
-  } else {
+  else
     hipLaunchKernelGGL(pool_mean_kernel<64>, dim3(a.n_q + a.n_k, BH), dim3(kThreads), 0, st,
                        a.q, a.k, a.qbar, a.kbar, a.N, a.block_q, a.block_k, a.n_q, a.n_k);
-    hipLaunchKernelGGL(block_logits_kernel<64>, dim3((tiles + 3) / 4), dim3(kThreads), 0, st,
-                       a.qbar, a.kbar, a.logits, a.n_q, a.n_k, tq, tk, tiles, a.scale);
+  const double* qs = a.qbar;
+  const double* ks = a.kbar;
+  if (a.wq) {  // router: project the pooled rows first (float64, scale 1)
+    const dim3 wgrid((a.d * a.d + kThreads - 1) / kThreads, BH);
+    hipLaunchKernelGGL(router_weights_kernel, wgrid, dim3(kThreads), 0, st, a.wq, a.wqT, a.H, a.d);
+    hipLaunchKernelGGL(router_weights_kernel, wgrid, dim3(kThreads), 0, st, a.wk, a.wkT, a.H, a.d);
+    scores(a.qbar, a.wqT, a.qbar_p, a.n_q, a.d, 1.0);
+    scores(a.kbar, a.wkT, a.kbar_p, a.n_k, a.d, 1.0);
+    qs = a.qbar_p;
+    ks = a.kbar_p;
   }
+  scores(qs, ks, a.logits, a.n_q, a.n_k, a.scale);
   switch (a.npad) {
     case 64: return launch_select_reg<64>(a, st);
     case 128: return launch_select_reg<128>(a, st);

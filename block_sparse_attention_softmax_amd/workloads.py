@@ -175,3 +175,13 @@ def generate(wl: Workload, threads: int | None = None):
 
 def sha256(a: np.ndarray) -> str:
     return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
+
+
+def router_weights(H: int, d: int, seed: int) -> tuple:
+    """Synthetic weights for the router's two projections (trained weights are
+    not available): float32 [H, d, d] each, entries N(0, 1) / sqrt(d) from a
+    PCG64 stream of `seed` (W_q drawn first, then W_k)."""
+    rng = np.random.default_rng(seed)
+    wq = (rng.standard_normal((H, d, d)) / np.sqrt(d)).astype(np.float32)
+    wk = (rng.standard_normal((H, d, d)) / np.sqrt(d)).astype(np.float32)
+    return wq, wk

@@ -93,6 +93,31 @@ int sparge_mask_predict(const void* q, const void* k, int B, int H, int N, int d
                         int32_t* kv_cnt, double* block_logits, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/* Device workspace (bytes) of sparge_mask_predict_routed: that of
+ * sparge_mask_predict plus the router weights as float64 and the projected
+ * pooled queries and keys. Returns 0 for arguments it would reject. */
+size_t sparge_mask_routed_workspace_bytes(int B, int H, int N, int d, int block_q,
+                                          int block_k);
+
+/* Block mask whose compressed score goes through a router, as in "SLA2:
+ * Sparse-Linear Attention with Learnable Routing and QAT", section 2B: the
+ * pooled queries and keys are projected by learnable linear maps before the
+ * score, s_ij = scale * <Qbar_i W_q[h], Kbar_j W_k[h]>; the selection that
+ * follows is the hybrid rule of sparge_mask_predict (p_mass = 0 gives the
+ * router's hard Top-k, section 2D). Projections and scores are float64.
+ *
+ *  w_q, w_k : float32 [H, d, d], device, 4-byte aligned; per head, row c =
+ *             input channel, column j = output channel (Xbar W).
+ *  workspace: at least sparge_mask_routed_workspace_bytes(), 16-byte aligned.
+ *  Other arguments and outputs as for sparge_mask_predict.
+ */
+int sparge_mask_predict_routed(const void* q, const void* k, const float* w_q,
+                               const float* w_k, int B, int H, int N, int d, int block_q,
+                               int block_k, float k_frac, float p_mass, float scale,
+                               uint32_t* mask_bits, int32_t* kv_idx, int32_t* kv_cnt,
+                               double* block_logits, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
 /* Device workspace (bytes) that sparge_attn_fwd needs: V re-packed per
  * 64-key block into key-contiguous rows (bf16, B*H*ceil(N/64)*64*d values).
  * Returns 0 for arguments that sparge_attn_fwd would reject. */

@@ -138,3 +138,31 @@ def test_error_message_is_per_call():
     assert "d must be" in binding.lib().sparge_last_error().decode()
     assert _mask(kf=0.0) == -1
     assert "k_frac" in binding.lib().sparge_last_error().decode()
+
+
+def test_routed_mask_workspace_bytes():
+    L = binding.lib()
+    up = lambda x: (x + 255) // 256 * 256
+    B, H, N, d = 1, 12, 32760, 128
+    n_q, n_k = math.ceil(N / 128), math.ceil(N / 64)
+    plain = L.sparge_mask_workspace_bytes(B, H, N, d, 128, 64)
+    want = plain + 2 * up(B * H * d * d * 8) + up(B * H * n_q * d * 8) + up(B * H * n_k * d * 8)
+    assert L.sparge_mask_routed_workspace_bytes(B, H, N, d, 128, 64) == want
+    assert L.sparge_mask_routed_workspace_bytes(1, 1, 100, 96, 128, 64) == 0
+
+
+def _routed(**kw):
+    args = dict(q=A, k=A, wq=A, wk=A, B=1, H=2, N=1024, d=64, bq=64, bk=64, kf=0.1, p=0.9,
+                sc=0.125, bits=A, idx=A, cnt=A, logits=None, ws=A, wsb=1 << 30, st=None)
+    args.update(kw)
+    return binding.lib().sparge_mask_predict_routed(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(wq=None), -1), (dict(wk=None), -1), (dict(wq=ctypes.c_void_p(0x10002)), -1),
+    (dict(d=96), -2), (dict(kf=0.0), -1), (dict(q=None), -1),
+    (dict(wsb=binding.lib().sparge_mask_workspace_bytes(1, 2, 1024, 64, 64, 64)), -1),
+])
+def test_routed_mask_rejects_bad_arguments(kw, code):
+    assert _routed(**kw) == code
+    assert binding.lib().sparge_last_error().decode()

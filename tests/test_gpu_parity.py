@@ -109,6 +109,38 @@ def test_uniform_rows_keep_lowest_indices():
     assert (idx.cpu()[..., :2] == torch.tensor([0, 1], dtype=torch.int32)).all()
 
 
+# ------------------------------------------------- routed mask (SLA2 router)
+@pytest.mark.parametrize("name,k_frac,p_mass", [("tiny", None, None), ("wan1.3b", None, None),
+                                                ("wan1.3b", 0.10, 0.0)])
+def test_routed_mask_matches_oracle(name, k_frac, p_mass):
+    from block_sparse_attention_softmax_amd.workloads import router_weights
+    wl, Q, K, V, q, k, v = workload_tensors(name)
+    k_frac = wl.k_frac if k_frac is None else k_frac
+    p_mass = wl.p_mass if p_mass is None else p_mass
+    wq, wk = router_weights(wl.H, wl.d, 77)
+    bits, idx, cnt, logits = S.sparge_mask_predict_routed(
+        q, k, torch.from_numpy(wq).cuda(), torch.from_numpy(wk).cuda(), wl.block_q, wl.block_k,
+        k_frac, p_mass, wl.scale, return_logits=True)
+    torch.cuda.synchronize()
+    kept = gpu_bits_to_bool(bits, wl.n_k)
+    check_index_list(kept, idx.cpu().numpy(), cnt.cpu().numpy())
+    m = O.predict_mask_routed(Q, K, wq, wk, wl.block_q, wl.block_k, k_frac, p_mass, wl.scale)
+    np.testing.assert_allclose(logits.cpu().numpy(), m.logits, rtol=1e-12, atol=1e-12)
+    ties, differ = compare_masks(m, kept, k_frac, p_mass)
+    print(f"\n[routed mask] {name} k={k_frac} p={p_mass}: sparsity {1 - kept.mean():.4f} "
+          f"near-tie rows {ties} differing {differ}", flush=True)
+
+
+def test_routed_mask_with_identity_weights_is_the_plain_mask():
+    wl, Q, K, V, q, k, v = workload_tensors("wan1.3b")
+    eye = torch.eye(wl.d, dtype=torch.float32, device="cuda").expand(wl.H, wl.d, wl.d)
+    r = S.sparge_mask_predict_routed(q, k, eye.contiguous(), eye.contiguous(), wl.block_q,
+                                     wl.block_k, wl.k_frac, wl.p_mass, wl.scale)
+    p = S.sparge_mask_predict(q, k, wl.block_q, wl.block_k, wl.k_frac, wl.p_mass, wl.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(r[0], p[0]) and torch.equal(r[2], p[2])
+
+
 # --------------------------------------------------------------- attention
 def _random_lists(rng, B, H, n_q, n_k):
     kept = rng.random((B, H, n_q, n_k)) < rng.uniform(0.05, 0.7)
