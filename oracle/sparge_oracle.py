@@ -31,7 +31,10 @@ What it computes, step by step, in float64 with NumPy, written from the pages:
 9. the SLA2 variants: the router's learnable linear projections of the pooled
    queries and keys before the compressed score (SLA2 page, section 2B; hard
    Top-k at inference, section 2D), and the faithful mix O = alpha (*) O_s +
-   (1 - alpha) (*) O_l with a learned vector alpha in [0, 1] (section 2A).
+   (1 - alpha) (*) O_l with a learned vector alpha in [0, 1] (section 2A);
+10. post-tuning branch dropping (SALAD page): a head whose linear branch
+   carries only small weights loses the branch, and its output is what the
+   formula gives with the linear term removed.
 
 Readings of points the pages leave open (each also listed in the design
 notes): mean pooling over the valid tokens of a partial last block; no
@@ -39,7 +42,10 @@ correction of the short last key block's score; K_k = min(n_k, max(1,
 ceil(k * n_k - 1e-6))) computed from the float32 value of k; Top-p keeps the
 block that crosses p (C_m >= p) and p >= 1 keeps every block; rows whose kept
 list is empty produce zeros; the linear branch's phi is applied to the
-unscaled Q and K and its output is zero when no block was dropped.
+unscaled Q and K and its output is zero when no block was dropped; alpha of
+the mix is one value per output channel of a head; a branch counts as small
+when every one of its weights (alpha[h] of the added form, 1 - alpha[h, c] of
+the mix, each taken in float32) has magnitude <= a caller's threshold tau.
 """
 from __future__ import annotations
 
@@ -322,3 +328,37 @@ def sla2_mix_attention_head(q, k, v, kept, block_q: int, block_k: int, scale: fl
     o_l = linear_branch_head(q, k, v, kept, block_q, block_k, q_blocks)
     a = np.asarray(alpha, np.float32).astype(np.float64)
     return a * o_s + (1.0 - a) * o_l
+
+
+# ----------------------------------------------------- SALAD branch dropping
+def linear_branch_dropped(weights, tau: float) -> bool:
+    """Post-tuning branch dropping (SALAD page): the linear branch of a head is
+    removed when its scale is small. Reading: removed iff every weight it is
+    multiplied by has magnitude <= tau; the weights and the comparison are
+    taken in float32, so tau = 0 removes only a branch whose weights are all
+    exactly zero, which changes no output value."""
+    w = np.abs(np.asarray(weights, np.float32))
+    return bool(np.max(w) <= np.float32(tau))
+
+
+def linear_weights_of_mix(alpha) -> np.ndarray:
+    """The per-channel weights of O_l in the SLA2 mix, 1 - alpha, in float32."""
+    return np.float32(1.0) - np.asarray(alpha, np.float32)
+
+
+def sparse_linear_attention_head_dropping(q, k, v, kept, block_q: int, block_k: int,
+                                          scale: float, alpha: float, tau: float,
+                                          q_blocks=None):
+    """O = O_s + alpha * O_l, or O_s alone when the branch is dropped."""
+    if linear_branch_dropped([alpha], tau):
+        return masked_attention_head(q, k, v, kept, block_q, block_k, scale, q_blocks)
+    return sparse_linear_attention_head(q, k, v, kept, block_q, block_k, scale, alpha, q_blocks)
+
+
+def sla2_mix_attention_head_dropping(q, k, v, kept, block_q: int, block_k: int, scale: float,
+                                     alpha, tau: float, q_blocks=None):
+    """The SLA2 mix, or alpha (*) O_s alone when its linear term is dropped."""
+    if linear_branch_dropped(linear_weights_of_mix(alpha), tau):
+        a = np.asarray(alpha, np.float32).astype(np.float64)
+        return a * masked_attention_head(q, k, v, kept, block_q, block_k, scale, q_blocks)
+    return sla2_mix_attention_head(q, k, v, kept, block_q, block_k, scale, alpha, q_blocks)

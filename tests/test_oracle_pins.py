@@ -416,3 +416,57 @@ def test_mix_keeps_rows_normalised():
     np.testing.assert_allclose(o[rows], 1.0, rtol=0, atol=1e-14)
     np.testing.assert_allclose(o[~rows], np.broadcast_to(alpha.astype(np.float64),
                                                          o[~rows].shape), atol=1e-14)
+
+
+# -------------------------------------- SALAD post-tuning branch dropping
+def test_dropping_an_exactly_zero_branch_changes_nothing():
+    # tau = 0 removes only a branch whose weights are all zero, so the output
+    # is the evaluated formula's, bit for bit: O_s + 0 * O_l and 1 * O_s + 0 * O_l
+    q, k, v, kept = _mix_case(51)
+    add = O.sparse_linear_attention_head(q, k, v, kept, 64, 64, 0.25, 0.0)
+    assert np.array_equal(
+        O.sparse_linear_attention_head_dropping(q, k, v, kept, 64, 64, 0.25, 0.0, 0.0), add)
+    ones = np.ones(16, np.float32)
+    mix = O.sla2_mix_attention_head(q, k, v, kept, 64, 64, 0.25, ones)
+    assert np.array_equal(
+        O.sla2_mix_attention_head_dropping(q, k, v, kept, 64, 64, 0.25, ones, 0.0), mix)
+    # and the dropped output is the sparse branch alone
+    assert np.array_equal(add, O.masked_attention_head(q, k, v, kept, 64, 64, 0.25))
+
+
+def test_drop_decision_threshold_and_magnitude():
+    t = np.float32(0.1)
+    above = np.nextafter(t, np.float32(1))
+    assert O.linear_branch_dropped([t], 0.1)            # equal to tau: small
+    assert not O.linear_branch_dropped([above], 0.1)
+    assert O.linear_branch_dropped([-0.05], 0.1)        # magnitude, not sign
+    assert not O.linear_branch_dropped([-0.2], 0.1)
+    assert not O.linear_branch_dropped([0.0], -1.0)     # a negative tau drops nothing
+    # one large channel keeps the whole branch (the largest weight decides)
+    alpha = np.ones(16, np.float32)
+    alpha[7] = 0.5
+    assert not O.linear_branch_dropped(O.linear_weights_of_mix(alpha), 0.1)
+    alpha[7] = 0.95
+    assert O.linear_branch_dropped(O.linear_weights_of_mix(alpha), 0.1)
+    # 1 - alpha is taken in float32: alpha = 1 - 2^-24 gives exactly 2^-24
+    a = np.float32(1) - np.float32(2.0 ** -24)
+    assert O.linear_weights_of_mix([a])[0] == np.float32(2.0 ** -24)
+    assert not O.linear_branch_dropped(O.linear_weights_of_mix([a]), 0.0)
+
+
+def test_dropped_mix_removes_the_linear_term_without_renormalising():
+    # V = 1: the evaluated mix gives 1 on rows that dropped a block (the branches
+    # sum to 1); with the linear term removed the same rows give alpha
+    q, k, v, kept = _mix_case(52)
+    v = np.ones_like(v)
+    alpha = np.full(16, 0.97, np.float32)
+    kept_rows = np.repeat(~kept.all(axis=1), 64)[: q.shape[0]]
+    o = O.sla2_mix_attention_head_dropping(q, k, v, kept, 64, 64, 0.25, alpha, 0.05)
+    np.testing.assert_allclose(o, float(np.float32(0.97)), rtol=0, atol=1e-14)
+    o = O.sla2_mix_attention_head_dropping(q, k, v, kept, 64, 64, 0.25, alpha, 0.01)
+    np.testing.assert_allclose(o[kept_rows], 1.0, rtol=0, atol=1e-14)
+    # the additive form loses alpha * O_l: with V = 1, 1 + alpha -> 1
+    o = O.sparse_linear_attention_head_dropping(q, k, v, kept, 64, 64, 0.25, 0.04, 0.05)
+    np.testing.assert_allclose(o, 1.0, rtol=0, atol=1e-14)
+    o = O.sparse_linear_attention_head_dropping(q, k, v, kept, 64, 64, 0.25, 0.06, 0.05)
+    np.testing.assert_allclose(o[kept_rows], 1.0 + float(np.float32(0.06)), rtol=0, atol=1e-14)
