@@ -23,7 +23,7 @@ EXPORTS = ("sparge_mask_workspace_bytes", "sparge_mask_predict",
            "sparge_mask_routed_workspace_bytes", "sparge_mask_predict_routed",
            "sparge_attn_workspace_bytes", "sparge_attn_fwd", "sparge_attn_pack",
            "sparge_attn_fwd_packed", "sparse_linear_workspace_bytes", "sparse_linear_attn_fwd",
-           "sparge_last_error")
+           "sla2_mix_attn_fwd", "sparge_last_error")
 
 _lib = None
 
@@ -63,9 +63,9 @@ def lib() -> ctypes.CDLL:
         L.sparge_attn_fwd_packed.restype = c_int
         L.sparse_linear_workspace_bytes.argtypes = [c_int] * 4
         L.sparse_linear_workspace_bytes.restype = c_size
-        L.sparse_linear_attn_fwd.argtypes = [vp] * 6 + [c_int] * 6 + [c_float, vp, vp, c_size,
-                                                                       vp]
-        L.sparse_linear_attn_fwd.restype = c_int
+        for f in (L.sparse_linear_attn_fwd, L.sla2_mix_attn_fwd):
+            f.argtypes = [vp] * 6 + [c_int] * 6 + [c_float, c_float, vp, vp, c_size, vp]
+            f.restype = c_int
         L.sparge_last_error.argtypes = []
         L.sparge_last_error.restype = ctypes.c_char_p
         _lib = L
@@ -217,20 +217,38 @@ def linear_workspace_bytes(B, H, N, d) -> int:
     return lib().sparse_linear_workspace_bytes(B, H, N, d)
 
 
-def sparse_linear_attn_fwd(q, k, v, kv_idx, kv_cnt, alpha, block_q=128, block_k=64,
-                           scale=None, workspace=None, out=None):
-    """Sparse attention plus alpha[h] times elu+1 linear attention over dropped blocks."""
+def _linear(fn, q, k, v, kv_idx, kv_cnt, alpha, block_q, block_k, scale, drop_below,
+            workspace, out):
     B, H, N, d = _qkv(q, k, v)
-    if alpha.dtype != torch.float32 or not alpha.is_cuda or alpha.numel() != H:
-        raise ValueError("alpha must be a float32 GPU tensor of H values")
     o = torch.empty_like(q) if out is None else out
     if scale is None:
         scale = default_scale(d)
     ws_bytes = linear_workspace_bytes(B, H, N, d)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
-    _check(lib().sparse_linear_attn_fwd(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(kv_idx), _ptr(kv_cnt), _ptr(alpha.contiguous()), B, H,
-        N, d, block_q, block_k, scale, _ptr(o), _ptr(workspace), workspace.numel(),
-        _stream(q)))
+    _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_idx), _ptr(kv_cnt), _ptr(alpha), B, H, N, d,
+              block_q, block_k, scale, drop_below, _ptr(o), _ptr(workspace), workspace.numel(),
+              _stream(q)))
     return o
+
+
+def sparse_linear_attn_fwd(q, k, v, kv_idx, kv_cnt, alpha, block_q=128, block_k=64,
+                           scale=None, drop_below=0.0, workspace=None, out=None):
+    """Sparse attention plus alpha[h] times elu+1 linear attention over dropped blocks;
+    heads with |alpha[h]| <= drop_below skip the linear branch."""
+    H = q.shape[1]
+    if alpha.dtype != torch.float32 or not alpha.is_cuda or alpha.numel() != H:
+        raise ValueError("alpha must be a float32 GPU tensor of H values")
+    return _linear(lib().sparse_linear_attn_fwd, q, k, v, kv_idx, kv_cnt, alpha.contiguous(),
+                   block_q, block_k, scale, drop_below, workspace, out)
+
+
+def sla2_mix_attn_fwd(q, k, v, kv_idx, kv_cnt, alpha, block_q=128, block_k=64, scale=None,
+                      drop_below=0.0, workspace=None, out=None):
+    """SLA2 mix alpha[h][c] O_s + (1 - alpha[h][c]) O_l; alpha float32 [H, d] on the GPU.
+    Heads with every |1 - alpha[h][c]| <= drop_below skip the linear branch."""
+    H, d = q.shape[1], q.shape[3]
+    if alpha.dtype != torch.float32 or not alpha.is_cuda or tuple(alpha.shape) != (H, d):
+        raise ValueError("alpha must be a float32 GPU tensor of shape [H, d]")
+    return _linear(lib().sla2_mix_attn_fwd, q, k, v, kv_idx, kv_cnt, alpha.contiguous(),
+                   block_q, block_k, scale, drop_below, workspace, out)

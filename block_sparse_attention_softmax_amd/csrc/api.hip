@@ -300,15 +300,20 @@ size_t sparse_linear_workspace_bytes(int B, int H, int N, int d) {
   return sparge::linear_workspace_bytes(B, H, N, d);
 }
 
-int sparse_linear_attn_fwd(const void* q, const void* k, const void* v,
-                           const int32_t* kv_idx, const int32_t* kv_cnt, const float* alpha,
-                           int B, int H, int N, int d, int block_q, int block_k, float scale,
-                           void* o, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int linear_impl(const char* name, int mode, const void* q, const void* k, const void* v,
+                const int32_t* kv_idx, const int32_t* kv_cnt, const float* alpha, int B, int H,
+                int N, int d, int block_q, int block_k, float scale, float drop_below, void* o,
+                void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error.clear();
   int rc = check_attn_args(q, k, v, kv_idx, kv_cnt, B, H, N, d, block_q, block_k, scale, o);
   if (rc != SPARGE_OK) return rc;
   if (!alpha || !workspace) return fail(SPARGE_ERR_INVALID_ARG, "null pointer argument");
-  if (!aligned(alpha, 4) || !aligned(workspace, 16))
+  // the mix reads alpha[h][4c .. 4c+3] as one 16-byte load
+  if (!aligned(alpha, mode == sparge::kLinMix ? 16 : 4) || !aligned(workspace, 16))
     return fail(SPARGE_ERR_INVALID_ARG, "alpha / workspace misaligned");
   if (workspace_bytes < sparge::linear_workspace_bytes(B, H, N, d))
     return fail(SPARGE_ERR_INVALID_ARG, "workspace too small");
@@ -326,6 +331,8 @@ int sparse_linear_attn_fwd(const void* q, const void* k, const void* v,
   a.n_k = ceil_div(N, block_k);
   a.scale = scale;
   a.alpha = alpha;
+  a.lin_mode = mode;
+  a.drop_below = drop_below;
   const size_t BH = (size_t)B * H, packed = sparge::attn_workspace_bytes(B, H, N, d);
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   a.vt = reinterpret_cast<uint16_t*>(ws);
@@ -335,9 +342,33 @@ int sparse_linear_attn_fwd(const void* q, const void* k, const void* v,
   a.lin_z = a.lin_h + BH * d * d;
   a.part_h = a.lin_z + BH * d;
   a.part_z = a.part_h + BH * sparge::kLinSplit * d * d;
+  a.lin_on = reinterpret_cast<int32_t*>(a.part_z + BH * sparge::kLinSplit * d);
   const hipError_t e = sparge::launch_attn(a, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "sparse_linear_attn_fwd launch");
+  if (e != hipSuccess) return hip_fail(e, name);
   return SPARGE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sparse_linear_attn_fwd(const void* q, const void* k, const void* v,
+                           const int32_t* kv_idx, const int32_t* kv_cnt, const float* alpha,
+                           int B, int H, int N, int d, int block_q, int block_k, float scale,
+                           float drop_below, void* o, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  return linear_impl("sparse_linear_attn_fwd launch", sparge::kLinAdd, q, k, v, kv_idx, kv_cnt,
+                     alpha, B, H, N, d, block_q, block_k, scale, drop_below, o, workspace,
+                     workspace_bytes, stream);
+}
+
+int sla2_mix_attn_fwd(const void* q, const void* k, const void* v, const int32_t* kv_idx,
+                      const int32_t* kv_cnt, const float* alpha, int B, int H, int N, int d,
+                      int block_q, int block_k, float scale, float drop_below, void* o,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  return linear_impl("sla2_mix_attn_fwd launch", sparge::kLinMix, q, k, v, kv_idx, kv_cnt,
+                     alpha, B, H, N, d, block_q, block_k, scale, drop_below, o, workspace,
+                     workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -42,7 +42,8 @@ __device__ __forceinline__ int packed_key(int slot) {
 __device__ __forceinline__ float elu1(float x) { return x > 0.0f ? x + 1.0f : expf(x); }
 
 // vt[bh][j][d][slot] = V[bh][64*j + packed_key(slot)][d], zero past N; with
-// LIN also phikt[...] = bf16(phi(K[...])) in the same layout.
+// LIN also phikt[...] = bf16(phi(K[...])) in the same layout, for the heads
+// whose linear branch is evaluated (lin_on).
 // grid (n_k, B*H), 2*D threads; one 64-key block per workgroup. Thread t
 // takes keys 4q..4q+3 (q = t % 16) at d = 8c..8c+7 (c = t / 16): four 16-byte
 // rows in, transposed in registers, eight 8-byte pieces out. The four keys
@@ -53,13 +54,15 @@ __global__ __launch_bounds__(2 * D) void pack_kernel(const uint16_t* __restrict_
                                                      const uint16_t* __restrict__ k,
                                                      uint16_t* __restrict__ vt,
                                                      uint16_t* __restrict__ phikt, int N,
-                                                     int n_k) {
+                                                     int n_k, const int32_t* __restrict__ lin_on,
+                                                     int H) {
   const int j = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
   const int q = t & 15, c = t >> 4;
   // slot of key 4q: group q/4, then the inverse of packed_key within it
   const int slot0 = 16 * (q >> 2) + 8 * (q & 1) + 4 * ((q >> 1) & 1);
 #pragma unroll
   for (int w = 0; w < (LIN ? 2 : 1); ++w) {
+    if (w == 1 && !lin_on[bh % H]) break;  // the head's linear branch is dropped
     const uint16_t* src = (w == 0 ? v : k) + ((size_t)bh * N + (size_t)j * BK) * D + c * 8;
     uint32_t x[4][4];
 #pragma unroll
@@ -177,9 +180,12 @@ __global__ __launch_bounds__(D * 2) void linear_total_kernel(const uint16_t* __r
                                                              const uint16_t* __restrict__ vt,
                                                              float* __restrict__ part_h,
                                                              float* __restrict__ part_z,
-                                                             int n_k) {
+                                                             int n_k,
+                                                             const int32_t* __restrict__ lin_on,
+                                                             int H) {
   constexpr int DT = D / 32;
   const int split = blockIdx.x, bh = blockIdx.y;
+  if (!lin_on[bh % H]) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h2 = lane >> 5, l32 = lane & 31;
   floatx16 hacc[DT];
@@ -221,8 +227,11 @@ template <int D>
 __global__ __launch_bounds__(256) void linear_reduce_kernel(const float* __restrict__ part_h,
                                                             const float* __restrict__ part_z,
                                                             float* __restrict__ lin_h,
-                                                            float* __restrict__ lin_z) {
+                                                            float* __restrict__ lin_z,
+                                                            const int32_t* __restrict__ lin_on,
+                                                            int H) {
   const int bh = blockIdx.x;
+  if (!lin_on[bh % H]) return;
   for (int e = threadIdx.x; e < D * D + D; e += 256) {
     float acc = 0.0f;
     if (e < D * D) {
@@ -234,6 +243,24 @@ __global__ __launch_bounds__(256) void linear_reduce_kernel(const float* __restr
       lin_z[(size_t)bh * D + a] = acc;
     }
   }
+}
+
+// lin_on[h] = 1 unless every weight that head h's linear branch is multiplied
+// by (alpha[h]; 1 - alpha[h][c] in the mix, float32) has magnitude <= the
+// threshold: post-tuning branch dropping (SALAD page). A NaN weight keeps it.
+__global__ __launch_bounds__(64) void linear_flags_kernel(const float* __restrict__ alpha,
+                                                          int mode, int D, float drop_below,
+                                                          int32_t* __restrict__ lin_on) {
+  const int h = blockIdx.x, lane = threadIdx.x;
+  bool keep = false;
+  if (mode == kLinAdd) {
+    keep = lane == 0 && !(fabsf(alpha[h]) <= drop_below);
+  } else {
+    for (int c = lane; c < D; c += 64)
+      keep = keep || !(fabsf(1.0f - alpha[(size_t)h * D + c]) <= drop_below);
+  }
+  keep = __any(keep);
+  if (lane == 0) lin_on[h] = keep ? 1 : 0;
 }
 
 // ------------------------------------------------------ attention kernel
@@ -259,15 +286,22 @@ __global__ __launch_bounds__(256) void linear_reduce_kernel(const float* __restr
 // the same index (three-term split-bf16 MFMA product, about 16 significant
 // bits per operand), and hand O_l and the scale alpha[h] / (phi(Q) . z_D)
 // over through LDS in the attention wave's own register layout; the
-// attention wave writes O = O_s + alpha[h] * O_l.
-template <int D, int BQ, bool LIN>
+// attention wave writes O = O_s + alpha[h] * O_l, or in the SLA2 mix (SLA2
+// page, section 2A) O = alpha[h][c] O_s + (1 - alpha[h][c]) O_l with the
+// scale 1 / (phi(Q) . z_D). Heads whose branch is dropped (lin_on = 0) exit
+// at once here and run in a second launch of the plain kernel, which scales
+// O_s by alpha[h][c] in the mix.
+//
+// SEL (always with LIN) adds the head selection and the alpha scaling of the
+// epilogue; the plain kernel without it is compiled without either.
+template <int D, int BQ, bool LIN, bool SEL = LIN>
 __global__ __launch_bounds__(BQ * (LIN ? 4 : 2), (LIN || (D == 128 && BQ == 64)) ? 1 : 2) void sparse_attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ vt, const int32_t* __restrict__ kv_idx,
     const int32_t* __restrict__ kv_cnt, uint16_t* __restrict__ o, int H, int N, int n_q,
     int n_k, int total, float c, const float* __restrict__ alpha,
     const uint16_t* __restrict__ phikt, const float* __restrict__ lin_h,
-    const float* __restrict__ lin_z) {
+    const float* __restrict__ lin_z, const int32_t* __restrict__ head_sel, int lin_mode) {
   constexpr int NW = BQ / 32;
   using T = Tile<D>;
   constexpr int LOADS = BK * D / 8 / 64 / NW;
@@ -283,6 +317,11 @@ __global__ __launch_bounds__(BQ * (LIN ? 4 : 2), (LIN || (D == 128 && BQ == 64))
 
   const int tile = xcd_remap(blockIdx.x, total);
   const int bh = tile / n_q, qi = tile % n_q;
+  // with a head selection, LIN runs the heads whose linear branch is on and
+  // the plain kernel the others
+  if constexpr (SEL) {
+    if ((head_sel[bh % H] != 0) != LIN) return;
+  }
   const int t = threadIdx.x, lane = t & 63;
   const int wave_id = __builtin_amdgcn_readfirstlane(t >> 6);
   // LIN: waves NW.. are H waves (H_kept and z_kept for the d rows 32*wave..);
@@ -582,7 +621,7 @@ __global__ __launch_bounds__(BQ * (LIN ? 4 : 2), (LIN || (D == 128 && BQ == 64))
     }
   }
 
-  // ---- epilogue: O = O^T / l (+ alpha * O_l), bf16, rows < N only
+  // ---- epilogue: O = O^T / l, with the linear branch or alpha as above; bf16, rows < N only
   const float ltot = pair_sum(lsum);  // (H waves: z_kept entry 32*wave + l32)
   const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
   // LIN: O_l for this lane's (d, query) entries, in the oacc layout, and
@@ -656,7 +695,7 @@ __global__ __launch_bounds__(BQ * (LIN ? 4 : 2), (LIN || (D == 128 && BQ == 64))
         }
       }
       den = pair_sum(den);
-      lin_scale = den > 0.0f ? alpha[bh % H] / den : 0.0f;
+      lin_scale = den > 0.0f ? (lin_mode == kLinMix ? 1.0f : alpha[bh % H]) / den : 0.0f;
     }
     __syncthreads();  // every H wave is done reading H_D^T
     if (dropped && hwave) {
@@ -685,15 +724,30 @@ __global__ __launch_bounds__(BQ * (LIN ? 4 : 2), (LIN || (D == 128 && BQ == 64))
         float y[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) y[e] = oacc[i][4 * g + e] * inv;
+        // mix: alpha[h][d0..d0+3] (plain kernel: the scale of a dropped branch's alpha O_s)
+        const bool mix = SEL && (LIN ? lin_mode == kLinMix : alpha != nullptr);
+        float a[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+        if (mix) {
+          const float4 a4 = *reinterpret_cast<const float4*>(alpha + (size_t)(bh % H) * D + d0);
+          a[0] = a4.x; a[1] = a4.y; a[2] = a4.z; a[3] = a4.w;
+        }
+        bool have_l = false;
+        float lv[4] = {0.0f, 0.0f, 0.0f, 0.0f}, sl = 0.0f;
         if constexpr (LIN) {
           if (yl) {
             const float4 l = yl[((wave * DT + i) * 4 + g) * 64 + lane];
-            const float sl = ys[wave * 64 + lane];
-            y[0] = fmaf(l.x, sl, y[0]);
-            y[1] = fmaf(l.y, sl, y[1]);
-            y[2] = fmaf(l.z, sl, y[2]);
-            y[3] = fmaf(l.w, sl, y[3]);
+            lv[0] = l.x; lv[1] = l.y; lv[2] = l.z; lv[3] = l.w;
+            sl = ys[wave * 64 + lane];
+            have_l = true;
           }
+        }
+        if (mix) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            y[e] = have_l ? fmaf(a[e], y[e], (1.0f - a[e]) * (lv[e] * sl)) : a[e] * y[e];
+        } else if (have_l) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] = fmaf(lv[e], sl, y[e]);
         }
         uint2 pk;
         pk.x = pack2_bf16(y[0], y[1]);
@@ -709,19 +763,29 @@ hipError_t launch_sparse(const AttnLaunch& a, hipStream_t s, AttnPhase phase) {
   const float c = a.scale * 1.4426950408889634f;  // scale * log2(e)
   const int BH = a.B * a.H;
   if (phase != kAttendOnly) {
+    if constexpr (LIN)
+      hipLaunchKernelGGL(linear_flags_kernel, dim3(a.H), dim3(64), 0, s, a.alpha, a.lin_mode, D,
+                         a.drop_below, a.lin_on);
     hipLaunchKernelGGL((pack_kernel<D, LIN>), dim3(a.n_k, BH), dim3(2 * D), 0, s, a.v, a.k,
-                       a.vt, a.phikt, a.N, a.n_k);
+                       a.vt, a.phikt, a.N, a.n_k, a.lin_on, a.H);
     if constexpr (LIN) {
       hipLaunchKernelGGL((linear_total_kernel<D>), dim3(kLinSplit, BH), dim3(D * 2), 0, s,
-                         a.phikt, a.vt, a.part_h, a.part_z, a.n_k);
+                         a.phikt, a.vt, a.part_h, a.part_z, a.n_k, a.lin_on, a.H);
       hipLaunchKernelGGL((linear_reduce_kernel<D>), dim3(BH), dim3(256), 0, s, a.part_h,
-                         a.part_z, a.lin_h, a.lin_z);
+                         a.part_z, a.lin_h, a.lin_z, a.lin_on, a.H);
     }
   }
-  if (phase != kPackOnly)
+  if (phase != kPackOnly) {
     hipLaunchKernelGGL((sparse_attn_fwd_kernel<D, BQ, LIN>), dim3(total), dim3(BQ * (LIN ? 4 : 2)), 0, s,
                        a.q, a.k, a.vt, a.idx, a.cnt, a.o, a.H, a.N, a.n_q, a.n_k, total, c,
-                       a.alpha, a.phikt, a.lin_h, a.lin_z);
+                       a.alpha, a.phikt, a.lin_h, a.lin_z, LIN ? a.lin_on : nullptr, a.lin_mode);
+    // heads whose branch is dropped: plain sparse attention (times alpha in the mix)
+    if constexpr (LIN)
+      hipLaunchKernelGGL((sparse_attn_fwd_kernel<D, BQ, false, true>), dim3(total), dim3(BQ * 2), 0, s,
+                         a.q, a.k, a.vt, a.idx, a.cnt, a.o, a.H, a.N, a.n_q, a.n_k, total, c,
+                         a.lin_mode == kLinMix ? a.alpha : nullptr, nullptr, nullptr, nullptr,
+                         a.lin_on, a.lin_mode);
+  }
   return hipGetLastError();
 }
 
@@ -735,7 +799,8 @@ size_t attn_workspace_bytes(int B, int H, int N, int d) {
 size_t linear_workspace_bytes(int B, int H, int N, int d) {
   const size_t BH = (size_t)B * H;
   return 2 * attn_workspace_bytes(B, H, N, d) +                // packed V, packed phi(K)
-         BH * ((size_t)d * d + d) * (1 + kLinSplit) * sizeof(float);  // totals + partials
+         BH * ((size_t)d * d + d) * (1 + kLinSplit) * sizeof(float) +  // totals + partials
+         (size_t)H * sizeof(int32_t);                                 // per-head branch flags
 }
 
 hipError_t launch_attn(const AttnLaunch& a, hipStream_t s, AttnPhase phase) {

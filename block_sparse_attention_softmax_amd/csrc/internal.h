@@ -72,7 +72,10 @@ struct AttnLaunch {
   // workspace: V packed key-contiguous per block, [B*H, n_k, d, 64]
   uint16_t* vt;
   // linear branch (alpha == nullptr: plain sparse attention)
-  const float* alpha;  // [H]
+  const float* alpha;  // kLinAdd: [H]; kLinMix: [H, d]
+  int lin_mode;        // LinMode
+  float drop_below;    // a head whose linear weights are all <= this in magnitude skips the branch
+  int32_t* lin_on;     // [H] 1 where the branch is evaluated
   uint16_t* phikt;     // phi(K) packed like vt, bf16
   float* lin_h;        // [B*H, d, d]  sum_u phi(K_u)^T V_u  (row = phi(K) index)
   float* lin_z;        // [B*H, d]     sum_u phi(K_u)
@@ -80,6 +83,9 @@ struct AttnLaunch {
   float* part_z;       // [B*H, kLinSplit, d]
 };
 constexpr int kLinSplit = 16;
+// how the linear branch meets the sparse output: O_s + alpha[h] O_l, or the
+// per-channel mix alpha[h][c] O_s + (1 - alpha[h][c]) O_l
+enum LinMode { kLinAdd = 0, kLinMix = 1 };
 // pack (V, and phi(K) for the linear branch) then attend; or either half alone
 enum AttnPhase { kPackAndAttend = 0, kPackOnly = 1, kAttendOnly = 2 };
 hipError_t launch_attn(const AttnLaunch& a, hipStream_t s, AttnPhase phase = kPackAndAttend);

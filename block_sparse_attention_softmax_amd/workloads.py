@@ -185,3 +185,10 @@ def router_weights(H: int, d: int, seed: int) -> tuple:
     wq = (rng.standard_normal((H, d, d)) / np.sqrt(d)).astype(np.float32)
     wk = (rng.standard_normal((H, d, d)) / np.sqrt(d)).astype(np.float32)
     return wq, wk
+
+
+def mix_alpha(H: int, d: int, seed: int) -> np.ndarray:
+    """Synthetic learned ratios of the sparse / linear mix (trained values are
+    not available): float32 [H, d], uniform in [0, 1) from a PCG64 stream of
+    `seed`."""
+    return np.random.default_rng(seed).random((H, d)).astype(np.float32)

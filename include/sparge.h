@@ -173,8 +173,8 @@ int sparge_attn_fwd_packed(const void* q, const void* k, const int32_t* kv_idx,
 /* Device workspace (bytes) of sparse_linear_attn_fwd: the packed V of
  * sparge_attn_fwd, phi(K) packed the same way, and per (b, h) the float32
  * summaries sum_u phi(K_u)^T V_u (d x d) and sum_u phi(K_u) (d) with 16
- * split-K partials of each. Returns 0 for arguments that
- * sparse_linear_attn_fwd would reject. */
+ * split-K partials of each, and one int32 flag per head. Returns 0 for
+ * arguments that sparse_linear_attn_fwd would reject. */
 size_t sparse_linear_workspace_bytes(int B, int H, int N, int d);
 
 /* Sparse attention plus a linear-attention branch over the dropped blocks
@@ -188,18 +188,41 @@ size_t sparse_linear_workspace_bytes(int B, int H, int N, int d);
  * The linear branch accumulates in float32 from bf16-rounded phi(K) and V;
  * its final product phi(Q) . (sum over D_i) carries about 16 significant
  * bits per operand. Built for block_q == d (64 or 128); other block sizes
- * return SPARGE_ERR_UNSUPPORTED. Setting alpha[h] = 0 still evaluates the
- * branch; callers that drop it should call sparge_attn_fwd.
+ * return SPARGE_ERR_UNSUPPORTED.
  *
- *  alpha     : float32 [H], device.
+ * Post-tuning branch dropping (SALAD page): a head with |alpha[h]| <=
+ * drop_below (float32 comparison) skips its linear branch entirely (no phi(K)
+ * packing, summaries or H products) and its output is O_s alone. The decision
+ * is taken on the device, so alpha may change between calls without a host
+ * synchronisation. drop_below = 0 skips only heads with alpha[h] == 0, which
+ * changes no output value; a negative or NaN drop_below skips none.
+ *
+ *  alpha     : float32 [H], device, 4-byte aligned.
  *  workspace : device scratch of at least sparse_linear_workspace_bytes(),
  *              16-byte aligned; contents on entry do not matter.
  *  Other arguments as for sparge_attn_fwd. */
 int sparse_linear_attn_fwd(const void* q, const void* k, const void* v,
                            const int32_t* kv_idx, const int32_t* kv_cnt,
                            const float* alpha, int B, int H, int N, int d,
-                           int block_q, int block_k, float scale, void* o,
-                           void* workspace, size_t workspace_bytes, void* stream);
+                           int block_q, int block_k, float scale, float drop_below,
+                           void* o, void* workspace, size_t workspace_bytes, void* stream);
+
+/* SLA2's faithful sparse-linear output (SLA2 page, section 2A): a learned
+ * vector alpha in [0, 1] weighs the two branches channel by channel,
+ *   O_t[c] = alpha[h][c] * O_s,t[c] + (1 - alpha[h][c]) * O_l,t[c],
+ * with O_s and O_l (zero when D_i is empty) as in sparse_linear_attn_fwd.
+ * alpha holds one value per output channel of each head; a per-head ratio
+ * is the case of equal channels. Branch dropping as in
+ * sparse_linear_attn_fwd, on the weights 1 - alpha[h][c] (float32): a head
+ * whose every |1 - alpha[h][c]| <= drop_below has output alpha[h][c] O_s,t[c].
+ *
+ *  alpha     : float32 [H, d] row-major, device, 16-byte aligned.
+ *  workspace : as for sparse_linear_attn_fwd (same size).
+ *  Other arguments as for sparse_linear_attn_fwd. */
+int sla2_mix_attn_fwd(const void* q, const void* k, const void* v, const int32_t* kv_idx,
+                      const int32_t* kv_cnt, const float* alpha, int B, int H, int N, int d,
+                      int block_q, int block_k, float scale, float drop_below, void* o,
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* Message for the last non-OK return on the calling thread ("" if none).
  * The pointer stays valid until the next library call on that thread. */

@@ -45,7 +45,8 @@ def test_mask_workspace_bytes():
     packed_v = 40 * math.ceil(75600 / 64) * 64 * 128 * 2
     assert L.sparge_attn_workspace_bytes(1, 40, 75600, 128) == packed_v
     assert L.sparge_attn_workspace_bytes(1, 40, 75600, 96) == 0
-    lin = 2 * packed_v + 40 * (128 * 128 + 128) * 4 * (1 + 16)  # totals + 16 split partials
+    lin = (2 * packed_v + 40 * (128 * 128 + 128) * 4 * (1 + 16)  # totals + 16 split partials
+           + 40 * 4)                                              # per-head branch flags
     assert L.sparse_linear_workspace_bytes(1, 40, 75600, 128) == lin
 
 
@@ -91,11 +92,11 @@ def test_packed_attn_rejects_bad_arguments(kw, code):
     assert _packed(**kw) == code
 
 
-def _lin(**kw):
+def _lin(fn="sparse_linear_attn_fwd", **kw):
     args = dict(q=A, k=A, v=A, idx=A, cnt=A, alpha=A, B=1, H=2, N=1024, d=64, bq=64, bk=64,
-                sc=0.125, o=A, ws=A, wsb=1 << 30, st=None)
+                sc=0.125, drop=0.0, o=A, ws=A, wsb=1 << 30, st=None)
     args.update(kw)
-    return binding.lib().sparse_linear_attn_fwd(*args.values())
+    return getattr(binding.lib(), fn)(*args.values())
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -129,8 +130,18 @@ def test_attn_rejects_bad_arguments(kw, code):
     (dict(d=32), -2), (dict(alpha=ctypes.c_void_p(0x10001)), -1),
     (dict(bq=128), -2),  # the linear branch is built for block_q == d
 ])
-def test_linear_rejects_bad_arguments(kw, code):
-    assert _lin(**kw) == code
+@pytest.mark.parametrize("fn", ["sparse_linear_attn_fwd", "sla2_mix_attn_fwd"])
+def test_linear_rejects_bad_arguments(fn, kw, code):
+    assert _lin(fn, **kw) == code
+    assert binding.lib().sparge_last_error().decode()
+
+
+def test_mix_alpha_needs_16_byte_alignment():
+    # the mix reads four channels of alpha at once; the added form one value
+    assert _lin("sla2_mix_attn_fwd", alpha=ctypes.c_void_p(0x10004)) == -1
+    assert "misaligned" in binding.lib().sparge_last_error().decode()
+    assert _lin("sparse_linear_attn_fwd", alpha=ctypes.c_void_p(0x10004), q=None) == -1
+    assert "null" in binding.lib().sparge_last_error().decode()
 
 
 def test_error_message_is_per_call():

@@ -364,3 +364,140 @@ def test_sparse_linear_branch_contributes():
     diff = (half.float() - o_s.float()).abs().amax(dim=-1)  # [B, H, N]
     assert (diff[..., 256:384] == 0).all()
     assert (diff[..., :256] > 0).all() and (diff[..., 384:] > 0).all()
+
+
+# ------------------------------------------------------ SLA2 mix (section 2A)
+@pytest.mark.parametrize("B,H,N,d", [(1, 2, 1000, 128), (2, 1, 777, 64), (1, 3, 300, 128),
+                                     (1, 1, 64, 64)])
+def test_sla2_mix_small_shapes_in_full(B, H, N, d):
+    rng = np.random.default_rng(11 * N + d)
+    from block_sparse_attention_softmax_amd.workloads import f64_to_bf16_bits, mix_alpha
+    Q, K, V = (f64_to_bf16_bits(rng.standard_normal((B, H, N, d))) for _ in range(3))
+    n_q, n_k = -(-N // d), -(-N // 64)
+    kept = _random_lists(rng, B, H, n_q, n_k)  # includes an empty and a full row
+    idx, cnt = O.kept_to_index_list(kept)
+    alpha = mix_alpha(H, d, N)
+    alpha[0, :3] = (0.0, 1.0, 0.5)  # the two extremes and an exact half
+    print(f"\n[mix] B={B} H={H} N={N} d={d}", flush=True)
+    o = S.sla2_mix_attn_fwd(to_gpu(Q), to_gpu(K), to_gpu(V), torch.from_numpy(idx).cuda(),
+                            torch.from_numpy(cnt).cuda(), torch.from_numpy(alpha).cuda(), d, 64)
+    torch.cuda.synchronize()
+    got = O.bf16_to_f64(o.cpu().view(torch.uint16).numpy())
+    scale = S.default_scale(d)
+    for b in range(B):
+        for h in range(H):
+            ref = O.sla2_mix_attention_head(O.bf16_to_f64(Q[b, h]), O.bf16_to_f64(K[b, h]),
+                                            O.bf16_to_f64(V[b, h]), kept[b, h], d, 64, scale,
+                                            alpha[h])
+            mx, mean = compare_outputs(got[b, h], ref)
+            print(f"[mix] b={b} h={h}: max {mx:.2e} mean {mean:.2e}", flush=True)
+
+
+def test_sla2_mix_matches_oracle_on_workload():
+    """wan1.3b inputs and mask with per-channel ratios drawn in [0, 1)."""
+    from block_sparse_attention_softmax_amd.workloads import mix_alpha
+    wl, Q, K, V, q, k, v = workload_tensors("wan1.3b_linear")
+    bits, idx, cnt = S.sparge_mask_predict(q, k, wl.block_q, wl.block_k, wl.k_frac, wl.p_mass)
+    alpha = mix_alpha(wl.H, wl.d, 5)
+    o = S.sla2_mix_attn_fwd(q, k, v, idx, cnt, torch.from_numpy(alpha).cuda(), wl.block_q,
+                            wl.block_k)
+    torch.cuda.synchronize()
+    kept = gpu_bits_to_bool(bits, wl.n_k)
+    got = O.bf16_to_f64(o.cpu().view(torch.uint16).numpy())
+    rng = np.random.default_rng(98)
+    for h in rng.choice(wl.H, size=3, replace=False):
+        blocks = sorted({0, wl.n_q - 1, *rng.choice(wl.n_q, 4, replace=False)})
+        ref = O.sla2_mix_attention_head(O.bf16_to_f64(Q[0, h]), O.bf16_to_f64(K[0, h]),
+                                        O.bf16_to_f64(V[0, h]), kept[0, h], wl.block_q,
+                                        wl.block_k, wl.scale, alpha[h], q_blocks=blocks)
+        rows = ~np.isnan(ref[:, 0])
+        mx, mean = compare_outputs(got[0, h][rows], ref[rows])
+        print(f"[mix] wan1.3b h={h}: max {mx:.2e} mean {mean:.2e}", flush=True)
+
+
+# ------------------------------------- SALAD post-tuning branch dropping
+def _drop_case(seed, H=4, N=1000, d=128):
+    rng = np.random.default_rng(seed)
+    from block_sparse_attention_softmax_amd.workloads import f64_to_bf16_bits
+    Q, K, V = (f64_to_bf16_bits(rng.standard_normal((1, H, N, d))) for _ in range(3))
+    n_q, n_k = -(-N // d), -(-N // 64)
+    kept = _random_lists(rng, 1, H, n_q, n_k)
+    idx, cnt = O.kept_to_index_list(kept)
+    g = (to_gpu(Q), to_gpu(K), to_gpu(V), torch.from_numpy(idx).cuda(),
+         torch.from_numpy(cnt).cuda())
+    return Q, K, V, kept, g
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_branch_dropping_matches_oracle(d):
+    H, N = 4, 1000
+    Q, K, V, kept, g = _drop_case(21 + d, H, N, d)
+    scale, tau = S.default_scale(d), 0.05
+    f = lambda x, h: O.bf16_to_f64(x[0, h])
+    # added form: heads 0, 1, 3 are dropped (|alpha| <= tau), head 2 is evaluated
+    a_add = np.array([0.0, 0.03, 0.2, -0.04], np.float32)
+    # mix: heads 0, 1 dropped (all 1 - alpha small), 2 and 3 evaluated (3: one channel)
+    a_mix = np.ones((H, d), np.float32)
+    a_mix[1] = 0.97
+    a_mix[2] = np.random.default_rng(d).random(d)
+    a_mix[3, 5] = 0.5
+    ws = torch.empty(S.linear_workspace_bytes(1, H, N, d), dtype=torch.uint8, device="cuda")
+    o_add = S.sparse_linear_attn_fwd(*g, torch.from_numpy(a_add).cuda(), d, 64,
+                                     drop_below=tau, workspace=ws)
+    o_mix = S.sla2_mix_attn_fwd(*g, torch.from_numpy(a_mix).cuda(), d, 64, drop_below=tau,
+                                workspace=ws)
+    o_s = S.sparge_attn_fwd(*g, d, 64)
+    torch.cuda.synchronize()
+    got_add = O.bf16_to_f64(o_add.cpu().view(torch.uint16).numpy())
+    got_mix = O.bf16_to_f64(o_mix.cpu().view(torch.uint16).numpy())
+    print(f"\n[drop] d={d}", flush=True)
+    for h in range(H):
+        ref = O.sparse_linear_attention_head_dropping(f(Q, h), f(K, h), f(V, h), kept[0, h], d,
+                                                      64, scale, float(a_add[h]), tau)
+        mx, mean = compare_outputs(got_add[0, h], ref)
+        ref = O.sla2_mix_attention_head_dropping(f(Q, h), f(K, h), f(V, h), kept[0, h], d, 64,
+                                                 scale, a_mix[h], tau)
+        mx2, mean2 = compare_outputs(got_mix[0, h], ref)
+        print(f"[drop] h={h}: add max {mx:.2e} mean {mean:.2e}; mix max {mx2:.2e} "
+              f"mean {mean2:.2e}", flush=True)
+    # a dropped head of the added form is plain block-sparse attention, bit for bit
+    for h in (0, 1, 3):
+        assert torch.equal(o_add[0, h].view(torch.int16), o_s[0, h].view(torch.int16))
+    assert torch.equal(o_mix[0, 0].view(torch.int16), o_s[0, 0].view(torch.int16))
+    # the evaluated heads differ from it on rows that dropped a block
+    assert not torch.equal(o_add[0, 2], o_s[0, 2]) and not torch.equal(o_mix[0, 3], o_s[0, 3])
+
+
+def test_dropping_an_exactly_zero_branch_changes_no_output():
+    """drop_below = 0 skips only zero branches; evaluating them instead
+    (drop_below < 0) gives the same bits."""
+    H, N, d = 2, 777, 128
+    Q, K, V, kept, g = _drop_case(31, H, N, d)
+    zero = torch.zeros(H, device="cuda")
+    ones = torch.ones(H, d, device="cuda")
+    outs = [S.sparse_linear_attn_fwd(*g, zero, d, 64, drop_below=t) for t in (0.0, -1.0)]
+    outs += [S.sla2_mix_attn_fwd(*g, ones, d, 64, drop_below=t) for t in (0.0, -1.0)]
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    assert torch.equal(outs[2].view(torch.int16), outs[3].view(torch.int16))
+    assert torch.equal(outs[0].view(torch.int16), outs[2].view(torch.int16))
+
+
+def test_drop_decision_follows_alpha_between_calls():
+    """The decision is taken on the device at every call: the same workspace
+    serves a call that drops a head's branch and one that evaluates it."""
+    H, N, d = 2, 1000, 64
+    Q, K, V, kept, g = _drop_case(41, H, N, d)
+    ws = torch.empty(S.linear_workspace_bytes(1, H, N, d), dtype=torch.uint8, device="cuda")
+    f = lambda x, h: O.bf16_to_f64(x[0, h])
+    for a in ([0.3, 0.0], [0.0, 0.3], [0.3, 0.0]):
+        alpha = np.array(a, np.float32)
+        o = S.sparse_linear_attn_fwd(*g, torch.from_numpy(alpha).cuda(), d, 64,
+                                     drop_below=0.0, workspace=ws)
+        torch.cuda.synchronize()
+        got = O.bf16_to_f64(o.cpu().view(torch.uint16).numpy())
+        for h in range(H):
+            ref = O.sparse_linear_attention_head_dropping(f(Q, h), f(K, h), f(V, h), kept[0, h],
+                                                          d, 64, S.default_scale(d),
+                                                          float(alpha[h]), 0.0)
+            compare_outputs(got[0, h], ref)
