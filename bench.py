@@ -131,7 +131,8 @@ def main():
     import torch
 
     from block_sparse_attention_softmax_amd import binding as S
-    from block_sparse_attention_softmax_amd.workloads import WORKLOADS, generate
+    from block_sparse_attention_softmax_amd.workloads import (WORKLOADS, generate, mix_alpha,
+                                                              router_weights)
 
     wl = WORKLOADS[args.workload]
     Q, K, V = generate(wl)
@@ -149,6 +150,14 @@ def main():
     aws = torch.empty(S.attn_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
     lws = torch.empty(S.linear_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
     alpha = torch.full((H,), 0.1, dtype=torch.float32, device=dev)
+    # SLA2 / SALAD variants: per-channel mix ratios, router weights, dropped branches
+    alpha_mix = torch.from_numpy(mix_alpha(H, d, 5)).to(dev)
+    alpha_half = torch.tensor([0.1 if h % 2 else 0.0 for h in range(H)], dtype=torch.float32,
+                              device=dev)
+    alpha_none = torch.zeros(H, dtype=torch.float32, device=dev)
+    w_q, w_k = (torch.from_numpy(w).to(dev) for w in router_weights(H, d, 77))
+    rws = torch.empty(S.mask_routed_workspace_bytes(B, H, N, d, wl.block_q, wl.block_k),
+                      dtype=torch.uint8, device=dev)
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 20
         src = torch.ones(n, dtype=torch.uint8, device=dev)
@@ -161,7 +170,7 @@ def main():
     main = torch.cuda.current_stream()
     side = torch.cuda.Stream()  # default priority
 
-    def step(k_frac, p_mass, ev=None, linear=False):
+    def step(k_frac, p_mass, ev=None, linear=None, alpha_t=None, routed=False):
         """V pack (side stream) || mask (main stream) -> attention (main stream).
 
         The pack reads only V and the mask only Q and K, so the two halves of
@@ -178,13 +187,18 @@ def main():
                     ev[5].record()
         if ev is not None:
             ev[0].record()
-        S.sparge_mask_predict(q, k, wl.block_q, wl.block_k, k_frac, p_mass, wl.scale,
-                              workspace=ws, out=(bits, idx, cnt))
+        if routed:
+            S.sparge_mask_predict_routed(q, k, w_q, w_k, wl.block_q, wl.block_k, k_frac, p_mass,
+                                         wl.scale, workspace=rws, out=(bits, idx, cnt))
+        else:
+            S.sparge_mask_predict(q, k, wl.block_q, wl.block_k, k_frac, p_mass, wl.scale,
+                                  workspace=ws, out=(bits, idx, cnt))
         if ev is not None:
             ev[1].record()
         if linear:
-            S.sparse_linear_attn_fwd(q, k, v, idx, cnt, alpha, wl.block_q, wl.block_k, wl.scale,
-                                     workspace=lws, out=o)
+            fn = S.sla2_mix_attn_fwd if linear == "mix" else S.sparse_linear_attn_fwd
+            fn(q, k, v, idx, cnt, alpha_t, wl.block_q, wl.block_k, wl.scale, workspace=lws,
+               out=o)
             if ev is not None:
                 ev[2].record()
         else:
@@ -196,14 +210,14 @@ def main():
         if ev is not None:
             ev[3].record()
 
-    def timed(k_frac, p_mass, steps, warmup, linear=False):
+    def timed(k_frac, p_mass, steps, warmup, linear=None, alpha_t=None, routed=False):
         for _ in range(warmup):
-            step(k_frac, p_mass, linear=linear)
+            step(k_frac, p_mass, linear=linear, alpha_t=alpha_t, routed=routed)
         torch.cuda.synchronize()
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
         t0 = time.perf_counter()
         for i in range(steps):
-            step(k_frac, p_mass, evs[i], linear=linear)
+            step(k_frac, p_mass, evs[i], linear=linear, alpha_t=alpha_t, routed=routed)
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) / steps
         mask_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
@@ -233,12 +247,32 @@ def main():
             "attn_frac_bf16_peak": round(kf2 / (k2 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
     # the sparse-linear workload: same inputs and mask, plus alpha = 0.1 elu+1 linear branch
-    w3, m3, l3, _, kf3, frac3 = timed(wl.k_frac, wl.p_mass, max(5, args.steps // 2), 2,
-                                      linear=True)
+    n_lin = max(5, args.steps // 2)
+    w3, m3, l3, _, kf3, frac3 = timed(wl.k_frac, wl.p_mass, n_lin, 2, linear="add",
+                                      alpha_t=alpha)
     linear = {"workload": "wan1.3b_linear (alpha = 0.1, phi = elu + 1)",
               "ms_per_step": round(w3 * 1e3, 4), "mask_ms": round(m3, 4),
               "sparse_linear_ms": round(l3, 4),
               "dense_equiv_tflops": round(dense / w3 / 1e12, 2)}
+
+    # SLA2: router mask (projected pooled Q, K; hard Top-k) and the per-channel mix;
+    # SALAD: the added branch dropped on half of the heads, then on all of them
+    w4, m4, _, _, _, frac4 = timed(0.10, 0.0, n_lin, 2, routed=True)
+    w5, m5, l5, _, _, _ = timed(wl.k_frac, wl.p_mass, n_lin, 2, linear="mix",
+                                alpha_t=alpha_mix)
+    w6, _, l6, _, _, _ = timed(wl.k_frac, wl.p_mass, n_lin, 2, linear="add",
+                               alpha_t=alpha_half)
+    w7, _, l7, _, _, _ = timed(wl.k_frac, wl.p_mass, n_lin, 2, linear="add",
+                               alpha_t=alpha_none)
+    sla2 = {"routed_mask": {"k": 0.10, "p": 0.0, "weights": "N(0, 1/d) per head, float32",
+                            "mask_ms": round(m4, 4), "ms_per_step": round(w4 * 1e3, 4),
+                            "block_sparsity": round(1 - frac4, 4)},
+            "mix": {"alpha": "uniform [0, 1) per head and channel",
+                    "ms_per_step": round(w5 * 1e3, 4), "mix_attn_ms": round(l5, 4)},
+            "drop_half": {"alpha": "0.1 on odd heads, 0 (dropped) on even heads",
+                          "ms_per_step": round(w6 * 1e3, 4), "sparse_linear_ms": round(l6, 4)},
+            "drop_all": {"alpha": "0 on every head (every branch dropped)",
+                         "ms_per_step": round(w7 * 1e3, 4), "sparse_linear_ms": round(l7, 4)}}
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl, Q, K, V, args.cpu_blocks)
 
@@ -264,6 +298,7 @@ def main():
                      "flops_per_launch": kf},
         "operating_points": points,
         "sparse_linear": linear,
+        "sla2_salad": sla2,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -343,6 +343,7 @@ int linear_impl(const char* name, int mode, const void* q, const void* k, const 
   a.part_h = a.lin_z + BH * d;
   a.part_z = a.part_h + BH * sparge::kLinSplit * d * d;
   a.lin_on = reinterpret_cast<int32_t*>(a.part_z + BH * sparge::kLinSplit * d);
+  a.lin_lists = a.lin_on + H;
   const hipError_t e = sparge::launch_attn(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, name);
   return SPARGE_OK;

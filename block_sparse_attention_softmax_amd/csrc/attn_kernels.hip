@@ -248,19 +248,44 @@ __global__ __launch_bounds__(256) void linear_reduce_kernel(const float* __restr
 // lin_on[h] = 1 unless every weight that head h's linear branch is multiplied
 // by (alpha[h]; 1 - alpha[h][c] in the mix, float32) has magnitude <= the
 // threshold: post-tuning branch dropping (SALAD page). A NaN weight keeps it.
-__global__ __launch_bounds__(64) void linear_flags_kernel(const float* __restrict__ alpha,
-                                                          int mode, int D, float drop_below,
-                                                          int32_t* __restrict__ lin_on) {
-  const int h = blockIdx.x, lane = threadIdx.x;
-  bool keep = false;
-  if (mode == kLinAdd) {
-    keep = lane == 0 && !(fabsf(alpha[h]) <= drop_below);
-  } else {
-    for (int c = lane; c < D; c += 64)
-      keep = keep || !(fabsf(1.0f - alpha[(size_t)h * D + c]) <= drop_below);
+// Then the (batch, head) pairs b*H + h in increasing order, split by the flag:
+// lists[0] = #on, lists[1] = #off, lists[2 ..] those on, lists[2 + B*H ..]
+// those off. One workgroup; wave w decides heads w, w + 16, ...
+constexpr int kFlagThreads = 1024;
+__global__ __launch_bounds__(kFlagThreads) void linear_flags_kernel(
+    const float* __restrict__ alpha, int mode, int D, float drop_below, int B, int H,
+    int32_t* __restrict__ lin_on, int32_t* __restrict__ lists) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int h = wave; h < H; h += kFlagThreads / 64) {
+    bool keep = false;
+    if (mode == kLinAdd) {
+      keep = lane == 0 && !(fabsf(alpha[h]) <= drop_below);
+    } else {
+      for (int c = lane; c < D; c += 64)
+        keep = keep || !(fabsf(1.0f - alpha[(size_t)h * D + c]) <= drop_below);
+    }
+    keep = __any(keep);
+    if (lane == 0) lin_on[h] = keep ? 1 : 0;
   }
-  keep = __any(keep);
-  if (lane == 0) lin_on[h] = keep ? 1 : 0;
+  __syncthreads();
+  if (wave != 0) return;
+  const int BH = B * H;
+  int n_on = 0, n_off = 0;
+  for (int base = 0; base < BH; base += 64) {
+    const int bh = base + lane;
+    const bool valid = bh < BH;
+    const bool on = valid && lin_on[bh % H] != 0, off = valid && !on;
+    const uint64_t m_on = __ballot(on), m_off = __ballot(off);
+    const uint64_t below = (uint64_t(1) << lane) - 1;
+    if (on) lists[2 + n_on + __popcll(m_on & below)] = bh;
+    if (off) lists[2 + BH + n_off + __popcll(m_off & below)] = bh;
+    n_on += __popcll(m_on);
+    n_off += __popcll(m_off);
+  }
+  if (lane == 0) {
+    lists[0] = n_on;
+    lists[1] = n_off;
+  }
 }
 
 // ------------------------------------------------------ attention kernel
@@ -288,9 +313,10 @@ __global__ __launch_bounds__(64) void linear_flags_kernel(const float* __restric
 // over through LDS in the attention wave's own register layout; the
 // attention wave writes O = O_s + alpha[h] * O_l, or in the SLA2 mix (SLA2
 // page, section 2A) O = alpha[h][c] O_s + (1 - alpha[h][c]) O_l with the
-// scale 1 / (phi(Q) . z_D). Heads whose branch is dropped (lin_on = 0) exit
-// at once here and run in a second launch of the plain kernel, which scales
-// O_s by alpha[h][c] in the mix.
+// scale 1 / (phi(Q) . z_D). Heads whose branch is dropped (lin_on = 0) are
+// left to a second launch of the plain kernel, which scales O_s by
+// alpha[h][c] in the mix; each launch maps its workgroups onto its own heads
+// through the lists of linear_flags_kernel.
 //
 // SEL (always with LIN) adds the head selection and the alpha scaling of the
 // epilogue; the plain kernel without it is compiled without either.
@@ -301,7 +327,7 @@ __global__ __launch_bounds__(BQ * (LIN ? 4 : 2), (LIN || (D == 128 && BQ == 64))
     const int32_t* __restrict__ kv_cnt, uint16_t* __restrict__ o, int H, int N, int n_q,
     int n_k, int total, float c, const float* __restrict__ alpha,
     const uint16_t* __restrict__ phikt, const float* __restrict__ lin_h,
-    const float* __restrict__ lin_z, const int32_t* __restrict__ head_sel, int lin_mode) {
+    const float* __restrict__ lin_z, const int32_t* __restrict__ sel_lists, int lin_mode) {
   constexpr int NW = BQ / 32;
   using T = Tile<D>;
   constexpr int LOADS = BK * D / 8 / 64 / NW;
@@ -315,13 +341,20 @@ __global__ __launch_bounds__(BQ * (LIN ? 4 : 2), (LIN || (D == 128 && BQ == 64))
   unsigned char* const vbuf = smem + 2 * T::BYTES;
   unsigned char* const pbuf = smem + 4 * T::BYTES;
 
-  const int tile = xcd_remap(blockIdx.x, total);
-  const int bh = tile / n_q, qi = tile % n_q;
-  // with a head selection, LIN runs the heads whose linear branch is on and
-  // the plain kernel the others
+  // with a head selection, LIN runs the (batch, head) pairs whose linear
+  // branch is on and the plain kernel the others: the first n_sel * n_q
+  // workgroups take the selected heads' query blocks, spread over the XCDs
+  // like the full grid, and the rest exit
+  int tile;
   if constexpr (SEL) {
-    if ((head_sel[bh % H] != 0) != LIN) return;
+    const int n_sel = sel_lists[LIN ? 0 : 1];
+    if ((int)blockIdx.x >= n_sel * n_q) return;
+    const int t2 = xcd_remap(blockIdx.x, n_sel * n_q);
+    tile = sel_lists[2 + (LIN ? 0 : total / n_q) + t2 / n_q] * n_q + t2 % n_q;
+  } else {
+    tile = xcd_remap(blockIdx.x, total);
   }
+  const int bh = tile / n_q, qi = tile % n_q;
   const int t = threadIdx.x, lane = t & 63;
   const int wave_id = __builtin_amdgcn_readfirstlane(t >> 6);
   // LIN: waves NW.. are H waves (H_kept and z_kept for the d rows 32*wave..);
@@ -764,8 +797,8 @@ hipError_t launch_sparse(const AttnLaunch& a, hipStream_t s, AttnPhase phase) {
   const int BH = a.B * a.H;
   if (phase != kAttendOnly) {
     if constexpr (LIN)
-      hipLaunchKernelGGL(linear_flags_kernel, dim3(a.H), dim3(64), 0, s, a.alpha, a.lin_mode, D,
-                         a.drop_below, a.lin_on);
+      hipLaunchKernelGGL(linear_flags_kernel, dim3(1), dim3(kFlagThreads), 0, s, a.alpha,
+                         a.lin_mode, D, a.drop_below, a.B, a.H, a.lin_on, a.lin_lists);
     hipLaunchKernelGGL((pack_kernel<D, LIN>), dim3(a.n_k, BH), dim3(2 * D), 0, s, a.v, a.k,
                        a.vt, a.phikt, a.N, a.n_k, a.lin_on, a.H);
     if constexpr (LIN) {
@@ -778,13 +811,14 @@ hipError_t launch_sparse(const AttnLaunch& a, hipStream_t s, AttnPhase phase) {
   if (phase != kPackOnly) {
     hipLaunchKernelGGL((sparse_attn_fwd_kernel<D, BQ, LIN>), dim3(total), dim3(BQ * (LIN ? 4 : 2)), 0, s,
                        a.q, a.k, a.vt, a.idx, a.cnt, a.o, a.H, a.N, a.n_q, a.n_k, total, c,
-                       a.alpha, a.phikt, a.lin_h, a.lin_z, LIN ? a.lin_on : nullptr, a.lin_mode);
+                       a.alpha, a.phikt, a.lin_h, a.lin_z, LIN ? a.lin_lists : nullptr,
+                       a.lin_mode);
     // heads whose branch is dropped: plain sparse attention (times alpha in the mix)
     if constexpr (LIN)
       hipLaunchKernelGGL((sparse_attn_fwd_kernel<D, BQ, false, true>), dim3(total), dim3(BQ * 2), 0, s,
                          a.q, a.k, a.vt, a.idx, a.cnt, a.o, a.H, a.N, a.n_q, a.n_k, total, c,
                          a.lin_mode == kLinMix ? a.alpha : nullptr, nullptr, nullptr, nullptr,
-                         a.lin_on, a.lin_mode);
+                         a.lin_lists, a.lin_mode);
   }
   return hipGetLastError();
 }
@@ -800,7 +834,7 @@ size_t linear_workspace_bytes(int B, int H, int N, int d) {
   const size_t BH = (size_t)B * H;
   return 2 * attn_workspace_bytes(B, H, N, d) +                // packed V, packed phi(K)
          BH * ((size_t)d * d + d) * (1 + kLinSplit) * sizeof(float) +  // totals + partials
-         (size_t)H * sizeof(int32_t);                                 // per-head branch flags
+         ((size_t)H + 2 + 2 * BH) * sizeof(int32_t);  // branch flags and head lists
 }
 
 hipError_t launch_attn(const AttnLaunch& a, hipStream_t s, AttnPhase phase) {

@@ -76,6 +76,7 @@ struct AttnLaunch {
   int lin_mode;        // LinMode
   float drop_below;    // a head whose linear weights are all <= this in magnitude skips the branch
   int32_t* lin_on;     // [H] 1 where the branch is evaluated
+  int32_t* lin_lists;  // [2 + 2*B*H] counts, then the b*H + h with the branch on, then off
   uint16_t* phikt;     // phi(K) packed like vt, bf16
   float* lin_h;        // [B*H, d, d]  sum_u phi(K_u)^T V_u  (row = phi(K) index)
   float* lin_z;        // [B*H, d]     sum_u phi(K_u)

@@ -173,7 +173,8 @@ int sparge_attn_fwd_packed(const void* q, const void* k, const int32_t* kv_idx,
 /* Device workspace (bytes) of sparse_linear_attn_fwd: the packed V of
  * sparge_attn_fwd, phi(K) packed the same way, and per (b, h) the float32
  * summaries sum_u phi(K_u)^T V_u (d x d) and sum_u phi(K_u) (d) with 16
- * split-K partials of each, and one int32 flag per head. Returns 0 for
+ * split-K partials of each, and H + 2 + 2*B*H int32 for the per-head
+ * branch flags and the lists of (batch, head) pairs by flag. Returns 0 for
  * arguments that sparse_linear_attn_fwd would reject. */
 size_t sparse_linear_workspace_bytes(int B, int H, int N, int d);
 

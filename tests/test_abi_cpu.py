@@ -46,7 +46,7 @@ def test_mask_workspace_bytes():
     assert L.sparge_attn_workspace_bytes(1, 40, 75600, 128) == packed_v
     assert L.sparge_attn_workspace_bytes(1, 40, 75600, 96) == 0
     lin = (2 * packed_v + 40 * (128 * 128 + 128) * 4 * (1 + 16)  # totals + 16 split partials
-           + 40 * 4)                                              # per-head branch flags
+           + (40 + 2 + 2 * 40) * 4)                              # branch flags, head lists
     assert L.sparse_linear_workspace_bytes(1, 40, 75600, 128) == lin
 
 
