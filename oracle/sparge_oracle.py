@@ -34,7 +34,11 @@ What it computes, step by step, in float64 with NumPy, written from the pages:
    (1 - alpha) (*) O_l with a learned vector alpha in [0, 1] (section 2A);
 10. post-tuning branch dropping (SALAD page): a head whose linear branch
    carries only small weights loses the branch, and its output is what the
-   formula gives with the linear term removed.
+   formula gives with the linear term removed;
+11. the backward of step 7 (the sparse attention is fine-tuned, SpargeAttention2
+   page, section 2B, so gradients pass through it): the log-sum-exp of every
+   row's kept scores, and dQ, dK, dV of O = softmax(scale Q K^T, dropped keys
+   masked) V for an upstream gradient dO, written out as the chain rule.
 
 Readings of points the pages leave open (each also listed in the design
 notes): mean pooling over the valid tokens of a partial last block; no
@@ -362,3 +366,46 @@ def sla2_mix_attention_head_dropping(q, k, v, kept, block_q: int, block_k: int, 
         a = np.asarray(alpha, np.float32).astype(np.float64)
         return a * masked_attention_head(q, k, v, kept, block_q, block_k, scale, q_blocks)
     return sla2_mix_attention_head(q, k, v, kept, block_q, block_k, scale, alpha, q_blocks)
+
+
+# ------------------------------------------------- sparse attention backward
+def masked_scores_head(q, k, kept, block_q: int, block_k: int, scale: float) -> np.ndarray:
+    """scale * Q K^T with -inf wherever the key's block is dropped for the
+    query's row block; float64 [N, N]."""
+    N = q.shape[0]
+    qb, kb = np.arange(N) // block_q, np.arange(N) // block_k
+    s = scale * (q @ k.T)
+    return np.where(kept[qb][:, kb], s, -np.inf)
+
+
+def masked_attention_lse_head(q, k, kept, block_q: int, block_k: int,
+                              scale: float) -> np.ndarray:
+    """log sum_u exp(scale q_t . k_u) over the kept keys of each row t; -inf
+    for a row with no kept key (the log of an empty sum)."""
+    s = masked_scores_head(q, k, kept, block_q, block_k, scale)
+    m = s.max(axis=1)
+    finite = np.isfinite(m)
+    out = np.full(s.shape[0], -np.inf)
+    out[finite] = m[finite] + np.log(np.exp(s[finite] - m[finite, None]).sum(axis=1))
+    return out
+
+
+def masked_attention_backward_head(q, k, v, kept, block_q: int, block_k: int, scale: float,
+                                   do: np.ndarray):
+    """dQ, dK, dV of O = P V, P = softmax of the masked scores, for the
+    upstream gradient dO (all float64 [N, d]). A row with no kept key has
+    O = 0 and passes no gradient. With D_t = sum_c dO_tc O_tc:
+        dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),
+        dQ = scale dS K,  dK = scale dS^T Q."""
+    s = masked_scores_head(q, k, kept, block_q, block_k, scale)
+    m = s.max(axis=1, keepdims=True)
+    live = np.isfinite(m[:, 0])
+    P = np.zeros_like(s)
+    e = np.exp(s[live] - m[live])
+    P[live] = e / e.sum(axis=1, keepdims=True)
+    o = P @ v
+    dv = P.T @ do
+    dp = do @ v.T
+    D = (do * o).sum(axis=1, keepdims=True)
+    ds = P * (dp - D)
+    return scale * (ds @ k), scale * (ds.T @ q), dv

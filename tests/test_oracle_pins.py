@@ -470,3 +470,70 @@ def test_dropped_mix_removes_the_linear_term_without_renormalising():
     np.testing.assert_allclose(o, 1.0, rtol=0, atol=1e-14)
     o = O.sparse_linear_attention_head_dropping(q, k, v, kept, 64, 64, 0.25, 0.06, 0.05)
     np.testing.assert_allclose(o[kept_rows], 1.0 + float(np.float32(0.06)), rtol=0, atol=1e-14)
+
+
+# ------------------------------------------- sparse attention backward (fp64)
+def _bwd_case(seed, N=70, d=8, bq=16, bk=16):
+    rng = np.random.default_rng(seed)
+    q, k, v, do = (rng.standard_normal((N, d)) for _ in range(4))
+    n_q, n_k = -(-N // bq), -(-N // bk)
+    kept = rng.random((n_q, n_k)) < 0.5
+    kept[0] = False          # a row block with no kept key: O = 0, no gradient
+    kept[1] = True
+    kept[2] = False
+    kept[2, n_k - 1] = True  # only the short last key block (70 = 4 * 16 + 6)
+    return q, k, v, do, kept
+
+
+def test_lse_is_the_log_of_the_softmax_denominator():
+    q, k, v, do, kept = _bwd_case(61)
+    lse = O.masked_attention_lse_head(q, k, kept, 16, 16, 0.3)
+    assert np.all(lse[:16] == -np.inf)                 # the empty row block
+    from scipy.special import logsumexp
+    s = 0.3 * (q @ k.T)
+    np.testing.assert_allclose(lse[16:32], logsumexp(s[16:32], axis=1), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse[32:48], logsumexp(s[32:48, 64:], axis=1), rtol=0, atol=1e-12)
+    # exp(scores - lse) are the softmax weights: the attention output again
+    o = O.masked_attention_head(q, k, v, kept, 16, 16, 0.3)
+    sm = O.masked_scores_head(q, k, kept, 16, 16, 0.3)
+    w = np.exp(sm[16:] - lse[16:, None])
+    np.testing.assert_allclose(w @ v, o[16:], rtol=0, atol=1e-12)
+
+
+def test_backward_matches_central_differences():
+    # the gradient of L = sum(dO * O) with respect to every input entry, by
+    # central differences of the forward oracle itself
+    q, k, v, do, kept = _bwd_case(62, N=40, d=4)
+    dq, dk, dv = O.masked_attention_backward_head(q, k, v, kept, 16, 16, 0.7, do)
+    f = lambda q_, k_, v_: float((do * O.masked_attention_head(q_, k_, v_, kept, 16, 16,
+                                                               0.7)).sum())
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = {"q": (xp, k, v), "k": (q, xp, v), "v": (q, k, xp)}[name]
+            args_m = {"q": (xm, k, v), "k": (q, xm, v), "v": (q, k, xm)}[name]
+            num[idx] = (f(*args_p) - f(*args_m)) / (2 * h)
+        np.testing.assert_allclose(g, num, rtol=0, atol=2e-8, err_msg=name)
+    assert np.all(dq[:16] == 0)  # the empty row block passes nothing back
+
+
+def test_backward_matches_torch_autograd():
+    # torch's own attention with a boolean mask, differentiated by autograd in
+    # float64 (rows with no kept key are left out: torch returns NaN there)
+    q, k, v, do, kept = _bwd_case(63, N=100, d=16, bq=32, bk=16)
+    kept[0] = True
+    dq, dk, dv = O.masked_attention_backward_head(q, k, v, kept, 32, 16, 0.25, do)
+    N = q.shape[0]
+    mask = torch.from_numpy(kept[np.arange(N) // 32][:, np.arange(N) // 16])
+    live = mask.any(dim=1)
+    t = [torch.from_numpy(x).clone().requires_grad_(True) for x in (q, k, v)]
+    o = torch.nn.functional.scaled_dot_product_attention(t[0][None], t[1][None], t[2][None],
+                                                         attn_mask=mask[None], scale=0.25)[0]
+    (o[live] * torch.from_numpy(do)[live]).sum().backward()
+    np.testing.assert_allclose(dq, t[0].grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dk, t[1].grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv, t[2].grad.numpy(), rtol=0, atol=1e-12)
