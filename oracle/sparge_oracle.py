@@ -378,34 +378,86 @@ def masked_scores_head(q, k, kept, block_q: int, block_k: int, scale: float) -> 
     return np.where(kept[qb][:, kb], s, -np.inf)
 
 
-def masked_attention_lse_head(q, k, kept, block_q: int, block_k: int,
-                              scale: float) -> np.ndarray:
+def masked_attention_lse_head(q, k, kept, block_q: int, block_k: int, scale: float,
+                              q_blocks=None) -> np.ndarray:
     """log sum_u exp(scale q_t . k_u) over the kept keys of each row t; -inf
-    for a row with no kept key (the log of an empty sum)."""
-    s = masked_scores_head(q, k, kept, block_q, block_k, scale)
-    m = s.max(axis=1)
-    finite = np.isfinite(m)
-    out = np.full(s.shape[0], -np.inf)
-    out[finite] = m[finite] + np.log(np.exp(s[finite] - m[finite, None]).sum(axis=1))
+    for a row with no kept key (the log of an empty sum); NaN for rows of
+    query blocks not in `q_blocks`."""
+    N = q.shape[0]
+    out = np.full(N, np.nan)
+    qb = block_bounds(N, block_q)
+    for i in (range(len(qb)) if q_blocks is None else q_blocks):
+        s0, s1 = qb[i]
+        toks = _kept_tokens(kept[i], N, block_k)
+        if toks.size == 0:
+            out[s0:s1] = -np.inf
+            continue
+        s = scale * (q[s0:s1] @ k[toks].T)
+        m = s.max(axis=1)
+        out[s0:s1] = m + np.log(np.exp(s - m[:, None]).sum(axis=1))
     return out
 
 
 def masked_attention_backward_head(q, k, v, kept, block_q: int, block_k: int, scale: float,
-                                   do: np.ndarray):
+                                   do: np.ndarray, o=None):
     """dQ, dK, dV of O = P V, P = softmax of the masked scores, for the
     upstream gradient dO (all float64 [N, d]). A row with no kept key has
     O = 0 and passes no gradient. With D_t = sum_c dO_tc O_tc:
         dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),
-        dQ = scale dS K,  dK = scale dS^T Q."""
+        dQ = scale dS K,  dK = scale dS^T Q.
+    `o`, if given, is the output the backward is handed (for instance the
+    forward's result rounded to bf16) and D is taken from it, as a backward
+    that receives O does; by default O is the exact one."""
     s = masked_scores_head(q, k, kept, block_q, block_k, scale)
     m = s.max(axis=1, keepdims=True)
     live = np.isfinite(m[:, 0])
     P = np.zeros_like(s)
     e = np.exp(s[live] - m[live])
     P[live] = e / e.sum(axis=1, keepdims=True)
-    o = P @ v
+    o = P @ v if o is None else o
     dv = P.T @ do
     dp = do @ v.T
     D = (do * o).sum(axis=1, keepdims=True)
     ds = P * (dp - D)
     return scale * (ds @ k), scale * (ds.T @ q), dv
+
+
+def masked_attention_backward_sampled(q, k, v, kept, block_q: int, block_k: int, scale: float,
+                                      do: np.ndarray, q_blocks, k_blocks, o=None):
+    """The same gradients as masked_attention_backward_head, evaluated only
+    where sampled, row block by row block so that no N x N matrix is formed:
+    dQ for the rows of `q_blocks`, dK and dV for the keys of `k_blocks` (every
+    row block that keeps one of them contributes). Returns (dq, dk, dv) as
+    float64 [N, d] with NaN outside the sampled rows / keys. `o` as for
+    masked_attention_backward_head."""
+    N, d = q.shape
+    qb, kb = block_bounds(N, block_q), block_bounds(N, block_k)
+    dq = np.full((N, d), np.nan)
+    dk = np.full((N, d), np.nan)
+    dv = np.full((N, d), np.nan)
+    k_blocks = sorted(set(k_blocks))
+    for j in k_blocks:
+        dk[kb[j][0]:kb[j][1]] = 0.0
+        dv[kb[j][0]:kb[j][1]] = 0.0
+    rows = sorted(set(q_blocks) | {i for i in range(len(qb)) if kept[i, k_blocks].any()})
+    for i in rows:
+        s0, s1 = qb[i]
+        toks = _kept_tokens(kept[i], N, block_k)
+        if toks.size == 0:
+            if i in q_blocks:
+                dq[s0:s1] = 0.0
+            continue
+        P = row_softmax(scale * (q[s0:s1] @ k[toks].T))
+        o_i = P @ v[toks] if o is None else o[s0:s1]
+        D = (do[s0:s1] * o_i).sum(axis=1, keepdims=True)
+        dS = P * (do[s0:s1] @ v[toks].T - D)
+        if i in q_blocks:
+            dq[s0:s1] = scale * (dS @ k[toks])
+        for j in k_blocks:
+            if not kept[i, j]:
+                continue
+            k0, k1 = kb[j]
+            cols = np.searchsorted(toks, np.arange(k0, k1))  # kept tokens are ascending
+            dk[k0:k1] += scale * (dS[:, cols].T @ q[s0:s1])
+            dv[k0:k1] += P[:, cols].T @ do[s0:s1]
+    return dq, dk, dv

@@ -537,3 +537,54 @@ def test_backward_matches_torch_autograd():
     np.testing.assert_allclose(dq, t[0].grad.numpy(), rtol=0, atol=1e-12)
     np.testing.assert_allclose(dk, t[1].grad.numpy(), rtol=0, atol=1e-12)
     np.testing.assert_allclose(dv, t[2].grad.numpy(), rtol=0, atol=1e-12)
+
+
+def test_sampled_backward_equals_the_full_one():
+    q, k, v, do, kept = _bwd_case(64, N=150, d=8, bq=32, bk=16)
+    full = O.masked_attention_backward_head(q, k, v, kept, 32, 16, 0.4, do)
+    part = O.masked_attention_backward_sampled(q, k, v, kept, 32, 16, 0.4, do,
+                                               q_blocks=[0, 2, 4], k_blocks=[1, 5, 9])
+    qrows = np.concatenate([np.arange(0, 32), np.arange(64, 96), np.arange(128, 150)])
+    keys = np.concatenate([np.arange(16, 32), np.arange(80, 96), np.arange(144, 150)])
+    np.testing.assert_allclose(part[0][qrows], full[0][qrows], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(part[1][keys], full[1][keys], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(part[2][keys], full[2][keys], rtol=0, atol=1e-13)
+    others = np.setdiff1d(np.arange(150), keys)
+    assert np.isnan(part[1][others]).all() and np.isnan(part[2][others]).all()
+
+
+def test_backward_with_a_handed_output():
+    # o = the exact O gives the same gradients; another o shifts D_t by
+    # delta_t = dO_t.(o_t - O_t), hence dS_tu by -P_tu delta_t and
+    # dQ_t by -scale delta_t sum_u P_tu K_u (a closed form)
+    q, k, v, do, kept = _bwd_case(65, N=90, d=8, bq=32, bk=16)
+    kept[0] = True
+    exact = O.masked_attention_backward_head(q, k, v, kept, 32, 16, 0.5, do)
+    o = O.masked_attention_head(q, k, v, kept, 32, 16, 0.5)
+    same = O.masked_attention_backward_head(q, k, v, kept, 32, 16, 0.5, do, o=o)
+    for a, b in zip(exact, same):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-14)
+    o2 = o + 0.01 * np.random.default_rng(66).standard_normal(o.shape)
+    shifted = O.masked_attention_backward_head(q, k, v, kept, 32, 16, 0.5, do, o=o2)
+    s = O.masked_scores_head(q, k, kept, 32, 16, 0.5)
+    P = np.where(np.isfinite(s), np.exp(s - s.max(axis=1, keepdims=True)), 0.0)
+    P /= P.sum(axis=1, keepdims=True)
+    delta = (do * (o2 - o)).sum(axis=1, keepdims=True)
+    np.testing.assert_allclose(shifted[0] - exact[0], -0.5 * delta * (P @ k), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(shifted[2], exact[2], rtol=0, atol=1e-14)  # dV has no D
+    part = O.masked_attention_backward_sampled(q, k, v, kept, 32, 16, 0.5, do, [0, 2], [1, 4],
+                                               o=o2)
+    np.testing.assert_allclose(part[0][:32], shifted[0][:32], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(part[1][16:32], shifted[1][16:32], rtol=0, atol=1e-13)
+
+
+def test_lse_row_blocks_match_the_dense_form():
+    q, k, v, do, kept = _bwd_case(67, N=100, d=8, bq=32, bk=16)
+    lse = O.masked_attention_lse_head(q, k, kept, 32, 16, 0.3)
+    s = O.masked_scores_head(q, k, kept, 32, 16, 0.3)
+    live = np.isfinite(s).any(axis=1)
+    from scipy.special import logsumexp
+    np.testing.assert_allclose(lse[live], logsumexp(s[live], axis=1), rtol=0, atol=1e-12)
+    assert np.all(np.isneginf(lse[~live]))
+    part = O.masked_attention_lse_head(q, k, kept, 32, 16, 0.3, q_blocks=[1])
+    assert np.isnan(part[:32]).all() and np.array_equal(part[32:64], lse[32:64])
