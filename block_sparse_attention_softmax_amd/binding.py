@@ -23,7 +23,8 @@ EXPORTS = ("sparge_mask_workspace_bytes", "sparge_mask_predict",
            "sparge_mask_routed_workspace_bytes", "sparge_mask_predict_routed",
            "sparge_attn_workspace_bytes", "sparge_attn_fwd", "sparge_attn_pack",
            "sparge_attn_fwd_packed", "sparse_linear_workspace_bytes", "sparse_linear_attn_fwd",
-           "sla2_mix_attn_fwd", "sparge_last_error")
+           "sla2_mix_attn_fwd", "sparge_attn_fwd_lse", "sparge_attn_bwd_workspace_bytes",
+           "sparge_attn_bwd", "sparge_last_error")
 
 _lib = None
 
@@ -57,6 +58,13 @@ def lib() -> ctypes.CDLL:
         L.sparge_attn_workspace_bytes.restype = c_size
         L.sparge_attn_fwd.argtypes = [vp] * 5 + [c_int] * 6 + [c_float, vp, vp, c_size, vp]
         L.sparge_attn_fwd.restype = c_int
+        L.sparge_attn_fwd_lse.argtypes = [vp] * 5 + [c_int] * 6 + [c_float, vp, vp, vp, c_size,
+                                                                    vp]
+        L.sparge_attn_fwd_lse.restype = c_int
+        L.sparge_attn_bwd_workspace_bytes.argtypes = [c_int] * 6
+        L.sparge_attn_bwd_workspace_bytes.restype = c_size
+        L.sparge_attn_bwd.argtypes = [vp] * 8 + [c_int] * 6 + [c_float] + [vp] * 4 + [c_size, vp]
+        L.sparge_attn_bwd.restype = c_int
         L.sparge_attn_pack.argtypes = [vp] + [c_int] * 4 + [vp, c_size, vp]
         L.sparge_attn_pack.restype = c_int
         L.sparge_attn_fwd_packed.argtypes = [vp] * 4 + [c_int] * 6 + [c_float, vp, vp, c_size, vp]
@@ -187,6 +195,46 @@ def sparge_attn_fwd(q, k, v, kv_idx, kv_cnt, block_q=128, block_k=64, scale=None
                                  N, d, block_q, block_k, scale, _ptr(o), _ptr(workspace),
                                  workspace.numel(), _stream(q)))
     return o
+
+
+def sparge_attn_fwd_lse(q, k, v, kv_idx, kv_cnt, block_q=128, block_k=64, scale=None,
+                        out=None, workspace=None):
+    """sparge_attn_fwd plus each row's log-sum-exp (float32 [B, H, N]); returns (o, lse)."""
+    B, H, N, d = _qkv(q, k, v)
+    o, lse = (torch.empty_like(q), torch.empty((B, H, N), dtype=torch.float32,
+                                               device=q.device)) if out is None else out
+    if scale is None:
+        scale = default_scale(d)
+    if workspace is None:
+        workspace = torch.empty(max(attn_workspace_bytes(B, H, N, d), 16), dtype=torch.uint8,
+                                device=q.device)
+    _check(lib().sparge_attn_fwd_lse(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_idx), _ptr(kv_cnt), B,
+                                     H, N, d, block_q, block_k, scale, _ptr(o), _ptr(lse),
+                                     _ptr(workspace), workspace.numel(), _stream(q)))
+    return o, lse
+
+
+def attn_bwd_workspace_bytes(B, H, N, d, block_q=128, block_k=64) -> int:
+    return lib().sparge_attn_bwd_workspace_bytes(B, H, N, d, block_q, block_k)
+
+
+def sparge_attn_bwd(q, k, v, o, d_o, lse, kv_idx, kv_cnt, block_q=128, block_k=64, scale=None,
+                    out=None, workspace=None):
+    """dQ, dK, dV of the block-sparse attention for the upstream gradient d_o."""
+    B, H, N, d = _qkv(q, k, v, o, d_o)
+    if lse.dtype != torch.float32 or not lse.is_cuda or tuple(lse.shape) != (B, H, N):
+        raise ValueError("lse must be a float32 GPU tensor of shape [B, H, N]")
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3)) if out is None else out
+    if scale is None:
+        scale = default_scale(d)
+    if workspace is None:
+        workspace = torch.empty(max(attn_bwd_workspace_bytes(B, H, N, d, block_q, block_k), 16),
+                                dtype=torch.uint8, device=q.device)
+    _check(lib().sparge_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse),
+                                 _ptr(kv_idx), _ptr(kv_cnt), B, H, N, d, block_q, block_k, scale,
+                                 _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                                 workspace.numel(), _stream(q)))
+    return dq, dk, dv
 
 
 def sparge_attn_pack(v, workspace=None):

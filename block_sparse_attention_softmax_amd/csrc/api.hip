@@ -258,6 +258,67 @@ int sparge_attn_fwd(const void* q, const void* k, const void* v, const int32_t* 
   return SPARGE_OK;
 }
 
+int sparge_attn_fwd_lse(const void* q, const void* k, const void* v, const int32_t* kv_idx,
+                        const int32_t* kv_cnt, int B, int H, int N, int d, int block_q,
+                        int block_k, float scale, void* o, float* lse, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  int rc = check_attn_args(q, k, v, kv_idx, kv_cnt, B, H, N, d, block_q, block_k, scale, o);
+  if (rc == SPARGE_OK) rc = check_attn_workspace(workspace, workspace_bytes, B, H, N, d);
+  if (rc != SPARGE_OK) return rc;
+  if (!lse || !aligned(lse, 4)) return fail(SPARGE_ERR_INVALID_ARG, "lse null or misaligned");
+  sparge::AttnLaunch a =
+      attn_args(q, k, v, kv_idx, kv_cnt, B, H, N, d, block_q, block_k, scale, o, workspace);
+  a.lse = lse;
+  const hipError_t e = sparge::launch_attn(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "sparge_attn_fwd_lse launch");
+  return SPARGE_OK;
+}
+
+size_t sparge_attn_bwd_workspace_bytes(int B, int H, int N, int d, int block_q, int block_k) {
+  const std::string saved = g_last_error;
+  const int rc = check_shape(B, H, N, d, block_q, block_k);
+  g_last_error = saved;
+  if (rc != SPARGE_OK) return 0;
+  return sparge::bwd_workspace_bytes(B, H, N, d, block_q);
+}
+
+int sparge_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* d_o,
+                    const float* lse, const int32_t* kv_idx, const int32_t* kv_cnt, int B,
+                    int H, int N, int d, int block_q, int block_k, float scale, void* dq,
+                    void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  int rc = check_attn_args(q, k, v, kv_idx, kv_cnt, B, H, N, d, block_q, block_k, scale, o);
+  if (rc != SPARGE_OK) return rc;
+  if (!d_o || !lse || !dq || !dk || !dv || !workspace)
+    return fail(SPARGE_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned(d_o, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+      !aligned(lse, 4) || !aligned(workspace, 16))
+    return fail(SPARGE_ERR_INVALID_ARG, "d_o, dq, dk, dv, lse or workspace misaligned");
+  if (workspace_bytes < sparge::bwd_workspace_bytes(B, H, N, d, block_q))
+    return fail(SPARGE_ERR_INVALID_ARG, "workspace too small");
+  sparge::BwdLaunch a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<const uint16_t*>(o);
+  a.dO = static_cast<const uint16_t*>(d_o);
+  a.lse = lse;
+  a.idx = kv_idx;
+  a.cnt = kv_cnt;
+  a.dq = static_cast<uint16_t*>(dq);
+  a.dk = static_cast<uint16_t*>(dk);
+  a.dv = static_cast<uint16_t*>(dv);
+  a.B = B; a.H = H; a.N = N; a.d = d; a.block_q = block_q;
+  a.n_q = ceil_div(N, block_q);
+  a.n_k = ceil_div(N, block_k);
+  a.scale = scale;
+  a.workspace = static_cast<unsigned char*>(workspace);
+  const hipError_t e = sparge::launch_bwd(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "sparge_attn_bwd launch");
+  return SPARGE_OK;
+}
+
 int sparge_attn_pack(const void* v, int B, int H, int N, int d, void* workspace,
                      size_t workspace_bytes, void* stream) {
   g_last_error.clear();

@@ -21,149 +21,12 @@
 // (no register round trip), double-buffered so the copies overlap the
 // products of earlier blocks.
 #include "internal.h"
+#include "tiles.h"
 
 #include <type_traits>
 
 namespace sparge {
 namespace {
-
-constexpr int BK = 64;
-
-// ------------------------------------------------------------- V packing
-// Slot of a key inside its 16-key group in a packed V^T row: slots 8*h + e
-// (h = lane / 32, e = 0..7) hold key 8*(e/4) + 4*h + e%4, the key that
-// register 8*hk + e of an S^T accumulator holds for that lane.
-__device__ __forceinline__ int packed_key(int slot) {
-  const int g = slot >> 4, h = (slot >> 3) & 1, e = slot & 7;
-  return 16 * g + 8 * (e >> 2) + 4 * h + (e & 3);
-}
-
-// phi(x) = elu(x) + 1, the feature map of the linear branch
-__device__ __forceinline__ float elu1(float x) { return x > 0.0f ? x + 1.0f : expf(x); }
-
-// vt[bh][j][d][slot] = V[bh][64*j + packed_key(slot)][d], zero past N; with
-// LIN also phikt[...] = bf16(phi(K[...])) in the same layout, for the heads
-// whose linear branch is evaluated (lin_on).
-// grid (n_k, B*H), 2*D threads; one 64-key block per workgroup. Thread t
-// takes keys 4q..4q+3 (q = t % 16) at d = 8c..8c+7 (c = t / 16): four 16-byte
-// rows in, transposed in registers, eight 8-byte pieces out. The four keys
-// occupy four consecutive slots, and the 16 lanes sharing c write whole
-// 128-byte rows of the packed block.
-template <int D, bool LIN>
-__global__ __launch_bounds__(2 * D) void pack_kernel(const uint16_t* __restrict__ v,
-                                                     const uint16_t* __restrict__ k,
-                                                     uint16_t* __restrict__ vt,
-                                                     uint16_t* __restrict__ phikt, int N,
-                                                     int n_k, const int32_t* __restrict__ lin_on,
-                                                     int H) {
-  const int j = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
-  const int q = t & 15, c = t >> 4;
-  // slot of key 4q: group q/4, then the inverse of packed_key within it
-  const int slot0 = 16 * (q >> 2) + 8 * (q & 1) + 4 * ((q >> 1) & 1);
-#pragma unroll
-  for (int w = 0; w < (LIN ? 2 : 1); ++w) {
-    if (w == 1 && !lin_on[bh % H]) break;  // the head's linear branch is dropped
-    const uint16_t* src = (w == 0 ? v : k) + ((size_t)bh * N + (size_t)j * BK) * D + c * 8;
-    uint32_t x[4][4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = 4 * q + r;
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (j * BK + key < N) {
-        u = *reinterpret_cast<const uint4*>(src + (size_t)key * D);
-        if (w == 1) {  // phi(K), rounded to bf16
-          uint32_t* p = &u.x;
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            p[e] = f32_to_bf16_rne(elu1(bf16_lo(p[e]))) |
-                   (f32_to_bf16_rne(elu1(bf16_hi(p[e]))) << 16);
-        }
-      }
-      x[r][0] = u.x; x[r][1] = u.y; x[r][2] = u.z; x[r][3] = u.w;
-    }
-    uint16_t* dst = (w == 0 ? vt : phikt) + ((size_t)bh * n_k + j) * (size_t)D * BK +
-                    (size_t)(8 * c) * BK + slot0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {  // d = 8c + 2e (low halves) and 8c + 2e + 1 (high)
-      uint2 lo, hi;
-      lo.x = (x[0][e] & 0xFFFFu) | (x[1][e] << 16);
-      lo.y = (x[2][e] & 0xFFFFu) | (x[3][e] << 16);
-      hi.x = (x[0][e] >> 16) | (x[1][e] & 0xFFFF0000u);
-      hi.y = (x[2][e] >> 16) | (x[3][e] & 0xFFFF0000u);
-      *reinterpret_cast<uint2*>(dst + (size_t)(2 * e) * BK) = lo;
-      *reinterpret_cast<uint2*>(dst + (size_t)(2 * e + 1) * BK) = hi;
-    }
-  }
-}
-
-// ------------------------------------------------------------ LDS tiles
-// K tile: [64 keys][D] row-major; V tile: packed V^T, [D][64 slots]. The
-// 16-byte chunks of every row are XOR-swizzled with the row index so that
-// the MFMA operand reads (16 lanes per cycle, 16 consecutive rows at one
-// logical chunk) cover all 64 banks: K rows are 256 bytes, so chunk c of row
-// r goes to c ^ (r mod 16); V^T rows are 128 bytes, two per bank window, so
-// chunk c goes to c ^ ((r / 2) mod 8).
-template <int D>
-struct Tile {
-  static constexpr int KROWB = D * 2;   // bytes per K row
-  static constexpr int KCPR = D / 8;    // 16-byte chunks per K row
-  static constexpr int VROWB = BK * 2;  // bytes per V^T row (128)
-  static constexpr int VCPR = BK / 8;   // 8
-  static constexpr int BYTES = BK * D * 2;  // one K, V^T or phi(K)^T tile
-  __device__ static constexpr int kchunk(int row, int chunk) { return chunk ^ (row & (KCPR - 1)); }
-  __device__ static constexpr int vchunk(int row, int chunk) { return chunk ^ ((row >> 1) & (VCPR - 1)); }
-};
-
-__device__ __forceinline__ bf16x8 lds_read16(const unsigned char* p) {
-  return *reinterpret_cast<const bf16x8*>(p);
-}
-
-// 16-byte global -> LDS copy without a register round trip (global_load_lds
-// dwordx4). `lds` must be the same for the whole wave: lane i's 16 bytes land
-// at lds + 16 * i. (Kept out of the kernel templates: the host pass drops a
-// template kernel's launch stub when its body names this builtin.)
-__device__ __forceinline__ void dma16(const void* src, void* lds) {
-  __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
-}
-
-// two floats -> two bf16 (round to nearest even) in one dword, low half first
-__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 v = {(__bf16)a, (__bf16)b};
-  return __builtin_bit_cast(uint32_t, v);
-}
-
-__device__ __forceinline__ bf16x8 pack_bf16x8(const floatx16& x, int base) {
-  bf16x8 r;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = (__bf16)x[base + e];
-  return r;
-}
-
-// acc + sum of the 8 bf16 values (v_dot2 against ones, float32 accumulate)
-__device__ __forceinline__ float row_sum_bf16x8(const bf16x8& p, float acc) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-  for (int e = 0; e < 8; e += 2) {
-    const bf16x2 pr = {p[e], p[e + 1]};
-    acc = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc, false);
-  }
-  return acc;
-}
-
-// max / sum over the two half-waves (lane l and lane l ^ 32): the swap
-// returns both values of the pair in its two results
-__device__ __forceinline__ float pair_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
-                                                  false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
-                                                  false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 // A row's running maximum is only raised (and O rescaled) when a block
 // raises it by more than 2^8 in the exponent; until then P <= 2^8, which
@@ -319,15 +182,18 @@ __global__ __launch_bounds__(kFlagThreads) void linear_flags_kernel(
 // through the lists of linear_flags_kernel.
 //
 // SEL (always with LIN) adds the head selection and the alpha scaling of the
-// epilogue; the plain kernel without it is compiled without either.
-template <int D, int BQ, bool LIN, bool SEL = LIN>
+// epilogue; the plain kernel without it is compiled without either. LSE
+// (plain kernel only) also stores every row's log-sum-exp of its kept scores,
+// ln(sum_u exp(scale q.k_u)), for the backward.
+template <int D, int BQ, bool LIN, bool SEL = LIN, bool LSE = false>
 __global__ __launch_bounds__(BQ * (LIN ? 4 : 2), (LIN || (D == 128 && BQ == 64)) ? 1 : 2) void sparse_attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ vt, const int32_t* __restrict__ kv_idx,
     const int32_t* __restrict__ kv_cnt, uint16_t* __restrict__ o, int H, int N, int n_q,
     int n_k, int total, float c, const float* __restrict__ alpha,
     const uint16_t* __restrict__ phikt, const float* __restrict__ lin_h,
-    const float* __restrict__ lin_z, const int32_t* __restrict__ sel_lists, int lin_mode) {
+    const float* __restrict__ lin_z, const int32_t* __restrict__ sel_lists, int lin_mode,
+    float* __restrict__ lse) {
   constexpr int NW = BQ / 32;
   using T = Tile<D>;
   constexpr int LOADS = BK * D / 8 / 64 / NW;
@@ -657,6 +523,11 @@ __global__ __launch_bounds__(BQ * (LIN ? 4 : 2), (LIN || (D == 128 && BQ == 64))
   // ---- epilogue: O = O^T / l, with the linear branch or alpha as above; bf16, rows < N only
   const float ltot = pair_sum(lsum);  // (H waves: z_kept entry 32*wave + l32)
   const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
+  if constexpr (LSE) {  // sum_u exp(scale s_u) = 2^(m c) * ltot; -inf for an empty row
+    if (h2 == 0 && qrow < N)
+      lse[(size_t)bh * N + qrow] =
+          ltot > 0.0f ? (m * c + log2f(ltot)) * 0.6931471805599453f : -INFINITY;
+  }
   // LIN: O_l for this lane's (d, query) entries, in the oacc layout, and
   // alpha[h] / (phi(Q_t) . z_D) for its query, handed over through LDS by the
   // H wave of the same index
@@ -809,16 +680,21 @@ hipError_t launch_sparse(const AttnLaunch& a, hipStream_t s, AttnPhase phase) {
     }
   }
   if (phase != kPackOnly) {
-    hipLaunchKernelGGL((sparse_attn_fwd_kernel<D, BQ, LIN>), dim3(total), dim3(BQ * (LIN ? 4 : 2)), 0, s,
-                       a.q, a.k, a.vt, a.idx, a.cnt, a.o, a.H, a.N, a.n_q, a.n_k, total, c,
-                       a.alpha, a.phikt, a.lin_h, a.lin_z, LIN ? a.lin_lists : nullptr,
-                       a.lin_mode);
+    if (!LIN && a.lse)
+      hipLaunchKernelGGL((sparse_attn_fwd_kernel<D, BQ, false, false, true>), dim3(total),
+                         dim3(BQ * 2), 0, s, a.q, a.k, a.vt, a.idx, a.cnt, a.o, a.H, a.N, a.n_q,
+                         a.n_k, total, c, nullptr, nullptr, nullptr, nullptr, nullptr, 0, a.lse);
+    else
+      hipLaunchKernelGGL((sparse_attn_fwd_kernel<D, BQ, LIN>), dim3(total), dim3(BQ * (LIN ? 4 : 2)), 0, s,
+                         a.q, a.k, a.vt, a.idx, a.cnt, a.o, a.H, a.N, a.n_q, a.n_k, total, c,
+                         a.alpha, a.phikt, a.lin_h, a.lin_z, LIN ? a.lin_lists : nullptr,
+                         a.lin_mode, nullptr);
     // heads whose branch is dropped: plain sparse attention (times alpha in the mix)
     if constexpr (LIN)
       hipLaunchKernelGGL((sparse_attn_fwd_kernel<D, BQ, false, true>), dim3(total), dim3(BQ * 2), 0, s,
                          a.q, a.k, a.vt, a.idx, a.cnt, a.o, a.H, a.N, a.n_q, a.n_k, total, c,
                          a.lin_mode == kLinMix ? a.alpha : nullptr, nullptr, nullptr, nullptr,
-                         a.lin_lists, a.lin_mode);
+                         a.lin_lists, a.lin_mode, nullptr);
   }
   return hipGetLastError();
 }

@@ -1,0 +1,554 @@
+// Backward of the block-sparse attention (the sparse attention of the
+// SpargeAttention2 page is fine-tuned by distillation, section 2B, so its
+// gradients are needed). With P = softmax over the kept keys of scale Q K^T,
+// O = P V and an upstream gradient dO:
+//
+//   D_t = dO_t . O_t,  dP = dO V^T,  dS = P * (dP - D),
+//   dV = P^T dO,  dK = scale dS^T Q,  dQ = scale dS K,
+//
+// where P is recomputed from the forward's per-row log-sum-exp. Two kernels,
+// both deterministic (no atomics on the results):
+//
+//  * dK, dV: one workgroup per (b, h, key block j). It walks the query blocks
+//    that list j (the transposed lists built below) in increasing order and
+//    accumulates dV^T = dO^T P and dK^T = Q^T dS in registers. S = Q K_j^T is
+//    computed with one key per lane (lane % 32) so that P and dS, converted
+//    to bf16, feed the second products as B operands unchanged, against Q^T
+//    and dO^T pre-packed in the same slot order as the forward's V^T.
+//  * dQ: one workgroup per (b, h, query block), the forward's loop over the
+//    row's list: S^T = K Q^T and dP^T = V dO^T with one query per lane, then
+//    dQ^T += K^T dS^T against K^T packed like V^T.
+//
+// Every product takes 16-bit operands with fp32 accumulation: bf16, except
+// dQ^T = K^T dS^T, which takes fp16. A row's dS sums to zero, so dQ_t =
+// scale sum_u dS_tu (K_u - c) for any c: when the kept keys share a large
+// common part (neighbouring tokens of a smooth field) the sum cancels, and
+// bf16's 8-bit rounding of dS would break the cancellation; fp16 keeps 11
+// bits at the same MFMA rate (dS is small, and K converts to fp16 exactly
+// in the range of attention inputs).
+#include <algorithm>
+
+#include "internal.h"
+#include "tiles.h"
+
+namespace sparge {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ halfx8 lds_read16_h(const unsigned char* p) {
+  return *reinterpret_cast<const halfx8*>(p);
+}
+
+__device__ __forceinline__ halfx8 pack_f16x8(const floatx16& x, int base) {
+  halfx8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (_Float16)x[base + e];
+  return r;
+}
+
+// ------------------------------------------------------------ row terms
+// D[bh][t] = sum_c dO[t][c] O[t][c] (fp32 from the bf16 values) and
+// lse2[bh][t] = lse[bh][t] * log2(e). 16 lanes per row, 16 rows per workgroup.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_rows_kernel(const uint16_t* __restrict__ o,
+                                                       const uint16_t* __restrict__ dO,
+                                                       const float* __restrict__ lse,
+                                                       float* __restrict__ drow,
+                                                       float* __restrict__ lse2, size_t rows) {
+  constexpr int LPR = D / 8;  // lanes per row, 8 elements each
+  constexpr int RPW = 256 / LPR;
+  const size_t row = (size_t)blockIdx.x * RPW + threadIdx.x / LPR;
+  const int part = threadIdx.x % LPR;
+  float acc = 0.0f;
+  if (row < rows) {
+    const uint4 a = *reinterpret_cast<const uint4*>(o + row * D + part * 8);
+    const uint4 b = *reinterpret_cast<const uint4*>(dO + row * D + part * 8);
+    const uint32_t* pa = &a.x;
+    const uint32_t* pb = &b.x;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc = fmaf(bf16_lo(pa[e]), bf16_lo(pb[e]), acc);
+      acc = fmaf(bf16_hi(pa[e]), bf16_hi(pb[e]), acc);
+    }
+  }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (row < rows && part == 0) {
+    drow[row] = acc;
+    lse2[row] = lse[row] * kLog2e;
+  }
+}
+
+// ----------------------------------------------------- transposed lists
+// cmat[bh][j][i] = how many times row block i lists key block j (entries
+// clamped to [0, n_k) and counts to [0, n_k] as the forward does). One wave
+// per (b, h, query block).
+__global__ __launch_bounds__(256) void col_count_kernel(const int32_t* __restrict__ kv_idx,
+                                                        const int32_t* __restrict__ kv_cnt,
+                                                        int32_t* __restrict__ cmat, int n_q,
+                                                        int n_k, int rows) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const int bh = row / n_q, i = row % n_q;
+  const int count = min(max(kv_cnt[row], 0), n_k);
+  for (int e = lane; e < count; e += 64) {
+    const int j = min(max(kv_idx[(size_t)row * n_k + e], 0), n_k - 1);
+    atomicAdd(&cmat[((size_t)bh * n_k + j) * n_q + i], 1);
+  }
+}
+
+// colcnt[bh][j] = sum_i cmat[bh][j][i]; one wave per (b, h, key block).
+__global__ __launch_bounds__(256) void col_total_kernel(const int32_t* __restrict__ cmat,
+                                                        int32_t* __restrict__ colcnt, int n_q,
+                                                        int cols) {
+  const int col = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (col >= cols) return;
+  int acc = 0;
+  for (int i = lane; i < n_q; i += 64) acc += cmat[(size_t)col * n_q + i];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (lane == 0) colcnt[col] = acc;
+}
+
+// coloff[bh][j] = sum of colcnt[bh][0 .. j-1], j = 0 .. n_k; one workgroup per
+// (b, h): each thread scans a contiguous run, then the run totals are scanned
+// through LDS.
+__global__ __launch_bounds__(256) void col_scan_kernel(const int32_t* __restrict__ colcnt,
+                                                       int32_t* __restrict__ coloff, int n_k) {
+  __shared__ int part[256];
+  const int bh = blockIdx.x, t = threadIdx.x;
+  const int per = (n_k + 255) / 256, b0 = min(t * per, n_k), b1 = min(b0 + per, n_k);
+  const int32_t* cc = colcnt + (size_t)bh * n_k;
+  int run = 0;
+  for (int j = b0; j < b1; ++j) run += cc[j];
+  part[t] = run;
+  __syncthreads();
+  if (t == 0) {
+    int acc = 0;
+    for (int u = 0; u < 256; ++u) {
+      const int x = part[u];
+      part[u] = acc;
+      acc += x;
+    }
+  }
+  __syncthreads();
+  int32_t* off = coloff + (size_t)bh * (n_k + 1);
+  int acc = part[t];
+  for (int j = b0; j < b1; ++j) {
+    off[j] = acc;
+    acc += cc[j];
+  }
+  if (t == 255) off[n_k] = acc;
+}
+
+// collist[bh][coloff[j] ..] = the query blocks listing key block j, in
+// increasing order, each repeated as often as it lists j. One wave per column.
+__global__ __launch_bounds__(256) void col_list_kernel(const int32_t* __restrict__ cmat,
+                                                       const int32_t* __restrict__ coloff,
+                                                       int32_t* __restrict__ collist, int n_q,
+                                                       int n_k, int cols) {
+  const int col = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (col >= cols) return;
+  const int bh = col / n_k, j = col % n_k;
+  int32_t* out = collist + (size_t)bh * n_q * n_k + coloff[(size_t)bh * (n_k + 1) + j];
+  int pos = 0;
+  for (int base = 0; base < n_q; base += 64) {
+    const int i = base + lane;
+    const int c = i < n_q ? cmat[(size_t)col * n_q + i] : 0;
+    int incl = c;  // inclusive prefix over the wave
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    for (int r = 0; r < c; ++r) out[pos + incl - c + r] = i;
+    pos += __shfl(incl, 63);
+  }
+}
+
+// --------------------------------------------------------- stage copies
+// 16-byte chunks of a [64 rows][D] row-major block (rows >= nrows zero) into a
+// K-layout tile, and of a packed [D][64] block into a V^T-layout tile, by the
+// NT threads of a workgroup.
+template <int D, int NT>
+__device__ __forceinline__ void stage_rows(unsigned char* dst, const uint16_t* src, int nrows) {
+  using T = Tile<D>;
+  static_assert(64 * T::KCPR % NT == 0, "whole chunks per thread");
+#pragma unroll
+  for (int u = 0; u < 64 * T::KCPR / NT; ++u) {
+    const int p = u * NT + threadIdx.x, r = p / T::KCPR, ch = p % T::KCPR;
+    uint4 x = make_uint4(0, 0, 0, 0);
+    if (r < nrows) x = *reinterpret_cast<const uint4*>(src + (size_t)r * D + ch * 8);
+    *reinterpret_cast<uint4*>(dst + r * T::KROWB + T::kchunk(r, ch) * 16) = x;
+  }
+}
+
+template <int D, int NT>
+__device__ __forceinline__ void stage_packed(unsigned char* dst, const uint16_t* src) {
+  using T = Tile<D>;
+  static_assert(D * T::VCPR % NT == 0, "whole chunks per thread");
+#pragma unroll
+  for (int u = 0; u < D * T::VCPR / NT; ++u) {
+    const int p = u * NT + threadIdx.x, r = p / T::VCPR, ch = p % T::VCPR;
+    const uint4 x = *reinterpret_cast<const uint4*>(src + (size_t)r * BK + ch * 8);
+    *reinterpret_cast<uint4*>(dst + r * T::VROWB + T::vchunk(r, ch) * 16) = x;
+  }
+}
+
+// --------------------------------------------------------------- dK, dV
+// Workgroup (b, h, key block j), 4 waves: wave w holds keys 32*(w & 1) .. +31
+// of the block (one per lane % 32) and takes queries 32*(w >> 1) .. +31 of
+// every 64-query stage; the two query halves are summed at the end.
+template <int D, int BQ>
+__global__ __launch_bounds__(256, D == 128 ? 1 : 2) void sparse_attn_bwd_dkdv_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dO,
+    const uint16_t* __restrict__ qt, const uint16_t* __restrict__ dot,
+    const float* __restrict__ lse2, const float* __restrict__ drow,
+    const int32_t* __restrict__ coloff, const int32_t* __restrict__ collist,
+    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int N, int n_q, int n_k, int n64,
+    int total, float c, float scale) {
+  using T = Tile<D>;
+  constexpr int DT = D / 32, KSTEPS = D / 16, SUB = BQ / 64;
+  __shared__ __align__(16) unsigned char smem[4 * T::BYTES + 2 * 64 * 4];
+  unsigned char* const qs = smem;                  // Q rows of the stage
+  unsigned char* const ds = smem + T::BYTES;       // dO rows
+  unsigned char* const qts = smem + 2 * T::BYTES;  // Q^T, packed
+  unsigned char* const dts = smem + 3 * T::BYTES;  // dO^T, packed
+  float* const ls = reinterpret_cast<float*>(smem + 4 * T::BYTES);  // lse2 of the stage rows
+  float* const dd = ls + 64;                                         // D of the stage rows
+
+  const int tile = xcd_remap(blockIdx.x, total);
+  const int bh = tile / n_k, j = tile % n_k;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h2 = lane >> 5, l32 = lane & 31, kw = 32 * (wave & 1), qh = wave >> 1;
+  const size_t head = (size_t)bh * N * D;
+  const int key = j * BK + kw + l32;
+
+  bf16x8 kf[KSTEPS], vf[KSTEPS];  // this lane's key row (zero past N)
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) {
+    kf[s] = bf16x8{};
+    vf[s] = bf16x8{};
+    if (key < N) {
+      kf[s] = *reinterpret_cast<const bf16x8*>(k + head + (size_t)key * D + 16 * s + 8 * h2);
+      vf[s] = *reinterpret_cast<const bf16x8*>(v + head + (size_t)key * D + 16 * s + 8 * h2);
+    }
+  }
+  floatx16 dka[DT], dva[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dka[i][r] = dva[i][r] = 0.0f;
+
+  const int beg = coloff[(size_t)bh * (n_k + 1) + j], end = coloff[(size_t)bh * (n_k + 1) + j + 1];
+  const int32_t* lst = collist + (size_t)bh * n_q * n_k;
+  for (int e = beg; e < end; ++e) {
+    const int i = lst[e];
+    for (int sb = 0; sb < SUB; ++sb) {
+      const int r0 = i * BQ + sb * 64;
+      if (r0 >= N) break;
+      const int g = r0 / 64;
+      __syncthreads();  // the previous stage is fully read
+      stage_rows<D, 256>(qs, q + head + (size_t)r0 * D, N - r0);
+      stage_rows<D, 256>(ds, dO + head + (size_t)r0 * D, N - r0);
+      stage_packed<D, 256>(qts, qt + ((size_t)bh * n64 + g) * D * BK);
+      stage_packed<D, 256>(dts, dot + ((size_t)bh * n64 + g) * D * BK);
+      if (threadIdx.x < 64) {
+        const int t = r0 + threadIdx.x;
+        ls[threadIdx.x] = t < N ? lse2[(size_t)bh * N + t] : INFINITY;  // P = 0 past N
+        dd[threadIdx.x] = t < N ? drow[(size_t)bh * N + t] : 0.0f;
+      }
+      __syncthreads();
+
+      // S = Q K^T and dP = dO V^T for the wave's 32 queries x 32 keys
+      floatx16 S, dP;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) S[r] = dP[r] = 0.0f;
+      const int qr = qh * 32 + l32;
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) {
+        const int ch = 2 * s + h2;
+        const bf16x8 a = lds_read16(qs + qr * T::KROWB + T::kchunk(qr, ch) * 16);
+        const bf16x8 b = lds_read16(ds + qr * T::KROWB + T::kchunk(qr, ch) * 16);
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[s], S, 0, 0, 0);
+        dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, vf[s], dP, 0, 0, 0);
+      }
+      // P = 2^(S c - lse2), dS = P (dP - D); register r holds query
+      // 8*(r/4) + 4*h2 + r%4 of the wave's 32
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        const int t0 = qh * 32 + 8 * gg + 4 * h2;
+        const float4 l4 = *reinterpret_cast<const float4*>(ls + t0);
+        const float4 d4 = *reinterpret_cast<const float4*>(dd + t0);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const int r = 4 * gg + e2;
+          const float p = __builtin_amdgcn_exp2f(fmaf(S[r], c, -lv[e2]));
+          S[r] = p;
+          dP[r] = p * (dP[r] - dv4[e2]);
+        }
+      }
+      // dV^T += dO^T P, dK^T += Q^T dS (k = the wave's queries, in slot order)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const bf16x8 pb = pack_bf16x8(S, 8 * t);
+        const bf16x8 sb2 = pack_bf16x8(dP, 8 * t);
+        const int ch = 4 * qh + 2 * t + h2;
+#pragma unroll
+        for (int ii = 0; ii < DT; ++ii) {
+          const int row = 32 * ii + l32;
+          const bf16x8 ao = lds_read16(dts + row * T::VROWB + T::vchunk(row, ch) * 16);
+          const bf16x8 aq = lds_read16(qts + row * T::VROWB + T::vchunk(row, ch) * 16);
+          dva[ii] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, pb, dva[ii], 0, 0, 0);
+          dka[ii] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, sb2, dka[ii], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // sum the two query halves: waves 2, 3 hand theirs to waves 0, 1
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem);  // [2 key halves][2][DT][16][64]
+  static_assert(2 * 2 * DT * 16 * 64 * 4 <= 4 * T::BYTES, "reduction must fit the stage");
+  const int kh = wave & 1;
+  if (qh == 1) {
+#pragma unroll
+    for (int ii = 0; ii < DT; ++ii)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        red[(((kh * 2 + 0) * DT + ii) * 16 + r) * 64 + lane] = dka[ii][r];
+        red[(((kh * 2 + 1) * DT + ii) * 16 + r) * 64 + lane] = dva[ii][r];
+      }
+  }
+  __syncthreads();
+  if (qh == 0 && key < N) {
+    uint16_t* krow = dk + head + (size_t)key * D;
+    uint16_t* vrow = dv + head + (size_t)key * D;
+#pragma unroll
+    for (int ii = 0; ii < DT; ++ii)
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        float yk[4], yv[4];
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const int r = 4 * gg + e2;
+          yk[e2] = scale * (dka[ii][r] + red[(((kh * 2 + 0) * DT + ii) * 16 + r) * 64 + lane]);
+          yv[e2] = dva[ii][r] + red[(((kh * 2 + 1) * DT + ii) * 16 + r) * 64 + lane];
+        }
+        const int d0 = 32 * ii + 8 * gg + 4 * h2;
+        uint2 pk;
+        pk.x = pack2_bf16(yk[0], yk[1]);
+        pk.y = pack2_bf16(yk[2], yk[3]);
+        *reinterpret_cast<uint2*>(krow + d0) = pk;
+        pk.x = pack2_bf16(yv[0], yv[1]);
+        pk.y = pack2_bf16(yv[2], yv[3]);
+        *reinterpret_cast<uint2*>(vrow + d0) = pk;
+      }
+  }
+}
+
+// ------------------------------------------------------------------- dQ
+// Workgroup (b, h, query block), BQ/32 waves of 32 queries (one per lane % 32)
+// walking the row's list: stage K_j rows, V_j rows and packed K_j^T (fp16),
+// then S^T = K Q^T, dP^T = V dO^T, P^T, dS^T and dQ^T += K^T dS^T.
+template <int D, int BQ>
+__global__ __launch_bounds__(BQ * 2, 2) void sparse_attn_bwd_dq_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dO,
+    const uint16_t* __restrict__ kt, const float* __restrict__ lse2,
+    const float* __restrict__ drow, const int32_t* __restrict__ kv_idx,
+    const int32_t* __restrict__ kv_cnt, uint16_t* __restrict__ dq, int N, int n_q, int n_k,
+    int total, float c, float scale) {
+  using T = Tile<D>;
+  constexpr int DT = D / 32, KSTEPS = D / 16, NT = BQ * 2;
+  static_assert(NT == 256 || NT == 128, "BQ is 64 or 128");
+  __shared__ __align__(16) unsigned char smem[3 * T::BYTES];
+  unsigned char* const ks = smem;
+  unsigned char* const vs = smem + T::BYTES;
+  unsigned char* const kts = smem + 2 * T::BYTES;
+
+  const int tile = xcd_remap(blockIdx.x, total);
+  const int bh = tile / n_q, qi = tile % n_q;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h2 = lane >> 5, l32 = lane & 31;
+  const size_t head = (size_t)bh * N * D;
+  const int qrow = qi * BQ + wave * 32 + l32;
+  const bool valid = qrow < N;
+
+  bf16x8 qf[KSTEPS], df[KSTEPS];
+  {
+    const size_t ro = head + (size_t)min(qrow, N - 1) * D + 8 * h2;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      qf[s] = *reinterpret_cast<const bf16x8*>(q + ro + 16 * s);
+      df[s] = *reinterpret_cast<const bf16x8*>(dO + ro + 16 * s);
+    }
+  }
+  const float lq = valid ? lse2[(size_t)bh * N + qrow] : INFINITY;
+  const float dq_d = valid ? drow[(size_t)bh * N + qrow] : 0.0f;
+  floatx16 acc[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
+
+  const int count = min(max(kv_cnt[tile], 0), n_k);
+  const int32_t* ids = kv_idx + (size_t)tile * n_k;
+  for (int e = 0; e < count; ++e) {
+    const int j = min(max(ids[e], 0), n_k - 1);
+    const int key0 = j * BK;
+    __syncthreads();  // the previous block is fully read
+    stage_rows<D, NT>(ks, k + head + (size_t)key0 * D, N - key0);
+    stage_rows<D, NT>(vs, v + head + (size_t)key0 * D, N - key0);
+    stage_packed<D, NT>(kts, kt + ((size_t)bh * n_k + j) * D * BK);
+    __syncthreads();
+    floatx16 S[2], dP[2];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) S[tau][r] = dP[tau][r] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      const int ch = 2 * s + h2;
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau) {
+        const int kr = 32 * tau + l32;
+        const bf16x8 a = lds_read16(ks + kr * T::KROWB + T::kchunk(kr, ch) * 16);
+        const bf16x8 b = lds_read16(vs + kr * T::KROWB + T::kchunk(kr, ch) * 16);
+        S[tau] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], S[tau], 0, 0, 0);
+        dP[tau] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, df[s], dP[tau], 0, 0, 0);
+      }
+    }
+    const int nvalid = N - key0;  // keys past N take no part
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kk = 32 * tau + 8 * (r >> 2) + 4 * h2 + (r & 3);
+        const float p = kk < nvalid ? __builtin_amdgcn_exp2f(fmaf(S[tau][r], c, -lq)) : 0.0f;
+        dP[tau][r] = p * (dP[tau][r] - dq_d);
+      }
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+      for (int hk = 0; hk < 2; ++hk) {
+        const halfx8 b = pack_f16x8(dP[tau], 8 * hk);
+        const int ch = 4 * tau + 2 * hk + h2;
+#pragma unroll
+        for (int ii = 0; ii < DT; ++ii) {
+          const int row = 32 * ii + l32;
+          const halfx8 a = lds_read16_h(kts + row * T::VROWB + T::vchunk(row, ch) * 16);
+          acc[ii] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc[ii], 0, 0, 0);
+        }
+      }
+  }
+  if (valid) {
+    uint16_t* orow = dq + head + (size_t)qrow * D;
+#pragma unroll
+    for (int ii = 0; ii < DT; ++ii)
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        const int d0 = 32 * ii + 8 * gg + 4 * h2;
+        uint2 pk;
+        pk.x = pack2_bf16(scale * acc[ii][4 * gg + 0], scale * acc[ii][4 * gg + 1]);
+        pk.y = pack2_bf16(scale * acc[ii][4 * gg + 2], scale * acc[ii][4 * gg + 3]);
+        *reinterpret_cast<uint2*>(orow + d0) = pk;
+      }
+  }
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(int32_t* __restrict__ p, size_t n) {
+  for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (size_t)gridDim.x * 256)
+    p[e] = 0;
+}
+
+size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// workspace regions, in order
+struct BwdWs {
+  uint16_t *qt, *dot, *kt;
+  float *drow, *lse2;
+  int32_t *cmat, *colcnt, *coloff, *collist;
+};
+
+BwdWs bwd_layout(unsigned char* w, int B, int H, int N, int d, int block_q, size_t* bytes) {
+  const size_t BH = (size_t)B * H, n_q = (N + block_q - 1) / block_q, n_k = (N + BK - 1) / BK;
+  const size_t packed = up256(BH * n_k * BK * d * 2);
+  BwdWs r{};
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    unsigned char* p = w ? w + off : nullptr;
+    off += up256(n);
+    return p;
+  };
+  r.qt = reinterpret_cast<uint16_t*>(take(packed));
+  r.dot = reinterpret_cast<uint16_t*>(take(packed));
+  r.kt = reinterpret_cast<uint16_t*>(take(packed));
+  r.drow = reinterpret_cast<float*>(take(BH * N * 4));
+  r.lse2 = reinterpret_cast<float*>(take(BH * N * 4));
+  r.cmat = reinterpret_cast<int32_t*>(take(BH * n_k * n_q * 4));
+  r.colcnt = reinterpret_cast<int32_t*>(take(BH * n_k * 4));
+  r.coloff = reinterpret_cast<int32_t*>(take(BH * (n_k + 1) * 4));
+  r.collist = reinterpret_cast<int32_t*>(take(BH * n_q * n_k * 4));
+  if (bytes) *bytes = off;
+  return r;
+}
+
+template <int D, int BQ>
+hipError_t launch_bwd_t(const BwdLaunch& a, hipStream_t s) {
+  const BwdWs w = bwd_layout(a.workspace, a.B, a.H, a.N, a.d, a.block_q, nullptr);
+  const int BH = a.B * a.H, n64 = a.n_k;  // 64-row groups of Q and dO = key blocks
+  const float c = a.scale * kLog2e;
+  // Q^T, dO^T and K^T (fp16) packed in 64-row groups like V^T
+  hipLaunchKernelGGL((pack_kernel<D, false>), dim3(n64, BH), dim3(2 * D), 0, s, a.q, nullptr,
+                     w.qt, nullptr, a.N, n64, nullptr, a.H);
+  hipLaunchKernelGGL((pack_kernel<D, false>), dim3(n64, BH), dim3(2 * D), 0, s, a.dO, nullptr,
+                     w.dot, nullptr, a.N, n64, nullptr, a.H);
+  hipLaunchKernelGGL((pack_kernel<D, false, true>), dim3(n64, BH), dim3(2 * D), 0, s, a.k,
+                     nullptr, w.kt, nullptr, a.N, n64, nullptr, a.H);
+  const size_t rows = (size_t)BH * a.N;
+  constexpr int RPW = 256 / (D / 8);
+  hipLaunchKernelGGL((bwd_rows_kernel<D>), dim3((unsigned)((rows + RPW - 1) / RPW)), dim3(256), 0,
+                     s, a.o, a.dO, a.lse, w.drow, w.lse2, rows);
+  // the query blocks that list each key block
+  const size_t cm = (size_t)BH * a.n_k * a.n_q;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)std::min<size_t>((cm + 255) / 256, 4096)),
+                     dim3(256), 0, s, w.cmat, cm);
+  const int qrows = BH * a.n_q, cols = BH * a.n_k;
+  hipLaunchKernelGGL(col_count_kernel, dim3((qrows + 3) / 4), dim3(256), 0, s, a.idx, a.cnt,
+                     w.cmat, a.n_q, a.n_k, qrows);
+  hipLaunchKernelGGL(col_total_kernel, dim3((cols + 3) / 4), dim3(256), 0, s, w.cmat, w.colcnt,
+                     a.n_q, cols);
+  hipLaunchKernelGGL(col_scan_kernel, dim3(BH), dim3(256), 0, s, w.colcnt, w.coloff, a.n_k);
+  hipLaunchKernelGGL(col_list_kernel, dim3((cols + 3) / 4), dim3(256), 0, s, w.cmat, w.coloff,
+                     w.collist, a.n_q, a.n_k, cols);
+  hipLaunchKernelGGL((sparse_attn_bwd_dkdv_kernel<D, BQ>), dim3(cols), dim3(256), 0, s, a.q, a.k,
+                     a.v, a.dO, w.qt, w.dot, w.lse2, w.drow, w.coloff, w.collist, a.dk, a.dv,
+                     a.N, a.n_q, a.n_k, n64, cols, c, a.scale);
+  hipLaunchKernelGGL((sparse_attn_bwd_dq_kernel<D, BQ>), dim3(qrows), dim3(BQ * 2), 0, s, a.q,
+                     a.k, a.v, a.dO, w.kt, w.lse2, w.drow, a.idx, a.cnt, a.dq, a.N, a.n_q,
+                     a.n_k, qrows, c, a.scale);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t bwd_workspace_bytes(int B, int H, int N, int d, int block_q) {
+  size_t bytes = 0;
+  bwd_layout(nullptr, B, H, N, d, block_q, &bytes);
+  return bytes;
+}
+
+hipError_t launch_bwd(const BwdLaunch& a, hipStream_t s) {
+  if (a.d == 128 && a.block_q == 128) return launch_bwd_t<128, 128>(a, s);
+  if (a.d == 128 && a.block_q == 64) return launch_bwd_t<128, 64>(a, s);
+  if (a.d == 64 && a.block_q == 128) return launch_bwd_t<64, 128>(a, s);
+  return launch_bwd_t<64, 64>(a, s);
+}
+
+}  // namespace sparge

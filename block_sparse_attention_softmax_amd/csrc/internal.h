@@ -71,6 +71,7 @@ struct AttnLaunch {
   float scale;
   // workspace: V packed key-contiguous per block, [B*H, n_k, d, 64]
   uint16_t* vt;
+  float* lse;  // [B*H, N] natural log-sum-exp of each row's kept scores, or nullptr
   // linear branch (alpha == nullptr: plain sparse attention)
   const float* alpha;  // kLinAdd: [H]; kLinMix: [H, d]
   int lin_mode;        // LinMode
@@ -90,6 +91,25 @@ enum LinMode { kLinAdd = 0, kLinMix = 1 };
 // pack (V, and phi(K) for the linear branch) then attend; or either half alone
 enum AttnPhase { kPackAndAttend = 0, kPackOnly = 1, kAttendOnly = 2 };
 hipError_t launch_attn(const AttnLaunch& a, hipStream_t s, AttnPhase phase = kPackAndAttend);
+// backward of the block-sparse attention: dQ, dK, dV for an upstream dO
+struct BwdLaunch {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dO;
+  const float* lse;  // [B*H, N] from the forward
+  const int32_t* idx;
+  const int32_t* cnt;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  int B, H, N, d, block_q, n_q, n_k;
+  float scale;
+  unsigned char* workspace;  // bwd_workspace_bytes()
+};
+hipError_t launch_bwd(const BwdLaunch& a, hipStream_t s);
+size_t bwd_workspace_bytes(int B, int H, int N, int d, int block_q);
 size_t attn_workspace_bytes(int B, int H, int N, int d);    // packed V
 size_t linear_workspace_bytes(int B, int H, int N, int d);  // packed V + linear branch
 

@@ -170,6 +170,54 @@ int sparge_attn_fwd_packed(const void* q, const void* k, const int32_t* kv_idx,
                            int block_q, int block_k, float scale, void* o,
                            const void* workspace, size_t workspace_bytes, void* stream);
 
+/* sparge_attn_fwd that also stores, for the backward, the natural
+ * log-sum-exp of every row's kept scores:
+ *   lse[b][h][t] = ln sum_{u kept for t} exp(scale * Q_t . K_u),
+ * -inf for a row whose list is empty. Computed from the forward's own float32
+ * running maximum and sum (the sum of the bf16-rounded weights it normalises
+ * by). O is bit for bit that of sparge_attn_fwd.
+ *
+ *  lse : out float32 [B, H, N], device, 4-byte aligned.
+ *  Other arguments as for sparge_attn_fwd. */
+int sparge_attn_fwd_lse(const void* q, const void* k, const void* v,
+                        const int32_t* kv_idx, const int32_t* kv_cnt, int B, int H, int N,
+                        int d, int block_q, int block_k, float scale, void* o, float* lse,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Device workspace (bytes) of sparge_attn_bwd: Q, dO and K packed like V,
+ * two float32 values per row, and the transposed lists (for every key block,
+ * the query blocks that list it): about 3 * B*H*N*d*2 + 8*B*H*N +
+ * 8*B*H*n_q*n_k bytes. Returns 0 for arguments sparge_attn_bwd would reject. */
+size_t sparge_attn_bwd_workspace_bytes(int B, int H, int N, int d, int block_q, int block_k);
+
+/* Backward of sparge_attn_fwd (the sparse attention is fine-tuned in the
+ * SpargeAttention2 page, section 2B). For O = P V with P the softmax over the
+ * listed keys of scale Q K^T and an upstream gradient dO, with
+ * D_t = dO_t . O_t:
+ *   dV = P^T dO,  dS = P * (dO V^T - D),  dQ = scale dS K,  dK = scale dS^T Q.
+ * P is recomputed in float32 as exp(scale Q_t.K_u - lse_t); products take
+ * 16-bit operands with float32 accumulation: bf16 (P and dS rounded to
+ * bf16), except dQ = scale dS K, which takes dS and K as fp16 (a row's dS
+ * sums to zero, so dQ cancels where the kept keys are alike, and fp16 keeps
+ * three more bits; K must lie within fp16's range, |K| <= 65504); dQ, dK, dV
+ * are rounded to bf16. The same kv_idx / kv_cnt as the forward (any
+ * order; a block listed twice counts twice); keys in no list get dK = dV = 0,
+ * rows with an empty list dQ = 0. Deterministic: no atomics on the results.
+ *
+ *  q, k, v, o, d_o : bf16 [B, H, N, d], device, 16-byte aligned (o and lse
+ *                    from sparge_attn_fwd_lse on the same q, k, v and lists).
+ *  lse             : float32 [B, H, N], device.
+ *  dq, dk, dv      : out bf16 [B, H, N, d], device, 16-byte aligned; must
+ *                    not overlap the inputs or each other.
+ *  workspace       : device scratch of at least sparge_attn_bwd_workspace_bytes(),
+ *                    16-byte aligned; contents on entry do not matter.
+ *  Other arguments as for sparge_attn_fwd. */
+int sparge_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                    const void* d_o, const float* lse, const int32_t* kv_idx,
+                    const int32_t* kv_cnt, int B, int H, int N, int d, int block_q,
+                    int block_k, float scale, void* dq, void* dk, void* dv, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
 /* Device workspace (bytes) of sparse_linear_attn_fwd: the packed V of
  * sparge_attn_fwd, phi(K) packed the same way, and per (b, h) the float32
  * summaries sum_u phi(K_u)^T V_u (d x d) and sum_u phi(K_u) (d) with 16

@@ -177,3 +177,42 @@ def _routed(**kw):
 def test_routed_mask_rejects_bad_arguments(kw, code):
     assert _routed(**kw) == code
     assert binding.lib().sparge_last_error().decode()
+
+
+def test_backward_workspace_bytes():
+    L = binding.lib()
+    up = lambda x: (x + 255) // 256 * 256
+    B, H, N, d, bq = 1, 12, 32760, 128, 128
+    BH, n_q, n_k = B * H, math.ceil(N / bq), math.ceil(N / 64)
+    packed = up(BH * n_k * 64 * d * 2)
+    want = (3 * packed + 2 * up(BH * N * 4) + up(BH * n_k * n_q * 4) + up(BH * n_k * 4)
+            + up(BH * (n_k + 1) * 4) + up(BH * n_q * n_k * 4))
+    assert L.sparge_attn_bwd_workspace_bytes(B, H, N, d, bq, 64) == want
+    assert L.sparge_attn_bwd_workspace_bytes(1, 1, 100, 96, 128, 64) == 0
+
+
+def _bwd(**kw):
+    args = dict(q=A, k=A, v=A, o=A, do=A, lse=A, idx=A, cnt=A, B=1, H=2, N=1024, d=64, bq=64,
+                bk=64, sc=0.125, dq=A, dk=A, dv=A, ws=A, wsb=1 << 30, st=None)
+    args.update(kw)
+    return binding.lib().sparge_attn_bwd(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(do=None), -1), (dict(lse=None), -1), (dict(dq=None), -1), (dict(ws=None), -1),
+    (dict(do=MIS), -1), (dict(dk=MIS), -1), (dict(lse=ctypes.c_void_p(0x10001)), -1),
+    (dict(wsb=1024), -1), (dict(d=96), -2), (dict(bk=128), -2), (dict(sc=0.0), -1),
+    (dict(q=None), -1),
+])
+def test_backward_rejects_bad_arguments(kw, code):
+    assert _bwd(**kw) == code
+    assert binding.lib().sparge_last_error().decode()
+
+
+def test_forward_lse_rejects_bad_arguments():
+    L = binding.lib()
+    args = [A, A, A, A, A, 1, 2, 1024, 64, 64, 64, 0.125, A, None, A, 1 << 30, None]
+    assert L.sparge_attn_fwd_lse(*args) == -1
+    args[13] = ctypes.c_void_p(0x10002)
+    assert L.sparge_attn_fwd_lse(*args) == -1
+    assert "lse" in L.sparge_last_error().decode()
