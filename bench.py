@@ -274,6 +274,41 @@ def main():
             "drop_all": {"alpha": "0 on every head (every branch dropped)",
                          "ms_per_step": round(w7 * 1e3, 4), "sparse_linear_ms": round(l7, 4)}}
 
+    # backward of the sparse attention (dQ, dK, dV for a random dO), on the headline
+    # mask and at the 95% point; the forward with log-sum-exp runs once, untimed
+    d_o = torch.randn(q.shape, dtype=torch.float32, device=dev,
+                      generator=torch.Generator(device=dev).manual_seed(3)).to(torch.bfloat16)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    grads = [torch.empty_like(q) for _ in range(3)]
+    bws = torch.empty(S.attn_bwd_workspace_bytes(B, H, N, d, wl.block_q, wl.block_k),
+                      dtype=torch.uint8, device=dev)
+    backward = {}
+    for name, kfrac, pm, n_b in (("headline", wl.k_frac, wl.p_mass, max(3, args.steps // 5)),
+                                 ("p0_k5", 0.05, 0.0, max(5, args.steps // 2))):
+        S.sparge_mask_predict(q, k, wl.block_q, wl.block_k, kfrac, pm, wl.scale, workspace=ws,
+                              out=(bits, idx, cnt))
+        S.sparge_attn_fwd_lse(q, k, v, idx, cnt, wl.block_q, wl.block_k, wl.scale, out=(o, lse),
+                              workspace=aws)
+
+        def bwd():
+            S.sparge_attn_bwd(q, k, v, o, d_o, lse, idx, cnt, wl.block_q, wl.block_k, wl.scale,
+                              out=grads, workspace=bws)
+        bwd()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n_b):
+            bwd()
+        e1.record()
+        torch.cuda.synchronize()
+        b_ms = e0.elapsed_time(e1) / n_b
+        c_np, i_np = cnt.cpu().numpy(), idx.cpu().numpy()
+        kfb = 2.5 * kept_flops(c_np, i_np, N, d, wl.block_q, wl.block_k)  # 5 products
+        backward[name] = {"k": kfrac, "p": pm,
+                          "block_sparsity": round(1 - float(c_np.sum()) / (B * H * n_q * n_k), 4),
+                          "bwd_ms": round(b_ms, 4), "algorithmic_tflops": round(kfb / b_ms / 1e9, 2),
+                          "frac_bf16_peak": round(kfb / b_ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
+
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl, Q, K, V, args.cpu_blocks)
 
     line = {
@@ -299,6 +334,7 @@ def main():
         "operating_points": points,
         "sparse_linear": linear,
         "sla2_salad": sla2,
+        "backward": backward,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

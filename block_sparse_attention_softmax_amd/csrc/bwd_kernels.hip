@@ -51,21 +51,28 @@ __device__ __forceinline__ halfx8 pack_f16x8(const floatx16& x, int base) {
 
 // ------------------------------------------------------------ row terms
 // D[bh][t] = sum_c dO[t][c] O[t][c] (fp32 from the bf16 values) and
-// lse2[bh][t] = lse[bh][t] * log2(e). 16 lanes per row, 16 rows per workgroup.
+// lse2[bh][t] = lse[bh][t] * log2(e), in rows padded to NP = 64 * ceil(N / 64)
+// per (b, h) so that whole 64-row groups can be copied: padding rows get
+// D = 0 and lse2 = +inf (P = 0). D/8 lanes per row.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_rows_kernel(const uint16_t* __restrict__ o,
                                                        const uint16_t* __restrict__ dO,
                                                        const float* __restrict__ lse,
                                                        float* __restrict__ drow,
-                                                       float* __restrict__ lse2, size_t rows) {
+                                                       float* __restrict__ lse2, int N, int NP,
+                                                       size_t rows) {
   constexpr int LPR = D / 8;  // lanes per row, 8 elements each
   constexpr int RPW = 256 / LPR;
-  const size_t row = (size_t)blockIdx.x * RPW + threadIdx.x / LPR;
+  const size_t row = (size_t)blockIdx.x * RPW + threadIdx.x / LPR;  // padded row
   const int part = threadIdx.x % LPR;
+  const size_t bh = row / NP;
+  const int t = (int)(row % NP);
+  const bool live = row < rows && t < N;
+  const size_t src = bh * N + t;
   float acc = 0.0f;
-  if (row < rows) {
-    const uint4 a = *reinterpret_cast<const uint4*>(o + row * D + part * 8);
-    const uint4 b = *reinterpret_cast<const uint4*>(dO + row * D + part * 8);
+  if (live) {
+    const uint4 a = *reinterpret_cast<const uint4*>(o + src * D + part * 8);
+    const uint4 b = *reinterpret_cast<const uint4*>(dO + src * D + part * 8);
     const uint32_t* pa = &a.x;
     const uint32_t* pb = &b.x;
 #pragma unroll
@@ -78,7 +85,7 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(const uint16_t* __restric
   for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
   if (row < rows && part == 0) {
     drow[row] = acc;
-    lse2[row] = lse[row] * kLog2e;
+    lse2[row] = live ? lse[src] * kLog2e : INFINITY;
   }
 }
 
@@ -202,6 +209,25 @@ __device__ __forceinline__ void stage_packed(unsigned char* dst, const uint16_t*
 // Workgroup (b, h, key block j), 4 waves: wave w holds keys 32*(w & 1) .. +31
 // of the block (one per lane % 32) and takes queries 32*(w >> 1) .. +31 of
 // every 64-query stage; the two query halves are summed at the end.
+//
+// A stage (Q rows, dO rows, packed Q^T and dO^T of one 64-row group, and its
+// lse2 and D) is copied global -> LDS by direct-to-LDS loads into one of two
+// buffers while the waves compute on the other. Lane i of a wave's copy lands
+// at LDS base + 16 i, so each lane reads the global chunk that the tile's XOR
+// swizzle puts there; rows past N read row N - 1 instead (their lse2 is +inf,
+// so they contribute P = dS = 0).
+template <int D>
+struct DkdvStage {
+  using T = Tile<D>;
+  static constexpr int BYTES = 4 * T::BYTES + 2 * 64 * 4;
+  static constexpr int QS = 0, DS = T::BYTES, QTS = 2 * T::BYTES, DTS = 3 * T::BYTES,
+                       LS = 4 * T::BYTES, DD = 4 * T::BYTES + 256;
+};
+
+__device__ __forceinline__ void dma4(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds(src, lds, 4, 0, 0);
+}
+
 template <int D, int BQ>
 __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void sparse_attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -212,20 +238,18 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void sparse_attn_bwd_dkdv_ke
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int N, int n_q, int n_k, int n64,
     int total, float c, float scale) {
   using T = Tile<D>;
+  using ST = DkdvStage<D>;
   constexpr int DT = D / 32, KSTEPS = D / 16, SUB = BQ / 64;
-  __shared__ __align__(16) unsigned char smem[4 * T::BYTES + 2 * 64 * 4];
-  unsigned char* const qs = smem;                  // Q rows of the stage
-  unsigned char* const ds = smem + T::BYTES;       // dO rows
-  unsigned char* const qts = smem + 2 * T::BYTES;  // Q^T, packed
-  unsigned char* const dts = smem + 3 * T::BYTES;  // dO^T, packed
-  float* const ls = reinterpret_cast<float*>(smem + 4 * T::BYTES);  // lse2 of the stage rows
-  float* const dd = ls + 64;                                         // D of the stage rows
+  constexpr int KU = 64 * T::KCPR / 256, VU = D * T::VCPR / 256;  // 16-byte copies per thread
+  __shared__ __align__(16) unsigned char smem[2 * ST::BYTES];
 
   const int tile = xcd_remap(blockIdx.x, total);
   const int bh = tile / n_k, j = tile % n_k;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // copy bases are uniform
   const int h2 = lane >> 5, l32 = lane & 31, kw = 32 * (wave & 1), qh = wave >> 1;
   const size_t head = (size_t)bh * N * D;
+  const int NP = n64 * BK;
   const int key = j * BK + kw + l32;
 
   bf16x8 kf[KSTEPS], vf[KSTEPS];  // this lane's key row (zero past N)
@@ -244,77 +268,128 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void sparse_attn_bwd_dkdv_ke
 #pragma unroll
     for (int r = 0; r < 16; ++r) dka[i][r] = dva[i][r] = 0.0f;
 
+  // per-thread source offsets (elements) of the tile copies, within a row group
+  uint32_t krow_ofs[KU], vrow_ofs[VU];
+  int krow[KU];
+#pragma unroll
+  for (int u = 0; u < KU; ++u) {
+    const int p = u * 256 + threadIdx.x, r = p / T::KCPR;
+    krow[u] = r;
+    krow_ofs[u] = (uint32_t)(r * D + T::kchunk(r, p % T::KCPR) * 8);
+  }
+#pragma unroll
+  for (int u = 0; u < VU; ++u) {
+    const int p = u * 256 + threadIdx.x, r = p / T::VCPR;
+    vrow_ofs[u] = (uint32_t)(r * BK + T::vchunk(r, p % T::VCPR) * 8);
+  }
+
   const int beg = coloff[(size_t)bh * (n_k + 1) + j], end = coloff[(size_t)bh * (n_k + 1) + j + 1];
   const int32_t* lst = collist + (size_t)bh * n_q * n_k;
-  for (int e = beg; e < end; ++e) {
-    const int i = lst[e];
-    for (int sb = 0; sb < SUB; ++sb) {
-      const int r0 = i * BQ + sb * 64;
-      if (r0 >= N) break;
-      const int g = r0 / 64;
-      __syncthreads();  // the previous stage is fully read
-      stage_rows<D, 256>(qs, q + head + (size_t)r0 * D, N - r0);
-      stage_rows<D, 256>(ds, dO + head + (size_t)r0 * D, N - r0);
-      stage_packed<D, 256>(qts, qt + ((size_t)bh * n64 + g) * D * BK);
-      stage_packed<D, 256>(dts, dot + ((size_t)bh * n64 + g) * D * BK);
-      if (threadIdx.x < 64) {
-        const int t = r0 + threadIdx.x;
-        ls[threadIdx.x] = t < N ? lse2[(size_t)bh * N + t] : INFINITY;  // P = 0 past N
-        dd[threadIdx.x] = t < N ? drow[(size_t)bh * N + t] : 0.0f;
+  // stages: (entry e, sub-block sb) with row r0 = lst[e] * BQ + 64 sb < N
+  auto first_row = [&](int e, int sb) { return lst[e] * BQ + 64 * sb; };
+  auto advance = [&](int& e, int& sb) {  // to the next stage that starts before N
+    do {
+      if (++sb == SUB) {
+        sb = 0;
+        ++e;
       }
-      __syncthreads();
+    } while (e < end && first_row(e, sb) >= N);
+  };
+  auto issue = [&](int r0, unsigned char* buf) {
+    const uint16_t* qsrc = q + head + (size_t)r0 * D;
+    const uint16_t* dsrc = dO + head + (size_t)r0 * D;
+    const size_t g = (size_t)bh * n64 + r0 / 64;
+    const uint16_t* qtsrc = qt + g * D * BK;
+    const uint16_t* dtsrc = dot + g * D * BK;
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      const uint32_t back = (uint32_t)max(r0 + krow[u] - (N - 1), 0) * D;  // rows past N
+      unsigned char* dst = buf + (u * 256 + wave * 64) * 16;
+      dma16(qsrc + krow_ofs[u] - back, dst + ST::QS);
+      dma16(dsrc + krow_ofs[u] - back, dst + ST::DS);
+    }
+#pragma unroll
+    for (int u = 0; u < VU; ++u) {
+      unsigned char* dst = buf + (u * 256 + wave * 64) * 16;
+      dma16(qtsrc + vrow_ofs[u], dst + ST::QTS);
+      dma16(dtsrc + vrow_ofs[u], dst + ST::DTS);
+    }
+    if (wave == 0) dma4(lse2 + (size_t)bh * NP + r0 + lane, buf + ST::LS);
+    if (wave == 1) dma4(drow + (size_t)bh * NP + r0 + lane, buf + ST::DD);
+  };
 
-      // S = Q K^T and dP = dO V^T for the wave's 32 queries x 32 keys
-      floatx16 S, dP;
+  int e = beg, sb = 0;
+  if (e < end && first_row(e, sb) >= N) advance(e, sb);
+  int it = 0;
+  if (e < end) issue(first_row(e, sb), smem);
+  while (e < end) {
+    unsigned char* const buf = smem + (it & 1) * ST::BYTES;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of the stage landed
+    __syncthreads();                     // every wave's copies landed, the other buffer is free
+    int en = e, sn = sb;
+    advance(en, sn);
+    if (en < end) issue(first_row(en, sn), smem + ((it + 1) & 1) * ST::BYTES);
+
+    const unsigned char* qs = buf + ST::QS;
+    const unsigned char* ds = buf + ST::DS;
+    const unsigned char* qts = buf + ST::QTS;
+    const unsigned char* dts = buf + ST::DTS;
+    const float* ls = reinterpret_cast<const float*>(buf + ST::LS);
+    const float* dd = reinterpret_cast<const float*>(buf + ST::DD);
+
+    // S = Q K^T and dP = dO V^T for the wave's 32 queries x 32 keys
+    floatx16 S, dP;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) S[r] = dP[r] = 0.0f;
-      const int qr = qh * 32 + l32;
+    for (int r = 0; r < 16; ++r) S[r] = dP[r] = 0.0f;
+    const int qr = qh * 32 + l32;
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
-        const int ch = 2 * s + h2;
-        const bf16x8 a = lds_read16(qs + qr * T::KROWB + T::kchunk(qr, ch) * 16);
-        const bf16x8 b = lds_read16(ds + qr * T::KROWB + T::kchunk(qr, ch) * 16);
-        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[s], S, 0, 0, 0);
-        dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, vf[s], dP, 0, 0, 0);
-      }
-      // P = 2^(S c - lse2), dS = P (dP - D); register r holds query
-      // 8*(r/4) + 4*h2 + r%4 of the wave's 32
+    for (int s = 0; s < KSTEPS; ++s) {
+      const int ch = 2 * s + h2;
+      const bf16x8 a = lds_read16(qs + qr * T::KROWB + T::kchunk(qr, ch) * 16);
+      const bf16x8 b = lds_read16(ds + qr * T::KROWB + T::kchunk(qr, ch) * 16);
+      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[s], S, 0, 0, 0);
+      dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, vf[s], dP, 0, 0, 0);
+    }
+    // P = 2^(S c - lse2), dS = P (dP - D); register r holds query
+    // 8*(r/4) + 4*h2 + r%4 of the wave's 32
 #pragma unroll
-      for (int gg = 0; gg < 4; ++gg) {
-        const int t0 = qh * 32 + 8 * gg + 4 * h2;
-        const float4 l4 = *reinterpret_cast<const float4*>(ls + t0);
-        const float4 d4 = *reinterpret_cast<const float4*>(dd + t0);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+    for (int gg = 0; gg < 4; ++gg) {
+      const int t0 = qh * 32 + 8 * gg + 4 * h2;
+      const float4 l4 = *reinterpret_cast<const float4*>(ls + t0);
+      const float4 d4 = *reinterpret_cast<const float4*>(dd + t0);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          const int r = 4 * gg + e2;
-          const float p = __builtin_amdgcn_exp2f(fmaf(S[r], c, -lv[e2]));
-          S[r] = p;
-          dP[r] = p * (dP[r] - dv4[e2]);
-        }
-      }
-      // dV^T += dO^T P, dK^T += Q^T dS (k = the wave's queries, in slot order)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const bf16x8 pb = pack_bf16x8(S, 8 * t);
-        const bf16x8 sb2 = pack_bf16x8(dP, 8 * t);
-        const int ch = 4 * qh + 2 * t + h2;
-#pragma unroll
-        for (int ii = 0; ii < DT; ++ii) {
-          const int row = 32 * ii + l32;
-          const bf16x8 ao = lds_read16(dts + row * T::VROWB + T::vchunk(row, ch) * 16);
-          const bf16x8 aq = lds_read16(qts + row * T::VROWB + T::vchunk(row, ch) * 16);
-          dva[ii] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, pb, dva[ii], 0, 0, 0);
-          dka[ii] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, sb2, dka[ii], 0, 0, 0);
-        }
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const int r = 4 * gg + e2;
+        const float p = __builtin_amdgcn_exp2f(fmaf(S[r], c, -lv[e2]));
+        S[r] = p;
+        dP[r] = p * (dP[r] - dv4[e2]);
       }
     }
+    // dV^T += dO^T P, dK^T += Q^T dS (k = the wave's queries, in slot order)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const bf16x8 pb = pack_bf16x8(S, 8 * t);
+      const bf16x8 sb2 = pack_bf16x8(dP, 8 * t);
+      const int ch = 4 * qh + 2 * t + h2;
+#pragma unroll
+      for (int ii = 0; ii < DT; ++ii) {
+        const int row = 32 * ii + l32;
+        const bf16x8 ao = lds_read16(dts + row * T::VROWB + T::vchunk(row, ch) * 16);
+        const bf16x8 aq = lds_read16(qts + row * T::VROWB + T::vchunk(row, ch) * 16);
+        dva[ii] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, pb, dva[ii], 0, 0, 0);
+        dka[ii] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, sb2, dka[ii], 0, 0, 0);
+      }
+    }
+    e = en;
+    sb = sn;
+    ++it;
   }
 
   // sum the two query halves: waves 2, 3 hand theirs to waves 0, 1
   __syncthreads();
   float* red = reinterpret_cast<float*>(smem);  // [2 key halves][2][DT][16][64]
-  static_assert(2 * 2 * DT * 16 * 64 * 4 <= 4 * T::BYTES, "reduction must fit the stage");
+  static_assert(2 * 2 * DT * 16 * 64 * 4 <= 2 * DkdvStage<D>::BYTES, "reduction must fit");
   const int kh = wave & 1;
   if (qh == 1) {
 #pragma unroll
@@ -327,8 +402,8 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void sparse_attn_bwd_dkdv_ke
   }
   __syncthreads();
   if (qh == 0 && key < N) {
-    uint16_t* krow = dk + head + (size_t)key * D;
-    uint16_t* vrow = dv + head + (size_t)key * D;
+    uint16_t* krow_p = dk + head + (size_t)key * D;
+    uint16_t* vrow_p = dv + head + (size_t)key * D;
 #pragma unroll
     for (int ii = 0; ii < DT; ++ii)
 #pragma unroll
@@ -344,10 +419,10 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void sparse_attn_bwd_dkdv_ke
         uint2 pk;
         pk.x = pack2_bf16(yk[0], yk[1]);
         pk.y = pack2_bf16(yk[2], yk[3]);
-        *reinterpret_cast<uint2*>(krow + d0) = pk;
+        *reinterpret_cast<uint2*>(krow_p + d0) = pk;
         pk.x = pack2_bf16(yv[0], yv[1]);
         pk.y = pack2_bf16(yv[2], yv[3]);
-        *reinterpret_cast<uint2*>(vrow + d0) = pk;
+        *reinterpret_cast<uint2*>(vrow_p + d0) = pk;
       }
   }
 }
@@ -389,8 +464,9 @@ __global__ __launch_bounds__(BQ * 2, 2) void sparse_attn_bwd_dq_kernel(
       df[s] = *reinterpret_cast<const bf16x8*>(dO + ro + 16 * s);
     }
   }
-  const float lq = valid ? lse2[(size_t)bh * N + qrow] : INFINITY;
-  const float dq_d = valid ? drow[(size_t)bh * N + qrow] : 0.0f;
+  const int NP = 64 * ((N + 63) / 64);
+  const float lq = valid ? lse2[(size_t)bh * NP + qrow] : INFINITY;
+  const float dq_d = valid ? drow[(size_t)bh * NP + qrow] : 0.0f;
   floatx16 acc[DT];
 #pragma unroll
   for (int i = 0; i < DT; ++i)
@@ -489,8 +565,8 @@ BwdWs bwd_layout(unsigned char* w, int B, int H, int N, int d, int block_q, size
   r.qt = reinterpret_cast<uint16_t*>(take(packed));
   r.dot = reinterpret_cast<uint16_t*>(take(packed));
   r.kt = reinterpret_cast<uint16_t*>(take(packed));
-  r.drow = reinterpret_cast<float*>(take(BH * N * 4));
-  r.lse2 = reinterpret_cast<float*>(take(BH * N * 4));
+  r.drow = reinterpret_cast<float*>(take(BH * n_k * BK * 4));  // padded rows
+  r.lse2 = reinterpret_cast<float*>(take(BH * n_k * BK * 4));
   r.cmat = reinterpret_cast<int32_t*>(take(BH * n_k * n_q * 4));
   r.colcnt = reinterpret_cast<int32_t*>(take(BH * n_k * 4));
   r.coloff = reinterpret_cast<int32_t*>(take(BH * (n_k + 1) * 4));
@@ -511,10 +587,11 @@ hipError_t launch_bwd_t(const BwdLaunch& a, hipStream_t s) {
                      w.dot, nullptr, a.N, n64, nullptr, a.H);
   hipLaunchKernelGGL((pack_kernel<D, false, true>), dim3(n64, BH), dim3(2 * D), 0, s, a.k,
                      nullptr, w.kt, nullptr, a.N, n64, nullptr, a.H);
-  const size_t rows = (size_t)BH * a.N;
+  const int NP = n64 * BK;
+  const size_t rows = (size_t)BH * NP;
   constexpr int RPW = 256 / (D / 8);
   hipLaunchKernelGGL((bwd_rows_kernel<D>), dim3((unsigned)((rows + RPW - 1) / RPW)), dim3(256), 0,
-                     s, a.o, a.dO, a.lse, w.drow, w.lse2, rows);
+                     s, a.o, a.dO, a.lse, w.drow, w.lse2, a.N, NP, rows);
   // the query blocks that list each key block
   const size_t cm = (size_t)BH * a.n_k * a.n_q;
   hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)std::min<size_t>((cm + 255) / 256, 4096)),
