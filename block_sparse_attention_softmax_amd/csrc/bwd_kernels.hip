@@ -176,35 +176,6 @@ __global__ __launch_bounds__(256) void col_list_kernel(const int32_t* __restrict
   }
 }
 
-// --------------------------------------------------------- stage copies
-// 16-byte chunks of a [64 rows][D] row-major block (rows >= nrows zero) into a
-// K-layout tile, and of a packed [D][64] block into a V^T-layout tile, by the
-// NT threads of a workgroup.
-template <int D, int NT>
-__device__ __forceinline__ void stage_rows(unsigned char* dst, const uint16_t* src, int nrows) {
-  using T = Tile<D>;
-  static_assert(64 * T::KCPR % NT == 0, "whole chunks per thread");
-#pragma unroll
-  for (int u = 0; u < 64 * T::KCPR / NT; ++u) {
-    const int p = u * NT + threadIdx.x, r = p / T::KCPR, ch = p % T::KCPR;
-    uint4 x = make_uint4(0, 0, 0, 0);
-    if (r < nrows) x = *reinterpret_cast<const uint4*>(src + (size_t)r * D + ch * 8);
-    *reinterpret_cast<uint4*>(dst + r * T::KROWB + T::kchunk(r, ch) * 16) = x;
-  }
-}
-
-template <int D, int NT>
-__device__ __forceinline__ void stage_packed(unsigned char* dst, const uint16_t* src) {
-  using T = Tile<D>;
-  static_assert(D * T::VCPR % NT == 0, "whole chunks per thread");
-#pragma unroll
-  for (int u = 0; u < D * T::VCPR / NT; ++u) {
-    const int p = u * NT + threadIdx.x, r = p / T::VCPR, ch = p % T::VCPR;
-    const uint4 x = *reinterpret_cast<const uint4*>(src + (size_t)r * BK + ch * 8);
-    *reinterpret_cast<uint4*>(dst + r * T::VROWB + T::vchunk(r, ch) * 16) = x;
-  }
-}
-
 // --------------------------------------------------------------- dK, dV
 // Workgroup (b, h, key block j), 4 waves: wave w holds keys 32*(w & 1) .. +31
 // of the block (one per lane % 32) and takes queries 32*(w >> 1) .. +31 of
@@ -429,10 +400,14 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void sparse_attn_bwd_dkdv_ke
 
 // ------------------------------------------------------------------- dQ
 // Workgroup (b, h, query block), BQ/32 waves of 32 queries (one per lane % 32)
-// walking the row's list: stage K_j rows, V_j rows and packed K_j^T (fp16),
-// then S^T = K Q^T, dP^T = V dO^T, P^T, dS^T and dQ^T += K^T dS^T.
+// walking the row's list: S^T = K Q^T, dP^T = V dO^T, P^T, dS^T and
+// dQ^T += K^T dS^T. K_j and V_j rows are copied global -> LDS by direct-to-LDS
+// loads, double-buffered (the copies of block e+1 run during block e); the
+// packed fp16 K_j^T tile is single-buffered and refilled once every wave has
+// finished its dQ product, so that copy overlaps the next block's S^T and
+// dP^T products. 5 tiles: 80 KB for d = 128, two workgroups per CU.
 template <int D, int BQ>
-__global__ __launch_bounds__(BQ * 2, 2) void sparse_attn_bwd_dq_kernel(
+__global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void sparse_attn_bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dO,
     const uint16_t* __restrict__ kt, const float* __restrict__ lse2,
@@ -441,15 +416,17 @@ __global__ __launch_bounds__(BQ * 2, 2) void sparse_attn_bwd_dq_kernel(
     int total, float c, float scale) {
   using T = Tile<D>;
   constexpr int DT = D / 32, KSTEPS = D / 16, NT = BQ * 2;
-  static_assert(NT == 256 || NT == 128, "BQ is 64 or 128");
-  __shared__ __align__(16) unsigned char smem[3 * T::BYTES];
-  unsigned char* const ks = smem;
-  unsigned char* const vs = smem + T::BYTES;
-  unsigned char* const kts = smem + 2 * T::BYTES;
+  constexpr int KU = 64 * T::KCPR / NT, VU = D * T::VCPR / NT;  // 16-byte copies per thread
+  static_assert(64 * T::KCPR % NT == 0 && D * T::VCPR % NT == 0, "whole copies per thread");
+  __shared__ __align__(16) unsigned char smem[5 * T::BYTES];
+  unsigned char* const kbuf = smem;                // K rows, two buffers
+  unsigned char* const vbuf = smem + 2 * T::BYTES;  // V rows, two buffers
+  unsigned char* const kts = smem + 4 * T::BYTES;   // K^T, fp16, packed
 
   const int tile = xcd_remap(blockIdx.x, total);
   const int bh = tile / n_q, qi = tile % n_q;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // copy bases are uniform
   const int h2 = lane >> 5, l32 = lane & 31;
   const size_t head = (size_t)bh * N * D;
   const int qrow = qi * BQ + wave * 32 + l32;
@@ -473,16 +450,52 @@ __global__ __launch_bounds__(BQ * 2, 2) void sparse_attn_bwd_dq_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
 
+  uint32_t krow_ofs[KU], vrow_ofs[VU];
+  int krow[KU];
+#pragma unroll
+  for (int u = 0; u < KU; ++u) {
+    const int p = u * NT + threadIdx.x, r = p / T::KCPR;
+    krow[u] = r;
+    krow_ofs[u] = (uint32_t)(r * D + T::kchunk(r, p % T::KCPR) * 8);
+  }
+#pragma unroll
+  for (int u = 0; u < VU; ++u) {
+    const int p = u * NT + threadIdx.x, r = p / T::VCPR;
+    vrow_ofs[u] = (uint32_t)(r * BK + T::vchunk(r, p % T::VCPR) * 8);
+  }
   const int count = min(max(kv_cnt[tile], 0), n_k);
   const int32_t* ids = kv_idx + (size_t)tile * n_k;
-  for (int e = 0; e < count; ++e) {
-    const int j = min(max(ids[e], 0), n_k - 1);
+  auto jat = [&](int e) { return min(max(ids[e], 0), n_k - 1); };
+  auto issue_kv = [&](int j, int b) {  // rows past N read row N - 1 (their P is 0)
     const int key0 = j * BK;
-    __syncthreads();  // the previous block is fully read
-    stage_rows<D, NT>(ks, k + head + (size_t)key0 * D, N - key0);
-    stage_rows<D, NT>(vs, v + head + (size_t)key0 * D, N - key0);
-    stage_packed<D, NT>(kts, kt + ((size_t)bh * n_k + j) * D * BK);
-    __syncthreads();
+    const uint16_t* ksrc = k + head + (size_t)key0 * D;
+    const uint16_t* vsrc = v + head + (size_t)key0 * D;
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      const uint32_t back = (uint32_t)max(key0 + krow[u] - (N - 1), 0) * D;
+      const int slot = (u * NT + wave * 64) * 16;
+      dma16(ksrc + krow_ofs[u] - back, kbuf + b * T::BYTES + slot);
+      dma16(vsrc + krow_ofs[u] - back, vbuf + b * T::BYTES + slot);
+    }
+  };
+  auto issue_kt = [&](int j) {
+    const uint16_t* src = kt + ((size_t)bh * n_k + j) * D * BK;
+#pragma unroll
+    for (int u = 0; u < VU; ++u) dma16(src + vrow_ofs[u], kts + (u * NT + wave * 64) * 16);
+  };
+
+  if (count > 0) {
+    issue_kv(jat(0), 0);
+    issue_kt(jat(0));
+  }
+  for (int e = 0; e < count; ++e) {
+    const int j = jat(e);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies for block e landed
+    __syncthreads();                     // every wave's copies landed; buffer (e+1)&1 is free
+    if (e + 1 < count) issue_kv(jat(e + 1), (e + 1) & 1);
+    const unsigned char* ks = kbuf + (e & 1) * T::BYTES;
+    const unsigned char* vs = vbuf + (e & 1) * T::BYTES;
+
     floatx16 S[2], dP[2];
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau)
@@ -500,7 +513,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void sparse_attn_bwd_dq_kernel(
         dP[tau] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, df[s], dP[tau], 0, 0, 0);
       }
     }
-    const int nvalid = N - key0;  // keys past N take no part
+    const int nvalid = N - j * BK;  // keys past N take no part
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
@@ -522,6 +535,8 @@ __global__ __launch_bounds__(BQ * 2, 2) void sparse_attn_bwd_dq_kernel(
           acc[ii] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc[ii], 0, 0, 0);
         }
       }
+    __syncthreads();  // every wave is done with K^T of block e
+    if (e + 1 < count) issue_kt(jat(e + 1));
   }
   if (valid) {
     uint16_t* orow = dq + head + (size_t)qrow * D;
