@@ -461,3 +461,117 @@ def masked_attention_backward_sampled(q, k, v, kept, block_q: int, block_k: int,
             dk[k0:k1] += scale * (dS[:, cols].T @ q[s0:s1])
             dv[k0:k1] += P[:, cols].T @ do[s0:s1]
     return dq, dk, dv
+
+
+# ------------------------------------------------ linear branch backward
+def elu_plus_one_grad(x: np.ndarray) -> np.ndarray:
+    """phi'(x) for phi = elu + 1: 1 for x > 0, exp(x) otherwise."""
+    return np.where(x > 0, 1.0, np.exp(np.minimum(x, 0.0)))
+
+
+def linear_branch_backward_head(q, k, v, kept, block_q: int, block_k: int, g: np.ndarray):
+    """dQ, dK, dV of the linear branch O_l (linear_branch_head) for an upstream
+    gradient G on O_l (float64 [N, d]). Per row block i, with D_i its dropped
+    keys, H = sum_{u in D_i} phi(K_u)^T V_u, z = sum_{u in D_i} phi(K_u) and for
+    each of its rows num_t = phi(Q_t) H, den_t = phi(Q_t).z, O_l,t = num_t/den_t:
+        dnum_t = G_t / den_t,   dden_t = -(G_t . O_l,t) / den_t,
+        dphi(Q_t) = H dnum_t + z dden_t,
+        dH = sum_t phi(Q_t)^T dnum_t,   dz = sum_t phi(Q_t) dden_t,
+    and every dropped key u of the block receives dphi(K_u) += dH V_u + dz,
+    dV_u += phi(K_u) dH; dQ, dK follow through phi'. A block that dropped
+    nothing passes no gradient."""
+    N, d = q.shape
+    dq, dk, dv = np.zeros((N, d)), np.zeros((N, d)), np.zeros((N, v.shape[1]))
+    fq, fk = elu_plus_one(q), elu_plus_one(k)
+    dfk = np.zeros((N, d))
+    for i, (s0, s1) in enumerate(block_bounds(N, block_q)):
+        toks = _kept_tokens(~kept[i], N, block_k)
+        if toks.size == 0:
+            continue
+        H = fk[toks].T @ v[toks]
+        z = fk[toks].sum(axis=0)
+        num = fq[s0:s1] @ H
+        den = fq[s0:s1] @ z
+        ol = num / den[:, None]
+        dnum = g[s0:s1] / den[:, None]
+        dden = -(g[s0:s1] * ol).sum(axis=1) / den
+        dfq = dnum @ H.T + np.outer(dden, z)
+        dq[s0:s1] = dfq * elu_plus_one_grad(q[s0:s1])
+        dH = fq[s0:s1].T @ dnum
+        dz = fq[s0:s1].T @ dden
+        dfk[toks] += v[toks] @ dH.T + dz
+        dv[toks] += fk[toks] @ dH
+    dk = dfk * elu_plus_one_grad(k)
+    return dq, dk, dv
+
+
+def sparse_linear_attention_backward_head(q, k, v, kept, block_q: int, block_k: int,
+                                          scale: float, alpha: float, do: np.ndarray, o=None):
+    """dQ, dK, dV of O = O_s + alpha O_l: the sparse part receives dO (with
+    D_t = dO_t . O_s,t, O_s = O - alpha O_l when the handed O is given), the
+    linear part alpha dO."""
+    o_s = None
+    if o is not None:
+        o_s = o - float(np.float32(alpha)) * linear_branch_head(q, k, v, kept, block_q, block_k)
+    gs = masked_attention_backward_head(q, k, v, kept, block_q, block_k, scale, do, o=o_s)
+    gl = linear_branch_backward_head(q, k, v, kept, block_q, block_k,
+                                     float(np.float32(alpha)) * do)
+    return tuple(a + b for a, b in zip(gs, gl))
+
+
+def sla2_mix_attention_backward_head(q, k, v, kept, block_q: int, block_k: int, scale: float,
+                                     alpha, do: np.ndarray, o=None):
+    """dQ, dK, dV of O = alpha (*) O_s + (1 - alpha) (*) O_l: the sparse part
+    receives alpha (*) dO (with O_s = (O - (1 - alpha) O_l) / alpha from a handed
+    O, where alpha > 0), the linear part (1 - alpha) (*) dO."""
+    a = np.asarray(alpha, np.float32).astype(np.float64)
+    o_s = None
+    if o is not None:
+        o_s = (o - (1.0 - a) * linear_branch_head(q, k, v, kept, block_q, block_k)) / a
+    gs = masked_attention_backward_head(q, k, v, kept, block_q, block_k, scale, a * do, o=o_s)
+    gl = linear_branch_backward_head(q, k, v, kept, block_q, block_k, (1.0 - a) * do)
+    return tuple(x + y for x, y in zip(gs, gl))
+
+
+def linear_branch_backward_sampled(q, k, v, kept, block_q: int, block_k: int, g: np.ndarray,
+                                   q_blocks, k_blocks):
+    """linear_branch_backward_head evaluated only where sampled: dQ for the rows
+    of `q_blocks`, dK and dV for the keys of `k_blocks` (every row block that
+    drops one of them contributes). NaN elsewhere."""
+    N, d = q.shape
+    qb, kb = block_bounds(N, block_q), block_bounds(N, block_k)
+    dq = np.full((N, d), np.nan)
+    dk = np.full((N, d), np.nan)
+    dv = np.full((N, v.shape[1]), np.nan)
+    k_blocks = sorted(set(k_blocks))
+    keys = np.concatenate([np.arange(*kb[j]) for j in k_blocks])
+    dfk = np.zeros((keys.size, d))
+    dvk = np.zeros((keys.size, v.shape[1]))
+    fk = elu_plus_one(k)
+    for i, (s0, s1) in enumerate(qb):
+        drops = [j for j in k_blocks if not kept[i, j]]
+        if i not in q_blocks and not drops:
+            continue
+        toks = _kept_tokens(~kept[i], N, block_k)
+        if toks.size == 0:
+            if i in q_blocks:
+                dq[s0:s1] = 0.0
+            continue
+        fq = elu_plus_one(q[s0:s1])
+        H = fk[toks].T @ v[toks]
+        z = fk[toks].sum(axis=0)
+        num, den = fq @ H, fq @ z
+        ol = num / den[:, None]
+        dnum = g[s0:s1] / den[:, None]
+        dden = -(g[s0:s1] * ol).sum(axis=1) / den
+        if i in q_blocks:
+            dq[s0:s1] = (dnum @ H.T + np.outer(dden, z)) * elu_plus_one_grad(q[s0:s1])
+        if drops:
+            dH = fq.T @ dnum
+            dz = fq.T @ dden
+            sel = np.isin(keys, np.concatenate([np.arange(*kb[j]) for j in drops]))
+            dfk[sel] += v[keys[sel]] @ dH.T + dz
+            dvk[sel] += fk[keys[sel]] @ dH
+    dk[keys] = dfk * elu_plus_one_grad(k[keys])
+    dv[keys] = dvk
+    return dq, dk, dv

@@ -588,3 +588,98 @@ def test_lse_row_blocks_match_the_dense_form():
     assert np.all(np.isneginf(lse[~live]))
     part = O.masked_attention_lse_head(q, k, kept, 32, 16, 0.3, q_blocks=[1])
     assert np.isnan(part[:32]).all() and np.array_equal(part[32:64], lse[32:64])
+
+
+# ------------------------------------------------- linear branch backward
+def test_linear_backward_matches_central_differences():
+    q, k, v, g, kept = _bwd_case(71, N=40, d=4)
+    kept[1] = False          # a block that dropped everything
+    kept[0] = True           # and one that dropped nothing: no linear gradient
+    grads = O.linear_branch_backward_head(q, k, v, kept, 16, 16, g)
+    f = lambda q_, k_, v_: float((g * O.linear_branch_head(q_, k_, v_, kept, 16, 16)).sum())
+    h = 1e-6
+    for which, g_an in enumerate(grads):
+        x = (q, k, v)[which]
+        num = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            xp, xm = [a.copy() for a in (q, k, v)], [a.copy() for a in (q, k, v)]
+            xp[which][idx] += h
+            xm[which][idx] -= h
+            num[idx] = (f(*xp) - f(*xm)) / (2 * h)
+        np.testing.assert_allclose(g_an, num, rtol=0, atol=2e-8, err_msg="qkv"[which])
+    assert np.all(grads[0][:16] == 0)
+
+
+def test_linear_backward_matches_torch_autograd():
+    # the associative form phi(Q) (sum phi(K)^T V) / phi(Q) sum phi(K), written
+    # in torch per row block and differentiated by autograd in float64
+    q, k, v, g, kept = _bwd_case(72, N=100, d=8, bq=32, bk=16)
+    kept[1] = False
+    grads = O.linear_branch_backward_head(q, k, v, kept, 32, 16, g)
+    t = [torch.from_numpy(x).clone().requires_grad_(True) for x in (q, k, v)]
+    phi = lambda x: torch.nn.functional.elu(x) + 1.0
+    total = torch.zeros((), dtype=torch.float64)
+    for i in range(kept.shape[0]):
+        rows = slice(32 * i, min(100, 32 * i + 32))
+        drop = torch.from_numpy(np.repeat(~kept[i], 16)[:100])
+        if not drop.any():
+            continue
+        fk, vv = phi(t[1][drop]), t[2][drop]
+        fq = phi(t[0][rows])
+        ol = (fq @ (fk.T @ vv)) / (fq @ fk.sum(dim=0))[:, None]
+        total = total + (ol * torch.from_numpy(g[rows])).sum()
+    total.backward()
+    for a, b in zip(grads, t):
+        np.testing.assert_allclose(a, b.grad.numpy(), rtol=0, atol=1e-12)
+
+
+def test_sparse_linear_backward_is_the_sum_of_the_two():
+    q, k, v, do, kept = _bwd_case(73, N=40, d=4)
+    grads = O.sparse_linear_attention_backward_head(q, k, v, kept, 16, 16, 0.5, 0.25, do)
+    f = lambda q_, k_, v_: float((do * O.sparse_linear_attention_head(q_, k_, v_, kept, 16, 16,
+                                                                       0.5, 0.25)).sum())
+    h = 1e-6
+    for which, g_an in enumerate(grads):
+        x = (q, k, v)[which]
+        num = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            xp, xm = [a.copy() for a in (q, k, v)], [a.copy() for a in (q, k, v)]
+            xp[which][idx] += h
+            xm[which][idx] -= h
+            num[idx] = (f(*xp) - f(*xm)) / (2 * h)
+        np.testing.assert_allclose(g_an, num, rtol=0, atol=2e-8, err_msg="qkv"[which])
+    # handing the exact O changes nothing
+    o = O.sparse_linear_attention_head(q, k, v, kept, 16, 16, 0.5, 0.25)
+    again = O.sparse_linear_attention_backward_head(q, k, v, kept, 16, 16, 0.5, 0.25, do, o=o)
+    for a, b in zip(grads, again):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-13)
+
+
+def test_mix_backward_matches_central_differences():
+    q, k, v, do, kept = _bwd_case(74, N=40, d=4)
+    alpha = np.array([0.2, 0.7, 1.0, 0.45], np.float32)
+    grads = O.sla2_mix_attention_backward_head(q, k, v, kept, 16, 16, 0.5, alpha, do)
+    f = lambda q_, k_, v_: float((do * O.sla2_mix_attention_head(q_, k_, v_, kept, 16, 16, 0.5,
+                                                                 alpha)).sum())
+    h = 1e-6
+    for which, g_an in enumerate(grads):
+        x = (q, k, v)[which]
+        num = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            xp, xm = [a.copy() for a in (q, k, v)], [a.copy() for a in (q, k, v)]
+            xp[which][idx] += h
+            xm[which][idx] -= h
+            num[idx] = (f(*xp) - f(*xm)) / (2 * h)
+        np.testing.assert_allclose(g_an, num, rtol=0, atol=2e-8, err_msg="qkv"[which])
+
+
+def test_linear_backward_sampled_equals_the_full_one():
+    q, k, v, g, kept = _bwd_case(75, N=150, d=8, bq=32, bk=16)
+    full = O.linear_branch_backward_head(q, k, v, kept, 32, 16, g)
+    part = O.linear_branch_backward_sampled(q, k, v, kept, 32, 16, g, q_blocks=[0, 3],
+                                            k_blocks=[2, 9])
+    rows = np.r_[0:32, 96:128]
+    keys = np.r_[32:48, 144:150]
+    np.testing.assert_allclose(part[0][rows], full[0][rows], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(part[1][keys], full[1][keys], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(part[2][keys], full[2][keys], rtol=0, atol=1e-13)
