@@ -24,7 +24,8 @@ EXPORTS = ("sparge_mask_workspace_bytes", "sparge_mask_predict",
            "sparge_attn_workspace_bytes", "sparge_attn_fwd", "sparge_attn_pack",
            "sparge_attn_fwd_packed", "sparse_linear_workspace_bytes", "sparse_linear_attn_fwd",
            "sla2_mix_attn_fwd", "sparge_attn_fwd_lse", "sparge_attn_bwd_workspace_bytes",
-           "sparge_attn_bwd", "sparge_last_error")
+           "sparge_attn_bwd", "sparse_linear_bwd_workspace_bytes", "sparse_linear_attn_bwd",
+           "sla2_mix_attn_bwd", "sparge_last_error")
 
 _lib = None
 
@@ -65,6 +66,11 @@ def lib() -> ctypes.CDLL:
         L.sparge_attn_bwd_workspace_bytes.restype = c_size
         L.sparge_attn_bwd.argtypes = [vp] * 8 + [c_int] * 6 + [c_float] + [vp] * 4 + [c_size, vp]
         L.sparge_attn_bwd.restype = c_int
+        L.sparse_linear_bwd_workspace_bytes.argtypes = [c_int] * 4
+        L.sparse_linear_bwd_workspace_bytes.restype = c_size
+        for f in (L.sparse_linear_attn_bwd, L.sla2_mix_attn_bwd):
+            f.argtypes = [vp] * 9 + [c_int] * 6 + [c_float, c_float] + [vp] * 4 + [c_size, vp]
+            f.restype = c_int
         L.sparge_attn_pack.argtypes = [vp] + [c_int] * 4 + [vp, c_size, vp]
         L.sparge_attn_pack.restype = c_int
         L.sparge_attn_fwd_packed.argtypes = [vp] * 4 + [c_int] * 6 + [c_float, vp, vp, c_size, vp]
@@ -72,7 +78,7 @@ def lib() -> ctypes.CDLL:
         L.sparse_linear_workspace_bytes.argtypes = [c_int] * 4
         L.sparse_linear_workspace_bytes.restype = c_size
         for f in (L.sparse_linear_attn_fwd, L.sla2_mix_attn_fwd):
-            f.argtypes = [vp] * 6 + [c_int] * 6 + [c_float, c_float, vp, vp, c_size, vp]
+            f.argtypes = [vp] * 6 + [c_int] * 6 + [c_float, c_float, vp, vp, vp, c_size, vp]
             f.restype = c_int
         L.sparge_last_error.argtypes = []
         L.sparge_last_error.restype = ctypes.c_char_p
@@ -237,6 +243,47 @@ def sparge_attn_bwd(q, k, v, o, d_o, lse, kv_idx, kv_cnt, block_q=128, block_k=6
     return dq, dk, dv
 
 
+def linear_bwd_workspace_bytes(B, H, N, d) -> int:
+    return lib().sparse_linear_bwd_workspace_bytes(B, H, N, d)
+
+
+def _linear_bwd(fn, q, k, v, o, d_o, lse, kv_idx, kv_cnt, alpha, block_q, block_k, scale,
+                drop_below, out, workspace):
+    B, H, N, d = _qkv(q, k, v, o, d_o)
+    if lse.dtype != torch.float32 or not lse.is_cuda or tuple(lse.shape) != (B, H, N):
+        raise ValueError("lse must be a float32 GPU tensor of shape [B, H, N]")
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3)) if out is None else out
+    if scale is None:
+        scale = default_scale(d)
+    if workspace is None:
+        workspace = torch.empty(max(linear_bwd_workspace_bytes(B, H, N, d), 16),
+                                dtype=torch.uint8, device=q.device)
+    _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse), _ptr(kv_idx),
+              _ptr(kv_cnt), _ptr(alpha), B, H, N, d, block_q, block_k, scale, drop_below,
+              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), _stream(q)))
+    return dq, dk, dv
+
+
+def sparse_linear_attn_bwd(q, k, v, o, d_o, lse, kv_idx, kv_cnt, alpha, block_q=128, block_k=64,
+                           scale=None, drop_below=0.0, out=None, workspace=None):
+    """dQ, dK, dV of O = O_s + alpha[h] O_l (lse from sparse_linear_attn_fwd)."""
+    H = q.shape[1]
+    if alpha.dtype != torch.float32 or not alpha.is_cuda or alpha.numel() != H:
+        raise ValueError("alpha must be a float32 GPU tensor of H values")
+    return _linear_bwd(lib().sparse_linear_attn_bwd, q, k, v, o, d_o, lse, kv_idx, kv_cnt,
+                       alpha.contiguous(), block_q, block_k, scale, drop_below, out, workspace)
+
+
+def sla2_mix_attn_bwd(q, k, v, o, d_o, lse, kv_idx, kv_cnt, alpha, block_q=128, block_k=64,
+                      scale=None, drop_below=0.0, out=None, workspace=None):
+    """dQ, dK, dV of the SLA2 mix (lse from sla2_mix_attn_fwd); alpha float32 [H, d]."""
+    H, d = q.shape[1], q.shape[3]
+    if alpha.dtype != torch.float32 or not alpha.is_cuda or tuple(alpha.shape) != (H, d):
+        raise ValueError("alpha must be a float32 GPU tensor of shape [H, d]")
+    return _linear_bwd(lib().sla2_mix_attn_bwd, q, k, v, o, d_o, lse, kv_idx, kv_cnt,
+                       alpha.contiguous(), block_q, block_k, scale, drop_below, out, workspace)
+
+
 def sparge_attn_pack(v, workspace=None):
     """Pack V for sparge_attn_fwd_packed; returns the workspace holding it."""
     B, H, N, d = _qkv(v)
@@ -266,37 +313,39 @@ def linear_workspace_bytes(B, H, N, d) -> int:
 
 
 def _linear(fn, q, k, v, kv_idx, kv_cnt, alpha, block_q, block_k, scale, drop_below,
-            workspace, out):
+            workspace, out, lse=None):
     B, H, N, d = _qkv(q, k, v)
     o = torch.empty_like(q) if out is None else out
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N)):
+        raise ValueError("lse must be a float32 GPU tensor of shape [B, H, N]")
     if scale is None:
         scale = default_scale(d)
     ws_bytes = linear_workspace_bytes(B, H, N, d)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
     _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_idx), _ptr(kv_cnt), _ptr(alpha), B, H, N, d,
-              block_q, block_k, scale, drop_below, _ptr(o), _ptr(workspace), workspace.numel(),
-              _stream(q)))
+              block_q, block_k, scale, drop_below, _ptr(o), None if lse is None else _ptr(lse),
+              _ptr(workspace), workspace.numel(), _stream(q)))
     return o
 
 
 def sparse_linear_attn_fwd(q, k, v, kv_idx, kv_cnt, alpha, block_q=128, block_k=64,
-                           scale=None, drop_below=0.0, workspace=None, out=None):
+                           scale=None, drop_below=0.0, workspace=None, out=None, lse=None):
     """Sparse attention plus alpha[h] times elu+1 linear attention over dropped blocks;
     heads with |alpha[h]| <= drop_below skip the linear branch."""
     H = q.shape[1]
     if alpha.dtype != torch.float32 or not alpha.is_cuda or alpha.numel() != H:
         raise ValueError("alpha must be a float32 GPU tensor of H values")
     return _linear(lib().sparse_linear_attn_fwd, q, k, v, kv_idx, kv_cnt, alpha.contiguous(),
-                   block_q, block_k, scale, drop_below, workspace, out)
+                   block_q, block_k, scale, drop_below, workspace, out, lse)
 
 
 def sla2_mix_attn_fwd(q, k, v, kv_idx, kv_cnt, alpha, block_q=128, block_k=64, scale=None,
-                      drop_below=0.0, workspace=None, out=None):
+                      drop_below=0.0, workspace=None, out=None, lse=None):
     """SLA2 mix alpha[h][c] O_s + (1 - alpha[h][c]) O_l; alpha float32 [H, d] on the GPU.
     Heads with every |1 - alpha[h][c]| <= drop_below skip the linear branch."""
     H, d = q.shape[1], q.shape[3]
     if alpha.dtype != torch.float32 or not alpha.is_cuda or tuple(alpha.shape) != (H, d):
         raise ValueError("alpha must be a float32 GPU tensor of shape [H, d]")
     return _linear(lib().sla2_mix_attn_fwd, q, k, v, kv_idx, kv_cnt, alpha.contiguous(),
-                   block_q, block_k, scale, drop_below, workspace, out)
+                   block_q, block_k, scale, drop_below, workspace, out, lse)

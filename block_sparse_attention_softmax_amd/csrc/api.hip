@@ -283,20 +283,31 @@ size_t sparge_attn_bwd_workspace_bytes(int B, int H, int N, int d, int block_q, 
   return sparge::bwd_workspace_bytes(B, H, N, d, block_q);
 }
 
-int sparge_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* d_o,
-                    const float* lse, const int32_t* kv_idx, const int32_t* kv_cnt, int B,
-                    int H, int N, int d, int block_q, int block_k, float scale, void* dq,
-                    void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// the backward, plain (alpha == nullptr) or with the linear branch
+int bwd_impl(const char* name, int mode, const void* q, const void* k, const void* v,
+             const void* o, const void* d_o, const float* lse, const int32_t* kv_idx,
+             const int32_t* kv_cnt, const float* alpha, int B, int H, int N, int d, int block_q,
+             int block_k, float scale, float drop_below, void* dq, void* dk, void* dv,
+             void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error.clear();
   int rc = check_attn_args(q, k, v, kv_idx, kv_cnt, B, H, N, d, block_q, block_k, scale, o);
   if (rc != SPARGE_OK) return rc;
-  if (!d_o || !lse || !dq || !dk || !dv || !workspace)
+  const bool linear = mode >= 0;
+  if (!d_o || !lse || !dq || !dk || !dv || !workspace || (linear && !alpha))
     return fail(SPARGE_ERR_INVALID_ARG, "null pointer argument");
   if (!aligned(d_o, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
-      !aligned(lse, 4) || !aligned(workspace, 16))
-    return fail(SPARGE_ERR_INVALID_ARG, "d_o, dq, dk, dv, lse or workspace misaligned");
-  if (workspace_bytes < sparge::bwd_workspace_bytes(B, H, N, d, block_q))
+      !aligned(lse, 4) || !aligned(workspace, 16) ||
+      (linear && !aligned(alpha, mode == sparge::kLinMix ? 16 : 4)))
+    return fail(SPARGE_ERR_INVALID_ARG, "d_o, dq, dk, dv, lse, alpha or workspace misaligned");
+  if (workspace_bytes < sparge::bwd_workspace_bytes(B, H, N, d, block_q, linear))
     return fail(SPARGE_ERR_INVALID_ARG, "workspace too small");
+  if (linear && block_q != d)
+    return fail(SPARGE_ERR_UNSUPPORTED, "the linear branch is built for block_q == d (64 or 128)");
+  if (linear && ceil_div(N, block_k) > kMaxKeyBlocks)
+    return fail(SPARGE_ERR_UNSUPPORTED, "the linear backward supports at most 4096 key blocks");
   sparge::BwdLaunch a{};
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -314,9 +325,54 @@ int sparge_attn_bwd(const void* q, const void* k, const void* v, const void* o, 
   a.n_k = ceil_div(N, block_k);
   a.scale = scale;
   a.workspace = static_cast<unsigned char*>(workspace);
+  a.alpha = linear ? alpha : nullptr;
+  a.lin_mode = linear ? mode : 0;
+  a.drop_below = drop_below;
   const hipError_t e = sparge::launch_bwd(a, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "sparge_attn_bwd launch");
+  if (e != hipSuccess) return hip_fail(e, name);
   return SPARGE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int sparge_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* d_o,
+                    const float* lse, const int32_t* kv_idx, const int32_t* kv_cnt, int B,
+                    int H, int N, int d, int block_q, int block_k, float scale, void* dq,
+                    void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl("sparge_attn_bwd launch", -1, q, k, v, o, d_o, lse, kv_idx, kv_cnt, nullptr, B,
+                  H, N, d, block_q, block_k, scale, 0.0f, dq, dk, dv, workspace,
+                  workspace_bytes, stream);
+}
+
+size_t sparse_linear_bwd_workspace_bytes(int B, int H, int N, int d) {
+  const std::string saved = g_last_error;
+  const int rc = check_shape(B, H, N, d, d == 64 ? 64 : 128, 64);
+  g_last_error = saved;
+  if (rc != SPARGE_OK || ceil_div(N, 64) > kMaxKeyBlocks) return 0;
+  return sparge::bwd_workspace_bytes(B, H, N, d, d, true);
+}
+
+int sparse_linear_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                           const void* d_o, const float* lse, const int32_t* kv_idx,
+                           const int32_t* kv_cnt, const float* alpha, int B, int H, int N,
+                           int d, int block_q, int block_k, float scale, float drop_below,
+                           void* dq, void* dk, void* dv, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return bwd_impl("sparse_linear_attn_bwd launch", sparge::kLinAdd, q, k, v, o, d_o, lse, kv_idx,
+                  kv_cnt, alpha, B, H, N, d, block_q, block_k, scale, drop_below, dq, dk, dv,
+                  workspace, workspace_bytes, stream);
+}
+
+int sla2_mix_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                      const void* d_o, const float* lse, const int32_t* kv_idx,
+                      const int32_t* kv_cnt, const float* alpha, int B, int H, int N, int d,
+                      int block_q, int block_k, float scale, float drop_below, void* dq,
+                      void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  return bwd_impl("sla2_mix_attn_bwd launch", sparge::kLinMix, q, k, v, o, d_o, lse, kv_idx,
+                  kv_cnt, alpha, B, H, N, d, block_q, block_k, scale, drop_below, dq, dk, dv,
+                  workspace, workspace_bytes, stream);
 }
 
 int sparge_attn_pack(const void* v, int B, int H, int N, int d, void* workspace,
@@ -368,14 +424,15 @@ namespace {
 int linear_impl(const char* name, int mode, const void* q, const void* k, const void* v,
                 const int32_t* kv_idx, const int32_t* kv_cnt, const float* alpha, int B, int H,
                 int N, int d, int block_q, int block_k, float scale, float drop_below, void* o,
-                void* workspace, size_t workspace_bytes, void* stream) {
+                float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error.clear();
   int rc = check_attn_args(q, k, v, kv_idx, kv_cnt, B, H, N, d, block_q, block_k, scale, o);
   if (rc != SPARGE_OK) return rc;
   if (!alpha || !workspace) return fail(SPARGE_ERR_INVALID_ARG, "null pointer argument");
   // the mix reads alpha[h][4c .. 4c+3] as one 16-byte load
-  if (!aligned(alpha, mode == sparge::kLinMix ? 16 : 4) || !aligned(workspace, 16))
-    return fail(SPARGE_ERR_INVALID_ARG, "alpha / workspace misaligned");
+  if (!aligned(alpha, mode == sparge::kLinMix ? 16 : 4) || !aligned(workspace, 16) ||
+      !aligned(lse, 4))
+    return fail(SPARGE_ERR_INVALID_ARG, "alpha / workspace / lse misaligned");
   if (workspace_bytes < sparge::linear_workspace_bytes(B, H, N, d))
     return fail(SPARGE_ERR_INVALID_ARG, "workspace too small");
   if (block_q != d)
@@ -394,6 +451,7 @@ int linear_impl(const char* name, int mode, const void* q, const void* k, const 
   a.alpha = alpha;
   a.lin_mode = mode;
   a.drop_below = drop_below;
+  a.lse = lse;
   const size_t BH = (size_t)B * H, packed = sparge::attn_workspace_bytes(B, H, N, d);
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   a.vt = reinterpret_cast<uint16_t*>(ws);
@@ -417,19 +475,19 @@ extern "C" {
 int sparse_linear_attn_fwd(const void* q, const void* k, const void* v,
                            const int32_t* kv_idx, const int32_t* kv_cnt, const float* alpha,
                            int B, int H, int N, int d, int block_q, int block_k, float scale,
-                           float drop_below, void* o, void* workspace, size_t workspace_bytes,
-                           void* stream) {
+                           float drop_below, void* o, float* lse, void* workspace,
+                           size_t workspace_bytes, void* stream) {
   return linear_impl("sparse_linear_attn_fwd launch", sparge::kLinAdd, q, k, v, kv_idx, kv_cnt,
-                     alpha, B, H, N, d, block_q, block_k, scale, drop_below, o, workspace,
+                     alpha, B, H, N, d, block_q, block_k, scale, drop_below, o, lse, workspace,
                      workspace_bytes, stream);
 }
 
 int sla2_mix_attn_fwd(const void* q, const void* k, const void* v, const int32_t* kv_idx,
                       const int32_t* kv_cnt, const float* alpha, int B, int H, int N, int d,
                       int block_q, int block_k, float scale, float drop_below, void* o,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+                      float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   return linear_impl("sla2_mix_attn_fwd launch", sparge::kLinMix, q, k, v, kv_idx, kv_cnt,
-                     alpha, B, H, N, d, block_q, block_k, scale, drop_below, o, workspace,
+                     alpha, B, H, N, d, block_q, block_k, scale, drop_below, o, lse, workspace,
                      workspace_bytes, stream);
 }
 

@@ -22,6 +22,7 @@
 // products of earlier blocks.
 #include "internal.h"
 #include "tiles.h"
+#include "linear_common.h"
 
 #include <type_traits>
 
@@ -32,124 +33,6 @@ namespace {
 // raises it by more than 2^8 in the exponent; until then P <= 2^8, which
 // float32 sums and bf16 products carry without loss of relative precision.
 constexpr float kRescaleLog2 = 8.0f;
-
-// ------------------------------------------------- linear-branch totals
-// Split-K partials of H_tot = sum_u phi(K_u)^T V_u (d x d, row = phi index)
-// and z_tot = sum_u phi(K_u) from the packed tiles: workgroup (split, bh)
-// covers blocks j = split, split + kLinSplit, ...; D/32 waves, wave w owns
-// rows 32w..32w+31. Operands come straight from the packed global tiles.
-template <int D>
-__global__ __launch_bounds__(D * 2) void linear_total_kernel(const uint16_t* __restrict__ phikt,
-                                                             const uint16_t* __restrict__ vt,
-                                                             float* __restrict__ part_h,
-                                                             float* __restrict__ part_z,
-                                                             int n_k,
-                                                             const int32_t* __restrict__ lin_on,
-                                                             int H) {
-  constexpr int DT = D / 32;
-  const int split = blockIdx.x, bh = blockIdx.y;
-  if (!lin_on[bh % H]) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int h2 = lane >> 5, l32 = lane & 31;
-  floatx16 hacc[DT];
-#pragma unroll
-  for (int i = 0; i < DT; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) hacc[i][r] = 0.0f;
-  float zp = 0.0f;
-  const size_t tile = (size_t)D * BK;
-  for (int j = split; j < n_k; j += kLinSplit) {
-    const uint16_t* pk = phikt + ((size_t)bh * n_k + j) * tile + (size_t)(32 * wave + l32) * BK;
-    const uint16_t* vv = vt + ((size_t)bh * n_k + j) * tile + (size_t)l32 * BK;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(pk + 16 * g + 8 * h2);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) zp += (float)a[e];
-#pragma unroll
-      for (int i = 0; i < DT; ++i) {
-        const bf16x8 b = *reinterpret_cast<const bf16x8*>(vv + (size_t)32 * i * BK + 16 * g + 8 * h2);
-        hacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, hacc[i], 0, 0, 0);
-      }
-    }
-  }
-  float* ph = part_h + ((size_t)bh * kLinSplit + split) * D * D;
-#pragma unroll
-  for (int i = 0; i < DT; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int a = 32 * wave + 8 * (r >> 2) + 4 * h2 + (r & 3);
-      ph[(size_t)a * D + 32 * i + l32] = hacc[i][r];
-    }
-  zp += __shfl_xor(zp, 32);
-  if (h2 == 0) part_z[((size_t)bh * kLinSplit + split) * D + 32 * wave + l32] = zp;
-}
-
-// H_tot, z_tot = sums of the kLinSplit partials, in split order.
-template <int D>
-__global__ __launch_bounds__(256) void linear_reduce_kernel(const float* __restrict__ part_h,
-                                                            const float* __restrict__ part_z,
-                                                            float* __restrict__ lin_h,
-                                                            float* __restrict__ lin_z,
-                                                            const int32_t* __restrict__ lin_on,
-                                                            int H) {
-  const int bh = blockIdx.x;
-  if (!lin_on[bh % H]) return;
-  for (int e = threadIdx.x; e < D * D + D; e += 256) {
-    float acc = 0.0f;
-    if (e < D * D) {
-      for (int sp = 0; sp < kLinSplit; ++sp) acc += part_h[((size_t)bh * kLinSplit + sp) * D * D + e];
-      lin_h[(size_t)bh * D * D + e] = acc;
-    } else {
-      const int a = e - D * D;
-      for (int sp = 0; sp < kLinSplit; ++sp) acc += part_z[((size_t)bh * kLinSplit + sp) * D + a];
-      lin_z[(size_t)bh * D + a] = acc;
-    }
-  }
-}
-
-// lin_on[h] = 1 unless every weight that head h's linear branch is multiplied
-// by (alpha[h]; 1 - alpha[h][c] in the mix, float32) has magnitude <= the
-// threshold: post-tuning branch dropping (SALAD page). A NaN weight keeps it.
-// Then the (batch, head) pairs b*H + h in increasing order, split by the flag:
-// lists[0] = #on, lists[1] = #off, lists[2 ..] those on, lists[2 + B*H ..]
-// those off. One workgroup; wave w decides heads w, w + 16, ...
-constexpr int kFlagThreads = 1024;
-__global__ __launch_bounds__(kFlagThreads) void linear_flags_kernel(
-    const float* __restrict__ alpha, int mode, int D, float drop_below, int B, int H,
-    int32_t* __restrict__ lin_on, int32_t* __restrict__ lists) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int h = wave; h < H; h += kFlagThreads / 64) {
-    bool keep = false;
-    if (mode == kLinAdd) {
-      keep = lane == 0 && !(fabsf(alpha[h]) <= drop_below);
-    } else {
-      for (int c = lane; c < D; c += 64)
-        keep = keep || !(fabsf(1.0f - alpha[(size_t)h * D + c]) <= drop_below);
-    }
-    keep = __any(keep);
-    if (lane == 0) lin_on[h] = keep ? 1 : 0;
-  }
-  __syncthreads();
-  if (wave != 0) return;
-  const int BH = B * H;
-  int n_on = 0, n_off = 0;
-  for (int base = 0; base < BH; base += 64) {
-    const int bh = base + lane;
-    const bool valid = bh < BH;
-    const bool on = valid && lin_on[bh % H] != 0, off = valid && !on;
-    const uint64_t m_on = __ballot(on), m_off = __ballot(off);
-    const uint64_t below = (uint64_t(1) << lane) - 1;
-    if (on) lists[2 + n_on + __popcll(m_on & below)] = bh;
-    if (off) lists[2 + BH + n_off + __popcll(m_off & below)] = bh;
-    n_on += __popcll(m_on);
-    n_off += __popcll(m_off);
-  }
-  if (lane == 0) {
-    lists[0] = n_on;
-    lists[1] = n_off;
-  }
-}
 
 // ------------------------------------------------------ attention kernel
 // Software-pipelined over the listed blocks: the S^T product of block it+1
@@ -184,7 +67,7 @@ __global__ __launch_bounds__(kFlagThreads) void linear_flags_kernel(
 // SEL (always with LIN) adds the head selection and the alpha scaling of the
 // epilogue; the plain kernel without it is compiled without either. LSE
 // (plain kernel only) also stores every row's log-sum-exp of its kept scores,
-// ln(sum_u exp(scale q.k_u)), for the backward.
+// ln(sum_u exp(scale q.k_u)) of the sparse part, for the backward.
 template <int D, int BQ, bool LIN, bool SEL = LIN, bool LSE = false>
 __global__ __launch_bounds__(BQ * (LIN ? 4 : 2), (LIN || (D == 128 && BQ == 64)) ? 1 : 2) void sparse_attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -524,7 +407,7 @@ __global__ __launch_bounds__(BQ * (LIN ? 4 : 2), (LIN || (D == 128 && BQ == 64))
   const float ltot = pair_sum(lsum);  // (H waves: z_kept entry 32*wave + l32)
   const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
   if constexpr (LSE) {  // sum_u exp(scale s_u) = 2^(m c) * ltot; -inf for an empty row
-    if (h2 == 0 && qrow < N)
+    if (!hwave && h2 == 0 && qrow < N)
       lse[(size_t)bh * N + qrow] =
           ltot > 0.0f ? (m * c + log2f(ltot)) * 0.6931471805599453f : -INFINITY;
   }
@@ -680,21 +563,36 @@ hipError_t launch_sparse(const AttnLaunch& a, hipStream_t s, AttnPhase phase) {
     }
   }
   if (phase != kPackOnly) {
-    if (!LIN && a.lse)
+    if constexpr (LIN) {
+      // heads whose branch is on, then (plain kernel, times alpha in the mix) the others
+      const float* mix_alpha = a.lin_mode == kLinMix ? a.alpha : nullptr;
+      if (a.lse) {
+        hipLaunchKernelGGL((sparse_attn_fwd_kernel<D, BQ, true, true, true>), dim3(total),
+                           dim3(BQ * 4), 0, s, a.q, a.k, a.vt, a.idx, a.cnt, a.o, a.H, a.N, a.n_q,
+                           a.n_k, total, c, a.alpha, a.phikt, a.lin_h, a.lin_z, a.lin_lists,
+                           a.lin_mode, a.lse);
+        hipLaunchKernelGGL((sparse_attn_fwd_kernel<D, BQ, false, true, true>), dim3(total),
+                           dim3(BQ * 2), 0, s, a.q, a.k, a.vt, a.idx, a.cnt, a.o, a.H, a.N, a.n_q,
+                           a.n_k, total, c, mix_alpha, nullptr, nullptr, nullptr, a.lin_lists,
+                           a.lin_mode, a.lse);
+      } else {
+        hipLaunchKernelGGL((sparse_attn_fwd_kernel<D, BQ, true>), dim3(total), dim3(BQ * 4), 0, s,
+                           a.q, a.k, a.vt, a.idx, a.cnt, a.o, a.H, a.N, a.n_q, a.n_k, total, c,
+                           a.alpha, a.phikt, a.lin_h, a.lin_z, a.lin_lists, a.lin_mode, nullptr);
+        hipLaunchKernelGGL((sparse_attn_fwd_kernel<D, BQ, false, true>), dim3(total), dim3(BQ * 2),
+                           0, s, a.q, a.k, a.vt, a.idx, a.cnt, a.o, a.H, a.N, a.n_q, a.n_k, total,
+                           c, mix_alpha, nullptr, nullptr, nullptr, a.lin_lists, a.lin_mode,
+                           nullptr);
+      }
+    } else if (a.lse) {
       hipLaunchKernelGGL((sparse_attn_fwd_kernel<D, BQ, false, false, true>), dim3(total),
                          dim3(BQ * 2), 0, s, a.q, a.k, a.vt, a.idx, a.cnt, a.o, a.H, a.N, a.n_q,
                          a.n_k, total, c, nullptr, nullptr, nullptr, nullptr, nullptr, 0, a.lse);
-    else
-      hipLaunchKernelGGL((sparse_attn_fwd_kernel<D, BQ, LIN>), dim3(total), dim3(BQ * (LIN ? 4 : 2)), 0, s,
+    } else {
+      hipLaunchKernelGGL((sparse_attn_fwd_kernel<D, BQ, false>), dim3(total), dim3(BQ * 2), 0, s,
                          a.q, a.k, a.vt, a.idx, a.cnt, a.o, a.H, a.N, a.n_q, a.n_k, total, c,
-                         a.alpha, a.phikt, a.lin_h, a.lin_z, LIN ? a.lin_lists : nullptr,
-                         a.lin_mode, nullptr);
-    // heads whose branch is dropped: plain sparse attention (times alpha in the mix)
-    if constexpr (LIN)
-      hipLaunchKernelGGL((sparse_attn_fwd_kernel<D, BQ, false, true>), dim3(total), dim3(BQ * 2), 0, s,
-                         a.q, a.k, a.vt, a.idx, a.cnt, a.o, a.H, a.N, a.n_q, a.n_k, total, c,
-                         a.lin_mode == kLinMix ? a.alpha : nullptr, nullptr, nullptr, nullptr,
-                         a.lin_lists, a.lin_mode, nullptr);
+                         nullptr, nullptr, nullptr, nullptr, nullptr, 0, nullptr);
+    }
   }
   return hipGetLastError();
 }

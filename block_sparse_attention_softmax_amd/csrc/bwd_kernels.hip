@@ -29,6 +29,7 @@
 #include <algorithm>
 
 #include "internal.h"
+#include "linear_common.h"
 #include "tiles.h"
 
 namespace sparge {
@@ -207,7 +208,8 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void sparse_attn_bwd_dkdv_ke
     const float* __restrict__ lse2, const float* __restrict__ drow,
     const int32_t* __restrict__ coloff, const int32_t* __restrict__ collist,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int N, int n_q, int n_k, int n64,
-    int total, float c, float scale) {
+    int total, float c, float scale, const float* __restrict__ lin_dk,
+    const float* __restrict__ lin_dv) {
   using T = Tile<D>;
   using ST = DkdvStage<D>;
   constexpr int DT = D / 32, KSTEPS = D / 16, SUB = BQ / 64;
@@ -387,6 +389,12 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void sparse_attn_bwd_dkdv_ke
           yv[e2] = dva[ii][r] + red[(((kh * 2 + 1) * DT + ii) * 16 + r) * 64 + lane];
         }
         const int d0 = 32 * ii + 8 * gg + 4 * h2;
+        if (lin_dk) {  // the linear branch's share, float32
+          const float4 lk = *reinterpret_cast<const float4*>(lin_dk + head + (size_t)key * D + d0);
+          const float4 lv = *reinterpret_cast<const float4*>(lin_dv + head + (size_t)key * D + d0);
+          yk[0] += lk.x; yk[1] += lk.y; yk[2] += lk.z; yk[3] += lk.w;
+          yv[0] += lv.x; yv[1] += lv.y; yv[2] += lv.z; yv[3] += lv.w;
+        }
         uint2 pk;
         pk.x = pack2_bf16(yk[0], yk[1]);
         pk.y = pack2_bf16(yk[2], yk[3]);
@@ -413,7 +421,7 @@ __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void sparse
     const uint16_t* __restrict__ kt, const float* __restrict__ lse2,
     const float* __restrict__ drow, const int32_t* __restrict__ kv_idx,
     const int32_t* __restrict__ kv_cnt, uint16_t* __restrict__ dq, int N, int n_q, int n_k,
-    int total, float c, float scale) {
+    int total, float c, float scale, const float* __restrict__ lin_dq) {
   using T = Tile<D>;
   constexpr int DT = D / 32, KSTEPS = D / 16, NT = BQ * 2;
   constexpr int KU = 64 * T::KCPR / NT, VU = D * T::VCPR / NT;  // 16-byte copies per thread
@@ -545,12 +553,465 @@ __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void sparse
 #pragma unroll
       for (int gg = 0; gg < 4; ++gg) {
         const int d0 = 32 * ii + 8 * gg + 4 * h2;
+        float y[4];
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) y[e2] = scale * acc[ii][4 * gg + e2];
+        if (lin_dq) {  // the linear branch's share, float32
+          const float4 l = *reinterpret_cast<const float4*>(lin_dq + head + (size_t)qrow * D + d0);
+          y[0] += l.x; y[1] += l.y; y[2] += l.z; y[3] += l.w;
+        }
         uint2 pk;
-        pk.x = pack2_bf16(scale * acc[ii][4 * gg + 0], scale * acc[ii][4 * gg + 1]);
-        pk.y = pack2_bf16(scale * acc[ii][4 * gg + 2], scale * acc[ii][4 * gg + 3]);
+        pk.x = pack2_bf16(y[0], y[1]);
+        pk.y = pack2_bf16(y[2], y[3]);
         *reinterpret_cast<uint2*>(orow + d0) = pk;
       }
   }
+}
+
+// ------------------------------------------------ linear branch backward
+// The linear branch O_l,t = phi(Q_t) H_D / (phi(Q_t) . z_D) of a query block
+// with dropped keys D, H_D = sum_{u in D} phi(K_u)^T V_u, z_D = sum phi(K_u),
+// receives G_t = w (*) dO_t (w = alpha[h], or 1 - alpha[h][c] in the mix):
+//   dnum = G / den,  dden = -(G . O_l) / den,  dphi(Q_t) = H_D dnum + z_D dden,
+//   dH_D = sum_t phi(Q_t)^T dnum_t,  dz_D = sum_t phi(Q_t) dden_t,
+// and each dropped key u gets dphi(K_u) += dH_D V_u + dz_D, dV_u += phi(K_u) dH_D.
+// The sparse part's D_t = dO_t . O_s,t equals dO_t . O_t - G_t . O_l,t, so the
+// row kernel subtracts G . O_l from D.
+constexpr int kMaxLinKeyBlocks = 4096;  // capacity of the per-row kept bitmap
+
+// Per (b, h, query block of D rows), 4 waves. First H_D, z_D on the matrix
+// cores from the packed phi(K)^T and V^T tiles of whichever list is shorter:
+// H_tot minus the listed blocks (as the forward forms it), or the sum over the
+// blocks not listed. Then, 32 rows at a time in float32 on the vector units:
+// O_l, dnum, dden, the correction of D, dQ_l = dphi(Q) phi'(Q) and the block's
+// dH_D, dz_D (written for the key kernel). Heads whose branch is off and
+// blocks that dropped nothing write zeros.
+template <int D>
+__global__ __launch_bounds__(256, 1) void linear_bwd_rows_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ dO,
+    const uint16_t* __restrict__ phikt, const uint16_t* __restrict__ vt,
+    const float* __restrict__ lin_h, const float* __restrict__ lin_z,
+    const int32_t* __restrict__ kv_idx, const int32_t* __restrict__ kv_cnt,
+    const int32_t* __restrict__ lin_on, const float* __restrict__ alpha, int mode,
+    float* __restrict__ dql, float* __restrict__ dHq, float* __restrict__ dzq,
+    float* __restrict__ drow, int H, int N, int n_q, int n_k, int NP, int total) {
+  constexpr int DT = D / 32, HP = D + 4, CH = 32, NTILE = DT * DT, TPW = (NTILE + 3) / 4;
+  constexpr int AT = D / 16, CPT = D / 8;  // dH entries per thread per side; channels per thread
+  __shared__ __align__(16) float Hs[D * HP];
+  __shared__ __align__(16) float zs[D];
+  __shared__ __align__(16) float fq[CH * D];
+  __shared__ __align__(16) float dn[CH * D];
+  __shared__ float dden_s[CH];
+  __shared__ uint32_t kept_bits[kMaxLinKeyBlocks / 32];
+
+  const int tile = xcd_remap(blockIdx.x, total);
+  const int bh = tile / n_q, qi = tile % n_q, h = bh % H;
+  const int th = threadIdx.x, lane = th & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(th >> 6);
+  const int h2 = lane >> 5, l32 = lane & 31;
+  const size_t head = (size_t)bh * N * D;
+  const int row0 = qi * D;
+  const int count = min(max(kv_cnt[tile], 0), n_k);
+  const int a0 = (th / 16) * AT, c0 = (th % 16) * AT;
+  float* const dh_out = dHq + ((size_t)bh * n_q + qi) * D * D;
+  float* const dz_out = dzq + ((size_t)bh * n_q + qi) * D;
+
+  if (lin_on[h] == 0 || count >= n_k) {  // no linear gradient from this block
+    for (int e = th; e < CH * (D / CH) * D; e += 256) {
+      const int row = row0 + e / D;
+      if (row < N) dql[head + (size_t)row * D + e % D] = 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < AT; ++i)
+#pragma unroll
+      for (int j = 0; j < AT; ++j) dh_out[(size_t)(a0 + i) * D + c0 + j] = 0.0f;
+    if (th % 16 == 0)
+#pragma unroll
+      for (int i = 0; i < AT; ++i) dz_out[a0 + i] = 0.0f;
+    return;
+  }
+
+  // ---- H_D and z_D
+  const int words = (n_k + 31) / 32;
+  for (int w = th; w < words; w += 256) kept_bits[w] = 0u;
+  __syncthreads();
+  const int32_t* ids = kv_idx + (size_t)tile * n_k;
+  for (int e = th; e < count; e += 256) {
+    const int j = min(max(ids[e], 0), n_k - 1);
+    atomicOr(&kept_bits[j >> 5], 1u << (j & 31));
+  }
+  __syncthreads();
+  const bool use_kept = count <= n_k - count;
+  floatx16 acc[TPW];
+  float zp[TPW];
+#pragma unroll
+  for (int s2 = 0; s2 < TPW; ++s2) {
+    zp[s2] = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[s2][r] = 0.0f;
+  }
+  const size_t vtile = (size_t)D * BK;
+  auto add_block = [&](int j) {
+    const uint16_t* pk = phikt + ((size_t)bh * n_k + j) * vtile;
+    const uint16_t* pv = vt + ((size_t)bh * n_k + j) * vtile;
+#pragma unroll
+    for (int s2 = 0; s2 < TPW; ++s2) {
+      const int t = wave + 4 * s2;
+      if (t < NTILE) {
+        const int ra = t / DT, rc = t % DT;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(pk + (size_t)(32 * ra + l32) * BK + 16 * g + 8 * h2);
+          const bf16x8 b = *reinterpret_cast<const bf16x8*>(pv + (size_t)(32 * rc + l32) * BK + 16 * g + 8 * h2);
+          acc[s2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[s2], 0, 0, 0);
+          if (rc == 0) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) zp[s2] += (float)a[e];
+          }
+        }
+      }
+    }
+  };
+  if (use_kept) {
+    for (int e = 0; e < count; ++e) add_block(min(max(ids[e], 0), n_k - 1));
+  } else {
+    for (int j = 0; j < n_k; ++j)
+      if (!((kept_bits[j >> 5] >> (j & 31)) & 1u)) add_block(j);
+  }
+  const float* Ht = lin_h + (size_t)bh * D * D;
+#pragma unroll
+  for (int s2 = 0; s2 < TPW; ++s2) {
+    const int t = wave + 4 * s2;
+    if (t < NTILE) {
+      const int ra = t / DT, rc = t % DT;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int a = 32 * ra + 8 * (r >> 2) + 4 * h2 + (r & 3), cc = 32 * rc + l32;
+        Hs[a * HP + cc] = use_kept ? Ht[(size_t)a * D + cc] - acc[s2][r] : acc[s2][r];
+      }
+      if (rc == 0) {
+        const float zt = zp[s2] + __shfl_xor(zp[s2], 32);
+        const int a = 32 * ra + l32;
+        if (h2 == 0) zs[a] = use_kept ? lin_z[(size_t)bh * D + a] - zt : zt;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- rows, 32 at a time
+  float dh[AT][AT], dzacc[AT];
+#pragma unroll
+  for (int i = 0; i < AT; ++i) {
+    dzacc[i] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < AT; ++j) dh[i][j] = 0.0f;
+  }
+  const int t = th >> 3, part = th & 7, cb = part * CPT;
+  for (int chk = 0; chk < D / CH; ++chk) {
+    const int r0 = row0 + chk * CH;
+    for (int p = th; p < CH * D / 8; p += 256) {  // phi(Q) of the chunk, zero past N
+      const int tt = p / (D / 8), c8 = (p % (D / 8)) * 8;
+      float f[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+      if (r0 + tt < N) {
+        const uint4 u = *reinterpret_cast<const uint4*>(q + head + (size_t)(r0 + tt) * D + c8);
+        const uint32_t* w = &u.x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          f[2 * e] = elu1(bf16_lo(w[e]));
+          f[2 * e + 1] = elu1(bf16_hi(w[e]));
+        }
+      }
+      *reinterpret_cast<float4*>(fq + tt * D + c8) = make_float4(f[0], f[1], f[2], f[3]);
+      *reinterpret_cast<float4*>(fq + tt * D + c8 + 4) = make_float4(f[4], f[5], f[6], f[7]);
+    }
+    __syncthreads();
+    // num_t = phi(Q_t) H_D for this thread's channels, den_t = phi(Q_t) . z_D
+    float num[CPT];
+#pragma unroll
+    for (int cc = 0; cc < CPT; ++cc) num[cc] = 0.0f;
+    for (int a = 0; a < D; ++a) {
+      const float f = fq[t * D + a];
+#pragma unroll
+      for (int cc = 0; cc < CPT; cc += 4) {
+        const float4 hv = *reinterpret_cast<const float4*>(Hs + a * HP + cb + cc);
+        num[cc] = fmaf(f, hv.x, num[cc]);
+        num[cc + 1] = fmaf(f, hv.y, num[cc + 1]);
+        num[cc + 2] = fmaf(f, hv.z, num[cc + 2]);
+        num[cc + 3] = fmaf(f, hv.w, num[cc + 3]);
+      }
+    }
+    float den = 0.0f;
+    for (int a = cb; a < cb + CPT; ++a) den = fmaf(fq[t * D + a], zs[a], den);
+    den += __shfl_xor(den, 4);
+    den += __shfl_xor(den, 2);
+    den += __shfl_xor(den, 1);
+    const int row = r0 + t;
+    const bool live = row < N;
+    float g[CPT];
+#pragma unroll
+    for (int cc = 0; cc < CPT; ++cc) g[cc] = 0.0f;
+    if (live) {
+      const uint16_t* dp = dO + head + (size_t)row * D + cb;
+#pragma unroll
+      for (int cc = 0; cc < CPT; cc += 8) {
+        const uint4 u = *reinterpret_cast<const uint4*>(dp + cc);
+        const uint32_t* w = &u.x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          g[cc + 2 * e] = bf16_lo(w[e]);
+          g[cc + 2 * e + 1] = bf16_hi(w[e]);
+        }
+      }
+#pragma unroll
+      for (int cc = 0; cc < CPT; ++cc)
+        g[cc] *= mode == kLinAdd ? alpha[h] : 1.0f - alpha[(size_t)h * D + cb + cc];
+    }
+    const float inv_den = live ? 1.0f / den : 0.0f;
+    float corr = 0.0f;
+#pragma unroll
+    for (int cc = 0; cc < CPT; ++cc) {
+      corr = fmaf(g[cc], num[cc] * inv_den, corr);  // G . O_l
+      dn[t * D + cb + cc] = g[cc] * inv_den;          // dnum
+    }
+    corr += __shfl_xor(corr, 4);
+    corr += __shfl_xor(corr, 2);
+    corr += __shfl_xor(corr, 1);
+    if (part == 0) {
+      dden_s[t] = -corr * inv_den;
+      if (live) drow[(size_t)bh * NP + row] -= corr;
+    }
+    __syncthreads();
+    // dQ_l = (H_D dnum + z_D dden) phi'(Q), phi' = 1 where phi > 1, else phi
+    if (live) {
+      const float ddn = dden_s[t];
+      for (int a = cb; a < cb + CPT; ++a) {
+        float acc2 = zs[a] * ddn;
+        for (int cc = 0; cc < D; cc += 4) {
+          const float4 hv = *reinterpret_cast<const float4*>(Hs + a * HP + cc);
+          const float4 dv4 = *reinterpret_cast<const float4*>(dn + t * D + cc);
+          acc2 = fmaf(hv.x, dv4.x, acc2);
+          acc2 = fmaf(hv.y, dv4.y, acc2);
+          acc2 = fmaf(hv.z, dv4.z, acc2);
+          acc2 = fmaf(hv.w, dv4.w, acc2);
+        }
+        const float f = fq[t * D + a];
+        dql[head + (size_t)row * D + a] = acc2 * (f > 1.0f ? 1.0f : f);
+      }
+    }
+    // dH_D += phi(Q)^T dnum, dz_D += phi(Q)^T dden over the chunk's rows
+    for (int t2 = 0; t2 < CH; ++t2) {
+      float fa[AT], dc[AT];
+#pragma unroll
+      for (int i = 0; i < AT; i += 4) {
+        const float4 x = *reinterpret_cast<const float4*>(fq + t2 * D + a0 + i);
+        const float4 y = *reinterpret_cast<const float4*>(dn + t2 * D + c0 + i);
+        fa[i] = x.x; fa[i + 1] = x.y; fa[i + 2] = x.z; fa[i + 3] = x.w;
+        dc[i] = y.x; dc[i + 1] = y.y; dc[i + 2] = y.z; dc[i + 3] = y.w;
+      }
+#pragma unroll
+      for (int i = 0; i < AT; ++i)
+#pragma unroll
+        for (int j = 0; j < AT; ++j) dh[i][j] = fmaf(fa[i], dc[j], dh[i][j]);
+      const float dd2 = dden_s[t2];
+#pragma unroll
+      for (int i = 0; i < AT; ++i) dzacc[i] = fmaf(fa[i], dd2, dzacc[i]);
+    }
+    __syncthreads();  // the next chunk overwrites fq, dn
+  }
+#pragma unroll
+  for (int i = 0; i < AT; ++i)
+#pragma unroll
+    for (int j = 0; j < AT; ++j) dh_out[(size_t)(a0 + i) * D + c0 + j] = dh[i][j];
+  if (th % 16 == 0)
+#pragma unroll
+    for (int i = 0; i < AT; ++i) dz_out[a0 + i] = dzacc[i];
+}
+
+// dH_tot[bh] = sum over the query blocks of dH_D, dz_tot likewise, in block
+// order. Grid (B*H, chunks of 256 entries).
+template <int D>
+__global__ __launch_bounds__(256) void linear_bwd_total_kernel(const float* __restrict__ dHq,
+                                                               const float* __restrict__ dzq,
+                                                               float* __restrict__ dHt,
+                                                               float* __restrict__ dzt,
+                                                               int n_q) {
+  const int bh = blockIdx.x, e = blockIdx.y * 256 + threadIdx.x;
+  if (e >= D * D + D) return;
+  float acc = 0.0f;
+  if (e < D * D) {
+    for (int i = 0; i < n_q; ++i) acc += dHq[((size_t)bh * n_q + i) * D * D + e];
+    dHt[(size_t)bh * D * D + e] = acc;
+  } else {
+    const int a = e - D * D;
+    for (int i = 0; i < n_q; ++i) acc += dzq[((size_t)bh * n_q + i) * D + a];
+    dzt[(size_t)bh * D + a] = acc;
+  }
+}
+
+// Per (b, h, key block j): G_j = the sum of dH_D over the query blocks that
+// dropped j, as dH_tot minus the listing blocks or directly over the others,
+// whichever is shorter (g_j likewise), then for its 64 keys in float32
+// dV_l = phi(K) G_j and dK_l = (G_j V + g_j) phi'(K). Heads whose branch is
+// off write zeros.
+template <int D>
+__global__ __launch_bounds__(256, 1) void linear_bwd_keys_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ dHq, const float* __restrict__ dzq,
+    const float* __restrict__ dHt, const float* __restrict__ dzt,
+    const int32_t* __restrict__ cmat, const int32_t* __restrict__ colcnt,
+    const int32_t* __restrict__ coloff, const int32_t* __restrict__ collist,
+    const int32_t* __restrict__ lin_on, float* __restrict__ dkl, float* __restrict__ dvl,
+    int H, int N, int n_q, int n_k, int total) {
+  constexpr int HP = D + 4, F4 = D * D / 4 / 256, KPT = D / 4;  // float4 of G per thread
+  __shared__ __align__(16) float Gs[D * HP];
+  __shared__ __align__(16) float gs[D];
+  __shared__ __align__(16) float fk[BK * D];
+  __shared__ __align__(16) float vr[BK * D];
+  const int tile = xcd_remap(blockIdx.x, total);
+  const int bh = tile / n_k, j = tile % n_k, h = bh % H;
+  const int th = threadIdx.x;
+  const size_t head = (size_t)bh * N * D;
+  const int key0 = j * BK;
+  const int u = th >> 2, cb = (th & 3) * KPT;  // this thread's key and channel quarter
+  const bool live = key0 + u < N;
+
+  if (lin_on[h] == 0) {
+    if (live)
+      for (int cc = 0; cc < KPT; ++cc) {
+        dkl[head + (size_t)(key0 + u) * D + cb + cc] = 0.0f;
+        dvl[head + (size_t)(key0 + u) * D + cb + cc] = 0.0f;
+      }
+    return;
+  }
+  const int listed = colcnt[(size_t)bh * n_k + j];
+  const bool use_kept = listed <= n_q - listed;
+  float4 gacc[F4];
+  float4 zacc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  const bool zthread = th < D / 4;
+  if (use_kept) {
+    const float4* t4 = reinterpret_cast<const float4*>(dHt + (size_t)bh * D * D);
+#pragma unroll
+    for (int m = 0; m < F4; ++m) gacc[m] = t4[m * 256 + th];
+    if (zthread) zacc = reinterpret_cast<const float4*>(dzt + (size_t)bh * D)[th];
+    const int beg = coloff[(size_t)bh * (n_k + 1) + j], end = coloff[(size_t)bh * (n_k + 1) + j + 1];
+    const int32_t* lst = collist + (size_t)bh * n_q * n_k;
+    for (int e = beg; e < end; ++e) {
+      const int i = lst[e];
+      const float4* q4 = reinterpret_cast<const float4*>(dHq + ((size_t)bh * n_q + i) * D * D);
+#pragma unroll
+      for (int m = 0; m < F4; ++m) {
+        const float4 x = q4[m * 256 + th];
+        gacc[m].x -= x.x; gacc[m].y -= x.y; gacc[m].z -= x.z; gacc[m].w -= x.w;
+      }
+      if (zthread) {
+        const float4 x = reinterpret_cast<const float4*>(dzq + ((size_t)bh * n_q + i) * D)[th];
+        zacc.x -= x.x; zacc.y -= x.y; zacc.z -= x.z; zacc.w -= x.w;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < F4; ++m) gacc[m] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    const int32_t* cm = cmat + ((size_t)bh * n_k + j) * n_q;
+    for (int i = 0; i < n_q; ++i) {
+      if (cm[i] != 0) continue;
+      const float4* q4 = reinterpret_cast<const float4*>(dHq + ((size_t)bh * n_q + i) * D * D);
+#pragma unroll
+      for (int m = 0; m < F4; ++m) {
+        const float4 x = q4[m * 256 + th];
+        gacc[m].x += x.x; gacc[m].y += x.y; gacc[m].z += x.z; gacc[m].w += x.w;
+      }
+      if (zthread) {
+        const float4 x = reinterpret_cast<const float4*>(dzq + ((size_t)bh * n_q + i) * D)[th];
+        zacc.x += x.x; zacc.y += x.y; zacc.z += x.z; zacc.w += x.w;
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < F4; ++m) {
+    const int e = (m * 256 + th) * 4, a = e / D, cc = e % D;
+    *reinterpret_cast<float4*>(Gs + a * HP + cc) = gacc[m];
+  }
+  if (zthread) *reinterpret_cast<float4*>(gs + 4 * th) = zacc;
+  for (int p = th; p < BK * D / 8; p += 256) {  // phi(K) and V rows of the block, zero past N
+    const int uu = p / (D / 8), c8 = (p % (D / 8)) * 8;
+    float f[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    float w8[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    if (key0 + uu < N) {
+      const uint4 kk = *reinterpret_cast<const uint4*>(k + head + (size_t)(key0 + uu) * D + c8);
+      const uint4 vv = *reinterpret_cast<const uint4*>(v + head + (size_t)(key0 + uu) * D + c8);
+      const uint32_t* wk = &kk.x;
+      const uint32_t* wv = &vv.x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        f[2 * e] = elu1(bf16_lo(wk[e]));
+        f[2 * e + 1] = elu1(bf16_hi(wk[e]));
+        w8[2 * e] = bf16_lo(wv[e]);
+        w8[2 * e + 1] = bf16_hi(wv[e]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; e += 4) {
+      *reinterpret_cast<float4*>(fk + uu * D + c8 + e) = make_float4(f[e], f[e + 1], f[e + 2], f[e + 3]);
+      *reinterpret_cast<float4*>(vr + uu * D + c8 + e) = make_float4(w8[e], w8[e + 1], w8[e + 2], w8[e + 3]);
+    }
+  }
+  __syncthreads();
+  if (!live) return;
+  // dV_l[u][c] = sum_a phi(K_u)[a] G[a][c]
+  float dvv[KPT];
+#pragma unroll
+  for (int cc = 0; cc < KPT; ++cc) dvv[cc] = 0.0f;
+  for (int a = 0; a < D; ++a) {
+    const float f = fk[u * D + a];
+#pragma unroll
+    for (int cc = 0; cc < KPT; cc += 4) {
+      const float4 gv = *reinterpret_cast<const float4*>(Gs + a * HP + cb + cc);
+      dvv[cc] = fmaf(f, gv.x, dvv[cc]);
+      dvv[cc + 1] = fmaf(f, gv.y, dvv[cc + 1]);
+      dvv[cc + 2] = fmaf(f, gv.z, dvv[cc + 2]);
+      dvv[cc + 3] = fmaf(f, gv.w, dvv[cc + 3]);
+    }
+  }
+  float* const vo = dvl + head + (size_t)(key0 + u) * D + cb;
+#pragma unroll
+  for (int cc = 0; cc < KPT; cc += 4)
+    *reinterpret_cast<float4*>(vo + cc) = make_float4(dvv[cc], dvv[cc + 1], dvv[cc + 2], dvv[cc + 3]);
+  // dK_l[u][a] = (sum_c G[a][c] V_u[c] + g[a]) phi'(K_u[a]) for the thread's quarter of a
+  float* const ko = dkl + head + (size_t)(key0 + u) * D;
+  for (int a = cb; a < cb + KPT; ++a) {
+    float s2 = gs[a];
+    for (int cc = 0; cc < D; cc += 4) {
+      const float4 gv = *reinterpret_cast<const float4*>(Gs + a * HP + cc);
+      const float4 vv = *reinterpret_cast<const float4*>(vr + u * D + cc);
+      s2 = fmaf(gv.x, vv.x, s2);
+      s2 = fmaf(gv.y, vv.y, s2);
+      s2 = fmaf(gv.z, vv.z, s2);
+      s2 = fmaf(gv.w, vv.w, s2);
+    }
+    const float f = fk[u * D + a];
+    ko[a] = s2 * (f > 1.0f ? 1.0f : f);
+  }
+}
+
+// dO_s = alpha (*) dO (the mix's sparse share), bf16; one thread per 8 values.
+template <int D>
+__global__ __launch_bounds__(256) void scale_do_kernel(const uint16_t* __restrict__ dO,
+                                                       const float* __restrict__ alpha,
+                                                       uint16_t* __restrict__ dos, int H, int N,
+                                                       size_t n8) {
+  const size_t p = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (p >= n8) return;
+  const size_t e = p * 8;
+  const int h = (int)((e / ((size_t)N * D)) % H), c = (int)(e % D);
+  const uint4 u = *reinterpret_cast<const uint4*>(dO + e);
+  const uint32_t* w = &u.x;
+  uint4 o;
+  uint32_t* ow = &o.x;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    ow[i] = pack2_bf16(alpha[(size_t)h * D + c + 2 * i] * bf16_lo(w[i]),
+                       alpha[(size_t)h * D + c + 2 * i + 1] * bf16_hi(w[i]));
+  *reinterpret_cast<uint4*>(dos + e) = o;
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(int32_t* __restrict__ p, size_t n) {
@@ -560,16 +1021,22 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(int32_t* __restrict__ p,
 
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// workspace regions, in order
+// workspace regions, in order (the linear ones only when the branch is on)
 struct BwdWs {
   uint16_t *qt, *dot, *kt;
   float *drow, *lse2;
   int32_t *cmat, *colcnt, *coloff, *collist;
+  // linear branch
+  uint16_t *vtp, *phikt, *dos;
+  float *lin_h, *lin_z, *part_h, *part_z;
+  int32_t *lin_on, *lin_lists;
+  float *dql, *dkl, *dvl, *dHq, *dzq, *dHt, *dzt;
 };
 
-BwdWs bwd_layout(unsigned char* w, int B, int H, int N, int d, int block_q, size_t* bytes) {
+BwdWs bwd_layout(unsigned char* w, int B, int H, int N, int d, int block_q, bool linear,
+                 size_t* bytes) {
   const size_t BH = (size_t)B * H, n_q = (N + block_q - 1) / block_q, n_k = (N + BK - 1) / BK;
-  const size_t packed = up256(BH * n_k * BK * d * 2);
+  const size_t packed = BH * n_k * BK * d * 2, rows = BH * N * d;
   BwdWs r{};
   size_t off = 0;
   auto take = [&](size_t n) {
@@ -586,25 +1053,64 @@ BwdWs bwd_layout(unsigned char* w, int B, int H, int N, int d, int block_q, size
   r.colcnt = reinterpret_cast<int32_t*>(take(BH * n_k * 4));
   r.coloff = reinterpret_cast<int32_t*>(take(BH * (n_k + 1) * 4));
   r.collist = reinterpret_cast<int32_t*>(take(BH * n_q * n_k * 4));
+  if (linear) {
+    r.vtp = reinterpret_cast<uint16_t*>(take(packed));
+    r.phikt = reinterpret_cast<uint16_t*>(take(packed));
+    r.dos = reinterpret_cast<uint16_t*>(take(rows * 2));
+    r.lin_h = reinterpret_cast<float*>(take(BH * d * d * 4));
+    r.lin_z = reinterpret_cast<float*>(take(BH * d * 4));
+    r.part_h = reinterpret_cast<float*>(take(BH * kLinSplit * d * d * 4));
+    r.part_z = reinterpret_cast<float*>(take(BH * kLinSplit * d * 4));
+    r.lin_on = reinterpret_cast<int32_t*>(take(H * 4));
+    r.lin_lists = reinterpret_cast<int32_t*>(take((2 + 2 * BH) * 4));
+    r.dql = reinterpret_cast<float*>(take(rows * 4));
+    r.dkl = reinterpret_cast<float*>(take(rows * 4));
+    r.dvl = reinterpret_cast<float*>(take(rows * 4));
+    r.dHq = reinterpret_cast<float*>(take(BH * n_q * d * d * 4));
+    r.dzq = reinterpret_cast<float*>(take(BH * n_q * d * 4));
+    r.dHt = reinterpret_cast<float*>(take(BH * d * d * 4));
+    r.dzt = reinterpret_cast<float*>(take(BH * d * 4));
+  }
   if (bytes) *bytes = off;
   return r;
 }
 
 template <int D, int BQ>
 hipError_t launch_bwd_t(const BwdLaunch& a, hipStream_t s) {
-  const BwdWs w = bwd_layout(a.workspace, a.B, a.H, a.N, a.d, a.block_q, nullptr);
+  const bool linear = a.alpha != nullptr;
+  const BwdWs w = bwd_layout(a.workspace, a.B, a.H, a.N, a.d, a.block_q, linear, nullptr);
   const int BH = a.B * a.H, n64 = a.n_k;  // 64-row groups of Q and dO = key blocks
   const float c = a.scale * kLog2e;
+  const uint16_t* dos = a.dO;  // the sparse part's upstream gradient
+  if (linear) {
+    if constexpr (D == BQ) {
+      hipLaunchKernelGGL(linear_flags_kernel, dim3(1), dim3(kFlagThreads), 0, s, a.alpha,
+                         a.lin_mode, D, a.drop_below, a.B, a.H, w.lin_on, w.lin_lists);
+      hipLaunchKernelGGL((pack_kernel<D, true>), dim3(a.n_k, BH), dim3(2 * D), 0, s, a.v, a.k,
+                         w.vtp, w.phikt, a.N, a.n_k, w.lin_on, a.H);
+      hipLaunchKernelGGL((linear_total_kernel<D>), dim3(kLinSplit, BH), dim3(D * 2), 0, s,
+                         w.phikt, w.vtp, w.part_h, w.part_z, a.n_k, w.lin_on, a.H);
+      hipLaunchKernelGGL((linear_reduce_kernel<D>), dim3(BH), dim3(256), 0, s, w.part_h,
+                         w.part_z, w.lin_h, w.lin_z, w.lin_on, a.H);
+      if (a.lin_mode == kLinMix) {
+        const size_t n8 = (size_t)BH * a.N * D / 8;
+        hipLaunchKernelGGL((scale_do_kernel<D>), dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0,
+                           s, a.dO, a.alpha, w.dos, a.H, a.N, n8);
+        dos = w.dos;
+      }
+    }
+  }
   // Q^T, dO^T and K^T (fp16) packed in 64-row groups like V^T
   hipLaunchKernelGGL((pack_kernel<D, false>), dim3(n64, BH), dim3(2 * D), 0, s, a.q, nullptr,
                      w.qt, nullptr, a.N, n64, nullptr, a.H);
-  hipLaunchKernelGGL((pack_kernel<D, false>), dim3(n64, BH), dim3(2 * D), 0, s, a.dO, nullptr,
+  hipLaunchKernelGGL((pack_kernel<D, false>), dim3(n64, BH), dim3(2 * D), 0, s, dos, nullptr,
                      w.dot, nullptr, a.N, n64, nullptr, a.H);
   hipLaunchKernelGGL((pack_kernel<D, false, true>), dim3(n64, BH), dim3(2 * D), 0, s, a.k,
                      nullptr, w.kt, nullptr, a.N, n64, nullptr, a.H);
   const int NP = n64 * BK;
   const size_t rows = (size_t)BH * NP;
   constexpr int RPW = 256 / (D / 8);
+  // D = dO . O with the caller's dO and O (the linear kernel corrects it to the sparse share)
   hipLaunchKernelGGL((bwd_rows_kernel<D>), dim3((unsigned)((rows + RPW - 1) / RPW)), dim3(256), 0,
                      s, a.o, a.dO, a.lse, w.drow, w.lse2, a.N, NP, rows);
   // the query blocks that list each key block
@@ -619,20 +1125,34 @@ hipError_t launch_bwd_t(const BwdLaunch& a, hipStream_t s) {
   hipLaunchKernelGGL(col_scan_kernel, dim3(BH), dim3(256), 0, s, w.colcnt, w.coloff, a.n_k);
   hipLaunchKernelGGL(col_list_kernel, dim3((cols + 3) / 4), dim3(256), 0, s, w.cmat, w.coloff,
                      w.collist, a.n_q, a.n_k, cols);
+  if (linear) {
+    if constexpr (D == BQ) {
+      hipLaunchKernelGGL((linear_bwd_rows_kernel<D>), dim3(qrows), dim3(256), 0, s, a.q, a.dO,
+                         w.phikt, w.vtp, w.lin_h, w.lin_z, a.idx, a.cnt, w.lin_on, a.alpha,
+                         a.lin_mode, w.dql, w.dHq, w.dzq, w.drow, a.H, a.N, a.n_q, a.n_k, NP,
+                         qrows);
+      hipLaunchKernelGGL((linear_bwd_total_kernel<D>), dim3(BH, (D * D + D + 255) / 256),
+                         dim3(256), 0, s, w.dHq, w.dzq, w.dHt, w.dzt, a.n_q);
+      hipLaunchKernelGGL((linear_bwd_keys_kernel<D>), dim3(cols), dim3(256), 0, s, a.k, a.v,
+                         w.dHq, w.dzq, w.dHt, w.dzt, w.cmat, w.colcnt, w.coloff, w.collist,
+                         w.lin_on, w.dkl, w.dvl, a.H, a.N, a.n_q, a.n_k, cols);
+    }
+  }
   hipLaunchKernelGGL((sparse_attn_bwd_dkdv_kernel<D, BQ>), dim3(cols), dim3(256), 0, s, a.q, a.k,
-                     a.v, a.dO, w.qt, w.dot, w.lse2, w.drow, w.coloff, w.collist, a.dk, a.dv,
-                     a.N, a.n_q, a.n_k, n64, cols, c, a.scale);
+                     a.v, dos, w.qt, w.dot, w.lse2, w.drow, w.coloff, w.collist, a.dk, a.dv,
+                     a.N, a.n_q, a.n_k, n64, cols, c, a.scale, linear ? w.dkl : nullptr,
+                     linear ? w.dvl : nullptr);
   hipLaunchKernelGGL((sparse_attn_bwd_dq_kernel<D, BQ>), dim3(qrows), dim3(BQ * 2), 0, s, a.q,
-                     a.k, a.v, a.dO, w.kt, w.lse2, w.drow, a.idx, a.cnt, a.dq, a.N, a.n_q,
-                     a.n_k, qrows, c, a.scale);
+                     a.k, a.v, dos, w.kt, w.lse2, w.drow, a.idx, a.cnt, a.dq, a.N, a.n_q,
+                     a.n_k, qrows, c, a.scale, linear ? w.dql : nullptr);
   return hipGetLastError();
 }
 
 }  // namespace
 
-size_t bwd_workspace_bytes(int B, int H, int N, int d, int block_q) {
+size_t bwd_workspace_bytes(int B, int H, int N, int d, int block_q, bool linear) {
   size_t bytes = 0;
-  bwd_layout(nullptr, B, H, N, d, block_q, &bytes);
+  bwd_layout(nullptr, B, H, N, d, block_q, linear, &bytes);
   return bytes;
 }
 

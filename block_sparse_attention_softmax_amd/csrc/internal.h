@@ -107,9 +107,13 @@ struct BwdLaunch {
   int B, H, N, d, block_q, n_q, n_k;
   float scale;
   unsigned char* workspace;  // bwd_workspace_bytes()
+  // linear branch (alpha == nullptr: none), as in AttnLaunch; requires block_q == d
+  const float* alpha;
+  int lin_mode;
+  float drop_below;
 };
 hipError_t launch_bwd(const BwdLaunch& a, hipStream_t s);
-size_t bwd_workspace_bytes(int B, int H, int N, int d, int block_q);
+size_t bwd_workspace_bytes(int B, int H, int N, int d, int block_q, bool linear = false);
 size_t attn_workspace_bytes(int B, int H, int N, int d);    // packed V
 size_t linear_workspace_bytes(int B, int H, int N, int d);  // packed V + linear branch
 

@@ -247,6 +247,9 @@ size_t sparse_linear_workspace_bytes(int B, int H, int N, int d);
  * changes no output value; a negative or NaN drop_below skips none.
  *
  *  alpha     : float32 [H], device, 4-byte aligned.
+ *  lse       : nullptr, or out float32 [B, H, N], device, 4-byte aligned: the
+ *              log-sum-exp of each row's kept scores (of the sparse part), as
+ *              sparge_attn_fwd_lse writes it, for sparse_linear_attn_bwd.
  *  workspace : device scratch of at least sparse_linear_workspace_bytes(),
  *              16-byte aligned; contents on entry do not matter.
  *  Other arguments as for sparge_attn_fwd. */
@@ -254,7 +257,8 @@ int sparse_linear_attn_fwd(const void* q, const void* k, const void* v,
                            const int32_t* kv_idx, const int32_t* kv_cnt,
                            const float* alpha, int B, int H, int N, int d,
                            int block_q, int block_k, float scale, float drop_below,
-                           void* o, void* workspace, size_t workspace_bytes, void* stream);
+                           void* o, float* lse, void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 /* SLA2's faithful sparse-linear output (SLA2 page, section 2A): a learned
  * vector alpha in [0, 1] weighs the two branches channel by channel,
@@ -267,11 +271,57 @@ int sparse_linear_attn_fwd(const void* q, const void* k, const void* v,
  *
  *  alpha     : float32 [H, d] row-major, device, 16-byte aligned.
  *  workspace : as for sparse_linear_attn_fwd (same size).
- *  Other arguments as for sparse_linear_attn_fwd. */
+ *  Other arguments (lse included) as for sparse_linear_attn_fwd. */
 int sla2_mix_attn_fwd(const void* q, const void* k, const void* v, const int32_t* kv_idx,
                       const int32_t* kv_cnt, const float* alpha, int B, int H, int N, int d,
                       int block_q, int block_k, float scale, float drop_below, void* o,
-                      void* workspace, size_t workspace_bytes, void* stream);
+                      float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Device workspace (bytes) of sparse_linear_attn_bwd and sla2_mix_attn_bwd:
+ * that of sparge_attn_bwd, plus the linear branch's packed V and phi(K), its
+ * totals, the scaled dO of the mix, float32 dQ, dK, dV of the branch and one
+ * float32 d x d summary per query block. Returns 0 for arguments those calls
+ * would reject. */
+size_t sparse_linear_bwd_workspace_bytes(int B, int H, int N, int d);
+
+/* Backward of sparse_linear_attn_fwd (O = O_s + alpha[h] O_l) for an upstream
+ * gradient dO. The sparse part is sparge_attn_bwd's with the upstream gradient
+ * dO and D_t = dO_t . O_s,t (taken as dO_t . O_t - G_t . O_l,t); the linear
+ * part receives G = alpha[h] dO. With num_t = phi(Q_t) H_D, den_t = phi(Q_t).z_D
+ * (H_D = sum over the dropped keys D_i of phi(K_u)^T V_u, z_D = sum phi(K_u)):
+ *   dnum = G / den,  dden = -(G . O_l) / den,  dQ_t += (H_D dnum + z_D dden) phi'(Q_t),
+ *   dK_u += (dH V_u + dz) phi'(K_u),  dV_u += phi(K_u) dH  for u in D_i,
+ * dH = sum_t phi(Q_t)^T dnum_t, dz = sum_t phi(Q_t) dden_t over the rows of the
+ * block (the chain rule of the SLA2 page's sparse-linear output, section 1).
+ * The linear part runs in float32 (H_D from bf16 phi(K) and V on the matrix
+ * cores, as in the forward) and is added to the sparse part's float32
+ * results before dQ, dK, dV are rounded to bf16. Heads dropped by the same
+ * rule as the forward (|alpha[h]| <= drop_below) pass no linear gradient.
+ * Built for block_q == d and at most 4096 key blocks; deterministic.
+ *
+ *  o, lse    : from sparse_linear_attn_fwd with the same inputs (lse its
+ *              lse output).
+ *  alpha     : float32 [H], device.
+ *  workspace : at least sparse_linear_bwd_workspace_bytes(), 16-byte aligned.
+ *  Other arguments as for sparge_attn_bwd. */
+int sparse_linear_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                           const void* d_o, const float* lse, const int32_t* kv_idx,
+                           const int32_t* kv_cnt, const float* alpha, int B, int H, int N,
+                           int d, int block_q, int block_k, float scale, float drop_below,
+                           void* dq, void* dk, void* dv, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* Backward of sla2_mix_attn_fwd (O = alpha (*) O_s + (1 - alpha) (*) O_l, SLA2
+ * page, section 2A): as sparse_linear_attn_bwd with the sparse part receiving
+ * alpha (*) dO (rounded to bf16) and the linear part (1 - alpha) (*) dO.
+ *  alpha : float32 [H, d], device, 16-byte aligned.
+ *  Other arguments as for sparse_linear_attn_bwd (o, lse from sla2_mix_attn_fwd). */
+int sla2_mix_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                      const void* d_o, const float* lse, const int32_t* kv_idx,
+                      const int32_t* kv_cnt, const float* alpha, int B, int H, int N, int d,
+                      int block_q, int block_k, float scale, float drop_below, void* dq,
+                      void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                      void* stream);
 
 /* Message for the last non-OK return on the calling thread ("" if none).
  * The pointer stays valid until the next library call on that thread. */

@@ -94,7 +94,7 @@ def test_packed_attn_rejects_bad_arguments(kw, code):
 
 def _lin(fn="sparse_linear_attn_fwd", **kw):
     args = dict(q=A, k=A, v=A, idx=A, cnt=A, alpha=A, B=1, H=2, N=1024, d=64, bq=64, bk=64,
-                sc=0.125, drop=0.0, o=A, ws=A, wsb=1 << 30, st=None)
+                sc=0.125, drop=0.0, o=A, lse=None, ws=A, wsb=1 << 30, st=None)
     args.update(kw)
     return getattr(binding.lib(), fn)(*args.values())
 
@@ -216,3 +216,22 @@ def test_forward_lse_rejects_bad_arguments():
     args[13] = ctypes.c_void_p(0x10002)
     assert L.sparge_attn_fwd_lse(*args) == -1
     assert "lse" in L.sparge_last_error().decode()
+
+
+def test_linear_backward_workspace_and_rejections():
+    L = binding.lib()
+    plain = L.sparge_attn_bwd_workspace_bytes(1, 12, 32760, 128, 128, 64)
+    lin = L.sparse_linear_bwd_workspace_bytes(1, 12, 32760, 128)
+    assert lin > plain
+    assert L.sparse_linear_bwd_workspace_bytes(1, 1, 64 * 4097, 64) == 0  # > 4096 key blocks
+    args = dict(q=A, k=A, v=A, o=A, do=A, lse=A, idx=A, cnt=A, alpha=A, B=1, H=2, N=1024, d=64,
+                bq=64, bk=64, sc=0.125, drop=0.0, dq=A, dk=A, dv=A, ws=A, wsb=1 << 30, st=None)
+    for fn in ("sparse_linear_attn_bwd", "sla2_mix_attn_bwd"):
+        for kw, code in ((dict(alpha=None), -1), (dict(bq=128), -2), (dict(wsb=1024), -1),
+                         (dict(d=96), -2), (dict(do=MIS), -1)):
+            a2 = dict(args)
+            a2.update(kw)
+            assert getattr(L, fn)(*a2.values()) == code, (fn, kw)
+    a2 = dict(args)
+    a2.update(alpha=ctypes.c_void_p(0x10004))  # 4-byte aligned: enough for the added form only
+    assert L.sla2_mix_attn_bwd(*a2.values()) == -1

@@ -223,3 +223,122 @@ def test_forward_then_backward_on_workload_sampled():
             lim = (DQ_CHAIN_MAX_REL, DQ_CHAIN_MEAN_REL) if n == "dq" else ()
             rel.append(compare_grads(g[0, h][rows], r[rows], n, *lim))
         _report(f"chain workload h={h}", rel)
+
+
+# ------------------------------------------------------ linear branch backward
+LIN_SHAPES = [(1, 3, 1000, 128), (2, 1, 777, 64), (1, 2, 300, 128), (1, 2, 2048, 128)]
+
+
+def _lin_alpha(mode, H, d, seed):
+    rng = np.random.default_rng(seed)
+    if mode == "add":
+        a = rng.uniform(0.05, 0.8, H).astype(np.float32)
+        a[-1] = 0.0  # a dropped branch (drop_below = 0)
+    else:
+        a = rng.random((H, d)).astype(np.float32)
+        a[-1] = 1.0  # a dropped branch: the mix without its linear term
+    return a
+
+
+def _oracle_linear_forward(Q, K, V, kept, d, scale, alpha, mode, heads=None):
+    B, H, N, _ = Q.shape
+    o = np.zeros((B, H, N, d), np.uint16)
+    lse = np.zeros((B, H, N), np.float32)
+    for b, h in (np.ndindex(B, H) if heads is None else heads):
+        f = [_f(x, b, h) for x in (Q, K, V)]
+        if mode == "add":
+            out = O.sparse_linear_attention_head(*f, kept[b, h], d, 64, scale, float(alpha[h]))
+        else:
+            out = O.sla2_mix_attention_head(*f, kept[b, h], d, 64, scale, alpha[h])
+        o[b, h] = f64_to_bf16_bits(out)
+        lse[b, h] = O.masked_attention_lse_head(f[0], f[1], kept[b, h], d, 64, scale)
+    return o, lse
+
+
+@pytest.mark.parametrize("mode", ["add", "mix"])
+@pytest.mark.parametrize("B,H,N,d", LIN_SHAPES)
+def test_linear_backward_small_shapes_in_full(B, H, N, d, mode):
+    Q, K, V, dO, kept, idx, cnt = _case(B, H, N, d, d, 11 * N + d)
+    scale = S.default_scale(d)
+    alpha = _lin_alpha(mode, H, d, N)
+    o_bits, lse = _oracle_linear_forward(Q, K, V, kept, d, scale, alpha, mode)
+    fn = S.sparse_linear_attn_bwd if mode == "add" else S.sla2_mix_attn_bwd
+    print(f"\n[lin bwd {mode}] B={B} H={H} N={N} d={d}", flush=True)
+    grads = fn(to_gpu(Q), to_gpu(K), to_gpu(V), to_gpu(o_bits), to_gpu(dO),
+               torch.from_numpy(lse).cuda(), idx, cnt, torch.from_numpy(alpha).cuda(), d, 64)
+    torch.cuda.synchronize()
+    got = [_np(t) for t in grads]
+    for b in range(B):
+        for h in range(H):
+            f = [_f(x, b, h) for x in (Q, K, V)]
+            if mode == "add":
+                ref = O.sparse_linear_attention_backward_head(*f, kept[b, h], d, 64, scale,
+                                                              float(alpha[h]), _f(dO, b, h),
+                                                              o=_f(o_bits, b, h))
+            else:
+                ref = O.sla2_mix_attention_backward_head(*f, kept[b, h], d, 64, scale, alpha[h],
+                                                         _f(dO, b, h), o=_f(o_bits, b, h))
+            _report(f"lin bwd {mode} b={b} h={h}", [compare_grads(g[b, h], r, n)
+                                                    for g, r, n in zip(got, ref, NAMES)])
+
+
+@pytest.mark.parametrize("mode", ["add", "mix"])
+def test_linear_forward_then_backward(mode):
+    """The GPU linear forward's O and lse feed the GPU backward; the exact gradient."""
+    B, H, N, d = 1, 3, 1000, 128
+    Q, K, V, dO, kept, idx, cnt = _case(B, H, N, d, d, 1234)
+    alpha = _lin_alpha(mode, H, d, 5)
+    q, k, v, do = to_gpu(Q), to_gpu(K), to_gpu(V), to_gpu(dO)
+    a = torch.from_numpy(alpha).cuda()
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    fwd = S.sparse_linear_attn_fwd if mode == "add" else S.sla2_mix_attn_fwd
+    bwd = S.sparse_linear_attn_bwd if mode == "add" else S.sla2_mix_attn_bwd
+    o = fwd(q, k, v, idx, cnt, a, d, 64, lse=lse)
+    o_plain = fwd(q, k, v, idx, cnt, a, d, 64)
+    grads = bwd(q, k, v, o, do, lse, idx, cnt, a, d, 64)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o_plain.view(torch.int16))
+    got = [_np(t) for t in grads]
+    scale = S.default_scale(d)
+    print(f"\n[lin chain {mode}]", flush=True)
+    for h in range(H):
+        lse_ref = O.masked_attention_lse_head(_f(Q, 0, h), _f(K, 0, h), kept[0, h], d, 64, scale)
+        live = ~np.isneginf(lse_ref)
+        assert np.abs(lse.cpu().numpy()[0, h][live] - lse_ref[live]).max() <= 2.5e-3
+        f = [_f(x, 0, h) for x in (Q, K, V)]
+        if mode == "add":
+            ref = O.sparse_linear_attention_backward_head(*f, kept[0, h], d, 64, scale,
+                                                          float(alpha[h]), _f(dO, 0, h))
+        else:
+            ref = O.sla2_mix_attention_backward_head(*f, kept[0, h], d, 64, scale, alpha[h],
+                                                     _f(dO, 0, h))
+        _report(f"lin chain {mode} h={h}", [compare_grads(g[0, h], r, n)
+                                            for g, r, n in zip(got, ref, NAMES)])
+
+
+def test_linear_backward_on_workload_sampled():
+    """wan1.3b at the 95% point (p = 0, k = 5%), alpha = 0.1: O and lse from the
+    oracle for one head; dQ of sampled query blocks, dK, dV of sampled key blocks."""
+    wl, rng, Q, K, V, dO, q, k, v, do, idx, cnt, kept = _workload(0.05)
+    h = int(rng.integers(wl.H))
+    alpha = np.full(wl.H, 0.1, np.float32)
+    o_bits, lse = _oracle_linear_forward(Q, K, V, kept, wl.d, wl.scale, alpha, "add",
+                                         heads=[(0, h)])
+    grads = S.sparse_linear_attn_bwd(q, k, v, to_gpu(o_bits), do, torch.from_numpy(lse).cuda(),
+                                     idx, cnt, torch.from_numpy(alpha).cuda(), wl.block_q,
+                                     wl.block_k, wl.scale)
+    torch.cuda.synchronize()
+    got = [_np(t) for t in grads]
+    qb = sorted({0, wl.n_q - 1, *rng.choice(wl.n_q, 2, replace=False)})
+    kb = sorted({wl.n_k - 1, *rng.choice(wl.n_k, 2, replace=False)})
+    f = [_f(x, 0, h) for x in (Q, K, V)]
+    o_s = _f(o_bits, 0, h) - 0.1 * O.linear_branch_head(*f, kept[0, h], wl.block_q, wl.block_k)
+    gs = O.masked_attention_backward_sampled(*f, kept[0, h], wl.block_q, wl.block_k, wl.scale,
+                                             _f(dO, 0, h), qb, kb, o=o_s)
+    gl = O.linear_branch_backward_sampled(*f, kept[0, h], wl.block_q, wl.block_k,
+                                          float(np.float32(0.1)) * _f(dO, 0, h), qb, kb)
+    rel = []
+    for g, a, b2, n in zip(got, gs, gl, NAMES):
+        rows = ~np.isnan(a[:, 0])
+        rel.append(compare_grads(g[0, h][rows], a[rows] + b2[rows], n))
+    _report(f"lin bwd workload h={h}", rel)
