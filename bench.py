@@ -309,6 +309,31 @@ def main():
                           "bwd_ms": round(b_ms, 4), "algorithmic_tflops": round(kfb / b_ms / 1e9, 2),
                           "frac_bf16_peak": round(kfb / b_ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
 
+    # backward of the sparse-linear output (alpha = 0.1) on the headline mask
+    S.sparge_mask_predict(q, k, wl.block_q, wl.block_k, wl.k_frac, wl.p_mass, wl.scale,
+                          workspace=ws, out=(bits, idx, cnt))
+    S.sparse_linear_attn_fwd(q, k, v, idx, cnt, alpha, wl.block_q, wl.block_k, wl.scale,
+                             workspace=lws, out=o, lse=lse)
+    lbws = torch.empty(S.linear_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+
+    def lbwd():
+        S.sparse_linear_attn_bwd(q, k, v, o, d_o, lse, idx, cnt, alpha, wl.block_q, wl.block_k,
+                                 wl.scale, out=grads, workspace=lbws)
+    lbwd()
+    torch.cuda.synchronize()
+    n_b = max(3, args.steps // 5)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n_b):
+        lbwd()
+    e1.record()
+    torch.cuda.synchronize()
+    backward["sparse_linear_headline"] = {
+        "k": wl.k_frac, "p": wl.p_mass, "alpha": 0.1,
+        "bwd_ms": round(e0.elapsed_time(e1) / n_b, 4),
+        "vs_sparse_bwd": round(e0.elapsed_time(e1) / n_b / backward["headline"]["bwd_ms"], 3)}
+    del lbws
+
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl, Q, K, V, args.cpu_blocks)
 
     line = {
