@@ -575,3 +575,105 @@ def linear_branch_backward_sampled(q, k, v, kept, block_q: int, block_k: int, g:
     dk[keys] = dfk * elu_plus_one_grad(k[keys])
     dv[keys] = dvk
     return dq, dk, dv
+
+
+# --------------------------------------------------- low-bit sparse branch
+# SLA2 page, section 2C: the sparse branch runs with Q, K, P and V quantised in
+# the forward pass (low-bit attention such as INT8/FP8). Readings of what the
+# page leaves open: Q and K as INT8 with one float32 scale per block (query
+# blocks of block_q rows, key blocks of block_k rows): scale = amax / 127,
+# code = round-half-even(x * (127 / amax)) taken in float32; V as FP8 e4m3
+# (OCP e4m3fn: bias 7, largest finite 448) with one scale per (head, channel):
+# code = e4m3(x * (448 / amax)) in float32; P as e4m3 codes of 448 p, with p
+# taken against an exact running row maximum (so p <= 1), blocks visited in
+# the order of the row's list; O = sum p~ v~ / sum p~ over the visited blocks.
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(code: int) -> float:
+    """Value of an OCP e4m3fn byte (0x7f and 0xff are NaN)."""
+    s = -1.0 if code & 0x80 else 1.0
+    e, m = (code >> 3) & 0xF, code & 0x7
+    if e == 0xF and m == 0x7:
+        return math.nan
+    if e == 0:
+        return s * m * 2.0 ** -9                 # subnormal: m/8 * 2^-6
+    return s * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+def e4m3_round(x: np.ndarray) -> np.ndarray:
+    """Nearest e4m3 value, ties to the even code; |x| must not exceed 464
+    (the half-way point above 448)."""
+    x = np.asarray(x, np.float64)
+    a = np.abs(x)
+    assert np.all(a <= 464.0), "outside the e4m3 range"
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, -6.0)                      # subnormals share 2^-6's quantum
+    quantum = 2.0 ** (e - 3)
+    r = np.round(a / quantum) * quantum          # np.round: half to even
+    return np.sign(x) * np.minimum(r, E4M3_MAX)
+
+
+def int8_block_codes(x: np.ndarray, block: int):
+    """Rows of x (float32 values) in blocks of `block`: codes (int) and the
+    float32 scale of each block."""
+    x = np.asarray(x, np.float32)
+    n = x.shape[0]
+    codes = np.zeros(x.shape, np.int64)
+    scales = []
+    for s0, s1 in block_bounds(n, block):
+        amax = np.float32(np.abs(x[s0:s1]).max())
+        if amax == 0:
+            scales.append(np.float32(0))
+            continue
+        inv = np.float32(127) / amax
+        codes[s0:s1] = np.clip(np.rint(x[s0:s1] * inv), -127, 127).astype(np.int64)
+        scales.append(amax / np.float32(127))
+    return codes, np.array(scales, np.float32)
+
+
+def e4m3_channel_codes(x: np.ndarray):
+    """Columns of x (float32 values): e4m3 values of x * (448 / amax_c) and the
+    float32 scale amax_c / 448 of each column."""
+    x = np.asarray(x, np.float32)
+    amax = np.abs(x).max(axis=0).astype(np.float32)
+    inv = np.where(amax > 0, np.float32(E4M3_MAX) / np.where(amax > 0, amax, 1), 0)
+    vals = e4m3_round((x * inv.astype(np.float32)).astype(np.float32))
+    return vals, (amax / np.float32(E4M3_MAX)).astype(np.float32)
+
+
+def lowbit_attention_head(q, k, v, idx_rows, cnt_rows, block_q: int, block_k: int,
+                          scale: float, q_blocks=None) -> np.ndarray:
+    """The low-bit sparse branch for one head; q, k, v float64 [N, d] (bf16
+    values), idx_rows/cnt_rows the row lists. Rows of blocks not in
+    `q_blocks` are NaN; an empty list gives zeros."""
+    N, d = q.shape
+    qc, qs = int8_block_codes(q, block_q)
+    kc, ks = int8_block_codes(k, block_k)
+    vv, vs = e4m3_channel_codes(v)
+    v_deq = vv * vs.astype(np.float64)           # dequantised V
+    out = np.full((N, d), np.nan)
+    kb = block_bounds(N, block_k)
+    for i, (s0, s1) in enumerate(block_bounds(N, block_q)):
+        if q_blocks is not None and i not in q_blocks:
+            continue
+        m = np.full(s1 - s0, -np.inf)
+        l = np.zeros(s1 - s0)
+        acc = np.zeros((s1 - s0, d))
+        for e in range(int(cnt_rows[i])):
+            j = int(idx_rows[i, e])
+            k0, k1 = kb[j]
+            dot = (qc[s0:s1] @ kc[k0:k1].T).astype(np.float32)      # exact integers
+            s = dot * np.float32(qs[i] * ks[j])                      # float32, as stored
+            m_new = np.maximum(m, s.max(axis=1).astype(np.float64))
+            f = np.exp(scale * (m - m_new))
+            f[np.isneginf(m)] = 0.0
+            acc *= f[:, None]
+            l *= f
+            m = m_new
+            p = np.exp(scale * (s.astype(np.float64) - m[:, None]))
+            p8 = e4m3_round((p * E4M3_MAX).astype(np.float32)) / E4M3_MAX
+            l += p8.sum(axis=1)
+            acc += p8 @ v_deq[k0:k1]
+        out[s0:s1] = acc / l[:, None] if cnt_rows[i] > 0 else 0.0
+    return out

@@ -683,3 +683,69 @@ def test_linear_backward_sampled_equals_the_full_one():
     np.testing.assert_allclose(part[0][rows], full[0][rows], rtol=0, atol=1e-13)
     np.testing.assert_allclose(part[1][keys], full[1][keys], rtol=0, atol=1e-13)
     np.testing.assert_allclose(part[2][keys], full[2][keys], rtol=0, atol=1e-13)
+
+
+# ------------------------------------------------- low-bit sparse branch
+def test_e4m3_table():
+    # the format's own definition: every finite code decodes to a value that
+    # rounds back to itself; 448 is the largest, 2^-9 the smallest subnormal
+    vals = [O.e4m3_decode(c) for c in range(256)]
+    finite = [x for x in vals if not math.isnan(x)]
+    assert len(finite) == 254 and max(finite) == 448.0 and min(finite) == -448.0
+    assert O.e4m3_decode(0x01) == 2.0 ** -9 and O.e4m3_decode(0x08) == 2.0 ** -6
+    np.testing.assert_array_equal(O.e4m3_round(np.array(finite)), np.array(finite))
+    # half-way points go to the even code: 17 lies between 16 (0x58) and 18 (0x59)
+    assert O.e4m3_round(np.array([17.0, 19.0, 0.3, 2.0 ** -10, 3 * 2.0 ** -10]))[0] == 16.0
+    r = O.e4m3_round(np.array([19.0, 0.3, 2.0 ** -10, 3 * 2.0 ** -10, 460.0]))
+    np.testing.assert_array_equal(r, [20.0, 0.3125, 0.0, 2.0 ** -8, 448.0])
+
+
+def test_int8_codes():
+    rng = np.random.default_rng(81)
+    x = rng.standard_normal((200, 16)).astype(np.float32)
+    codes, scales = O.int8_block_codes(x, 64)
+    assert codes.min() >= -127 and codes.max() <= 127 and scales.shape == (4,)
+    for b, (s0, s1) in enumerate(O.block_bounds(200, 64)):
+        assert np.abs(codes[s0:s1]).max() == 127           # the block's extreme maps to 127
+        err = np.abs(codes[s0:s1] * np.float64(scales[b]) - x[s0:s1])
+        assert err.max() <= 0.5 * scales[b] * (1 + 1e-6)  # half a step
+    z, zs = O.int8_block_codes(np.zeros((10, 4), np.float32), 8)
+    assert not z.any() and not zs.any()
+
+
+def _lowbit_case(seed, N=300, d=16, bq=64, bk=64):
+    rng = np.random.default_rng(seed)
+    q, k, v = (rng.standard_normal((N, d)) for _ in range(3))
+    n_q, n_k = -(-N // bq), -(-N // bk)
+    kept = rng.random((n_q, n_k)) < 0.6
+    kept[0] = False
+    kept[1] = True
+    idx, cnt = O.kept_to_index_list(kept[None, None])
+    return q, k, v, kept, idx[0, 0], cnt[0, 0]
+
+
+def test_lowbit_constant_v_and_empty_rows():
+    # V constant per channel: the e4m3 code of amax * 448 / amax is 448 exactly, so
+    # every dequantised row is the constant (up to the float32 rounding of the
+    # scale amax / 448, 2^-24 relative) and the normalised output is too
+    q, k, v, kept, idx, cnt = _lowbit_case(82)
+    v = np.tile(np.array([0.5, -1.25, 3.0, 0.0] * 4), (q.shape[0], 1))
+    o = O.lowbit_attention_head(q, k, v, idx, cnt, 64, 64, 0.25)
+    assert np.all(o[:64] == 0)                                 # empty list
+    np.testing.assert_allclose(o[64:], np.broadcast_to(v[0], o[64:].shape), rtol=1.2e-7, atol=0)
+
+
+def test_lowbit_is_close_to_exact_attention():
+    # quantisation moves scores by < 1% of their spread and weights / values by
+    # at most 2^-4 relative: the output stays near the exact masked attention
+    q, k, v, kept, idx, cnt = _lowbit_case(83, N=500, d=32)
+    o = O.lowbit_attention_head(q, k, v, idx, cnt, 64, 64, 1 / math.sqrt(32))
+    ref = O.masked_attention_head(q, k, v, kept, 64, 64, 1 / math.sqrt(32))
+    err = np.abs(o - ref)
+    assert err.max() < 0.15 and err.mean() < 0.02
+    # and the block order only changes rounding
+    idx2 = idx.copy()
+    for i in range(idx.shape[0]):
+        idx2[i, :cnt[i]] = idx[i, :cnt[i]][::-1]
+    o2 = O.lowbit_attention_head(q, k, v, idx2, cnt, 64, 64, 1 / math.sqrt(32))
+    assert np.abs(o2 - o).max() < 0.05
