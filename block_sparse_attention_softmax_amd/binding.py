@@ -25,7 +25,8 @@ EXPORTS = ("sparge_mask_workspace_bytes", "sparge_mask_predict",
            "sparge_attn_fwd_packed", "sparse_linear_workspace_bytes", "sparse_linear_attn_fwd",
            "sla2_mix_attn_fwd", "sparge_attn_fwd_lse", "sparge_attn_bwd_workspace_bytes",
            "sparge_attn_bwd", "sparse_linear_bwd_workspace_bytes", "sparse_linear_attn_bwd",
-           "sla2_mix_attn_bwd", "sparge_last_error")
+           "sla2_mix_attn_bwd", "sparge_attn_lowbit_workspace_bytes", "sparge_attn_fwd_lowbit",
+           "sparge_last_error")
 
 _lib = None
 
@@ -66,6 +67,10 @@ def lib() -> ctypes.CDLL:
         L.sparge_attn_bwd_workspace_bytes.restype = c_size
         L.sparge_attn_bwd.argtypes = [vp] * 8 + [c_int] * 6 + [c_float] + [vp] * 4 + [c_size, vp]
         L.sparge_attn_bwd.restype = c_int
+        L.sparge_attn_lowbit_workspace_bytes.argtypes = [c_int] * 6
+        L.sparge_attn_lowbit_workspace_bytes.restype = c_size
+        L.sparge_attn_fwd_lowbit.argtypes = [vp] * 5 + [c_int] * 6 + [c_float, vp, vp, c_size, vp]
+        L.sparge_attn_fwd_lowbit.restype = c_int
         L.sparse_linear_bwd_workspace_bytes.argtypes = [c_int] * 4
         L.sparse_linear_bwd_workspace_bytes.restype = c_size
         for f in (L.sparse_linear_attn_bwd, L.sla2_mix_attn_bwd):
@@ -241,6 +246,26 @@ def sparge_attn_bwd(q, k, v, o, d_o, lse, kv_idx, kv_cnt, block_q=128, block_k=6
                                  _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
                                  workspace.numel(), _stream(q)))
     return dq, dk, dv
+
+
+def lowbit_workspace_bytes(B, H, N, d, block_q=128, block_k=64) -> int:
+    return lib().sparge_attn_lowbit_workspace_bytes(B, H, N, d, block_q, block_k)
+
+
+def sparge_attn_fwd_lowbit(q, k, v, kv_idx, kv_cnt, block_q=128, block_k=64, scale=None,
+                           out=None, workspace=None):
+    """The sparse branch with INT8 Q/K and e4m3 P/V (see sparge.h)."""
+    B, H, N, d = _qkv(q, k, v)
+    o = torch.empty_like(q) if out is None else out
+    if scale is None:
+        scale = default_scale(d)
+    if workspace is None:
+        workspace = torch.empty(max(lowbit_workspace_bytes(B, H, N, d, block_q, block_k), 256),
+                                dtype=torch.uint8, device=q.device)
+    _check(lib().sparge_attn_fwd_lowbit(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_idx), _ptr(kv_cnt), B,
+                                        H, N, d, block_q, block_k, scale, _ptr(o),
+                                        _ptr(workspace), workspace.numel(), _stream(q)))
+    return o
 
 
 def linear_bwd_workspace_bytes(B, H, N, d) -> int:

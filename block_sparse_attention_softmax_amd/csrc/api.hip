@@ -345,6 +345,42 @@ int sparge_attn_bwd(const void* q, const void* k, const void* v, const void* o, 
                   workspace_bytes, stream);
 }
 
+size_t sparge_attn_lowbit_workspace_bytes(int B, int H, int N, int d, int block_q, int block_k) {
+  const std::string saved = g_last_error;
+  const int rc = check_shape(B, H, N, d, block_q, block_k);
+  g_last_error = saved;
+  if (rc != SPARGE_OK) return 0;
+  return sparge::lowbit_workspace_bytes(B, H, N, d, block_q);
+}
+
+int sparge_attn_fwd_lowbit(const void* q, const void* k, const void* v, const int32_t* kv_idx,
+                           const int32_t* kv_cnt, int B, int H, int N, int d, int block_q,
+                           int block_k, float scale, void* o, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  int rc = check_attn_args(q, k, v, kv_idx, kv_cnt, B, H, N, d, block_q, block_k, scale, o);
+  if (rc != SPARGE_OK) return rc;
+  if (!workspace) return fail(SPARGE_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned(workspace, 256)) return fail(SPARGE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (workspace_bytes < sparge::lowbit_workspace_bytes(B, H, N, d, block_q))
+    return fail(SPARGE_ERR_INVALID_ARG, "workspace too small");
+  sparge::LowbitLaunch a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.idx = kv_idx;
+  a.cnt = kv_cnt;
+  a.o = static_cast<uint16_t*>(o);
+  a.B = B; a.H = H; a.N = N; a.d = d; a.block_q = block_q;
+  a.n_q = ceil_div(N, block_q);
+  a.n_k = ceil_div(N, block_k);
+  a.scale = scale;
+  sparge::lowbit_layout(a, static_cast<unsigned char*>(workspace));
+  const hipError_t e = sparge::launch_lowbit(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "sparge_attn_fwd_lowbit launch");
+  return SPARGE_OK;
+}
+
 size_t sparse_linear_bwd_workspace_bytes(int B, int H, int N, int d) {
   const std::string saved = g_last_error;
   const int rc = check_shape(B, H, N, d, d == 64 ? 64 : 128, 64);

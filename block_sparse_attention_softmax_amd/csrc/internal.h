@@ -114,6 +114,27 @@ struct BwdLaunch {
 };
 hipError_t launch_bwd(const BwdLaunch& a, hipStream_t s);
 size_t bwd_workspace_bytes(int B, int H, int N, int d, int block_q, bool linear = false);
+// low-bit sparse branch: INT8 Q, K per block, e4m3 V per channel, e4m3 P
+struct LowbitLaunch {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* idx;
+  const int32_t* cnt;
+  uint16_t* o;
+  int B, H, N, d, block_q, n_q, n_k;
+  float scale;
+  // workspace (lowbit_layout)
+  int8_t* qc;       // [B*H, N, d] INT8 codes of Q
+  int8_t* kc;       // [B*H, N, d] INT8 codes of K
+  float* qs;        // [B*H, n_q] scales of Q
+  float* ks;        // [B*H, n_k] scales of K
+  uint32_t* vmax;   // [B*H, d] amax of each V channel (float bits)
+  uint8_t* vt8;     // [B*H, n_k, d, 64] e4m3 codes of V^T, packed
+};
+hipError_t launch_lowbit(const LowbitLaunch& a, hipStream_t s);
+size_t lowbit_workspace_bytes(int B, int H, int N, int d, int block_q);
+void lowbit_layout(LowbitLaunch& a, unsigned char* workspace);
 size_t attn_workspace_bytes(int B, int H, int N, int d);    // packed V
 size_t linear_workspace_bytes(int B, int H, int N, int d);  // packed V + linear branch
 

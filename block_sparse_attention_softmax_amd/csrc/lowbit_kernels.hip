@@ -1,0 +1,364 @@
+// Low-bit sparse branch (SLA2 page, section 2C: Q, K, P and V quantised in
+// the forward pass of the sparse attention):
+//
+//   Q, K  INT8 codes, one float32 scale per block (query blocks of block_q
+//         rows, key blocks of 64): scale = amax / 127, code = rint(x * 127/amax)
+//   V     FP8 e4m3 (OCP e4m3fn) codes of x * 448/amax_c, one scale per
+//         (head, channel)
+//   P     e4m3 codes of 448 p, p = exp(scale (s - m)) against the exact
+//         running row maximum m (so p <= 1), blocks in list order
+//   O     = sum p~ v~ / sum p~
+//
+// S^T = K Q^T runs on v_mfma_i32_32x32x32_i8 (exact integer sums), the
+// product O^T += V^T P^T on v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales
+// (one instruction per 32 channels covers the block's 64 keys). As in the
+// bf16 kernel, the transposed products keep one query per lane, and V^T is
+// packed so that the P^T codes of a lane feed the B operand unchanged: for
+// lane half h the 64-key operand index 32 h + i holds key
+// 32 (i / 16) + 8 ((i % 16) / 4) + 4 h + i % 4, the key whose score register
+// 16 (i / 16) + i % 16 of that lane holds.
+#include "internal.h"
+#include "tiles.h"
+
+namespace sparge {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+constexpr float kE4m3Max = 448.0f;
+
+__global__ __launch_bounds__(256) void fill_u32_zero_kernel(uint32_t* __restrict__ p, size_t n) {
+  const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (e < n) p[e] = 0u;
+}
+
+// --------------------------------------------------------- quantisation
+// INT8 codes of one block of rows of a [rows][D] bf16 array and its scale.
+// One workgroup (256 threads) per (block, b*h).
+template <int D>
+__global__ __launch_bounds__(256) void quant_int8_kernel(const uint16_t* __restrict__ x,
+                                                         int8_t* __restrict__ codes,
+                                                         float* __restrict__ scales, int N,
+                                                         int block, int nblocks) {
+  __shared__ float red[4];
+  const int bi = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+  const int r0 = bi * block, rows = min(block, N - r0);
+  const size_t base = ((size_t)bh * N + r0) * D;
+  const int n8 = rows * D / 8;
+  float amax = 0.0f;
+  for (int p = t; p < n8; p += 256) {
+    const uint4 u = *reinterpret_cast<const uint4*>(x + base + (size_t)p * 8);
+    const uint32_t* w = &u.x;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(w[e])), fabsf(bf16_hi(w[e]))));
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  if ((t & 63) == 0) red[t >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+  if (t == 0) scales[(size_t)bh * nblocks + bi] = amax / 127.0f;
+  for (int p = t; p < n8; p += 256) {
+    const uint4 u = *reinterpret_cast<const uint4*>(x + base + (size_t)p * 8);
+    const uint32_t* w = &u.x;
+    uint32_t out[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const uint32_t ww = w[2 * h + e];
+        const int lo = (int)fminf(fmaxf(rintf(bf16_lo(ww) * inv), -127.0f), 127.0f);
+        const int hi = (int)fminf(fmaxf(rintf(bf16_hi(ww) * inv), -127.0f), 127.0f);
+        word |= ((uint32_t)(lo & 0xFF) | ((uint32_t)(hi & 0xFF) << 8)) << (16 * e);
+      }
+      out[h] = word;
+    }
+    *reinterpret_cast<uint2*>(codes + base + (size_t)p * 8) = make_uint2(out[0], out[1]);
+  }
+}
+
+// amax over the rows of each channel of V: as float bits (non-negative floats
+// order like their bits), max-combined into vmax[bh][c], which starts at 0.
+// Grid (row chunks of 256, b*h), D threads, thread c walks its chunk.
+template <int D>
+__global__ __launch_bounds__(D) void v_amax_kernel(const uint16_t* __restrict__ v,
+                                                   uint32_t* __restrict__ vmax, int N) {
+  const int bh = blockIdx.y, c = threadIdx.x;
+  const int r0 = blockIdx.x * 256, r1 = min(r0 + 256, N);
+  float amax = 0.0f;
+  for (int r = r0; r < r1; ++r)
+    amax = fmaxf(amax, fabsf(__uint_as_float((uint32_t)v[((size_t)bh * N + r) * D + c] << 16)));
+  atomicMax(&vmax[(size_t)bh * D + c], __float_as_uint(amax));
+}
+
+// Slot of the packed fp8 V^T block (see the file comment) -> key.
+__device__ __forceinline__ int fp8_slot_key(int slot) {
+  const int h = slot >> 5, i = slot & 31;
+  return 32 * (i >> 4) + 8 * ((i & 15) >> 2) + 4 * h + (i & 3);
+}
+
+// vt8[bh][j][c][slot] = e4m3(V[bh][64 j + key(slot)][c] * 448 / amax_c), zero
+// past N. Grid (key blocks, b*h), 256 threads; each thread writes 4-byte
+// groups of slots of one channel row.
+template <int D>
+__global__ __launch_bounds__(256) void pack_v_fp8_kernel(const uint16_t* __restrict__ v,
+                                                         const uint32_t* __restrict__ vmax,
+                                                         uint8_t* __restrict__ vt8, int N,
+                                                         int n_k) {
+  const int j = blockIdx.x, bh = blockIdx.y;
+  for (int p = threadIdx.x; p < D * 16; p += 256) {
+    const int c = p / 16, s0 = (p % 16) * 4;
+    const float amax = __uint_as_float(vmax[(size_t)bh * D + c]);
+    const float inv = amax > 0.0f ? kE4m3Max / amax : 0.0f;
+    float x[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int key = j * BK + fp8_slot_key(s0 + e);
+      x[e] = key < N ? __uint_as_float((uint32_t)v[((size_t)bh * N + key) * D + c] << 16) * inv
+                     : 0.0f;
+    }
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], w, true);
+    *reinterpret_cast<int*>(vt8 + (((size_t)bh * n_k + j) * D + c) * BK + s0) = w;
+  }
+}
+
+// ------------------------------------------------------------ attention
+// LDS tiles: K codes [64 keys][D bytes] and packed V^T codes [D][64 bytes],
+// 16-byte chunks XOR-swizzled so that the 32 rows an operand read touches
+// cover all banks: rows of R bytes share a 256-byte bank window 256 / R at a
+// time, so chunk c of row r is stored at c ^ ((r / (256 / R)) mod (R / 16)).
+template <int R>
+struct Tile8 {
+  static constexpr int CPR = R / 16;          // chunks per row
+  static constexpr int RPW = 256 / R;         // rows per bank window
+  static constexpr int BYTES = 64 * R;        // K tile (64 rows); V^T tile has D rows of 64 bytes
+  __device__ static constexpr int swz(int row, int chunk) { return chunk ^ ((row / RPW) & (CPR - 1)); }
+};
+
+template <int D, int BQ>
+__global__ __launch_bounds__(BQ * 2, 2) void sparse_attn_lowbit_kernel(
+    const int8_t* __restrict__ qc, const float* __restrict__ qs, const int8_t* __restrict__ kc,
+    const float* __restrict__ ks, const uint8_t* __restrict__ vt8,
+    const uint32_t* __restrict__ vmax, const int32_t* __restrict__ kv_idx,
+    const int32_t* __restrict__ kv_cnt, uint16_t* __restrict__ o, int N, int n_q, int n_k,
+    int total, float c) {
+  using TK = Tile8<D>;   // K rows: D bytes
+  using TV = Tile8<BK>;  // V^T rows: 64 bytes
+  constexpr int NT = BQ * 2, DT = D / 32, KS = D / 32;
+  constexpr int KBYTES = BK * D, VBYTES = D * BK;
+  constexpr int KU = KBYTES / 16 / NT, VU = VBYTES / 16 / NT;  // 16-byte copies per thread
+  static_assert(KBYTES % (16 * NT) == 0 && VBYTES % (16 * NT) == 0, "whole copies per thread");
+  __shared__ __align__(16) unsigned char smem[2 * (KBYTES + VBYTES)];
+
+  const int tile = xcd_remap(blockIdx.x, total);
+  const int bh = tile / n_q, qi = tile % n_q;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h2 = lane >> 5, l32 = lane & 31;
+  const size_t head = (size_t)bh * N * D;
+  const int qrow = qi * BQ + wave * 32 + l32;
+
+  v4i qf[KS];  // Q codes of this lane's query, d = 32 s + 16 h2 .. +15
+  {
+    const int8_t* qp = qc + head + (size_t)min(qrow, N - 1) * D + 16 * h2;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[s] = *reinterpret_cast<const v4i*>(qp + 32 * s);
+  }
+  const float sq = qs[(size_t)bh * n_q + qi];
+  const int count = min(max(kv_cnt[tile], 0), n_k);
+  const int32_t* ids = kv_idx + (size_t)tile * n_k;
+  auto jat = [&](int e) { return min(max(ids[e], 0), n_k - 1); };
+
+  // per-thread copy offsets within a tile
+  uint32_t ksrc[KU], vsrc[VU];
+  int krow[KU];
+#pragma unroll
+  for (int u = 0; u < KU; ++u) {
+    const int p = u * NT + threadIdx.x, r = p / TK::CPR;
+    krow[u] = r;
+    ksrc[u] = (uint32_t)(r * D + TK::swz(r, p % TK::CPR) * 16);
+  }
+#pragma unroll
+  for (int u = 0; u < VU; ++u) {
+    const int p = u * NT + threadIdx.x, r = p / TV::CPR;
+    vsrc[u] = (uint32_t)(r * BK + TV::swz(r, p % TV::CPR) * 16);
+  }
+  auto issue = [&](int j, int b) {  // K rows past N read row N - 1 (masked below)
+    const int key0 = j * BK;
+    const int8_t* kb = kc + head + (size_t)key0 * D;
+    const uint8_t* vb = vt8 + ((size_t)bh * n_k + j) * VBYTES;
+    unsigned char* kd = smem + b * (KBYTES + VBYTES);
+    unsigned char* vd = kd + KBYTES;
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      const uint32_t back = (uint32_t)max(key0 + krow[u] - (N - 1), 0) * D;
+      dma16(kb + ksrc[u] - back, kd + (u * NT + wave * 64) * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < VU; ++u) dma16(vb + vsrc[u], vd + (u * NT + wave * 64) * 16);
+  };
+
+  floatx16 oacc[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[i][r] = 0.0f;
+  float m = -INFINITY, lsum = 0.0f;  // running max of s; sum of P codes' values
+
+  if (count > 0) issue(jat(0), 0);
+  for (int e = 0; e < count; ++e) {
+    const int j = jat(e);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of block e landed
+    __syncthreads();                     // all copies landed; the other buffer is free
+    if (e + 1 < count) issue(jat(e + 1), (e + 1) & 1);
+    const unsigned char* kt = smem + (e & 1) * (KBYTES + VBYTES);
+    const unsigned char* vtl = kt + KBYTES;
+
+    // S^T = K Q^T in exact integers, then s = dot * (sq sk) in float32
+    v16i si[2];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) si[tau][r] = 0;
+      const int kr = 32 * tau + l32;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const v4i a = *reinterpret_cast<const v4i*>(kt + kr * D + TK::swz(kr, 2 * s + h2) * 16);
+        si[tau] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qf[s], si[tau], 0, 0, 0);
+      }
+    }
+    const float sqk = sq * ks[(size_t)bh * n_k + j];
+    const int nvalid = N - j * BK;
+    float sv[2][16];
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * tau + 8 * (r >> 2) + 4 * h2 + (r & 3);
+        sv[tau][r] = key < nvalid ? (float)si[tau][r] * sqk : -INFINITY;
+        mloc = fmaxf(mloc, sv[tau][r]);
+      }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    const float m_new = fmaxf(m, mloc);
+    if (__any(m_new > m)) {  // exact running maximum: rescale whenever it rises
+      const float f = m_new > m ? __builtin_amdgcn_exp2f((m - m_new) * c) : 1.0f;
+      lsum *= f;
+#pragma unroll
+      for (int i = 0; i < DT; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[i][r] *= f;
+      m = m_new;
+    }
+    // P codes: e4m3(448 p), four per dword, in register order
+    v8i pb;
+    const float mc = m * c;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const int tau = w >> 2, r0 = (w & 3) * 4;
+      float p[4];
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2)
+        p[e2] = __builtin_amdgcn_exp2f(fmaf(sv[tau][r0 + e2], c, -mc)) * kE4m3Max;
+      int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+      word = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
+      pb[w] = word;
+      lsum += (__builtin_amdgcn_cvt_f32_fp8(word, 0) + __builtin_amdgcn_cvt_f32_fp8(word, 1)) +
+              (__builtin_amdgcn_cvt_f32_fp8(word, 2) + __builtin_amdgcn_cvt_f32_fp8(word, 3));
+    }
+    // O^T += V^T P^T, one instruction per 32 channels covers the 64 keys
+#pragma unroll
+    for (int i = 0; i < DT; ++i) {
+      const int row = 32 * i + l32;
+      const v4i a0 = *reinterpret_cast<const v4i*>(vtl + row * BK + TV::swz(row, 2 * h2) * 16);
+      const v4i a1 = *reinterpret_cast<const v4i*>(vtl + row * BK + TV::swz(row, 2 * h2 + 1) * 16);
+      const v8i a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      oacc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb, oacc[i], 0, 0, 0, 127, 0,
+                                                                 127);
+    }
+  }
+
+  // O = sv_c * sum(codeP codeV) / sum(codeP) (the 448s cancel)
+  const float ltot = lsum + __shfl_xor(lsum, 32);
+  const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
+  if (qrow < N) {
+    uint16_t* orow = o + head + (size_t)qrow * D;
+#pragma unroll
+    for (int i = 0; i < DT; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * i + 8 * g + 4 * h2;
+        float y[4];
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const float sv_c = __uint_as_float(vmax[(size_t)bh * D + d0 + e2]) / kE4m3Max;
+          y[e2] = oacc[i][4 * g + e2] * sv_c * inv;
+        }
+        uint2 pk;
+        pk.x = pack2_bf16(y[0], y[1]);
+        pk.y = pack2_bf16(y[2], y[3]);
+        *reinterpret_cast<uint2*>(orow + d0) = pk;
+      }
+  }
+}
+
+template <int D, int BQ>
+hipError_t launch_lowbit_t(const LowbitLaunch& a, hipStream_t s) {
+  const int BH = a.B * a.H, total = BH * a.n_q;
+  hipLaunchKernelGGL((quant_int8_kernel<D>), dim3(a.n_q, BH), dim3(256), 0, s, a.q, a.qc, a.qs,
+                     a.N, BQ, a.n_q);
+  hipLaunchKernelGGL((quant_int8_kernel<D>), dim3(a.n_k, BH), dim3(256), 0, s, a.k, a.kc, a.ks,
+                     a.N, BK, a.n_k);
+  const size_t nv = (size_t)BH * D;
+  hipLaunchKernelGGL(fill_u32_zero_kernel, dim3((unsigned)((nv + 255) / 256)), dim3(256), 0, s,
+                     a.vmax, nv);
+  hipLaunchKernelGGL((v_amax_kernel<D>), dim3((a.N + 255) / 256, BH), dim3(D), 0, s, a.v, a.vmax,
+                     a.N);
+  hipLaunchKernelGGL((pack_v_fp8_kernel<D>), dim3(a.n_k, BH), dim3(256), 0, s, a.v, a.vmax,
+                     a.vt8, a.N, a.n_k);
+  hipLaunchKernelGGL((sparse_attn_lowbit_kernel<D, BQ>), dim3(total), dim3(BQ * 2), 0, s, a.qc,
+                     a.qs, a.kc, a.ks, a.vt8, a.vmax, a.idx, a.cnt, a.o, a.N, a.n_q, a.n_k, total,
+                     a.scale * 1.4426950408889634f);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t lowbit_workspace_bytes(int B, int H, int N, int d, int block_q) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t BH = (size_t)B * H, n_q = (N + block_q - 1) / block_q, n_k = (N + BK - 1) / BK;
+  return 2 * up(BH * N * d) + up(BH * n_q * 4) + up(BH * n_k * 4) + up(BH * d * 4) +
+         up(BH * n_k * BK * d);
+}
+
+void lowbit_layout(LowbitLaunch& a, unsigned char* w) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t BH = (size_t)a.B * a.H;
+  size_t off = 0;
+  a.qc = reinterpret_cast<int8_t*>(w + off);
+  off += up(BH * a.N * a.d);
+  a.kc = reinterpret_cast<int8_t*>(w + off);
+  off += up(BH * a.N * a.d);
+  a.qs = reinterpret_cast<float*>(w + off);
+  off += up(BH * a.n_q * 4);
+  a.ks = reinterpret_cast<float*>(w + off);
+  off += up(BH * a.n_k * 4);
+  a.vmax = reinterpret_cast<uint32_t*>(w + off);
+  off += up(BH * a.d * 4);
+  a.vt8 = w + off;
+}
+
+hipError_t launch_lowbit(const LowbitLaunch& a, hipStream_t s) {
+  if (a.d == 128 && a.block_q == 128) return launch_lowbit_t<128, 128>(a, s);
+  if (a.d == 128 && a.block_q == 64) return launch_lowbit_t<128, 64>(a, s);
+  if (a.d == 64 && a.block_q == 128) return launch_lowbit_t<64, 128>(a, s);
+  return launch_lowbit_t<64, 64>(a, s);
+}
+
+}  // namespace sparge

@@ -277,6 +277,35 @@ int sla2_mix_attn_fwd(const void* q, const void* k, const void* v, const int32_t
                       int block_q, int block_k, float scale, float drop_below, void* o,
                       float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Device workspace (bytes) of sparge_attn_fwd_lowbit: INT8 codes of Q and K,
+ * their per-block scales, the per-channel scales of V and its packed e4m3
+ * codes (about 3 * B*H*N*d bytes). Returns 0 for arguments it would reject. */
+size_t sparge_attn_lowbit_workspace_bytes(int B, int H, int N, int d, int block_q,
+                                          int block_k);
+
+/* The sparse branch with low-bit operands (SLA2 page, section 2C: Q, K, P and
+ * V quantised in the forward pass), over the key blocks of kv_idx / kv_cnt:
+ *   Q, K : INT8, one float32 scale per block (block_q query rows; 64 keys):
+ *          scale = amax / 127, code = round-half-even(x * (127 / amax)) in float32;
+ *   V    : FP8 e4m3 (OCP e4m3fn, largest 448), one scale per (b, h, channel):
+ *          code = e4m3(x * (448 / amax_c)), round to nearest even;
+ *   S    : exact integer dot products of the codes times (scale_q scale_k);
+ *   P    : e4m3 codes of 448 exp(scale (S - m)), m the exact running row
+ *          maximum over the blocks visited so far, in list order (P <= 1);
+ *   O    = sum P~ V~ / sum P~ over the listed blocks, rounded to bf16
+ *          (zeros for an empty list).
+ * S^T runs on INT8 MFMA (v_mfma_i32_32x32x32_i8) and P V on FP8 MFMA
+ * (v_mfma_scale_f32_32x32x64_f8f6f4, unit scales), float32 accumulation. The
+ * result depends on the order of each row's list only through rounding.
+ *
+ *  workspace : at least sparge_attn_lowbit_workspace_bytes(), 256-byte
+ *              aligned; contents on entry do not matter.
+ *  Other arguments as for sparge_attn_fwd. */
+int sparge_attn_fwd_lowbit(const void* q, const void* k, const void* v,
+                           const int32_t* kv_idx, const int32_t* kv_cnt, int B, int H, int N,
+                           int d, int block_q, int block_k, float scale, void* o,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 /* Device workspace (bytes) of sparse_linear_attn_bwd and sla2_mix_attn_bwd:
  * that of sparge_attn_bwd, plus the linear branch's packed V and phi(K), its
  * totals, the scaled dO of the mix, float32 dQ, dK, dV of the branch and one

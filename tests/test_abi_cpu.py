@@ -235,3 +235,25 @@ def test_linear_backward_workspace_and_rejections():
     a2 = dict(args)
     a2.update(alpha=ctypes.c_void_p(0x10004))  # 4-byte aligned: enough for the added form only
     assert L.sla2_mix_attn_bwd(*a2.values()) == -1
+
+
+def test_lowbit_workspace_and_rejections():
+    L = binding.lib()
+    up = lambda x: (x + 255) // 256 * 256
+    B, H, N, d = 1, 12, 32760, 128
+    n_q, n_k = math.ceil(N / 128), math.ceil(N / 64)
+    BH = B * H
+    want = (2 * up(BH * N * d) + up(BH * n_q * 4) + up(BH * n_k * 4) + up(BH * d * 4)
+            + up(BH * n_k * 64 * d))
+    assert L.sparge_attn_lowbit_workspace_bytes(B, H, N, d, 128, 64) == want
+    assert L.sparge_attn_lowbit_workspace_bytes(1, 1, 100, 96, 128, 64) == 0
+    args = [A, A, A, A, A, 1, 2, 1024, 64, 64, 64, 0.125, A, A, 1 << 30, None]
+    bad = list(args)
+    bad[13] = ctypes.c_void_p(0x10010)                   # 16- but not 256-byte aligned
+    assert L.sparge_attn_fwd_lowbit(*bad) == -1
+    bad = list(args)
+    bad[14] = 1024
+    assert L.sparge_attn_fwd_lowbit(*bad) == -1
+    bad = list(args)
+    bad[8] = 80
+    assert L.sparge_attn_fwd_lowbit(*bad) == -2
