@@ -17,6 +17,8 @@
 // lane half h the 64-key operand index 32 h + i holds key
 // 32 (i / 16) + 8 ((i % 16) / 4) + 4 h + i % 4, the key whose score register
 // 16 (i / 16) + i % 16 of that lane holds.
+#include <climits>
+
 #include "internal.h"
 #include "tiles.h"
 
@@ -84,16 +86,34 @@ __global__ __launch_bounds__(256) void quant_int8_kernel(const uint16_t* __restr
 
 // amax over the rows of each channel of V: as float bits (non-negative floats
 // order like their bits), max-combined into vmax[bh][c], which starts at 0.
-// Grid (row chunks of 256, b*h), D threads, thread c walks its chunk.
+// Grid (chunks of 512 rows, b*h), 256 threads: D/8 threads cover a row with
+// 16-byte loads, 256/(D/8) rows at a time; the row lanes meet through LDS.
 template <int D>
-__global__ __launch_bounds__(D) void v_amax_kernel(const uint16_t* __restrict__ v,
-                                                   uint32_t* __restrict__ vmax, int N) {
-  const int bh = blockIdx.y, c = threadIdx.x;
-  const int r0 = blockIdx.x * 256, r1 = min(r0 + 256, N);
-  float amax = 0.0f;
-  for (int r = r0; r < r1; ++r)
-    amax = fmaxf(amax, fabsf(__uint_as_float((uint32_t)v[((size_t)bh * N + r) * D + c] << 16)));
-  atomicMax(&vmax[(size_t)bh * D + c], __float_as_uint(amax));
+__global__ __launch_bounds__(256) void v_amax_kernel(const uint16_t* __restrict__ v,
+                                                     uint32_t* __restrict__ vmax, int N) {
+  constexpr int CG = D / 8, RL = 256 / CG;  // channel groups, row lanes
+  __shared__ float part[RL][D];
+  const int bh = blockIdx.y, t = threadIdx.x, cg = t % CG, rl = t / CG;
+  const int r0 = blockIdx.x * 512, r1 = min(r0 + 512, N);
+  float mx[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+  for (int r = r0 + rl; r < r1; r += RL) {
+    const uint4 u = *reinterpret_cast<const uint4*>(v + ((size_t)bh * N + r) * D + 8 * cg);
+    const uint32_t* w = &u.x;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      mx[2 * e] = fmaxf(mx[2 * e], fabsf(bf16_lo(w[e])));
+      mx[2 * e + 1] = fmaxf(mx[2 * e + 1], fabsf(bf16_hi(w[e])));
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) part[rl][8 * cg + e] = mx[e];
+  __syncthreads();
+  if (t < D) {
+    float m = 0.0f;
+#pragma unroll
+    for (int l = 0; l < RL; ++l) m = fmaxf(m, part[l][t]);
+    atomicMax(&vmax[(size_t)bh * D + t], __float_as_uint(m));
+  }
 }
 
 // Slot of the packed fp8 V^T block (see the file comment) -> key.
@@ -103,25 +123,36 @@ __device__ __forceinline__ int fp8_slot_key(int slot) {
 }
 
 // vt8[bh][j][c][slot] = e4m3(V[bh][64 j + key(slot)][c] * 448 / amax_c), zero
-// past N. Grid (key blocks, b*h), 256 threads; each thread writes 4-byte
-// groups of slots of one channel row.
+// past N. Grid (key blocks, b*h), 256 threads: the 64 V rows are staged in
+// LDS with 16-byte loads, then each thread writes 4-byte groups of slots of
+// one channel row.
 template <int D>
 __global__ __launch_bounds__(256) void pack_v_fp8_kernel(const uint16_t* __restrict__ v,
                                                          const uint32_t* __restrict__ vmax,
                                                          uint8_t* __restrict__ vt8, int N,
                                                          int n_k) {
-  const int j = blockIdx.x, bh = blockIdx.y;
-  for (int p = threadIdx.x; p < D * 16; p += 256) {
+  __shared__ uint16_t vs[BK * (D + 2)];  // rows padded by one word against bank conflicts
+  const int j = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+  for (int p = t; p < BK * D / 8; p += 256) {
+    const int r = p / (D / 8), c8 = (p % (D / 8)) * 8;
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if (j * BK + r < N) u = *reinterpret_cast<const uint4*>(v + ((size_t)bh * N + j * BK + r) * D + c8);
+    const uint32_t* w = &u.x;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      vs[r * (D + 2) + c8 + 2 * e] = (uint16_t)(w[e] & 0xFFFFu);
+      vs[r * (D + 2) + c8 + 2 * e + 1] = (uint16_t)(w[e] >> 16);
+    }
+  }
+  __syncthreads();
+  for (int p = t; p < D * 16; p += 256) {
     const int c = p / 16, s0 = (p % 16) * 4;
     const float amax = __uint_as_float(vmax[(size_t)bh * D + c]);
     const float inv = amax > 0.0f ? kE4m3Max / amax : 0.0f;
     float x[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int key = j * BK + fp8_slot_key(s0 + e);
-      x[e] = key < N ? __uint_as_float((uint32_t)v[((size_t)bh * N + key) * D + c] << 16) * inv
-                     : 0.0f;
-    }
+    for (int e = 0; e < 4; ++e)
+      x[e] = __uint_as_float((uint32_t)vs[fp8_slot_key(s0 + e) * (D + 2) + c] << 16) * inv;
     int w = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], w, true);
     *reinterpret_cast<int*>(vt8 + (((size_t)bh * n_k + j) * D + c) * BK + s0) = w;
@@ -233,19 +264,21 @@ __global__ __launch_bounds__(BQ * 2, 2) void sparse_attn_lowbit_kernel(
         si[tau] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qf[s], si[tau], 0, 0, 0);
       }
     }
+    // s = dot * (sq sk): the row maximum is taken on the integers (the scale is
+    // positive), and 448 p = 2^(dot (sq sk c) - m c + log2 448) in one FMA
     const float sqk = sq * ks[(size_t)bh * n_k + j];
-    const int nvalid = N - j * BK;
-    float sv[2][16];
-    float mloc = -INFINITY;
+    const int nvalid = N - j * BK;  // keys past N (last block only) take no part
+    const bool tail = nvalid < BK;
+    int dmax = INT_MIN;
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = 32 * tau + 8 * (r >> 2) + 4 * h2 + (r & 3);
-        sv[tau][r] = key < nvalid ? (float)si[tau][r] * sqk : -INFINITY;
-        mloc = fmaxf(mloc, sv[tau][r]);
+        dmax = max(dmax, (tail && key >= nvalid) ? INT_MIN : si[tau][r]);
       }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    dmax = max(dmax, __shfl_xor(dmax, 32));
+    const float mloc = (float)dmax * sqk;
     const float m_new = fmaxf(m, mloc);
     if (__any(m_new > m)) {  // exact running maximum: rescale whenever it rises
       const float f = m_new > m ? __builtin_amdgcn_exp2f((m - m_new) * c) : 1.0f;
@@ -258,19 +291,23 @@ __global__ __launch_bounds__(BQ * 2, 2) void sparse_attn_lowbit_kernel(
     }
     // P codes: e4m3(448 p), four per dword, in register order
     v8i pb;
-    const float mc = m * c;
+    const float sc = sqk * c, bias = 8.807354922057604f - m * c;  // log2(448) - m c
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
       const int tau = w >> 2, r0 = (w & 3) * 4;
       float p[4];
 #pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2)
-        p[e2] = __builtin_amdgcn_exp2f(fmaf(sv[tau][r0 + e2], c, -mc)) * kE4m3Max;
+      for (int e2 = 0; e2 < 4; ++e2) {
+        p[e2] = __builtin_amdgcn_exp2f(fmaf((float)si[tau][r0 + e2], sc, bias));
+        if (tail && 32 * tau + 8 * ((r0 + e2) >> 2) + 4 * h2 + ((r0 + e2) & 3) >= nvalid)
+          p[e2] = 0.0f;
+      }
       int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
       word = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
       pb[w] = word;
-      lsum += (__builtin_amdgcn_cvt_f32_fp8(word, 0) + __builtin_amdgcn_cvt_f32_fp8(word, 1)) +
-              (__builtin_amdgcn_cvt_f32_fp8(word, 2) + __builtin_amdgcn_cvt_f32_fp8(word, 3));
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
+      lsum += (lo[0] + lo[1]) + (hi[0] + hi[1]);
     }
     // O^T += V^T P^T, one instruction per 32 channels covers the 64 keys
 #pragma unroll
@@ -318,8 +355,8 @@ hipError_t launch_lowbit_t(const LowbitLaunch& a, hipStream_t s) {
   const size_t nv = (size_t)BH * D;
   hipLaunchKernelGGL(fill_u32_zero_kernel, dim3((unsigned)((nv + 255) / 256)), dim3(256), 0, s,
                      a.vmax, nv);
-  hipLaunchKernelGGL((v_amax_kernel<D>), dim3((a.N + 255) / 256, BH), dim3(D), 0, s, a.v, a.vmax,
-                     a.N);
+  hipLaunchKernelGGL((v_amax_kernel<D>), dim3((a.N + 511) / 512, BH), dim3(256), 0, s, a.v,
+                     a.vmax, a.N);
   hipLaunchKernelGGL((pack_v_fp8_kernel<D>), dim3(a.n_k, BH), dim3(256), 0, s, a.v, a.vmax,
                      a.vt8, a.N, a.n_k);
   hipLaunchKernelGGL((sparse_attn_lowbit_kernel<D, BQ>), dim3(total), dim3(BQ * 2), 0, s, a.qc,
