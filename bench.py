@@ -334,6 +334,39 @@ def main():
         "vs_sparse_bwd": round(e0.elapsed_time(e1) / n_b / backward["headline"]["bwd_ms"], 3)}
     del lbws
 
+    # the low-bit sparse branch (INT8 Q/K, e4m3 P/V) on the same masks: whole call
+    # (quantisation of Q, K and V included) against the bf16 attention call
+    lowbit = {}
+    lws8 = torch.empty(S.lowbit_workspace_bytes(B, H, N, d, wl.block_q, wl.block_k),
+                       dtype=torch.uint8, device=dev)
+    for name, kfrac, pm in (("headline", wl.k_frac, wl.p_mass), ("p0_k10", 0.10, 0.0),
+                            ("p0_k5", 0.05, 0.0)):
+        S.sparge_mask_predict(q, k, wl.block_q, wl.block_k, kfrac, pm, wl.scale, workspace=ws,
+                              out=(bits, idx, cnt))
+        c_np, i_np = cnt.cpu().numpy(), idx.cpu().numpy()
+        kf_lb = kept_flops(c_np, i_np, N, d, wl.block_q, wl.block_k)
+        res = {}
+        for tag, fn in (("lowbit", lambda: S.sparge_attn_fwd_lowbit(
+                             q, k, v, idx, cnt, wl.block_q, wl.block_k, wl.scale, out=o,
+                             workspace=lws8)),
+                        ("bf16", lambda: S.sparge_attn_fwd(q, k, v, idx, cnt, wl.block_q,
+                                                           wl.block_k, wl.scale, out=o,
+                                                           workspace=aws))):
+            fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            n_l = max(5, args.steps // 2)
+            e0.record()
+            for _ in range(n_l):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            res[tag] = e0.elapsed_time(e1) / n_l
+        lowbit[name] = {"k": kfrac, "p": pm, "lowbit_call_ms": round(res["lowbit"], 4),
+                        "bf16_call_ms": round(res["bf16"], 4),
+                        "lowbit_kept_tops": round(kf_lb / res["lowbit"] / 1e9, 1)}
+    del lws8
+
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl, Q, K, V, args.cpu_blocks)
 
     line = {
@@ -360,6 +393,7 @@ def main():
         "sparse_linear": linear,
         "sla2_salad": sla2,
         "backward": backward,
+        "lowbit": lowbit,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
