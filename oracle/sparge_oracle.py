@@ -677,3 +677,81 @@ def lowbit_attention_head(q, k, v, idx_rows, cnt_rows, block_q: int, block_k: in
             acc += p8 @ v_deq[k0:k1]
         out[s0:s1] = acc / l[:, None] if cnt_rows[i] > 0 else 0.0
     return out
+
+
+# ------------------------------------------------- SVG2 semantic permutation
+# "Sparse VideoGen2" page, section 2A: Q and K tokens are clustered
+# independently by k-means into C_q and C_k clusters and permuted so that each
+# cluster is contiguous (the output is permuted back, so attention itself is
+# unchanged); section 2B: scores between cluster centroids stand in for the
+# attention scores, clusters are sorted by them and taken in order until the
+# cumulative score reaches p. Readings of what the page leaves open: Lloyd's
+# k-means with the initial centroids at tokens floor(c N / C), a fixed number
+# of iterations, squared Euclidean distance in float64 with ties to the lower
+# cluster, an empty cluster keeping its centroid, centroids the float64 mean of
+# their members summed in token order; the centroid score has the attention's
+# scale, and a key cluster's probability is weighted by its size (softmax of
+# s + ln |cluster|, empty clusters excluded), so that a cluster stands for its
+# tokens; the selection is the hybrid rule with Top-k reduced to one cluster.
+def kmeans_assign(x: np.ndarray, cent: np.ndarray) -> np.ndarray:
+    """argmin_c |x - c|^2 per row (float64), ties to the lower c: computed as
+    |c|^2 - 2 x.c, the part that depends on c."""
+    d2 = (cent * cent).sum(axis=1)[None, :] - 2.0 * (x @ cent.T)
+    return np.argmin(d2, axis=1)
+
+
+def kmeans_update(x: np.ndarray, assign: np.ndarray, cent: np.ndarray) -> np.ndarray:
+    """Mean of each cluster's members, summed in token order; an empty
+    cluster keeps its centroid."""
+    new = cent.copy()
+    for c in range(cent.shape[0]):
+        members = np.nonzero(assign == c)[0]
+        if members.size:
+            new[c] = np.cumsum(x[members], axis=0)[-1] / members.size
+    return new
+
+
+def kmeans(x: np.ndarray, n_clusters: int, iters: int):
+    """Lloyd's k-means on the rows of x (float64): `iters` rounds of assign then
+    update from centroids at rows floor(c N / C), then a final assignment.
+    Returns (assignment, centroids)."""
+    N = x.shape[0]
+    cent = x[(np.arange(n_clusters) * N) // n_clusters].copy()
+    for _ in range(iters):
+        cent = kmeans_update(x, kmeans_assign(x, cent), cent)
+    return kmeans_assign(x, cent), cent
+
+
+def svg2_permutation(assign: np.ndarray, n_clusters: int):
+    """Tokens ordered by cluster, in token order within a cluster: the
+    permutation (position -> token) and each cluster's [start, end)."""
+    perm = np.argsort(assign * len(assign) + np.arange(len(assign)), kind="stable")
+    sizes = np.bincount(assign, minlength=n_clusters)
+    starts = np.concatenate([[0], np.cumsum(sizes)[:-1]])
+    return perm, starts, sizes
+
+
+def svg2_select(cq: np.ndarray, ck: np.ndarray, k_sizes: np.ndarray, scale: float,
+                p_mass: float) -> RowSelection:
+    """Top-p over key clusters for every query cluster on the size-weighted
+    centroid scores (Top-k reduced to one cluster)."""
+    s = scale * (cq @ ck.T)
+    with np.errstate(divide="ignore"):
+        s = s + np.log(k_sizes.astype(np.float64))[None, :]   # -inf for empty clusters
+    return hybrid_select(s, 1.0 / len(k_sizes), p_mass), s
+
+
+def svg2_attention_head(q, k, v, n_q_clusters: int, n_k_clusters: int, iters: int,
+                        scale: float, p_mass: float):
+    """SVG2's sparse attention for one head (float64 [N, d] inputs): each query
+    attends to the tokens of the key clusters its cluster selected. Returns
+    (O, q-assignment, k-assignment, selection)."""
+    qa, cq = kmeans(q, n_q_clusters, iters)
+    ka, ck = kmeans(k, n_k_clusters, iters)
+    sizes = np.bincount(ka, minlength=n_k_clusters)
+    sel, _ = svg2_select(cq, ck, sizes, scale, p_mass)
+    mask = sel.kept[qa][:, ka]                                   # [N, N] token pairs
+    s = np.where(mask, scale * (q @ k.T), -np.inf)
+    P = np.exp(s - s.max(axis=1, keepdims=True))
+    P /= P.sum(axis=1, keepdims=True)
+    return P @ v, qa, ka, sel

@@ -749,3 +749,66 @@ def test_lowbit_is_close_to_exact_attention():
         idx2[i, :cnt[i]] = idx[i, :cnt[i]][::-1]
     o2 = O.lowbit_attention_head(q, k, v, idx2, cnt, 64, 64, 1 / math.sqrt(32))
     assert np.abs(o2 - o).max() < 0.05
+
+
+# ------------------------------------------------- SVG2 semantic permutation
+def test_kmeans_recovers_separated_clusters():
+    # four tight, far-apart groups, one per quarter of the sequence with a few
+    # members scattered elsewhere: the initial rows floor(c N / C) fall one in
+    # each group, and a few rounds put every token with its group
+    rng = np.random.default_rng(91)
+    centres = rng.standard_normal((4, 8)) * 20
+    truth = np.arange(400) // 100
+    swap = rng.choice(400, 40, replace=False)
+    swap = swap[swap % 100 != 0]                    # keep the initial rows in place
+    truth[swap] = rng.integers(0, 4, swap.size)
+    x = centres[truth] + 0.01 * rng.standard_normal((400, 8))
+    assign, cent = O.kmeans(x, 4, 5)
+    for g in range(4):  # one cluster per group, and the centroid is the group mean
+        ids = np.unique(assign[truth == g])
+        assert ids.size == 1
+        np.testing.assert_allclose(cent[ids[0]], x[truth == g].mean(axis=0), atol=1e-12)
+    assert np.unique(assign).size == 4
+
+
+def test_kmeans_steps_are_argmin_and_mean():
+    rng = np.random.default_rng(92)
+    x = rng.standard_normal((300, 6))
+    cent = x[[0, 50, 100, 150, 200]].copy()
+    a = O.kmeans_assign(x, cent)
+    brute = np.argmin(((x[:, None, :] - cent[None]) ** 2).sum(axis=2), axis=1)
+    assert np.array_equal(a, brute)
+    new = O.kmeans_update(x, a, cent)
+    for c in range(5):
+        np.testing.assert_allclose(new[c], x[a == c].mean(axis=0), atol=1e-13)
+    # Lloyd never increases the objective
+    obj = lambda aa, cc: ((x - cc[aa]) ** 2).sum()
+    prev = obj(a, cent)
+    for _ in range(4):
+        cent = O.kmeans_update(x, O.kmeans_assign(x, cent), cent)
+        cur = obj(O.kmeans_assign(x, cent), cent)
+        assert cur <= prev + 1e-9
+        prev = cur
+
+
+def test_svg2_permutation_and_size_weighting():
+    assign = np.array([2, 0, 2, 1, 0, 2])
+    perm, starts, sizes = O.svg2_permutation(assign, 4)
+    assert perm.tolist() == [1, 4, 3, 0, 2, 5] and starts.tolist() == [0, 2, 3, 6]
+    assert sizes.tolist() == [2, 1, 3, 0]
+    # a cluster of two tokens with centroid score s weighs like two clusters of one
+    cq = np.array([[1.0, 0.0]])
+    ck = np.array([[0.5, 0.0], [0.5, 0.0], [0.2, 0.0], [0.0, 0.0]])
+    sel, s = O.svg2_select(cq, ck, np.array([1, 1, 2, 0]), 1.0, 0.99)
+    P = O.row_softmax(s)
+    assert P[0, 3] == 0.0 and sel.kept[0, 3] == False  # empty cluster never kept
+    np.testing.assert_allclose(P[0, 2] / P[0, 0], 2 * np.exp(0.2 - 0.5), rtol=1e-14)
+
+
+def test_svg2_keeping_everything_is_dense_attention():
+    rng = np.random.default_rng(93)
+    q, k, v = (rng.standard_normal((200, 8)) for _ in range(3))
+    o, qa, ka, sel = O.svg2_attention_head(q, k, v, 5, 7, 3, 0.3, 1.0)
+    assert sel.kept[:, np.bincount(ka, minlength=7) > 0].all()
+    P = O.row_softmax(0.3 * (q @ k.T))
+    np.testing.assert_allclose(o, P @ v, atol=1e-13)
