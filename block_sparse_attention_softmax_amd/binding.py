@@ -26,7 +26,7 @@ EXPORTS = ("sparge_mask_workspace_bytes", "sparge_mask_predict",
            "sla2_mix_attn_fwd", "sparge_attn_fwd_lse", "sparge_attn_bwd_workspace_bytes",
            "sparge_attn_bwd", "sparse_linear_bwd_workspace_bytes", "sparse_linear_attn_bwd",
            "sla2_mix_attn_bwd", "sparge_attn_lowbit_workspace_bytes", "sparge_attn_fwd_lowbit",
-           "sparge_last_error")
+           "svg2_attn_workspace_bytes", "svg2_attn_fwd", "sparge_last_error")
 
 _lib = None
 
@@ -71,6 +71,10 @@ def lib() -> ctypes.CDLL:
         L.sparge_attn_lowbit_workspace_bytes.restype = c_size
         L.sparge_attn_fwd_lowbit.argtypes = [vp] * 5 + [c_int] * 6 + [c_float, vp, vp, c_size, vp]
         L.sparge_attn_fwd_lowbit.restype = c_int
+        L.svg2_attn_workspace_bytes.argtypes = [c_int] * 7
+        L.svg2_attn_workspace_bytes.restype = c_size
+        L.svg2_attn_fwd.argtypes = [vp] * 3 + [c_int] * 8 + [c_float, c_float, vp, vp, c_size, vp]
+        L.svg2_attn_fwd.restype = c_int
         L.sparse_linear_bwd_workspace_bytes.argtypes = [c_int] * 4
         L.sparse_linear_bwd_workspace_bytes.restype = c_size
         for f in (L.sparse_linear_attn_bwd, L.sla2_mix_attn_bwd):
@@ -265,6 +269,27 @@ def sparge_attn_fwd_lowbit(q, k, v, kv_idx, kv_cnt, block_q=128, block_k=64, sca
     _check(lib().sparge_attn_fwd_lowbit(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_idx), _ptr(kv_cnt), B,
                                         H, N, d, block_q, block_k, scale, _ptr(o),
                                         _ptr(workspace), workspace.numel(), _stream(q)))
+    return o
+
+
+def svg2_workspace_bytes(B, H, N, d, block_q, n_q_clusters, n_k_clusters) -> int:
+    return lib().svg2_attn_workspace_bytes(B, H, N, d, block_q, n_q_clusters, n_k_clusters)
+
+
+def svg2_attn_fwd(q, k, v, n_q_clusters, n_k_clusters, iters=10, p_mass=0.9, block_q=128,
+                  scale=None, out=None, workspace=None):
+    """SVG2: k-means permutation, size-weighted centroid Top-p, clustered attention."""
+    B, H, N, d = _qkv(q, k, v)
+    o = torch.empty_like(q) if out is None else out
+    if scale is None:
+        scale = default_scale(d)
+    if workspace is None:
+        workspace = torch.empty(max(svg2_workspace_bytes(B, H, N, d, block_q, n_q_clusters,
+                                                         n_k_clusters), 256),
+                                dtype=torch.uint8, device=q.device)
+    _check(lib().svg2_attn_fwd(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, block_q, n_q_clusters,
+                               n_k_clusters, iters, p_mass, scale, _ptr(o), _ptr(workspace),
+                               workspace.numel(), _stream(q)))
     return o
 
 

@@ -381,6 +381,51 @@ int sparge_attn_fwd_lowbit(const void* q, const void* k, const void* v, const in
   return SPARGE_OK;
 }
 
+size_t svg2_attn_workspace_bytes(int B, int H, int N, int d, int block_q, int n_q_clusters,
+                                 int n_k_clusters) {
+  const std::string saved = g_last_error;
+  const int rc = check_shape(B, H, N, d, block_q, 64);
+  g_last_error = saved;
+  if (rc != SPARGE_OK || n_q_clusters < 1 || n_k_clusters < 1 || n_q_clusters > N ||
+      n_k_clusters > N || n_k_clusters > kMaxKeyBlocks)
+    return 0;
+  return sparge::svg2_workspace_bytes(B, H, N, d, block_q, n_q_clusters, n_k_clusters);
+}
+
+int svg2_attn_fwd(const void* q, const void* k, const void* v, int B, int H, int N, int d,
+                  int block_q, int n_q_clusters, int n_k_clusters, int iters, float p_mass,
+                  float scale, void* o, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  int rc = check_shape(B, H, N, d, block_q, 64);
+  if (rc != SPARGE_OK) return rc;
+  if (!q || !k || !v || !o || !workspace) return fail(SPARGE_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(workspace, 256))
+    return fail(SPARGE_ERR_INVALID_ARG, "q, k, v, o must be 16-byte and workspace 256-byte aligned");
+  if (n_q_clusters < 1 || n_k_clusters < 1 || n_q_clusters > N || n_k_clusters > N)
+    return fail(SPARGE_ERR_INVALID_ARG, "cluster counts must lie in [1, N]");
+  if (n_k_clusters > kMaxKeyBlocks)
+    return fail(SPARGE_ERR_UNSUPPORTED, "at most 4096 key clusters");
+  if (iters < 0 || iters > 1000) return fail(SPARGE_ERR_INVALID_ARG, "iters must lie in [0, 1000]");
+  if (!(p_mass >= 0.0f) || !(scale > 0.0f) || !isfinite(scale))
+    return fail(SPARGE_ERR_INVALID_ARG, "p_mass must be >= 0 and scale finite and > 0");
+  if (workspace_bytes < sparge::svg2_workspace_bytes(B, H, N, d, block_q, n_q_clusters, n_k_clusters))
+    return fail(SPARGE_ERR_INVALID_ARG, "workspace too small");
+  sparge::Svg2Launch a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<uint16_t*>(o);
+  a.B = B; a.H = H; a.N = N; a.d = d; a.block_q = block_q;
+  a.Cq = n_q_clusters; a.Ck = n_k_clusters; a.iters = iters;
+  a.scale = scale;
+  a.p = (double)p_mass;
+  sparge::svg2_layout(a, static_cast<unsigned char*>(workspace));
+  const hipError_t e = sparge::launch_svg2(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "svg2_attn_fwd launch");
+  return SPARGE_OK;
+}
+
 size_t sparse_linear_bwd_workspace_bytes(int B, int H, int N, int d) {
   const std::string saved = g_last_error;
   const int rc = check_shape(B, H, N, d, d == 64 ? 64 : 128, 64);

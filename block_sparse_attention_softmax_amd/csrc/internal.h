@@ -59,6 +59,11 @@ struct MaskLaunch {
   int32_t* cnt;
 };
 hipError_t launch_mask(const MaskLaunch& a, hipStream_t s);
+// sc * X Y^T per (b, h) in float64: X [BH][nx][d], Y [BH][ny][d] -> [BH][nx][ny]
+hipError_t launch_scores_f64(const double* x, const double* y, double* out, int BH, int nx,
+                             int ny, int d, double sc, hipStream_t st);
+// the hybrid selection alone, on a.logits ([B*H*n_q][n_k]) into bits / idx / cnt
+hipError_t launch_select_rows(const MaskLaunch& a, hipStream_t st);
 
 struct AttnLaunch {
   const uint16_t* q;
@@ -135,6 +140,28 @@ struct LowbitLaunch {
 hipError_t launch_lowbit(const LowbitLaunch& a, hipStream_t s);
 size_t lowbit_workspace_bytes(int B, int H, int N, int d, int block_q);
 void lowbit_layout(LowbitLaunch& a, unsigned char* workspace);
+// SVG2: k-means permutation, centroid Top-p, attention over padded clusters
+struct Svg2Launch {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  int B, H, N, d, block_q, Cq, Ck, iters;
+  float scale;
+  double p;
+  int max_tiles, max_chunks;  // padded query tiles / 64-key chunks per (b, h), upper bounds
+  // workspace (svg2_layout)
+  double *xq, *xk, *dot, *centq, *centk, *normq, *normk, *clog;
+  int32_t *assign_q, *assign_k, *rank, *ccount, *size_q, *size_k, *off_q, *off_k, *perm_q,
+      *perm_k;
+  uint32_t* sbits;
+  int32_t *sidx, *scnt, *qpad_off, *kpad_off, *tile_cluster, *chunk_valid, *n_tiles, *lists,
+      *list_cnt;
+  uint16_t *qp, *kp, *vp, *vtp;
+};
+hipError_t launch_svg2(const Svg2Launch& a, hipStream_t s);
+size_t svg2_workspace_bytes(int B, int H, int N, int d, int block_q, int Cq, int Ck);
+size_t svg2_layout(Svg2Launch& a, unsigned char* workspace);  // fills pointers; returns bytes
 size_t attn_workspace_bytes(int B, int H, int N, int d);    // packed V
 size_t linear_workspace_bytes(int B, int H, int N, int d);  // packed V + linear branch
 

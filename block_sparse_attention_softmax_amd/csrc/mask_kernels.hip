@@ -487,6 +487,30 @@ hipError_t launch_select(const MaskLaunch& a, hipStream_t st) {
 
 }  // namespace
 
+hipError_t launch_scores_f64(const double* x, const double* y, double* out, int BH, int nx,
+                             int ny, int d, double sc, hipStream_t st) {
+  const int tq = (nx + 31) / 32, tk = (ny + 31) / 32, tiles = BH * tq * tk;
+  if (d == 128)
+    hipLaunchKernelGGL(block_logits_kernel<128>, dim3((tiles + 3) / 4), dim3(kThreads), 0, st, x,
+                       y, out, nx, ny, tq, tk, tiles, sc);
+  else
+    hipLaunchKernelGGL(block_logits_kernel<64>, dim3((tiles + 3) / 4), dim3(kThreads), 0, st, x,
+                       y, out, nx, ny, tq, tk, tiles, sc);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_rows(const MaskLaunch& a, hipStream_t st) {
+  switch (a.npad) {
+    case 64: return launch_select_reg<64>(a, st);
+    case 128: return launch_select_reg<128>(a, st);
+    case 256: return launch_select_reg<256>(a, st);
+    case 512: return launch_select_reg<512>(a, st);
+    case 1024: return launch_select<1024>(a, st);
+    case 2048: return launch_select<2048>(a, st);
+    default: return launch_select<4096>(a, st);
+  }
+}
+
 hipError_t launch_mask(const MaskLaunch& a, hipStream_t st) {
   const int BH = a.B * a.H;
   auto scores = [&](const double* x, const double* y, double* out, int nx, int ny, double sc) {

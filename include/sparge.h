@@ -306,6 +306,36 @@ int sparge_attn_fwd_lowbit(const void* q, const void* k, const void* v,
                            int d, int block_q, int block_k, float scale, void* o,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* Device workspace (bytes) of svg2_attn_fwd (float64 copies of Q and K, the
+ * token-by-centroid distances, the clustering, the selection and the padded
+ * permuted Q, K, V); 0 for arguments svg2_attn_fwd would reject. */
+size_t svg2_attn_workspace_bytes(int B, int H, int N, int d, int block_q, int n_q_clusters,
+                                 int n_k_clusters);
+
+/* SVG2's semantic-aware sparse attention ("Sparse VideoGen2" page, section 2),
+ * per (b, h):
+ *  1. k-means of the query tokens into n_q_clusters and of the key tokens into
+ *     n_k_clusters (Lloyd: `iters` rounds from centroids at tokens
+ *     floor(c N / C), squared Euclidean distance in float64 with ties to the
+ *     lower cluster, centroids the float64 mean of their members, an empty
+ *     cluster keeps its centroid; then a final assignment);
+ *  2. the tokens are permuted so each cluster is contiguous (in token order
+ *     inside a cluster);
+ *  3. every query cluster keeps the key clusters chosen by the hybrid rule of
+ *     sparge_mask_predict on the logits scale * c_q . c_k + ln |key cluster|
+ *     (empty clusters -inf), with Top-p mass p_mass and Top-k of one cluster;
+ *  4. every query attends (softmax over scale Q K^T in float32, bf16 products)
+ *     to the tokens of its cluster's kept key clusters; the output is written
+ *     at the tokens' original positions, so O is the attention of the
+ *     original sequence under that token-level mask.
+ * q, k, v, o: bf16 [B, H, N, d], device, 16-byte aligned; block_q (64 or 128)
+ * is the query tile of the attention step; at most 4096 key clusters. The
+ * workspace (256-byte aligned) holds every intermediate, including float64
+ * distances of N x max(C) per (b, h). */
+int svg2_attn_fwd(const void* q, const void* k, const void* v, int B, int H, int N, int d,
+                  int block_q, int n_q_clusters, int n_k_clusters, int iters, float p_mass,
+                  float scale, void* o, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Device workspace (bytes) of sparse_linear_attn_bwd and sla2_mix_attn_bwd:
  * that of sparge_attn_bwd, plus the linear branch's packed V and phi(K), its
  * totals, the scaled dO of the mix, float32 dQ, dK, dV of the branch and one

@@ -742,16 +742,18 @@ def svg2_select(cq: np.ndarray, ck: np.ndarray, k_sizes: np.ndarray, scale: floa
 
 
 def svg2_attention_head(q, k, v, n_q_clusters: int, n_k_clusters: int, iters: int,
-                        scale: float, p_mass: float):
+                        scale: float, p_mass: float, q_rows=None):
     """SVG2's sparse attention for one head (float64 [N, d] inputs): each query
     attends to the tokens of the key clusters its cluster selected. Returns
-    (O, q-assignment, k-assignment, selection)."""
+    (O, q-assignment, k-assignment, selection); with `q_rows`, O holds only
+    those rows (in that order)."""
     qa, cq = kmeans(q, n_q_clusters, iters)
     ka, ck = kmeans(k, n_k_clusters, iters)
     sizes = np.bincount(ka, minlength=n_k_clusters)
     sel, _ = svg2_select(cq, ck, sizes, scale, p_mass)
-    mask = sel.kept[qa][:, ka]                                   # [N, N] token pairs
-    s = np.where(mask, scale * (q @ k.T), -np.inf)
+    rows = np.arange(q.shape[0]) if q_rows is None else np.asarray(q_rows)
+    mask = sel.kept[qa[rows]][:, ka]                             # token pairs
+    s = np.where(mask, scale * (q[rows] @ k.T), -np.inf)
     P = np.exp(s - s.max(axis=1, keepdims=True))
     P /= P.sum(axis=1, keepdims=True)
     return P @ v, qa, ka, sel

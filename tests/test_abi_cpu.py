@@ -257,3 +257,16 @@ def test_lowbit_workspace_and_rejections():
     bad = list(args)
     bad[8] = 80
     assert L.sparge_attn_fwd_lowbit(*bad) == -2
+
+
+def test_svg2_workspace_and_rejections():
+    L = binding.lib()
+    assert L.svg2_attn_workspace_bytes(1, 12, 32760, 128, 128, 256, 512) > 0
+    assert L.svg2_attn_workspace_bytes(1, 1, 100, 128, 128, 0, 8) == 0
+    assert L.svg2_attn_workspace_bytes(1, 1, 100, 128, 128, 8, 101) == 0   # more clusters than tokens
+    args = [A, A, A, 1, 2, 1024, 64, 64, 8, 16, 3, 0.9, 0.125, A, A, 1 << 34, None]
+    for i, v, code in ((8, 0, -1), (9, 5000, -1), (10, -1, -1), (11, -0.5, -1), (12, 0.0, -1),
+                       (6, 96, -2), (14, ctypes.c_void_p(0x10010), -1), (15, 1024, -1)):
+        bad = list(args)
+        bad[i] = v
+        assert L.svg2_attn_fwd(*bad) == code, (i, v)
