@@ -367,6 +367,25 @@ def main():
                         "lowbit_kept_tops": round(kf_lb / res["lowbit"] / 1e9, 1)}
     del lws8
 
+    # SVG2's clustered attention (256 query / 512 key clusters, 3 k-means rounds, p = 0.9)
+    sws = torch.empty(S.svg2_workspace_bytes(B, H, N, d, wl.block_q, 256, 512), dtype=torch.uint8,
+                      device=dev)
+
+    def svg2():
+        S.svg2_attn_fwd(q, k, v, 256, 512, iters=3, p_mass=0.9, block_q=wl.block_q, scale=wl.scale,
+                        out=o, workspace=sws)
+    svg2()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(3):
+        svg2()
+    e1.record()
+    torch.cuda.synchronize()
+    svg2_line = {"clusters": [256, 512], "kmeans_rounds": 3, "p": 0.9,
+                 "call_ms": round(e0.elapsed_time(e1) / 3, 3)}
+    del sws
+
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl, Q, K, V, args.cpu_blocks)
 
     line = {
@@ -394,6 +413,7 @@ def main():
         "sla2_salad": sla2,
         "backward": backward,
         "lowbit": lowbit,
+        "svg2": svg2_line,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
