@@ -13,8 +13,8 @@
 //    that list j (the transposed lists built below) in increasing order and
 //    accumulates dV^T = dO^T P and dK^T = Q^T dS in registers. S = Q K_j^T is
 //    computed with one key per lane (lane % 32) so that P and dS, converted
-//    to bf16, feed the second products as B operands unchanged, against Q^T
-//    and dO^T pre-packed in the same slot order as the forward's V^T.
+//    to bf16, feed the second products as B operands unchanged, against
+//    dO^T and Q^T taken from the staged Q and dO rows by transposing reads.
 //  * dQ: one workgroup per (b, h, query block), the forward's loop over the
 //    row's list: S^T = K Q^T and dP^T = V dO^T with one query per lane, then
 //    dQ^T += K^T dS^T against K^T packed like V^T.
@@ -52,9 +52,9 @@ __device__ __forceinline__ halfx8 pack_f16x8(const floatx16& x, int base) {
 
 // ------------------------------------------------------------ row terms
 // D[bh][t] = sum_c dO[t][c] O[t][c] (fp32 from the bf16 values) and
-// lse2[bh][t] = lse[bh][t] * log2(e), in rows padded to NP = 64 * ceil(N / 64)
-// per (b, h) so that whole 64-row groups can be copied: padding rows get
-// D = 0 and lse2 = +inf (P = 0). D/8 lanes per row.
+// lse2[bh][t] = lse[bh][t] * log2(e), in rows padded to NP = block_q * n_q
+// per (b, h) so that whole query blocks can be copied: padding rows get D = 0
+// and lse2 = +inf (P = 0). D/8 lanes per row.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_rows_kernel(const uint16_t* __restrict__ o,
                                                        const uint16_t* __restrict__ dO,
@@ -179,41 +179,89 @@ __global__ __launch_bounds__(256) void col_list_kernel(const int32_t* __restrict
 
 // --------------------------------------------------------------- dK, dV
 // Workgroup (b, h, key block j), 4 waves: wave w holds keys 32*(w & 1) .. +31
-// of the block (one per lane % 32) and takes queries 32*(w >> 1) .. +31 of
-// every 64-query stage; the two query halves are summed at the end.
+// of the block (one per lane % 32) and takes rows (w >> 1) * BQ/2 .. +BQ/2-1
+// of every query block that lists j, as BQ/64 sub-tiles of 32 queries; the
+// two row halves are summed at the end.
 //
-// A stage (Q rows, dO rows, packed Q^T and dO^T of one 64-row group, and its
-// lse2 and D) is copied global -> LDS by direct-to-LDS loads into one of two
-// buffers while the waves compute on the other. Lane i of a wave's copy lands
-// at LDS base + 16 i, so each lane reads the global chunk that the tile's XOR
-// swizzle puts there; rows past N read row N - 1 instead (their lse2 is +inf,
-// so they contribute P = dS = 0).
+// A stage is one listed query block: its Q and dO rows, lse2 and D, copied
+// global -> LDS by direct-to-LDS loads into one of two buffers while the
+// waves compute on the other (lane i of a wave's copy lands at LDS base +
+// 16 i, so each lane reads the global chunk that the swizzle puts there; rows
+// past N read row N - 1, and their lse2 = +inf gives P = dS = 0). The S and dP
+// products read the rows as they are; the dV and dK products need them
+// transposed (8 queries of one channel per lane, in the slot order of the P
+// and dS registers), which transposing LDS reads take from the same rows.
+
+// Q / dO rows in LDS, 16-byte chunks XOR-swizzled per row so that both access
+// patterns spread over all 64 banks: 16 lanes reading one chunk of 16
+// consecutive rows, and 32 lanes reading 64 bytes of 4 consecutive rows (the
+// transposing reads). d = 128: the row's low two bits pick the 64-byte group,
+// the next two the chunk within it; d = 64 (two rows per bank cycle) uses row
+// bits 1 and 2, 3 likewise.
 template <int D>
+struct RowTile {
+  static constexpr int ROWB = D * 2, CPR = D / 8;
+  __device__ static constexpr int swz(int row) {
+    return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3))
+                    : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+  }
+  __device__ static constexpr int chunk(int row, int c) { return c ^ swz(row); }
+};
+
+template <int D, int BQ>
 struct DkdvStage {
-  using T = Tile<D>;
-  static constexpr int BYTES = 4 * T::BYTES + 2 * 64 * 4;
-  static constexpr int QS = 0, DS = T::BYTES, QTS = 2 * T::BYTES, DTS = 3 * T::BYTES,
-                       LS = 4 * T::BYTES, DD = 4 * T::BYTES + 256;
+  static constexpr int ROWS = BQ * RowTile<D>::ROWB;  // one tensor's rows
+  static constexpr int QS = 0, DS = ROWS, LS = 2 * ROWS, DD = 2 * ROWS + BQ * 4;
+  static constexpr int BYTES = 2 * ROWS + 2 * BQ * 4;
 };
 
 __device__ __forceinline__ void dma4(const void* src, void* lds) {
   __builtin_amdgcn_global_load_lds(src, lds, 4, 0, 0);
 }
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// 32-bit LDS address of a pointer into __shared__ memory
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)(p);
+}
+
+// Four transposing LDS reads (ds_read_b64_tr_b16): within each group of 16
+// lanes, lane i receives element i & 3 of the 4-element rows that lanes
+// 4e + (i >> 2), e = 0..3, address. Written as one asm block that also waits
+// for them: as a builtin the compiler holds such a read until every
+// direct-to-LDS copy in flight has landed, the next stage's included.
+__device__ __forceinline__ void lds_read_tr4(v4i16& r0, v4i16& r1, v4i16& r2, v4i16& r3,
+                                             uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4\n\t"
+      "ds_read_b64_tr_b16 %1, %5\n\t"
+      "ds_read_b64_tr_b16 %2, %6\n\t"
+      "ds_read_b64_tr_b16 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+      : "memory");
+}
+
+__device__ __forceinline__ bf16x8 join_tr(v4i16 lo, v4i16 hi) {
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  return __builtin_bit_cast(bf16x8, (v8i16)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 template <int D, int BQ>
 __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void sparse_attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dO,
-    const uint16_t* __restrict__ qt, const uint16_t* __restrict__ dot,
     const float* __restrict__ lse2, const float* __restrict__ drow,
     const int32_t* __restrict__ coloff, const int32_t* __restrict__ collist,
-    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int N, int n_q, int n_k, int n64,
-    int total, float c, float scale, const float* __restrict__ lin_dk,
-    const float* __restrict__ lin_dv) {
-  using T = Tile<D>;
-  using ST = DkdvStage<D>;
-  constexpr int DT = D / 32, KSTEPS = D / 16, SUB = BQ / 64;
-  constexpr int KU = 64 * T::KCPR / 256, VU = D * T::VCPR / 256;  // 16-byte copies per thread
+    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int N, int n_q, int n_k, int total,
+    float c, float scale, const float* __restrict__ lin_dk, const float* __restrict__ lin_dv) {
+  using RT = RowTile<D>;
+  using ST = DkdvStage<D, BQ>;
+  constexpr int DT = D / 32, KSTEPS = D / 16, NS = BQ / 64;
+  constexpr int CU = BQ * RT::CPR / 256;  // 16-byte copies per thread and tensor
+  static_assert(BQ * RT::CPR % 256 == 0, "whole copies per thread");
   __shared__ __align__(16) unsigned char smem[2 * ST::BYTES];
 
   const int tile = xcd_remap(blockIdx.x, total);
@@ -222,7 +270,7 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void sparse_attn_bwd_dkdv_ke
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // copy bases are uniform
   const int h2 = lane >> 5, l32 = lane & 31, kw = 32 * (wave & 1), qh = wave >> 1;
   const size_t head = (size_t)bh * N * D;
-  const int NP = n64 * BK;
+  const int NP = n_q * BQ;
   const int key = j * BK + kw + l32;
 
   bf16x8 kf[KSTEPS], vf[KSTEPS];  // this lane's key row (zero past N)
@@ -241,128 +289,111 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void sparse_attn_bwd_dkdv_ke
 #pragma unroll
     for (int r = 0; r < 16; ++r) dka[i][r] = dva[i][r] = 0.0f;
 
-  // per-thread source offsets (elements) of the tile copies, within a row group
-  uint32_t krow_ofs[KU], vrow_ofs[VU];
-  int krow[KU];
+  // per-thread source offsets (elements) of the row copies within a block
+  uint32_t src_ofs[CU];
+  int src_row[CU];
 #pragma unroll
-  for (int u = 0; u < KU; ++u) {
-    const int p = u * 256 + threadIdx.x, r = p / T::KCPR;
-    krow[u] = r;
-    krow_ofs[u] = (uint32_t)(r * D + T::kchunk(r, p % T::KCPR) * 8);
+  for (int u = 0; u < CU; ++u) {
+    const int p = u * 256 + threadIdx.x, r = p / RT::CPR;
+    src_row[u] = r;
+    src_ofs[u] = (uint32_t)(r * D + RT::chunk(r, p % RT::CPR) * 8);
   }
-#pragma unroll
-  for (int u = 0; u < VU; ++u) {
-    const int p = u * 256 + threadIdx.x, r = p / T::VCPR;
-    vrow_ofs[u] = (uint32_t)(r * BK + T::vchunk(r, p % T::VCPR) * 8);
-  }
+  // transposing reads: lane 16g + 4e + m addresses row R0 + 4*h2 + e of the
+  // fragment and the 8 bytes at channel 32 ii + 16 (g & 1) + 4 m; with R0 a
+  // multiple of 8 the swizzled chunk is (4 ii + ((R0 >> 2) & 3)) ^ tr_lane
+  const int e_l = (lane >> 2) & 3, m_l = lane & 3, g1 = (lane >> 4) & 1;
+  const int tr_swz = D == 128 ? ((e_l << 2) | h2) : ((((e_l >> 1) & 1) << 2) | h2);
+  const int tr_lane = (2 * g1 + (m_l >> 1)) ^ tr_swz;
+  const uint32_t tr_row = (uint32_t)((4 * h2 + e_l) * RT::ROWB + 8 * (m_l & 1));
 
   const int beg = coloff[(size_t)bh * (n_k + 1) + j], end = coloff[(size_t)bh * (n_k + 1) + j + 1];
   const int32_t* lst = collist + (size_t)bh * n_q * n_k;
-  // stages: (entry e, sub-block sb) with row r0 = lst[e] * BQ + 64 sb < N
-  auto first_row = [&](int e, int sb) { return lst[e] * BQ + 64 * sb; };
-  auto advance = [&](int& e, int& sb) {  // to the next stage that starts before N
-    do {
-      if (++sb == SUB) {
-        sb = 0;
-        ++e;
-      }
-    } while (e < end && first_row(e, sb) >= N);
-  };
-  auto issue = [&](int r0, unsigned char* buf) {
+  auto issue = [&](int r0, unsigned char* buf) {  // the rows of query block r0 / BQ
     const uint16_t* qsrc = q + head + (size_t)r0 * D;
     const uint16_t* dsrc = dO + head + (size_t)r0 * D;
-    const size_t g = (size_t)bh * n64 + r0 / 64;
-    const uint16_t* qtsrc = qt + g * D * BK;
-    const uint16_t* dtsrc = dot + g * D * BK;
 #pragma unroll
-    for (int u = 0; u < KU; ++u) {
-      const uint32_t back = (uint32_t)max(r0 + krow[u] - (N - 1), 0) * D;  // rows past N
+    for (int u = 0; u < CU; ++u) {
+      const uint32_t back = (uint32_t)max(r0 + src_row[u] - (N - 1), 0) * D;  // rows past N
       unsigned char* dst = buf + (u * 256 + wave * 64) * 16;
-      dma16(qsrc + krow_ofs[u] - back, dst + ST::QS);
-      dma16(dsrc + krow_ofs[u] - back, dst + ST::DS);
+      dma16(qsrc + src_ofs[u] - back, dst + ST::QS);
+      dma16(dsrc + src_ofs[u] - back, dst + ST::DS);
     }
-#pragma unroll
-    for (int u = 0; u < VU; ++u) {
-      unsigned char* dst = buf + (u * 256 + wave * 64) * 16;
-      dma16(qtsrc + vrow_ofs[u], dst + ST::QTS);
-      dma16(dtsrc + vrow_ofs[u], dst + ST::DTS);
+    if (wave < 2 * NS) {  // lse2 (waves 0 .. NS-1) and D (the next NS), 64 rows each
+      const int part = wave % NS;
+      const float* src = (wave < NS ? lse2 : drow) + (size_t)bh * NP + r0 + 64 * part + lane;
+      dma4(src, buf + (wave < NS ? ST::LS : ST::DD) + 256 * part);
     }
-    if (wave == 0) dma4(lse2 + (size_t)bh * NP + r0 + lane, buf + ST::LS);
-    if (wave == 1) dma4(drow + (size_t)bh * NP + r0 + lane, buf + ST::DD);
   };
 
-  int e = beg, sb = 0;
-  if (e < end && first_row(e, sb) >= N) advance(e, sb);
-  int it = 0;
-  if (e < end) issue(first_row(e, sb), smem);
-  while (e < end) {
-    unsigned char* const buf = smem + (it & 1) * ST::BYTES;
+  if (beg < end) issue(min(max(lst[beg], 0), n_q - 1) * BQ, smem);
+  for (int e = beg; e < end; ++e) {
+    const int nxt = e + 1 < end ? min(max(lst[e + 1], 0), n_q - 1) : 0;
+    unsigned char* const buf = smem + ((e - beg) & 1) * ST::BYTES;
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of the stage landed
     __syncthreads();                     // every wave's copies landed, the other buffer is free
-    int en = e, sn = sb;
-    advance(en, sn);
-    if (en < end) issue(first_row(en, sn), smem + ((it + 1) & 1) * ST::BYTES);
+    if (e + 1 < end) issue(nxt * BQ, smem + ((e - beg + 1) & 1) * ST::BYTES);
+    const uint32_t bufa = lds_addr(buf) + tr_row;
 
-    const unsigned char* qs = buf + ST::QS;
-    const unsigned char* ds = buf + ST::DS;
-    const unsigned char* qts = buf + ST::QTS;
-    const unsigned char* dts = buf + ST::DTS;
-    const float* ls = reinterpret_cast<const float*>(buf + ST::LS);
-    const float* dd = reinterpret_cast<const float*>(buf + ST::DD);
-
-    // S = Q K^T and dP = dO V^T for the wave's 32 queries x 32 keys
-    floatx16 S, dP;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) S[r] = dP[r] = 0.0f;
-    const int qr = qh * 32 + l32;
+    for (int n = 0; n < NS; ++n) {
+      const int qb = qh * (BQ / 2) + 32 * n;  // the sub-tile's first row in the block
+      // S = Q K^T and dP = dO V^T for the sub-tile's 32 queries x the wave's 32 keys
+      floatx16 S, dP;
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-      const int ch = 2 * s + h2;
-      const bf16x8 a = lds_read16(qs + qr * T::KROWB + T::kchunk(qr, ch) * 16);
-      const bf16x8 b = lds_read16(ds + qr * T::KROWB + T::kchunk(qr, ch) * 16);
-      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[s], S, 0, 0, 0);
-      dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, vf[s], dP, 0, 0, 0);
-    }
-    // P = 2^(S c - lse2), dS = P (dP - D); register r holds query
-    // 8*(r/4) + 4*h2 + r%4 of the wave's 32
+      for (int r = 0; r < 16; ++r) S[r] = dP[r] = 0.0f;
+      const int qr = qb + l32;
 #pragma unroll
-    for (int gg = 0; gg < 4; ++gg) {
-      const int t0 = qh * 32 + 8 * gg + 4 * h2;
-      const float4 l4 = *reinterpret_cast<const float4*>(ls + t0);
-      const float4 d4 = *reinterpret_cast<const float4*>(dd + t0);
-      const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+      for (int s = 0; s < KSTEPS; ++s) {
+        const int ch = RT::chunk(qr, 2 * s + h2);
+        const bf16x8 a = lds_read16(buf + ST::QS + qr * RT::ROWB + ch * 16);
+        const bf16x8 b = lds_read16(buf + ST::DS + qr * RT::ROWB + ch * 16);
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[s], S, 0, 0, 0);
+        dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, vf[s], dP, 0, 0, 0);
+      }
+      // P = 2^(S c - lse2), dS = P (dP - D); register r holds row
+      // qb + 8*(r/4) + 4*h2 + r%4 (the row terms are read as 16-byte
+      // fragments: as float4 the compiler waits here for the next stage's
+      // copies in flight into the other buffer)
 #pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        const int r = 4 * gg + e2;
-        const float p = __builtin_amdgcn_exp2f(fmaf(S[r], c, -lv[e2]));
-        S[r] = p;
-        dP[r] = p * (dP[r] - dv4[e2]);
+      for (int gg = 0; gg < 4; ++gg) {
+        const int t0 = qb + 8 * gg + 4 * h2;
+        const float4 l4 = __builtin_bit_cast(float4, lds_read16(buf + ST::LS + 4 * t0));
+        const float4 d4 = __builtin_bit_cast(float4, lds_read16(buf + ST::DD + 4 * t0));
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const int r = 4 * gg + e2;
+          const float p = __builtin_amdgcn_exp2f(fmaf(S[r], c, -lv[e2]));
+          S[r] = p;
+          dP[r] = p * (dP[r] - dv4[e2]);
+        }
+      }
+      // dV^T += dO^T P, dK^T += Q^T dS: k-slots 0..3 of half t are rows
+      // qb + 16 t + 4 h2 + 0..3, slots 4..7 the same + 8
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const bf16x8 pb = pack_bf16x8(S, 8 * t);
+        const bf16x8 sb2 = pack_bf16x8(dP, 8 * t);
+        const int R0 = qb + 16 * t;
+        const int C0 = (R0 >> 2) & 3, C1 = ((R0 + 8) >> 2) & 3;
+#pragma unroll
+        for (int ii = 0; ii < DT; ++ii) {
+          const uint32_t o0 = (uint32_t)(R0 * RT::ROWB + (((4 * ii + C0) ^ tr_lane) << 4));
+          const uint32_t o1 = (uint32_t)((R0 + 8) * RT::ROWB + (((4 * ii + C1) ^ tr_lane) << 4));
+          v4i16 d0, d1, q0, q1;
+          lds_read_tr4(d0, d1, q0, q1, bufa + ST::DS + o0, bufa + ST::DS + o1, bufa + ST::QS + o0,
+                       bufa + ST::QS + o1);
+          dva[ii] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join_tr(d0, d1), pb, dva[ii], 0, 0, 0);
+          dka[ii] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join_tr(q0, q1), sb2, dka[ii], 0, 0, 0);
+        }
       }
     }
-    // dV^T += dO^T P, dK^T += Q^T dS (k = the wave's queries, in slot order)
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const bf16x8 pb = pack_bf16x8(S, 8 * t);
-      const bf16x8 sb2 = pack_bf16x8(dP, 8 * t);
-      const int ch = 4 * qh + 2 * t + h2;
-#pragma unroll
-      for (int ii = 0; ii < DT; ++ii) {
-        const int row = 32 * ii + l32;
-        const bf16x8 ao = lds_read16(dts + row * T::VROWB + T::vchunk(row, ch) * 16);
-        const bf16x8 aq = lds_read16(qts + row * T::VROWB + T::vchunk(row, ch) * 16);
-        dva[ii] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, pb, dva[ii], 0, 0, 0);
-        dka[ii] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, sb2, dka[ii], 0, 0, 0);
-      }
-    }
-    e = en;
-    sb = sn;
-    ++it;
   }
 
-  // sum the two query halves: waves 2, 3 hand theirs to waves 0, 1
+  // sum the two row halves: waves 2, 3 hand theirs to waves 0, 1
   __syncthreads();
   float* red = reinterpret_cast<float*>(smem);  // [2 key halves][2][DT][16][64]
-  static_assert(2 * 2 * DT * 16 * 64 * 4 <= 2 * DkdvStage<D>::BYTES, "reduction must fit");
+  static_assert(2 * 2 * DT * 16 * 64 * 4 <= 2 * ST::BYTES, "reduction must fit");
   const int kh = wave & 1;
   if (qh == 1) {
 #pragma unroll
@@ -449,7 +480,7 @@ __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void sparse
       df[s] = *reinterpret_cast<const bf16x8*>(dO + ro + 16 * s);
     }
   }
-  const int NP = 64 * ((N + 63) / 64);
+  const int NP = n_q * BQ;
   const float lq = valid ? lse2[(size_t)bh * NP + qrow] : INFINITY;
   const float dq_d = valid ? drow[(size_t)bh * NP + qrow] : 0.0f;
   floatx16 acc[DT];
@@ -1023,7 +1054,7 @@ size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // workspace regions, in order (the linear ones only when the branch is on)
 struct BwdWs {
-  uint16_t *qt, *dot, *kt;
+  uint16_t* kt;
   float *drow, *lse2;
   int32_t *cmat, *colcnt, *coloff, *collist;
   // linear branch
@@ -1044,11 +1075,9 @@ BwdWs bwd_layout(unsigned char* w, int B, int H, int N, int d, int block_q, bool
     off += up256(n);
     return p;
   };
-  r.qt = reinterpret_cast<uint16_t*>(take(packed));
-  r.dot = reinterpret_cast<uint16_t*>(take(packed));
   r.kt = reinterpret_cast<uint16_t*>(take(packed));
-  r.drow = reinterpret_cast<float*>(take(BH * n_k * BK * 4));  // padded rows
-  r.lse2 = reinterpret_cast<float*>(take(BH * n_k * BK * 4));
+  r.drow = reinterpret_cast<float*>(take(BH * n_q * block_q * 4));  // rows padded to whole blocks
+  r.lse2 = reinterpret_cast<float*>(take(BH * n_q * block_q * 4));
   r.cmat = reinterpret_cast<int32_t*>(take(BH * n_k * n_q * 4));
   r.colcnt = reinterpret_cast<int32_t*>(take(BH * n_k * 4));
   r.coloff = reinterpret_cast<int32_t*>(take(BH * (n_k + 1) * 4));
@@ -1079,7 +1108,7 @@ template <int D, int BQ>
 hipError_t launch_bwd_t(const BwdLaunch& a, hipStream_t s) {
   const bool linear = a.alpha != nullptr;
   const BwdWs w = bwd_layout(a.workspace, a.B, a.H, a.N, a.d, a.block_q, linear, nullptr);
-  const int BH = a.B * a.H, n64 = a.n_k;  // 64-row groups of Q and dO = key blocks
+  const int BH = a.B * a.H;
   const float c = a.scale * kLog2e;
   const uint16_t* dos = a.dO;  // the sparse part's upstream gradient
   if (linear) {
@@ -1100,14 +1129,10 @@ hipError_t launch_bwd_t(const BwdLaunch& a, hipStream_t s) {
       }
     }
   }
-  // Q^T, dO^T and K^T (fp16) packed in 64-row groups like V^T
-  hipLaunchKernelGGL((pack_kernel<D, false>), dim3(n64, BH), dim3(2 * D), 0, s, a.q, nullptr,
-                     w.qt, nullptr, a.N, n64, nullptr, a.H);
-  hipLaunchKernelGGL((pack_kernel<D, false>), dim3(n64, BH), dim3(2 * D), 0, s, dos, nullptr,
-                     w.dot, nullptr, a.N, n64, nullptr, a.H);
-  hipLaunchKernelGGL((pack_kernel<D, false, true>), dim3(n64, BH), dim3(2 * D), 0, s, a.k,
-                     nullptr, w.kt, nullptr, a.N, n64, nullptr, a.H);
-  const int NP = n64 * BK;
+  // K^T (fp16) packed in 64-row groups like V^T
+  hipLaunchKernelGGL((pack_kernel<D, false, true>), dim3(a.n_k, BH), dim3(2 * D), 0, s, a.k,
+                     nullptr, w.kt, nullptr, a.N, a.n_k, nullptr, a.H);
+  const int NP = a.n_q * BQ;
   const size_t rows = (size_t)BH * NP;
   constexpr int RPW = 256 / (D / 8);
   // D = dO . O with the caller's dO and O (the linear kernel corrects it to the sparse share)
@@ -1139,9 +1164,8 @@ hipError_t launch_bwd_t(const BwdLaunch& a, hipStream_t s) {
     }
   }
   hipLaunchKernelGGL((sparse_attn_bwd_dkdv_kernel<D, BQ>), dim3(cols), dim3(256), 0, s, a.q, a.k,
-                     a.v, dos, w.qt, w.dot, w.lse2, w.drow, w.coloff, w.collist, a.dk, a.dv,
-                     a.N, a.n_q, a.n_k, n64, cols, c, a.scale, linear ? w.dkl : nullptr,
-                     linear ? w.dvl : nullptr);
+                     a.v, dos, w.lse2, w.drow, w.coloff, w.collist, a.dk, a.dv, a.N, a.n_q,
+                     a.n_k, cols, c, a.scale, linear ? w.dkl : nullptr, linear ? w.dvl : nullptr);
   hipLaunchKernelGGL((sparse_attn_bwd_dq_kernel<D, BQ>), dim3(qrows), dim3(BQ * 2), 0, s, a.q,
                      a.k, a.v, dos, w.kt, w.lse2, w.drow, a.idx, a.cnt, a.dq, a.N, a.n_q,
                      a.n_k, qrows, c, a.scale, linear ? w.dql : nullptr);

@@ -184,10 +184,11 @@ int sparge_attn_fwd_lse(const void* q, const void* k, const void* v,
                         int d, int block_q, int block_k, float scale, void* o, float* lse,
                         void* workspace, size_t workspace_bytes, void* stream);
 
-/* Device workspace (bytes) of sparge_attn_bwd: Q, dO and K packed like V,
- * two float32 values per row, and the transposed lists (for every key block,
- * the query blocks that list it): about 3 * B*H*N*d*2 + 8*B*H*N +
- * 8*B*H*n_q*n_k bytes. Returns 0 for arguments sparge_attn_bwd would reject. */
+/* Device workspace (bytes) of sparge_attn_bwd: K packed like V (fp16), two
+ * float32 values per row (rows padded to whole query blocks), and the
+ * transposed lists (for every key block, the query blocks that list it):
+ * about B*H*N*d*2 + 8*B*H*N + 8*B*H*n_q*n_k bytes. Returns 0 for arguments
+ * sparge_attn_bwd would reject. */
 size_t sparge_attn_bwd_workspace_bytes(int B, int H, int N, int d, int block_q, int block_k);
 
 /* Backward of sparge_attn_fwd (the sparse attention is fine-tuned in the

@@ -185,7 +185,7 @@ def test_backward_workspace_bytes():
     B, H, N, d, bq = 1, 12, 32760, 128, 128
     BH, n_q, n_k = B * H, math.ceil(N / bq), math.ceil(N / 64)
     packed = up(BH * n_k * 64 * d * 2)
-    want = (3 * packed + 2 * up(BH * n_k * 64 * 4) + up(BH * n_k * n_q * 4) + up(BH * n_k * 4)
+    want = (packed + 2 * up(BH * n_q * bq * 4) + up(BH * n_k * n_q * 4) + up(BH * n_k * 4)
             + up(BH * (n_k + 1) * 4) + up(BH * n_q * n_k * 4))
     assert L.sparge_attn_bwd_workspace_bytes(B, H, N, d, bq, 64) == want
     assert L.sparge_attn_bwd_workspace_bytes(1, 1, 100, 96, 128, 64) == 0
