@@ -268,15 +268,18 @@ __global__ __launch_bounds__(BQ * 2, 2) void sparse_attn_lowbit_kernel(
     // positive), and 448 p = 2^(dot (sq sk c) - m c + log2 448) in one FMA
     const float sqk = sq * ks[(size_t)bh * n_k + j];
     const int nvalid = N - j * BK;  // keys past N (last block only) take no part
-    const bool tail = nvalid < BK;
+    if (nvalid < BK) {              // a ragged last block: a uniform branch, taken once per row
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * tau + 8 * (r >> 2) + 4 * h2 + (r & 3) >= nvalid) si[tau][r] = INT_MIN;
+    }
     int dmax = INT_MIN;
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 32 * tau + 8 * (r >> 2) + 4 * h2 + (r & 3);
-        dmax = max(dmax, (tail && key >= nvalid) ? INT_MIN : si[tau][r]);
-      }
+      for (int r = 0; r < 16; r += 2) dmax = max(dmax, max(si[tau][r], si[tau][r + 1]));
     dmax = max(dmax, __shfl_xor(dmax, 32));
     const float mloc = (float)dmax * sqk;
     const float m_new = fmaxf(m, mloc);
@@ -289,7 +292,8 @@ __global__ __launch_bounds__(BQ * 2, 2) void sparse_attn_lowbit_kernel(
         for (int r = 0; r < 16; ++r) oacc[i][r] *= f;
       m = m_new;
     }
-    // P codes: e4m3(448 p), four per dword, in register order
+    // P codes: e4m3(448 p), four per dword, in register order (word w holds
+    // keys 32 (w / 4) + 8 (w % 4) + 4 h2 + 0..3)
     v8i pb;
     const float sc = sqk * c, bias = 8.807354922057604f - m * c;  // log2(448) - m c
 #pragma unroll
@@ -297,16 +301,22 @@ __global__ __launch_bounds__(BQ * 2, 2) void sparse_attn_lowbit_kernel(
       const int tau = w >> 2, r0 = (w & 3) * 4;
       float p[4];
 #pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
+      for (int e2 = 0; e2 < 4; ++e2)
         p[e2] = __builtin_amdgcn_exp2f(fmaf((float)si[tau][r0 + e2], sc, bias));
-        if (tail && 32 * tau + 8 * ((r0 + e2) >> 2) + 4 * h2 + ((r0 + e2) & 3) >= nvalid)
-          p[e2] = 0.0f;
-      }
       int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-      word = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
-      pb[w] = word;
-      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
-      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
+      pb[w] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
+    }
+    if (nvalid < BK) {  // masked keys get code 0 (byte-wise, keys ascend within a word)
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        const int nv = min(max(nvalid - (32 * (w >> 2) + 8 * (w & 3) + 4 * h2), 0), 4);
+        pb[w] &= nv >= 4 ? -1 : (int)((1u << (8 * nv)) - 1u);
+      }
+    }
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(pb[w], false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(pb[w], true);
       lsum += (lo[0] + lo[1]) + (hi[0] + hi[1]);
     }
     // O^T += V^T P^T, one instruction per 32 channels covers the 64 keys
