@@ -613,10 +613,26 @@ constexpr int kMaxLinKeyBlocks = 4096;  // capacity of the per-row kept bitmap
 // Per (b, h, query block of D rows), 4 waves. First H_D, z_D on the matrix
 // cores from the packed phi(K)^T and V^T tiles of whichever list is shorter:
 // H_tot minus the listed blocks (as the forward forms it), or the sum over the
-// blocks not listed. Then, 32 rows at a time in float32 on the vector units:
-// O_l, dnum, dden, the correction of D, dQ_l = dphi(Q) phi'(Q) and the block's
-// dH_D, dz_D (written for the key kernel). Heads whose branch is off and
+// blocks not listed (their list is built in LDS in increasing order). The
+// tiles are copied global -> LDS by direct-to-LDS loads three blocks ahead of
+// the products (four buffers in the space the second part reuses). Then, 32
+// rows at a time in float32 on the vector units: O_l, dnum, dden, the
+// correction of D, dQ_l = dphi(Q) phi'(Q) and the block's dH_D, dz_D (written
+// for the key kernel). Rows of phi(Q) and dnum in LDS are padded by 4 floats
+// and the dQ loop takes channels part + 8 i, so that the 8 rows or channels a
+// wave reads at once fall in different banks. Heads whose branch is off and
 // blocks that dropped nothing write zeros.
+template <int D>
+struct LinRowsLds {
+  static constexpr int HP = D + 4, FP = D + 4, CH = 32, TILE = D * BK * 2;
+  // part one: four stages of (phi(K)^T, V^T); part two reuses the space
+  static constexpr int STAGE = 2 * TILE, NBUF = 4, BUFS = NBUF * STAGE;
+  static constexpr int HS = 0, ZS = HS + D * HP * 4, FQ = ZS + D * 4, DN = FQ + CH * FP * 4,
+                       DDEN = DN + CH * FP * 4, PART2 = DDEN + CH * 4;
+  static constexpr int LIST = (BUFS > PART2 ? BUFS : PART2), BITS = LIST + kMaxLinKeyBlocks / 2 * 4,
+                       BYTES = BITS + kMaxLinKeyBlocks / 8;
+};
+
 template <int D>
 __global__ __launch_bounds__(256, 1) void linear_bwd_rows_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ dO,
@@ -626,14 +642,20 @@ __global__ __launch_bounds__(256, 1) void linear_bwd_rows_kernel(
     const int32_t* __restrict__ lin_on, const float* __restrict__ alpha, int mode,
     float* __restrict__ dql, float* __restrict__ dHq, float* __restrict__ dzq,
     float* __restrict__ drow, int H, int N, int n_q, int n_k, int NP, int total) {
-  constexpr int DT = D / 32, HP = D + 4, CH = 32, NTILE = DT * DT, TPW = (NTILE + 3) / 4;
+  using T = Tile<D>;
+  using LS = LinRowsLds<D>;
+  constexpr int DT = D / 32, HP = LS::HP, FP = LS::FP, CH = LS::CH, NTILE = DT * DT,
+                TPW = (NTILE + 3) / 4;
   constexpr int AT = D / 16, CPT = D / 8;  // dH entries per thread per side; channels per thread
-  __shared__ __align__(16) float Hs[D * HP];
-  __shared__ __align__(16) float zs[D];
-  __shared__ __align__(16) float fq[CH * D];
-  __shared__ __align__(16) float dn[CH * D];
-  __shared__ float dden_s[CH];
-  __shared__ uint32_t kept_bits[kMaxLinKeyBlocks / 32];
+  constexpr int VU = D * T::VCPR / 256;    // 16-byte copies per thread and tile
+  __shared__ __align__(16) unsigned char smem[LS::BYTES];
+  float* const Hs = reinterpret_cast<float*>(smem + LS::HS);
+  float* const zs = reinterpret_cast<float*>(smem + LS::ZS);
+  float* const fq = reinterpret_cast<float*>(smem + LS::FQ);
+  float* const dn = reinterpret_cast<float*>(smem + LS::DN);
+  float* const dden_s = reinterpret_cast<float*>(smem + LS::DDEN);
+  int32_t* const clist = reinterpret_cast<int32_t*>(smem + LS::LIST);
+  uint32_t* const kept_bits = reinterpret_cast<uint32_t*>(smem + LS::BITS);
 
   const int tile = xcd_remap(blockIdx.x, total);
   const int bh = tile / n_q, qi = tile % n_q, h = bh % H;
@@ -672,7 +694,59 @@ __global__ __launch_bounds__(256, 1) void linear_bwd_rows_kernel(
     atomicOr(&kept_bits[j >> 5], 1u << (j & 31));
   }
   __syncthreads();
-  const bool use_kept = count <= n_k - count;
+  // wave 0 lists the blocks not listed in increasing order (at most CAP of
+  // them) and counts them; that list is used when it is the shorter one
+  constexpr int CAP = kMaxLinKeyBlocks / 2 - 1;  // clist[CAP] holds the count
+  if (wave == 0) {
+    int base = 0;
+    for (int w0 = 0; w0 < words; w0 += 64) {
+      const int w = w0 + lane;
+      uint32_t inv = 0u;
+      if (w < words) {
+        inv = ~kept_bits[w];
+        if (32 * w + 32 > n_k) inv &= (1u << (n_k - 32 * w)) - 1u;
+      }
+      const int c1 = __popc(inv);
+      int incl = c1;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+      }
+      int pos = base + incl - c1;
+      while (inv) {
+        if (pos < CAP) clist[pos] = 32 * w + __ffs(inv) - 1;
+        ++pos;
+        inv &= inv - 1u;
+      }
+      base += __shfl(incl, 63);
+    }
+    if (lane == 0) clist[CAP] = base;
+  }
+  __syncthreads();
+  const int n_off = __builtin_amdgcn_readfirstlane(clist[CAP]);
+  const bool use_kept = !(n_off < count && n_off <= CAP);
+  const int L = use_kept ? count : n_off;
+  auto blk = [&](int e) {
+    return use_kept ? min(max(ids[e], 0), n_k - 1) : __builtin_amdgcn_readfirstlane(clist[e]);
+  };
+  uint32_t vofs[VU];  // per-thread source offsets (elements) of the tile copies
+#pragma unroll
+  for (int u = 0; u < VU; ++u) {
+    const int p = u * 256 + th, r = p / T::VCPR;
+    vofs[u] = (uint32_t)(r * BK + T::vchunk(r, p % T::VCPR) * 8);
+  }
+  const size_t vtile = (size_t)D * BK;
+  auto issue = [&](int j, int b) {  // 2 VU copies per thread, the same for every wave
+    const uint16_t* pk = phikt + ((size_t)bh * n_k + j) * vtile;
+    const uint16_t* pv = vt + ((size_t)bh * n_k + j) * vtile;
+    unsigned char* dst = smem + b * LS::STAGE + (wave * 64) * 16;
+#pragma unroll
+    for (int u = 0; u < VU; ++u) {
+      dma16(pk + vofs[u], dst + u * 256 * 16);
+      dma16(pv + vofs[u], dst + LS::TILE + u * 256 * 16);
+    }
+  };
   floatx16 acc[TPW];
   float zp[TPW];
 #pragma unroll
@@ -681,10 +755,21 @@ __global__ __launch_bounds__(256, 1) void linear_bwd_rows_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[s2][r] = 0.0f;
   }
-  const size_t vtile = (size_t)D * BK;
-  auto add_block = [&](int j) {
-    const uint16_t* pk = phikt + ((size_t)bh * n_k + j) * vtile;
-    const uint16_t* pv = vt + ((size_t)bh * n_k + j) * vtile;
+  const int pre = min(L, LS::NBUF - 1);
+  for (int e = 0; e < pre; ++e) issue(blk(e), e);
+  for (int e = 0; e < L; ++e) {
+    const int ahead = min(L - 1 - e, LS::NBUF - 2);  // later blocks already in flight
+    static_assert(2 * VU * (LS::NBUF - 2) <= 63, "vmcnt range");
+    if (ahead >= 2)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | ((4 * VU) & 15) | (((4 * VU) >> 4) << 14));
+    else if (ahead == 1)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | ((2 * VU) & 15) | (((2 * VU) >> 4) << 14));
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+    barrier_no_fence();  // block e landed for every wave; the buffer of block e - 1 is free
+    if (e + LS::NBUF - 1 < L) issue(blk(e + LS::NBUF - 1), (e + LS::NBUF - 1) % LS::NBUF);
+    const unsigned char* pkb = smem + (e % LS::NBUF) * LS::STAGE;
+    const unsigned char* pvb = pkb + LS::TILE;
 #pragma unroll
     for (int s2 = 0; s2 < TPW; ++s2) {
       const int t = wave + 4 * s2;
@@ -692,23 +777,19 @@ __global__ __launch_bounds__(256, 1) void linear_bwd_rows_kernel(
         const int ra = t / DT, rc = t % DT;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(pk + (size_t)(32 * ra + l32) * BK + 16 * g + 8 * h2);
-          const bf16x8 b = *reinterpret_cast<const bf16x8*>(pv + (size_t)(32 * rc + l32) * BK + 16 * g + 8 * h2);
-          acc[s2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[s2], 0, 0, 0);
+          const int rowa = 32 * ra + l32, rowb = 32 * rc + l32;
+          const bf16x8 av = lds_read16(pkb + rowa * T::VROWB + T::vchunk(rowa, 2 * g + h2) * 16);
+          const bf16x8 bv = lds_read16(pvb + rowb * T::VROWB + T::vchunk(rowb, 2 * g + h2) * 16);
+          acc[s2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[s2], 0, 0, 0);
           if (rc == 0) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) zp[s2] += (float)a[e];
+            for (int e2 = 0; e2 < 8; ++e2) zp[s2] += (float)av[e2];
           }
         }
       }
     }
-  };
-  if (use_kept) {
-    for (int e = 0; e < count; ++e) add_block(min(max(ids[e], 0), n_k - 1));
-  } else {
-    for (int j = 0; j < n_k; ++j)
-      if (!((kept_bits[j >> 5] >> (j & 31)) & 1u)) add_block(j);
   }
+  __syncthreads();  // every wave is done with the stage buffers, which Hs overlays
   const float* Ht = lin_h + (size_t)bh * D * D;
 #pragma unroll
   for (int s2 = 0; s2 < TPW; ++s2) {
@@ -752,8 +833,8 @@ __global__ __launch_bounds__(256, 1) void linear_bwd_rows_kernel(
           f[2 * e + 1] = elu1(bf16_hi(w[e]));
         }
       }
-      *reinterpret_cast<float4*>(fq + tt * D + c8) = make_float4(f[0], f[1], f[2], f[3]);
-      *reinterpret_cast<float4*>(fq + tt * D + c8 + 4) = make_float4(f[4], f[5], f[6], f[7]);
+      *reinterpret_cast<float4*>(fq + tt * FP + c8) = make_float4(f[0], f[1], f[2], f[3]);
+      *reinterpret_cast<float4*>(fq + tt * FP + c8 + 4) = make_float4(f[4], f[5], f[6], f[7]);
     }
     __syncthreads();
     // num_t = phi(Q_t) H_D for this thread's channels, den_t = phi(Q_t) . z_D
@@ -761,7 +842,7 @@ __global__ __launch_bounds__(256, 1) void linear_bwd_rows_kernel(
 #pragma unroll
     for (int cc = 0; cc < CPT; ++cc) num[cc] = 0.0f;
     for (int a = 0; a < D; ++a) {
-      const float f = fq[t * D + a];
+      const float f = fq[t * FP + a];
 #pragma unroll
       for (int cc = 0; cc < CPT; cc += 4) {
         const float4 hv = *reinterpret_cast<const float4*>(Hs + a * HP + cb + cc);
@@ -772,7 +853,7 @@ __global__ __launch_bounds__(256, 1) void linear_bwd_rows_kernel(
       }
     }
     float den = 0.0f;
-    for (int a = cb; a < cb + CPT; ++a) den = fmaf(fq[t * D + a], zs[a], den);
+    for (int a = cb; a < cb + CPT; ++a) den = fmaf(fq[t * FP + a], zs[a], den);
     den += __shfl_xor(den, 4);
     den += __shfl_xor(den, 2);
     den += __shfl_xor(den, 1);
@@ -802,7 +883,7 @@ __global__ __launch_bounds__(256, 1) void linear_bwd_rows_kernel(
 #pragma unroll
     for (int cc = 0; cc < CPT; ++cc) {
       corr = fmaf(g[cc], num[cc] * inv_den, corr);  // G . O_l
-      dn[t * D + cb + cc] = g[cc] * inv_den;          // dnum
+      dn[t * FP + cb + cc] = g[cc] * inv_den;         // dnum
     }
     corr += __shfl_xor(corr, 4);
     corr += __shfl_xor(corr, 2);
@@ -812,20 +893,23 @@ __global__ __launch_bounds__(256, 1) void linear_bwd_rows_kernel(
       if (live) drow[(size_t)bh * NP + row] -= corr;
     }
     __syncthreads();
-    // dQ_l = (H_D dnum + z_D dden) phi'(Q), phi' = 1 where phi > 1, else phi
+    // dQ_l = (H_D dnum + z_D dden) phi'(Q), phi' = 1 where phi > 1, else phi;
+    // this thread takes channels part + 8 i
     if (live) {
       const float ddn = dden_s[t];
-      for (int a = cb; a < cb + CPT; ++a) {
+#pragma unroll 2
+      for (int i = 0; i < CPT; ++i) {
+        const int a = part + 8 * i;
         float acc2 = zs[a] * ddn;
         for (int cc = 0; cc < D; cc += 4) {
           const float4 hv = *reinterpret_cast<const float4*>(Hs + a * HP + cc);
-          const float4 dv4 = *reinterpret_cast<const float4*>(dn + t * D + cc);
+          const float4 dv4 = *reinterpret_cast<const float4*>(dn + t * FP + cc);
           acc2 = fmaf(hv.x, dv4.x, acc2);
           acc2 = fmaf(hv.y, dv4.y, acc2);
           acc2 = fmaf(hv.z, dv4.z, acc2);
           acc2 = fmaf(hv.w, dv4.w, acc2);
         }
-        const float f = fq[t * D + a];
+        const float f = fq[t * FP + a];
         dql[head + (size_t)row * D + a] = acc2 * (f > 1.0f ? 1.0f : f);
       }
     }
@@ -834,8 +918,8 @@ __global__ __launch_bounds__(256, 1) void linear_bwd_rows_kernel(
       float fa[AT], dc[AT];
 #pragma unroll
       for (int i = 0; i < AT; i += 4) {
-        const float4 x = *reinterpret_cast<const float4*>(fq + t2 * D + a0 + i);
-        const float4 y = *reinterpret_cast<const float4*>(dn + t2 * D + c0 + i);
+        const float4 x = *reinterpret_cast<const float4*>(fq + t2 * FP + a0 + i);
+        const float4 y = *reinterpret_cast<const float4*>(dn + t2 * FP + c0 + i);
         fa[i] = x.x; fa[i + 1] = x.y; fa[i + 2] = x.z; fa[i + 3] = x.w;
         dc[i] = y.x; dc[i + 1] = y.y; dc[i + 2] = y.z; dc[i + 3] = y.w;
       }

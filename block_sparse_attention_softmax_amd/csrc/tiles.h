@@ -116,6 +116,18 @@ __device__ __forceinline__ void dma16(const void* src, void* lds) {
   __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
 }
 
+// Workgroup barrier without the memory fence of __syncthreads, whose release
+// half waits for every direct-to-LDS copy still in flight, prefetches of later
+// stages included. Callers first wait (s_waitcnt vmcnt) for the copies the
+// next step reads; every LDS read of a buffer is consumed before the barrier
+// after which that buffer is refilled. The empty asm statements keep the
+// compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void barrier_no_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // two floats -> two bf16 (round to nearest even) in one dword, low half first
 __device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
