@@ -226,22 +226,44 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)(p);
 }
 
-// Four transposing LDS reads (ds_read_b64_tr_b16): within each group of 16
-// lanes, lane i receives element i & 3 of the 4-element rows that lanes
-// 4e + (i >> 2), e = 0..3, address. Written as one asm block that also waits
-// for them: as a builtin the compiler holds such a read until every
+// NR transposing LDS reads (ds_read_b64_tr_b16; NR = 8 or 16): within each
+// group of 16 lanes, lane i receives element i & 3 of the 4-element rows that
+// lanes 4e + (i >> 2), e = 0..3, address. Written as one asm block that also
+// waits for them: as a builtin the compiler holds such a read until every
 // direct-to-LDS copy in flight has landed, the next stage's included.
-__device__ __forceinline__ void lds_read_tr4(v4i16& r0, v4i16& r1, v4i16& r2, v4i16& r3,
-                                             uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3) {
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %4\n\t"
-      "ds_read_b64_tr_b16 %1, %5\n\t"
-      "ds_read_b64_tr_b16 %2, %6\n\t"
-      "ds_read_b64_tr_b16 %3, %7\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
-      : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
-      : "memory");
+template <int NR>
+__device__ __forceinline__ void lds_read_tr(v4i16 (&r)[NR], const uint32_t (&a)[NR]) {
+  static_assert(NR == 8 || NR == 16, "8 or 16 reads");
+  if constexpr (NR == 8) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n\tds_read_b64_tr_b16 %1, %9\n\t"
+        "ds_read_b64_tr_b16 %2, %10\n\tds_read_b64_tr_b16 %3, %11\n\t"
+        "ds_read_b64_tr_b16 %4, %12\n\tds_read_b64_tr_b16 %5, %13\n\t"
+        "ds_read_b64_tr_b16 %6, %14\n\tds_read_b64_tr_b16 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+          "=&v"(r[6]), "=&v"(r[7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %16\n\tds_read_b64_tr_b16 %1, %17\n\t"
+        "ds_read_b64_tr_b16 %2, %18\n\tds_read_b64_tr_b16 %3, %19\n\t"
+        "ds_read_b64_tr_b16 %4, %20\n\tds_read_b64_tr_b16 %5, %21\n\t"
+        "ds_read_b64_tr_b16 %6, %22\n\tds_read_b64_tr_b16 %7, %23\n\t"
+        "ds_read_b64_tr_b16 %8, %24\n\tds_read_b64_tr_b16 %9, %25\n\t"
+        "ds_read_b64_tr_b16 %10, %26\n\tds_read_b64_tr_b16 %11, %27\n\t"
+        "ds_read_b64_tr_b16 %12, %28\n\tds_read_b64_tr_b16 %13, %29\n\t"
+        "ds_read_b64_tr_b16 %14, %30\n\tds_read_b64_tr_b16 %15, %31\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+          "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]),
+          "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]),
+          "v"(a[8]), "v"(a[9]), "v"(a[10]), "v"(a[11]), "v"(a[12]), "v"(a[13]), "v"(a[14]),
+          "v"(a[15])
+        : "memory");
+  }
 }
 
 __device__ __forceinline__ bf16x8 join_tr(v4i16 lo, v4i16 hi) {
@@ -376,15 +398,25 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void sparse_attn_bwd_dkdv_ke
         const bf16x8 sb2 = pack_bf16x8(dP, 8 * t);
         const int R0 = qb + 16 * t;
         const int C0 = (R0 >> 2) & 3, C1 = ((R0 + 8) >> 2) & 3;
+        // all of the half's fragments in one block of reads, then its products
+        uint32_t ad[4 * DT];
+        v4i16 fr[4 * DT];
 #pragma unroll
         for (int ii = 0; ii < DT; ++ii) {
           const uint32_t o0 = (uint32_t)(R0 * RT::ROWB + (((4 * ii + C0) ^ tr_lane) << 4));
           const uint32_t o1 = (uint32_t)((R0 + 8) * RT::ROWB + (((4 * ii + C1) ^ tr_lane) << 4));
-          v4i16 d0, d1, q0, q1;
-          lds_read_tr4(d0, d1, q0, q1, bufa + ST::DS + o0, bufa + ST::DS + o1, bufa + ST::QS + o0,
-                       bufa + ST::QS + o1);
-          dva[ii] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join_tr(d0, d1), pb, dva[ii], 0, 0, 0);
-          dka[ii] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join_tr(q0, q1), sb2, dka[ii], 0, 0, 0);
+          ad[4 * ii] = bufa + ST::DS + o0;
+          ad[4 * ii + 1] = bufa + ST::DS + o1;
+          ad[4 * ii + 2] = bufa + ST::QS + o0;
+          ad[4 * ii + 3] = bufa + ST::QS + o1;
+        }
+        lds_read_tr<4 * DT>(fr, ad);
+#pragma unroll
+        for (int ii = 0; ii < DT; ++ii) {
+          dva[ii] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join_tr(fr[4 * ii], fr[4 * ii + 1]), pb,
+                                                            dva[ii], 0, 0, 0);
+          dka[ii] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join_tr(fr[4 * ii + 2], fr[4 * ii + 3]),
+                                                            sb2, dka[ii], 0, 0, 0);
         }
       }
     }
