@@ -364,13 +364,17 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void sparse_attn_bwd_dkdv_ke
 #pragma unroll
       for (int r = 0; r < 16; ++r) S[r] = dP[r] = 0.0f;
       const int qr = qb + l32;
+      bf16x8 fa[KSTEPS], fb[KSTEPS];  // every fragment first: one wait, not one per k-step
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) {
         const int ch = RT::chunk(qr, 2 * s + h2);
-        const bf16x8 a = lds_read16(buf + ST::QS + qr * RT::ROWB + ch * 16);
-        const bf16x8 b = lds_read16(buf + ST::DS + qr * RT::ROWB + ch * 16);
-        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[s], S, 0, 0, 0);
-        dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, vf[s], dP, 0, 0, 0);
+        fa[s] = lds_read16(buf + ST::QS + qr * RT::ROWB + ch * 16);
+        fb[s] = lds_read16(buf + ST::DS + qr * RT::ROWB + ch * 16);
+      }
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) {
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s], kf[s], S, 0, 0, 0);
+        dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[s], vf[s], dP, 0, 0, 0);
       }
       // P = 2^(S c - lse2), dS = P (dP - D); register r holds row
       // qb + 8*(r/4) + 4*h2 + r%4 (the row terms are read as 16-byte

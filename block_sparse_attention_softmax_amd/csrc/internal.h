@@ -151,7 +151,7 @@ struct Svg2Launch {
   double p;
   int max_tiles, max_chunks;  // padded query tiles / 64-key chunks per (b, h), upper bounds
   // workspace (svg2_layout)
-  double *xq, *xk, *dot, *centq, *centk, *normq, *normk, *clog;
+  double *xq, *xk, *centq, *centk, *normq, *normk, *clog;
   int32_t *assign_q, *assign_k, *rank, *ccount, *size_q, *size_k, *off_q, *off_k, *perm_q,
       *perm_k;
   uint32_t* sbits;

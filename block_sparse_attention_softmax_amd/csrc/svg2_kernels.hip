@@ -3,8 +3,9 @@
 //  1. k-means on the query tokens (C_q clusters) and, independently, on the
 //     key tokens (C_k clusters): Lloyd's rounds in float64 from centroids at
 //     tokens floor(c N / C); distances |c|^2 - 2 x.c on the float64 matrix
-//     cores (the rows-against-rows product of the mask), argmin with ties to
-//     the lower cluster; centroids the mean of their members in token order.
+//     cores with the argmin (ties to the lower cluster) taken in the same
+//     kernel, so no distance matrix is stored; centroids the mean of their
+//     members in token order.
 //  2. the permutation: a stable counting sort of the tokens by cluster, so
 //     each cluster is contiguous (ranks inside 64-token chunks by lane
 //     comparisons, per-chunk counts, scans; no atomics, so the order is
@@ -66,35 +67,96 @@ __global__ __launch_bounds__(D) void km_init_kernel(const double* __restrict__ x
   if (t == 0) cnorm[(size_t)bh * C + c] = s;
 }
 
-// assign[t] = argmin_c (|c|^2 - 2 dot[t][c]), ties to the lower c. One wave
-// per token, lanes over the clusters.
-__global__ __launch_bounds__(256) void km_argmin_kernel(const double* __restrict__ dot,
-                                                        const double* __restrict__ cnorm,
-                                                        int32_t* __restrict__ assign, int N,
-                                                        int C, size_t total) {
-  const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= total) return;
-  const size_t bh = row / N;
-  double best = INFINITY;
-  int bi = C;
-  for (int c = lane; c < C; c += 64) {
-    const double v = cnorm[bh * C + c] - 2.0 * dot[row * C + c];
-    if (v < best) {  // lanes visit their clusters in increasing order
-      best = v;
-      bi = c;
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+// assign[t] = argmin_c (|c|^2 - 2 x_t . c), ties to the lower c, without
+// storing the distances. Workgroup (64 tokens, b, h): wave w holds tokens
+// 16 w .. 16 w + 15 in registers (lane: token 16 w + lane % 16, channels
+// 8 s + 2 (lane / 16) + 0..1), the centroids stream through LDS 64 at a time
+// (rows padded by two doubles so that 16 lanes reading 16 rows hit different
+// banks), and each lane keeps the best of its column of every 16 x 16 product
+// for the 4 tokens it holds; the 16 lanes of a token group merge at the end.
+// The float64 products run in the instruction order of block_logits_kernel
+// (two 16x16x4 steps per 8 channels, per accumulator), so every distance has
+// the bits of the distance-matrix route it replaces.
+template <int D>
+__global__ __launch_bounds__(256, 2) void km_assign_kernel(const double* __restrict__ x,
+                                                           const double* __restrict__ cent,
+                                                           const double* __restrict__ cnorm,
+                                                           int32_t* __restrict__ assign, int N,
+                                                           int C) {
+  constexpr int CT = 64, RP = D + 2;  // centroids per tile; LDS row (doubles)
+  __shared__ __align__(16) double cs[CT * RP];
+  __shared__ double cn[CT];
+  const int bh = blockIdx.y, t0 = blockIdx.x * 64;
+  const int th = threadIdx.x, lane = th & 63, wave = th >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const size_t xb = (size_t)bh * N;
+  const int tok = min(t0 + 16 * wave + r, N - 1);  // tokens past N are computed, not stored
+  double2 xr[D / 8];
+#pragma unroll
+  for (int s = 0; s < D / 8; ++s)
+    xr[s] = *reinterpret_cast<const double2*>(x + (xb + tok) * D + 8 * s + 2 * g);
+  double best[4] = {INFINITY, INFINITY, INFINITY, INFINITY};
+  int bi[4] = {C, C, C, C};
+  const double* cb0 = cent + (size_t)bh * C * D;
+  for (int cb = 0; cb < C; cb += CT) {
+    __syncthreads();  // the previous tile is consumed
+    for (int p = th; p < CT * D / 2; p += 256) {
+      const int row = p / (D / 2), c2 = p % (D / 2);
+      const int cr = min(cb + row, C - 1);
+      *reinterpret_cast<double2*>(cs + row * RP + 2 * c2) =
+          *reinterpret_cast<const double2*>(cb0 + (size_t)cr * D + 2 * c2);
+    }
+    if (th < CT) cn[th] = cnorm[(size_t)bh * C + min(cb + th, C - 1)];
+    __syncthreads();
+    f64x4 acc[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[b] = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll 4
+    for (int s = 0; s < D / 8; ++s) {
+      double2 y[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        y[b] = *reinterpret_cast<const double2*>(cs + (16 * b + r) * RP + 8 * s + 2 * g);
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        acc[b] = __builtin_amdgcn_mfma_f64_16x16x4f64(xr[s].x, y[b].x, acc[b], 0, 0, 0);
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        acc[b] = __builtin_amdgcn_mfma_f64_16x16x4f64(xr[s].y, y[b].y, acc[b], 0, 0, 0);
+    }
+    // lane: tokens 4 e + g of the wave's 16, centroid cb + 16 b + r (increasing)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int c = cb + 16 * b + r;
+      if (c < C) {
+        const double cnc = cn[16 * b + r];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const double v = cnc - 2.0 * acc[b][e];
+          if (v < best[e]) {
+            best[e] = v;
+            bi[e] = c;
+          }
+        }
+      }
     }
   }
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const double ob = __shfl_xor(best, off);
-    const int oi = __shfl_xor(bi, off);
-    if (ob < best || (ob == best && oi < bi)) {
-      best = ob;
-      bi = oi;
+  for (int e = 0; e < 4; ++e) {
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const double ob = __shfl_xor(best[e], off);
+      const int oi = __shfl_xor(bi[e], off);
+      if (ob < best[e] || (ob == best[e] && oi < bi[e])) {
+        best[e] = ob;
+        bi[e] = oi;
+      }
     }
+    const int t = t0 + 16 * wave + 4 * e + g;
+    if (r == 0 && t < N) assign[xb + t] = bi[e];
   }
-  if (lane == 0) assign[row] = bi;
 }
 
 // Stable counting sort by cluster, step 1: per 64-token chunk (one wave),
@@ -123,31 +185,60 @@ __global__ __launch_bounds__(256) void km_rank_kernel(const int32_t* __restrict_
   }
 }
 
-// Step 2, per (b, h): exclusive scan of each cluster's counts over the chunks
-// (in place), the cluster sizes, and the clusters' offsets.
-__global__ __launch_bounds__(256) void km_scan_kernel(int32_t* __restrict__ ccount,
-                                                      int32_t* __restrict__ size,
-                                                      int32_t* __restrict__ off, int C, int nch) {
-  const int bh = blockIdx.x;
-  for (int c = threadIdx.x; c < C; c += 256) {
-    int run = 0;
-    for (int ch = 0; ch < nch; ++ch) {
-      int32_t* p = ccount + ((size_t)bh * nch + ch) * C + c;
-      const int x = *p;
-      *p = run;
-      run += x;
-    }
-    size[(size_t)bh * C + c] = run;
-  }
+// Step 2: ccount[bh][ch][c] becomes the number of tokens of cluster c in the
+// chunks before ch, and size[c] the cluster's total. Workgroup (64 clusters,
+// b, h): lanes over clusters (coalesced rows), the 4 waves over quarters of
+// the chunks, their sums combined through LDS.
+__global__ __launch_bounds__(256) void km_colscan_kernel(int32_t* __restrict__ ccount,
+                                                         int32_t* __restrict__ size, int C,
+                                                         int nch) {
+  __shared__ int part[4][64];
+  const int bh = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = blockIdx.x * 64 + lane;
+  const int q = (nch + 3) / 4, ch0 = min(wave * q, nch), ch1 = min(ch0 + q, nch);
+  int32_t* col = ccount + (size_t)bh * nch * C + c;
+  int sum = 0;
+  if (c < C)
+    for (int ch = ch0; ch < ch1; ++ch) sum += col[(size_t)ch * C];
+  part[wave][lane] = sum;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int c = 0; c < C; ++c) {
-      off[(size_t)bh * (C + 1) + c] = run;
-      run += size[(size_t)bh * C + c];
+  int run = 0;
+  for (int w = 0; w < wave; ++w) run += part[w][lane];
+  if (c < C) {
+    for (int ch = ch0; ch < ch1; ++ch) {
+      const int v = col[(size_t)ch * C];
+      col[(size_t)ch * C] = run;
+      run += v;
     }
-    off[(size_t)bh * (C + 1) + C] = run;
+    if (wave == 3) size[(size_t)bh * C + c] = run;
   }
+}
+
+// off[bh][c] = the clusters before c in size order, off[bh][C] = N. One
+// workgroup per (b, h), 256 clusters per pass with a carry.
+__global__ __launch_bounds__(256) void km_offsets_kernel(const int32_t* __restrict__ size,
+                                                         int32_t* __restrict__ off, int C) {
+  __shared__ int wsum[4];
+  const int bh = blockIdx.x, th = threadIdx.x, lane = th & 63, wave = th >> 6;
+  int carry = 0;
+  for (int base = 0; base < C; base += 256) {
+    const int c = base + th;
+    const int v = c < C ? size[(size_t)bh * C + c] : 0;
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int wbase = 0;
+    for (int w = 0; w < wave; ++w) wbase += wsum[w];
+    if (c < C) off[(size_t)bh * (C + 1) + c] = carry + wbase + incl - v;
+    carry += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();  // wsum is reused
+  }
+  if (th == 0) off[(size_t)bh * (C + 1) + C] = carry;
 }
 
 // Step 3: perm[off[c] + base[chunk][c] + rank] = token.
@@ -434,15 +525,15 @@ hipError_t kmeans_run(const Svg2Launch& a, const double* x, int C, double* cent,
   const size_t rows = (size_t)BH * a.N, chunks = (size_t)BH * nch, cc = chunks * C;
   hipLaunchKernelGGL((km_init_kernel<D>), dim3(C, BH), dim3(D), 0, s, x, cent, cnorm, a.N, C);
   for (int it = 0; it <= a.iters; ++it) {
-    hipError_t e = launch_scores_f64(x, cent, a.dot, BH, a.N, C, D, 1.0, s);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(km_argmin_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a.dot,
-                       cnorm, assign, a.N, C, rows);
+    hipLaunchKernelGGL((km_assign_kernel<D>), dim3(nch, BH), dim3(256), 0, s, x, cent, cnorm,
+                       assign, a.N, C);
     hipLaunchKernelGGL(fill_i32_zero_kernel, dim3((unsigned)std::min<size_t>((cc + 255) / 256, 4096)),
                        dim3(256), 0, s, a.ccount, cc);
     hipLaunchKernelGGL(km_rank_kernel, dim3((unsigned)((chunks + 3) / 4)), dim3(256), 0, s, assign,
                        a.rank, a.ccount, a.N, C, nch, chunks);
-    hipLaunchKernelGGL(km_scan_kernel, dim3(BH), dim3(256), 0, s, a.ccount, size, off, C, nch);
+    hipLaunchKernelGGL(km_colscan_kernel, dim3((C + 63) / 64, BH), dim3(256), 0, s, a.ccount, size,
+                       C, nch);
+    hipLaunchKernelGGL(km_offsets_kernel, dim3(BH), dim3(256), 0, s, size, off, C);
     hipLaunchKernelGGL(km_scatter_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s,
                        assign, a.rank, a.ccount, off, perm, a.N, C, nch, rows);
     if (it < a.iters)
@@ -530,7 +621,6 @@ size_t svg2_layout(Svg2Launch& a, unsigned char* w) {
   };
   a.xq = reinterpret_cast<double*>(take(BH * N * d * 8));
   a.xk = reinterpret_cast<double*>(take(BH * N * d * 8));
-  a.dot = reinterpret_cast<double*>(take(BH * N * Cm * 8));
   a.centq = reinterpret_cast<double*>(take(BH * a.Cq * d * 8));
   a.centk = reinterpret_cast<double*>(take(BH * a.Ck * d * 8));
   a.normq = reinterpret_cast<double*>(take(BH * a.Cq * 8));

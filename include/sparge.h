@@ -308,8 +308,8 @@ int sparge_attn_fwd_lowbit(const void* q, const void* k, const void* v,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* Device workspace (bytes) of svg2_attn_fwd (float64 copies of Q and K, the
- * token-by-centroid distances, the clustering, the selection and the padded
- * permuted Q, K, V); 0 for arguments svg2_attn_fwd would reject. */
+ * clustering, the selection and the padded permuted Q, K, V); 0 for arguments
+ * svg2_attn_fwd would reject. */
 size_t svg2_attn_workspace_bytes(int B, int H, int N, int d, int block_q, int n_q_clusters,
                                  int n_k_clusters);
 
