@@ -644,7 +644,6 @@ __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void sparse
 // and each dropped key u gets dphi(K_u) += dH_D V_u + dz_D, dV_u += phi(K_u) dH_D.
 // The sparse part's D_t = dO_t . O_s,t equals dO_t . O_t - G_t . O_l,t, so the
 // row kernel subtracts G . O_l from D.
-constexpr int kMaxLinKeyBlocks = 4096;  // capacity of the per-row kept bitmap
 
 // Per (b, h, query block of D rows), 4 waves. First H_D, z_D on the matrix
 // cores from the packed phi(K)^T and V^T tiles of whichever list is shorter:
@@ -658,16 +657,6 @@ constexpr int kMaxLinKeyBlocks = 4096;  // capacity of the per-row kept bitmap
 // and the dQ loop takes channels part + 8 i, so that the 8 rows or channels a
 // wave reads at once fall in different banks. Heads whose branch is off and
 // blocks that dropped nothing write zeros.
-template <int D>
-struct LinRowsLds {
-  static constexpr int HP = D + 4, FP = D + 4, CH = 32, TILE = D * BK * 2;
-  // part one: four stages of (phi(K)^T, V^T); part two reuses the space
-  static constexpr int STAGE = 2 * TILE, NBUF = 4, BUFS = NBUF * STAGE;
-  static constexpr int HS = 0, ZS = HS + D * HP * 4, FQ = ZS + D * 4, DN = FQ + CH * FP * 4,
-                       DDEN = DN + CH * FP * 4, PART2 = DDEN + CH * 4;
-  static constexpr int LIST = (BUFS > PART2 ? BUFS : PART2), BITS = LIST + kMaxLinKeyBlocks / 2 * 4,
-                       BYTES = BITS + kMaxLinKeyBlocks / 8;
-};
 
 template <int D>
 __global__ __launch_bounds__(256, 1) void linear_bwd_rows_kernel(
@@ -678,26 +667,19 @@ __global__ __launch_bounds__(256, 1) void linear_bwd_rows_kernel(
     const int32_t* __restrict__ lin_on, const float* __restrict__ alpha, int mode,
     float* __restrict__ dql, float* __restrict__ dHq, float* __restrict__ dzq,
     float* __restrict__ drow, int H, int N, int n_q, int n_k, int NP, int total) {
-  using T = Tile<D>;
   using LS = LinRowsLds<D>;
-  constexpr int DT = D / 32, HP = LS::HP, FP = LS::FP, CH = LS::CH, NTILE = DT * DT,
-                TPW = (NTILE + 3) / 4;
+  constexpr int HP = LS::HP, FP = LS::FP, CH = LS::CH;
   constexpr int AT = D / 16, CPT = D / 8;  // dH entries per thread per side; channels per thread
-  constexpr int VU = D * T::VCPR / 256;    // 16-byte copies per thread and tile
   __shared__ __align__(16) unsigned char smem[LS::BYTES];
-  float* const Hs = reinterpret_cast<float*>(smem + LS::HS);
-  float* const zs = reinterpret_cast<float*>(smem + LS::ZS);
+  const float* const Hs = reinterpret_cast<const float*>(smem + LS::HS);
+  const float* const zs = reinterpret_cast<const float*>(smem + LS::ZS);
   float* const fq = reinterpret_cast<float*>(smem + LS::FQ);
   float* const dn = reinterpret_cast<float*>(smem + LS::DN);
   float* const dden_s = reinterpret_cast<float*>(smem + LS::DDEN);
-  int32_t* const clist = reinterpret_cast<int32_t*>(smem + LS::LIST);
-  uint32_t* const kept_bits = reinterpret_cast<uint32_t*>(smem + LS::BITS);
 
   const int tile = xcd_remap(blockIdx.x, total);
   const int bh = tile / n_q, qi = tile % n_q, h = bh % H;
-  const int th = threadIdx.x, lane = th & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(th >> 6);
-  const int h2 = lane >> 5, l32 = lane & 31;
+  const int th = threadIdx.x;
   const size_t head = (size_t)bh * N * D;
   const int row0 = qi * D;
   const int count = min(max(kv_cnt[tile], 0), n_k);
@@ -721,130 +703,7 @@ __global__ __launch_bounds__(256, 1) void linear_bwd_rows_kernel(
   }
 
   // ---- H_D and z_D
-  const int words = (n_k + 31) / 32;
-  for (int w = th; w < words; w += 256) kept_bits[w] = 0u;
-  __syncthreads();
-  const int32_t* ids = kv_idx + (size_t)tile * n_k;
-  for (int e = th; e < count; e += 256) {
-    const int j = min(max(ids[e], 0), n_k - 1);
-    atomicOr(&kept_bits[j >> 5], 1u << (j & 31));
-  }
-  __syncthreads();
-  // wave 0 lists the blocks not listed in increasing order (at most CAP of
-  // them) and counts them; that list is used when it is the shorter one
-  constexpr int CAP = kMaxLinKeyBlocks / 2 - 1;  // clist[CAP] holds the count
-  if (wave == 0) {
-    int base = 0;
-    for (int w0 = 0; w0 < words; w0 += 64) {
-      const int w = w0 + lane;
-      uint32_t inv = 0u;
-      if (w < words) {
-        inv = ~kept_bits[w];
-        if (32 * w + 32 > n_k) inv &= (1u << (n_k - 32 * w)) - 1u;
-      }
-      const int c1 = __popc(inv);
-      int incl = c1;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(incl, off);
-        if (lane >= off) incl += y;
-      }
-      int pos = base + incl - c1;
-      while (inv) {
-        if (pos < CAP) clist[pos] = 32 * w + __ffs(inv) - 1;
-        ++pos;
-        inv &= inv - 1u;
-      }
-      base += __shfl(incl, 63);
-    }
-    if (lane == 0) clist[CAP] = base;
-  }
-  __syncthreads();
-  const int n_off = __builtin_amdgcn_readfirstlane(clist[CAP]);
-  const bool use_kept = !(n_off < count && n_off <= CAP);
-  const int L = use_kept ? count : n_off;
-  auto blk = [&](int e) {
-    return use_kept ? min(max(ids[e], 0), n_k - 1) : __builtin_amdgcn_readfirstlane(clist[e]);
-  };
-  uint32_t vofs[VU];  // per-thread source offsets (elements) of the tile copies
-#pragma unroll
-  for (int u = 0; u < VU; ++u) {
-    const int p = u * 256 + th, r = p / T::VCPR;
-    vofs[u] = (uint32_t)(r * BK + T::vchunk(r, p % T::VCPR) * 8);
-  }
-  const size_t vtile = (size_t)D * BK;
-  auto issue = [&](int j, int b) {  // 2 VU copies per thread, the same for every wave
-    const uint16_t* pk = phikt + ((size_t)bh * n_k + j) * vtile;
-    const uint16_t* pv = vt + ((size_t)bh * n_k + j) * vtile;
-    unsigned char* dst = smem + b * LS::STAGE + (wave * 64) * 16;
-#pragma unroll
-    for (int u = 0; u < VU; ++u) {
-      dma16(pk + vofs[u], dst + u * 256 * 16);
-      dma16(pv + vofs[u], dst + LS::TILE + u * 256 * 16);
-    }
-  };
-  floatx16 acc[TPW];
-  float zp[TPW];
-#pragma unroll
-  for (int s2 = 0; s2 < TPW; ++s2) {
-    zp[s2] = 0.0f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[s2][r] = 0.0f;
-  }
-  const int pre = min(L, LS::NBUF - 1);
-  for (int e = 0; e < pre; ++e) issue(blk(e), e);
-  for (int e = 0; e < L; ++e) {
-    const int ahead = min(L - 1 - e, LS::NBUF - 2);  // later blocks already in flight
-    static_assert(2 * VU * (LS::NBUF - 2) <= 63, "vmcnt range");
-    if (ahead >= 2)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | ((4 * VU) & 15) | (((4 * VU) >> 4) << 14));
-    else if (ahead == 1)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | ((2 * VU) & 15) | (((2 * VU) >> 4) << 14));
-    else
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-    barrier_no_fence();  // block e landed for every wave; the buffer of block e - 1 is free
-    if (e + LS::NBUF - 1 < L) issue(blk(e + LS::NBUF - 1), (e + LS::NBUF - 1) % LS::NBUF);
-    const unsigned char* pkb = smem + (e % LS::NBUF) * LS::STAGE;
-    const unsigned char* pvb = pkb + LS::TILE;
-#pragma unroll
-    for (int s2 = 0; s2 < TPW; ++s2) {
-      const int t = wave + 4 * s2;
-      if (t < NTILE) {
-        const int ra = t / DT, rc = t % DT;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int rowa = 32 * ra + l32, rowb = 32 * rc + l32;
-          const bf16x8 av = lds_read16(pkb + rowa * T::VROWB + T::vchunk(rowa, 2 * g + h2) * 16);
-          const bf16x8 bv = lds_read16(pvb + rowb * T::VROWB + T::vchunk(rowb, 2 * g + h2) * 16);
-          acc[s2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[s2], 0, 0, 0);
-          if (rc == 0) {
-#pragma unroll
-            for (int e2 = 0; e2 < 8; ++e2) zp[s2] += (float)av[e2];
-          }
-        }
-      }
-    }
-  }
-  __syncthreads();  // every wave is done with the stage buffers, which Hs overlays
-  const float* Ht = lin_h + (size_t)bh * D * D;
-#pragma unroll
-  for (int s2 = 0; s2 < TPW; ++s2) {
-    const int t = wave + 4 * s2;
-    if (t < NTILE) {
-      const int ra = t / DT, rc = t % DT;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int a = 32 * ra + 8 * (r >> 2) + 4 * h2 + (r & 3), cc = 32 * rc + l32;
-        Hs[a * HP + cc] = use_kept ? Ht[(size_t)a * D + cc] - acc[s2][r] : acc[s2][r];
-      }
-      if (rc == 0) {
-        const float zt = zp[s2] + __shfl_xor(zp[s2], 32);
-        const int a = 32 * ra + l32;
-        if (h2 == 0) zs[a] = use_kept ? lin_z[(size_t)bh * D + a] - zt : zt;
-      }
-    }
-  }
-  __syncthreads();
+  form_hd<D>(smem, phikt, vt, lin_h, lin_z, kv_idx + (size_t)tile * n_k, count, bh, n_k);
 
   // ---- rows, 32 at a time
   float dh[AT][AT], dzacc[AT];
