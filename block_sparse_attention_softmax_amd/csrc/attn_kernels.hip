@@ -46,13 +46,17 @@ constexpr float kRescaleLog2 = 8.0f;
 // so the waves of a CU do not queue behind each other's copies.
 //
 // LIN adds the linear branch over the dropped blocks with a second set of
-// BQ/32 waves in the workgroup (H waves). phi(K)^T tiles are staged beside
-// the V^T tiles; per listed block, H wave w accumulates rows 32w..32w+31 of
-// H_kept += phi(K_j)^T V_j and its share of z_kept += sum phi(K_j), with one
-// barrier per block like the attention waves, whose loop is the plain one.
+// BQ/32 waves in the workgroup (H waves), which pass the attention waves'
+// barriers one for one (the attention waves' loop is the plain one). Per
+// listed block, H wave w accumulates rows 32w..32w+31 of H_kept +=
+// phi(K_j)^T V_j and its share of z_kept += sum phi(K_j), from the V^T tile
+// the attention waves staged and a phi(K)^T tile the H waves copy beside it;
+// when more than half of the blocks are listed they instead sum the blocks
+// not listed (found from a bitmap of the list), copying both tiles of those
+// themselves, and H_D is that sum rather than H_tot - H_kept.
 // The H waves' matrix products fill the attention waves' softmax gaps on the
 // same SIMDs, and the attention waves carry no extra accumulator. At the end
-// the H waves form H_D = H_tot - H_kept and z_D = z_tot - z_kept in LDS, then
+// the H waves form H_D (and z_D likewise) in LDS, then
 // O_l = phi(Q) H_D / (phi(Q) . z_D) for the queries of the attention wave of
 // the same index (three-term split-bf16 MFMA product, about 16 significant
 // bits per operand), and hand O_l and the scale alpha[h] / (phi(Q) . z_D)
@@ -84,11 +88,15 @@ __global__ __launch_bounds__(BQ * (LIN ? 4 : 2), (LIN || (D == 128 && BQ == 64))
   constexpr int KSTEPS = D / 16;
   static_assert(!LIN || NW == DT, "the linear branch needs one wave per 32 rows of d");
 
-  // K0 K1 V0 V1 (LIN: phi(K)^T 0, 1); buffer b of block i is (i + ...) & 1 as below
-  __shared__ __align__(16) unsigned char smem[(LIN ? 6 : 4) * T::BYTES];
+  // K0 K1 V0 V1 (LIN: phi(K)^T 0, 1, the H waves' V^T 0, 1 and the kept-block
+  // bitmap); buffer b of block i is (i + ...) & 1 as below
+  __shared__ __align__(16)
+      unsigned char smem[LIN ? 8 * T::BYTES + kMaxLinKeyBlocks / 8 : 4 * T::BYTES];
   unsigned char* const kbuf = smem;
   unsigned char* const vbuf = smem + 2 * T::BYTES;
   unsigned char* const pbuf = smem + 4 * T::BYTES;
+  unsigned char* const hvbuf = smem + 6 * T::BYTES;
+  uint32_t* const kbits = reinterpret_cast<uint32_t*>(smem + (LIN ? 8 : 4) * T::BYTES);
 
   // with a head selection, LIN runs the (batch, head) pairs whose linear
   // branch is on and the plain kernel the others: the first n_sel * n_q
@@ -172,16 +180,35 @@ __global__ __launch_bounds__(BQ * (LIN ? 4 : 2), (LIN || (D == 128 && BQ == 64))
       }
     }
   };
-  auto stageV = [&](int j, int b) {  // V^T tile (LIN: and the phi(K)^T tile)
+  auto stageV = [&](int j, int b) {  // V^T tile
     const char* vtt = reinterpret_cast<const char*>(vth + (size_t)j * vtile);
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) dma16(vtt + vofs(u), vbuf + b * T::BYTES + 1024 * (u * NW + wave));
-    if constexpr (LIN) {
-      const char* ptt = reinterpret_cast<const char*>(pkh + (size_t)j * vtile);
-#pragma unroll
-      for (int u = 0; u < LOADS; ++u) dma16(ptt + vofs(u), pbuf + b * T::BYTES + 1024 * (u * NW + wave));
-    }
   };
+  auto stageP = [&](int j, int b) {  // phi(K)^T tile (LIN)
+    const char* ptt = reinterpret_cast<const char*>(pkh + (size_t)j * vtile);
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) dma16(ptt + vofs(u), pbuf + b * T::BYTES + 1024 * (u * NW + wave));
+  };
+
+  // LIN: the H waves sum phi(K_j)^T V_j over the listed blocks (H_D = H_tot -
+  // that sum, the listed blocks' tiles arriving with the attention's own) or,
+  // when that is the longer list, over the blocks not listed (their tiles
+  // copied by the H waves themselves). Deciding needs the number of distinct
+  // listed blocks: a bitmap of the list, built before the first barrier.
+  const bool maybe_off = LIN && count > n_k - count && n_k <= kMaxLinKeyBlocks;
+  const int words = (n_k + 31) / 32;
+  if constexpr (LIN) {
+    if (maybe_off) {  // bits past n_k count as listed
+      for (int w = t; w < words; w += BQ * 4)
+        kbits[w] = 32 * w + 32 > n_k ? ~((1u << (n_k - 32 * w)) - 1u) : 0u;
+      __syncthreads();
+      for (int e = t; e < count; e += BQ * 4) {
+        const int j = min(max(ids[e], 0), n_k - 1);
+        atomicOr(&kbits[j >> 5], 1u << (j & 31));
+      }
+    }
+  }
 
   int koff[KSTEPS];
 #pragma unroll
@@ -233,10 +260,29 @@ __global__ __launch_bounds__(BQ * (LIN ? 4 : 2), (LIN || (D == 128 && BQ == 64))
       stageK(jcur, 0);
       stageV(jcur, 0);
       if (count > 1) stageK(jat(1), 1);
+    } else if (!maybe_off) {
+      stageP(jat(0), 0);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
     if (!hwave) qk(kbuf, sc, Zero{}, Full{}, [](int) {});
+  }
+  // hoff: the H waves take the n_off < count blocks not listed (every wave
+  // counts the bitmap's clear bits); otherwise the listed blocks, whose first
+  // phi(K)^T tile, when the route was open until now, they copy here (read
+  // after step 0's barrier)
+  int n_off = n_k;
+  bool hoff = false;
+  if constexpr (LIN) {
+    if (maybe_off) {
+      int c0 = 0;
+      for (int w = lane; w < words; w += 64) c0 += __popc(~kbits[w]);
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) c0 += __shfl_xor(c0, o);
+      n_off = __builtin_amdgcn_readfirstlane(c0);
+      hoff = n_off < count;
+    }
+    if (hwave && maybe_off && !hoff) stageP(jat(0), 0);
   }
 
   // one listed block: softmax and P V of block `it` (S^T in sc), and with
@@ -251,7 +297,6 @@ __global__ __launch_bounds__(BQ * (LIN ? 4 : 2), (LIN || (D == 128 && BQ == 64))
     // buffer is not read again) and V^T of block it+1
     const char* ksrc = nullptr;
     const char* vsrc = nullptr;
-    const char* psrc = nullptr;
     uint32_t ko[LOADS];
     if constexpr (NEXT) {
       if (it + 1 == w0 + 64) {  // slide the windows; the load lands with this step's copies
@@ -264,7 +309,6 @@ __global__ __launch_bounds__(BQ * (LIN ? 4 : 2), (LIN || (D == 128 && BQ == 64))
       const int key0 = jk * BK;
       ksrc = reinterpret_cast<const char*>(kh + (size_t)key0 * D);
       vsrc = reinterpret_cast<const char*>(vth + (size_t)jn * vtile);
-      if constexpr (LIN) psrc = reinterpret_cast<const char*>(pkh + (size_t)jn * vtile);
       if (key0 + BK <= N) {
 #pragma unroll
         for (int u = 0; u < LOADS; ++u) ko[u] = kofs(u);
@@ -278,7 +322,6 @@ __global__ __launch_bounds__(BQ * (LIN ? 4 : 2), (LIN || (D == 128 && BQ == 64))
     }
     unsigned char* kdst = kbuf + (it & 1) * T::BYTES;
     unsigned char* vdst = vbuf + ((it + 1) & 1) * T::BYTES;
-    unsigned char* pdst = pbuf + ((it + 1) & 1) * T::BYTES;
     constexpr int HALF = KSTEPS / 2;
     auto kdma = [&](int sl) {
 #pragma unroll
@@ -288,10 +331,7 @@ __global__ __launch_bounds__(BQ * (LIN ? 4 : 2), (LIN || (D == 128 && BQ == 64))
     auto vdma = [&](int sl) {
 #pragma unroll
       for (int u = 0; u < LOADS; ++u)
-        if (u * HALF / LOADS == sl) {
-          dma16(vsrc + vofs(u), vdst + 1024 * (u * NW + wave));
-          if constexpr (LIN) dma16(psrc + vofs(u), pdst + 1024 * (u * NW + wave));
-        }
+        if (u * HALF / LOADS == sl) dma16(vsrc + vofs(u), vdst + 1024 * (u * NW + wave));
     };
     const unsigned char* kn = kbuf + ((it + 1) & 1) * T::BYTES;
     const unsigned char* vb = vbuf + (it & 1) * T::BYTES;
@@ -362,13 +402,8 @@ __global__ __launch_bounds__(BQ * (LIN ? 4 : 2), (LIN || (D == 128 && BQ == 64))
   };
   if (hwave) {
     // H waves: one barrier per listed block, like the attention waves' steps;
-    // H_kept += phi(K_it)^T V_it and z_kept += sum phi(K_it) from the tiles
-    // of block it (V^T and phi(K)^T buffers it & 1)
-    for (int it = 0; it < count; ++it) {
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-      __syncthreads();
-      const unsigned char* vbh = vbuf + (it & 1) * T::BYTES;
-      const unsigned char* pbh = pbuf + (it & 1) * T::BYTES;
+    // H += phi(K_j)^T V_j and z += sum phi(K_j) from a (V^T, phi(K)^T) pair
+    auto h_block = [&](const unsigned char* vbh, const unsigned char* pbh) {
 #pragma unroll
       for (int G = 0; G < 4; ++G) {
         const bf16x8 pkf = lds_read16(pbh + wave * 32 * T::VROWB + voff[G]);
@@ -378,6 +413,52 @@ __global__ __launch_bounds__(BQ * (LIN ? 4 : 2), (LIN || (D == 128 && BQ == 64))
         for (int i = 0; i < DT; ++i)
           oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
               pkf, lds_read16(vbh + i * 32 * T::VROWB + voff[G]), oacc[i], 0, 0, 0);
+      }
+    };
+    if (hoff) {
+      // the blocks not listed, in increasing order: block e is copied (phi(K)^T
+      // to phi buffer e & 1, V^T to the H waves' V buffer e & 1) after barrier
+      // e and summed after barrier e + 1, so n_off < count barriers suffice
+      auto next_off = [&](int j) {  // the first block after j that is not listed
+        int w = (j + 1) >> 5;
+        uint32_t m = w < words ? ~kbits[w] & (~0u << ((j + 1) & 31)) : 0u;
+        while (m == 0u && ++w < words) m = ~kbits[w];
+        return m ? 32 * w + __builtin_ctz(m) : n_k;
+      };
+      int jo = next_off(-1);
+      for (int it = 0; it < count; ++it) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+        if (it < n_off) {
+          const char* ptt = reinterpret_cast<const char*>(pkh + (size_t)jo * vtile);
+          const char* vtt = reinterpret_cast<const char*>(vth + (size_t)jo * vtile);
+#pragma unroll
+          for (int u = 0; u < LOADS; ++u) {
+            dma16(ptt + vofs(u), pbuf + (it & 1) * T::BYTES + 1024 * (u * NW + wave));
+            dma16(vtt + vofs(u), hvbuf + (it & 1) * T::BYTES + 1024 * (u * NW + wave));
+          }
+          jo = next_off(jo);
+        }
+        if (it >= 1 && it - 1 < n_off)
+          h_block(hvbuf + ((it - 1) & 1) * T::BYTES, pbuf + ((it - 1) & 1) * T::BYTES);
+      }
+    } else {
+      // the listed blocks: V^T of block it from the attention waves' buffer
+      // it & 1, its phi(K)^T (copied by the H waves after the barrier before)
+      // from phi buffer it & 1; list entries come from the lane-held windows,
+      // slid like the attention waves' (no scalar loads next to LDS reads)
+      for (int it = 0; it < count; ++it) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+        if (it + 1 < count) {
+          if (it + 1 == w0 + 64) {
+            win0 = win1;
+            w0 += 64;
+            win1 = load_win(w0 + 64);
+          }
+          stageP(jat(it + 1), (it + 1) & 1);
+        }
+        h_block(vbuf + (it & 1) * T::BYTES, pbuf + (it & 1) * T::BYTES);
       }
     }
   } else {
@@ -404,7 +485,7 @@ __global__ __launch_bounds__(BQ * (LIN ? 4 : 2), (LIN || (D == 128 && BQ == 64))
   }
 
   // ---- epilogue: O = O^T / l, with the linear branch or alpha as above; bf16, rows < N only
-  const float ltot = pair_sum(lsum);  // (H waves: z_kept entry 32*wave + l32)
+  const float ltot = pair_sum(lsum);  // (H waves: their z entry 32*wave + l32)
   const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
   if constexpr (LSE) {  // sum_u exp(scale s_u) = 2^(m c) * ltot; -inf for an empty row
     if (!hwave && h2 == 0 && qrow < N)
@@ -429,21 +510,32 @@ __global__ __launch_bounds__(BQ * (LIN ? 4 : 2), (LIN || (D == 128 && BQ == 64))
     float* ysds = reinterpret_cast<float*>(ylds + NW * DT * 4 * 64);
     const bool dropped = count < n_k;  // D_i is empty when every block is kept
     __syncthreads();                   // every wave is done with the staging buffers
-    if (dropped && hwave) {
+    if (dropped && hwave) {  // H_D = H_tot - the listed sum, or the sum itself
       const float* Ht = lin_h + (size_t)bh * D * D;
+      if (hoff) {
 #pragma unroll
-      for (int i = 0; i < DT; ++i)
+        for (int i = 0; i < DT; ++i)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int a0 = 32 * wave + 8 * g + 4 * h2, b = 32 * i + l32;
-          float4 x;
-          x.x = Ht[(size_t)(a0 + 0) * D + b] - oacc[i][4 * g + 0];
-          x.y = Ht[(size_t)(a0 + 1) * D + b] - oacc[i][4 * g + 1];
-          x.z = Ht[(size_t)(a0 + 2) * D + b] - oacc[i][4 * g + 2];
-          x.w = Ht[(size_t)(a0 + 3) * D + b] - oacc[i][4 * g + 3];
-          *reinterpret_cast<float4*>(ht + b * HP + a0) = x;
-        }
-      if (h2 == 0) zd[32 * wave + l32] = lin_z[(size_t)bh * D + 32 * wave + l32] - ltot;
+          for (int g = 0; g < 4; ++g)
+            *reinterpret_cast<float4*>(ht + (32 * i + l32) * HP + 32 * wave + 8 * g + 4 * h2) =
+                make_float4(oacc[i][4 * g + 0], oacc[i][4 * g + 1], oacc[i][4 * g + 2],
+                            oacc[i][4 * g + 3]);
+        if (h2 == 0) zd[32 * wave + l32] = ltot;
+      } else {
+#pragma unroll
+        for (int i = 0; i < DT; ++i)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int a0 = 32 * wave + 8 * g + 4 * h2, b = 32 * i + l32;
+            float4 x;
+            x.x = Ht[(size_t)(a0 + 0) * D + b] - oacc[i][4 * g + 0];
+            x.y = Ht[(size_t)(a0 + 1) * D + b] - oacc[i][4 * g + 1];
+            x.z = Ht[(size_t)(a0 + 2) * D + b] - oacc[i][4 * g + 2];
+            x.w = Ht[(size_t)(a0 + 3) * D + b] - oacc[i][4 * g + 3];
+            *reinterpret_cast<float4*>(ht + b * HP + a0) = x;
+          }
+        if (h2 == 0) zd[32 * wave + l32] = lin_z[(size_t)bh * D + 32 * wave + l32] - ltot;
+      }
     }
     __syncthreads();
     float lin_scale = 0.0f;  // alpha[h] / (phi(Q_t) . z_D)

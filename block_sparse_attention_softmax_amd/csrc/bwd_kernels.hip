@@ -356,14 +356,14 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void sparse_attn_bwd_dkdv_ke
     if (e + 1 < end) issue(nxt * BQ, smem + ((e - beg + 1) & 1) * ST::BYTES);
     const uint32_t bufa = lds_addr(buf) + tr_row;
 
+    // S = Q K^T and dP = dO V^T for every sub-tile's 32 queries x the wave's
+    // 32 keys first: 2 NS independent accumulator chains
+    floatx16 Sa[NS], dPa[NS];
 #pragma unroll
     for (int n = 0; n < NS; ++n) {
-      const int qb = qh * (BQ / 2) + 32 * n;  // the sub-tile's first row in the block
-      // S = Q K^T and dP = dO V^T for the sub-tile's 32 queries x the wave's 32 keys
-      floatx16 S, dP;
+      const int qr = qh * (BQ / 2) + 32 * n + l32;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) S[r] = dP[r] = 0.0f;
-      const int qr = qb + l32;
+      for (int r = 0; r < 16; ++r) Sa[n][r] = dPa[n][r] = 0.0f;
       bf16x8 fa[KSTEPS], fb[KSTEPS];  // every fragment first: one wait, not one per k-step
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) {
@@ -373,9 +373,15 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void sparse_attn_bwd_dkdv_ke
       }
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) {
-        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s], kf[s], S, 0, 0, 0);
-        dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[s], vf[s], dP, 0, 0, 0);
+        Sa[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s], kf[s], Sa[n], 0, 0, 0);
+        dPa[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[s], vf[s], dPa[n], 0, 0, 0);
       }
+    }
+#pragma unroll
+    for (int n = 0; n < NS; ++n) {
+      const int qb = qh * (BQ / 2) + 32 * n;  // the sub-tile's first row in the block
+      floatx16& S = Sa[n];
+      floatx16& dP = dPa[n];
       // P = 2^(S c - lse2), dS = P (dP - D); register r holds row
       // qb + 8*(r/4) + 4*h2 + r%4 (the row terms are read as 16-byte
       // fragments: as float4 the compiler waits here for the next stage's

@@ -323,6 +323,36 @@ def test_sparse_linear_small_shapes_in_full(B, H, N, d, bq):
             print(f"[linear] b={b} h={h}: max {mx:.2e} mean {mean:.2e}", flush=True)
 
 
+@pytest.mark.parametrize("B,H,N,d", [(1, 2, 1000, 128), (2, 1, 1500, 64)])
+def test_sparse_linear_dense_lists_sum_the_dropped_blocks(B, H, N, d):
+    """Rows listing more than half of the key blocks take the branch's other
+    route (the dropped blocks summed directly); every row here does, except a
+    full one (no linear part) and an empty one."""
+    rng = np.random.default_rng(11 * N + d)
+    from block_sparse_attention_softmax_amd.workloads import f64_to_bf16_bits
+    Q, K, V = (f64_to_bf16_bits(rng.standard_normal((B, H, N, d))) for _ in range(3))
+    n_q, n_k = -(-N // d), -(-N // 64)
+    kept = rng.random((B, H, n_q, n_k)) < 0.8
+    flat = kept.reshape(-1, n_k)
+    flat[0] = True
+    flat[1] = False
+    idx, cnt = O.kept_to_index_list(kept)
+    alpha = rng.uniform(0.05, 0.8, size=H).astype(np.float32)
+    o = S.sparse_linear_attn_fwd(to_gpu(Q), to_gpu(K), to_gpu(V), torch.from_numpy(idx).cuda(),
+                                 torch.from_numpy(cnt).cuda(), torch.from_numpy(alpha).cuda(),
+                                 d, 64)
+    torch.cuda.synchronize()
+    got = O.bf16_to_f64(o.cpu().view(torch.uint16).numpy())
+    scale = S.default_scale(d)
+    for b in range(B):
+        for h in range(H):
+            ref = O.sparse_linear_attention_head(O.bf16_to_f64(Q[b, h]), O.bf16_to_f64(K[b, h]),
+                                                 O.bf16_to_f64(V[b, h]), kept[b, h], d, 64,
+                                                 scale, float(alpha[h]))
+            mx, mean = compare_outputs(got[b, h], ref)
+            print(f"[linear dense lists] b={b} h={h}: max {mx:.2e} mean {mean:.2e}", flush=True)
+
+
 def test_sparse_linear_matches_oracle_on_workload():
     """The sparse-linear workload: wan1.3b inputs and mask, alpha = 0.1 per head."""
     wl, Q, K, V, q, k, v = workload_tensors("wan1.3b_linear")
