@@ -11,8 +11,11 @@ Default workload: the Wan2.1-1.3B-shaped grid (B=1, H=12, N=32760 =
 throughput: 4*B*H*N^2*d floating-point operations per step divided by the
 step time (TFLOP/s). Next to it the line reports the attention kernel against
 the bf16 MFMA roofline at the kept-block count, the same path at the Top-k
-operating points of 90% and 95% block sparsity (p = 0, k = 10% / 5%), and the
-CPU oracle timed on a bounded sample of the same workload.
+operating points of 90% and 95% block sparsity (p = 0, k = 10% / 5%), the
+backward, low-bit, sparse-linear, SLA2/SALAD and SVG2 variants on the same
+inputs, the forward at two more configurations (95% sparsity on mixed-range
+heads, and a Wan2.1-14B 720p grid: H=40, N=75600), and the CPU oracle timed on
+a bounded sample of the default workload.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -116,6 +119,8 @@ def main():
     ap.add_argument("--cpu-blocks", type=int, default=768,
                     help="query blocks of the oracle's CPU sample (heads 0, 1, ... in order)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the forward at the 95%% and Wan 14B 720p configurations")
     ap.add_argument("--no-overlap", action="store_true",
                     help="pack V on the main stream after the mask instead of beside it")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -386,6 +391,63 @@ def main():
                  "call_ms": round(e0.elapsed_time(e1) / 3, 3)}
     del sws
 
+    # the forward at the two other configurations: 95% sparsity on mixed-range heads
+    # (k = 3%, p = 0.8) and Wan 14B at 720p (H = 40, N = 75600); mask, V pack and the
+    # attention kernel, each timed on its own over the same launches
+    other = {}
+    if not args.no_other_configs:
+        for name in ("wan1.3b_s95", "wan14b_720p"):
+            w2 = WORKLOADS[name]
+            q2, k2, v2 = (g(a) for a in generate(w2))
+            B2, H2, N2, d2 = q2.shape
+            bits2 = torch.empty((B2, H2, w2.n_q, -(-w2.n_k // 32)), dtype=torch.int32,
+                                device=dev)
+            idx2 = torch.empty((B2, H2, w2.n_q, w2.n_k), dtype=torch.int32, device=dev)
+            cnt2 = torch.empty((B2, H2, w2.n_q), dtype=torch.int32, device=dev)
+            ws2 = torch.empty(S.mask_workspace_bytes(B2, H2, N2, d2, w2.block_q, w2.block_k),
+                              dtype=torch.uint8, device=dev)
+            aws2 = torch.empty(S.attn_workspace_bytes(B2, H2, N2, d2), dtype=torch.uint8,
+                               device=dev)
+            o2 = torch.empty_like(q2)
+
+            def fwd2(ev=None):
+                if ev is not None:
+                    ev[0].record()
+                S.sparge_mask_predict(q2, k2, w2.block_q, w2.block_k, w2.k_frac, w2.p_mass,
+                                      w2.scale, workspace=ws2, out=(bits2, idx2, cnt2))
+                if ev is not None:
+                    ev[1].record()
+                S.sparge_attn_pack(v2, workspace=aws2)
+                if ev is not None:
+                    ev[2].record()
+                S.sparge_attn_fwd_packed(q2, k2, idx2, cnt2, aws2, w2.block_q, w2.block_k,
+                                         w2.scale, out=o2)
+                if ev is not None:
+                    ev[3].record()
+            fwd2()
+            torch.cuda.synchronize()
+            n_o = max(3, args.steps // 4)
+            evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_o)]
+            for i in range(n_o):
+                fwd2(evs[i])
+            torch.cuda.synchronize()
+            ms = [float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j in range(3)]
+            c_np, i_np = cnt2.cpu().numpy(), idx2.cpu().numpy()
+            kf2 = kept_flops(c_np, i_np, N2, d2, w2.block_q, w2.block_k)
+            dense2 = 4.0 * B2 * H2 * float(N2) * N2 * d2
+            total = sum(ms)
+            other[name] = {
+                "shape": f"B={B2} H={H2} N={N2} d={d2} blocks {w2.block_q}x{w2.block_k}",
+                "k": w2.k_frac, "p": w2.p_mass,
+                "block_sparsity": round(1 - float(c_np.sum()) / c_np.size / w2.n_k, 4),
+                "mask_ms": round(ms[0], 4), "pack_ms": round(ms[1], 4),
+                "attn_kernel_ms": round(ms[2], 4), "sequential_ms": round(total, 4),
+                "dense_equiv_tflops": round(dense2 / total / 1e9, 2),
+                "attn_kept_tflops": round(kf2 / ms[2] / 1e9, 2),
+                "attn_frac_bf16_peak": round(kf2 / ms[2] / 1e9 / PEAK_BF16_TFLOPS, 4)}
+            del q2, k2, v2, bits2, idx2, cnt2, ws2, aws2, o2
+            torch.cuda.empty_cache()
+
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl, Q, K, V, args.cpu_blocks)
 
     line = {
@@ -414,6 +476,7 @@ def main():
         "backward": backward,
         "lowbit": lowbit,
         "svg2": svg2_line,
+        "other_configs": other,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
