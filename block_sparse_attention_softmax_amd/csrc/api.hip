@@ -31,6 +31,8 @@ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 // Shape checks common to every entry point. Returns SPARGE_OK or an error.
 int check_shape(int B, int H, int N, int d, int block_q, int block_k) {
   if (B < 1 || H < 1 || N < 1) return fail(SPARGE_ERR_INVALID_ARG, "B, H and N must be >= 1");
+  // block counts are formed as (N + size - 1) / size in 32-bit arithmetic
+  if (N > 0x7FFFFFFF - 1024) return fail(SPARGE_ERR_INVALID_ARG, "N too large");
   if (d != 64 && d != 128) return fail(SPARGE_ERR_UNSUPPORTED, "d must be 64 or 128");
   if (block_q != 64 && block_q != 128)
     return fail(SPARGE_ERR_UNSUPPORTED, "block_q must be 64 or 128");

@@ -120,6 +120,7 @@ def test_mask_rejects_bad_arguments(kw, code):
     (dict(d=80), -2), (dict(bq=256), -2), (dict(bk=32), -2), (dict(N=0), -1),
     (dict(sc=-1.0), -1), (dict(sc=float("inf")), -1),
     (dict(ws=None), -1), (dict(ws=MIS), -1), (dict(wsb=1024 * 64 * 2 * 2 - 1), -1),
+    (dict(N=2**31 - 1, B=1, H=1), -1),  # block counts would overflow 32-bit arithmetic
 ])
 def test_attn_rejects_bad_arguments(kw, code):
     assert _attn(**kw) == code
