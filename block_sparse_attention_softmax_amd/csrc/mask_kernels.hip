@@ -11,10 +11,12 @@
 //                       desc, index asc), float64 prefix sum for Top-p, union
 //                       with Top-k (SpargeAttention2 page, sections 1 and 2A),
 //                       then the bitmask and the ascending index list.
-//                       hybrid_select_reg_kernel: rows of up to 512 blocks, one
-//                       wave per row, the sort in registers and lane shuffles;
-//                       hybrid_select_kernel: wider rows, one workgroup per row,
-//                       the sort in LDS.
+//                       hybrid_select_reg_kernel: rows of up to 2048 blocks,
+//                       one wave per row, the sort in registers and lane
+//                       shuffles; hybrid_select_kernel: one workgroup per row,
+//                       the sort in LDS, for wider rows and for rows of more
+//                       than 512 blocks when there are too few of them to
+//                       fill the chip one wave each.
 //
 // Everything that decides the mask is float64, so the selection is the one a
 // float64 evaluation of the definition gives, up to summation order.
@@ -332,19 +334,22 @@ __global__ __launch_bounds__(256) void hybrid_select_kernel(
   if (lane == 0) cnt_out[row] = count;
 }
 
-// Rows of up to 512 padded entries: one wave per row, entries in registers.
+// Rows of up to 2048 padded entries: one wave per row, entries in registers.
 // Lane L holds sorted positions L*E .. L*E+E-1 (E = NPAD/64) once the bitonic
 // network has run; a compare distance below E pairs two registers of one
 // lane, a larger one pairs the same register of lanes L and L ^ (jj/E),
-// exchanged with shuffles. The softmax total, the probabilities and the
-// Top-p prefix sums are formed exactly as by the LDS variant above.
+// exchanged with shuffles. Up to 512 entries the whole network is unrolled;
+// wider rows loop over the stages, with the in-lane distances (compile-time
+// register pairs) unrolled per distance. The softmax total, the
+// probabilities and the Top-p prefix sums are formed exactly as by the LDS
+// variant above.
 template <int NPAD>
 __global__ __launch_bounds__(256) void hybrid_select_reg_kernel(
     const double* __restrict__ s, int rows, int n_k, int words, int K_k,
     int keep_all, double p, uint32_t* __restrict__ bits_out,
     int32_t* __restrict__ idx_out, int32_t* __restrict__ cnt_out) {
   constexpr int E = NPAD / 64;
-  static_assert(E >= 1 && E <= 8, "register rows hold 64 .. 512 entries");
+  static_assert(E >= 1 && E <= 32, "register rows hold 64 .. 2048 entries");
   __shared__ uint32_t wbs[4][NPAD / 32 > 0 ? NPAD / 32 : 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const size_t row = (size_t)blockIdx.x * 4 + wave;
@@ -374,36 +379,54 @@ __global__ __launch_bounds__(256) void hybrid_select_reg_kernel(
   tot = wave_sum(tot);
 
   // 2. bitonic sort: position 0 = highest score, equal scores lower index first
+  auto in_lane = [&](int jj, int kk) {  // jj < E: register pairs (e, e ^ jj)
 #pragma unroll
-  for (int kk = 2; kk <= NPAD; kk <<= 1) {
-#pragma unroll
-    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
-      if (jj < E) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          if (e & jj) continue;
-          const int f = e ^ jj;
-          const bool desc = ((lane * E + e) & kk) == 0;
-          const bool b_first = (sc[f] > sc[e]) || (sc[f] == sc[e] && ix[f] < ix[e]);
-          if (b_first == desc) {
-            const double ts = sc[e]; sc[e] = sc[f]; sc[f] = ts;
-            const int ti = ix[e]; ix[e] = ix[f]; ix[f] = ti;
-          }
-        }
-      } else {
-        const int m = jj / E;
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const double os = __shfl_xor(sc[e], m);
-          const int oi = __shfl_xor(ix[e], m);
-          const int pos = lane * E + e;
-          const bool lower = (pos & jj) == 0, desc = (pos & kk) == 0;
-          const double as = lower ? sc[e] : os, bs = lower ? os : sc[e];
-          const int ai = lower ? ix[e] : oi, bi = lower ? oi : ix[e];
-          const bool b_first = (bs > as) || (bs == as && bi < ai);
-          if (b_first == desc) { sc[e] = os; ix[e] = oi; }
-        }
+    for (int e = 0; e < E; ++e) {
+      if (e & jj) continue;
+      const int f = e ^ jj;
+      const bool desc = ((lane * E + e) & kk) == 0;
+      const bool b_first = (sc[f] > sc[e]) || (sc[f] == sc[e] && ix[f] < ix[e]);
+      if (b_first == desc) {
+        const double ts = sc[e]; sc[e] = sc[f]; sc[f] = ts;
+        const int ti = ix[e]; ix[e] = ix[f]; ix[f] = ti;
       }
+    }
+  };
+  auto cross_lane = [&](int jj, int kk) {  // jj >= E: lanes L and L ^ (jj / E)
+    const int m = jj / E;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const double os = __shfl_xor(sc[e], m);
+      const int oi = __shfl_xor(ix[e], m);
+      const int pos = lane * E + e;
+      const bool lower = (pos & jj) == 0, desc = (pos & kk) == 0;
+      const double as = lower ? sc[e] : os, bs = lower ? os : sc[e];
+      const int ai = lower ? ix[e] : oi, bi = lower ? oi : ix[e];
+      const bool b_first = (bs > as) || (bs == as && bi < ai);
+      if (b_first == desc) { sc[e] = os; ix[e] = oi; }
+    }
+  };
+  if constexpr (E <= 8) {
+#pragma unroll
+    for (int kk = 2; kk <= NPAD; kk <<= 1) {
+#pragma unroll
+      for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+        if (jj < E) in_lane(jj, kk);
+        else cross_lane(jj, kk);
+      }
+    }
+  } else {
+#pragma unroll 1
+    for (int kk = 2; kk <= NPAD; kk <<= 1) {
+#pragma unroll 1
+      for (int jj = kk >> 1; jj >= E; jj >>= 1) cross_lane(jj, kk);
+      // then the in-lane distances min(kk, E) / 2 .. 1, each unrolled
+      const int jmax = min(kk, E) >> 1;
+      if constexpr (E >= 32) if (jmax >= 16) in_lane(16, kk);
+      if (jmax >= 8) in_lane(8, kk);
+      if (jmax >= 4) in_lane(4, kk);
+      if (jmax >= 2) in_lane(2, kk);
+      in_lane(1, kk);
     }
   }
 
@@ -499,14 +522,22 @@ hipError_t launch_scores_f64(const double* x, const double* y, double* out, int 
   return hipGetLastError();
 }
 
+constexpr int kRegSelectMinRows = 1024;
+
 hipError_t launch_select_rows(const MaskLaunch& a, hipStream_t st) {
   switch (a.npad) {
     case 64: return launch_select_reg<64>(a, st);
     case 128: return launch_select_reg<128>(a, st);
     case 256: return launch_select_reg<256>(a, st);
     case 512: return launch_select_reg<512>(a, st);
-    case 1024: return launch_select<1024>(a, st);
-    case 2048: return launch_select<2048>(a, st);
+    // 1024 / 2048 entries: one wave per row needs about a thousand rows to
+    // fill the chip; with fewer, a workgroup per row (the LDS sort) is faster
+    case 1024:
+      return a.B * a.H * a.n_q >= kRegSelectMinRows ? launch_select_reg<1024>(a, st)
+                                                      : launch_select<1024>(a, st);
+    case 2048:
+      return a.B * a.H * a.n_q >= kRegSelectMinRows ? launch_select_reg<2048>(a, st)
+                                                      : launch_select<2048>(a, st);
     default: return launch_select<4096>(a, st);
   }
 }
@@ -545,8 +576,14 @@ hipError_t launch_mask(const MaskLaunch& a, hipStream_t st) {
     case 128: return launch_select_reg<128>(a, st);
     case 256: return launch_select_reg<256>(a, st);
     case 512: return launch_select_reg<512>(a, st);
-    case 1024: return launch_select<1024>(a, st);
-    case 2048: return launch_select<2048>(a, st);
+    // 1024 / 2048 entries: one wave per row needs about a thousand rows to
+    // fill the chip; with fewer, a workgroup per row (the LDS sort) is faster
+    case 1024:
+      return a.B * a.H * a.n_q >= kRegSelectMinRows ? launch_select_reg<1024>(a, st)
+                                                      : launch_select<1024>(a, st);
+    case 2048:
+      return a.B * a.H * a.n_q >= kRegSelectMinRows ? launch_select_reg<2048>(a, st)
+                                                      : launch_select<2048>(a, st);
     default: return launch_select<4096>(a, st);
   }
   return hipGetLastError();

@@ -60,7 +60,10 @@ def test_mask_matches_oracle(name):
 @pytest.mark.parametrize("B,H,N,d,bq,k_frac,p_mass", [
     (1, 2, 5000, 128, 128, 0.1, 0.5),      # n_k 79   -> sort width 128
     (2, 1, 12345, 64, 64, 0.02, 0.95),     # n_k 193  -> 256
-    (1, 1, 60000, 64, 128, 0.05, 0.0),     # n_k 938  -> 1024, Top-k alone
+    (1, 1, 60000, 64, 128, 0.05, 0.0),     # n_k 938  -> 1024, Top-k alone (469 rows: LDS sort)
+    (1, 2, 40000, 64, 64, 0.05, 0.9),      # n_k 625  -> 1024, 1250 rows: register sort
+    (2, 1, 70000, 64, 128, 0.03, 0.8),     # n_k 1094 -> 2048, 1094 rows: register sort
+    (1, 1, 100000, 64, 128, 0.02, 0.9),    # n_k 1563 -> 2048, 782 rows: LDS sort
     (1, 1, 200000, 64, 128, 0.01, 0.7),    # n_k 3125 -> 4096 (the largest supported width)
     (1, 3, 777, 128, 64, 1.0, 0.9),        # k = 100% keeps everything
     (1, 2, 3000, 64, 64, 0.2, 1.0)])       # p >= 1 keeps everything
