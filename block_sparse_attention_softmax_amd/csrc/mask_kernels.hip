@@ -342,7 +342,8 @@ __global__ __launch_bounds__(256) void hybrid_select_kernel(
 // wider rows loop over the stages, with the in-lane distances (compile-time
 // register pairs) unrolled per distance. The softmax total, the
 // probabilities and the Top-p prefix sums are formed exactly as by the LDS
-// variant above.
+// variant above. With Top-k alone (p = 0) or p >= 1 the kept count is known
+// before any ordering, so the kernel selects instead of sorting.
 template <int NPAD>
 __global__ __launch_bounds__(256) void hybrid_select_reg_kernel(
     const double* __restrict__ s, int rows, int n_k, int words, int K_k,
@@ -367,6 +368,55 @@ __global__ __launch_bounds__(256) void hybrid_select_reg_kernel(
     sc[e] = j < n_k ? srow[j] : -INFINITY;
     ix[e] = j;
   }
+
+  if (keep_all || !(p > 0.0)) {
+    // Top-k alone (or every block): the count is known, and the kept set is
+    // the `count` largest (score, index) pairs in the order above. No sort:
+    // a bitwise search finds the count-th largest score key T, then the
+    // entries scoring exactly T are taken in increasing index order.
+    const int count = keep_all ? n_k : K_k;
+    // order-preserving integer keys of the scores (-0 folded into +0 so
+    // that equal scores get equal keys); entries past n_k get key 0, below
+    // every score
+    uint64_t key[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const uint64_t b = (uint64_t)__double_as_longlong(sc[e] + 0.0);
+      key[e] = lane + 64 * e < n_k ? (b >> 63 ? ~b : b | (1ull << 63)) : 0ull;
+    }
+    uint64_t T = 0;
+    for (int bit = 63; bit >= 0; --bit) {
+      const uint64_t cand = T | (1ull << bit);
+      int c = 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) c += __popcll(__ballot(key[e] >= cand));
+      if (c >= count) T = cand;
+    }
+    int ties = count;  // entries scoring T still to take
+#pragma unroll
+    for (int e = 0; e < E; ++e) ties -= __popcll(__ballot(key[e] > T));
+    // emit in index order j = lane + 64 e: register by register, lanes in order
+    const uint64_t below = (1ull << lane) - 1ull;
+    int before = 0, pos = 0;
+    uint32_t myword = 0u;
+    int32_t* irow = idx_out + row * (size_t)n_k;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const bool eq = key[e] == T && key[e] != 0ull;
+      const uint64_t meq = __ballot(eq);
+      const bool kept = key[e] > T || (eq && before + __popcll(meq & below) < ties);
+      before += __popcll(meq);
+      const uint64_t mk = __ballot(kept);
+      if (lane == 2 * e) myword = (uint32_t)mk;
+      if (lane == 2 * e + 1) myword = (uint32_t)(mk >> 32);
+      if (kept) irow[pos + __popcll(mk & below)] = lane + 64 * e;
+      pos += __popcll(mk);
+    }
+    if (lane < words) bits_out[row * words + lane] = myword;
+    if (lane == 0) cnt_out[row] = count;
+    return;
+  }
+
   for (int w = lane; w < words; w += 64) wb[w] = 0u;
   double mx = -INFINITY;
 #pragma unroll
