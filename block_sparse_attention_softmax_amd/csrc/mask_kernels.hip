@@ -540,17 +540,23 @@ hipError_t launch_select_reg(const MaskLaunch& a, hipStream_t st) {
 }
 
 // one row per workgroup; the kernel's dynamic-LDS limit is raised once per
-// instantiation (the 4096-entry rows need 73 KiB)
+// instantiation and device (the 4096-entry rows need 73 KiB)
+constexpr int kMaxDevices = 64;
+
 template <int NPAD>
 hipError_t launch_select(const MaskLaunch& a, hipStream_t st) {
-  static std::once_flag lds_once;
-  static hipError_t lds_err = hipSuccess;
-  std::call_once(lds_once, [] {
-    lds_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&hybrid_select_kernel<NPAD>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  (int)select_lds_bytes(NPAD));
+  static std::once_flag lds_once[kMaxDevices];
+  static hipError_t lds_err[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(lds_once[dev], [dev] {
+    lds_err[dev] = hipFuncSetAttribute(reinterpret_cast<const void*>(&hybrid_select_kernel<NPAD>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)select_lds_bytes(NPAD));
   });
-  if (lds_err != hipSuccess) return lds_err;
+  if (lds_err[dev] != hipSuccess) return lds_err[dev];
   const int rows = a.B * a.H * a.n_q;
   hipLaunchKernelGGL(hybrid_select_kernel<NPAD>, dim3(rows), dim3(select_threads(NPAD)),
                      select_lds_bytes(NPAD), st, a.logits, rows, a.n_k, a.words, a.K_k,

@@ -33,7 +33,8 @@
  *    nothing is launched and sparge_last_error() says why. A failed launch
  *    returns SPARGE_ERR_HIP. No call throws.
  *  - Calls are thread-safe; the library keeps no state besides the
- *    per-thread error message.
+ *    per-thread error message and, per device, whether the LDS limit of the
+ *    widest mask-selection kernel has been raised (done once, on first use).
  */
 #ifndef SPARGE_H
 #define SPARGE_H
