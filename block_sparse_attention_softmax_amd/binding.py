@@ -114,6 +114,36 @@ def _qkv(*ts):
     return shape
 
 
+def _buf(t, name, dtype, shape, device):
+    """A caller-supplied tensor the library reads or writes through a raw pointer."""
+    if (not isinstance(t, torch.Tensor) or t.dtype != dtype or t.device != device
+            or not t.is_contiguous() or tuple(t.shape) != tuple(shape)):
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {list(shape)} "
+                         f"on {device}")
+    return t
+
+
+def _blocks(N, block_q, block_k):
+    # invalid block sizes are left to the library, which rejects them
+    return (-(-N // block_q) if block_q > 0 else 0), (-(-N // block_k) if block_k > 0 else 0)
+
+
+def _lists(kv_idx, kv_cnt, q, block_q, block_k):
+    B, H, N, _ = q.shape
+    n_q, n_k = _blocks(N, block_q, block_k)
+    _buf(kv_idx, "kv_idx", torch.int32, (B, H, n_q, n_k), q.device)
+    _buf(kv_cnt, "kv_cnt", torch.int32, (B, H, n_q), q.device)
+
+
+def _workspace(ws, need, device):
+    """(workspace tensor, its size in bytes): a new one of `need` bytes, or the caller's."""
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    elif (not isinstance(ws, torch.Tensor) or ws.device != device or not ws.is_contiguous()):
+        raise ValueError(f"workspace must be a contiguous tensor on {device}")
+    return ws, ws.numel() * ws.element_size()
+
+
 def default_scale(d: int) -> float:
     return float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
 
@@ -126,6 +156,20 @@ def mask_workspace_bytes(B, H, N, d, block_q, block_k) -> int:
     return lib().sparge_mask_workspace_bytes(B, H, N, d, block_q, block_k)
 
 
+def _mask_outputs(q, block_q, block_k, out, return_logits):
+    B, H, N, _ = q.shape
+    n_q, n_k = _blocks(N, block_q, block_k)
+    shapes = ((B, H, n_q, -(-n_k // 32)), (B, H, n_q, n_k), (B, H, n_q))
+    if out is None:
+        bits, idx, cnt = (torch.empty(sh, dtype=torch.int32, device=q.device) for sh in shapes)
+    else:
+        bits, idx, cnt = (_buf(t, name, torch.int32, sh, q.device)
+                          for t, name, sh in zip(out, ("mask_bits", "kv_idx", "kv_cnt"), shapes))
+    logits = (torch.empty((B, H, n_q, n_k), dtype=torch.float64, device=q.device)
+              if return_logits else None)
+    return bits, idx, cnt, logits
+
+
 def sparge_mask_predict(q, k, block_q=128, block_k=64, k_frac=0.05, p_mass=0.9, scale=None,
                         return_logits=False, workspace=None, out=None):
     """Hybrid Top-k + Top-p block mask.
@@ -134,25 +178,14 @@ def sparge_mask_predict(q, k, block_q=128, block_k=64, k_frac=0.05, p_mass=0.9, 
     [B,H,n_q,n_k], kv_cnt int32 [B,H,n_q][, logits float64 [B,H,n_q,n_k]]).
     """
     B, H, N, d = _qkv(q, k)
-    n_q, n_k = -(-N // block_q), -(-N // block_k)
-    dev = q.device
-    if out is None:
-        bits = torch.empty((B, H, n_q, -(-n_k // 32)), dtype=torch.int32, device=dev)
-        idx = torch.empty((B, H, n_q, n_k), dtype=torch.int32, device=dev)
-        cnt = torch.empty((B, H, n_q), dtype=torch.int32, device=dev)
-    else:
-        bits, idx, cnt = out
-    logits = (torch.empty((B, H, n_q, n_k), dtype=torch.float64, device=dev)
-              if return_logits else None)
-    ws_bytes = mask_workspace_bytes(B, H, N, d, block_q, block_k)
-    if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    bits, idx, cnt, logits = _mask_outputs(q, block_q, block_k, out, return_logits)
+    workspace, ws_bytes = _workspace(workspace, mask_workspace_bytes(B, H, N, d, block_q, block_k),
+                                     q.device)
     if scale is None:
         scale = default_scale(d)
     _check(lib().sparge_mask_predict(
         _ptr(q), _ptr(k), B, H, N, d, block_q, block_k, k_frac, p_mass, scale,
-        _ptr(bits), _ptr(idx), _ptr(cnt), _ptr(logits), _ptr(workspace),
-        workspace.numel(), _stream(q)))
+        _ptr(bits), _ptr(idx), _ptr(cnt), _ptr(logits), _ptr(workspace), ws_bytes, _stream(q)))
     return (bits, idx, cnt, logits) if return_logits else (bits, idx, cnt)
 
 
@@ -167,28 +200,18 @@ def sparge_mask_predict_routed(q, k, w_q, w_k, block_q=128, block_k=64, k_frac=0
     tensors [H, d, d]); outputs as sparge_mask_predict."""
     B, H, N, d = _qkv(q, k)
     for w in (w_q, w_k):
-        if w.dtype != torch.float32 or not w.is_cuda or tuple(w.shape) != (H, d, d):
+        if w.dtype != torch.float32 or w.device != q.device or tuple(w.shape) != (H, d, d):
             raise ValueError("w_q, w_k must be float32 GPU tensors [H, d, d]")
     w_q, w_k = w_q.contiguous(), w_k.contiguous()
-    n_q, n_k = -(-N // block_q), -(-N // block_k)
-    dev = q.device
-    if out is None:
-        bits = torch.empty((B, H, n_q, -(-n_k // 32)), dtype=torch.int32, device=dev)
-        idx = torch.empty((B, H, n_q, n_k), dtype=torch.int32, device=dev)
-        cnt = torch.empty((B, H, n_q), dtype=torch.int32, device=dev)
-    else:
-        bits, idx, cnt = out
-    logits = (torch.empty((B, H, n_q, n_k), dtype=torch.float64, device=dev)
-              if return_logits else None)
-    if workspace is None:
-        workspace = torch.empty(max(mask_routed_workspace_bytes(B, H, N, d, block_q, block_k),
-                                    16), dtype=torch.uint8, device=dev)
+    bits, idx, cnt, logits = _mask_outputs(q, block_q, block_k, out, return_logits)
+    workspace, ws_bytes = _workspace(
+        workspace, mask_routed_workspace_bytes(B, H, N, d, block_q, block_k), q.device)
     if scale is None:
         scale = default_scale(d)
     _check(lib().sparge_mask_predict_routed(
         _ptr(q), _ptr(k), _ptr(w_q), _ptr(w_k), B, H, N, d, block_q, block_k, k_frac, p_mass,
-        scale, _ptr(bits), _ptr(idx), _ptr(cnt), _ptr(logits), _ptr(workspace),
-        workspace.numel(), _stream(q)))
+        scale, _ptr(bits), _ptr(idx), _ptr(cnt), _ptr(logits), _ptr(workspace), ws_bytes,
+        _stream(q)))
     return (bits, idx, cnt, logits) if return_logits else (bits, idx, cnt)
 
 
@@ -200,15 +223,14 @@ def sparge_attn_fwd(q, k, v, kv_idx, kv_cnt, block_q=128, block_k=64, scale=None
                     workspace=None):
     """Block-sparse attention over the key blocks listed in kv_idx/kv_cnt."""
     B, H, N, d = _qkv(q, k, v)
-    o = torch.empty_like(q) if out is None else out
+    _lists(kv_idx, kv_cnt, q, block_q, block_k)
+    o = torch.empty_like(q) if out is None else _buf(out, "out", torch.bfloat16, q.shape, q.device)
     if scale is None:
         scale = default_scale(d)
-    if workspace is None:
-        workspace = torch.empty(max(attn_workspace_bytes(B, H, N, d), 16), dtype=torch.uint8,
-                                device=q.device)
+    workspace, ws_bytes = _workspace(workspace, attn_workspace_bytes(B, H, N, d), q.device)
     _check(lib().sparge_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_idx), _ptr(kv_cnt), B, H,
                                  N, d, block_q, block_k, scale, _ptr(o), _ptr(workspace),
-                                 workspace.numel(), _stream(q)))
+                                 ws_bytes, _stream(q)))
     return o
 
 
@@ -216,17 +238,27 @@ def sparge_attn_fwd_lse(q, k, v, kv_idx, kv_cnt, block_q=128, block_k=64, scale=
                         out=None, workspace=None):
     """sparge_attn_fwd plus each row's log-sum-exp (float32 [B, H, N]); returns (o, lse)."""
     B, H, N, d = _qkv(q, k, v)
-    o, lse = (torch.empty_like(q), torch.empty((B, H, N), dtype=torch.float32,
-                                               device=q.device)) if out is None else out
+    _lists(kv_idx, kv_cnt, q, block_q, block_k)
+    if out is None:
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    else:
+        o = _buf(out[0], "out[0]", torch.bfloat16, q.shape, q.device)
+        lse = _buf(out[1], "out[1] (lse)", torch.float32, (B, H, N), q.device)
     if scale is None:
         scale = default_scale(d)
-    if workspace is None:
-        workspace = torch.empty(max(attn_workspace_bytes(B, H, N, d), 16), dtype=torch.uint8,
-                                device=q.device)
+    workspace, ws_bytes = _workspace(workspace, attn_workspace_bytes(B, H, N, d), q.device)
     _check(lib().sparge_attn_fwd_lse(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_idx), _ptr(kv_cnt), B,
                                      H, N, d, block_q, block_k, scale, _ptr(o), _ptr(lse),
-                                     _ptr(workspace), workspace.numel(), _stream(q)))
+                                     _ptr(workspace), ws_bytes, _stream(q)))
     return o, lse
+
+
+def _grads(q, out):
+    if out is None:
+        return tuple(torch.empty_like(q) for _ in range(3))
+    return tuple(_buf(t, name, torch.bfloat16, q.shape, q.device)
+                 for t, name in zip(out, ("dq", "dk", "dv")))
 
 
 def attn_bwd_workspace_bytes(B, H, N, d, block_q=128, block_k=64) -> int:
@@ -237,18 +269,17 @@ def sparge_attn_bwd(q, k, v, o, d_o, lse, kv_idx, kv_cnt, block_q=128, block_k=6
                     out=None, workspace=None):
     """dQ, dK, dV of the block-sparse attention for the upstream gradient d_o."""
     B, H, N, d = _qkv(q, k, v, o, d_o)
-    if lse.dtype != torch.float32 or not lse.is_cuda or tuple(lse.shape) != (B, H, N):
-        raise ValueError("lse must be a float32 GPU tensor of shape [B, H, N]")
-    dq, dk, dv = (torch.empty_like(q) for _ in range(3)) if out is None else out
+    _buf(lse, "lse", torch.float32, (B, H, N), q.device)
+    _lists(kv_idx, kv_cnt, q, block_q, block_k)
+    dq, dk, dv = _grads(q, out)
     if scale is None:
         scale = default_scale(d)
-    if workspace is None:
-        workspace = torch.empty(max(attn_bwd_workspace_bytes(B, H, N, d, block_q, block_k), 16),
-                                dtype=torch.uint8, device=q.device)
+    workspace, ws_bytes = _workspace(
+        workspace, attn_bwd_workspace_bytes(B, H, N, d, block_q, block_k), q.device)
     _check(lib().sparge_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse),
                                  _ptr(kv_idx), _ptr(kv_cnt), B, H, N, d, block_q, block_k, scale,
-                                 _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
-                                 workspace.numel(), _stream(q)))
+                                 _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes,
+                                 _stream(q)))
     return dq, dk, dv
 
 
@@ -260,15 +291,15 @@ def sparge_attn_fwd_lowbit(q, k, v, kv_idx, kv_cnt, block_q=128, block_k=64, sca
                            out=None, workspace=None):
     """The sparse branch with INT8 Q/K and e4m3 P/V (see sparge.h)."""
     B, H, N, d = _qkv(q, k, v)
-    o = torch.empty_like(q) if out is None else out
+    _lists(kv_idx, kv_cnt, q, block_q, block_k)
+    o = torch.empty_like(q) if out is None else _buf(out, "out", torch.bfloat16, q.shape, q.device)
     if scale is None:
         scale = default_scale(d)
-    if workspace is None:
-        workspace = torch.empty(max(lowbit_workspace_bytes(B, H, N, d, block_q, block_k), 256),
-                                dtype=torch.uint8, device=q.device)
+    workspace, ws_bytes = _workspace(
+        workspace, lowbit_workspace_bytes(B, H, N, d, block_q, block_k), q.device)
     _check(lib().sparge_attn_fwd_lowbit(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_idx), _ptr(kv_cnt), B,
                                         H, N, d, block_q, block_k, scale, _ptr(o),
-                                        _ptr(workspace), workspace.numel(), _stream(q)))
+                                        _ptr(workspace), ws_bytes, _stream(q)))
     return o
 
 
@@ -280,16 +311,15 @@ def svg2_attn_fwd(q, k, v, n_q_clusters, n_k_clusters, iters=10, p_mass=0.9, blo
                   scale=None, out=None, workspace=None):
     """SVG2: k-means permutation, size-weighted centroid Top-p, clustered attention."""
     B, H, N, d = _qkv(q, k, v)
-    o = torch.empty_like(q) if out is None else out
+    o = torch.empty_like(q) if out is None else _buf(out, "out", torch.bfloat16, q.shape, q.device)
     if scale is None:
         scale = default_scale(d)
-    if workspace is None:
-        workspace = torch.empty(max(svg2_workspace_bytes(B, H, N, d, block_q, n_q_clusters,
-                                                         n_k_clusters), 256),
-                                dtype=torch.uint8, device=q.device)
+    workspace, ws_bytes = _workspace(
+        workspace, svg2_workspace_bytes(B, H, N, d, block_q, n_q_clusters, n_k_clusters),
+        q.device)
     _check(lib().svg2_attn_fwd(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, block_q, n_q_clusters,
                                n_k_clusters, iters, p_mass, scale, _ptr(o), _ptr(workspace),
-                               workspace.numel(), _stream(q)))
+                               ws_bytes, _stream(q)))
     return o
 
 
@@ -300,17 +330,15 @@ def linear_bwd_workspace_bytes(B, H, N, d) -> int:
 def _linear_bwd(fn, q, k, v, o, d_o, lse, kv_idx, kv_cnt, alpha, block_q, block_k, scale,
                 drop_below, out, workspace):
     B, H, N, d = _qkv(q, k, v, o, d_o)
-    if lse.dtype != torch.float32 or not lse.is_cuda or tuple(lse.shape) != (B, H, N):
-        raise ValueError("lse must be a float32 GPU tensor of shape [B, H, N]")
-    dq, dk, dv = (torch.empty_like(q) for _ in range(3)) if out is None else out
+    _buf(lse, "lse", torch.float32, (B, H, N), q.device)
+    _lists(kv_idx, kv_cnt, q, block_q, block_k)
+    dq, dk, dv = _grads(q, out)
     if scale is None:
         scale = default_scale(d)
-    if workspace is None:
-        workspace = torch.empty(max(linear_bwd_workspace_bytes(B, H, N, d), 16),
-                                dtype=torch.uint8, device=q.device)
+    workspace, ws_bytes = _workspace(workspace, linear_bwd_workspace_bytes(B, H, N, d), q.device)
     _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse), _ptr(kv_idx),
               _ptr(kv_cnt), _ptr(alpha), B, H, N, d, block_q, block_k, scale, drop_below,
-              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), _stream(q)))
+              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, _stream(q)))
     return dq, dk, dv
 
 
@@ -318,7 +346,7 @@ def sparse_linear_attn_bwd(q, k, v, o, d_o, lse, kv_idx, kv_cnt, alpha, block_q=
                            scale=None, drop_below=0.0, out=None, workspace=None):
     """dQ, dK, dV of O = O_s + alpha[h] O_l (lse from sparse_linear_attn_fwd)."""
     H = q.shape[1]
-    if alpha.dtype != torch.float32 or not alpha.is_cuda or alpha.numel() != H:
+    if alpha.dtype != torch.float32 or alpha.device != q.device or alpha.numel() != H:
         raise ValueError("alpha must be a float32 GPU tensor of H values")
     return _linear_bwd(lib().sparse_linear_attn_bwd, q, k, v, o, d_o, lse, kv_idx, kv_cnt,
                        alpha.contiguous(), block_q, block_k, scale, drop_below, out, workspace)
@@ -328,7 +356,7 @@ def sla2_mix_attn_bwd(q, k, v, o, d_o, lse, kv_idx, kv_cnt, alpha, block_q=128, 
                       scale=None, drop_below=0.0, out=None, workspace=None):
     """dQ, dK, dV of the SLA2 mix (lse from sla2_mix_attn_fwd); alpha float32 [H, d]."""
     H, d = q.shape[1], q.shape[3]
-    if alpha.dtype != torch.float32 or not alpha.is_cuda or tuple(alpha.shape) != (H, d):
+    if alpha.dtype != torch.float32 or alpha.device != q.device or tuple(alpha.shape) != (H, d):
         raise ValueError("alpha must be a float32 GPU tensor of shape [H, d]")
     return _linear_bwd(lib().sla2_mix_attn_bwd, q, k, v, o, d_o, lse, kv_idx, kv_cnt,
                        alpha.contiguous(), block_q, block_k, scale, drop_below, out, workspace)
@@ -337,11 +365,8 @@ def sla2_mix_attn_bwd(q, k, v, o, d_o, lse, kv_idx, kv_cnt, alpha, block_q=128, 
 def sparge_attn_pack(v, workspace=None):
     """Pack V for sparge_attn_fwd_packed; returns the workspace holding it."""
     B, H, N, d = _qkv(v)
-    if workspace is None:
-        workspace = torch.empty(max(attn_workspace_bytes(B, H, N, d), 16), dtype=torch.uint8,
-                                device=v.device)
-    _check(lib().sparge_attn_pack(_ptr(v), B, H, N, d, _ptr(workspace), workspace.numel(),
-                                  _stream(v)))
+    workspace, ws_bytes = _workspace(workspace, attn_workspace_bytes(B, H, N, d), v.device)
+    _check(lib().sparge_attn_pack(_ptr(v), B, H, N, d, _ptr(workspace), ws_bytes, _stream(v)))
     return workspace
 
 
@@ -349,12 +374,16 @@ def sparge_attn_fwd_packed(q, k, kv_idx, kv_cnt, workspace, block_q=128, block_k
                            out=None):
     """Block-sparse attention with V already packed into `workspace`."""
     B, H, N, d = _qkv(q, k)
-    o = torch.empty_like(q) if out is None else out
+    _lists(kv_idx, kv_cnt, q, block_q, block_k)
+    o = torch.empty_like(q) if out is None else _buf(out, "out", torch.bfloat16, q.shape, q.device)
     if scale is None:
         scale = default_scale(d)
+    if workspace is None:
+        raise ValueError("workspace must hold V packed by sparge_attn_pack")
+    workspace, ws_bytes = _workspace(workspace, 0, q.device)
     _check(lib().sparge_attn_fwd_packed(_ptr(q), _ptr(k), _ptr(kv_idx), _ptr(kv_cnt), B, H, N, d,
                                         block_q, block_k, scale, _ptr(o), _ptr(workspace),
-                                        workspace.numel(), _stream(q)))
+                                        ws_bytes, _stream(q)))
     return o
 
 
@@ -365,17 +394,16 @@ def linear_workspace_bytes(B, H, N, d) -> int:
 def _linear(fn, q, k, v, kv_idx, kv_cnt, alpha, block_q, block_k, scale, drop_below,
             workspace, out, lse=None):
     B, H, N, d = _qkv(q, k, v)
-    o = torch.empty_like(q) if out is None else out
-    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N)):
-        raise ValueError("lse must be a float32 GPU tensor of shape [B, H, N]")
+    _lists(kv_idx, kv_cnt, q, block_q, block_k)
+    o = torch.empty_like(q) if out is None else _buf(out, "out", torch.bfloat16, q.shape, q.device)
+    if lse is not None:
+        _buf(lse, "lse", torch.float32, (B, H, N), q.device)
     if scale is None:
         scale = default_scale(d)
-    ws_bytes = linear_workspace_bytes(B, H, N, d)
-    if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    workspace, ws_bytes = _workspace(workspace, linear_workspace_bytes(B, H, N, d), q.device)
     _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_idx), _ptr(kv_cnt), _ptr(alpha), B, H, N, d,
               block_q, block_k, scale, drop_below, _ptr(o), None if lse is None else _ptr(lse),
-              _ptr(workspace), workspace.numel(), _stream(q)))
+              _ptr(workspace), ws_bytes, _stream(q)))
     return o
 
 
@@ -384,7 +412,7 @@ def sparse_linear_attn_fwd(q, k, v, kv_idx, kv_cnt, alpha, block_q=128, block_k=
     """Sparse attention plus alpha[h] times elu+1 linear attention over dropped blocks;
     heads with |alpha[h]| <= drop_below skip the linear branch."""
     H = q.shape[1]
-    if alpha.dtype != torch.float32 or not alpha.is_cuda or alpha.numel() != H:
+    if alpha.dtype != torch.float32 or alpha.device != q.device or alpha.numel() != H:
         raise ValueError("alpha must be a float32 GPU tensor of H values")
     return _linear(lib().sparse_linear_attn_fwd, q, k, v, kv_idx, kv_cnt, alpha.contiguous(),
                    block_q, block_k, scale, drop_below, workspace, out, lse)
@@ -395,7 +423,7 @@ def sla2_mix_attn_fwd(q, k, v, kv_idx, kv_cnt, alpha, block_q=128, block_k=64, s
     """SLA2 mix alpha[h][c] O_s + (1 - alpha[h][c]) O_l; alpha float32 [H, d] on the GPU.
     Heads with every |1 - alpha[h][c]| <= drop_below skip the linear branch."""
     H, d = q.shape[1], q.shape[3]
-    if alpha.dtype != torch.float32 or not alpha.is_cuda or tuple(alpha.shape) != (H, d):
+    if alpha.dtype != torch.float32 or alpha.device != q.device or tuple(alpha.shape) != (H, d):
         raise ValueError("alpha must be a float32 GPU tensor of shape [H, d]")
     return _linear(lib().sla2_mix_attn_fwd, q, k, v, kv_idx, kv_cnt, alpha.contiguous(),
                    block_q, block_k, scale, drop_below, workspace, out, lse)

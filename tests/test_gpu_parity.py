@@ -534,3 +534,30 @@ def test_drop_decision_follows_alpha_between_calls():
                                                           d, 64, S.default_scale(d),
                                                           float(alpha[h]), 0.0)
             compare_outputs(got[0, h], ref)
+
+
+def test_binding_rejects_mismatched_buffers():
+    """Index lists, outputs and workspaces of the wrong shape, dtype or device are
+    refused before the library sees their pointers."""
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.zeros((1, 2, 300, 64), dtype=torch.bfloat16, device=dev) for _ in range(3))
+    bits, idx, cnt = S.sparge_mask_predict(q, k, 64, 64, 0.5, 0.5)
+    with pytest.raises(ValueError):
+        S.sparge_attn_fwd(q, k, v, idx[..., :-1].contiguous(), cnt, 64, 64)
+    with pytest.raises(ValueError):
+        S.sparge_attn_fwd(q, k, v, idx, cnt.to(torch.int64), 64, 64)
+    with pytest.raises(ValueError):
+        S.sparge_attn_fwd(q, k, v, idx.cpu(), cnt, 64, 64)
+    with pytest.raises(ValueError):
+        S.sparge_attn_fwd(q, k, v, idx, cnt, 64, 64, out=torch.empty((1, 2, 300, 64), device=dev))
+    with pytest.raises(ValueError):
+        S.sparge_attn_fwd(q, k, v, idx, cnt, 64, 64, workspace=torch.empty(1 << 20, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        S.sparge_mask_predict(q, k, 64, 64, 0.5, 0.5, out=(bits, idx[:, :1].contiguous(), cnt))
+    with pytest.raises(ValueError):
+        S.sparge_attn_fwd_packed(q, k, idx, cnt, None, 64, 64)
+    # a workspace of another dtype is measured in bytes
+    ws = torch.empty(S.attn_workspace_bytes(1, 2, 300, 64) // 4 + 1, dtype=torch.float32, device=dev)
+    o = S.sparge_attn_fwd(q, k, v, idx, cnt, 64, 64, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all()
