@@ -593,8 +593,15 @@ __global__ __launch_bounds__(BQ * (LIN ? 4 : 2), (LIN || (D == 128 && BQ == 64))
       ys = ysds;
     }
   }
-  if (!hwave && qrow < N) {
-    uint16_t* orow = o + head + (size_t)qrow * D;
+  // O leaves through LDS: each wave writes its 32 x D tile into its own slice
+  // of buffers no wave reads any more (the K tiles, which the last block does
+  // not use; LIN: the H waves' V^T tiles, past the H_D and O_l staging), rows
+  // with their 16-byte chunks XOR-swizzled, then copies whole rows out, so
+  // that every store instruction writes 64 x 16 contiguous bytes
+  if (!hwave) {
+    unsigned char* stg = smem + (LIN ? 6 * T::BYTES : 0) + wave * 32 * D * 2;
+    static_assert(NW * 32 * D * 2 <= 2 * T::BYTES, "the O tiles must fit two staging buffers");
+    constexpr int CPR = D / 8;  // 16-byte chunks per row
 #pragma unroll
     for (int i = 0; i < DT; ++i)
 #pragma unroll
@@ -631,8 +638,19 @@ __global__ __launch_bounds__(BQ * (LIN ? 4 : 2), (LIN || (D == 128 && BQ == 64))
         uint2 pk;
         pk.x = pack2_bf16(y[0], y[1]);
         pk.y = pack2_bf16(y[2], y[3]);
-        *reinterpret_cast<uint2*>(orow + d0) = pk;
+        const int chunk = (d0 >> 3) ^ (l32 & (CPR - 1));
+        *reinterpret_cast<uint2*>(stg + l32 * D * 2 + chunk * 16 + (d0 & 4) * 2) = pk;
       }
+    wave_lds_fence();
+    constexpr int RPI = 64 / CPR;  // rows per copy instruction
+#pragma unroll
+    for (int r0 = 0; r0 < 32; r0 += RPI) {
+      const int rr = r0 + lane / CPR, cc = lane % CPR;
+      const uint4 val =
+          *reinterpret_cast<const uint4*>(stg + rr * D * 2 + ((cc ^ (rr & (CPR - 1))) << 4));
+      const int row = qi * BQ + wave * 32 + rr;
+      if (row < N) *reinterpret_cast<uint4*>(o + head + (size_t)row * D + cc * 8) = val;
+    }
   }
 }
 

@@ -122,6 +122,15 @@ __device__ __forceinline__ void dma16(const void* src, void* lds) {
 // next step reads; every LDS read of a buffer is consumed before the barrier
 // after which that buffer is refilled. The empty asm statements keep the
 // compiler from moving memory accesses across the barrier.
+// orders a wave's own LDS writes before its later LDS reads of other lanes'
+// data (a wave's LDS instructions execute in order; this keeps the compiler
+// from moving the reads up)
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ void barrier_no_fence() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
