@@ -180,6 +180,36 @@ def test_attention_small_shapes_in_full(B, H, N, d, bq):
             compare_outputs(got[b, h], ref)
 
 
+@pytest.mark.parametrize("N,d,bq,k_frac,p_mass", [
+    (1, 64, 64, 0.1, 0.9), (37, 128, 128, 0.5, 0.0), (64, 64, 64, 0.3, 0.5),
+    (65, 128, 64, 0.2, 0.9), (129, 64, 128, 0.05, 1.0), (200, 128, 128, 1.0, 0.0)])
+def test_mask_and_attention_at_tiny_lengths(N, d, bq, k_frac, p_mass):
+    """The whole path where the sequence is at most a few blocks: one block,
+    a short only block, exact multiples and a one-token last block."""
+    rng = np.random.default_rng(7 * N + d)
+    from block_sparse_attention_softmax_amd.workloads import f64_to_bf16_bits
+    B, H = 2, 2
+    Q, K, V = (f64_to_bf16_bits(rng.standard_normal((B, H, N, d))) for _ in range(3))
+    scale = S.default_scale(d)
+    q, k, v = to_gpu(Q), to_gpu(K), to_gpu(V)
+    bits, idx, cnt = S.sparge_mask_predict(q, k, bq, 64, k_frac, p_mass, scale)
+    o = S.sparge_attn_fwd(q, k, v, idx, cnt, bq, 64, scale)
+    torch.cuda.synchronize()
+    n_k = -(-N // 64)
+    kept = gpu_bits_to_bool(bits, n_k)
+    check_index_list(kept, idx.cpu().numpy(), cnt.cpu().numpy())
+    m = O.predict_mask(Q, K, bq, 64, k_frac, p_mass, scale)
+    ties, differ = compare_masks(m, kept, k_frac, p_mass)
+    print(f"\n[tiny] N={N} d={d} bq={bq} k={k_frac} p={p_mass}: near-tie rows {ties} "
+          f"differing {differ}", flush=True)
+    got = O.bf16_to_f64(o.cpu().view(torch.uint16).numpy())
+    for b in range(B):
+        for h in range(H):
+            ref = O.masked_attention_head(O.bf16_to_f64(Q[b, h]), O.bf16_to_f64(K[b, h]),
+                                          O.bf16_to_f64(V[b, h]), kept[b, h], bq, 64, scale)
+            compare_outputs(got[b, h], ref)
+
+
 def test_pack_then_packed_equals_one_call():
     wl, Q, K, V, q, k, v = workload_tensors("tiny")
     bits, idx, cnt = S.sparge_mask_predict(q, k, wl.block_q, wl.block_k, wl.k_frac, wl.p_mass)
