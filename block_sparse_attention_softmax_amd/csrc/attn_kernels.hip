@@ -649,7 +649,13 @@ __global__ __launch_bounds__(BQ * (LIN ? 4 : 2), (LIN || (D == 128 && BQ == 64))
       const uint4 val =
           *reinterpret_cast<const uint4*>(stg + rr * D * 2 + ((cc ^ (rr & (CPR - 1))) << 4));
       const int row = qi * BQ + wave * 32 + rr;
-      if (row < N) *reinterpret_cast<uint4*>(o + head + (size_t)row * D + cc * 8) = val;
+      // O is not read again here: stream it past the caches the K and V
+      // tiles of the other workgroups are using
+      if (row < N) {
+        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 w = {val.x, val.y, val.z, val.w};
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(o + head + (size_t)row * D + cc * 8));
+      }
     }
   }
 }
