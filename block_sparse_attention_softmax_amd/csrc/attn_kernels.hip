@@ -599,64 +599,43 @@ __global__ __launch_bounds__(BQ * (LIN ? 4 : 2), (LIN || (D == 128 && BQ == 64))
   // with their 16-byte chunks XOR-swizzled, then copies whole rows out, so
   // that every store instruction writes 64 x 16 contiguous bytes
   if (!hwave) {
-    unsigned char* stg = smem + (LIN ? 6 * T::BYTES : 0) + wave * 32 * D * 2;
     static_assert(NW * 32 * D * 2 <= 2 * T::BYTES, "the O tiles must fit two staging buffers");
-    constexpr int CPR = D / 8;  // 16-byte chunks per row
+    unsigned char* stg = smem + (LIN ? 6 * T::BYTES : 0) + wave * 32 * D * 2;
+    store_rows_via_lds<D>(stg, o + head, qi * BQ + wave * 32, N, lane, [&](int i, int g) {
+      const int d0 = 32 * i + 8 * g + 4 * h2;
+      float y[4];
 #pragma unroll
-    for (int i = 0; i < DT; ++i)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * i + 8 * g + 4 * h2;
-        float y[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = oacc[i][4 * g + e] * inv;
-        // mix: alpha[h][d0..d0+3] (plain kernel: the scale of a dropped branch's alpha O_s)
-        const bool mix = SEL && (LIN ? lin_mode == kLinMix : alpha != nullptr);
-        float a[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-        if (mix) {
-          const float4 a4 = *reinterpret_cast<const float4*>(alpha + (size_t)(bh % H) * D + d0);
-          a[0] = a4.x; a[1] = a4.y; a[2] = a4.z; a[3] = a4.w;
-        }
-        bool have_l = false;
-        float lv[4] = {0.0f, 0.0f, 0.0f, 0.0f}, sl = 0.0f;
-        if constexpr (LIN) {
-          if (yl) {
-            const float4 l = yl[((wave * DT + i) * 4 + g) * 64 + lane];
-            lv[0] = l.x; lv[1] = l.y; lv[2] = l.z; lv[3] = l.w;
-            sl = ys[wave * 64 + lane];
-            have_l = true;
-          }
-        }
-        if (mix) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            y[e] = have_l ? fmaf(a[e], y[e], (1.0f - a[e]) * (lv[e] * sl)) : a[e] * y[e];
-        } else if (have_l) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) y[e] = fmaf(lv[e], sl, y[e]);
-        }
-        uint2 pk;
-        pk.x = pack2_bf16(y[0], y[1]);
-        pk.y = pack2_bf16(y[2], y[3]);
-        const int chunk = (d0 >> 3) ^ (l32 & (CPR - 1));
-        *reinterpret_cast<uint2*>(stg + l32 * D * 2 + chunk * 16 + (d0 & 4) * 2) = pk;
+      for (int e = 0; e < 4; ++e) y[e] = oacc[i][4 * g + e] * inv;
+      // mix: alpha[h][d0..d0+3] (plain kernel: the scale of a dropped branch's alpha O_s)
+      const bool mix = SEL && (LIN ? lin_mode == kLinMix : alpha != nullptr);
+      float a[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+      if (mix) {
+        const float4 a4 = *reinterpret_cast<const float4*>(alpha + (size_t)(bh % H) * D + d0);
+        a[0] = a4.x; a[1] = a4.y; a[2] = a4.z; a[3] = a4.w;
       }
-    wave_lds_fence();
-    constexpr int RPI = 64 / CPR;  // rows per copy instruction
-#pragma unroll
-    for (int r0 = 0; r0 < 32; r0 += RPI) {
-      const int rr = r0 + lane / CPR, cc = lane % CPR;
-      const uint4 val =
-          *reinterpret_cast<const uint4*>(stg + rr * D * 2 + ((cc ^ (rr & (CPR - 1))) << 4));
-      const int row = qi * BQ + wave * 32 + rr;
-      // O is not read again here: stream it past the caches the K and V
-      // tiles of the other workgroups are using
-      if (row < N) {
-        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-        const u32x4 w = {val.x, val.y, val.z, val.w};
-        __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(o + head + (size_t)row * D + cc * 8));
+      bool have_l = false;
+      float lv[4] = {0.0f, 0.0f, 0.0f, 0.0f}, sl = 0.0f;
+      if constexpr (LIN) {
+        if (yl) {
+          const float4 l = yl[((wave * DT + i) * 4 + g) * 64 + lane];
+          lv[0] = l.x; lv[1] = l.y; lv[2] = l.z; lv[3] = l.w;
+          sl = ys[wave * 64 + lane];
+          have_l = true;
+        }
       }
-    }
+      if (mix) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          y[e] = have_l ? fmaf(a[e], y[e], (1.0f - a[e]) * (lv[e] * sl)) : a[e] * y[e];
+      } else if (have_l) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = fmaf(lv[e], sl, y[e]);
+      }
+      uint2 pk;
+      pk.x = pack2_bf16(y[0], y[1]);
+      pk.y = pack2_bf16(y[2], y[3]);
+      return pk;
+    });
   }
 }
 

@@ -334,25 +334,25 @@ __global__ __launch_bounds__(BQ * 2, 2) void sparse_attn_lowbit_kernel(
   // O = sv_c * sum(codeP codeV) / sum(codeP) (the 448s cancel)
   const float ltot = lsum + __shfl_xor(lsum, 32);
   const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
-  if (qrow < N) {
-    uint16_t* orow = o + head + (size_t)qrow * D;
+  // O leaves through LDS as whole rows (each wave's 32 x D tile in its own
+  // slice of the tile buffers, free once every wave is past its last block)
+  static_assert(BQ * D * 2 <= (int)sizeof(smem), "the O tiles must fit the tile buffers");
+  __syncthreads();
+  store_rows_via_lds<D>(smem + wave * 32 * D * 2, o + head, qi * BQ + wave * 32, N, lane,
+                        [&](int i, int g) {
+                          const int d0 = 32 * i + 8 * g + 4 * h2;
+                          float y[4];
 #pragma unroll
-    for (int i = 0; i < DT; ++i)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * i + 8 * g + 4 * h2;
-        float y[4];
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          const float sv_c = __uint_as_float(vmax[(size_t)bh * D + d0 + e2]) / kE4m3Max;
-          y[e2] = oacc[i][4 * g + e2] * sv_c * inv;
-        }
-        uint2 pk;
-        pk.x = pack2_bf16(y[0], y[1]);
-        pk.y = pack2_bf16(y[2], y[3]);
-        *reinterpret_cast<uint2*>(orow + d0) = pk;
-      }
-  }
+                          for (int e2 = 0; e2 < 4; ++e2) {
+                            const float sv_c =
+                                __uint_as_float(vmax[(size_t)bh * D + d0 + e2]) / kE4m3Max;
+                            y[e2] = oacc[i][4 * g + e2] * sv_c * inv;
+                          }
+                          uint2 pk;
+                          pk.x = pack2_bf16(y[0], y[1]);
+                          pk.y = pack2_bf16(y[2], y[3]);
+                          return pk;
+                        });
 }
 
 template <int D, int BQ>

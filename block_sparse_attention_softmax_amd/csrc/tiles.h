@@ -131,6 +131,41 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// A wave's 32 output rows (queries row0 .. row0+31, D channels, bf16) leave
+// through LDS: pk(i, g) gives the 8 bytes of channels 32 i + 8 g + 4 h .. +3
+// (h = lane / 32) for the lane's query lane % 32, in the register layout of a
+// 32x32 MFMA accumulator. They are written into the wave's own tile at `stg`
+// (32 x D, 16-byte chunks XOR-swizzled by row) and copied out as whole rows,
+// 64 x 16 contiguous bytes per store instruction, with non-temporal stores
+// (the rows are not read again by the kernel). Rows at or past N are skipped.
+template <int D, typename F>
+__device__ __forceinline__ void store_rows_via_lds(unsigned char* stg, uint16_t* out, int row0,
+                                                   int N, int lane, F&& pk) {
+  constexpr int CPR = D / 8, DT = D / 32;  // 16-byte chunks per row, 32-channel tiles
+  const int l32 = lane & 31, h2 = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < DT; ++i)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = 32 * i + 8 * g + 4 * h2;
+      const int chunk = (d0 >> 3) ^ (l32 & (CPR - 1));
+      *reinterpret_cast<uint2*>(stg + l32 * D * 2 + chunk * 16 + (d0 & 4) * 2) = pk(i, g);
+    }
+  wave_lds_fence();
+  constexpr int RPI = 64 / CPR;  // rows per copy instruction
+#pragma unroll
+  for (int r0 = 0; r0 < 32; r0 += RPI) {
+    const int rr = r0 + lane / CPR, cc = lane % CPR;
+    const uint4 val = *reinterpret_cast<const uint4*>(stg + rr * D * 2 + ((cc ^ (rr & (CPR - 1))) << 4));
+    const int row = row0 + rr;
+    if (row < N) {
+      typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+      const u32x4 w = {val.x, val.y, val.z, val.w};
+      __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(out + (size_t)row * D + cc * 8));
+    }
+  }
+}
+
 __device__ __forceinline__ void barrier_no_fence() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
