@@ -2,9 +2,9 @@
 
 One step = the whole path on one batch of synthetic input: mask prediction
 (pool Q and K, float64 block scores, hybrid selection, index list) and the
-re-packing of V (on a second stream, overlapping the mask), then the
-block-sparse attention forward over the kept key blocks. Inputs are resident
-in HBM before the timed region starts.
+re-packing of V (on a second stream, after the pooling and beside the scores
+and the selection), then the block-sparse attention forward over the kept key
+blocks. Inputs are resident in HBM before the timed region starts.
 
 Default workload: the Wan2.1-1.3B-shaped grid (B=1, H=12, N=32760 =
 21x30x52, d=128, blocks 128x64, k=5%, p=0.9). `value` is dense-equivalent
@@ -122,7 +122,8 @@ def main():
     ap.add_argument("--no-other-configs", action="store_true",
                     help="skip the forward at the 95%% and Wan 14B 720p configurations")
     ap.add_argument("--no-overlap", action="store_true",
-                    help="pack V on the main stream after the mask instead of beside it")
+                    help="pack V on the main stream between the mask's halves instead of beside "
+                         "the second")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one device-to-device copy of this many MiB first, as a "
                          "known-size reference for hardware byte counters")
@@ -175,29 +176,44 @@ def main():
     main = torch.cuda.current_stream()
     side = torch.cuda.Stream()  # default priority
 
-    def step(k_frac, p_mass, ev=None, linear=None, alpha_t=None, routed=False):
-        """V pack (side stream) || mask (main stream) -> attention (main stream).
+    pooled = torch.cuda.Event()
 
-        The pack reads only V and the mask only Q and K, so the two halves of
-        sparge_attn_fwd's work overlap; the side stream first waits for the
-        previous step's attention, which reads the packed V."""
+    def step(k_frac, p_mass, ev=None, linear=None, alpha_t=None, routed=False):
+        """mask pooling -> (V pack on the side stream || block scores and selection)
+        -> attention, all but the pack on the main stream.
+
+        Pooling and the V pack both stream a whole tensor from HBM, the scores
+        and the selection do not, so the pack waits for the pooling and runs
+        beside the rest of the mask. The pack's wait on the pooling also orders
+        it after the previous step's attention, which reads the packed V. (The
+        routed mask, kept in one call, runs beside the whole pack.)"""
         pack_stream = main if args.no_overlap else side
-        if not linear:
-            side.wait_stream(main)
+
+        def pack():
             with torch.cuda.stream(pack_stream):
                 if ev is not None:
                     ev[4].record()
                 S.sparge_attn_pack(v, workspace=aws)
                 if ev is not None:
                     ev[5].record()
-        if ev is not None:
-            ev[0].record()
+
         if routed:
+            side.wait_stream(main)
+            pack()
+            if ev is not None:
+                ev[0].record()
             S.sparge_mask_predict_routed(q, k, w_q, w_k, wl.block_q, wl.block_k, k_frac, p_mass,
                                          wl.scale, workspace=rws, out=(bits, idx, cnt))
         else:
-            S.sparge_mask_predict(q, k, wl.block_q, wl.block_k, k_frac, p_mass, wl.scale,
-                                  workspace=ws, out=(bits, idx, cnt))
+            if ev is not None:
+                ev[0].record()
+            S.sparge_mask_pool(q, k, wl.block_q, wl.block_k, workspace=ws)
+            if not linear:
+                pooled.record(main)
+                side.wait_event(pooled)
+                pack()
+            S.sparge_mask_select(q, ws, wl.block_q, wl.block_k, k_frac, p_mass, wl.scale,
+                                 out=(bits, idx, cnt))
         if ev is not None:
             ev[1].record()
         if linear:

@@ -19,7 +19,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsparge.s
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP = 0, -1, -2, -3
 
 # every symbol the public header declares
-EXPORTS = ("sparge_mask_workspace_bytes", "sparge_mask_predict",
+EXPORTS = ("sparge_mask_workspace_bytes", "sparge_mask_predict", "sparge_mask_pool",
+           "sparge_mask_select",
            "sparge_mask_routed_workspace_bytes", "sparge_mask_predict_routed",
            "sparge_attn_workspace_bytes", "sparge_attn_fwd", "sparge_attn_pack",
            "sparge_attn_fwd_packed", "sparse_linear_workspace_bytes", "sparse_linear_attn_fwd",
@@ -51,6 +52,10 @@ def lib() -> ctypes.CDLL:
         L.sparge_mask_predict.argtypes = [vp, vp] + [c_int] * 6 + [c_float] * 3 + [vp] * 5 + [
             c_size, vp]
         L.sparge_mask_predict.restype = c_int
+        L.sparge_mask_pool.argtypes = [vp, vp] + [c_int] * 6 + [vp, c_size, vp]
+        L.sparge_mask_pool.restype = c_int
+        L.sparge_mask_select.argtypes = [c_int] * 6 + [c_float] * 3 + [vp] * 5 + [c_size, vp]
+        L.sparge_mask_select.restype = c_int
         L.sparge_mask_routed_workspace_bytes.argtypes = [c_int] * 6
         L.sparge_mask_routed_workspace_bytes.restype = c_size
         L.sparge_mask_predict_routed.argtypes = [vp] * 4 + [c_int] * 6 + [c_float] * 3 + [
@@ -186,6 +191,35 @@ def sparge_mask_predict(q, k, block_q=128, block_k=64, k_frac=0.05, p_mass=0.9, 
     _check(lib().sparge_mask_predict(
         _ptr(q), _ptr(k), B, H, N, d, block_q, block_k, k_frac, p_mass, scale,
         _ptr(bits), _ptr(idx), _ptr(cnt), _ptr(logits), _ptr(workspace), ws_bytes, _stream(q)))
+    return (bits, idx, cnt, logits) if return_logits else (bits, idx, cnt)
+
+
+def sparge_mask_pool(q, k, block_q=128, block_k=64, workspace=None):
+    """First half of sparge_mask_predict: pooled Q and K into the workspace,
+    which it returns (pass it to sparge_mask_select)."""
+    B, H, N, d = _qkv(q, k)
+    workspace, ws_bytes = _workspace(workspace, mask_workspace_bytes(B, H, N, d, block_q, block_k),
+                                     q.device)
+    _check(lib().sparge_mask_pool(_ptr(q), _ptr(k), B, H, N, d, block_q, block_k,
+                                  _ptr(workspace), ws_bytes, _stream(q)))
+    return workspace
+
+
+def sparge_mask_select(q, workspace, block_q=128, block_k=64, k_frac=0.05, p_mass=0.9,
+                       scale=None, return_logits=False, out=None):
+    """Second half of sparge_mask_predict, from the workspace sparge_mask_pool
+    filled (q gives the shape, device and stream only); outputs as
+    sparge_mask_predict."""
+    B, H, N, d = _qkv(q)
+    if workspace is None:
+        raise ValueError("workspace must hold the pooled Q and K of sparge_mask_pool")
+    workspace, ws_bytes = _workspace(workspace, 0, q.device)
+    bits, idx, cnt, logits = _mask_outputs(q, block_q, block_k, out, return_logits)
+    if scale is None:
+        scale = default_scale(d)
+    _check(lib().sparge_mask_select(B, H, N, d, block_q, block_k, k_frac, p_mass, scale,
+                                    _ptr(bits), _ptr(idx), _ptr(cnt), _ptr(logits),
+                                    _ptr(workspace), ws_bytes, _stream(q)))
     return (bits, idx, cnt, logits) if return_logits else (bits, idx, cnt)
 
 

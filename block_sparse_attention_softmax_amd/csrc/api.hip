@@ -104,29 +104,34 @@ size_t sparge_mask_workspace_bytes(int B, int H, int N, int d, int block_q, int 
 }  // extern "C"
 
 namespace {
-// the mask, optionally with the router's projections (wq, wk both set)
+// the mask, optionally with the router's projections (wq, wk both set);
+// phase 1 pools only (q, k, workspace), phase 2 does the rest (workspace and
+// outputs), phase 0 both
 int mask_impl(const void* q, const void* k, const float* wq, const float* wk, int B, int H,
               int N, int d, int block_q, int block_k, float k_frac, float p_mass, float scale,
               uint32_t* mask_bits, int32_t* kv_idx, int32_t* kv_cnt, double* block_logits,
-              void* workspace, size_t workspace_bytes, void* stream) {
+              void* workspace, size_t workspace_bytes, void* stream, int phase = 0) {
   int rc = check_shape(B, H, N, d, block_q, block_k);
   if (rc != SPARGE_OK) return rc;
   const int n_q = ceil_div(N, block_q), n_k = ceil_div(N, block_k);
   if (n_k > kMaxKeyBlocks)
     return fail(SPARGE_ERR_UNSUPPORTED, "more than 4096 key blocks (N > 262144)");
-  if (!(k_frac > 0.0f) || !(k_frac <= 1.0f))
-    return fail(SPARGE_ERR_INVALID_ARG, "k_frac must satisfy 0 < k_frac <= 1");
-  if (!(p_mass >= 0.0f) || !isfinite(p_mass))
-    return fail(SPARGE_ERR_INVALID_ARG, "p_mass must be finite and >= 0");
-  if (!(scale > 0.0f) || !isfinite(scale))
-    return fail(SPARGE_ERR_INVALID_ARG, "scale must be finite and > 0");
-  if (!q || !k || !mask_bits || !kv_idx || !kv_cnt || !workspace)
+  const bool pools = phase != 2, selects = phase != 1;
+  if (selects) {
+    if (!(k_frac > 0.0f) || !(k_frac <= 1.0f))
+      return fail(SPARGE_ERR_INVALID_ARG, "k_frac must satisfy 0 < k_frac <= 1");
+    if (!(p_mass >= 0.0f) || !isfinite(p_mass))
+      return fail(SPARGE_ERR_INVALID_ARG, "p_mass must be finite and >= 0");
+    if (!(scale > 0.0f) || !isfinite(scale))
+      return fail(SPARGE_ERR_INVALID_ARG, "scale must be finite and > 0");
+  }
+  if ((pools && (!q || !k)) || (selects && (!mask_bits || !kv_idx || !kv_cnt)) || !workspace)
     return fail(SPARGE_ERR_INVALID_ARG, "null pointer argument");
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(workspace, 16))
+  if ((pools && (!aligned(q, 16) || !aligned(k, 16))) || !aligned(workspace, 16))
     return fail(SPARGE_ERR_INVALID_ARG, "q, k and workspace must be 16-byte aligned");
-  if (!aligned(mask_bits, 4) || !aligned(kv_idx, 4) || !aligned(kv_cnt, 4))
+  if (selects && (!aligned(mask_bits, 4) || !aligned(kv_idx, 4) || !aligned(kv_cnt, 4)))
     return fail(SPARGE_ERR_INVALID_ARG, "mask_bits, kv_idx, kv_cnt must be 4-byte aligned");
-  if (block_logits && !aligned(block_logits, 8))
+  if (selects && block_logits && !aligned(block_logits, 8))
     return fail(SPARGE_ERR_INVALID_ARG, "block_logits must be 8-byte aligned");
   const bool routed = wq != nullptr;
   if (routed && (!aligned(wq, 4) || !aligned(wk, 4)))
@@ -136,6 +141,7 @@ int mask_impl(const void* q, const void* k, const float* wq, const float* wk, in
   if (workspace_bytes < need) return fail(SPARGE_ERR_INVALID_ARG, "workspace too small");
 
   sparge::MaskLaunch a{};
+  a.phase = phase;
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
   a.B = B; a.H = H; a.N = N; a.d = d; a.block_q = block_q; a.block_k = block_k;
@@ -186,6 +192,23 @@ int sparge_mask_predict(const void* q, const void* k, int B, int H, int N, int d
   g_last_error.clear();
   return mask_impl(q, k, nullptr, nullptr, B, H, N, d, block_q, block_k, k_frac, p_mass, scale,
                    mask_bits, kv_idx, kv_cnt, block_logits, workspace, workspace_bytes, stream);
+}
+
+int sparge_mask_pool(const void* q, const void* k, int B, int H, int N, int d, int block_q,
+                     int block_k, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  return mask_impl(q, k, nullptr, nullptr, B, H, N, d, block_q, block_k, 1.0f, 0.0f, 1.0f,
+                   nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes, stream, 1);
+}
+
+int sparge_mask_select(int B, int H, int N, int d, int block_q, int block_k, float k_frac,
+                       float p_mass, float scale, uint32_t* mask_bits, int32_t* kv_idx,
+                       int32_t* kv_cnt, double* block_logits, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  return mask_impl(nullptr, nullptr, nullptr, nullptr, B, H, N, d, block_q, block_k, k_frac,
+                   p_mass, scale, mask_bits, kv_idx, kv_cnt, block_logits, workspace,
+                   workspace_bytes, stream, 2);
 }
 
 size_t sparge_mask_routed_workspace_bytes(int B, int H, int N, int d, int block_q, int block_k) {

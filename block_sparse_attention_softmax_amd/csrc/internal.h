@@ -37,6 +37,7 @@ __device__ __forceinline__ int xcd_remap(int wg, int total) {
 
 // ---- launchers (each returns the hipError_t of its launches) ----
 struct MaskLaunch {
+  int phase;  // 0: the whole mask; 1: pooling only; 2: everything after the pooling
   const uint16_t* q;
   const uint16_t* k;
   int B, H, N, d, block_q, block_k, n_q, n_k, npad, words;

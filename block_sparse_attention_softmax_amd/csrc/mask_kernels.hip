@@ -609,12 +609,15 @@ hipError_t launch_mask(const MaskLaunch& a, hipStream_t st) {
       hipLaunchKernelGGL(block_logits_kernel<64>, dim3((tiles + 3) / 4), dim3(kThreads), 0, st,
                          x, y, out, nx, ny, tq, tk, tiles, sc);
   };
-  if (a.d == 128)
-    hipLaunchKernelGGL(pool_mean_kernel<128>, dim3(a.n_q + a.n_k, BH), dim3(kThreads), 0, st,
-                       a.q, a.k, a.qbar, a.kbar, a.N, a.block_q, a.block_k, a.n_q, a.n_k);
-  else
-    hipLaunchKernelGGL(pool_mean_kernel<64>, dim3(a.n_q + a.n_k, BH), dim3(kThreads), 0, st,
-                       a.q, a.k, a.qbar, a.kbar, a.N, a.block_q, a.block_k, a.n_q, a.n_k);
+  if (a.phase != 2) {
+    if (a.d == 128)
+      hipLaunchKernelGGL(pool_mean_kernel<128>, dim3(a.n_q + a.n_k, BH), dim3(kThreads), 0, st,
+                         a.q, a.k, a.qbar, a.kbar, a.N, a.block_q, a.block_k, a.n_q, a.n_k);
+    else
+      hipLaunchKernelGGL(pool_mean_kernel<64>, dim3(a.n_q + a.n_k, BH), dim3(kThreads), 0, st,
+                         a.q, a.k, a.qbar, a.kbar, a.N, a.block_q, a.block_k, a.n_q, a.n_k);
+    if (a.phase == 1) return hipGetLastError();
+  }
   const double* qs = a.qbar;
   const double* ks = a.kbar;
   if (a.wq) {  // router: project the pooled rows first (float64, scale 1)

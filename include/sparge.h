@@ -94,6 +94,22 @@ int sparge_mask_predict(const void* q, const void* k, int B, int H, int N, int d
                         int32_t* kv_cnt, double* block_logits, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/* The two halves of sparge_mask_predict, for callers that run other work
+ * beside the second: sparge_mask_pool writes the pooled queries and keys
+ * (Qbar, Kbar above) into the workspace; sparge_mask_select forms the block
+ * scores from them and selects. Enqueued in that order on one stream, with
+ * the same B, H, N, d, block sizes and workspace (its contents left alone in
+ * between), they give exactly the outputs of one sparge_mask_predict call.
+ * sparge_mask_pool reads only q and k (bandwidth-bound); sparge_mask_select
+ * reads only the workspace. Arguments, layouts and errors as for
+ * sparge_mask_predict; each checks the arguments it takes. */
+int sparge_mask_pool(const void* q, const void* k, int B, int H, int N, int d, int block_q,
+                     int block_k, void* workspace, size_t workspace_bytes, void* stream);
+int sparge_mask_select(int B, int H, int N, int d, int block_q, int block_k, float k_frac,
+                       float p_mass, float scale, uint32_t* mask_bits, int32_t* kv_idx,
+                       int32_t* kv_cnt, double* block_logits, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
 /* Device workspace (bytes) of sparge_mask_predict_routed: that of
  * sparge_mask_predict plus the router weights as float64 and the projected
  * pooled queries and keys. Returns 0 for arguments it would reject. */

@@ -115,6 +115,37 @@ def test_mask_rejects_bad_arguments(kw, code):
     assert binding.lib().sparge_last_error().decode()
 
 
+def _pool(**kw):
+    args = dict(q=A, k=A, B=1, H=2, N=1024, d=64, bq=64, bk=64, ws=A, wsb=1 << 30, st=None)
+    args.update(kw)
+    return binding.lib().sparge_mask_pool(*args.values())
+
+
+def _select(**kw):
+    args = dict(B=1, H=2, N=1024, d=64, bq=64, bk=64, kf=0.1, p=0.9, sc=0.125, bits=A, idx=A,
+                cnt=A, logits=None, ws=A, wsb=1 << 30, st=None)
+    args.update(kw)
+    return binding.lib().sparge_mask_select(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(k=MIS), -1), (dict(ws=None), -1), (dict(ws=MIS), -1),
+    (dict(d=96), -2), (dict(bq=32), -2), (dict(N=0), -1), (dict(wsb=100), -1),
+    (dict(N=64 * 4097), -2)])
+def test_mask_pool_rejects_bad_arguments(kw, code):
+    assert _pool(**kw) == code
+    assert binding.lib().sparge_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(bits=None), -1), (dict(idx=MIS), -1), (dict(cnt=None), -1), (dict(ws=None), -1),
+    (dict(logits=ctypes.c_void_p(0x10004)), -1), (dict(kf=0.0), -1), (dict(p=float("nan")), -1),
+    (dict(sc=-1.0), -1), (dict(d=96), -2), (dict(bk=128), -2), (dict(wsb=100), -1)])
+def test_mask_select_rejects_bad_arguments(kw, code):
+    assert _select(**kw) == code
+    assert binding.lib().sparge_last_error().decode()
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), -1), (dict(o=None), -1), (dict(cnt=None), -1), (dict(v=MIS), -1),
     (dict(d=80), -2), (dict(bq=256), -2), (dict(bk=32), -2), (dict(N=0), -1),

@@ -566,6 +566,26 @@ def test_drop_decision_follows_alpha_between_calls():
             compare_outputs(got[0, h], ref)
 
 
+@pytest.mark.parametrize("name,k_frac,p_mass", [("wan1.3b", 0.05, 0.9), ("wan1.3b", 0.05, 0.0),
+                                                ("tiny", 0.1, 0.9)])
+def test_mask_in_two_halves_equals_one_call(name, k_frac, p_mass):
+    """sparge_mask_pool then sparge_mask_select on one stream give exactly the
+    outputs of sparge_mask_predict, scores included."""
+    wl, Q, K, V, q, k, v = workload_tensors(name)
+    one = S.sparge_mask_predict(q, k, wl.block_q, wl.block_k, k_frac, p_mass, wl.scale,
+                                return_logits=True)
+    ws = S.sparge_mask_pool(q, k, wl.block_q, wl.block_k)
+    two = S.sparge_mask_select(q, ws, wl.block_q, wl.block_k, k_frac, p_mass, wl.scale,
+                               return_logits=True)
+    torch.cuda.synchronize()
+    bits1, idx1, cnt1, lg1 = one
+    bits2, idx2, cnt2, lg2 = two
+    assert torch.equal(bits1, bits2) and torch.equal(cnt1, cnt2) and torch.equal(lg1, lg2)
+    pos = torch.arange(idx1.shape[-1], device=idx1.device)
+    valid = pos < cnt1.unsqueeze(-1)
+    assert torch.equal(idx1[valid], idx2[valid])
+
+
 def test_binding_rejects_mismatched_buffers():
     """Index lists, outputs and workspaces of the wrong shape, dtype or device are
     refused before the library sees their pointers."""
