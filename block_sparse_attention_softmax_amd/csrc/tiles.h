@@ -116,13 +116,7 @@ __device__ __forceinline__ void dma16(const void* src, void* lds) {
   __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
 }
 
-// Workgroup barrier without the memory fence of __syncthreads, whose release
-// half waits for every direct-to-LDS copy still in flight, prefetches of later
-// stages included. Callers first wait (s_waitcnt vmcnt) for the copies the
-// next step reads; every LDS read of a buffer is consumed before the barrier
-// after which that buffer is refilled. The empty asm statements keep the
-// compiler from moving memory accesses across the barrier.
-// orders a wave's own LDS writes before its later LDS reads of other lanes'
+// Orders a wave's own LDS writes before its later LDS reads of other lanes'
 // data (a wave's LDS instructions execute in order; this keeps the compiler
 // from moving the reads up)
 __device__ __forceinline__ void wave_lds_fence() {
@@ -166,6 +160,12 @@ __device__ __forceinline__ void store_rows_via_lds(unsigned char* stg, uint16_t*
   }
 }
 
+// Workgroup barrier without the memory fence of __syncthreads, whose release
+// half waits for every direct-to-LDS copy still in flight, prefetches of later
+// stages included. Callers first wait (s_waitcnt vmcnt) for the copies the
+// next step reads; every LDS read of a buffer is consumed before the barrier
+// after which that buffer is refilled. The empty asm statements keep the
+// compiler from moving memory accesses across the barrier.
 __device__ __forceinline__ void barrier_no_fence() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
