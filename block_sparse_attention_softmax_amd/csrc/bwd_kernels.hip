@@ -619,26 +619,25 @@ __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void sparse
     __syncthreads();  // every wave is done with K^T of block e
     if (e + 1 < count) issue_kt(jat(e + 1));
   }
-  if (valid) {
-    uint16_t* orow = dq + head + (size_t)qrow * D;
+  // dQ leaves through LDS as whole rows (every buffer is free after the
+  // loop's last barrier; each wave uses its own 32 x D slice)
+  static_assert(BQ * D * 2 <= (int)sizeof(smem), "the dQ tiles must fit the buffers");
+  store_rows_via_lds<D>(smem + wave * 32 * D * 2, dq + head, qi * BQ + wave * 32, N, lane,
+                        [&](int ii, int gg) {
+                          const int d0 = 32 * ii + 8 * gg + 4 * h2;
+                          float y[4];
 #pragma unroll
-    for (int ii = 0; ii < DT; ++ii)
-#pragma unroll
-      for (int gg = 0; gg < 4; ++gg) {
-        const int d0 = 32 * ii + 8 * gg + 4 * h2;
-        float y[4];
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) y[e2] = scale * acc[ii][4 * gg + e2];
-        if (lin_dq) {  // the linear branch's share, float32
-          const float4 l = *reinterpret_cast<const float4*>(lin_dq + head + (size_t)qrow * D + d0);
-          y[0] += l.x; y[1] += l.y; y[2] += l.z; y[3] += l.w;
-        }
-        uint2 pk;
-        pk.x = pack2_bf16(y[0], y[1]);
-        pk.y = pack2_bf16(y[2], y[3]);
-        *reinterpret_cast<uint2*>(orow + d0) = pk;
-      }
-  }
+                          for (int e2 = 0; e2 < 4; ++e2) y[e2] = scale * acc[ii][4 * gg + e2];
+                          if (lin_dq && valid) {  // the linear branch's share, float32
+                            const float4 l = *reinterpret_cast<const float4*>(
+                                lin_dq + head + (size_t)qrow * D + d0);
+                            y[0] += l.x; y[1] += l.y; y[2] += l.z; y[3] += l.w;
+                          }
+                          uint2 pk;
+                          pk.x = pack2_bf16(y[0], y[1]);
+                          pk.y = pack2_bf16(y[2], y[3]);
+                          return pk;
+                        });
 }
 
 // ------------------------------------------------ linear branch backward
