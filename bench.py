@@ -4,7 +4,11 @@ One step = the whole path on one batch of synthetic input: mask prediction
 (pool Q and K, float64 block scores, hybrid selection, index list) and the
 re-packing of V (on a second stream, after the pooling and beside the scores
 and the selection), then the block-sparse attention forward over the kept key
-blocks. Inputs are resident in HBM before the timed region starts.
+blocks. Inputs are resident in HBM before the timed region starts. The step
+time is the average over K steps replayed from a HIP graph of one step (every
+launch and stream join of the step, nothing skipped; --no-graph times them
+eagerly); the mask, pack and attention-kernel times come from an eager pass of
+the same K steps with HIP events around each part.
 
 Default workload: the Wan2.1-1.3B-shaped grid (B=1, H=12, N=32760 =
 21x30x52, d=128, blocks 128x64, k=5%, p=0.9). `value` is dense-equivalent
@@ -121,6 +125,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-configs", action="store_true",
                     help="skip the forward at the 95%% and Wan 14B 720p configurations")
+    ap.add_argument("--no-graph", dest="graph", action="store_false",
+                    help="time the plain step eagerly instead of replaying a HIP graph of it")
     ap.add_argument("--no-overlap", action="store_true",
                     help="pack V on the main stream between the mask's halves instead of beside "
                          "the second")
@@ -187,7 +193,8 @@ def main():
         beside the rest of the mask. The pack's wait on the pooling also orders
         it after the previous step's attention, which reads the packed V. (The
         routed mask, kept in one call, runs beside the whole pack.)"""
-        pack_stream = main if args.no_overlap else side
+        cur = torch.cuda.current_stream()  # the main stream, or the capture stream
+        pack_stream = cur if args.no_overlap else side
 
         def pack():
             with torch.cuda.stream(pack_stream):
@@ -198,7 +205,7 @@ def main():
                     ev[5].record()
 
         if routed:
-            side.wait_stream(main)
+            side.wait_stream(cur)
             pack()
             if ev is not None:
                 ev[0].record()
@@ -209,7 +216,7 @@ def main():
                 ev[0].record()
             S.sparge_mask_pool(q, k, wl.block_q, wl.block_k, workspace=ws)
             if not linear:
-                pooled.record(main)
+                pooled.record(cur)
                 side.wait_event(pooled)
                 pack()
             S.sparge_mask_select(q, ws, wl.block_q, wl.block_k, k_frac, p_mass, wl.scale,
@@ -223,7 +230,7 @@ def main():
             if ev is not None:
                 ev[2].record()
         else:
-            main.wait_stream(side)
+            cur.wait_stream(side)
             if ev is not None:
                 ev[2].record()
             S.sparge_attn_fwd_packed(q, k, idx, cnt, aws, wl.block_q, wl.block_k, wl.scale,
@@ -231,16 +238,44 @@ def main():
         if ev is not None:
             ev[3].record()
 
-    def timed(k_frac, p_mass, steps, warmup, linear=None, alpha_t=None, routed=False):
-        for _ in range(warmup):
-            step(k_frac, p_mass, linear=linear, alpha_t=alpha_t, routed=routed)
+    def capture(fn):
+        """A HIP graph of fn's launches (both streams), captured after one run on
+        the capture stream."""
+        graph, cs = torch.cuda.CUDAGraph(), torch.cuda.Stream()
+        cs.wait_stream(main)
+        with torch.cuda.stream(cs):
+            fn()
+        main.wait_stream(cs)
         torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=cs):
+            fn()
+        return graph
+
+    def timed(k_frac, p_mass, steps, warmup, linear=None, alpha_t=None, routed=False):
+        kw = dict(linear=linear, alpha_t=alpha_t, routed=routed)
+        for _ in range(warmup):
+            step(k_frac, p_mass, **kw)
+        torch.cuda.synchronize()
+        # the breakdown: the steps once with events around their parts
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
-        t0 = time.perf_counter()
         for i in range(steps):
-            step(k_frac, p_mass, evs[i], linear=linear, alpha_t=alpha_t, routed=routed)
+            step(k_frac, p_mass, evs[i], **kw)
+        torch.cuda.synchronize()
+        # the step time: the same steps without events; the plain path replayed
+        # from a HIP graph of one step (its launches and stream joins)
+        run = lambda: step(k_frac, p_mass, **kw)
+        graph = None
+        if args.graph and not linear and not routed:
+            graph = capture(run)
+            run = graph.replay
+            run()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            run()
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) / steps
+        del graph
         mask_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
         pack_ms = (float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) if linear else
                    float(np.mean([e[4].elapsed_time(e[5]) for e in evs])))

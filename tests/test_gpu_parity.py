@@ -611,3 +611,61 @@ def test_binding_rejects_mismatched_buffers():
     o = S.sparge_attn_fwd(q, k, v, idx, cnt, 64, 64, workspace=ws)
     torch.cuda.synchronize()
     assert torch.isfinite(o.float()).all()
+
+
+@pytest.mark.parametrize("k_frac,p_mass", [(0.05, 0.9), (0.05, 0.0)])
+def test_step_graph_replays_match_eager(k_frac, p_mass):
+    """One forward step (pool; V repack on a second stream; select; join;
+    attention) captured in a HIP graph: every replay, with eager steps and
+    synchronizations between the replays, gives exactly the eager step's
+    mask and output, which equal the one-call entry points' results."""
+    wl, Q, K, V, q, k, v = workload_tensors("wan1.3b")
+    B, H, N, d = q.shape
+    dev = q.device
+    bits = torch.empty((B, H, wl.n_q, -(-wl.n_k // 32)), dtype=torch.int32, device=dev)
+    idx = torch.empty((B, H, wl.n_q, wl.n_k), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, H, wl.n_q), dtype=torch.int32, device=dev)
+    ws = torch.empty(S.mask_workspace_bytes(B, H, N, d, wl.block_q, wl.block_k),
+                     dtype=torch.uint8, device=dev)
+    aws = torch.empty(S.attn_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+    o = torch.empty_like(q)
+    side, pooled = torch.cuda.Stream(), torch.cuda.Event()
+
+    def step():
+        cur = torch.cuda.current_stream()
+        S.sparge_mask_pool(q, k, wl.block_q, wl.block_k, workspace=ws)
+        pooled.record(cur)
+        side.wait_event(pooled)
+        with torch.cuda.stream(side):
+            S.sparge_attn_pack(v, workspace=aws)
+        S.sparge_mask_select(q, ws, wl.block_q, wl.block_k, k_frac, p_mass, wl.scale,
+                             out=(bits, idx, cnt))
+        cur.wait_stream(side)
+        S.sparge_attn_fwd_packed(q, k, idx, cnt, aws, wl.block_q, wl.block_k, wl.scale, out=o)
+
+    step()
+    torch.cuda.synchronize()
+    ref = (bits.clone(), cnt.clone(), o.clone())
+    bits1, idx1, cnt1 = S.sparge_mask_predict(q, k, wl.block_q, wl.block_k, k_frac, p_mass, wl.scale)
+    o1 = S.sparge_attn_fwd(q, k, v, idx1, cnt1, wl.block_q, wl.block_k, wl.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(bits1, ref[0]) and torch.equal(cnt1, ref[1]) and torch.equal(o1, ref[2])
+
+    graph, cs = torch.cuda.CUDAGraph(), torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        step()
+    torch.cuda.current_stream().wait_stream(cs)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=cs):
+        step()
+    for _ in range(3):
+        for t in (bits, cnt, o):
+            t.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(bits, ref[0]) and torch.equal(cnt, ref[1]) and torch.equal(o, ref[2])
+        step()  # eager work between the replays
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref[2])
+    del graph
