@@ -35,6 +35,11 @@
  *  - Calls are thread-safe; the library keeps no state besides the
  *    per-thread error message and, per device, whether the LDS limit of the
  *    widest mask-selection kernel has been raised (done once, on first use).
+ *  - A call enqueues kernel launches only: no allocation, no memset, no copy
+ *    and no synchronisation, so a sequence of calls may be captured into a
+ *    HIP graph and replayed. Make one mask call on the device before a
+ *    capture, so that the one-time attribute change above is not made while
+ *    capturing. A replay reads and writes the buffers given at capture.
  */
 #ifndef SPARGE_H
 #define SPARGE_H
