@@ -669,3 +669,46 @@ def test_step_graph_replays_match_eager(k_frac, p_mass):
         torch.cuda.synchronize()
         assert torch.equal(o, ref[2])
     del graph
+
+
+@pytest.mark.parametrize("name", ["tiny", "wan1.3b"])
+def test_one_call_entry_points_replay_from_a_graph(name):
+    """The one-call mask, the forward with lse, its backward and the low-bit
+    forward captured together in a HIP graph (outputs allocated in the
+    graph's pool): every replay, with eager calls and synchronizations in
+    between, reproduces the eager results exactly (the kernels clear their
+    own counters with fill kernels and add no floating-point atomics)."""
+    wl, Q, K, V, q, k, v = workload_tensors(name)
+    d_o = torch.randn(q.shape, generator=torch.Generator().manual_seed(7)).to(q.device,
+                                                                              torch.bfloat16)
+
+    def calls():
+        bits, idx, cnt = S.sparge_mask_predict(q, k, wl.block_q, wl.block_k, wl.k_frac,
+                                               wl.p_mass, wl.scale)
+        o, lse = S.sparge_attn_fwd_lse(q, k, v, idx, cnt, wl.block_q, wl.block_k, wl.scale)
+        dq, dk, dv = S.sparge_attn_bwd(q, k, v, o, d_o, lse, idx, cnt, wl.block_q, wl.block_k,
+                                       wl.scale)
+        ol = S.sparge_attn_fwd_lowbit(q, k, v, idx, cnt, wl.block_q, wl.block_k, wl.scale)
+        return bits, cnt, o, lse, dq, dk, dv, ol
+
+    ref = [t.clone() for t in calls()]
+    torch.cuda.synchronize()
+    graph, cs = torch.cuda.CUDAGraph(), torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        calls()
+    torch.cuda.current_stream().wait_stream(cs)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=cs):
+        outs = calls()
+    names = ("bits", "cnt", "o", "lse", "dq", "dk", "dv", "o_lowbit")
+    for _ in range(3):
+        for t in outs:
+            t.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        for n, a, b in zip(names, outs, ref):
+            assert torch.equal(a, b), n
+        calls()  # eager work between the replays
+        torch.cuda.synchronize()
+    del graph
