@@ -812,3 +812,157 @@ def test_svg2_keeping_everything_is_dense_attention():
     assert sel.kept[:, np.bincount(ka, minlength=7) > 0].all()
     P = O.row_softmax(0.3 * (q @ k.T))
     np.testing.assert_allclose(o, P @ v, atol=1e-13)
+
+
+# --------------------------------------- pins that planted mistakes must fail
+# Each check below is run on the oracle function and on copies of it with a
+# plausible mistake planted in the source (tests/mutants.py); every copy must
+# fail the check.
+from mutants import mutant  # noqa: E402
+
+
+def _topp_margin_rows(select):
+    """Hand rows where the Top-p half of the near-tie margin decides it
+    (SpargeAttention2 page, section 1: Top-p keeps blocks until the
+    cumulative probability reaches p). Logits ln P give softmax P exactly
+    (the P sum to 1). Sorted P = (0.4, 0.3, 0.2, 0.1): C = (0, .4, .7, .9, 1)."""
+    P4 = np.log(np.array([[0.1, 0.4, 0.2, 0.3]]))       # order: blocks 1, 3, 2, 0
+    p32 = lambda p: float(np.float32(p))                # the ABI takes p as float32
+    rank = math.log(0.3 / 0.2)                          # s_(1) - s_(2)
+    # (a) m_p = 2 > K_k = 1; the upper gap C_2 - p = 0.01 is the smaller one
+    sel = select(P4, 0.25, 0.69)
+    assert sel.count[0] == 2 and sel.m_p[0] == 2
+    assert abs(sel.margin[0] - (0.7 - p32(0.69))) < 1e-12
+    # (b) same row, p = 0.41: the lower gap p - C_1 = 0.01 is the smaller one
+    sel = select(P4, 0.25, 0.41)
+    assert sel.count[0] == 2 and abs(sel.margin[0] - (p32(0.41) - 0.4)) < 1e-12
+    # (c) m_p = K_k = 2: count is set by both; the Top-p gap 0.02 < rank gap 0.405
+    sel = select(P4, 0.5, 0.68)
+    assert sel.count[0] == 2 and abs(sel.margin[0] - (0.7 - p32(0.68))) < 1e-12
+    assert rank > 0.4
+    # (d) every block kept by Top-p (m_p = n_k): no rank gap, only C_3 = 0.9 vs p
+    sel = select(P4, 0.25, 0.92)
+    assert sel.count[0] == 4 and abs(sel.margin[0] - (p32(0.92) - 0.9)) < 1e-12
+    # (e) Top-k decides (m_p = 1 < K_k = 2): the Top-p gap does not enter
+    P3 = np.log(np.array([[0.3, 0.6, 0.1]]))
+    sel = select(P3, 0.5, 0.59)
+    assert sel.m_p[0] == 1 and sel.count[0] == 2
+    assert abs(sel.margin[0] - math.log(3.0)) < 1e-12
+
+
+def test_topp_margin_hand_rows():
+    _topp_margin_rows(O.hybrid_select)
+
+
+@pytest.mark.parametrize("old,new", [
+    ("C[r, m_p[r]] - p", "C[r, m_p[r] + 1] - p"),          # upper gap one too far
+    ("p - C[r, m_p[r] - 1]", "p - C[r, m_p[r] - 2]"),      # lower gap one too far
+    ("p - C[r, m_p[r] - 1]", "p - C[r, m_p[r]]"),          # lower gap at C_mp
+    ("(m_p >= K_k) & (m_p >= 1)", "(m_p > K_k) & (m_p >= 1)"),  # m_p = K_k left out
+    ("(m_p >= K_k) & (m_p >= 1)", "(m_p >= 1)"),           # also when Top-k decides
+])
+def test_topp_margin_pin_catches_planted_mistakes(old, new):
+    with pytest.raises((AssertionError, IndexError)):
+        _topp_margin_rows(mutant(O.hybrid_select, old, new))
+
+
+def _svg2_groups_case():
+    """Queries in two groups and keys in three, far apart and scattered over
+    the sequence (the rows floor(c N / C) that seed k-means sit one in each
+    group). Key groups point along e0, e1, e2; query group 0 along e0, group 1
+    along e1 + e2. With scale 0.5 the centroid scores give query group 0 a
+    probability > 0.999 on key group 0 alone, and query group 1 about half on
+    each of key groups 1 and 2, so p = 0.9 keeps {0} for group 0 and {1, 2}
+    for group 1."""
+    rng = np.random.default_rng(94)
+    N, d = 120, 8
+    tq = rng.integers(0, 2, N)
+    tq[[0, 60]] = [0, 1]
+    tk = rng.integers(0, 3, N)
+    tk[[0, 40, 80]] = [0, 1, 2]
+    e = np.eye(d)
+    qdir = np.stack([3.0 * e[0], 2.0 * (e[1] + e[2])])
+    kdir = 6.0 * e[:3]
+    q = qdir[tq] + 0.01 * rng.standard_normal((N, d))
+    k = kdir[tk] + 0.01 * rng.standard_normal((N, d))
+    v = rng.standard_normal((N, d))
+    allowed = np.array([[True, False, False], [False, True, True]])
+    return q, k, v, allowed[tq][:, tk]
+
+
+def _svg2_token_mask(attn):
+    """"Sparse VideoGen2" page, section 2B: a query attends only to the tokens
+    of the key clusters its cluster kept. Expected: torch's CPU scaled-dot-
+    product attention in float64 over exactly the tokens of the kept groups."""
+    q, k, v, mask = _svg2_groups_case()
+    o, qa, ka, sel = attn(q, k, v, 2, 3, 3, 0.5, 0.9)
+    assert 0 < mask.mean() < 1
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(k)[None], torch.from_numpy(v)[None],
+        attn_mask=torch.from_numpy(mask)[None], scale=0.5)[0].numpy()
+    np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
+
+
+def test_svg2_partial_selection_attends_to_exactly_the_kept_tokens():
+    _svg2_token_mask(O.svg2_attention_head)
+
+
+@pytest.mark.parametrize("old,new", [
+    ("mask = sel.kept[qa[rows]][:, ka]", "mask = np.ones((len(rows), k.shape[0]), bool)"),
+    ("mask = sel.kept[qa[rows]][:, ka]", "mask = sel.kept[qa[rows]][:, ka[::-1]]"),
+    ("ka, ck = kmeans(k,", "ka, ck = kmeans(q,"),
+    ("sel, _ = svg2_select(cq, ck, sizes, scale, p_mass)",
+     "sel, _ = svg2_select(cq, ck, sizes, scale, 1.0)"),
+])
+def test_svg2_token_mask_pin_catches_planted_mistakes(old, new):
+    with pytest.raises((AssertionError, IndexError)):
+        _svg2_token_mask(mutant(O.svg2_attention_head, old, new))
+
+
+def _lowbit_p_codes(attn):
+    """SLA2 page, section 2C: P is quantised in the forward pass. One query
+    row (all four rows equal, so every INT8 code of Q is 127) against three key
+    blocks of two keys, visited in list order, d = 1, scale 1. Key values
+    [A, 0], [B, 0], [C, 0] give INT8 codes [127, 0] per block, so the scores are
+    A, 0, B, 0, C, 0 (to the float32 rounding of the block scales). With
+    A = ln(1/0.3), B = A + ln 5, C = B - ln 2 and the exact running maximum:
+      block 0: m = A, p = (1, 0.3): 448 p = (448, 134.4) -> e4m3 (448, 128);
+      block 1: m = B, the sums so far scale by e^(A-B) = 0.2, p = (1, 0.06):
+               448 p = (448, 26.88) -> (448, 26);
+      block 2: m stays B, p = (0.5, 0.06) -> (224, 26).
+    V = (1, 0.5 | 0.25, 0.125 | -0.5, 0.25): amax 1, so 448 v is an exact code
+    and the dequantised V equals v (to the float32 scale's 2^-24)."""
+    A = -math.log(0.3)
+    B = A + math.log(5.0)
+    C = B - math.log(2.0)
+    q = np.ones((6, 1))
+    k = np.array([[A], [0.0], [B], [0.0], [C], [0.0]])
+    v = np.array([[1.0], [0.5], [0.25], [0.125], [-0.5], [0.25]])
+    idx = np.array([[0, 1, 2]])
+    o = attn(q, k, v, idx, np.array([3]), 6, 2, 1.0)
+    w = [[1.0, 128 / 448], [1.0, 26 / 448], [224 / 448, 26 / 448]]   # decoded codes
+    num = 0.2 * (w[0][0] * 1.0 + w[0][1] * 0.5) + (w[1][0] * 0.25 + w[1][1] * 0.125) \
+        + (w[2][0] * -0.5 + w[2][1] * 0.25)
+    den = 0.2 * sum(w[0]) + sum(w[1]) + sum(w[2])
+    np.testing.assert_allclose(o, np.full((6, 1), num / den), rtol=2e-6, atol=0)
+
+
+def test_lowbit_p_codes_hand_example():
+    _lowbit_p_codes(O.lowbit_attention_head)
+
+
+@pytest.mark.parametrize("edits", [
+    ("l += p8.sum(axis=1)", "l += p.sum(axis=1)"),                # unquantised normaliser
+    # lagged maximum: p against the maximum before this block (the block's own
+    # maximum for the first), clipped to 1 so that every code stays in range
+    ("            m = m_new\n", "            m_old = np.where(np.isneginf(m), m_new, m)\n"
+     "            m = m_new\n",
+     "- m[:, None]))", "- m_old[:, None]))\n            p = np.minimum(p, 1.0)"),
+    ("- m[:, None]))", "- s.max(axis=1, keepdims=True).astype(np.float64)))"),  # block max
+    ("e4m3_round((p * E4M3_MAX).astype(np.float32)) / E4M3_MAX",
+     "e4m3_round(p.astype(np.float32))"),                          # codes of p, not 448 p
+    ("            acc *= f[:, None]\n", ""),                        # no rescale of O
+])
+def test_lowbit_pin_catches_planted_mistakes(edits):
+    with pytest.raises(AssertionError):
+        _lowbit_p_codes(mutant(O.lowbit_attention_head, *edits))
