@@ -170,8 +170,12 @@ def _mask_outputs(q, block_q, block_k, out, return_logits):
     else:
         bits, idx, cnt = (_buf(t, name, torch.int32, sh, q.device)
                           for t, name, sh in zip(out, ("mask_bits", "kv_idx", "kv_cnt"), shapes))
-    logits = (torch.empty((B, H, n_q, n_k), dtype=torch.float64, device=q.device)
-              if return_logits else None)
+    logits = None
+    if return_logits:
+        if out is not None and len(out) > 3:   # the caller's float64 score buffer
+            logits = _buf(out[3], "block_logits", torch.float64, (B, H, n_q, n_k), q.device)
+        else:
+            logits = torch.empty((B, H, n_q, n_k), dtype=torch.float64, device=q.device)
     return bits, idx, cnt, logits
 
 
@@ -181,6 +185,7 @@ def sparge_mask_predict(q, k, block_q=128, block_k=64, k_frac=0.05, p_mass=0.9, 
 
     Returns (mask_bits int32-viewed uint32 [B,H,n_q,ceil(n_k/32)], kv_idx int32
     [B,H,n_q,n_k], kv_cnt int32 [B,H,n_q][, logits float64 [B,H,n_q,n_k]]).
+    `out` may name the tensors to write: (bits, idx, cnt[, logits]).
     """
     B, H, N, d = _qkv(q, k)
     bits, idx, cnt, logits = _mask_outputs(q, block_q, block_k, out, return_logits)

@@ -539,24 +539,37 @@ hipError_t launch_select_reg(const MaskLaunch& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// one row per workgroup; the kernel's dynamic-LDS limit is raised once per
-// instantiation and device (the 4096-entry rows need 73 KiB)
+// one row per workgroup. The dynamic-LDS limit of every instantiation (the
+// 4096-entry rows need 73 KiB) is raised together, once per device, on the
+// first mask call of any width, so that a later call of another width makes
+// no attribute change (which could otherwise fall inside a graph capture)
 constexpr int kMaxDevices = 64;
 
 template <int NPAD>
-hipError_t launch_select(const MaskLaunch& a, hipStream_t st) {
-  static std::once_flag lds_once[kMaxDevices];
-  static hipError_t lds_err[kMaxDevices];
+hipError_t raise_select_lds() {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&hybrid_select_kernel<NPAD>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)select_lds_bytes(NPAD));
+}
+
+hipError_t select_lds_ready() {
+  static std::once_flag once[kMaxDevices];
+  static hipError_t err[kMaxDevices];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  std::call_once(lds_once[dev], [dev] {
-    lds_err[dev] = hipFuncSetAttribute(reinterpret_cast<const void*>(&hybrid_select_kernel<NPAD>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)select_lds_bytes(NPAD));
+  std::call_once(once[dev], [dev] {
+    hipError_t r = raise_select_lds<1024>();
+    if (r == hipSuccess) r = raise_select_lds<2048>();
+    if (r == hipSuccess) r = raise_select_lds<4096>();
+    err[dev] = r;
   });
-  if (lds_err[dev] != hipSuccess) return lds_err[dev];
+  return err[dev];
+}
+
+template <int NPAD>
+hipError_t launch_select(const MaskLaunch& a, hipStream_t st) {
   const int rows = a.B * a.H * a.n_q;
   hipLaunchKernelGGL(hybrid_select_kernel<NPAD>, dim3(rows), dim3(select_threads(NPAD)),
                      select_lds_bytes(NPAD), st, a.logits, rows, a.n_k, a.words, a.K_k,
@@ -581,6 +594,8 @@ hipError_t launch_scores_f64(const double* x, const double* y, double* out, int 
 constexpr int kRegSelectMinRows = 1024;
 
 hipError_t launch_select_rows(const MaskLaunch& a, hipStream_t st) {
+  hipError_t e = select_lds_ready();
+  if (e != hipSuccess) return e;
   switch (a.npad) {
     case 64: return launch_select_reg<64>(a, st);
     case 128: return launch_select_reg<128>(a, st);

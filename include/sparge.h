@@ -33,13 +33,17 @@
  *    nothing is launched and sparge_last_error() says why. A failed launch
  *    returns SPARGE_ERR_HIP. No call throws.
  *  - Calls are thread-safe; the library keeps no state besides the
- *    per-thread error message and, per device, whether the LDS limit of the
- *    widest mask-selection kernel has been raised (done once, on first use).
+ *    per-thread error message and, per device, whether the dynamic-LDS
+ *    limits of the mask-selection kernels have been raised: the first call
+ *    on a device that selects a mask (sparge_mask_predict, _select,
+ *    _predict_routed, svg2_attn_fwd), whatever its shape, raises them for
+ *    every row width at once.
  *  - A call enqueues kernel launches only: no allocation, no memset, no copy
  *    and no synchronisation, so a sequence of calls may be captured into a
- *    HIP graph and replayed. Make one mask call on the device before a
- *    capture, so that the one-time attribute change above is not made while
- *    capturing. A replay reads and writes the buffers given at capture.
+ *    HIP graph and replayed. Make one mask-selecting call (any shape) on the
+ *    device before a capture, so that the one-time attribute change above
+ *    is not made while capturing. A replay reads and writes the buffers
+ *    given at capture.
  */
 #ifndef SPARGE_H
 #define SPARGE_H
@@ -222,7 +226,9 @@ size_t sparge_attn_bwd_workspace_bytes(int B, int H, int N, int d, int block_q, 
  * 16-bit operands with float32 accumulation: bf16 (P and dS rounded to
  * bf16), except dQ = scale dS K, which takes dS and K as fp16 (a row's dS
  * sums to zero, so dQ cancels where the kept keys are alike, and fp16 keeps
- * three more bits; K must lie within fp16's range, |K| <= 65504); dQ, dK, dV
+ * three more bits; K must lie within fp16's range, |K| <= 65504, a larger
+ * value giving an infinite dQ, and values under 2^-14 keep fewer bits as fp16
+ * subnormals); dQ, dK, dV
  * are rounded to bf16. The same kv_idx / kv_cnt as the forward (any
  * order; a block listed twice counts twice); keys in no list get dK = dV = 0,
  * rows with an empty list dQ = 0. Deterministic: no atomics on the results.
@@ -353,8 +359,11 @@ size_t svg2_attn_workspace_bytes(int B, int H, int N, int d, int block_q, int n_
  *     original sequence under that token-level mask.
  * q, k, v, o: bf16 [B, H, N, d], device, 16-byte aligned; block_q (64 or 128)
  * is the query tile of the attention step; at most 4096 key clusters. The
- * workspace (256-byte aligned) holds every intermediate, including float64
- * distances of N x max(C) per (b, h). */
+ * workspace (256-byte aligned) holds every intermediate: the float64 copies
+ * of Q and K the clustering reads, the centroids, assignments, counting-sort
+ * counts and permutations, the centroid scores and selection, and Q, K, V and
+ * the packed V^T gathered into cluster-contiguous, tile-padded order
+ * (svg2_attn_workspace_bytes gives the total). */
 int svg2_attn_fwd(const void* q, const void* k, const void* v, int B, int H, int N, int d,
                   int block_q, int n_q_clusters, int n_k_clusters, int iters, float p_mass,
                   float scale, void* o, void* workspace, size_t workspace_bytes, void* stream);

@@ -15,7 +15,7 @@ import torch
 from block_sparse_attention_softmax_amd import binding as S
 from block_sparse_attention_softmax_amd.workloads import WORKLOADS, f64_to_bf16_bits, generate
 from oracle import sparge_oracle as O
-from parity import (DQ_CHAIN_MAX_REL, DQ_CHAIN_MEAN_REL, compare_grads, gpu_bits_to_bool,
+from parity import (assert_all_written, nan_like, DQ_CHAIN_MAX_REL, DQ_CHAIN_MEAN_REL, compare_grads, gpu_bits_to_bool,
                     to_gpu)
 
 pytestmark = pytest.mark.gpu
@@ -211,10 +211,13 @@ def test_forward_then_backward_on_workload_sampled():
     """The GPU forward then the backward at the 95% point, against the exact
     gradient; dQ within its conditioning bound (see parity.py)."""
     wl, rng, Q, K, V, dO, q, k, v, do, idx, cnt, kept = _workload(0.05)
-    o, lse = S.sparge_attn_fwd_lse(q, k, v, idx, cnt, wl.block_q, wl.block_k, wl.scale)
+    lse0 = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device=q.device)
+    o, lse = S.sparge_attn_fwd_lse(q, k, v, idx, cnt, wl.block_q, wl.block_k, wl.scale,
+                                   out=(nan_like(q), lse0))
     dq, dk, dv = S.sparge_attn_bwd(q, k, v, o, do, lse, idx, cnt, wl.block_q, wl.block_k,
-                                   wl.scale)
+                                   wl.scale, out=tuple(nan_like(q) for _ in range(3)))
     torch.cuda.synchronize()
+    assert_all_written(o, lse, dq, dk, dv)   # every head, row and key
     got = [_np(t) for t in (dq, dk, dv)]
     for h, qb, kb in _samples(wl, rng):
         ref = O.masked_attention_backward_sampled(_f(Q, 0, h), _f(K, 0, h), _f(V, 0, h),

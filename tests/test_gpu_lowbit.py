@@ -9,7 +9,7 @@ import torch
 from block_sparse_attention_softmax_amd import binding as S
 from block_sparse_attention_softmax_amd.workloads import WORKLOADS, f64_to_bf16_bits, generate
 from oracle import sparge_oracle as O
-from parity import compare_outputs, gpu_bits_to_bool, to_gpu
+from parity import assert_all_written, compare_outputs, gpu_bits_to_bool, nan_like, to_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -62,15 +62,17 @@ def test_lowbit_on_workload_sampled(k_frac, p_mass):
     q, k, v = to_gpu(Q), to_gpu(K), to_gpu(V)
     bits, idx, cnt = S.sparge_mask_predict(q, k, wl.block_q, wl.block_k, k_frac, p_mass,
                                            wl.scale)
-    o = S.sparge_attn_fwd_lowbit(q, k, v, idx, cnt, wl.block_q, wl.block_k, wl.scale)
+    o = S.sparge_attn_fwd_lowbit(q, k, v, idx, cnt, wl.block_q, wl.block_k, wl.scale,
+                                 out=nan_like(q))
     o16 = S.sparge_attn_fwd(q, k, v, idx, cnt, wl.block_q, wl.block_k, wl.scale)
     torch.cuda.synchronize()
+    assert_all_written(o)
     got, got16 = _np(o), _np(o16)
     idx_np, cnt_np = idx.cpu().numpy(), cnt.cpu().numpy()
     rng = np.random.default_rng(7)
     print(f"\n[lowbit workload] k={k_frac} p={p_mass}: |lowbit - bf16| max "
           f"{np.abs(got - got16).max():.2e} mean {np.abs(got - got16).mean():.2e}", flush=True)
-    for h in rng.choice(wl.H, size=2, replace=False):
+    for h in rng.choice(wl.H, size=4, replace=False):
         blocks = sorted({0, wl.n_q - 1, *rng.choice(wl.n_q, 4, replace=False)})
         ref = O.lowbit_attention_head(_f(Q, 0, h), _f(K, 0, h), _f(V, 0, h), idx_np[0, h],
                                       cnt_np[0, h], wl.block_q, wl.block_k, wl.scale,

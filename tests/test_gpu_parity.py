@@ -1,11 +1,13 @@
 """GPU parity: the HIP path through the C ABI against the CPU oracle.
 
-Masks are compared bit for bit outside near-tie rows (see parity.py);
-outputs within max-abs 2e-2 and mean-abs 2e-3 of the float64 oracle. Small
-shapes are compared in full (several tiles and a ragged tail in both the
-query and the key direction); the full-size workloads compare every mask row
-and a seeded sample of query blocks of the output, in the launch
-configuration the benchmark times.
+Masks are compared bit for bit on every row, near-tie rows included (see
+parity.py); outputs within max-abs 2e-2 and mean-abs 2e-3 of the float64
+oracle. Small shapes are compared in full (several tiles and a ragged tail in
+both the query and the key direction); the full-size workloads compare every
+mask row and a seeded sample of query blocks of the output (heads from every
+group of the workload), in the launch configuration the benchmark times, and
+check that every element of every head's output was written (outputs are
+pre-filled with NaN).
 """
 import numpy as np
 import pytest
@@ -14,8 +16,8 @@ import torch
 from block_sparse_attention_softmax_amd import binding as S
 from block_sparse_attention_softmax_amd.workloads import WORKLOADS, generate
 from oracle import sparge_oracle as O
-from parity import (check_index_list, compare_masks, compare_outputs, gpu_bits_to_bool,
-                    to_gpu)
+from parity import (assert_all_written, check_bit_padding, check_index_list, compare_masks,
+                    compare_outputs, gpu_bits_to_bool, nan_like, sentinel_mask_outputs, to_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -34,10 +36,12 @@ def workload_tensors(name):
 def run_mask(wl, q, k, k_frac=None, p_mass=None):
     k_frac = wl.k_frac if k_frac is None else k_frac
     p_mass = wl.p_mass if p_mass is None else p_mass
+    out = sentinel_mask_outputs(wl.B, wl.H, wl.n_q, wl.n_k, q.device)
     bits, idx, cnt, logits = S.sparge_mask_predict(q, k, wl.block_q, wl.block_k, k_frac, p_mass,
-                                                   wl.scale, return_logits=True)
+                                                   wl.scale, return_logits=True, out=out)
     torch.cuda.synchronize()
     n_k = wl.n_k
+    check_bit_padding(bits, n_k)
     kept = gpu_bits_to_bool(bits, n_k)
     idx_np, cnt_np = idx.cpu().numpy(), cnt.cpu().numpy()
     check_index_list(kept, idx_np, cnt_np)
@@ -75,10 +79,12 @@ def test_mask_matches_oracle_across_sort_widths(B, H, N, d, bq, k_frac, p_mass):
     Q, K = (f64_to_bf16_bits(rng.standard_normal((B, H, N, d)) + 3 * trend) for _ in range(2))
     scale = S.default_scale(d)
     print(f"\n[mask] B={B} H={H} N={N} d={d} bq={bq} k={k_frac} p={p_mass}", flush=True)
-    bits, idx, cnt, logits = S.sparge_mask_predict(to_gpu(Q), to_gpu(K), bq, 64, k_frac, p_mass,
-                                                   scale, return_logits=True)
-    torch.cuda.synchronize()
     n_k = -(-N // 64)
+    out = sentinel_mask_outputs(B, H, -(-N // bq), n_k, "cuda")
+    bits, idx, cnt, logits = S.sparge_mask_predict(to_gpu(Q), to_gpu(K), bq, 64, k_frac, p_mass,
+                                                   scale, return_logits=True, out=out)
+    torch.cuda.synchronize()
+    check_bit_padding(bits, n_k)
     kept = gpu_bits_to_bool(bits, n_k)
     check_index_list(kept, idx.cpu().numpy(), cnt.cpu().numpy())
     m = O.predict_mask(Q, K, bq, 64, k_frac, p_mass, scale)
@@ -123,8 +129,10 @@ def test_routed_mask_matches_oracle(name, k_frac, p_mass):
     wq, wk = router_weights(wl.H, wl.d, 77)
     bits, idx, cnt, logits = S.sparge_mask_predict_routed(
         q, k, torch.from_numpy(wq).cuda(), torch.from_numpy(wk).cuda(), wl.block_q, wl.block_k,
-        k_frac, p_mass, wl.scale, return_logits=True)
+        k_frac, p_mass, wl.scale, return_logits=True,
+        out=sentinel_mask_outputs(wl.B, wl.H, wl.n_q, wl.n_k, q.device))
     torch.cuda.synchronize()
+    check_bit_padding(bits, wl.n_k)
     kept = gpu_bits_to_bool(bits, wl.n_k)
     check_index_list(kept, idx.cpu().numpy(), cnt.cpu().numpy())
     m = O.predict_mask_routed(Q, K, wq, wk, wl.block_q, wl.block_k, k_frac, p_mass, wl.scale)
@@ -192,10 +200,13 @@ def test_mask_and_attention_at_tiny_lengths(N, d, bq, k_frac, p_mass):
     Q, K, V = (f64_to_bf16_bits(rng.standard_normal((B, H, N, d))) for _ in range(3))
     scale = S.default_scale(d)
     q, k, v = to_gpu(Q), to_gpu(K), to_gpu(V)
-    bits, idx, cnt = S.sparge_mask_predict(q, k, bq, 64, k_frac, p_mass, scale)
-    o = S.sparge_attn_fwd(q, k, v, idx, cnt, bq, 64, scale)
-    torch.cuda.synchronize()
     n_k = -(-N // 64)
+    out = sentinel_mask_outputs(B, H, -(-N // bq), n_k, q.device)[:3]
+    bits, idx, cnt = S.sparge_mask_predict(q, k, bq, 64, k_frac, p_mass, scale, out=out)
+    o = S.sparge_attn_fwd(q, k, v, idx, cnt, bq, 64, scale, out=nan_like(q))
+    torch.cuda.synchronize()
+    assert_all_written(o)
+    check_bit_padding(bits, n_k)
     kept = gpu_bits_to_bool(bits, n_k)
     check_index_list(kept, idx.cpu().numpy(), cnt.cpu().numpy())
     m = O.predict_mask(Q, K, bq, 64, k_frac, p_mass, scale)
@@ -231,20 +242,32 @@ def test_attention_is_deterministic():
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
 
 
-@pytest.mark.parametrize("name,samples", [("tiny", None), ("wan1.3b", 6), ("wan1.3b_s95", 6),
-                                          ("wan14b_720p", 4)])
+def sample_heads(name, H, rng, n=4):
+    """Heads to compare on a workload: wan1.3b_s95 takes half from its
+    near-uniform heads (0-5) and half from its sink heads (6-11)."""
+    if name == "wan1.3b_s95":
+        half = H // 2
+        return sorted([*rng.choice(half, n // 2, replace=False),
+                       *(half + rng.choice(H - half, n - n // 2, replace=False))])
+    return sorted(rng.choice(H, size=min(n, H), replace=False))
+
+
+@pytest.mark.parametrize("name,samples", [("tiny", None), ("wan1.3b", 8), ("wan1.3b_s95", 8),
+                                          ("wan14b_720p", 6)])
 def test_attention_matches_oracle_on_workloads(name, samples):
-    """Mask and attention as the benchmark runs them; the oracle uses the GPU's mask."""
+    """Mask and attention as the benchmark runs them; the oracle uses the GPU's mask.
+    Every element of every head is checked to have been written."""
     wl, Q, K, V, q, k, v = workload_tensors(name)
     print(f"\n[attn] {name}", flush=True)
     bits, idx, cnt = S.sparge_mask_predict(q, k, wl.block_q, wl.block_k, wl.k_frac, wl.p_mass)
-    o = S.sparge_attn_fwd(q, k, v, idx, cnt, wl.block_q, wl.block_k)
+    o = S.sparge_attn_fwd(q, k, v, idx, cnt, wl.block_q, wl.block_k, out=nan_like(q))
     torch.cuda.synchronize()
+    assert_all_written(o)
     kept = gpu_bits_to_bool(bits, wl.n_k)
     got = O.bf16_to_f64(o.cpu().view(torch.uint16).numpy())
     rng = np.random.default_rng(2024)
     for b in range(wl.B):
-        heads = range(wl.H) if samples is None else rng.choice(wl.H, size=2, replace=False)
+        heads = range(wl.H) if samples is None else sample_heads(name, wl.H, rng)
         for h in heads:
             if samples is None:
                 blocks = None
@@ -265,13 +288,14 @@ def test_attention_matches_oracle_at_topk_operating_points(k_frac):
     wl, Q, K, V, q, k, v = workload_tensors("wan1.3b")
     bits, idx, cnt = S.sparge_mask_predict(q, k, wl.block_q, wl.block_k, k_frac, 0.0)
     ws = S.sparge_attn_pack(v)
-    o = S.sparge_attn_fwd_packed(q, k, idx, cnt, ws, wl.block_q, wl.block_k)
+    o = S.sparge_attn_fwd_packed(q, k, idx, cnt, ws, wl.block_q, wl.block_k, out=nan_like(q))
     torch.cuda.synchronize()
+    assert_all_written(o)
     kept = gpu_bits_to_bool(bits, wl.n_k)
     got = O.bf16_to_f64(o.cpu().view(torch.uint16).numpy())
     rng = np.random.default_rng(int(k_frac * 1000))
-    for h in rng.choice(wl.H, size=2, replace=False):
-        blocks = sorted({0, wl.n_q - 1, *rng.choice(wl.n_q, 4, replace=False)})
+    for h in sample_heads("wan1.3b", wl.H, rng):
+        blocks = sorted({0, wl.n_q - 1, *rng.choice(wl.n_q, 6, replace=False)})
         ref = O.masked_attention_head(O.bf16_to_f64(Q[0, h]), O.bf16_to_f64(K[0, h]),
                                       O.bf16_to_f64(V[0, h]), kept[0, h], wl.block_q,
                                       wl.block_k, wl.scale, q_blocks=blocks)
@@ -316,9 +340,11 @@ def test_attention_long_rows_sampled():
     kept[0, 0, n_q - 1] = False
     kept[0, 0, n_q - 1, n_k - 1] = True    # only the short last key block
     idx, cnt = O.kept_to_index_list(kept)
-    o = S.sparge_attn_fwd(to_gpu(Q), to_gpu(K), to_gpu(V), torch.from_numpy(idx).cuda(),
-                          torch.from_numpy(cnt).cuda(), bq, 64, None)
+    qg = to_gpu(Q)
+    o = S.sparge_attn_fwd(qg, to_gpu(K), to_gpu(V), torch.from_numpy(idx).cuda(),
+                          torch.from_numpy(cnt).cuda(), bq, 64, None, out=nan_like(qg))
     torch.cuda.synchronize()
+    assert_all_written(o)
     got = O.bf16_to_f64(o[0, 0].cpu().view(torch.uint16).numpy())
     blocks = sorted({0, 1, n_q // 2, n_q - 1})
     ref = O.masked_attention_head(O.bf16_to_f64(Q[0, 0]), O.bf16_to_f64(K[0, 0]),
@@ -391,12 +417,14 @@ def test_sparse_linear_matches_oracle_on_workload():
     wl, Q, K, V, q, k, v = workload_tensors("wan1.3b_linear")
     bits, idx, cnt = S.sparge_mask_predict(q, k, wl.block_q, wl.block_k, wl.k_frac, wl.p_mass)
     alpha = torch.full((wl.H,), wl.linear_alpha, dtype=torch.float32, device="cuda")
-    o = S.sparse_linear_attn_fwd(q, k, v, idx, cnt, alpha, wl.block_q, wl.block_k)
+    o = S.sparse_linear_attn_fwd(q, k, v, idx, cnt, alpha, wl.block_q, wl.block_k,
+                                 out=nan_like(q))
     torch.cuda.synchronize()
+    assert_all_written(o)
     kept = gpu_bits_to_bool(bits, wl.n_k)
     got = O.bf16_to_f64(o.cpu().view(torch.uint16).numpy())
     rng = np.random.default_rng(99)
-    for h in rng.choice(wl.H, size=3, replace=False):
+    for h in sample_heads("wan1.3b_linear", wl.H, rng):
         blocks = sorted({0, wl.n_q - 1, *rng.choice(wl.n_q, 4, replace=False)})
         ref = O.sparse_linear_attention_head(O.bf16_to_f64(Q[0, h]), O.bf16_to_f64(K[0, h]),
                                              O.bf16_to_f64(V[0, h]), kept[0, h], wl.block_q,
@@ -463,12 +491,13 @@ def test_sla2_mix_matches_oracle_on_workload():
     bits, idx, cnt = S.sparge_mask_predict(q, k, wl.block_q, wl.block_k, wl.k_frac, wl.p_mass)
     alpha = mix_alpha(wl.H, wl.d, 5)
     o = S.sla2_mix_attn_fwd(q, k, v, idx, cnt, torch.from_numpy(alpha).cuda(), wl.block_q,
-                            wl.block_k)
+                            wl.block_k, out=nan_like(q))
     torch.cuda.synchronize()
+    assert_all_written(o)
     kept = gpu_bits_to_bool(bits, wl.n_k)
     got = O.bf16_to_f64(o.cpu().view(torch.uint16).numpy())
     rng = np.random.default_rng(98)
-    for h in rng.choice(wl.H, size=3, replace=False):
+    for h in sample_heads("wan1.3b_linear", wl.H, rng):
         blocks = sorted({0, wl.n_q - 1, *rng.choice(wl.n_q, 4, replace=False)})
         ref = O.sla2_mix_attention_head(O.bf16_to_f64(Q[0, h]), O.bf16_to_f64(K[0, h]),
                                         O.bf16_to_f64(V[0, h]), kept[0, h], wl.block_q,
@@ -712,3 +741,45 @@ def test_one_call_entry_points_replay_from_a_graph(name):
         calls()  # eager work between the replays
         torch.cuda.synchronize()
     del graph
+
+
+_CAPTURE_SCRIPT = r"""
+import sys, torch
+sys.path.insert(0, {root!r})
+from block_sparse_attention_softmax_amd import binding as S
+g = torch.Generator().manual_seed(5)
+small = torch.randn(1, 2, 4000, 64, generator=g).to("cuda", torch.bfloat16)
+S.sparge_mask_predict(small, small, 128, 64, 0.1, 0.9)       # width 64: the register sort
+torch.cuda.synchronize()
+q, k = (torch.randn(1, 1, 100000, 64, generator=g).to("cuda", torch.bfloat16) for _ in range(2))
+ref = S.sparge_mask_predict(q, k, 128, 64, 0.02, 0.9)        # 782 rows of 1563: the LDS sort
+torch.cuda.synchronize()
+ref = [t.clone() for t in ref]
+out = [torch.empty_like(t) for t in ref]
+graph, cs = torch.cuda.CUDAGraph(), torch.cuda.Stream()
+with torch.cuda.graph(graph, stream=cs):
+    S.sparge_mask_predict(q, k, 128, 64, 0.02, 0.9, out=tuple(out))
+for _ in range(3):
+    for t in out:
+        t.zero_()
+    graph.replay()
+    torch.cuda.synchronize()
+    valid = torch.arange(ref[1].shape[-1], device="cuda") < ref[2].unsqueeze(-1)
+    assert torch.equal(out[0], ref[0]) and torch.equal(out[2], ref[2])
+    assert torch.equal(out[1][valid], ref[1][valid])
+print("capture ok")
+"""
+
+
+def test_lds_sort_mask_captured_after_a_narrow_call():
+    """In a fresh process, a mask call whose rows use the register sort comes
+    first; a mask call at a width that takes the LDS sort is then captured in a
+    HIP graph and replayed: the one-time LDS-limit change was already made for
+    every width, so nothing is set during the capture."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", _CAPTURE_SCRIPT.format(root=root)],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0 and "capture ok" in r.stdout, r.stdout[-2000:] + r.stderr[-2000:]

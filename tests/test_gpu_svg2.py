@@ -8,7 +8,7 @@ import torch
 from block_sparse_attention_softmax_amd import binding as S
 from block_sparse_attention_softmax_amd.workloads import WORKLOADS, f64_to_bf16_bits, generate
 from oracle import sparge_oracle as O
-from parity import compare_outputs, to_gpu
+from parity import assert_all_written, compare_outputs, nan_like, to_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -48,11 +48,13 @@ def test_svg2_on_workload_sampled():
     block's worth of tokens each), 3 rounds, p = 0.9: sampled rows of two heads."""
     wl = WORKLOADS["wan1.3b"]
     Q, K, V = generate(wl)
-    o = S.svg2_attn_fwd(to_gpu(Q), to_gpu(K), to_gpu(V), 256, 512, iters=3, p_mass=0.9)
+    q = to_gpu(Q)
+    o = S.svg2_attn_fwd(q, to_gpu(K), to_gpu(V), 256, 512, iters=3, p_mass=0.9, out=nan_like(q))
     torch.cuda.synchronize()
+    assert_all_written(o)
     got = _np(o)
     rng = np.random.default_rng(23)
-    for h in rng.choice(wl.H, size=2, replace=False):
+    for h in rng.choice(wl.H, size=3, replace=False):
         rows = np.sort(rng.choice(wl.N, 300, replace=False))
         ref, qa, ka, sel = O.svg2_attention_head(O.bf16_to_f64(Q[0, h]), O.bf16_to_f64(K[0, h]),
                                                  O.bf16_to_f64(V[0, h]), 256, 512, 3, wl.scale,
