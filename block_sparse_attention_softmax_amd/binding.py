@@ -27,7 +27,8 @@ EXPORTS = ("sparge_mask_workspace_bytes", "sparge_mask_predict", "sparge_mask_po
            "sla2_mix_attn_fwd", "sparge_attn_fwd_lse", "sparge_attn_bwd_workspace_bytes",
            "sparge_attn_bwd", "sparse_linear_bwd_workspace_bytes", "sparse_linear_attn_bwd",
            "sla2_mix_attn_bwd", "sparge_attn_lowbit_workspace_bytes", "sparge_attn_fwd_lowbit",
-           "svg2_attn_workspace_bytes", "svg2_attn_fwd", "sparge_last_error")
+           "svg2_attn_workspace_bytes", "svg2_attn_fwd", "sparge_mask_noalloc_scratch_bytes",
+           "sparge_mask_predict_noalloc", "sparge_last_error")
 
 _lib = None
 
@@ -52,6 +53,11 @@ def lib() -> ctypes.CDLL:
         L.sparge_mask_predict.argtypes = [vp, vp] + [c_int] * 6 + [c_float] * 3 + [vp] * 5 + [
             c_size, vp]
         L.sparge_mask_predict.restype = c_int
+        L.sparge_mask_noalloc_scratch_bytes.argtypes = []
+        L.sparge_mask_noalloc_scratch_bytes.restype = c_size
+        L.sparge_mask_predict_noalloc.argtypes = [vp, vp] + [c_int] * 6 + [c_float] * 3 + [
+            vp] * 5
+        L.sparge_mask_predict_noalloc.restype = c_int
         L.sparge_mask_pool.argtypes = [vp, vp] + [c_int] * 6 + [vp, c_size, vp]
         L.sparge_mask_pool.restype = c_int
         L.sparge_mask_select.argtypes = [c_int] * 6 + [c_float] * 3 + [vp] * 5 + [c_size, vp]
@@ -196,6 +202,22 @@ def sparge_mask_predict(q, k, block_q=128, block_k=64, k_frac=0.05, p_mass=0.9, 
     _check(lib().sparge_mask_predict(
         _ptr(q), _ptr(k), B, H, N, d, block_q, block_k, k_frac, p_mass, scale,
         _ptr(bits), _ptr(idx), _ptr(cnt), _ptr(logits), _ptr(workspace), ws_bytes, _stream(q)))
+    return (bits, idx, cnt, logits) if return_logits else (bits, idx, cnt)
+
+
+def sparge_mask_predict_noalloc(q, k, block_q=128, block_k=64, k_frac=0.05, p_mass=0.9,
+                                scale=None, return_logits=False, out=None):
+    """sparge_mask_predict through the entry point that takes no workspace (its
+    scratch is the library's per-GPU array); outputs as sparge_mask_predict.
+    With `out` given (and, for return_logits, its float64 score buffer) this
+    wrapper allocates nothing either."""
+    B, H, N, d = _qkv(q, k)
+    bits, idx, cnt, logits = _mask_outputs(q, block_q, block_k, out, return_logits)
+    if scale is None:
+        scale = default_scale(d)
+    _check(lib().sparge_mask_predict_noalloc(
+        _ptr(q), _ptr(k), B, H, N, d, block_q, block_k, k_frac, p_mass, scale,
+        _ptr(bits), _ptr(idx), _ptr(cnt), _ptr(logits), _stream(q)))
     return (bits, idx, cnt, logits) if return_logits else (bits, idx, cnt)
 
 

@@ -3,6 +3,7 @@
 #include <math.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 
 #include "../../include/sparge.h"
@@ -110,7 +111,8 @@ namespace {
 int mask_impl(const void* q, const void* k, const float* wq, const float* wk, int B, int H,
               int N, int d, int block_q, int block_k, float k_frac, float p_mass, float scale,
               uint32_t* mask_bits, int32_t* kv_idx, int32_t* kv_cnt, double* block_logits,
-              void* workspace, size_t workspace_bytes, void* stream, int phase = 0) {
+              void* workspace, size_t workspace_bytes, void* stream, int phase = 0,
+              bool launch = true) {
   int rc = check_shape(B, H, N, d, block_q, block_k);
   if (rc != SPARGE_OK) return rc;
   const int n_q = ceil_div(N, block_q), n_k = ceil_div(N, block_k);
@@ -136,9 +138,14 @@ int mask_impl(const void* q, const void* k, const float* wq, const float* wk, in
   const bool routed = wq != nullptr;
   if (routed && (!aligned(wq, 4) || !aligned(wk, 4)))
     return fail(SPARGE_ERR_INVALID_ARG, "w_q and w_k must be 4-byte aligned");
+  // scores written to the caller's block_logits need no room in the workspace
+  const size_t BH_ = (size_t)B * H;
+  const size_t score_bytes = (BH_ * n_q * n_k * sizeof(double) + 255) & ~(size_t)255;
   const size_t need = routed ? routed_mask_ws(B, H, N, d, block_q, block_k)
-                             : mask_ws(B, H, N, d, block_q, block_k);
+                      : (block_logits && selects) ? mask_ws(B, H, N, d, block_q, block_k) - score_bytes
+                                                  : mask_ws(B, H, N, d, block_q, block_k);
   if (workspace_bytes < need) return fail(SPARGE_ERR_INVALID_ARG, "workspace too small");
+  if (!launch) return SPARGE_OK;  // arguments checked only
 
   sparge::MaskLaunch a{};
   a.phase = phase;
@@ -228,6 +235,92 @@ int sparge_mask_predict_routed(const void* q, const void* k, const float* w_q, c
   if (!w_q || !w_k) return fail(SPARGE_ERR_INVALID_ARG, "null pointer argument");
   return mask_impl(q, k, w_q, w_k, B, H, N, d, block_q, block_k, k_frac, p_mass, scale,
                    mask_bits, kv_idx, kv_cnt, block_logits, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Mask prediction without a caller workspace. Its scratch (the pooled means
+// and, unless the caller takes them, the block scores) lives in one
+// file-scope device array per GPU, held from the library's first use on that
+// GPU until the process ends. In host code `scratch` is only a stand-in for
+// the symbol: its device address is looked up once per device with
+// hipGetSymbolAddress and only that address is handed to the kernels.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+
+std::once_flag g_scratch_once[kMaxScratchDevices];
+hipError_t g_scratch_err[kMaxScratchDevices];
+void* g_scratch_ptr[kMaxScratchDevices];
+
+// this device's address of `scratch` (nullptr and a message on failure)
+void* scratch_on_current_device(int* rc) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *rc = hip_fail(e, "hipGetDevice");
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxScratchDevices) {
+    *rc = fail(SPARGE_ERR_UNSUPPORTED, "device index above 63");
+    return nullptr;
+  }
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev]) {
+    *rc = hip_fail(g_scratch_err[dev] != hipSuccess ? g_scratch_err[dev] : hipErrorUnknown,
+                   "hipGetSymbolAddress(scratch)");
+    return nullptr;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" {
+
+size_t sparge_mask_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+int sparge_mask_predict_noalloc(const void* q, const void* k, int B, int H, int N, int d,
+                                int block_q, int block_k, float k_frac, float p_mass,
+                                float scale, uint32_t* mask_bits, int32_t* kv_idx,
+                                int32_t* kv_cnt, double* block_logits, void* stream) {
+  g_last_error.clear();
+  int rc = check_shape(B, H, N, d, block_q, block_k);
+  if (rc != SPARGE_OK) return rc;
+  if (ceil_div(N, block_k) > kMaxKeyBlocks)
+    return fail(SPARGE_ERR_UNSUPPORTED, "more than 4096 key blocks (N > 262144)");
+  // the means always, the scores only when the caller does not take them
+  const size_t BH = (size_t)B * H;
+  const size_t n_q = ceil_div(N, block_q), n_k = ceil_div(N, block_k);
+  const size_t need = block_logits ? mask_ws(B, H, N, d, block_q, block_k) -
+                                         ((BH * n_q * n_k * sizeof(double) + 255) & ~(size_t)255)
+                                   : mask_ws(B, H, N, d, block_q, block_k);
+  if (need > kNoAllocScratchBytes) {
+    char buf[200];
+    snprintf(buf, sizeof buf,
+             "this shape needs %zu bytes of scratch, more than the %zu bytes the "
+             "no-allocation mask call holds (pass block_logits, or use "
+             "sparge_mask_predict with a workspace)",
+             need, kNoAllocScratchBytes);
+    return fail(SPARGE_ERR_UNSUPPORTED, buf);
+  }
+  // every other argument is checked before any HIP call: a dry run against an
+  // aligned stand-in for the scratch address
+  rc = mask_impl(q, k, nullptr, nullptr, B, H, N, d, block_q, block_k, k_frac, p_mass, scale,
+                 mask_bits, kv_idx, kv_cnt, block_logits, reinterpret_cast<void*>(256),
+                 kNoAllocScratchBytes, stream, 0, false);
+  if (rc != SPARGE_OK) return rc;
+  void* ws = scratch_on_current_device(&rc);
+  if (!ws) return rc;
+  return mask_impl(q, k, nullptr, nullptr, B, H, N, d, block_q, block_k, k_frac, p_mass, scale,
+                   mask_bits, kv_idx, kv_cnt, block_logits, ws, kNoAllocScratchBytes, stream);
 }
 
 size_t sparge_attn_workspace_bytes(int B, int H, int N, int d) {

@@ -95,13 +95,38 @@ size_t sparge_mask_workspace_bytes(int B, int H, int N, int d, int block_q,
  *  block_logits: optional out float64 [B, H, n_q, n_k] (the scores s), or
  *                NULL. 8-byte aligned.
  *  workspace   : device scratch of at least sparge_mask_workspace_bytes(),
- *                16-byte aligned; contents on entry do not matter.
+ *                16-byte aligned; contents on entry do not matter. With
+ *                block_logits given, the scores go there and the workspace
+ *                needs only the pooled means (B*H*(n_q + n_k)*d*8 bytes, each
+ *                part rounded up to 256).
  */
 int sparge_mask_predict(const void* q, const void* k, int B, int H, int N, int d,
                         int block_q, int block_k, float k_frac, float p_mass,
                         float scale, uint32_t* mask_bits, int32_t* kv_idx,
                         int32_t* kv_cnt, double* block_logits, void* workspace,
                         size_t workspace_bytes, void* stream);
+
+/* sparge_mask_predict for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. It takes no workspace and allocates nothing (no hipMalloc,
+ * hipFree or allocating library call); its scratch (the float64 pooled means
+ * and, when block_logits is NULL, the float64 block scores) is one
+ * library-owned device array of sparge_mask_noalloc_scratch_bytes() (64 MiB)
+ * per GPU, held from the library's first use on that GPU until the process
+ * ends. Shapes whose scratch exceeds it are rejected with
+ * SPARGE_ERR_UNSUPPORTED before anything is enqueued (the Wan-1.3B shape
+ * needs 22 MB; passing block_logits leaves only the means, B*H*(n_q + n_k)*d*8
+ * bytes). Every call on a GPU shares that GPU's array, so calls that overlap
+ * on one GPU (other streams, other threads) race on it: order them on one
+ * stream or serialise them. Nothing in the array needs to start cleared.
+ * The first call on a device also looks up the array's address there.
+ * Arguments, outputs and results are those of sparge_mask_predict, bit for
+ * bit. */
+size_t sparge_mask_noalloc_scratch_bytes(void);
+int sparge_mask_predict_noalloc(const void* q, const void* k, int B, int H, int N, int d,
+                                int block_q, int block_k, float k_frac, float p_mass,
+                                float scale, uint32_t* mask_bits, int32_t* kv_idx,
+                                int32_t* kv_cnt, double* block_logits, void* stream);
 
 /* The two halves of sparge_mask_predict, for callers that run other work
  * beside the second: sparge_mask_pool writes the pooled queries and keys

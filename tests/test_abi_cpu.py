@@ -302,3 +302,40 @@ def test_svg2_workspace_and_rejections():
         bad = list(args)
         bad[i] = v
         assert L.svg2_attn_fwd(*bad) == code, (i, v)
+
+
+def _noalloc(**kw):
+    args = dict(q=A, k=A, B=1, H=2, N=1024, d=64, bq=64, bk=64, kf=0.1, p=0.9, sc=0.125,
+                bits=A, idx=A, cnt=A, logits=None, st=None)
+    args.update(kw)
+    return binding.lib().sparge_mask_predict_noalloc(*args.values())
+
+
+def test_noalloc_mask_checks_arguments_before_any_hip_call():
+    L = binding.lib()
+    assert L.sparge_mask_noalloc_scratch_bytes() == 64 << 20
+    for kw, code in [(dict(d=96), binding.ERR_UNSUPPORTED), (dict(kf=0.0), binding.ERR_INVALID_ARG),
+                     (dict(p=-1.0), binding.ERR_INVALID_ARG), (dict(q=None), binding.ERR_INVALID_ARG),
+                     (dict(bits=MIS), binding.ERR_INVALID_ARG),
+                     (dict(logits=MIS), binding.ERR_INVALID_ARG),
+                     (dict(N=64 * 4097), binding.ERR_UNSUPPORTED)]:
+        assert _noalloc(**kw) == code, kw
+    # beyond the 64 MiB scratch: Wan-14B-720p's scores alone are 224 MB, and its
+    # means 72.6 MB, so it is refused with or without block_logits
+    for logits in (None, A):
+        assert _noalloc(B=1, H=40, N=75600, d=128, bq=128, logits=logits) == binding.ERR_UNSUPPORTED
+        assert b"scratch" in L.sparge_last_error()
+    # Wan-1.3B needs 22 MB: it passes every check (a call here would reach HIP)
+    up = lambda x: (x + 255) // 256 * 256
+    need = up(12 * 256 * 128 * 8) + up(12 * 512 * 128 * 8) + up(12 * 256 * 512 * 8)
+    assert need < 64 << 20
+
+
+def test_mask_workspace_without_scores_when_block_logits_given():
+    """With block_logits the scores go to the caller's buffer: a workspace of
+    the pooled means alone is enough, and one byte less is refused."""
+    up = lambda x: (x + 255) // 256 * 256
+    means = up(2 * 16 * 64 * 8) + up(2 * 16 * 64 * 8)
+    assert _mask(wsb=means - 1, logits=A) == binding.ERR_INVALID_ARG
+    assert b"workspace" in binding.lib().sparge_last_error()
+    assert _mask(wsb=means + up(2 * 16 * 16 * 8) - 1) == binding.ERR_INVALID_ARG
