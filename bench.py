@@ -8,7 +8,10 @@ blocks. Inputs are resident in HBM before the timed region starts. The step
 time is the average over K steps replayed from a HIP graph of one step (every
 launch and stream join of the step, nothing skipped; --no-graph times them
 eagerly); the mask, pack and attention-kernel times come from an eager pass of
-the same K steps with HIP events around each part.
+the same K steps with HIP events around each part; the median, 10th and 90th
+percentile of the step come from the same steps timed one by one, and a "cold"
+pass times each step again after writing 512 MiB (more than the Infinity
+Cache holds) so that it starts from HBM.
 
 Default workload: the Wan2.1-1.3B-shaped grid (B=1, H=12, N=32760 =
 21x30x52, d=128, blocks 128x64, k=5%, p=0.9). `value` is dense-equivalent
@@ -18,8 +21,10 @@ the bf16 MFMA roofline at the kept-block count, the same path at the Top-k
 operating points of 90% and 95% block sparsity (p = 0, k = 10% / 5%), the
 backward, low-bit, sparse-linear, SLA2/SALAD and SVG2 variants on the same
 inputs, the forward at two more configurations (95% sparsity on mixed-range
-heads, and a Wan2.1-14B 720p grid: H=40, N=75600), and the CPU oracle timed on
-a bounded sample of the default workload.
+heads, and a Wan2.1-14B 720p grid: H=40, N=75600, and the tiny case), the
+measured MFMA and HBM ceilings, and the CPU oracle timed on a bounded sample
+of the default workload, followed (untimed) by the oracle's check of the
+benchmarked masks and of sampled output rows for every configuration.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -58,6 +63,33 @@ def measured_traffic():
         return None
 
 
+def dist(ms) -> dict:
+    """Median, 10th and 90th percentile of a list of times (ms)."""
+    a = np.asarray(ms, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 4), "p10": round(float(np.percentile(a, 10)), 4),
+            "p90": round(float(np.percentile(a, 90)), 4), "n": int(a.size)}
+
+
+def host_info() -> dict:
+    """The host the oracle runs on: core counts, CPU model, BLAS threads."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas = None
+    affinity = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None
+    return {"nproc": os.cpu_count(), "affinity_cpus": affinity, "cpu_model": model,
+            "blas_threads": blas}
+
+
 def kept_flops(cnt: np.ndarray, idx: np.ndarray, N: int, d: int, block_q: int,
                block_k: int) -> float:
     """Algorithmic FLOPs of the attention over the kept tiles: for every kept
@@ -82,11 +114,8 @@ def cpu_baseline(wl, Q, K, V, blocks: int):
     `blocks` query blocks have been attended."""
     from oracle import sparge_oracle as O
 
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+    host = host_info()
+    cores = host["blas_threads"] or host["affinity_cpus"] or host["nproc"] or 1
     t_mask = t_attn = 0.0
     rows = heads = done = 0
     for h in range(wl.H):
@@ -111,14 +140,109 @@ def cpu_baseline(wl, Q, K, V, blocks: int):
             "kind": "oracle",
             "sample": f"{wl.name} heads 0-{heads - 1}: mask of every query block of each head "
                       f"({t_mask:.2f} s) + attention of {done} query blocks ({t_attn:.2f} s), "
-                      f"float64 NumPy"}
+                      f"float64 NumPy",
+            "host": host, "mask_s": round(t_mask, 3), "attn_s": round(t_attn, 3)}
+
+
+def measure_ceilings(torch, dev) -> dict:
+    """The dense bf16 MFMA rate the probe kernel sustains (TFLOP/s; the better of
+    4 and 8 independent chains per wave) and the HBM bandwidth of a 1 GiB
+    device-to-device copy (GB/s, read + write bytes)."""
+    import ctypes
+    out = {"mfma_bf16_tflops": None, "hbm_copy_gbs": None}
+    probe = os.path.join(ROOT, "block_sparse_attention_softmax_amd", "libsparge_probe.so")
+    L = ctypes.CDLL(probe)
+    L.sparge_probe_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_void_p]
+    L.sparge_probe_mfma_bf16.restype = ctypes.c_int
+    L.sparge_probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    L.sparge_probe_mfma_flops.restype = ctypes.c_double
+    blocks, iters = 256 * 2 * 8, 8192  # 8 waves per CU, 8 rounds of the chip
+    buf = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    best = []
+    for chains in (4, 8):
+        rates = []
+        for rep in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            rc = L.sparge_probe_mfma_bf16(ctypes.c_void_p(buf.data_ptr()), blocks, iters, chains,
+                                          st)
+            e1.record()
+            torch.cuda.synchronize()
+            if rc != 0:
+                raise RuntimeError(f"MFMA probe launch failed: HIP error {rc}")
+            if rep:  # the first launch warms the clock and loads the code
+                rates.append(L.sparge_probe_mfma_flops(blocks, iters, chains) /
+                             (e0.elapsed_time(e1) * 1e9))
+        best.append(float(np.median(rates)))
+    out["mfma_bf16_tflops"] = round(max(best), 1)
+    out["mfma_bf16_tflops_4_8_chains"] = [round(x, 1) for x in best]
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    gbs = []
+    for rep in range(6):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        if rep:
+            gbs.append(2.0 * src.numel() / (e0.elapsed_time(e1) * 1e6))
+    out["hbm_copy_gbs"] = round(float(np.median(gbs)), 1)
+    del src, dst, buf
+    torch.cuda.empty_cache()
+    return out
+
+
+def oracle_check(samples, inputs) -> dict:
+    """Untimed parity check of the benchmarked GPU results against the oracle,
+    per configuration: the oracle's mask over every row (its near-tie rows, and
+    rows where the GPU's mask differs) and the oracle's attention on the seeded
+    sample of query blocks the GPU output was kept for (max / mean abs error)."""
+    from oracle import sparge_oracle as O
+
+    out = {}
+    masks = {}
+    for smp in samples:
+        wl = smp["wl"]
+        Q, K, V = inputs[smp["inputs"]]
+        key = (smp["inputs"], smp["k"], smp["p"])
+        if key not in masks:
+            masks[key] = O.predict_mask(Q, K, wl.block_q, wl.block_k, smp["k"], smp["p"],
+                                        wl.scale)
+        m = masks[key]
+        j = np.arange(wl.n_k)
+        gpu_kept = ((smp["bits"][..., j // 32] >> (j % 32).astype(np.uint32)) & 1).astype(bool)
+        rows_differ = int((gpu_kept != m.kept).any(-1).sum())
+        errs = []
+        for h, blocks, got in smp["rows"]:
+            q, k, v = (O.bf16_to_f64(X[0, h]) for X in (Q, K, V))
+            if smp["alpha"] is None:
+                ref = O.masked_attention_head(q, k, v, m.kept[0, h], wl.block_q, wl.block_k,
+                                              wl.scale, q_blocks=blocks)
+            else:
+                ref = O.sparse_linear_attention_head(q, k, v, m.kept[0, h], wl.block_q,
+                                                     wl.block_k, wl.scale, smp["alpha"],
+                                                     q_blocks=blocks)
+            valid = ~np.isnan(ref[:, 0])
+            errs.append(np.abs(O.bf16_to_f64(got) - ref[valid]))
+        e = np.concatenate([x.ravel() for x in errs])
+        out[smp["name"]] = {
+            "mask_rows": int(m.kept[..., 0].size), "near_tie_rows": int((m.margin < 1e-5).sum()),
+            "rows_differing_from_oracle": rows_differ,
+            "output_sample": f"{sum(len(b) for _, b, _ in smp['rows'])} query blocks of heads "
+                             f"{[h for h, _, _ in smp['rows']]}",
+            "max_abs_err": float(e.max()), "mean_abs_err": float(e.mean())}
+    return out
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="wan1.3b")
     ap.add_argument("--cpu-blocks", type=int, default=768,
                     help="query blocks of the oracle's CPU sample (heads 0, 1, ... in order)")
@@ -133,6 +257,9 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one device-to-device copy of this many MiB first, as a "
                          "known-size reference for hardware byte counters")
+    ap.add_argument("--point", default=None, metavar="K,P",
+                    help="time only the forward step at Top-k fraction K and Top-p mass P on the "
+                         "workload (for profiling one operating point) and print its line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
@@ -238,6 +365,27 @@ def main():
         if ev is not None:
             ev[3].record()
 
+    def gpu_sample(name, w, k_frac, p_mass, bits_t, o_t, alpha=None, inputs=None):
+        """Copies, outside every timed region, of a benchmarked GPU mask and of
+        its output rows on a seeded sample of query blocks (first, last and four
+        more, on two heads: for the mixed-range configuration one near-uniform
+        and one sink head), for the oracle check."""
+        rng = np.random.default_rng(len(name) + int(k_frac * 1000))
+        if w.name == "wan1.3b_s95":
+            heads = [int(rng.integers(0, w.H // 2)), int(rng.integers(w.H // 2, w.H))]
+        else:
+            heads = sorted(int(h) for h in rng.choice(w.H, size=min(2, w.H), replace=False))
+        rows = []
+        for h in heads:
+            blocks = sorted({0, w.n_q - 1, *(int(b) for b in rng.choice(w.n_q, min(4, w.n_q),
+                                                                          replace=False))})
+            sel = np.concatenate([np.arange(b * w.block_q, min((b + 1) * w.block_q, w.N))
+                                  for b in blocks])
+            got = o_t[0, h][torch.from_numpy(sel).to(o_t.device)]
+            rows.append((h, blocks, got.cpu().view(torch.uint16).numpy()))
+        return {"name": name, "wl": w, "inputs": inputs or w.name, "k": k_frac, "p": p_mass,
+                "alpha": alpha, "bits": bits_t.cpu().numpy().view(np.uint32), "rows": rows}
+
     def capture(fn):
         """A HIP graph of fn's launches (both streams), captured after one run on
         the capture stream."""
@@ -251,7 +399,12 @@ def main():
             fn()
         return graph
 
-    def timed(k_frac, p_mass, steps, warmup, linear=None, alpha_t=None, routed=False):
+    # writing this between repetitions evicts the 256 MiB Infinity Cache (MALL)
+    # and every L2, so the next step starts from HBM ("cold")
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def timed(k_frac, p_mass, steps, warmup, linear=None, alpha_t=None, routed=False,
+              cold=False):
         kw = dict(linear=linear, alpha_t=alpha_t, routed=routed)
         for _ in range(warmup):
             step(k_frac, p_mass, **kw)
@@ -275,51 +428,99 @@ def main():
             run()
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) / steps
+        # the distribution: each step of the same kind between two events
+        se = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for e in se:
+            e[0].record()
+            run()
+            e[1].record()
+        torch.cuda.synchronize()
         del graph
-        mask_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-        pack_ms = (float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) if linear else
-                   float(np.mean([e[4].elapsed_time(e[5]) for e in evs])))
-        attn_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+        mask = [e[0].elapsed_time(e[1]) for e in evs]
+        pack = ([e[1].elapsed_time(e[2]) for e in evs] if linear else
+                [e[4].elapsed_time(e[5]) for e in evs])
+        attn = [e[2].elapsed_time(e[3]) for e in evs]
+        r = {"wall": wall, "mask_ms": float(np.mean(mask)), "pack_ms": float(np.mean(pack)),
+             "attn_ms": float(np.mean(attn)), "step_dist": dist([a.elapsed_time(b) for a, b in se]),
+             "attn_dist": dist(attn)}
+        if cold:
+            # each step after the cache flush: eager, events around its parts
+            ce = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+            for i in range(steps):
+                flush.fill_(i & 0xFF)
+                step(k_frac, p_mass, ce[i], **kw)
+            torch.cuda.synchronize()
+            r["cold"] = {"step_ms": dist([e[0].elapsed_time(e[3]) for e in ce]),
+                         "mask_ms": dist([e[0].elapsed_time(e[1]) for e in ce]),
+                         "attn_kernel_ms": dist([e[2].elapsed_time(e[3]) for e in ce])}
         c_np, i_np = cnt.cpu().numpy(), idx.cpu().numpy()
-        kf = kept_flops(c_np, i_np, N, d, wl.block_q, wl.block_k)
-        kept_frac = float(c_np.sum()) / (B * H * n_q * n_k)
-        return wall, mask_ms, pack_ms, attn_ms, kf, kept_frac
+        r["kf"] = kept_flops(c_np, i_np, N, d, wl.block_q, wl.block_k)
+        r["kept_frac"] = float(c_np.sum()) / (B * H * n_q * n_k)
+        return r
+
+    if args.point:
+        kp, pp = (float(x) for x in args.point.split(","))
+        r = timed(kp, pp, args.steps, args.warmup)
+        tf = r["kf"] / (r["attn_ms"] * 1e-3) / 1e12
+        print(json.dumps({"workload": wl.name, "k": kp, "p": pp, "steps": args.steps,
+                          "block_sparsity": round(1 - r["kept_frac"], 4),
+                          "ms_per_step": round(r["wall"] * 1e3, 4),
+                          "attn_kernel_ms": round(r["attn_ms"], 4),
+                          "attn_kernel_ms_dist": r["attn_dist"], "flops_per_launch": r["kf"],
+                          "attn_kept_tflops": round(tf, 2),
+                          "attn_frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}), flush=True)
+        return
+
+    # measured ceilings beside the nameplate figures: dense bf16 MFMA (a probe
+    # kernel of independent 32x32x16 chains) and HBM (a 1 GiB device copy)
+    ceilings = measure_ceilings(torch, dev)
 
     dense = 4.0 * B * H * float(N) * N * d
-    wall, mask_ms, pack_ms, kern_ms, kf, kept_frac = timed(wl.k_frac, wl.p_mass, args.steps,
-                                                            args.warmup)
+    head = timed(wl.k_frac, wl.p_mass, args.steps, args.warmup, cold=True)
+    wall, mask_ms, pack_ms, kern_ms = head["wall"], head["mask_ms"], head["pack_ms"], head["attn_ms"]
+    kf, kept_frac = head["kf"], head["kept_frac"]
     achieved = kf / (kern_ms * 1e-3) / 1e12
+    checks = [gpu_sample("wan1.3b", wl, wl.k_frac, wl.p_mass, bits, o)]
 
     points = {}
     for kfrac in (0.10, 0.05):
-        w2, m2, p2, k2, kf2, frac2 = timed(kfrac, 0.0, max(5, args.steps // 2), 2)
+        r2 = timed(kfrac, 0.0, args.steps, 2, cold=True)
+        w2, k2, kf2 = r2["wall"], r2["attn_ms"], r2["kf"]
+        tf2 = kf2 / (k2 * 1e-3) / 1e12
         points[f"p0_k{int(kfrac * 100)}"] = {
-            "k": kfrac, "p": 0.0, "block_sparsity": round(1 - frac2, 4),
-            "ms_per_step": round(w2 * 1e3, 4), "mask_ms": round(m2, 4),
-            "pack_ms": round(p2, 4), "attn_kernel_ms": round(k2, 4),
+            "k": kfrac, "p": 0.0, "block_sparsity": round(1 - r2["kept_frac"], 4),
+            "ms_per_step": round(w2 * 1e3, 4), "mask_ms": round(r2["mask_ms"], 4),
+            "pack_ms": round(r2["pack_ms"], 4), "attn_kernel_ms": round(k2, 4),
+            "step_ms_dist": r2["step_dist"], "attn_kernel_ms_dist": r2["attn_dist"],
             "dense_equiv_tflops": round(dense / w2 / 1e12, 2),
             "attn_dense_equiv_tflops": round(dense / (k2 * 1e-3) / 1e12, 2),
-            "attn_kept_tflops": round(kf2 / (k2 * 1e-3) / 1e12, 2),
-            "attn_frac_bf16_peak": round(kf2 / (k2 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+            "attn_kept_tflops": round(tf2, 2),
+            "attn_frac_bf16_peak": round(tf2 / PEAK_BF16_TFLOPS, 4),
+            "attn_frac_measured_mfma": round(tf2 / ceilings["mfma_bf16_tflops"], 4),
+            "flops_per_launch": kf2, "cold": r2["cold"]}
+        checks.append(gpu_sample(f"wan1.3b p=0 k={kfrac}", wl, kfrac, 0.0, bits, o))
 
     # the sparse-linear workload: same inputs and mask, plus alpha = 0.1 elu+1 linear branch
-    n_lin = max(5, args.steps // 2)
-    w3, m3, l3, _, kf3, frac3 = timed(wl.k_frac, wl.p_mass, n_lin, 2, linear="add",
-                                      alpha_t=alpha)
+    n_lin = max(5, args.steps // 4)
+    r3 = timed(wl.k_frac, wl.p_mass, n_lin, 2, linear="add", alpha_t=alpha)
+    w3 = r3["wall"]
     linear = {"workload": "wan1.3b_linear (alpha = 0.1, phi = elu + 1)",
-              "ms_per_step": round(w3 * 1e3, 4), "mask_ms": round(m3, 4),
-              "sparse_linear_ms": round(l3, 4),
+              "ms_per_step": round(w3 * 1e3, 4), "mask_ms": round(r3["mask_ms"], 4),
+              "sparse_linear_ms": round(r3["pack_ms"], 4), "step_ms_dist": r3["step_dist"],
               "dense_equiv_tflops": round(dense / w3 / 1e12, 2)}
+    checks.append(gpu_sample("wan1.3b_linear", WORKLOADS["wan1.3b_linear"], wl.k_frac, wl.p_mass,
+                             bits, o, alpha=0.1, inputs=wl.name))
 
     # SLA2: router mask (projected pooled Q, K; hard Top-k) and the per-channel mix;
     # SALAD: the added branch dropped on half of the heads, then on all of them
-    w4, m4, _, _, _, frac4 = timed(0.10, 0.0, n_lin, 2, routed=True)
-    w5, m5, l5, _, _, _ = timed(wl.k_frac, wl.p_mass, n_lin, 2, linear="mix",
-                                alpha_t=alpha_mix)
-    w6, _, l6, _, _, _ = timed(wl.k_frac, wl.p_mass, n_lin, 2, linear="add",
-                               alpha_t=alpha_half)
-    w7, _, l7, _, _, _ = timed(wl.k_frac, wl.p_mass, n_lin, 2, linear="add",
-                               alpha_t=alpha_none)
+    r4 = timed(0.10, 0.0, n_lin, 2, routed=True)
+    w4, m4, frac4 = r4["wall"], r4["mask_ms"], r4["kept_frac"]
+    r5 = timed(wl.k_frac, wl.p_mass, n_lin, 2, linear="mix", alpha_t=alpha_mix)
+    w5, l5 = r5["wall"], r5["pack_ms"]
+    r6 = timed(wl.k_frac, wl.p_mass, n_lin, 2, linear="add", alpha_t=alpha_half)
+    w6, l6 = r6["wall"], r6["pack_ms"]
+    r7 = timed(wl.k_frac, wl.p_mass, n_lin, 2, linear="add", alpha_t=alpha_none)
+    w7, l7 = r7["wall"], r7["pack_ms"]
     sla2 = {"routed_mask": {"k": 0.10, "p": 0.0, "weights": "N(0, 1/d) per head, float32",
                             "mask_ms": round(m4, 4), "ms_per_step": round(w4 * 1e3, 4),
                             "block_sparsity": round(1 - frac4, 4)},
@@ -442,14 +643,18 @@ def main():
                  "call_ms": round(e0.elapsed_time(e1) / 3, 3)}
     del sws
 
-    # the forward at the two other configurations: 95% sparsity on mixed-range heads
-    # (k = 3%, p = 0.8) and Wan 14B at 720p (H = 40, N = 75600); mask, V pack and the
-    # attention kernel, each timed on its own over the same launches
+    # the forward at the other configurations: the tiny case, 95% sparsity on
+    # mixed-range heads (k = 3%, p = 0.8) and Wan 14B at 720p (H = 40, N = 75600);
+    # mask, V pack and the attention kernel, each timed on its own over the same
+    # launches
     other = {}
+    inputs = {wl.name: (Q, K, V)}
     if not args.no_other_configs:
-        for name in ("wan1.3b_s95", "wan14b_720p"):
+        for name in ("tiny", "wan1.3b_s95", "wan14b_720p"):
             w2 = WORKLOADS[name]
-            q2, k2, v2 = (g(a) for a in generate(w2))
+            arrays = generate(w2)
+            inputs[name] = arrays
+            q2, k2, v2 = (g(a) for a in arrays)
             B2, H2, N2, d2 = q2.shape
             bits2 = torch.empty((B2, H2, w2.n_q, -(-w2.n_k // 32)), dtype=torch.int32,
                                 device=dev)
@@ -477,12 +682,13 @@ def main():
                     ev[3].record()
             fwd2()
             torch.cuda.synchronize()
-            n_o = max(3, args.steps // 4)
+            n_o = max(3, args.steps // 4) if name == "wan14b_720p" else args.steps
             evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_o)]
             for i in range(n_o):
                 fwd2(evs[i])
             torch.cuda.synchronize()
             ms = [float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j in range(3)]
+            checks.append(gpu_sample(name, w2, w2.k_frac, w2.p_mass, bits2, o2))
             c_np, i_np = cnt2.cpu().numpy(), idx2.cpu().numpy()
             kf2 = kept_flops(c_np, i_np, N2, d2, w2.block_q, w2.block_k)
             dense2 = 4.0 * B2 * H2 * float(N2) * N2 * d2
@@ -493,13 +699,19 @@ def main():
                 "block_sparsity": round(1 - float(c_np.sum()) / c_np.size / w2.n_k, 4),
                 "mask_ms": round(ms[0], 4), "pack_ms": round(ms[1], 4),
                 "attn_kernel_ms": round(ms[2], 4), "sequential_ms": round(total, 4),
+                "attn_kernel_ms_dist": dist([e[2].elapsed_time(e[3]) for e in evs]),
                 "dense_equiv_tflops": round(dense2 / total / 1e9, 2),
                 "attn_kept_tflops": round(kf2 / ms[2] / 1e9, 2),
                 "attn_frac_bf16_peak": round(kf2 / ms[2] / 1e9 / PEAK_BF16_TFLOPS, 4)}
             del q2, k2, v2, bits2, idx2, cnt2, ws2, aws2, o2
             torch.cuda.empty_cache()
 
-    cpu = None if args.no_cpu_baseline else cpu_baseline(wl, Q, K, V, args.cpu_blocks)
+    cpu = check = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, Q, K, V, args.cpu_blocks)
+        t0 = time.perf_counter()
+        check = oracle_check(checks, inputs)
+        check["seconds"] = round(time.perf_counter() - t0, 1)
 
     line = {
         "metric": METRIC,
@@ -516,11 +728,16 @@ def main():
                    "block_sparsity": round(1 - kept_frac, 4)},
         "mask_ms": round(mask_ms, 4), "pack_ms": round(pack_ms, 4),
         "attn_kernel_ms": round(kern_ms, 4),
+        "step_ms_dist": head["step_dist"], "attn_kernel_ms_dist": head["attn_dist"],
+        "cold": head["cold"],
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(),
                      "kernel": "sparse_attn_fwd_kernel<128,128,false>",
-                     "flops_per_launch": kf},
+                     "flops_per_launch": kf,
+                     "measured_ceiling": ceilings["mfma_bf16_tflops"],
+                     "frac_measured_ceiling": round(achieved / ceilings["mfma_bf16_tflops"], 4)},
+        "ceilings": ceilings,
         "operating_points": points,
         "sparse_linear": linear,
         "sla2_salad": sla2,
@@ -529,6 +746,7 @@ def main():
         "svg2": svg2_line,
         "other_configs": other,
         "cpu_baseline": cpu,
+        "oracle_check": check,
     }
     print(json.dumps(line), flush=True)
 

@@ -3,7 +3,8 @@
     python -m block_sparse_attention_softmax_amd.build
 
 Every translation unit under csrc/ is compiled with hipcc for gfx950 only and
-linked into block_sparse_attention_softmax_amd/libsparge.so.
+linked into block_sparse_attention_softmax_amd/libsparge.so; the measurement
+probe under csrc/probe/ becomes libsparge_probe.so beside it.
 """
 from __future__ import annotations
 
@@ -45,6 +46,25 @@ def _compile(src: str) -> str:
     return obj
 
 
+PROBE_SRC = os.path.join(CSRC, "probe", "ceilings.hip")
+PROBE_LIB = os.path.join(PKG, "libsparge_probe.so")
+
+
+def build_probe(verbose: bool = True) -> str:
+    """The measurement probe (a dense-MFMA ceiling kernel the benchmark runs
+    beside the attention path; not part of the library's ABI)."""
+    obj = _compile(PROBE_SRC)
+    tmp = PROBE_LIB + ".tmp"
+    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", obj, "-o", tmp],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"probe link failed:\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    if verbose:
+        print(f"built {PROBE_LIB}")
+    return PROBE_LIB
+
+
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sources()
@@ -61,6 +81,7 @@ def build(verbose: bool = True) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
+    build_probe(verbose)
     return LIB
 
 
