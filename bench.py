@@ -593,6 +593,24 @@ def main():
 
     # the low-bit sparse branch (INT8 Q/K, e4m3 P/V) on the same masks: whole call
     # (quantisation of Q, K and V included) against the bf16 attention call
+    # the low-bit sparse branch (INT8 Q/K, e4m3 P/V) on the same masks. Its Q and K
+    # codes come from the mask's pooling pass (sparge_mask_pool_lowbit), which
+    # streams those blocks anyway; the attention call is then the V pack and the
+    # kernel, as the bf16 call is the bf16 V pack and its kernel. Also timed: both
+    # kernels alone, the pooling with and without the codes, the whole step of
+    # each kind (pooling, selection, pack, attention, eager, in that order) and
+    # the one-call form that quantises Q and K itself.
+    def med(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+        for e in evs:
+            e[0].record()
+            fn()
+            e[1].record()
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in evs]))
+
     lowbit = {}
     lws8 = torch.empty(S.lowbit_workspace_bytes(B, H, N, d, wl.block_q, wl.block_k),
                        dtype=torch.uint8, device=dev)
@@ -602,26 +620,51 @@ def main():
                               out=(bits, idx, cnt))
         c_np, i_np = cnt.cpu().numpy(), idx.cpu().numpy()
         kf_lb = kept_flops(c_np, i_np, N, d, wl.block_q, wl.block_k)
-        res = {}
-        for tag, fn in (("lowbit", lambda: S.sparge_attn_fwd_lowbit(
-                             q, k, v, idx, cnt, wl.block_q, wl.block_k, wl.scale, out=o,
-                             workspace=lws8)),
-                        ("bf16", lambda: S.sparge_attn_fwd(q, k, v, idx, cnt, wl.block_q,
-                                                           wl.block_k, wl.scale, out=o,
-                                                           workspace=aws))):
-            fn()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            n_l = max(5, args.steps // 2)
-            e0.record()
-            for _ in range(n_l):
-                fn()
-            e1.record()
-            torch.cuda.synchronize()
-            res[tag] = e0.elapsed_time(e1) / n_l
-        lowbit[name] = {"k": kfrac, "p": pm, "lowbit_call_ms": round(res["lowbit"], 4),
-                        "bf16_call_ms": round(res["bf16"], 4),
-                        "lowbit_kept_tops": round(kf_lb / res["lowbit"] / 1e9, 1)}
+        n_l = max(5, args.steps // 2) if name != "headline" else max(3, args.steps // 5)
+        S.sparge_mask_pool_lowbit(q, k, wl.block_q, wl.block_k, workspace=ws,
+                                  lowbit_workspace=lws8)
+        S.sparge_attn_lowbit_pack(v, lws8, wl.block_q)
+
+        def lb_call():
+            S.sparge_attn_lowbit_pack(v, lws8, wl.block_q)
+            S.sparge_attn_fwd_lowbit_packed(q, idx, cnt, lws8, wl.block_q, wl.block_k, wl.scale,
+                                            out=o)
+
+        def lb_step():
+            S.sparge_mask_pool_lowbit(q, k, wl.block_q, wl.block_k, workspace=ws,
+                                      lowbit_workspace=lws8)
+            S.sparge_mask_select(q, ws, wl.block_q, wl.block_k, kfrac, pm, wl.scale,
+                                 out=(bits, idx, cnt))
+            lb_call()
+
+        def bf_step():
+            S.sparge_mask_pool(q, k, wl.block_q, wl.block_k, workspace=ws)
+            S.sparge_mask_select(q, ws, wl.block_q, wl.block_k, kfrac, pm, wl.scale,
+                                 out=(bits, idx, cnt))
+            S.sparge_attn_fwd(q, k, v, idx, cnt, wl.block_q, wl.block_k, wl.scale, out=o,
+                              workspace=aws)
+        t = {
+            "lowbit_call_ms": med(lb_call, n_l),
+            "bf16_call_ms": med(lambda: S.sparge_attn_fwd(q, k, v, idx, cnt, wl.block_q,
+                                                          wl.block_k, wl.scale, out=o,
+                                                          workspace=aws), n_l),
+            "lowbit_kernel_ms": med(lambda: S.sparge_attn_fwd_lowbit_packed(
+                q, idx, cnt, lws8, wl.block_q, wl.block_k, wl.scale, out=o), n_l),
+            "bf16_kernel_ms": med(lambda: S.sparge_attn_fwd_packed(
+                q, k, idx, cnt, aws, wl.block_q, wl.block_k, wl.scale, out=o), n_l),
+            "pool_lowbit_ms": med(lambda: S.sparge_mask_pool_lowbit(
+                q, k, wl.block_q, wl.block_k, workspace=ws, lowbit_workspace=lws8), n_l),
+            "pool_ms": med(lambda: S.sparge_mask_pool(q, k, wl.block_q, wl.block_k,
+                                                      workspace=ws), n_l),
+            "lowbit_step_ms": med(lb_step, n_l),
+            "bf16_step_ms": med(bf_step, n_l),
+            "one_call_lowbit_ms": med(lambda: S.sparge_attn_fwd_lowbit(
+                q, k, v, idx, cnt, wl.block_q, wl.block_k, wl.scale, out=o, workspace=lws8),
+                n_l)}
+        lowbit[name] = {"k": kfrac, "p": pm, **{key: round(x, 4) for key, x in t.items()},
+                        "call_speedup": round(t["bf16_call_ms"] / t["lowbit_call_ms"], 3),
+                        "step_speedup": round(t["bf16_step_ms"] / t["lowbit_step_ms"], 3),
+                        "lowbit_kept_tops": round(kf_lb / t["lowbit_kernel_ms"] / 1e9, 1)}
     del lws8
 
     # SVG2's clustered attention (256 query / 512 key clusters, 3 k-means rounds, p = 0.9)

@@ -28,7 +28,8 @@ EXPORTS = ("sparge_mask_workspace_bytes", "sparge_mask_predict", "sparge_mask_po
            "sparge_attn_bwd", "sparse_linear_bwd_workspace_bytes", "sparse_linear_attn_bwd",
            "sla2_mix_attn_bwd", "sparge_attn_lowbit_workspace_bytes", "sparge_attn_fwd_lowbit",
            "svg2_attn_workspace_bytes", "svg2_attn_fwd", "sparge_mask_noalloc_scratch_bytes",
-           "sparge_mask_predict_noalloc", "sparge_last_error")
+           "sparge_mask_predict_noalloc", "sparge_mask_pool_lowbit", "sparge_attn_lowbit_pack",
+           "sparge_attn_fwd_lowbit_packed", "sparge_last_error")
 
 _lib = None
 
@@ -58,6 +59,14 @@ def lib() -> ctypes.CDLL:
         L.sparge_mask_predict_noalloc.argtypes = [vp, vp] + [c_int] * 6 + [c_float] * 3 + [
             vp] * 5
         L.sparge_mask_predict_noalloc.restype = c_int
+        L.sparge_mask_pool_lowbit.argtypes = [vp, vp] + [c_int] * 6 + [vp, c_size, vp, c_size,
+                                                                        vp]
+        L.sparge_mask_pool_lowbit.restype = c_int
+        L.sparge_attn_lowbit_pack.argtypes = [vp] + [c_int] * 5 + [vp, c_size, vp]
+        L.sparge_attn_lowbit_pack.restype = c_int
+        L.sparge_attn_fwd_lowbit_packed.argtypes = [vp, vp] + [c_int] * 6 + [c_float, vp, vp,
+                                                                              c_size, vp]
+        L.sparge_attn_fwd_lowbit_packed.restype = c_int
         L.sparge_mask_pool.argtypes = [vp, vp] + [c_int] * 6 + [vp, c_size, vp]
         L.sparge_mask_pool.restype = c_int
         L.sparge_mask_select.argtypes = [c_int] * 6 + [c_float] * 3 + [vp] * 5 + [c_size, vp]
@@ -361,6 +370,49 @@ def sparge_attn_fwd_lowbit(q, k, v, kv_idx, kv_cnt, block_q=128, block_k=64, sca
     _check(lib().sparge_attn_fwd_lowbit(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_idx), _ptr(kv_cnt), B,
                                         H, N, d, block_q, block_k, scale, _ptr(o),
                                         _ptr(workspace), ws_bytes, _stream(q)))
+    return o
+
+
+def sparge_mask_pool_lowbit(q, k, block_q=128, block_k=64, workspace=None, lowbit_workspace=None):
+    """sparge_mask_pool whose pass also writes the INT8 codes and scales of Q and K
+    into the low-bit workspace; returns (workspace, lowbit_workspace)."""
+    B, H, N, d = _qkv(q, k)
+    workspace, ws_bytes = _workspace(workspace, mask_workspace_bytes(B, H, N, d, block_q, block_k),
+                                     q.device)
+    lowbit_workspace, lb_bytes = _workspace(
+        lowbit_workspace, lowbit_workspace_bytes(B, H, N, d, block_q, block_k), q.device)
+    _check(lib().sparge_mask_pool_lowbit(_ptr(q), _ptr(k), B, H, N, d, block_q, block_k,
+                                         _ptr(workspace), ws_bytes, _ptr(lowbit_workspace),
+                                         lb_bytes, _stream(q)))
+    return workspace, lowbit_workspace
+
+
+def sparge_attn_lowbit_pack(v, lowbit_workspace, block_q=128):
+    """V's channel scales and packed e4m3 codes into the low-bit workspace."""
+    B, H, N, d = _qkv(v)
+    if lowbit_workspace is None:
+        raise ValueError("lowbit_workspace must be the low-bit workspace of the pooling call")
+    lowbit_workspace, lb_bytes = _workspace(lowbit_workspace, 0, v.device)
+    _check(lib().sparge_attn_lowbit_pack(_ptr(v), B, H, N, d, block_q, _ptr(lowbit_workspace),
+                                         lb_bytes, _stream(v)))
+    return lowbit_workspace
+
+
+def sparge_attn_fwd_lowbit_packed(q, kv_idx, kv_cnt, lowbit_workspace, block_q=128, block_k=64,
+                                  scale=None, out=None):
+    """The low-bit attention from the codes in the workspace (q gives the shape,
+    device and stream only)."""
+    B, H, N, d = _qkv(q)
+    _lists(kv_idx, kv_cnt, q, block_q, block_k)
+    if lowbit_workspace is None:
+        raise ValueError("lowbit_workspace must hold the codes of the pooling and pack calls")
+    lowbit_workspace, lb_bytes = _workspace(lowbit_workspace, 0, q.device)
+    o = torch.empty_like(q) if out is None else _buf(out, "out", torch.bfloat16, q.shape, q.device)
+    if scale is None:
+        scale = default_scale(d)
+    _check(lib().sparge_attn_fwd_lowbit_packed(_ptr(kv_idx), _ptr(kv_cnt), B, H, N, d, block_q,
+                                               block_k, scale, _ptr(o), _ptr(lowbit_workspace),
+                                               lb_bytes, _stream(q)))
     return o
 
 

@@ -112,7 +112,7 @@ int mask_impl(const void* q, const void* k, const float* wq, const float* wk, in
               int N, int d, int block_q, int block_k, float k_frac, float p_mass, float scale,
               uint32_t* mask_bits, int32_t* kv_idx, int32_t* kv_cnt, double* block_logits,
               void* workspace, size_t workspace_bytes, void* stream, int phase = 0,
-              bool launch = true) {
+              bool launch = true, void* lowbit_ws = nullptr, size_t lowbit_ws_bytes = 0) {
   int rc = check_shape(B, H, N, d, block_q, block_k);
   if (rc != SPARGE_OK) return rc;
   const int n_q = ceil_div(N, block_q), n_k = ceil_div(N, block_k);
@@ -145,6 +145,12 @@ int mask_impl(const void* q, const void* k, const float* wq, const float* wk, in
                       : (block_logits && selects) ? mask_ws(B, H, N, d, block_q, block_k) - score_bytes
                                                   : mask_ws(B, H, N, d, block_q, block_k);
   if (workspace_bytes < need) return fail(SPARGE_ERR_INVALID_ARG, "workspace too small");
+  if (lowbit_ws) {  // the pooling pass also writes the low-bit codes of Q and K
+    if (!aligned(lowbit_ws, 256))
+      return fail(SPARGE_ERR_INVALID_ARG, "lowbit_workspace must be 256-byte aligned");
+    if (lowbit_ws_bytes < sparge::lowbit_workspace_bytes(B, H, N, d, block_q))
+      return fail(SPARGE_ERR_INVALID_ARG, "lowbit_workspace too small");
+  }
   if (!launch) return SPARGE_OK;  // arguments checked only
 
   sparge::MaskLaunch a{};
@@ -183,6 +189,12 @@ int mask_impl(const void* q, const void* k, const float* wq, const float* wk, in
   a.bits = mask_bits;
   a.idx = kv_idx;
   a.cnt = kv_cnt;
+  if (lowbit_ws) {
+    sparge::LowbitLaunch l{};
+    l.B = B; l.H = H; l.N = N; l.d = d; l.block_q = block_q; l.n_q = n_q; l.n_k = n_k;
+    sparge::lowbit_layout(l, static_cast<unsigned char*>(lowbit_ws));
+    a.qc = l.qc; a.kc = l.kc; a.qsc = l.qs; a.ksc = l.ks;
+  }
   const hipError_t e = sparge::launch_mask(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "mask prediction launch");
   return SPARGE_OK;
@@ -206,6 +218,17 @@ int sparge_mask_pool(const void* q, const void* k, int B, int H, int N, int d, i
   g_last_error.clear();
   return mask_impl(q, k, nullptr, nullptr, B, H, N, d, block_q, block_k, 1.0f, 0.0f, 1.0f,
                    nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes, stream, 1);
+}
+
+int sparge_mask_pool_lowbit(const void* q, const void* k, int B, int H, int N, int d,
+                            int block_q, int block_k, void* workspace, size_t workspace_bytes,
+                            void* lowbit_workspace, size_t lowbit_workspace_bytes,
+                            void* stream) {
+  g_last_error.clear();
+  if (!lowbit_workspace) return fail(SPARGE_ERR_INVALID_ARG, "null pointer argument");
+  return mask_impl(q, k, nullptr, nullptr, B, H, N, d, block_q, block_k, 1.0f, 0.0f, 1.0f,
+                   nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes, stream, 1,
+                   true, lowbit_workspace, lowbit_workspace_bytes);
 }
 
 int sparge_mask_select(int B, int H, int N, int d, int block_q, int block_k, float k_frac,
@@ -471,18 +494,34 @@ size_t sparge_attn_lowbit_workspace_bytes(int B, int H, int N, int d, int block_
   return sparge::lowbit_workspace_bytes(B, H, N, d, block_q);
 }
 
-int sparge_attn_fwd_lowbit(const void* q, const void* k, const void* v, const int32_t* kv_idx,
-                           const int32_t* kv_cnt, int B, int H, int N, int d, int block_q,
-                           int block_k, float scale, void* o, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// the low-bit branch, whole (phase kLowbitAll) or in its parts; arguments a
+// part does not read may be null
+int lowbit_impl(const char* what, int phase, const void* q, const void* k, const void* v,
+                const int32_t* kv_idx, const int32_t* kv_cnt, int B, int H, int N, int d,
+                int block_q, int block_k, float scale, void* o, void* workspace,
+                size_t workspace_bytes, void* stream) {
   g_last_error.clear();
-  int rc = check_attn_args(q, k, v, kv_idx, kv_cnt, B, H, N, d, block_q, block_k, scale, o);
+  int rc = check_shape(B, H, N, d, block_q, block_k);
   if (rc != SPARGE_OK) return rc;
-  if (!workspace) return fail(SPARGE_ERR_INVALID_ARG, "null pointer argument");
+  const bool quant = phase == sparge::kLowbitAll, packs = phase != sparge::kLowbitAttend;
+  const bool attends = phase != sparge::kLowbitPackV;
+  if (!workspace || (quant && (!q || !k)) || (packs && !v) || (attends && (!o || !kv_idx || !kv_cnt)))
+    return fail(SPARGE_ERR_INVALID_ARG, "null pointer argument");
+  if ((quant && (!aligned(q, 16) || !aligned(k, 16))) || (packs && !aligned(v, 16)) ||
+      (attends && !aligned(o, 16)))
+    return fail(SPARGE_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
+  if (attends && (!aligned(kv_idx, 4) || !aligned(kv_cnt, 4)))
+    return fail(SPARGE_ERR_INVALID_ARG, "kv_idx and kv_cnt must be 4-byte aligned");
+  if (attends && (!(scale > 0.0f) || !isfinite(scale)))
+    return fail(SPARGE_ERR_INVALID_ARG, "scale must be finite and > 0");
   if (!aligned(workspace, 256)) return fail(SPARGE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   if (workspace_bytes < sparge::lowbit_workspace_bytes(B, H, N, d, block_q))
     return fail(SPARGE_ERR_INVALID_ARG, "workspace too small");
   sparge::LowbitLaunch a{};
+  a.phase = phase;
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
   a.v = static_cast<const uint16_t*>(v);
@@ -495,8 +534,37 @@ int sparge_attn_fwd_lowbit(const void* q, const void* k, const void* v, const in
   a.scale = scale;
   sparge::lowbit_layout(a, static_cast<unsigned char*>(workspace));
   const hipError_t e = sparge::launch_lowbit(a, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "sparge_attn_fwd_lowbit launch");
+  if (e != hipSuccess) return hip_fail(e, what);
   return SPARGE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int sparge_attn_fwd_lowbit(const void* q, const void* k, const void* v, const int32_t* kv_idx,
+                           const int32_t* kv_cnt, int B, int H, int N, int d, int block_q,
+                           int block_k, float scale, void* o, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return lowbit_impl("sparge_attn_fwd_lowbit launch", sparge::kLowbitAll, q, k, v, kv_idx,
+                     kv_cnt, B, H, N, d, block_q, block_k, scale, o, workspace,
+                     workspace_bytes, stream);
+}
+
+int sparge_attn_lowbit_pack(const void* v, int B, int H, int N, int d, int block_q,
+                            void* lowbit_workspace, size_t lowbit_workspace_bytes,
+                            void* stream) {
+  return lowbit_impl("sparge_attn_lowbit_pack launch", sparge::kLowbitPackV, nullptr, nullptr,
+                     v, nullptr, nullptr, B, H, N, d, block_q, 64, 1.0f, nullptr,
+                     lowbit_workspace, lowbit_workspace_bytes, stream);
+}
+
+int sparge_attn_fwd_lowbit_packed(const int32_t* kv_idx, const int32_t* kv_cnt, int B, int H,
+                                  int N, int d, int block_q, int block_k, float scale, void* o,
+                                  void* lowbit_workspace, size_t lowbit_workspace_bytes,
+                                  void* stream) {
+  return lowbit_impl("sparge_attn_fwd_lowbit_packed launch", sparge::kLowbitAttend, nullptr,
+                     nullptr, nullptr, kv_idx, kv_cnt, B, H, N, d, block_q, block_k, scale, o,
+                     lowbit_workspace, lowbit_workspace_bytes, stream);
 }
 
 size_t svg2_attn_workspace_bytes(int B, int H, int N, int d, int block_q, int n_q_clusters,

@@ -23,6 +23,21 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return u >> 16;
 }
 
+// INT8 codes of the four bf16 values in w0, w1 (low half first) at
+// inv = 127 / amax: rint(x * inv) in float32, clamped to [-127, 127], packed
+// little-endian (the low-bit branch's Q and K codes).
+__device__ __forceinline__ uint32_t int8_pack4(uint32_t w0, uint32_t w1, float inv) {
+  const uint32_t ws[2] = {w0, w1};
+  uint32_t word = 0;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int lo = (int)fminf(fmaxf(rintf(bf16_lo(ws[e]) * inv), -127.0f), 127.0f);
+    const int hi = (int)fminf(fmaxf(rintf(bf16_hi(ws[e]) * inv), -127.0f), 127.0f);
+    word |= ((uint32_t)(lo & 0xFF) | ((uint32_t)(hi & 0xFF) << 8)) << (16 * e);
+  }
+  return word;
+}
+
 // Workgroup id -> tile id such that the tiles of one XCD are contiguous.
 // Workgroups are dispatched round-robin over the 8 XCDs (wg % 8), so the
 // remap gives each XCD a contiguous, head-major range of tiles and the
@@ -38,6 +53,12 @@ __device__ __forceinline__ int xcd_remap(int wg, int total) {
 // ---- launchers (each returns the hipError_t of its launches) ----
 struct MaskLaunch {
   int phase;  // 0: the whole mask; 1: pooling only; 2: everything after the pooling
+  // optional (pooling): INT8 codes and per-block scales of Q and K for the
+  // low-bit branch, written by the pooling pass from the same blocks
+  int8_t* qc;
+  int8_t* kc;
+  float* qsc;
+  float* ksc;
   const uint16_t* q;
   const uint16_t* k;
   int B, H, N, d, block_q, block_k, n_q, n_k, npad, words;
@@ -130,6 +151,7 @@ struct LowbitLaunch {
   uint16_t* o;
   int B, H, N, d, block_q, n_q, n_k;
   float scale;
+  int phase;  // LowbitPhase
   // workspace (lowbit_layout)
   int8_t* qc;       // [B*H, N, d] INT8 codes of Q
   int8_t* kc;       // [B*H, N, d] INT8 codes of K
@@ -138,6 +160,9 @@ struct LowbitLaunch {
   uint32_t* vmax;   // [B*H, d] amax of each V channel (float bits)
   uint8_t* vt8;     // [B*H, n_k, d, 64] e4m3 codes of V^T, packed
 };
+// everything from bf16 Q, K, V; only V's channel scales and packed codes; only
+// the attention from codes already in the workspace
+enum LowbitPhase { kLowbitAll = 0, kLowbitPackV = 1, kLowbitAttend = 2 };
 hipError_t launch_lowbit(const LowbitLaunch& a, hipStream_t s);
 size_t lowbit_workspace_bytes(int B, int H, int N, int d, int block_q);
 void lowbit_layout(LowbitLaunch& a, unsigned char* workspace);

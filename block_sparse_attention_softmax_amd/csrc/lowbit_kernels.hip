@@ -66,21 +66,8 @@ __global__ __launch_bounds__(256) void quant_int8_kernel(const uint16_t* __restr
   if (t == 0) scales[(size_t)bh * nblocks + bi] = amax / 127.0f;
   for (int p = t; p < n8; p += 256) {
     const uint4 u = *reinterpret_cast<const uint4*>(x + base + (size_t)p * 8);
-    const uint32_t* w = &u.x;
-    uint32_t out[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      uint32_t word = 0;
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const uint32_t ww = w[2 * h + e];
-        const int lo = (int)fminf(fmaxf(rintf(bf16_lo(ww) * inv), -127.0f), 127.0f);
-        const int hi = (int)fminf(fmaxf(rintf(bf16_hi(ww) * inv), -127.0f), 127.0f);
-        word |= ((uint32_t)(lo & 0xFF) | ((uint32_t)(hi & 0xFF) << 8)) << (16 * e);
-      }
-      out[h] = word;
-    }
-    *reinterpret_cast<uint2*>(codes + base + (size_t)p * 8) = make_uint2(out[0], out[1]);
+    *reinterpret_cast<uint2*>(codes + base + (size_t)p * 8) =
+        make_uint2(int8_pack4(u.x, u.y, inv), int8_pack4(u.z, u.w, inv));
   }
 }
 
@@ -172,8 +159,11 @@ struct Tile8 {
   __device__ static constexpr int swz(int row, int chunk) { return chunk ^ ((row / RPW) & (CPR - 1)); }
 };
 
+// Three workgroups per CU (168 registers per wave at BQ = 128): the kernel is
+// bound by its softmax VALU work, so a third wave per SIMD to interleave pays
+// more than a deeper pipeline within a wave would (4% measured over two).
 template <int D, int BQ>
-__global__ __launch_bounds__(BQ * 2, 2) void sparse_attn_lowbit_kernel(
+__global__ __launch_bounds__(BQ * 2, 3) void sparse_attn_lowbit_kernel(
     const int8_t* __restrict__ qc, const float* __restrict__ qs, const int8_t* __restrict__ kc,
     const float* __restrict__ ks, const uint8_t* __restrict__ vt8,
     const uint32_t* __restrict__ vmax, const int32_t* __restrict__ kv_idx,
@@ -240,7 +230,16 @@ __global__ __launch_bounds__(BQ * 2, 2) void sparse_attn_lowbit_kernel(
   for (int i = 0; i < DT; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[i][r] = 0.0f;
-  float m = -INFINITY, lsum = 0.0f;  // running max of s; sum of P codes' values
+  float m = -INFINITY;  // running max of s
+  // The sum of the P codes' values comes from one more FP8 product: an A
+  // operand of e4m3 ones (0x38) gives, in every register of every lane, the
+  // sum over the block's 64 keys of that lane's query (instead of decoding the
+  // codes on the VALU); register 0 is kept.
+  constexpr int one8 = 0x38383838;
+  const v8i ones = {one8, one8, one8, one8, one8, one8, one8, one8};
+  floatx16 lacc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) lacc[r] = 0.0f;
 
   if (count > 0) issue(jat(0), 0);
   for (int e = 0; e < count; ++e) {
@@ -285,7 +284,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void sparse_attn_lowbit_kernel(
     const float m_new = fmaxf(m, mloc);
     if (__any(m_new > m)) {  // exact running maximum: rescale whenever it rises
       const float f = m_new > m ? __builtin_amdgcn_exp2f((m - m_new) * c) : 1.0f;
-      lsum *= f;
+      lacc[0] *= f;
 #pragma unroll
       for (int i = 0; i < DT; ++i)
 #pragma unroll
@@ -313,12 +312,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void sparse_attn_lowbit_kernel(
         pb[w] &= nv >= 4 ? -1 : (int)((1u << (8 * nv)) - 1u);
       }
     }
-#pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(pb[w], false);
-      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(pb[w], true);
-      lsum += (lo[0] + lo[1]) + (hi[0] + hi[1]);
-    }
+    lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pb, lacc, 0, 0, 0, 127, 0, 127);
     // O^T += V^T P^T, one instruction per 32 channels covers the 64 keys
 #pragma unroll
     for (int i = 0; i < DT; ++i) {
@@ -332,7 +326,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void sparse_attn_lowbit_kernel(
   }
 
   // O = sv_c * sum(codeP codeV) / sum(codeP) (the 448s cancel)
-  const float ltot = lsum + __shfl_xor(lsum, 32);
+  const float ltot = lacc[0];
   const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
   // O leaves through LDS as whole rows (each wave's 32 x D tile in its own
   // slice of the tile buffers, free once every wave is past its last block)
@@ -358,17 +352,22 @@ __global__ __launch_bounds__(BQ * 2, 2) void sparse_attn_lowbit_kernel(
 template <int D, int BQ>
 hipError_t launch_lowbit_t(const LowbitLaunch& a, hipStream_t s) {
   const int BH = a.B * a.H, total = BH * a.n_q;
-  hipLaunchKernelGGL((quant_int8_kernel<D>), dim3(a.n_q, BH), dim3(256), 0, s, a.q, a.qc, a.qs,
-                     a.N, BQ, a.n_q);
-  hipLaunchKernelGGL((quant_int8_kernel<D>), dim3(a.n_k, BH), dim3(256), 0, s, a.k, a.kc, a.ks,
-                     a.N, BK, a.n_k);
-  const size_t nv = (size_t)BH * D;
-  hipLaunchKernelGGL(fill_u32_zero_kernel, dim3((unsigned)((nv + 255) / 256)), dim3(256), 0, s,
-                     a.vmax, nv);
-  hipLaunchKernelGGL((v_amax_kernel<D>), dim3((a.N + 511) / 512, BH), dim3(256), 0, s, a.v,
-                     a.vmax, a.N);
-  hipLaunchKernelGGL((pack_v_fp8_kernel<D>), dim3(a.n_k, BH), dim3(256), 0, s, a.v, a.vmax,
-                     a.vt8, a.N, a.n_k);
+  if (a.phase == kLowbitAll) {
+    hipLaunchKernelGGL((quant_int8_kernel<D>), dim3(a.n_q, BH), dim3(256), 0, s, a.q, a.qc, a.qs,
+                       a.N, BQ, a.n_q);
+    hipLaunchKernelGGL((quant_int8_kernel<D>), dim3(a.n_k, BH), dim3(256), 0, s, a.k, a.kc, a.ks,
+                       a.N, BK, a.n_k);
+  }
+  if (a.phase != kLowbitAttend) {
+    const size_t nv = (size_t)BH * D;
+    hipLaunchKernelGGL(fill_u32_zero_kernel, dim3((unsigned)((nv + 255) / 256)), dim3(256), 0, s,
+                       a.vmax, nv);
+    hipLaunchKernelGGL((v_amax_kernel<D>), dim3((a.N + 511) / 512, BH), dim3(256), 0, s, a.v,
+                       a.vmax, a.N);
+    hipLaunchKernelGGL((pack_v_fp8_kernel<D>), dim3(a.n_k, BH), dim3(256), 0, s, a.v, a.vmax,
+                       a.vt8, a.N, a.n_k);
+    if (a.phase == kLowbitPackV) return hipGetLastError();
+  }
   hipLaunchKernelGGL((sparse_attn_lowbit_kernel<D, BQ>), dim3(total), dim3(BQ * 2), 0, s, a.qc,
                      a.qs, a.kc, a.ks, a.vt8, a.vmax, a.idx, a.cnt, a.o, a.N, a.n_q, a.n_k, total,
                      a.scale * 1.4426950408889634f);

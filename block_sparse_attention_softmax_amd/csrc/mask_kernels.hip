@@ -33,13 +33,19 @@ constexpr int kThreads = 256;
 // ----------------------------------------------------------------- pooling
 // One workgroup per block of Q (blockIdx.x < nq) or K (the rest); grid.y =
 // B*H. Thread t owns 16-byte column chunk t % CH and rows t / CH + RSTEP*i.
-template <int D>
+// With Q8 the same pass also writes the low-bit branch's INT8 codes of the
+// block and its scale amax / 127 (the block is in registers already): the
+// codes and scales quant_int8_kernel would produce, bit for bit.
+template <int D, bool Q8 = false>
 __global__ __launch_bounds__(kThreads) void pool_mean_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, double* __restrict__ qbar,
-    double* __restrict__ kbar, int N, int block_q, int block_k, int nq, int nk) {
+    double* __restrict__ kbar, int N, int block_q, int block_k, int nq, int nk,
+    int8_t* __restrict__ qc = nullptr, int8_t* __restrict__ kc = nullptr,
+    float* __restrict__ qsc = nullptr, float* __restrict__ ksc = nullptr) {
   constexpr int CH = D / 8;              // 16-byte chunks per row
   constexpr int RSTEP = kThreads / CH;   // rows handled per pass
   __shared__ double red[kThreads][9];    // +1 pad against bank conflicts
+  __shared__ float amx[kThreads / 64];
 
   const bool isq = (int)blockIdx.x < nq;
   const int blk = isq ? blockIdx.x : blockIdx.x - nq;
@@ -76,12 +82,39 @@ __global__ __launch_bounds__(kThreads) void pool_mean_kernel(
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) red[t][e] = acc[e];
+  if constexpr (Q8) {  // block amax (rows past the block are zeros), then the codes
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < MAXIT; ++i) {
+      const uint32_t ws[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a = fmaxf(a, fmaxf(fabsf(bf16_lo(ws[e])), fabsf(bf16_hi(ws[e]))));
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) a = fmaxf(a, __shfl_xor(a, off));
+    if ((t & 63) == 0) amx[t >> 6] = a;
+  }
   __syncthreads();
   if (t < D) {
     const int cc = t / 8, e = t % 8;
     double s = 0.0;
     for (int r = 0; r < RSTEP; ++r) s += red[r * CH + cc][e];
     out[((size_t)bh * nblk + blk) * D + t] = s / (double)rows;
+  }
+  if constexpr (Q8) {
+    float amax = amx[0];
+#pragma unroll
+    for (int i = 1; i < kThreads / 64; ++i) amax = fmaxf(amax, amx[i]);
+    const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+    if (t == 0) (isq ? qsc : ksc)[(size_t)bh * nblk + blk] = amax / 127.0f;
+    int8_t* codes = (isq ? qc : kc) + ((size_t)bh * N + start) * D + 8 * c;
+#pragma unroll
+    for (int i = 0; i < MAXIT; ++i) {
+      const int r = r0 + RSTEP * i;
+      if (r < rows)
+        *reinterpret_cast<uint2*>(codes + (size_t)r * D) =
+            make_uint2(int8_pack4(w[i].x, w[i].y, inv), int8_pack4(w[i].z, w[i].w, inv));
+    }
   }
 }
 
@@ -625,12 +658,25 @@ hipError_t launch_mask(const MaskLaunch& a, hipStream_t st) {
                          x, y, out, nx, ny, tq, tk, tiles, sc);
   };
   if (a.phase != 2) {
-    if (a.d == 128)
-      hipLaunchKernelGGL(pool_mean_kernel<128>, dim3(a.n_q + a.n_k, BH), dim3(kThreads), 0, st,
-                         a.q, a.k, a.qbar, a.kbar, a.N, a.block_q, a.block_k, a.n_q, a.n_k);
-    else
-      hipLaunchKernelGGL(pool_mean_kernel<64>, dim3(a.n_q + a.n_k, BH), dim3(kThreads), 0, st,
-                         a.q, a.k, a.qbar, a.kbar, a.N, a.block_q, a.block_k, a.n_q, a.n_k);
+    const dim3 grid(a.n_q + a.n_k, BH);
+    if (a.qc) {
+      if (a.d == 128)
+        hipLaunchKernelGGL((pool_mean_kernel<128, true>), grid, dim3(kThreads), 0, st, a.q, a.k,
+                           a.qbar, a.kbar, a.N, a.block_q, a.block_k, a.n_q, a.n_k, a.qc, a.kc,
+                           a.qsc, a.ksc);
+      else
+        hipLaunchKernelGGL((pool_mean_kernel<64, true>), grid, dim3(kThreads), 0, st, a.q, a.k,
+                           a.qbar, a.kbar, a.N, a.block_q, a.block_k, a.n_q, a.n_k, a.qc, a.kc,
+                           a.qsc, a.ksc);
+    } else if (a.d == 128) {
+      hipLaunchKernelGGL((pool_mean_kernel<128>), grid, dim3(kThreads), 0, st, a.q, a.k, a.qbar,
+                         a.kbar, a.N, a.block_q, a.block_k, a.n_q, a.n_k, nullptr, nullptr,
+                         nullptr, nullptr);
+    } else {
+      hipLaunchKernelGGL((pool_mean_kernel<64>), grid, dim3(kThreads), 0, st, a.q, a.k, a.qbar,
+                         a.kbar, a.N, a.block_q, a.block_k, a.n_q, a.n_k, nullptr, nullptr,
+                         nullptr, nullptr);
+    }
     if (a.phase == 1) return hipGetLastError();
   }
   const double* qs = a.qbar;
@@ -645,22 +691,7 @@ hipError_t launch_mask(const MaskLaunch& a, hipStream_t st) {
     ks = a.kbar_p;
   }
   scores(qs, ks, a.logits, a.n_q, a.n_k, a.scale);
-  switch (a.npad) {
-    case 64: return launch_select_reg<64>(a, st);
-    case 128: return launch_select_reg<128>(a, st);
-    case 256: return launch_select_reg<256>(a, st);
-    case 512: return launch_select_reg<512>(a, st);
-    // 1024 / 2048 entries: one wave per row needs about a thousand rows to
-    // fill the chip; with fewer, a workgroup per row (the LDS sort) is faster
-    case 1024:
-      return a.B * a.H * a.n_q >= kRegSelectMinRows ? launch_select_reg<1024>(a, st)
-                                                      : launch_select<1024>(a, st);
-    case 2048:
-      return a.B * a.H * a.n_q >= kRegSelectMinRows ? launch_select_reg<2048>(a, st)
-                                                      : launch_select<2048>(a, st);
-    default: return launch_select<4096>(a, st);
-  }
-  return hipGetLastError();
+  return launch_select_rows(a, st);
 }
 
 }  // namespace sparge

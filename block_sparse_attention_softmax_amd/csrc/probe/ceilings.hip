@@ -26,7 +26,6 @@ __global__ __launch_bounds__(256, 2) void mfma_bf16_probe_kernel(float* __restri
   for (int c = 0; c < kChains; ++c)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[c][r] = 0.0f;
-#pragma unroll 4
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
     for (int c = 0; c < kChains; ++c)

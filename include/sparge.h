@@ -360,6 +360,38 @@ int sparge_attn_fwd_lowbit(const void* q, const void* k, const void* v,
                            int d, int block_q, int block_k, float scale, void* o,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* sparge_attn_fwd_lowbit in parts, so that Q and K are not read again for
+ * their INT8 codes: the mask's pooling pass already streams every query and
+ * key block, so it writes the codes and scales of those same blocks.
+ *
+ *  sparge_mask_pool_lowbit      : sparge_mask_pool, whose pass also writes the
+ *                                 INT8 codes and per-block scales of Q and K
+ *                                 (as defined for sparge_attn_fwd_lowbit)
+ *                                 into lowbit_workspace;
+ *  sparge_attn_lowbit_pack      : V's per-channel scales and its packed e4m3
+ *                                 codes into lowbit_workspace (reads v only);
+ *  sparge_attn_fwd_lowbit_packed: the attention of sparge_attn_fwd_lowbit from
+ *                                 the codes in lowbit_workspace (reads no
+ *                                 bf16 input).
+ * Enqueued on one stream with the same shapes and workspaces (the pack may
+ * come before or after the pooling; sparge_mask_select between the pooling
+ * and the attention as usual), they give exactly the outputs of
+ * sparge_mask_pool + sparge_mask_select + sparge_attn_fwd_lowbit.
+ * lowbit_workspace: at least sparge_attn_lowbit_workspace_bytes(), 256-byte
+ * aligned; other arguments as for the calls named above. The attention may
+ * be repeated on one pack and one pooling (other lists, same inputs). */
+int sparge_mask_pool_lowbit(const void* q, const void* k, int B, int H, int N, int d,
+                            int block_q, int block_k, void* workspace, size_t workspace_bytes,
+                            void* lowbit_workspace, size_t lowbit_workspace_bytes,
+                            void* stream);
+int sparge_attn_lowbit_pack(const void* v, int B, int H, int N, int d, int block_q,
+                            void* lowbit_workspace, size_t lowbit_workspace_bytes,
+                            void* stream);
+int sparge_attn_fwd_lowbit_packed(const int32_t* kv_idx, const int32_t* kv_cnt, int B, int H,
+                                  int N, int d, int block_q, int block_k, float scale, void* o,
+                                  void* lowbit_workspace, size_t lowbit_workspace_bytes,
+                                  void* stream);
+
 /* Device workspace (bytes) of svg2_attn_fwd (float64 copies of Q and K, the
  * clustering, the selection and the padded permuted Q, K, V); 0 for arguments
  * svg2_attn_fwd would reject. */

@@ -339,3 +339,29 @@ def test_mask_workspace_without_scores_when_block_logits_given():
     assert _mask(wsb=means - 1, logits=A) == binding.ERR_INVALID_ARG
     assert b"workspace" in binding.lib().sparge_last_error()
     assert _mask(wsb=means + up(2 * 16 * 16 * 8) - 1) == binding.ERR_INVALID_ARG
+
+
+def test_lowbit_parts_check_arguments():
+    L = binding.lib()
+    need = L.sparge_attn_lowbit_workspace_bytes(1, 2, 1024, 64, 64, 64)
+    mws = L.sparge_mask_workspace_bytes(1, 2, 1024, 64, 64, 64)
+    # pooling with codes: null / misaligned / small low-bit workspace, bad shape
+    assert L.sparge_mask_pool_lowbit(A, A, 1, 2, 1024, 64, 64, 64, A, mws, None, need,
+                                     None) == binding.ERR_INVALID_ARG
+    assert L.sparge_mask_pool_lowbit(A, A, 1, 2, 1024, 64, 64, 64, A, mws,
+                                     ctypes.c_void_p(0x10010), need, None) == binding.ERR_INVALID_ARG
+    assert b"256-byte" in L.sparge_last_error()
+    assert L.sparge_mask_pool_lowbit(A, A, 1, 2, 1024, 64, 64, 64, A, mws, A, need - 1,
+                                     None) == binding.ERR_INVALID_ARG
+    assert b"lowbit_workspace too small" in L.sparge_last_error()
+    assert L.sparge_mask_pool_lowbit(A, A, 1, 2, 1024, 96, 64, 64, A, mws, A, need,
+                                     None) == binding.ERR_UNSUPPORTED
+    # the V pack reads v only; the attention reads lists, o and the workspace only
+    assert L.sparge_attn_lowbit_pack(None, 1, 2, 1024, 64, 64, A, need, None) == binding.ERR_INVALID_ARG
+    assert L.sparge_attn_lowbit_pack(MIS, 1, 2, 1024, 64, 64, A, need, None) == binding.ERR_INVALID_ARG
+    assert L.sparge_attn_lowbit_pack(A, 1, 2, 1024, 64, 64, A, need - 1, None) == binding.ERR_INVALID_ARG
+    f = L.sparge_attn_fwd_lowbit_packed
+    assert f(A, A, 1, 2, 1024, 64, 64, 64, ctypes.c_float(0.0), A, A, need, None) == binding.ERR_INVALID_ARG
+    assert f(None, A, 1, 2, 1024, 64, 64, 64, ctypes.c_float(0.125), A, A, need, None) == binding.ERR_INVALID_ARG
+    assert f(A, A, 1, 2, 1024, 64, 64, 32, ctypes.c_float(0.125), A, A, need, None) == binding.ERR_UNSUPPORTED
+    assert f(A, A, 1, 2, 1024, 64, 64, 64, ctypes.c_float(0.125), MIS, A, need, None) == binding.ERR_INVALID_ARG

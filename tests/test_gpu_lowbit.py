@@ -80,3 +80,35 @@ def test_lowbit_on_workload_sampled(k_frac, p_mass):
         rows = ~np.isnan(ref[:, 0])
         mx, mean = compare_outputs(got[0, h][rows], ref[rows])
         print(f"[lowbit workload] h={h}: max {mx:.2e} mean {mean:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("name,B,H,N,d,bq,k_frac,p_mass", [
+    ("small", 1, 2, 1000, 128, 128, 0.2, 0.9), ("small", 2, 1, 777, 64, 64, 0.3, 0.5),
+    ("small", 1, 3, 300, 128, 64, 0.5, 0.0), ("small", 1, 1, 50, 64, 128, 1.0, 0.9),
+    ("wan1.3b", 1, 12, 32760, 128, 128, 0.05, 0.0), ("wan1.3b", 1, 12, 32760, 128, 128, 0.05, 0.9)])
+def test_lowbit_in_parts_equals_one_call(name, B, H, N, d, bq, k_frac, p_mass):
+    """The pooling pass that also writes the Q and K codes, the V pack and the
+    attention from the workspace give exactly the one-call mask and low-bit
+    output; the pooling's means (hence the mask) are unchanged by the codes."""
+    if name == "wan1.3b":
+        wl = WORKLOADS["wan1.3b"]
+        Q, K, V = generate(wl)
+    else:
+        rng = np.random.default_rng(19 * N + d)
+        Q, K, V = (f64_to_bf16_bits(rng.standard_normal((B, H, N, d)) * 1.3) for _ in range(3))
+    q, k, v = to_gpu(Q), to_gpu(K), to_gpu(V)
+    print(f"\n[lowbit parts] {name} B={B} H={H} N={N} d={d} bq={bq} k={k_frac} p={p_mass}",
+          flush=True)
+    ref_mask = S.sparge_mask_predict(q, k, bq, 64, k_frac, p_mass, return_logits=True)
+    ref = S.sparge_attn_fwd_lowbit(q, k, v, ref_mask[1], ref_mask[2], bq, 64, out=nan_like(q))
+    ws, lws = S.sparge_mask_pool_lowbit(q, k, bq, 64)
+    S.sparge_attn_lowbit_pack(v, lws, bq)
+    bits, idx, cnt, lg = S.sparge_mask_select(q, ws, bq, 64, k_frac, p_mass, return_logits=True)
+    o = S.sparge_attn_fwd_lowbit_packed(q, idx, cnt, lws, bq, 64, out=nan_like(q))
+    o2 = S.sparge_attn_fwd_lowbit_packed(q, idx, cnt, lws, bq, 64, out=nan_like(q))  # again
+    torch.cuda.synchronize()
+    assert_all_written(ref, o)
+    assert torch.equal(bits, ref_mask[0]) and torch.equal(cnt, ref_mask[2])
+    assert torch.equal(lg.view(torch.int64), ref_mask[3].view(torch.int64))
+    assert torch.equal(o.view(torch.int16), ref.view(torch.int16))
+    assert torch.equal(o2.view(torch.int16), ref.view(torch.int16))

@@ -702,8 +702,8 @@ def test_step_graph_replays_match_eager(k_frac, p_mass):
 
 @pytest.mark.parametrize("name", ["tiny", "wan1.3b"])
 def test_one_call_entry_points_replay_from_a_graph(name):
-    """The one-call mask, the forward with lse, its backward and the low-bit
-    forward captured together in a HIP graph (outputs allocated in the
+    """The one-call mask, the forward with lse, its backward, the low-bit
+    forward and its split form captured together in a HIP graph (outputs allocated in the
     graph's pool): every replay, with eager calls and synchronizations in
     between, reproduces the eager results exactly (the kernels clear their
     own counters with fill kernels and add no floating-point atomics)."""
@@ -718,7 +718,13 @@ def test_one_call_entry_points_replay_from_a_graph(name):
         dq, dk, dv = S.sparge_attn_bwd(q, k, v, o, d_o, lse, idx, cnt, wl.block_q, wl.block_k,
                                        wl.scale)
         ol = S.sparge_attn_fwd_lowbit(q, k, v, idx, cnt, wl.block_q, wl.block_k, wl.scale)
-        return bits, cnt, o, lse, dq, dk, dv, ol
+        ws, lws = S.sparge_mask_pool_lowbit(q, k, wl.block_q, wl.block_k)
+        S.sparge_attn_lowbit_pack(v, lws, wl.block_q)
+        _, idx2, cnt2 = S.sparge_mask_select(q, ws, wl.block_q, wl.block_k, wl.k_frac, wl.p_mass,
+                                             wl.scale)
+        ol2 = S.sparge_attn_fwd_lowbit_packed(q, idx2, cnt2, lws, wl.block_q, wl.block_k,
+                                              wl.scale)
+        return bits, cnt, o, lse, dq, dk, dv, ol, ol2
 
     ref = [t.clone() for t in calls()]
     torch.cuda.synchronize()
@@ -730,7 +736,7 @@ def test_one_call_entry_points_replay_from_a_graph(name):
     torch.cuda.synchronize()
     with torch.cuda.graph(graph, stream=cs):
         outs = calls()
-    names = ("bits", "cnt", "o", "lse", "dq", "dk", "dv", "o_lowbit")
+    names = ("bits", "cnt", "o", "lse", "dq", "dk", "dv", "o_lowbit", "o_lowbit_parts")
     for _ in range(3):
         for t in outs:
             t.zero_()
