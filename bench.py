@@ -238,6 +238,41 @@ def oracle_check(samples, inputs) -> dict:
     return out
 
 
+def svg2_measure(S, q, k, v, o, ws, wl, cq, ck, iters, p_mass, reps=3):
+    """SVG2 call, clustering and attention times and the token-pair counts."""
+    import torch
+    B, H, N, d = q.shape
+
+    def med(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+    call = med(lambda: S.svg2_attn_fwd(q, k, v, cq, ck, iters=iters, p_mass=p_mass,
+                                       block_q=wl.block_q, scale=wl.scale, out=o, workspace=ws))
+    clus = med(lambda: S.svg2_attn_cluster(q, k, v, cq, ck, iters=iters, p_mass=p_mass,
+                                           block_q=wl.block_q, scale=wl.scale, workspace=ws))
+    att = med(lambda: S.svg2_attn_apply(q, cq, ck, ws, wl.block_q, wl.scale, out=o))
+    counts = S.svg2_attn_pair_counts(q, cq, ck, ws, wl.block_q).cpu().numpy()
+    useful, computed = float(counts[..., 0].sum()), float(counts[..., 1].sum())
+    tf_useful = 4.0 * d * useful / (att * 1e-3) / 1e12
+    return {"clusters": [cq, ck], "kmeans_rounds": iters, "p": p_mass,
+            "call_ms": round(call, 3), "cluster_ms": round(clus, 3), "attn_ms": round(att, 3),
+            "token_density": round(useful / (B * H * float(N) * N), 4),
+            "useful_pairs": useful, "computed_pairs": computed,
+            "padding_share": round(1.0 - useful / computed, 4),
+            "attn_useful_tflops": round(tf_useful, 1),
+            "attn_useful_frac_bf16_peak": round(tf_useful / PEAK_BF16_TFLOPS, 4),
+            "attn_computed_tflops": round(4.0 * d * computed / (att * 1e-3) / 1e12, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -257,6 +292,9 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one device-to-device copy of this many MiB first, as a "
                          "known-size reference for hardware byte counters")
+    ap.add_argument("--svg2", action="store_true",
+                    help="time only the SVG2 call and its parts on the workload (for profiling) "
+                         "and print its line")
     ap.add_argument("--point", default=None, metavar="K,P",
                     help="time only the forward step at Top-k fraction K and Top-p mass P on the "
                          "workload (for profiling one operating point) and print its line")
@@ -458,6 +496,13 @@ def main():
         r["kept_frac"] = float(c_np.sum()) / (B * H * n_q * n_k)
         return r
 
+    if args.svg2:
+        sws = torch.empty(S.svg2_workspace_bytes(B, H, N, d, wl.block_q, 256, 512),
+                          dtype=torch.uint8, device=dev)
+        print(json.dumps({"workload": wl.name, **svg2_measure(S, q, k, v, o, sws, wl, 256, 512, 3,
+                                                                0.9, reps=max(3, args.steps // 10))}),
+              flush=True)
+        return
     if args.point:
         kp, pp = (float(x) for x in args.point.split(","))
         r = timed(kp, pp, args.steps, args.warmup)
@@ -667,23 +712,13 @@ def main():
                         "lowbit_kept_tops": round(kf_lb / t["lowbit_kernel_ms"] / 1e9, 1)}
     del lws8
 
-    # SVG2's clustered attention (256 query / 512 key clusters, 3 k-means rounds, p = 0.9)
+    # SVG2's clustered attention (256 query / 512 key clusters, 3 k-means rounds, p = 0.9):
+    # the whole call, and its two parts (clustering with the gathers; the attention
+    # over the clusters, timed on its own with HIP events), with the token pairs
+    # that take part and those the attention kernel evaluates (padding included)
     sws = torch.empty(S.svg2_workspace_bytes(B, H, N, d, wl.block_q, 256, 512), dtype=torch.uint8,
                       device=dev)
-
-    def svg2():
-        S.svg2_attn_fwd(q, k, v, 256, 512, iters=3, p_mass=0.9, block_q=wl.block_q, scale=wl.scale,
-                        out=o, workspace=sws)
-    svg2()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(3):
-        svg2()
-    e1.record()
-    torch.cuda.synchronize()
-    svg2_line = {"clusters": [256, 512], "kmeans_rounds": 3, "p": 0.9,
-                 "call_ms": round(e0.elapsed_time(e1) / 3, 3)}
+    svg2_line = svg2_measure(S, q, k, v, o, sws, wl, 256, 512, 3, 0.9)
     del sws
 
     # the forward at the other configurations: the tiny case, 95% sparsity on

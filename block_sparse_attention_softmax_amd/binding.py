@@ -29,7 +29,8 @@ EXPORTS = ("sparge_mask_workspace_bytes", "sparge_mask_predict", "sparge_mask_po
            "sla2_mix_attn_bwd", "sparge_attn_lowbit_workspace_bytes", "sparge_attn_fwd_lowbit",
            "svg2_attn_workspace_bytes", "svg2_attn_fwd", "sparge_mask_noalloc_scratch_bytes",
            "sparge_mask_predict_noalloc", "sparge_mask_pool_lowbit", "sparge_attn_lowbit_pack",
-           "sparge_attn_fwd_lowbit_packed", "sparge_last_error")
+           "sparge_attn_fwd_lowbit_packed", "svg2_attn_pair_counts", "svg2_attn_cluster",
+           "svg2_attn_apply", "sparge_last_error")
 
 _lib = None
 
@@ -67,6 +68,12 @@ def lib() -> ctypes.CDLL:
         L.sparge_attn_fwd_lowbit_packed.argtypes = [vp, vp] + [c_int] * 6 + [c_float, vp, vp,
                                                                               c_size, vp]
         L.sparge_attn_fwd_lowbit_packed.restype = c_int
+        L.svg2_attn_cluster.argtypes = [vp] * 3 + [c_int] * 8 + [c_float] * 2 + [vp, c_size, vp]
+        L.svg2_attn_cluster.restype = c_int
+        L.svg2_attn_apply.argtypes = [c_int] * 7 + [c_float, vp, vp, c_size, vp]
+        L.svg2_attn_apply.restype = c_int
+        L.svg2_attn_pair_counts.argtypes = [c_int] * 7 + [vp, vp, c_size, vp]
+        L.svg2_attn_pair_counts.restype = c_int
         L.sparge_mask_pool.argtypes = [vp, vp] + [c_int] * 6 + [vp, c_size, vp]
         L.sparge_mask_pool.restype = c_int
         L.sparge_mask_select.argtypes = [c_int] * 6 + [c_float] * 3 + [vp] * 5 + [c_size, vp]
@@ -434,6 +441,50 @@ def svg2_attn_fwd(q, k, v, n_q_clusters, n_k_clusters, iters=10, p_mass=0.9, blo
                                n_k_clusters, iters, p_mass, scale, _ptr(o), _ptr(workspace),
                                ws_bytes, _stream(q)))
     return o
+
+
+def svg2_attn_cluster(q, k, v, n_q_clusters, n_k_clusters, iters=10, p_mass=0.9, block_q=128,
+                      scale=None, workspace=None):
+    """SVG2 steps 1-3 and the gathers into the workspace, which it returns."""
+    B, H, N, d = _qkv(q, k, v)
+    if scale is None:
+        scale = default_scale(d)
+    workspace, ws_bytes = _workspace(
+        workspace, svg2_workspace_bytes(B, H, N, d, block_q, n_q_clusters, n_k_clusters),
+        q.device)
+    _check(lib().svg2_attn_cluster(_ptr(q), _ptr(k), _ptr(v), B, H, N, d, block_q, n_q_clusters,
+                                   n_k_clusters, iters, p_mass, scale, _ptr(workspace), ws_bytes,
+                                   _stream(q)))
+    return workspace
+
+
+def svg2_attn_apply(q, n_q_clusters, n_k_clusters, workspace, block_q=128, scale=None, out=None):
+    """SVG2 step 4 from the workspace of svg2_attn_cluster (q gives the shape,
+    device and stream only)."""
+    B, H, N, d = _qkv(q)
+    if workspace is None:
+        raise ValueError("workspace must be the one svg2_attn_cluster filled")
+    workspace, ws_bytes = _workspace(workspace, 0, q.device)
+    o = torch.empty_like(q) if out is None else _buf(out, "out", torch.bfloat16, q.shape, q.device)
+    if scale is None:
+        scale = default_scale(d)
+    _check(lib().svg2_attn_apply(B, H, N, d, block_q, n_q_clusters, n_k_clusters, scale, _ptr(o),
+                                 _ptr(workspace), ws_bytes, _stream(q)))
+    return o
+
+
+def svg2_attn_pair_counts(q, n_q_clusters, n_k_clusters, workspace, block_q=128):
+    """After svg2_attn_fwd with this workspace: int64 [B, H, 2] of (token pairs
+    that take part, pairs the kernel evaluates) per head (q gives the shape,
+    device and stream only)."""
+    B, H, N, d = _qkv(q)
+    if workspace is None:
+        raise ValueError("workspace must be the one svg2_attn_fwd used")
+    workspace, ws_bytes = _workspace(workspace, 0, q.device)
+    counts = torch.empty((B, H, 2), dtype=torch.int64, device=q.device)
+    _check(lib().svg2_attn_pair_counts(B, H, N, d, block_q, n_q_clusters, n_k_clusters,
+                                       _ptr(counts), _ptr(workspace), ws_bytes, _stream(q)))
+    return counts
 
 
 def linear_bwd_workspace_bytes(B, H, N, d) -> int:

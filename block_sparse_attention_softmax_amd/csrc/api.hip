@@ -578,15 +578,20 @@ size_t svg2_attn_workspace_bytes(int B, int H, int N, int d, int block_q, int n_
   return sparge::svg2_workspace_bytes(B, H, N, d, block_q, n_q_clusters, n_k_clusters);
 }
 
-int svg2_attn_fwd(const void* q, const void* k, const void* v, int B, int H, int N, int d,
-                  int block_q, int n_q_clusters, int n_k_clusters, int iters, float p_mass,
-                  float scale, void* o, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+int svg2_impl(int phase, const void* q, const void* k, const void* v, int B, int H, int N,
+              int d, int block_q, int n_q_clusters, int n_k_clusters, int iters, float p_mass,
+              float scale, void* o, void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error.clear();
   int rc = check_shape(B, H, N, d, block_q, 64);
   if (rc != SPARGE_OK) return rc;
-  if (!q || !k || !v || !o || !workspace) return fail(SPARGE_ERR_INVALID_ARG, "null pointer argument");
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
-      !aligned(workspace, 256))
+  const bool clusters = phase != sparge::kSvg2Attend, attends = phase != sparge::kSvg2Cluster;
+  if ((clusters && (!q || !k || !v)) || (attends && !o) || !workspace)
+    return fail(SPARGE_ERR_INVALID_ARG, "null pointer argument");
+  if ((clusters && (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))) ||
+      (attends && !aligned(o, 16)) || !aligned(workspace, 256))
     return fail(SPARGE_ERR_INVALID_ARG, "q, k, v, o must be 16-byte and workspace 256-byte aligned");
   if (n_q_clusters < 1 || n_k_clusters < 1 || n_q_clusters > N || n_k_clusters > N)
     return fail(SPARGE_ERR_INVALID_ARG, "cluster counts must lie in [1, N]");
@@ -606,9 +611,60 @@ int svg2_attn_fwd(const void* q, const void* k, const void* v, int B, int H, int
   a.Cq = n_q_clusters; a.Ck = n_k_clusters; a.iters = iters;
   a.scale = scale;
   a.p = (double)p_mass;
+  a.phase = phase;
   sparge::svg2_layout(a, static_cast<unsigned char*>(workspace));
   const hipError_t e = sparge::launch_svg2(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "svg2_attn_fwd launch");
+  return SPARGE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int svg2_attn_fwd(const void* q, const void* k, const void* v, int B, int H, int N, int d,
+                  int block_q, int n_q_clusters, int n_k_clusters, int iters, float p_mass,
+                  float scale, void* o, void* workspace, size_t workspace_bytes, void* stream) {
+  return svg2_impl(sparge::kSvg2All, q, k, v, B, H, N, d, block_q, n_q_clusters, n_k_clusters,
+                   iters, p_mass, scale, o, workspace, workspace_bytes, stream);
+}
+
+int svg2_attn_cluster(const void* q, const void* k, const void* v, int B, int H, int N, int d,
+                      int block_q, int n_q_clusters, int n_k_clusters, int iters, float p_mass,
+                      float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  return svg2_impl(sparge::kSvg2Cluster, q, k, v, B, H, N, d, block_q, n_q_clusters,
+                   n_k_clusters, iters, p_mass, scale, nullptr, workspace, workspace_bytes,
+                   stream);
+}
+
+int svg2_attn_apply(int B, int H, int N, int d, int block_q, int n_q_clusters, int n_k_clusters,
+                    float scale, void* o, void* workspace, size_t workspace_bytes, void* stream) {
+  return svg2_impl(sparge::kSvg2Attend, nullptr, nullptr, nullptr, B, H, N, d, block_q,
+                   n_q_clusters, n_k_clusters, 0, 0.0f, scale, o, workspace, workspace_bytes,
+                   stream);
+}
+
+int svg2_attn_pair_counts(int B, int H, int N, int d, int block_q, int n_q_clusters,
+                          int n_k_clusters, uint64_t* counts, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  int rc = check_shape(B, H, N, d, block_q, 64);
+  if (rc != SPARGE_OK) return rc;
+  if (!counts || !workspace) return fail(SPARGE_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned(counts, 8) || !aligned(workspace, 256))
+    return fail(SPARGE_ERR_INVALID_ARG, "counts must be 8-byte and workspace 256-byte aligned");
+  if (n_q_clusters < 1 || n_k_clusters < 1 || n_q_clusters > N || n_k_clusters > N)
+    return fail(SPARGE_ERR_INVALID_ARG, "cluster counts must lie in [1, N]");
+  if (n_k_clusters > kMaxKeyBlocks)
+    return fail(SPARGE_ERR_UNSUPPORTED, "at most 4096 key clusters");
+  if (workspace_bytes < sparge::svg2_workspace_bytes(B, H, N, d, block_q, n_q_clusters, n_k_clusters))
+    return fail(SPARGE_ERR_INVALID_ARG, "workspace too small");
+  sparge::Svg2Launch a{};
+  a.B = B; a.H = H; a.N = N; a.d = d; a.block_q = block_q;
+  a.Cq = n_q_clusters; a.Ck = n_k_clusters;
+  sparge::svg2_layout(a, static_cast<unsigned char*>(workspace));
+  const hipError_t e = sparge::launch_svg2_pairs(
+      a, reinterpret_cast<unsigned long long*>(counts), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "svg2_attn_pair_counts launch");
   return SPARGE_OK;
 }
 

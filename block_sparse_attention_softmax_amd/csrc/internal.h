@@ -175,17 +175,25 @@ struct Svg2Launch {
   int B, H, N, d, block_q, Cq, Ck, iters;
   float scale;
   double p;
-  int max_tiles, max_chunks;  // padded query tiles / 64-key chunks per (b, h), upper bounds
+  int phase;  // Svg2Phase
+  // per (b, h), upper bounds: padded query tiles; 16-key groups of the padded
+  // keys; list entries of one query cluster (groups rounded up to whole
+  // 64-key chunks); packed 64-slot V^T tiles
+  int max_tiles, max_groups, max_list, n_ktiles;
   // workspace (svg2_layout)
   double *xq, *xk, *centq, *centk, *normq, *normk, *clog;
   int32_t *assign_q, *assign_k, *rank, *ccount, *size_q, *size_k, *off_q, *off_k, *perm_q,
       *perm_k;
   uint32_t* sbits;
-  int32_t *sidx, *scnt, *qpad_off, *kpad_off, *tile_cluster, *chunk_valid, *n_tiles, *lists,
-      *list_cnt;
+  int32_t *sidx, *scnt, *qpad_off, *kpad_off, *tile_cluster, *n_tiles, *lists, *list_cnt;
   uint16_t *qp, *kp, *vp, *vtp;
 };
+// everything; steps 1-3 and the gathers only; the attention only (from the workspace)
+enum Svg2Phase { kSvg2All = 0, kSvg2Cluster = 1, kSvg2Attend = 2 };
 hipError_t launch_svg2(const Svg2Launch& a, hipStream_t s);
+// per (b, h) of a finished svg2 call: query-key token pairs that take part in
+// the attention, and pairs the kernel computes (whole waves x whole chunks)
+hipError_t launch_svg2_pairs(const Svg2Launch& a, unsigned long long* counts, hipStream_t s);
 size_t svg2_workspace_bytes(int B, int H, int N, int d, int block_q, int Cq, int Ck);
 size_t svg2_layout(Svg2Launch& a, unsigned char* workspace);  // fills pointers; returns bytes
 size_t attn_workspace_bytes(int B, int H, int N, int d);    // packed V

@@ -13,13 +13,16 @@
 //  3. centroid Top-p: scale * c_q . c_k plus ln |cluster| (a cluster weighs as
 //     many tokens as it holds) and the mask's hybrid selection, Top-k reduced
 //     to one cluster.
-//  4. attention over variable-size clusters: every cluster is padded to whole
-//     tiles (query clusters to block_q rows, key clusters to 64 keys), the
-//     permuted Q, K, V are gathered into those padded layouts, each query tile
-//     walks the 64-key chunks of its cluster's selected key clusters with the
-//     keys past a cluster's end masked, and the output rows are written back
-//     to their original positions (the inverse permutation).
+//  4. attention over variable-size clusters: query clusters are padded to
+//     whole tiles of block_q rows, key clusters only to whole 16-key groups;
+//     the permuted Q, K, V are gathered into those layouts, each query tile
+//     walks 64-key chunks made of four groups of its cluster's selected key
+//     clusters (gathered into LDS group by group), with the keys past a
+//     group's valid count masked and waves past the cluster's end idle, and
+//     the output rows are written back to their original positions (the
+//     inverse permutation).
 #include <algorithm>
+#include <type_traits>
 
 #include "internal.h"
 #include "tiles.h"
@@ -295,55 +298,103 @@ __global__ __launch_bounds__(256) void svg2_weigh_kernel(double* __restrict__ lo
 
 // ------------------------------------------------------------- layouts
 // Per (b, h): padded offsets of the query clusters (whole tiles of BQ rows)
-// and key clusters (whole 64-key chunks), the cluster of every query tile,
-// the valid keys of every chunk, and the tile count.
-__global__ __launch_bounds__(64) void svg2_layout_kernel(
+// and of the key clusters (whole 16-key groups), the cluster of every query
+// tile and the tile count. One workgroup per (b, h): exclusive scans of the
+// per-cluster tile and group counts, 256 clusters at a time.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int& total) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) tmp[w] = x;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    before += i < w ? tmp[i] : 0;
+    total += tmp[i];
+  }
+  __syncthreads();
+  return before + x - v;
+}
+
+__global__ __launch_bounds__(256) void svg2_layout_kernel(
     const int32_t* __restrict__ qsize, const int32_t* __restrict__ ksize,
     int32_t* __restrict__ qpad_off, int32_t* __restrict__ kpad_off,
-    int32_t* __restrict__ tile_cluster, int32_t* __restrict__ chunk_valid,
-    int32_t* __restrict__ n_tiles, int Cq, int Ck, int BQ, int max_tiles, int max_chunks) {
-  const int bh = blockIdx.x;
-  if (threadIdx.x != 0) return;
+    int32_t* __restrict__ tile_cluster, int32_t* __restrict__ n_tiles, int Cq, int Ck, int BQ,
+    int max_tiles) {
+  __shared__ int tmp[4];
+  const int bh = blockIdx.x, t = threadIdx.x;
   int tiles = 0;
-  for (int c = 0; c < Cq; ++c) {
-    qpad_off[(size_t)bh * Cq + c] = tiles * BQ;
-    const int nt = (qsize[(size_t)bh * Cq + c] + BQ - 1) / BQ;
-    for (int u = 0; u < nt; ++u) tile_cluster[(size_t)bh * max_tiles + tiles + u] = c;
-    tiles += nt;
+  for (int c0 = 0; c0 < Cq; c0 += 256) {
+    const int c = c0 + t;
+    const int nt = c < Cq ? (qsize[(size_t)bh * Cq + c] + BQ - 1) / BQ : 0;
+    int chunk_total;
+    const int first = tiles + block_exclusive_scan(nt, tmp, chunk_total);
+    if (c < Cq) {
+      qpad_off[(size_t)bh * Cq + c] = first * BQ;
+      for (int u = 0; u < nt; ++u) tile_cluster[(size_t)bh * max_tiles + first + u] = c;
+    }
+    tiles += chunk_total;
   }
-  n_tiles[bh] = tiles;
-  int chunks = 0;
-  for (int c = 0; c < Ck; ++c) {
-    const int n = ksize[(size_t)bh * Ck + c], nc = (n + BK - 1) / BK;
-    kpad_off[(size_t)bh * Ck + c] = chunks * BK;
-    for (int u = 0; u < nc; ++u)
-      chunk_valid[(size_t)bh * max_chunks + chunks + u] = min(BK, n - u * BK);
-    chunks += nc;
+  if (t == 0) n_tiles[bh] = tiles;
+  int groups = 0;
+  for (int c0 = 0; c0 < Ck; c0 += 256) {
+    const int c = c0 + t;
+    const int ng = c < Ck ? (ksize[(size_t)bh * Ck + c] + 15) / 16 : 0;
+    int chunk_total;
+    const int first = groups + block_exclusive_scan(ng, tmp, chunk_total);
+    if (c < Ck) kpad_off[(size_t)bh * Ck + c] = first * 16;
+    groups += chunk_total;
   }
 }
 
-// Per (b, h, query cluster), one wave: the chunks of its selected key
-// clusters, in the selection's order.
+// Per (b, h, query cluster), one wave: the 16-key groups of its selected key
+// clusters, in the selection's order, as entries 32 * group + (valid keys of
+// the group); the list is padded to whole 64-key chunks (four entries) with
+// entries of no valid key, and list_cnt holds the chunk count. The selected
+// clusters are taken 64 at a time, one per lane, placed by a wave scan of
+// their group counts.
 __global__ __launch_bounds__(256) void svg2_lists_kernel(const int32_t* __restrict__ sidx,
                                                          const int32_t* __restrict__ scnt,
                                                          const int32_t* __restrict__ kpad_off,
                                                          const int32_t* __restrict__ ksize,
                                                          int32_t* __restrict__ lists,
                                                          int32_t* __restrict__ list_cnt, int Cq,
-                                                         int Ck, int max_chunks, size_t rows) {
+                                                         int Ck, int max_list, size_t rows) {
   const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= rows) return;
   const size_t bh = row / Cq;
   const int cnt = scnt[row];
+  int32_t* out = lists + row * max_list;
   int pos = 0;
-  for (int e = 0; e < cnt; ++e) {
-    const int j = sidx[row * Ck + e];
-    const int nc = (ksize[bh * Ck + j] + BK - 1) / BK, base = kpad_off[bh * Ck + j] / BK;
-    for (int u = lane; u < nc; u += 64) lists[row * max_chunks + pos + u] = base + u;
-    pos += nc;
+  for (int e0 = 0; e0 < cnt; e0 += 64) {
+    const int e = e0 + lane;
+    int n = 0, base = 0;
+    if (e < cnt) {
+      const int j = sidx[row * Ck + e];
+      n = ksize[bh * Ck + j];
+      base = kpad_off[bh * Ck + j] / 16;
+    }
+    const int ng = (n + 15) / 16;
+    int x = ng;  // inclusive scan of the group counts over the lanes
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off);
+      if (lane >= off) x += y;
+    }
+    const int first = pos + x - ng;
+    for (int u = 0; u < ng; ++u) out[first + u] = (base + u) * 32 + min(16, n - 16 * u);
+    pos += __shfl(x, 63);
   }
-  if (lane == 0) list_cnt[row] = pos;
+  const int padded = (pos + 3) & ~3;
+  if (lane < padded - pos) out[pos + lane] = 0;  // group 0 (finite data), no valid key
+  if (lane == 0) list_cnt[row] = padded / 4;
 }
 
 // Gather the rows of each cluster (in permuted order) into its padded slot;
@@ -372,34 +423,51 @@ __global__ __launch_bounds__(256) void svg2_gather_kernel(const uint16_t* __rest
 }
 
 // ------------------------------------------------------------ attention
-// One workgroup per padded query tile (BQ rows of one cluster), BQ/32 waves of
-// 32 queries: S^T = K Q^T and O^T += V^T P^T on bf16 MFMA as in the sparse
-// kernel, online softmax with an exact running maximum, K rows and packed V^T
-// of each 64-key chunk double-buffered by direct-to-LDS copies; keys past the
-// chunk's valid count get -inf; rows go back to their tokens.
+// The variable-size clusters without padding to whole tiles on the key side
+// ("Sparse VideoGen2" page, section 2C: sparse loading of the scattered keys
+// and values, dense compute on contiguous queries). Key clusters are padded
+// only to whole 16-key groups; a query cluster's list names the groups of its
+// kept key clusters, four to a 64-key chunk. One workgroup per padded query
+// tile (BQ rows of one cluster), BQ/32 waves of 32 queries (rows past the
+// cluster's end are zero and their results are not stored). Every chunk's K rows and packed V^T slots are gathered group by group
+// global -> LDS by direct-to-LDS copies with per-lane source addresses (K:
+// one group per copy instruction and wave; V^T: the two 16-byte halves of a
+// group's slots in every channel row), into the tile layouts of the sparse
+// kernel. The loop is the sparse kernel's: the S^T product of chunk it+1 is
+// issued during the softmax and P V of chunk it, K tiles and V^T tiles are
+// double-buffered one chunk apart, the running maximum is raised lazily, and
+// a chunk's keys past their group's valid count get -inf. Rows go back to
+// their tokens.
+// (D = 128 with BQ = 64 holds one wave per SIMD: two workgroups of two waves
+// fill a CU's LDS)
 template <int D, int BQ>
-__global__ __launch_bounds__(BQ * 2, 2) void svg2_attn_kernel(
+__global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void svg2_attn_kernel(
     const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp,
-    const uint16_t* __restrict__ vtp, const int32_t* __restrict__ chunk_valid,
-    const int32_t* __restrict__ tile_cluster, const int32_t* __restrict__ n_tiles,
-    const int32_t* __restrict__ lists, const int32_t* __restrict__ list_cnt,
-    const int32_t* __restrict__ perm_q, const int32_t* __restrict__ off_q,
-    const int32_t* __restrict__ size_q, const int32_t* __restrict__ qpad_off,
-    uint16_t* __restrict__ o, int N, int NQP, int NKP, int Cq, int max_tiles, int max_chunks,
-    float c) {
+    const uint16_t* __restrict__ vtp, const int32_t* __restrict__ tile_cluster,
+    const int32_t* __restrict__ n_tiles, const int32_t* __restrict__ lists,
+    const int32_t* __restrict__ list_cnt, const int32_t* __restrict__ perm_q,
+    const int32_t* __restrict__ off_q, const int32_t* __restrict__ size_q,
+    const int32_t* __restrict__ qpad_off, uint16_t* __restrict__ o, int N, int NQP, int NKP,
+    int Cq, int max_tiles, int max_list, int n_ktiles, float c) {
+  constexpr int NW = BQ / 32;
   using T = Tile<D>;
-  constexpr int NT = BQ * 2, DT = D / 32, KSTEPS = D / 16;
-  constexpr int KU = 64 * T::KCPR / NT, VU = D * T::VCPR / NT;
+  constexpr int LOADS = BK * D / 8 / 64 / NW;
+  constexpr int DT = D / 32, KSTEPS = D / 16, HALF = KSTEPS / 2;
+  constexpr float kRescale = 8.0f;  // raise the running maximum only past 2^8 (P <= 2^8)
   __shared__ __align__(16) unsigned char smem[4 * T::BYTES];
-  const int bh = blockIdx.x / max_tiles, tile = blockIdx.x % max_tiles;
+  unsigned char* const kbuf = smem;
+  unsigned char* const vbuf = smem + 2 * T::BYTES;
+
+  const int wg = xcd_remap(blockIdx.x, (int)gridDim.x);
+  const int bh = wg / max_tiles, tile = wg % max_tiles;
   if (tile >= n_tiles[bh]) return;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h2 = lane >> 5, l32 = lane & 31;
   const int cq = tile_cluster[(size_t)bh * max_tiles + tile];
+  const int qsz = size_q[(size_t)bh * Cq + cq];
+  const int local = tile * BQ - qpad_off[(size_t)bh * Cq + cq] + wave * 32 + l32;
   const int prow = tile * BQ + wave * 32 + l32;  // row of the padded permuted Q
-  const int local = prow - qpad_off[(size_t)bh * Cq + cq];
-  const bool valid = local < size_q[(size_t)bh * Cq + cq];
 
   bf16x8 qf[KSTEPS];
   {
@@ -408,28 +476,84 @@ __global__ __launch_bounds__(BQ * 2, 2) void svg2_attn_kernel(
     for (int s = 0; s < KSTEPS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qr + 16 * s);
   }
   const size_t lrow = (size_t)bh * Cq + cq;
-  const int count = list_cnt[lrow];
-  const int32_t* ids = lists + lrow * max_chunks;
+  const int count = min(max(list_cnt[lrow], 0), max_list / 4);
+  const int32_t* ents = lists + lrow * max_list;
+  const int gmax = n_ktiles * 4 - 1;  // last valid group index
+  // the four entries of chunk i sit in lanes 0..3 of one register, loaded two
+  // steps before their first use
+  auto load_ent = [&](int i) { return i < count && lane < 4 ? ents[4 * i + lane] : 0; };
+  auto gid_of = [&](int e) { return min(max(e >> 5, 0), gmax); };
 
-  uint32_t kofs[KU], vofs[VU];
+  const char* kh = reinterpret_cast<const char*>(kp + (size_t)bh * NKP * D);
+  const char* vh = reinterpret_cast<const char*>(vtp + (size_t)bh * n_ktiles * D * BK);
+  // Copy u of this wave covers tile positions p = p0 + 64 NW u. K: row
+  // kr = p / KCPR, i.e. row kr mod 16 of group kgroup(u) (one group for the
+  // whole wave). V^T: channel row vr = p / 8 and logical chunk sc, the 16-byte
+  // half sc mod 2 of group sc / 2's slots (the lane's own group). The lane's
+  // parts that do not depend on u are computed once: the swizzles see u only
+  // through multiples of their period.
+  const int p0 = 64 * wave + lane;
+  constexpr int KRU = 64 * NW / T::KCPR;  // K rows per copy step
+  const int kr0 = p0 / T::KCPR, kc0 = p0 % T::KCPR;
+  auto kl = [&](int u) {
+    const int kr = kr0 + KRU * u;
+    return (uint32_t)(((kr & 15) * D + T::kchunk(kr, kc0) * 8) * 2);
+  };
+  const int vr0 = p0 / T::VCPR, vsc = T::vchunk(vr0, p0 % T::VCPR), vgrp = vsc >> 1;
+  const uint32_t vl0 = (uint32_t)((vr0 * BK + (vsc & 1) * 8) * 2);
+  auto kgroup = [&](int u) { return (64 * (u * NW + wave)) / (16 * T::KCPR); };
+  // byte offsets (within the head) of K copy u and V^T copy u for a chunk
+  // whose entries are in e (lanes 0..3)
+  auto koff_of = [&](int e, int u) {
+    const int gid = gid_of(__builtin_amdgcn_readlane(e, kgroup(u)));
+    return (uint32_t)gid * (16 * D * 2) + kl(u);
+  };
+  auto vsel = [&](int e) {  // this lane's group: tile and slot offset
+    uint32_t t = 0;
 #pragma unroll
-  for (int u = 0; u < KU; ++u) {
-    const int p = u * NT + threadIdx.x, r = p / T::KCPR;
-    kofs[u] = (uint32_t)(r * D + T::kchunk(r, p % T::KCPR) * 8);
-  }
+    for (int g = 0; g < 4; ++g) {
+      const int gid = gid_of(__builtin_amdgcn_readlane(e, g));
+      const uint32_t tg = (uint32_t)((gid >> 2) * D * BK * 2 + (gid & 3) * 32);
+      t = vgrp == g ? tg : t;
+    }
+    return t + vl0;
+  };
+  auto voff_of = [&](uint32_t vs, int u) { return vs + (uint32_t)(8 * NW * u * BK * 2); };
+  auto stageK = [&](int e, int b) {
 #pragma unroll
-  for (int u = 0; u < VU; ++u) {
-    const int p = u * NT + threadIdx.x, r = p / T::VCPR;
-    vofs[u] = (uint32_t)(r * BK + T::vchunk(r, p % T::VCPR) * 8);
-  }
-  auto issue = [&](int j, int b) {
-    const uint16_t* ks = kp + ((size_t)bh * NKP + (size_t)j * BK) * D;
-    const uint16_t* vs = vtp + ((size_t)bh * (NKP / BK) + j) * (size_t)D * BK;
+    for (int u = 0; u < LOADS; ++u)
+      dma16(kh + koff_of(e, u), kbuf + b * T::BYTES + 1024 * (u * NW + wave));
+  };
+  auto stageV = [&](int e, int b) {
+    const uint32_t vs = vsel(e);
 #pragma unroll
-    for (int u = 0; u < KU; ++u) dma16(ks + kofs[u], smem + b * T::BYTES + (u * NT + wave * 64) * 16);
+    for (int u = 0; u < LOADS; ++u)
+      dma16(vh + voff_of(vs, u), vbuf + b * T::BYTES + 1024 * (u * NW + wave));
+  };
+
+  int koff[KSTEPS];
 #pragma unroll
-    for (int u = 0; u < VU; ++u)
-      dma16(vs + vofs[u], smem + (2 + b) * T::BYTES + (u * NT + wave * 64) * 16);
+  for (int s = 0; s < KSTEPS; ++s) koff[s] = l32 * T::KROWB + (T::kchunk(l32, 2 * s + h2) << 4);
+  int voff[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) voff[g] = l32 * T::VROWB + (T::vchunk(l32, 2 * g + h2) << 4);
+
+  // k-steps [S0, S1) of S^T = K Q^T from the K tile at kb
+  auto qk = [&](const unsigned char* kb, floatx16(&st)[2], int S0, int S1, auto&& hook) {
+    bf16x8 ka[2] = {lds_read16(kb + koff[S0]), lds_read16(kb + 32 * T::KROWB + koff[S0])};
+#pragma unroll
+    for (int s = S0; s < S1; ++s) {
+      hook(s - S0);
+      bf16x8 kn[2];
+      if (s + 1 < S1) {
+        kn[0] = lds_read16(kb + koff[s + 1]);
+        kn[1] = lds_read16(kb + 32 * T::KROWB + koff[s + 1]);
+      }
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau)
+        st[tau] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[tau], qf[s], st[tau], 0, 0, 0);
+      if (s + 1 < S1) { ka[0] = kn[0]; ka[1] = kn[1]; }
+    }
   };
 
   floatx16 oacc[DT];
@@ -438,70 +562,131 @@ __global__ __launch_bounds__(BQ * 2, 2) void svg2_attn_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[i][r] = 0.0f;
   float m = -INFINITY, lsum = 0.0f;
-  if (count > 0) issue(ids[0], 0);
-  for (int e = 0; e < count; ++e) {
-    const int j = ids[e];
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of chunk e landed
-    __syncthreads();                     // all copies landed; the other buffers are free
-    if (e + 1 < count) issue(ids[e + 1], (e + 1) & 1);
-    const unsigned char* kt = smem + (e & 1) * T::BYTES;
-    const unsigned char* vt = smem + (2 + (e & 1)) * T::BYTES;
-    floatx16 S[2];
+  // An S^T accumulator starts at 0 for the chunk's valid keys and at -inf for
+  // the keys past their group's valid count, so the product leaves those at
+  // -inf (the K rows are finite): the mask costs what zeroing costs.
+  auto init_s = [&](floatx16(&st)[2], int e) {
+    int val[4];
 #pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) S[tau][r] = 0.0f;
-      const int kr = 32 * tau + l32;
-#pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
-        const bf16x8 a = lds_read16(kt + kr * T::KROWB + T::kchunk(kr, 2 * s + h2) * 16);
-        S[tau] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], S[tau], 0, 0, 0);
-      }
-    }
-    const int nvalid = chunk_valid[(size_t)bh * max_chunks + j];
-    float mloc = -INFINITY;
+    for (int g = 0; g < 4; ++g) val[g] = __builtin_amdgcn_readlane(e, g) & 31;
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = 32 * tau + 8 * (r >> 2) + 4 * h2 + (r & 3);
-        if (key >= nvalid) S[tau][r] = -INFINITY;
-        mloc = fmaxf(mloc, S[tau][r]);
+        const int g = 2 * tau + (r >> 3);
+        const int within = 8 * ((r >> 2) & 1) + 4 * h2 + (r & 3);
+        st[tau][r] = within < val[g] ? 0.0f : -INFINITY;
       }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m, mloc);
-    if (__any(m_new > m)) {
-      const float f = m_new > m ? __builtin_amdgcn_exp2f((m - m_new) * c) : 1.0f;
-      lsum *= f;
+  };
+  floatx16 sc[2], sn[2];  // S^T of the current and the next chunk
+  // entries of chunks it, it+1, it+2 (and it+3 in flight)
+  int e0 = load_ent(0), e1 = load_ent(1), e2 = load_ent(2);
+  init_s(sc, e0);
+  if (count > 0) {
+    stageK(e0, 0);
+    stageV(e0, 0);
+    if (count > 1) stageK(e1, 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    qk(kbuf, sc, 0, KSTEPS, [](int) {});
+  }
+
+  // one chunk: softmax and P V of chunk it (S^T in sc), and with NEXT the
+  // S^T of chunk it+1 into sn, interleaved with the copies for later steps
+  auto step = [&](int it, auto next_tag, floatx16(&sc)[2], floatx16(&sn)[2]) {
+    constexpr bool NEXT = decltype(next_tag)::value;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K of it+1, V^T of it, entries landed
+    __syncthreads();                     // and every wave is done with step it-1's buffers
+    const int e3 = load_ent(it + 3);
+    unsigned char* kdst = kbuf + (it & 1) * T::BYTES;         // K of chunk it+2
+    unsigned char* vdst = vbuf + ((it + 1) & 1) * T::BYTES;   // V^T of chunk it+1
+    const int ek = it + 2 < count ? e2 : e1;  // a repeat of it+1 when there is none (not read)
+    uint32_t vs = 0;
+    if constexpr (NEXT) vs = vsel(e1);
+    auto kdma = [&](int sl) {
 #pragma unroll
-      for (int i = 0; i < DT; ++i)
+      for (int u = 0; u < LOADS; ++u)
+        if (u * HALF / LOADS == sl) dma16(kh + koff_of(ek, u), kdst + 1024 * (u * NW + wave));
+    };
+    auto vdma = [&](int sl) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[i][r] *= f;
-      m = m_new;
-    }
-    const float mc = m * c;
+      for (int u = 0; u < LOADS; ++u)
+        if (u * HALF / LOADS == sl) dma16(vh + voff_of(vs, u), vdst + 1024 * (u * NW + wave));
+    };
+    const unsigned char* kn = kbuf + ((it + 1) & 1) * T::BYTES;
+    const unsigned char* vb = vbuf + (it & 1) * T::BYTES;
+    {
+      if constexpr (NEXT) {
+        init_s(sn, e1);
+        qk(kn, sn, 0, HALF, kdma);
+      }
+
+      float mloc = -INFINITY;
 #pragma unroll
-    for (int tau = 0; tau < 2; ++tau)
+      for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) S[tau][r] = __builtin_amdgcn_exp2f(fmaf(S[tau][r], c, -mc));
+        for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sc[tau][r]);
+      mloc = pair_max(mloc);
+      if (__any((mloc - m) * c > kRescale)) {
+        const float m_new = fmaxf(m, mloc);
+        const float alpha_r = m_new > -INFINITY ? __builtin_amdgcn_exp2f((m - m_new) * c) : 1.0f;
+        m = m_new;
+        lsum *= alpha_r;
 #pragma unroll
-    for (int tau = 0; tau < 2; ++tau)
+        for (int i = 0; i < DT; ++i)
 #pragma unroll
-      for (int hk = 0; hk < 2; ++hk) {
-        const bf16x8 pb = pack_bf16x8(S[tau], 8 * hk);
+          for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha_r;
+      }
+
+      if constexpr (NEXT) qk(kn, sn, HALF, KSTEPS, vdma);
+      // a row with no valid key yet (m = -inf) gives P = 0
+      const float mc = m > -INFINITY ? m * c : 0.0f;
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[tau][r] = __builtin_amdgcn_exp2f(fmaf(sc[tau][r], c, -mc));
+
+      bf16x8 va[DT];
+#pragma unroll
+      for (int i = 0; i < DT; ++i) va[i] = lds_read16(vb + i * 32 * T::VROWB + voff[0]);
+#pragma unroll
+      for (int G = 0; G < 4; ++G) {
+        const int tau = G >> 1, hk = G & 1;
+        const bf16x8 pb = pack_bf16x8(sc[tau], 8 * hk);
         lsum = row_sum_bf16x8(pb, lsum);
-        const int ch = 4 * tau + 2 * hk + h2;
+        bf16x8 vn[DT];
+        if (G + 1 < 4) {
 #pragma unroll
-        for (int i = 0; i < DT; ++i) {
-          const int row = 32 * i + l32;
-          const bf16x8 a = lds_read16(vt + row * T::VROWB + T::vchunk(row, ch) * 16);
-          oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[i], 0, 0, 0);
+          for (int i = 0; i < DT; ++i) vn[i] = lds_read16(vb + i * 32 * T::VROWB + voff[G + 1]);
+        }
+#pragma unroll
+        for (int i = 0; i < DT; ++i)
+          oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], pb, oacc[i], 0, 0, 0);
+        if (G + 1 < 4) {
+#pragma unroll
+          for (int i = 0; i < DT; ++i) va[i] = vn[i];
         }
       }
+    }
+    e0 = e1;
+    e1 = e2;
+    e2 = e3;
+  };
+  int it = 0;
+  for (; it + 2 < count; it += 2) {
+    step(it, std::true_type{}, sc, sn);
+    step(it + 1, std::true_type{}, sn, sc);
   }
-  const float ltot = lsum + __shfl_xor(lsum, 32);
+  if (it + 1 < count) {
+    step(it, std::true_type{}, sc, sn);
+    step(it + 1, std::false_type{}, sn, sc);
+  } else if (it < count) {
+    step(it, std::false_type{}, sc, sn);
+  }
+
+  const float ltot = pair_sum(lsum);
   const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
-  if (valid) {
+  if (local < qsz) {
     const int tok = perm_q[(size_t)bh * N + off_q[(size_t)bh * (Cq + 1) + cq] + local];
     uint16_t* orow = o + ((size_t)bh * N + tok) * D;
 #pragma unroll
@@ -515,6 +700,33 @@ __global__ __launch_bounds__(BQ * 2, 2) void svg2_attn_kernel(
         *reinterpret_cast<uint2*>(orow + d0) = pk;
       }
   }
+}
+
+// Token pairs per (b, h): useful = sum over query clusters of |cluster| times
+// the tokens of its kept key clusters; computed = the pairs the attention
+// kernel evaluates, BQ rows per query tile times 64 keys per listed chunk.
+__global__ __launch_bounds__(256) void svg2_pairs_kernel(
+    const int32_t* __restrict__ sidx, const int32_t* __restrict__ scnt,
+    const int32_t* __restrict__ size_q, const int32_t* __restrict__ size_k,
+    const int32_t* __restrict__ list_cnt, unsigned long long* __restrict__ counts, int Cq,
+    int Ck, int BQ) {
+  __shared__ unsigned long long acc[2];
+  const int bh = blockIdx.x;
+  if (threadIdx.x < 2) acc[threadIdx.x] = 0ull;
+  __syncthreads();
+  unsigned long long useful = 0, computed = 0;
+  for (int cq = threadIdx.x; cq < Cq; cq += 256) {
+    const size_t row = (size_t)bh * Cq + cq;
+    const long long nq = size_q[row];
+    long long keys = 0;
+    for (int e = 0; e < scnt[row]; ++e) keys += size_k[(size_t)bh * Ck + sidx[row * Ck + e]];
+    useful += (unsigned long long)(nq * keys);
+    computed += (unsigned long long)(BQ * ((nq + BQ - 1) / BQ)) * 64ull * (unsigned)list_cnt[row];
+  }
+  atomicAdd(&acc[0], useful);
+  atomicAdd(&acc[1], computed);
+  __syncthreads();
+  if (threadIdx.x < 2) counts[2 * (size_t)bh + threadIdx.x] = acc[threadIdx.x];
 }
 
 // --------------------------------------------------------------- driver
@@ -546,6 +758,14 @@ hipError_t kmeans_run(const Svg2Launch& a, const double* x, int C, double* cent,
 template <int D, int BQ>
 hipError_t launch_svg2_t(const Svg2Launch& a, hipStream_t s) {
   const int BH = a.B * a.H;
+  const int NQP = a.max_tiles * BQ, NKP = a.n_ktiles * BK;
+  if (a.phase == kSvg2Attend) {
+    hipLaunchKernelGGL((svg2_attn_kernel<D, BQ>), dim3(BH * a.max_tiles), dim3(BQ * 2), 0, s, a.qp,
+                       a.kp, a.vtp, a.tile_cluster, a.n_tiles, a.lists, a.list_cnt, a.perm_q,
+                       a.off_q, a.size_q, a.qpad_off, a.o, a.N, NQP, NKP, a.Cq, a.max_tiles,
+                       a.max_list, a.n_ktiles, a.scale * 1.4426950408889634f);
+    return hipGetLastError();
+  }
   const size_t n = (size_t)BH * a.N * D;
   hipLaunchKernelGGL(to_f64_kernel, dim3(4096), dim3(256), 0, s, a.q, a.xq, n);
   hipLaunchKernelGGL(to_f64_kernel, dim3(4096), dim3(256), 0, s, a.k, a.xk, n);
@@ -575,27 +795,27 @@ hipError_t launch_svg2_t(const Svg2Launch& a, hipStream_t s) {
   m.cnt = a.scnt;
   e = launch_select_rows(m, s);
   if (e != hipSuccess) return e;
-  // padded layouts, chunk lists, gathers
-  hipLaunchKernelGGL(svg2_layout_kernel, dim3(BH), dim3(64), 0, s, a.size_q, a.size_k,
-                     a.qpad_off, a.kpad_off, a.tile_cluster, a.chunk_valid, a.n_tiles, a.Cq, a.Ck,
-                     BQ, a.max_tiles, a.max_chunks);
+  // padded layouts, group lists, gathers
+  hipLaunchKernelGGL(svg2_layout_kernel, dim3(BH), dim3(256), 0, s, a.size_q, a.size_k,
+                     a.qpad_off, a.kpad_off, a.tile_cluster, a.n_tiles, a.Cq, a.Ck, BQ,
+                     a.max_tiles);
   const size_t lrows = (size_t)BH * a.Cq;
   hipLaunchKernelGGL(svg2_lists_kernel, dim3((unsigned)((lrows + 3) / 4)), dim3(256), 0, s, a.sidx,
-                     a.scnt, a.kpad_off, a.size_k, a.lists, a.list_cnt, a.Cq, a.Ck, a.max_chunks,
+                     a.scnt, a.kpad_off, a.size_k, a.lists, a.list_cnt, a.Cq, a.Ck, a.max_list,
                      lrows);
-  const int NQP = a.max_tiles * BQ, NKP = a.max_chunks * BK;
   hipLaunchKernelGGL((svg2_gather_kernel<D>), dim3(a.Cq, BH), dim3(256), 0, s, a.q, a.perm_q,
                      a.off_q, a.size_q, a.qpad_off, a.qp, a.N, a.Cq, BQ, NQP);
   hipLaunchKernelGGL((svg2_gather_kernel<D>), dim3(a.Ck, BH), dim3(256), 0, s, a.k, a.perm_k,
-                     a.off_k, a.size_k, a.kpad_off, a.kp, a.N, a.Ck, BK, NKP);
+                     a.off_k, a.size_k, a.kpad_off, a.kp, a.N, a.Ck, 16, NKP);
   hipLaunchKernelGGL((svg2_gather_kernel<D>), dim3(a.Ck, BH), dim3(256), 0, s, a.v, a.perm_k,
-                     a.off_k, a.size_k, a.kpad_off, a.vp, a.N, a.Ck, BK, NKP);
-  hipLaunchKernelGGL((pack_kernel<D, false>), dim3(a.max_chunks, BH), dim3(2 * D), 0, s, a.vp,
-                     nullptr, a.vtp, nullptr, NKP, a.max_chunks, nullptr, a.H);
+                     a.off_k, a.size_k, a.kpad_off, a.vp, a.N, a.Ck, 16, NKP);
+  hipLaunchKernelGGL((pack_kernel<D, false>), dim3(a.n_ktiles, BH), dim3(2 * D), 0, s, a.vp,
+                     nullptr, a.vtp, nullptr, NKP, a.n_ktiles, nullptr, a.H);
+  if (a.phase == kSvg2Cluster) return hipGetLastError();
   hipLaunchKernelGGL((svg2_attn_kernel<D, BQ>), dim3(BH * a.max_tiles), dim3(BQ * 2), 0, s, a.qp,
-                     a.kp, a.vtp, a.chunk_valid, a.tile_cluster, a.n_tiles, a.lists, a.list_cnt,
-                     a.perm_q, a.off_q, a.size_q, a.qpad_off, a.o, a.N, NQP, NKP, a.Cq,
-                     a.max_tiles, a.max_chunks, a.scale * 1.4426950408889634f);
+                     a.kp, a.vtp, a.tile_cluster, a.n_tiles, a.lists, a.list_cnt, a.perm_q,
+                     a.off_q, a.size_q, a.qpad_off, a.o, a.N, NQP, NKP, a.Cq, a.max_tiles,
+                     a.max_list, a.n_ktiles, a.scale * 1.4426950408889634f);
   return hipGetLastError();
 }
 
@@ -611,8 +831,10 @@ size_t svg2_layout(Svg2Launch& a, unsigned char* w) {
   const size_t BH = (size_t)a.B * a.H, N = a.N, d = a.d, nch = (N + 63) / 64;
   const size_t Cm = (size_t)std::max(a.Cq, a.Ck);
   a.max_tiles = (int)((N + a.block_q - 1) / a.block_q + a.Cq);
-  a.max_chunks = (int)(nch + a.Ck);
-  const size_t NQP = (size_t)a.max_tiles * a.block_q, NKP = (size_t)a.max_chunks * BK;
+  a.max_groups = (int)((N + 15) / 16 + a.Ck);
+  a.n_ktiles = (a.max_groups + 3) / 4;
+  a.max_list = 4 * a.n_ktiles;
+  const size_t NQP = (size_t)a.max_tiles * a.block_q, NKP = (size_t)a.n_ktiles * BK;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     unsigned char* p = w ? w + off : nullptr;
@@ -642,15 +864,20 @@ size_t svg2_layout(Svg2Launch& a, unsigned char* w) {
   a.qpad_off = reinterpret_cast<int32_t*>(take(BH * a.Cq * 4));
   a.kpad_off = reinterpret_cast<int32_t*>(take(BH * a.Ck * 4));
   a.tile_cluster = reinterpret_cast<int32_t*>(take(BH * a.max_tiles * 4));
-  a.chunk_valid = reinterpret_cast<int32_t*>(take(BH * a.max_chunks * 4));
   a.n_tiles = reinterpret_cast<int32_t*>(take(BH * 4));
-  a.lists = reinterpret_cast<int32_t*>(take(BH * a.Cq * a.max_chunks * 4));
+  a.lists = reinterpret_cast<int32_t*>(take(BH * a.Cq * a.max_list * 4));
   a.list_cnt = reinterpret_cast<int32_t*>(take(BH * a.Cq * 4));
   a.qp = reinterpret_cast<uint16_t*>(take(BH * NQP * d * 2));
   a.kp = reinterpret_cast<uint16_t*>(take(BH * NKP * d * 2));
   a.vp = reinterpret_cast<uint16_t*>(take(BH * NKP * d * 2));
   a.vtp = reinterpret_cast<uint16_t*>(take(BH * NKP * d * 2));
   return off;
+}
+
+hipError_t launch_svg2_pairs(const Svg2Launch& a, unsigned long long* counts, hipStream_t s) {
+  hipLaunchKernelGGL(svg2_pairs_kernel, dim3(a.B * a.H), dim3(256), 0, s, a.sidx, a.scnt,
+                     a.size_q, a.size_k, a.list_cnt, counts, a.Cq, a.Ck, a.block_q);
+  return hipGetLastError();
 }
 
 hipError_t launch_svg2(const Svg2Launch& a, hipStream_t s) {

@@ -418,12 +418,36 @@ size_t svg2_attn_workspace_bytes(int B, int H, int N, int d, int block_q, int n_
  * is the query tile of the attention step; at most 4096 key clusters. The
  * workspace (256-byte aligned) holds every intermediate: the float64 copies
  * of Q and K the clustering reads, the centroids, assignments, counting-sort
- * counts and permutations, the centroid scores and selection, and Q, K, V and
- * the packed V^T gathered into cluster-contiguous, tile-padded order
- * (svg2_attn_workspace_bytes gives the total). */
+ * counts and permutations, the centroid scores and selection, the group
+ * lists, and Q, K, V and the packed V^T gathered into cluster-contiguous
+ * order (query clusters padded to whole block_q tiles, key clusters only to
+ * whole 16-key groups; svg2_attn_workspace_bytes gives the total). */
 int svg2_attn_fwd(const void* q, const void* k, const void* v, int B, int H, int N, int d,
                   int block_q, int n_q_clusters, int n_k_clusters, int iters, float p_mass,
                   float scale, void* o, void* workspace, size_t workspace_bytes, void* stream);
+
+/* svg2_attn_fwd in two parts: svg2_attn_cluster takes steps 1-3 and gathers
+ * Q, K, V into the workspace (o is not touched); svg2_attn_apply then runs
+ * step 4 from the workspace alone (reads no q, k, v) and writes o. Enqueued
+ * in that order on one stream with the same shapes, cluster counts and
+ * workspace, they give exactly svg2_attn_fwd's output; svg2_attn_apply may
+ * be repeated. Arguments and errors as for svg2_attn_fwd. */
+int svg2_attn_cluster(const void* q, const void* k, const void* v, int B, int H, int N, int d,
+                      int block_q, int n_q_clusters, int n_k_clusters, int iters, float p_mass,
+                      float scale, void* workspace, size_t workspace_bytes, void* stream);
+int svg2_attn_apply(int B, int H, int N, int d, int block_q, int n_q_clusters, int n_k_clusters,
+                    float scale, void* o, void* workspace, size_t workspace_bytes, void* stream);
+
+/* After an svg2_attn_fwd call on this stream, with the same arguments and its
+ * workspace untouched since: per (b, h), counts[2 (b H + h)] = the query-key
+ * token pairs that take part in the attention (each query with every token of
+ * its cluster's kept key clusters) and counts[2 (b H + h) + 1] = the pairs
+ * the attention kernel evaluates (whole block_q query tiles times whole
+ * 64-key chunks, padding included). counts: uint64 [B, H, 2], device,
+ * 8-byte aligned. For reporting the padding share; reads the workspace only. */
+int svg2_attn_pair_counts(int B, int H, int N, int d, int block_q, int n_q_clusters,
+                          int n_k_clusters, uint64_t* counts, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 /* Device workspace (bytes) of sparse_linear_attn_bwd and sla2_mix_attn_bwd:
  * that of sparge_attn_bwd, plus the linear branch's packed V and phi(K), its

@@ -30,8 +30,14 @@ def test_svg2_small_shapes_in_full(B, H, N, d, bq, Cq, Ck, p):
     Q, K = mk(), mk()
     V = f64_to_bf16_bits(rng.standard_normal((B, H, N, d)))
     print(f"\n[svg2] B={B} H={H} N={N} d={d} bq={bq} Cq={Cq} Ck={Ck} p={p}", flush=True)
-    o = S.svg2_attn_fwd(to_gpu(Q), to_gpu(K), to_gpu(V), Cq, Ck, iters=4, p_mass=p, block_q=bq)
+    q = to_gpu(Q)
+    ws = torch.empty(S.svg2_workspace_bytes(B, H, N, d, bq, Cq, Ck), dtype=torch.uint8,
+                     device="cuda")
+    o = S.svg2_attn_fwd(q, to_gpu(K), to_gpu(V), Cq, Ck, iters=4, p_mass=p, block_q=bq,
+                        out=nan_like(q), workspace=ws)
+    counts = S.svg2_attn_pair_counts(q, Cq, Ck, ws, bq).cpu().numpy()
     torch.cuda.synchronize()
+    assert_all_written(o)
     got = _np(o)
     scale = S.default_scale(d)
     for b in range(B):
@@ -39,8 +45,17 @@ def test_svg2_small_shapes_in_full(B, H, N, d, bq, Cq, Ck, p):
             ref, qa, ka, sel = O.svg2_attention_head(O.bf16_to_f64(Q[b, h]), O.bf16_to_f64(K[b, h]),
                                                      O.bf16_to_f64(V[b, h]), Cq, Ck, 4, scale, p)
             mx, mean = compare_outputs(got[b, h], ref)
+            useful = _useful_pairs(qa, ka, sel, Cq, Ck)
+            assert counts[b, h, 0] == useful and counts[b, h, 1] >= useful
             print(f"[svg2] b={b} h={h}: kept pairs {sel.kept.mean():.3f} max {mx:.2e} "
-                  f"mean {mean:.2e}", flush=True)
+                  f"mean {mean:.2e} useful/computed {useful / counts[b, h, 1]:.3f}", flush=True)
+
+
+def _useful_pairs(qa, ka, sel, Cq, Ck):
+    """Query-key token pairs of the oracle's selection: every query with every
+    token of its cluster's kept key clusters."""
+    qs, ks = np.bincount(qa, minlength=Cq), np.bincount(ka, minlength=Ck)
+    return int((qs[:, None] * ks[None, :] * sel.kept).sum())
 
 
 def test_svg2_on_workload_sampled():
@@ -49,7 +64,11 @@ def test_svg2_on_workload_sampled():
     wl = WORKLOADS["wan1.3b"]
     Q, K, V = generate(wl)
     q = to_gpu(Q)
-    o = S.svg2_attn_fwd(q, to_gpu(K), to_gpu(V), 256, 512, iters=3, p_mass=0.9, out=nan_like(q))
+    ws = torch.empty(S.svg2_workspace_bytes(wl.B, wl.H, wl.N, wl.d, 128, 256, 512),
+                     dtype=torch.uint8, device="cuda")
+    o = S.svg2_attn_fwd(q, to_gpu(K), to_gpu(V), 256, 512, iters=3, p_mass=0.9, out=nan_like(q),
+                        workspace=ws)
+    counts = S.svg2_attn_pair_counts(q, 256, 512, ws).cpu().numpy()
     torch.cuda.synchronize()
     assert_all_written(o)
     got = _np(o)
@@ -62,5 +81,29 @@ def test_svg2_on_workload_sampled():
         mx, mean = compare_outputs(got[0, h][rows], ref)
         sizes = np.bincount(ka, minlength=512)
         density = (sel.kept[qa] * sizes[None]).sum() / (wl.N * wl.N)
+        useful = _useful_pairs(qa, ka, sel, 256, 512)
+        assert counts[0, h, 0] == useful and counts[0, h, 1] >= useful
         print(f"\n[svg2 workload] h={h}: token density {density:.3f} max {mx:.2e} "
-              f"mean {mean:.2e}", flush=True)
+              f"mean {mean:.2e} useful/computed {useful / counts[0, h, 1]:.3f}", flush=True)
+
+
+@pytest.mark.parametrize("name,B,H,N,d,bq,Cq,Ck", [("small", 1, 2, 1000, 128, 128, 8, 16),
+                                                  ("small", 2, 1, 777, 64, 64, 5, 12),
+                                                  ("wan1.3b", 1, 12, 32760, 128, 128, 256, 512)])
+def test_svg2_in_two_parts_equals_one_call(name, B, H, N, d, bq, Cq, Ck):
+    """svg2_attn_cluster then svg2_attn_apply (twice) give exactly svg2_attn_fwd."""
+    if name == "wan1.3b":
+        Q, K, V = generate(WORKLOADS["wan1.3b"])
+    else:
+        rng = np.random.default_rng(N + Ck)
+        Q, K, V = (f64_to_bf16_bits(rng.standard_normal((B, H, N, d))) for _ in range(3))
+    q, k, v = to_gpu(Q), to_gpu(K), to_gpu(V)
+    print(f"\n[svg2 parts] {name} B={B} H={H} N={N} d={d} bq={bq} Cq={Cq} Ck={Ck}", flush=True)
+    one = S.svg2_attn_fwd(q, k, v, Cq, Ck, iters=3, p_mass=0.9, block_q=bq, out=nan_like(q))
+    ws = S.svg2_attn_cluster(q, k, v, Cq, Ck, iters=3, p_mass=0.9, block_q=bq)
+    a = S.svg2_attn_apply(q, Cq, Ck, ws, bq, out=nan_like(q))
+    b = S.svg2_attn_apply(q, Cq, Ck, ws, bq, out=nan_like(q))
+    torch.cuda.synchronize()
+    assert_all_written(one)
+    assert torch.equal(a.view(torch.int16), one.view(torch.int16))
+    assert torch.equal(b.view(torch.int16), one.view(torch.int16))
