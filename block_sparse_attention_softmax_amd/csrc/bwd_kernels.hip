@@ -15,6 +15,9 @@
 //    computed with one key per lane (lane % 32) so that P and dS, converted
 //    to bf16, feed the second products as B operands unchanged, against
 //    dO^T and Q^T taken from the staged Q and dO rows by transposing reads.
+//    d = 64 uses 4 waves; d = 128 uses 8 (two per SIMD), with V staged in
+//    LDS so that a wave's registers hold only its K row beside the
+//    accumulators.
 //  * dQ: one workgroup per (b, h, query block), the forward's loop over the
 //    row's list: S^T = K Q^T and dP^T = V dO^T with one query per lane, then
 //    dQ^T += K^T dS^T against K^T packed like V^T.
@@ -460,6 +463,228 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void sparse_attn_bwd_dkdv_ke
           const int r = 4 * gg + e2;
           yk[e2] = scale * (dka[ii][r] + red[(((kh * 2 + 0) * DT + ii) * 16 + r) * 64 + lane]);
           yv[e2] = dva[ii][r] + red[(((kh * 2 + 1) * DT + ii) * 16 + r) * 64 + lane];
+        }
+        const int d0 = 32 * ii + 8 * gg + 4 * h2;
+        if (lin_dk) {  // the linear branch's share, float32
+          const float4 lk = *reinterpret_cast<const float4*>(lin_dk + head + (size_t)key * D + d0);
+          const float4 lv = *reinterpret_cast<const float4*>(lin_dv + head + (size_t)key * D + d0);
+          yk[0] += lk.x; yk[1] += lk.y; yk[2] += lk.z; yk[3] += lk.w;
+          yv[0] += lv.x; yv[1] += lv.y; yv[2] += lv.z; yv[3] += lv.w;
+        }
+        uint2 pk;
+        pk.x = pack2_bf16(yk[0], yk[1]);
+        pk.y = pack2_bf16(yk[2], yk[3]);
+        *reinterpret_cast<uint2*>(krow_p + d0) = pk;
+        pk.x = pack2_bf16(yv[0], yv[1]);
+        pk.y = pack2_bf16(yv[2], yv[3]);
+        *reinterpret_cast<uint2*>(vrow_p + d0) = pk;
+      }
+  }
+}
+
+// d = 128: 8 waves, two per SIMD. Holding a key row of both K and V in
+// registers (64 VGPRs) beside the 128 of the dK, dV accumulators leaves too
+// little for two waves per SIMD, so V of the block is staged in LDS once and
+// each wave keeps only its K row. Wave w holds keys 32 (w & 1) .. +31 and
+// rows 32 (w >> 1) .. +31 of each 128-row stage. A stage is two 64-row
+// segments: the halves of one listed query block (block_q = 128) or two
+// consecutive listed blocks (block_q = 64); when the list leaves an odd
+// segment count, the last stage's second segment is copied but not computed.
+// The four row quarters are summed at the end in two rounds through LDS.
+template <int BQ>
+__global__ __launch_bounds__(512, 1) void sparse_attn_bwd_dkdv8_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dO,
+    const float* __restrict__ lse2, const float* __restrict__ drow,
+    const int32_t* __restrict__ coloff, const int32_t* __restrict__ collist,
+    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int N, int n_q, int n_k, int total,
+    float c, float scale, const float* __restrict__ lin_dk, const float* __restrict__ lin_dv) {
+  constexpr int D = 128, SB = 128, SEG = 64, SPB = BQ / SEG;
+  using RT = RowTile<D>;
+  using ST = DkdvStage<D, SB>;
+  constexpr int DT = D / 32, KSTEPS = D / 16;
+  constexpr int CU = SB * RT::CPR / 512;  // 16-byte copies per thread and tensor
+  constexpr int VB = BK * RT::ROWB;       // the block's V rows
+  static_assert(CU == 4 && BQ % SEG == 0, "copy split");
+  __shared__ __align__(16) unsigned char smem[2 * ST::BYTES + VB];
+  unsigned char* const vt = smem + 2 * ST::BYTES;
+
+  const int tile = xcd_remap(blockIdx.x, total);
+  const int bh = tile / n_k, j = tile % n_k;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // copy bases are uniform
+  const int h2 = lane >> 5, l32 = lane & 31, kw = 32 * (wave & 1), qq = wave >> 1;
+  const size_t head = (size_t)bh * N * D;
+  const int NP = n_q * BQ;
+  const int key = j * BK + kw + l32;
+
+  bf16x8 kf[KSTEPS];  // this lane's key row (zero past N)
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) {
+    kf[s] = bf16x8{};
+    if (key < N) kf[s] = *reinterpret_cast<const bf16x8*>(k + head + (size_t)key * D + 16 * s + 8 * h2);
+  }
+  // V rows of the block, swizzled like the stage rows (rows past N read row N - 1)
+#pragma unroll
+  for (int u = 0; u < BK * RT::CPR / 512; ++u) {
+    const int p = u * 512 + threadIdx.x, r = p / RT::CPR, ch = p % RT::CPR;
+    const int row = min(j * BK + r, N - 1);
+    *reinterpret_cast<bf16x8*>(vt + r * RT::ROWB + RT::chunk(r, ch) * 16) =
+        *reinterpret_cast<const bf16x8*>(v + head + (size_t)row * D + ch * 8);
+  }
+  floatx16 dka[DT], dva[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dka[i][r] = dva[i][r] = 0.0f;
+
+  const int e_l = (lane >> 2) & 3, m_l = lane & 3, g1 = (lane >> 4) & 1;
+  const int tr_swz = (e_l << 2) | h2;
+  const int tr_lane = (2 * g1 + (m_l >> 1)) ^ tr_swz;
+  const uint32_t tr_row = (uint32_t)((4 * h2 + e_l) * RT::ROWB + 8 * (m_l & 1));
+
+  const int beg = coloff[(size_t)bh * (n_k + 1) + j], end = coloff[(size_t)bh * (n_k + 1) + j + 1];
+  const int32_t* lst = collist + (size_t)bh * n_q * n_k;
+  const int nseg = (end - beg) * SPB, stages = (nseg + 1) / 2;
+  auto seg_row = [&](int g) {  // first query row of segment g
+    return min(max(lst[beg + g / SPB], 0), n_q - 1) * BQ + (g % SPB) * SEG;
+  };
+  auto issue = [&](int t, unsigned char* buf) {  // the two segments of stage t
+    const int ra = seg_row(2 * t), rb = 2 * t + 1 < nseg ? seg_row(2 * t + 1) : ra;
+#pragma unroll
+    for (int u = 0; u < CU; ++u) {
+      const int p = u * 512 + threadIdx.x, r = p / RT::CPR;  // r / 64 == u / 2
+      const int r0 = u < CU / 2 ? ra : rb, rr = r % SEG;
+      const uint32_t back = (uint32_t)max(r0 + rr - (N - 1), 0) * D;  // rows past N
+      const uint32_t ofs = (uint32_t)(rr * D + RT::chunk(r, p % RT::CPR) * 8);
+      unsigned char* dst = buf + (u * 512 + wave * 64) * 16;
+      dma16(q + head + (size_t)r0 * D + ofs - back, dst + ST::QS);
+      dma16(dO + head + (size_t)r0 * D + ofs - back, dst + ST::DS);
+    }
+    if (wave < 4) {  // lse2 (waves 0, 1) and D (waves 2, 3), one segment each
+      const int sg = wave & 1;
+      const float* src = (wave < 2 ? lse2 : drow) + (size_t)bh * NP + (sg ? rb : ra) + lane;
+      dma4(src, buf + (wave < 2 ? ST::LS : ST::DD) + 256 * sg);
+    }
+  };
+
+  if (stages > 0) issue(0, smem);
+  for (int t = 0; t < stages; ++t) {
+    unsigned char* const buf = smem + (t & 1) * ST::BYTES;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of the stage landed
+    __syncthreads();                     // every wave's copies landed, the other buffer is free
+    if (t + 1 < stages) issue(t + 1, smem + ((t + 1) & 1) * ST::BYTES);
+    if (2 * t + (qq >> 1) >= nseg) continue;  // an uncomputed trailing segment
+    const uint32_t bufa = lds_addr(buf) + tr_row;
+    const int qb = 32 * qq, qr = qb + l32, vr = kw + l32;
+
+    // S = Q K^T and dP = dO V^T for the wave's 32 rows x 32 keys
+    floatx16 S, dP;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) S[r] = dP[r] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      const int ch = RT::chunk(qr, 2 * s + h2);
+      const bf16x8 fa = lds_read16(buf + ST::QS + qr * RT::ROWB + ch * 16);
+      const bf16x8 fb = lds_read16(buf + ST::DS + qr * RT::ROWB + ch * 16);
+      const bf16x8 vb = lds_read16(vt + vr * RT::ROWB + RT::chunk(vr, 2 * s + h2) * 16);
+      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, kf[s], S, 0, 0, 0);
+      dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb, vb, dP, 0, 0, 0);
+    }
+    // P = 2^(S c - lse2), dS = P (dP - D); register r holds stage row
+    // qb + 8*(r/4) + 4*h2 + r%4
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg) {
+      const int t0 = qb + 8 * gg + 4 * h2;
+      const float4 l4 = __builtin_bit_cast(float4, lds_read16(buf + ST::LS + 4 * t0));
+      const float4 d4 = __builtin_bit_cast(float4, lds_read16(buf + ST::DD + 4 * t0));
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const int r = 4 * gg + e2;
+        const float p = __builtin_amdgcn_exp2f(fmaf(S[r], c, -lv[e2]));
+        S[r] = p;
+        dP[r] = p * (dP[r] - dv4[e2]);
+      }
+    }
+    // dV^T += dO^T P, dK^T += Q^T dS, in two halves of 16 rows; P and dS
+    // go to bf16 first (their float32 registers are then free), and the
+    // transposed fragments are read two channel groups at a time
+    const bf16x8 pb[2] = {pack_bf16x8(S, 0), pack_bf16x8(S, 8)};
+    const bf16x8 sb[2] = {pack_bf16x8(dP, 0), pack_bf16x8(dP, 8)};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int R0 = qb + 16 * h;
+      const int C0 = (R0 >> 2) & 3, C1 = ((R0 + 8) >> 2) & 3;
+#pragma unroll
+      for (int i2 = 0; i2 < DT; i2 += 2) {
+        uint32_t ad[8];
+        v4i16 fr[8];
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const int ii = i2 + x;
+          const uint32_t o0 = (uint32_t)(R0 * RT::ROWB + (((4 * ii + C0) ^ tr_lane) << 4));
+          const uint32_t o1 = (uint32_t)((R0 + 8) * RT::ROWB + (((4 * ii + C1) ^ tr_lane) << 4));
+          ad[4 * x] = bufa + ST::DS + o0;
+          ad[4 * x + 1] = bufa + ST::DS + o1;
+          ad[4 * x + 2] = bufa + ST::QS + o0;
+          ad[4 * x + 3] = bufa + ST::QS + o1;
+        }
+        lds_read_tr<8>(fr, ad);
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const int ii = i2 + x;
+          dva[ii] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join_tr(fr[4 * x], fr[4 * x + 1]),
+                                                            pb[h], dva[ii], 0, 0, 0);
+          dka[ii] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join_tr(fr[4 * x + 2], fr[4 * x + 3]),
+                                                            sb[h], dka[ii], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // sum the four row quarters: quarters 2, 3 into 0, 1, then 1 into 0
+  float* red = reinterpret_cast<float*>(smem);  // [4 waves][2][DT][16][64]
+  static_assert(4 * 2 * DT * 16 * 64 * 4 <= 2 * ST::BYTES, "reduction must fit");
+  const int kh = wave & 1;
+#pragma unroll
+  for (int round = 0; round < 2; ++round) {
+    const int hi = round == 0 ? 2 : 1;  // quarters [hi, 2 hi) hand theirs to [0, hi)
+    __syncthreads();
+    if (qq >= hi && qq < 2 * hi) {
+      const int slot = (qq - hi) * 2 + kh;
+#pragma unroll
+      for (int ii = 0; ii < DT; ++ii)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          red[(((slot * 2 + 0) * DT + ii) * 16 + r) * 64 + lane] = dka[ii][r];
+          red[(((slot * 2 + 1) * DT + ii) * 16 + r) * 64 + lane] = dva[ii][r];
+        }
+    }
+    __syncthreads();
+    if (qq < hi) {
+      const int slot = qq * 2 + kh;
+#pragma unroll
+      for (int ii = 0; ii < DT; ++ii)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          dka[ii][r] += red[(((slot * 2 + 0) * DT + ii) * 16 + r) * 64 + lane];
+          dva[ii][r] += red[(((slot * 2 + 1) * DT + ii) * 16 + r) * 64 + lane];
+        }
+    }
+  }
+  if (qq == 0 && key < N) {
+    uint16_t* krow_p = dk + head + (size_t)key * D;
+    uint16_t* vrow_p = dv + head + (size_t)key * D;
+#pragma unroll
+    for (int ii = 0; ii < DT; ++ii)
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        float yk[4], yv[4];
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          yk[e2] = scale * dka[ii][4 * gg + e2];
+          yv[e2] = dva[ii][4 * gg + e2];
         }
         const int d0 = 32 * ii + 8 * gg + 4 * h2;
         if (lin_dk) {  // the linear branch's share, float32
@@ -1147,9 +1372,14 @@ hipError_t launch_bwd_t(const BwdLaunch& a, hipStream_t s) {
                          w.lin_on, w.dkl, w.dvl, a.H, a.N, a.n_q, a.n_k, cols);
     }
   }
-  hipLaunchKernelGGL((sparse_attn_bwd_dkdv_kernel<D, BQ>), dim3(cols), dim3(256), 0, s, a.q, a.k,
-                     a.v, dos, w.lse2, w.drow, w.coloff, w.collist, a.dk, a.dv, a.N, a.n_q,
-                     a.n_k, cols, c, a.scale, linear ? w.dkl : nullptr, linear ? w.dvl : nullptr);
+  if constexpr (D == 128)
+    hipLaunchKernelGGL((sparse_attn_bwd_dkdv8_kernel<BQ>), dim3(cols), dim3(512), 0, s, a.q, a.k,
+                       a.v, dos, w.lse2, w.drow, w.coloff, w.collist, a.dk, a.dv, a.N, a.n_q,
+                       a.n_k, cols, c, a.scale, linear ? w.dkl : nullptr, linear ? w.dvl : nullptr);
+  else
+    hipLaunchKernelGGL((sparse_attn_bwd_dkdv_kernel<D, BQ>), dim3(cols), dim3(256), 0, s, a.q,
+                       a.k, a.v, dos, w.lse2, w.drow, w.coloff, w.collist, a.dk, a.dv, a.N, a.n_q,
+                       a.n_k, cols, c, a.scale, linear ? w.dkl : nullptr, linear ? w.dvl : nullptr);
   hipLaunchKernelGGL((sparse_attn_bwd_dq_kernel<D, BQ>), dim3(qrows), dim3(BQ * 2), 0, s, a.q,
                      a.k, a.v, dos, w.kt, w.lse2, w.drow, a.idx, a.cnt, a.dq, a.N, a.n_q,
                      a.n_k, qrows, c, a.scale, linear ? w.dql : nullptr);
