@@ -63,6 +63,14 @@ def measured_traffic():
         return None
 
 
+_T0 = time.perf_counter()
+
+
+def progress(phase: str):
+    """One line on stderr as each part of the run ends (the JSON line stays alone on stdout)."""
+    print(f"bench: {phase} done at {time.perf_counter() - _T0:.0f} s", file=sys.stderr, flush=True)
+
+
 def dist(ms) -> dict:
     """Median, 10th and 90th percentile of a list of times (ms)."""
     a = np.asarray(ms, dtype=np.float64)
@@ -516,6 +524,8 @@ def main():
                           "attn_frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}), flush=True)
         return
 
+    progress("headline step")
+
     # measured ceilings beside the nameplate figures: dense bf16 MFMA (a probe
     # kernel of independent 32x32x16 chains) and HBM (a 1 GiB device copy)
     ceilings = measure_ceilings(torch, dev)
@@ -545,6 +555,8 @@ def main():
             "flops_per_launch": kf2, "cold": r2["cold"]}
         checks.append(gpu_sample(f"wan1.3b p=0 k={kfrac}", wl, kfrac, 0.0, bits, o))
 
+    progress("ceilings and operating points")
+
     # the sparse-linear workload: same inputs and mask, plus alpha = 0.1 elu+1 linear branch
     n_lin = max(5, args.steps // 4)
     r3 = timed(wl.k_frac, wl.p_mass, n_lin, 2, linear="add", alpha_t=alpha)
@@ -555,6 +567,8 @@ def main():
               "dense_equiv_tflops": round(dense / w3 / 1e12, 2)}
     checks.append(gpu_sample("wan1.3b_linear", WORKLOADS["wan1.3b_linear"], wl.k_frac, wl.p_mass,
                              bits, o, alpha=0.1, inputs=wl.name))
+
+    progress("sparse-linear")
 
     # SLA2: router mask (projected pooled Q, K; hard Top-k) and the per-channel mix;
     # SALAD: the added branch dropped on half of the heads, then on all of them
@@ -575,6 +589,8 @@ def main():
                           "ms_per_step": round(w6 * 1e3, 4), "sparse_linear_ms": round(l6, 4)},
             "drop_all": {"alpha": "0 on every head (every branch dropped)",
                          "ms_per_step": round(w7 * 1e3, 4), "sparse_linear_ms": round(l7, 4)}}
+
+    progress("SLA2 / SALAD")
 
     # backward of the sparse attention (dQ, dK, dV for a random dO), on the headline
     # mask and at the 95% point; the forward with log-sum-exp runs once, untimed
@@ -611,6 +627,8 @@ def main():
                           "bwd_ms": round(b_ms, 4), "algorithmic_tflops": round(kfb / b_ms / 1e9, 2),
                           "frac_bf16_peak": round(kfb / b_ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
 
+    progress("sparse backward")
+
     # backward of the sparse-linear output (alpha = 0.1) on the headline mask
     S.sparge_mask_predict(q, k, wl.block_q, wl.block_k, wl.k_frac, wl.p_mass, wl.scale,
                           workspace=ws, out=(bits, idx, cnt))
@@ -636,8 +654,8 @@ def main():
         "vs_sparse_bwd": round(e0.elapsed_time(e1) / n_b / backward["headline"]["bwd_ms"], 3)}
     del lbws
 
-    # the low-bit sparse branch (INT8 Q/K, e4m3 P/V) on the same masks: whole call
-    # (quantisation of Q, K and V included) against the bf16 attention call
+    progress("sparse-linear backward")
+
     # the low-bit sparse branch (INT8 Q/K, e4m3 P/V) on the same masks. Its Q and K
     # codes come from the mask's pooling pass (sparge_mask_pool_lowbit), which
     # streams those blocks anyway; the attention call is then the V pack and the
@@ -712,6 +730,8 @@ def main():
                         "lowbit_kept_tops": round(kf_lb / t["lowbit_kernel_ms"] / 1e9, 1)}
     del lws8
 
+    progress("low-bit")
+
     # SVG2's clustered attention (256 query / 512 key clusters, 3 k-means rounds, p = 0.9):
     # the whole call, and its two parts (clustering with the gathers; the attention
     # over the clusters, timed on its own with HIP events), with the token pairs
@@ -720,6 +740,8 @@ def main():
                       device=dev)
     svg2_line = svg2_measure(S, q, k, v, o, sws, wl, 256, 512, 3, 0.9)
     del sws
+
+    progress("SVG2")
 
     # the forward at the other configurations: the tiny case, 95% sparsity on
     # mixed-range heads (k = 3%, p = 0.8) and Wan 14B at 720p (H = 40, N = 75600);
@@ -767,6 +789,7 @@ def main():
             torch.cuda.synchronize()
             ms = [float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j in range(3)]
             checks.append(gpu_sample(name, w2, w2.k_frac, w2.p_mass, bits2, o2))
+            progress(f"forward at {name}")
             c_np, i_np = cnt2.cpu().numpy(), idx2.cpu().numpy()
             kf2 = kept_flops(c_np, i_np, N2, d2, w2.block_q, w2.block_k)
             dense2 = 4.0 * B2 * H2 * float(N2) * N2 * d2
@@ -787,6 +810,7 @@ def main():
     cpu = check = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, Q, K, V, args.cpu_blocks)
+        progress("cpu baseline")
         t0 = time.perf_counter()
         check = oracle_check(checks, inputs)
         check["seconds"] = round(time.perf_counter() - t0, 1)
