@@ -562,26 +562,33 @@ __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void svg2_a
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[i][r] = 0.0f;
   float m = -INFINITY, lsum = 0.0f;
-  // An S^T accumulator starts at 0 for the chunk's valid keys and at -inf for
-  // the keys past their group's valid count, so the product leaves those at
-  // -inf (the K rows are finite): the mask costs what zeroing costs.
-  auto init_s = [&](floatx16(&st)[2], int e) {
-    int val[4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) val[g] = __builtin_amdgcn_readlane(e, g) & 31;
+  auto zero_s = [&](floatx16(&st)[2]) {
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int g = 2 * tau + (r >> 3);
-        const int within = 8 * ((r >> 2) & 1) + 4 * h2 + (r & 3);
-        st[tau][r] = within < val[g] ? 0.0f : -INFINITY;
+      for (int r = 0; r < 16; ++r) st[tau][r] = 0.0f;
+  };
+  // keys past their group's valid count get -inf; group g of the chunk is
+  // registers 8 (g & 1) .. + 7 of S^T tile g / 2, and most groups are full,
+  // so only a partial group's registers are touched (a uniform branch each)
+  auto mask_s = [&](floatx16(&st)[2], int e) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int val = __builtin_amdgcn_readlane(e, g) & 31;
+      if (val < 16) {
+#pragma unroll
+        for (int r8 = 0; r8 < 8; ++r8) {
+          const int r = 8 * (g & 1) + r8;
+          const int within = 8 * (r8 >> 2) + 4 * h2 + (r8 & 3);
+          if (within >= val) st[g >> 1][r] = -INFINITY;
+        }
       }
+    }
   };
   floatx16 sc[2], sn[2];  // S^T of the current and the next chunk
   // entries of chunks it, it+1, it+2 (and it+3 in flight)
   int e0 = load_ent(0), e1 = load_ent(1), e2 = load_ent(2);
-  init_s(sc, e0);
+  zero_s(sc);
   if (count > 0) {
     stageK(e0, 0);
     stageV(e0, 0);
@@ -617,10 +624,11 @@ __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void svg2_a
     const unsigned char* vb = vbuf + (it & 1) * T::BYTES;
     {
       if constexpr (NEXT) {
-        init_s(sn, e1);
+        zero_s(sn);
         qk(kn, sn, 0, HALF, kdma);
       }
 
+      mask_s(sc, e0);
       float mloc = -INFINITY;
 #pragma unroll
       for (int tau = 0; tau < 2; ++tau)
