@@ -162,6 +162,102 @@ __global__ __launch_bounds__(256, 2) void km_assign_kernel(const double* __restr
   }
 }
 
+// d = 128: the same products and argmin, 256 tokens per workgroup (16 waves
+// of 16 tokens, so each centroid tile read from L2 serves four times as many
+// tokens), with the centroids in tiles of 32 double-buffered in LDS by
+// direct-to-LDS copies (one 1 KB row per copy instruction, rows padded by two
+// doubles as above): tile t + 1 is copied while tile t is multiplied. Each
+// accumulator takes its products in the order above, so the distances and
+// the assignment are bit-identical to km_assign_kernel's.
+__global__ __launch_bounds__(1024, 1) void km_assign128_kernel(const double* __restrict__ x,
+                                                              const double* __restrict__ cent,
+                                                              const double* __restrict__ cnorm,
+                                                              int32_t* __restrict__ assign, int N,
+                                                              int C) {
+  constexpr int D = 128, CT = 32, RP = D + 2;
+  __shared__ __align__(16) double cs[2 * CT * RP];
+  const int bh = blockIdx.y, t0 = blockIdx.x * 256;
+  const int th = threadIdx.x, lane = th & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(th >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const size_t xb = (size_t)bh * N;
+  const int tok = min(t0 + 16 * wave + r, N - 1);  // tokens past N are computed, not stored
+  double2 xr[D / 8];
+#pragma unroll
+  for (int s = 0; s < D / 8; ++s)
+    xr[s] = *reinterpret_cast<const double2*>(x + (xb + tok) * D + 8 * s + 2 * g);
+  double best[4] = {INFINITY, INFINITY, INFINITY, INFINITY};
+  int bi[4] = {C, C, C, C};
+  const double* cb0 = cent + (size_t)bh * C * D;
+  const double* cn0 = cnorm + (size_t)bh * C;
+  const int tiles = (C + CT - 1) / CT;
+  // tile t's rows: wave w copies rows 2 w, 2 w + 1 (rows past C repeat row C - 1)
+  auto issue = [&](int t) {
+    double* buf = cs + (t & 1) * CT * RP;
+#pragma unroll
+    for (int i = 0; i < CT / 16; ++i) {
+      const int row = 2 * wave + i;
+      const int cr = min(t * CT + row, C - 1);
+      dma16(cb0 + (size_t)cr * D + 2 * lane, buf + row * RP);
+    }
+  };
+  issue(0);
+  double cnx[2];  // |c|^2 of this lane's two centroids of the tile
+  for (int t = 0; t < tiles; ++t) {
+    const int cb = t * CT;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) cnx[b] = cn0[min(cb + 16 * b + r, C - 1)];
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's rows of tile t landed
+    __syncthreads();                     // every wave's rows landed; the other buffer is free
+    if (t + 1 < tiles) issue(t + 1);
+    const double* buf = cs + (t & 1) * CT * RP;
+    f64x4 acc[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[b] = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll 4
+    for (int s = 0; s < D / 8; ++s) {
+      double2 y[2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        y[b] = *reinterpret_cast<const double2*>(buf + (16 * b + r) * RP + 8 * s + 2 * g);
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        acc[b] = __builtin_amdgcn_mfma_f64_16x16x4f64(xr[s].x, y[b].x, acc[b], 0, 0, 0);
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        acc[b] = __builtin_amdgcn_mfma_f64_16x16x4f64(xr[s].y, y[b].y, acc[b], 0, 0, 0);
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int c = cb + 16 * b + r;
+      if (c < C) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const double v = cnx[b] - 2.0 * acc[b][e];
+          if (v < best[e]) {
+            best[e] = v;
+            bi[e] = c;
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const double ob = __shfl_xor(best[e], off);
+      const int oi = __shfl_xor(bi[e], off);
+      if (ob < best[e] || (ob == best[e] && oi < bi[e])) {
+        best[e] = ob;
+        bi[e] = oi;
+      }
+    }
+    const int t = t0 + 16 * wave + 4 * e + g;
+    if (r == 0 && t < N) assign[xb + t] = bi[e];
+  }
+}
+
 // Stable counting sort by cluster, step 1: per 64-token chunk (one wave),
 // each token's rank among the earlier tokens of its cluster in the chunk, and
 // the chunk's count of each cluster (written by the cluster's last token;
@@ -274,8 +370,19 @@ __global__ __launch_bounds__(D) void km_update_kernel(const double* __restrict__
   double* cp = cent + ((size_t)bh * C + c) * D + t;
   double v = *cp;
   if (n > 0) {
+    // members in token order; eight rows in flight at a time, summed in order
+    const int32_t* pm = perm + (size_t)bh * N + o0;
+    const double* xh = x + (size_t)bh * N * D + t;
     double acc = 0.0;
-    for (int m = 0; m < n; ++m) acc += x[((size_t)bh * N + perm[(size_t)bh * N + o0 + m]) * D + t];
+    int m = 0;
+    for (; m + 8 <= n; m += 8) {
+      double xv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xv[e] = xh[(size_t)pm[m + e] * D];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc += xv[e];
+    }
+    for (; m < n; ++m) acc += xh[(size_t)pm[m] * D];
     v = acc / n;
     *cp = v;
   }
@@ -745,8 +852,12 @@ hipError_t kmeans_run(const Svg2Launch& a, const double* x, int C, double* cent,
   const size_t rows = (size_t)BH * a.N, chunks = (size_t)BH * nch, cc = chunks * C;
   hipLaunchKernelGGL((km_init_kernel<D>), dim3(C, BH), dim3(D), 0, s, x, cent, cnorm, a.N, C);
   for (int it = 0; it <= a.iters; ++it) {
-    hipLaunchKernelGGL((km_assign_kernel<D>), dim3(nch, BH), dim3(256), 0, s, x, cent, cnorm,
-                       assign, a.N, C);
+    if constexpr (D == 128)
+      hipLaunchKernelGGL(km_assign128_kernel, dim3((a.N + 255) / 256, BH), dim3(1024), 0, s, x,
+                         cent, cnorm, assign, a.N, C);
+    else
+      hipLaunchKernelGGL((km_assign_kernel<D>), dim3(nch, BH), dim3(256), 0, s, x, cent, cnorm,
+                         assign, a.N, C);
     hipLaunchKernelGGL(fill_i32_zero_kernel, dim3((unsigned)std::min<size_t>((cc + 255) / 256, 4096)),
                        dim3(256), 0, s, a.ccount, cc);
     hipLaunchKernelGGL(km_rank_kernel, dim3((unsigned)((chunks + 3) / 4)), dim3(256), 0, s, assign,
