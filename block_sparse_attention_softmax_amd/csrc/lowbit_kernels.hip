@@ -49,10 +49,18 @@ __global__ __launch_bounds__(256) void quant_int8_kernel(const uint16_t* __restr
   const int r0 = bi * block, rows = min(block, N - r0);
   const size_t base = ((size_t)bh * N + r0) * D;
   const int n8 = rows * D / 8;
+  // the block (at most 128 rows) stays in registers between its amax and its codes
+  constexpr int MAXU = 128 * D / 8 / 256;
+  uint4 u[MAXU];
+#pragma unroll
+  for (int q8 = 0; q8 < MAXU; ++q8) {
+    const int p = q8 * 256 + t;
+    u[q8] = p < n8 ? *reinterpret_cast<const uint4*>(x + base + (size_t)p * 8) : make_uint4(0, 0, 0, 0);
+  }
   float amax = 0.0f;
-  for (int p = t; p < n8; p += 256) {
-    const uint4 u = *reinterpret_cast<const uint4*>(x + base + (size_t)p * 8);
-    const uint32_t* w = &u.x;
+#pragma unroll
+  for (int q8 = 0; q8 < MAXU; ++q8) {
+    const uint32_t* w = &u[q8].x;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(w[e])), fabsf(bf16_hi(w[e]))));
@@ -64,10 +72,12 @@ __global__ __launch_bounds__(256) void quant_int8_kernel(const uint16_t* __restr
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
   if (t == 0) scales[(size_t)bh * nblocks + bi] = amax / 127.0f;
-  for (int p = t; p < n8; p += 256) {
-    const uint4 u = *reinterpret_cast<const uint4*>(x + base + (size_t)p * 8);
-    *reinterpret_cast<uint2*>(codes + base + (size_t)p * 8) =
-        make_uint2(int8_pack4(u.x, u.y, inv), int8_pack4(u.z, u.w, inv));
+#pragma unroll
+  for (int q8 = 0; q8 < MAXU; ++q8) {
+    const int p = q8 * 256 + t;
+    if (p < n8)
+      *reinterpret_cast<uint2*>(codes + base + (size_t)p * 8) =
+          make_uint2(int8_pack4(u[q8].x, u[q8].y, inv), int8_pack4(u[q8].z, u[q8].w, inv));
   }
 }
 
@@ -83,13 +93,22 @@ __global__ __launch_bounds__(256) void v_amax_kernel(const uint16_t* __restrict_
   const int bh = blockIdx.y, t = threadIdx.x, cg = t % CG, rl = t / CG;
   const int r0 = blockIdx.x * 512, r1 = min(r0 + 512, N);
   float mx[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-  for (int r = r0 + rl; r < r1; r += RL) {
-    const uint4 u = *reinterpret_cast<const uint4*>(v + ((size_t)bh * N + r) * D + 8 * cg);
-    const uint32_t* w = &u.x;
+  constexpr int UNR = 8;  // rows in flight per thread (their loads issued together)
+  for (int rb = r0 + rl; rb < r1; rb += RL * UNR) {
+    uint4 u[UNR];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      mx[2 * e] = fmaxf(mx[2 * e], fabsf(bf16_lo(w[e])));
-      mx[2 * e + 1] = fmaxf(mx[2 * e + 1], fabsf(bf16_hi(w[e])));
+    for (int x = 0; x < UNR; ++x) {
+      const int r = min(rb + RL * x, r1 - 1);  // a repeated row leaves the maximum unchanged
+      u[x] = *reinterpret_cast<const uint4*>(v + ((size_t)bh * N + r) * D + 8 * cg);
+    }
+#pragma unroll
+    for (int x = 0; x < UNR; ++x) {
+      const uint32_t* w = &u[x].x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        mx[2 * e] = fmaxf(mx[2 * e], fabsf(bf16_lo(w[e])));
+        mx[2 * e + 1] = fmaxf(mx[2 * e + 1], fabsf(bf16_hi(w[e])));
+      }
     }
   }
 #pragma unroll
@@ -119,12 +138,25 @@ __global__ __launch_bounds__(256) void pack_v_fp8_kernel(const uint16_t* __restr
                                                          uint8_t* __restrict__ vt8, int N,
                                                          int n_k) {
   __shared__ uint16_t vs[BK * (D + 2)];  // rows padded by one word against bank conflicts
+  __shared__ float sinv[D];               // 448 / amax per channel
   const int j = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
-  for (int p = t; p < BK * D / 8; p += 256) {
-    const int r = p / (D / 8), c8 = (p % (D / 8)) * 8;
-    uint4 u = make_uint4(0, 0, 0, 0);
-    if (j * BK + r < N) u = *reinterpret_cast<const uint4*>(v + ((size_t)bh * N + j * BK + r) * D + c8);
-    const uint32_t* w = &u.x;
+  constexpr int LU = BK * D / 8 / 256;  // 16-byte loads per thread, issued together
+  static_assert(BK * D / 8 % 256 == 0, "whole loads per thread");
+  uint4 u[LU];
+#pragma unroll
+  for (int x = 0; x < LU; ++x) {
+    const int p = x * 256 + t, r = p / (D / 8), c8 = (p % (D / 8)) * 8;
+    u[x] = make_uint4(0, 0, 0, 0);
+    if (j * BK + r < N) u[x] = *reinterpret_cast<const uint4*>(v + ((size_t)bh * N + j * BK + r) * D + c8);
+  }
+  if (t < D) {
+    const float amax = __uint_as_float(vmax[(size_t)bh * D + t]);
+    sinv[t] = amax > 0.0f ? kE4m3Max / amax : 0.0f;
+  }
+#pragma unroll
+  for (int x = 0; x < LU; ++x) {
+    const int p = x * 256 + t, r = p / (D / 8), c8 = (p % (D / 8)) * 8;
+    const uint32_t* w = &u[x].x;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       vs[r * (D + 2) + c8 + 2 * e] = (uint16_t)(w[e] & 0xFFFFu);
@@ -134,8 +166,7 @@ __global__ __launch_bounds__(256) void pack_v_fp8_kernel(const uint16_t* __restr
   __syncthreads();
   for (int p = t; p < D * 16; p += 256) {
     const int c = p / 16, s0 = (p % 16) * 4;
-    const float amax = __uint_as_float(vmax[(size_t)bh * D + c]);
-    const float inv = amax > 0.0f ? kE4m3Max / amax : 0.0f;
+    const float inv = sinv[c];
     float x[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
