@@ -296,18 +296,30 @@ __global__ __launch_bounds__(256) void km_colscan_kernel(int32_t* __restrict__ c
   const int c = blockIdx.x * 64 + lane;
   const int q = (nch + 3) / 4, ch0 = min(wave * q, nch), ch1 = min(ch0 + q, nch);
   int32_t* col = ccount + (size_t)bh * nch * C + c;
+  constexpr int U = 16;  // chunk counts in flight per lane (their loads issued together)
   int sum = 0;
   if (c < C)
-    for (int ch = ch0; ch < ch1; ++ch) sum += col[(size_t)ch * C];
+    for (int cb = ch0; cb < ch1; cb += U) {
+      int v[U];
+#pragma unroll
+      for (int x = 0; x < U; ++x) v[x] = cb + x < ch1 ? col[(size_t)(cb + x) * C] : 0;
+#pragma unroll
+      for (int x = 0; x < U; ++x) sum += v[x];
+    }
   part[wave][lane] = sum;
   __syncthreads();
   int run = 0;
   for (int w = 0; w < wave; ++w) run += part[w][lane];
   if (c < C) {
-    for (int ch = ch0; ch < ch1; ++ch) {
-      const int v = col[(size_t)ch * C];
-      col[(size_t)ch * C] = run;
-      run += v;
+    for (int cb = ch0; cb < ch1; cb += U) {
+      int v[U];
+#pragma unroll
+      for (int x = 0; x < U; ++x) v[x] = cb + x < ch1 ? col[(size_t)(cb + x) * C] : 0;
+#pragma unroll
+      for (int x = 0; x < U; ++x) {
+        if (cb + x < ch1) col[(size_t)(cb + x) * C] = run;
+        run += v[x];
+      }
     }
     if (wave == 3) size[(size_t)bh * C + c] = run;
   }
