@@ -653,8 +653,8 @@ hipError_t launch_sparse(const AttnLaunch& a, hipStream_t s, AttnPhase phase) {
     if constexpr (LIN) {
       hipLaunchKernelGGL((linear_total_kernel<D>), dim3(kLinSplit, BH), dim3(D * 2), 0, s,
                          a.phikt, a.vt, a.part_h, a.part_z, a.n_k, a.lin_on, a.H);
-      hipLaunchKernelGGL((linear_reduce_kernel<D>), dim3(BH), dim3(256), 0, s, a.part_h,
-                         a.part_z, a.lin_h, a.lin_z, a.lin_on, a.H);
+      hipLaunchKernelGGL((linear_reduce_kernel<D>), dim3(BH, (D * D + D + 255) / 256), dim3(256),
+                         0, s, a.part_h, a.part_z, a.lin_h, a.lin_z, a.lin_on, a.H);
     }
   }
   if (phase != kPackOnly) {

@@ -1328,8 +1328,8 @@ hipError_t launch_bwd_t(const BwdLaunch& a, hipStream_t s) {
                          w.vtp, w.phikt, a.N, a.n_k, w.lin_on, a.H);
       hipLaunchKernelGGL((linear_total_kernel<D>), dim3(kLinSplit, BH), dim3(D * 2), 0, s,
                          w.phikt, w.vtp, w.part_h, w.part_z, a.n_k, w.lin_on, a.H);
-      hipLaunchKernelGGL((linear_reduce_kernel<D>), dim3(BH), dim3(256), 0, s, w.part_h,
-                         w.part_z, w.lin_h, w.lin_z, w.lin_on, a.H);
+      hipLaunchKernelGGL((linear_reduce_kernel<D>), dim3(BH, (D * D + D + 255) / 256), dim3(256),
+                         0, s, w.part_h, w.part_z, w.lin_h, w.lin_z, w.lin_on, a.H);
       if (a.lin_mode == kLinMix) {
         const size_t n8 = (size_t)BH * a.N * D / 8;
         hipLaunchKernelGGL((scale_do_kernel<D>), dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0,

@@ -111,7 +111,7 @@ struct AttnLaunch {
   float* part_h;       // [B*H, kLinSplit, d, d] split-K partials of lin_h
   float* part_z;       // [B*H, kLinSplit, d]
 };
-constexpr int kLinSplit = 16;
+constexpr int kLinSplit = 64;
 // how the linear branch meets the sparse output: O_s + alpha[h] O_l, or the
 // per-channel mix alpha[h][c] O_s + (1 - alpha[h][c]) O_l
 enum LinMode { kLinAdd = 0, kLinMix = 1 };

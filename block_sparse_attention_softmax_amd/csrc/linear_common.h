@@ -258,7 +258,9 @@ __global__ __launch_bounds__(D * 2) void linear_total_kernel(const uint16_t* __r
   if (h2 == 0) part_z[((size_t)bh * kLinSplit + split) * D + 32 * wave + l32] = zp;
 }
 
-// H_tot, z_tot = sums of the kLinSplit partials, in split order.
+// H_tot, z_tot = sums of the kLinSplit partials, in split order. Grid (b*h,
+// chunks of 256 entries of H then z); each thread sums one entry, its
+// partials loaded eight at a time.
 template <int D>
 __global__ __launch_bounds__(256) void linear_reduce_kernel(const float* __restrict__ part_h,
                                                             const float* __restrict__ part_z,
@@ -266,19 +268,25 @@ __global__ __launch_bounds__(256) void linear_reduce_kernel(const float* __restr
                                                             float* __restrict__ lin_z,
                                                             const int32_t* __restrict__ lin_on,
                                                             int H) {
-  const int bh = blockIdx.x;
-  if (!lin_on[bh % H]) return;
-  for (int e = threadIdx.x; e < D * D + D; e += 256) {
-    float acc = 0.0f;
-    if (e < D * D) {
-      for (int sp = 0; sp < kLinSplit; ++sp) acc += part_h[((size_t)bh * kLinSplit + sp) * D * D + e];
-      lin_h[(size_t)bh * D * D + e] = acc;
-    } else {
-      const int a = e - D * D;
-      for (int sp = 0; sp < kLinSplit; ++sp) acc += part_z[((size_t)bh * kLinSplit + sp) * D + a];
-      lin_z[(size_t)bh * D + a] = acc;
-    }
+  const int bh = blockIdx.x, e = blockIdx.y * 256 + threadIdx.x;
+  if (!lin_on[bh % H] || e >= D * D + D) return;
+  const bool hpart = e < D * D;
+  const float* src = hpart ? part_h + (size_t)bh * kLinSplit * D * D + e
+                           : part_z + (size_t)bh * kLinSplit * D + (e - D * D);
+  const size_t stride = hpart ? (size_t)D * D : (size_t)D;
+  static_assert(kLinSplit % 8 == 0, "whole groups of partials");
+  float acc = 0.0f;
+  for (int sp = 0; sp < kLinSplit; sp += 8) {
+    float v[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) v[x] = src[(size_t)(sp + x) * stride];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) acc += v[x];
   }
+  if (hpart)
+    lin_h[(size_t)bh * D * D + e] = acc;
+  else
+    lin_z[(size_t)bh * D + (e - D * D)] = acc;
 }
 
 // lin_on[h] = 1 unless every weight that head h's linear branch is multiplied

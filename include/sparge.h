@@ -274,7 +274,7 @@ int sparge_attn_bwd(const void* q, const void* k, const void* v, const void* o,
 
 /* Device workspace (bytes) of sparse_linear_attn_fwd: the packed V of
  * sparge_attn_fwd, phi(K) packed the same way, and per (b, h) the float32
- * summaries sum_u phi(K_u)^T V_u (d x d) and sum_u phi(K_u) (d) with 16
+ * summaries sum_u phi(K_u)^T V_u (d x d) and sum_u phi(K_u) (d) with 64
  * split-K partials of each, and H + 2 + 2*B*H int32 for the per-head
  * branch flags and the lists of (batch, head) pairs by flag. Returns 0 for
  * arguments that sparse_linear_attn_fwd would reject. */
