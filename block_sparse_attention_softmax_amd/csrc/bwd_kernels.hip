@@ -1077,15 +1077,24 @@ __global__ __launch_bounds__(256) void linear_bwd_total_kernel(const float* __re
                                                                int n_q) {
   const int bh = blockIdx.x, e = blockIdx.y * 256 + threadIdx.x;
   if (e >= D * D + D) return;
-  float acc = 0.0f;
-  if (e < D * D) {
-    for (int i = 0; i < n_q; ++i) acc += dHq[((size_t)bh * n_q + i) * D * D + e];
-    dHt[(size_t)bh * D * D + e] = acc;
-  } else {
-    const int a = e - D * D;
-    for (int i = 0; i < n_q; ++i) acc += dzq[((size_t)bh * n_q + i) * D + a];
-    dzt[(size_t)bh * D + a] = acc;
+  const bool hpart = e < D * D;
+  const float* src = hpart ? dHq + (size_t)bh * n_q * D * D + e
+                           : dzq + (size_t)bh * n_q * D + (e - D * D);
+  const size_t stride = hpart ? (size_t)D * D : (size_t)D;
+  float acc = 0.0f;  // in block order, eight blocks' entries loaded at a time
+  int i = 0;
+  for (; i + 8 <= n_q; i += 8) {
+    float v[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) v[x] = src[(size_t)(i + x) * stride];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) acc += v[x];
   }
+  for (; i < n_q; ++i) acc += src[(size_t)i * stride];
+  if (hpart)
+    dHt[(size_t)bh * D * D + e] = acc;
+  else
+    dzt[(size_t)bh * D + (e - D * D)] = acc;
 }
 
 // Per (b, h, key block j): G_j = the sum of dH_D over the query blocks that
@@ -1125,6 +1134,35 @@ __global__ __launch_bounds__(256, 1) void linear_bwd_keys_kernel(
   }
   const int listed = colcnt[(size_t)bh * n_k + j];
   const bool use_kept = listed <= n_q - listed;
+  // the query blocks to take, in increasing order: those that list j (their
+  // dH_D is subtracted from dH_tot) or those that do not (summed); the latter
+  // are gathered from the count matrix into LDS by a ballot compaction
+  __shared__ int blist[kMaxLinQueryBlocks];
+  int nb;
+  const int32_t* lsrc;
+  if (use_kept) {
+    nb = listed;
+    lsrc = collist + (size_t)bh * n_q * n_k + coloff[(size_t)bh * (n_k + 1) + j];
+  } else {
+    __shared__ int wcnt[4];
+    const int32_t* cm = cmat + ((size_t)bh * n_k + j) * n_q;
+    int base = 0;
+    for (int i0b = 0; i0b < n_q; i0b += 256) {
+      const int i = i0b + th;
+      const bool take = i < n_q && cm[i] == 0;
+      const uint64_t bal = __ballot(take);
+      const int lane = th & 63, wv = th >> 6;
+      if (lane == 0) wcnt[wv] = __popcll(bal);
+      __syncthreads();
+      int before = base;
+      for (int w = 0; w < wv; ++w) before += wcnt[w];
+      if (take) blist[before + __popcll(bal & ((1ull << lane) - 1ull))] = i;
+      base += wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
+      __syncthreads();
+    }
+    nb = base;
+    lsrc = blist;
+  }
   float4 gacc[F4];
   float4 zacc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   const bool zthread = th < D / 4;
@@ -1133,37 +1171,43 @@ __global__ __launch_bounds__(256, 1) void linear_bwd_keys_kernel(
 #pragma unroll
     for (int m = 0; m < F4; ++m) gacc[m] = t4[m * 256 + th];
     if (zthread) zacc = reinterpret_cast<const float4*>(dzt + (size_t)bh * D)[th];
-    const int beg = coloff[(size_t)bh * (n_k + 1) + j], end = coloff[(size_t)bh * (n_k + 1) + j + 1];
-    const int32_t* lst = collist + (size_t)bh * n_q * n_k;
-    for (int e = beg; e < end; ++e) {
-      const int i = lst[e];
-      const float4* q4 = reinterpret_cast<const float4*>(dHq + ((size_t)bh * n_q + i) * D * D);
-#pragma unroll
-      for (int m = 0; m < F4; ++m) {
-        const float4 x = q4[m * 256 + th];
-        gacc[m].x -= x.x; gacc[m].y -= x.y; gacc[m].z -= x.z; gacc[m].w -= x.w;
-      }
-      if (zthread) {
-        const float4 x = reinterpret_cast<const float4*>(dzq + ((size_t)bh * n_q + i) * D)[th];
-        zacc.x -= x.x; zacc.y -= x.y; zacc.z -= x.z; zacc.w -= x.w;
-      }
-    }
   } else {
 #pragma unroll
     for (int m = 0; m < F4; ++m) gacc[m] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    const int32_t* cm = cmat + ((size_t)bh * n_k + j) * n_q;
-    for (int i = 0; i < n_q; ++i) {
-      if (cm[i] != 0) continue;
-      const float4* q4 = reinterpret_cast<const float4*>(dHq + ((size_t)bh * n_q + i) * D * D);
+  }
+  const float sg = use_kept ? -1.0f : 1.0f;  // exact: x * -1 and x * 1 change no bit
+  // two blocks' dH_D in flight: the loads of block e + 1 are issued before the
+  // sums of block e, which are taken in order
+  auto load_blk = [&](int e, float4 (&x)[F4], float4& z) {
+    const int i = lsrc[e];
+    const float4* q4 = reinterpret_cast<const float4*>(dHq + ((size_t)bh * n_q + i) * D * D);
 #pragma unroll
-      for (int m = 0; m < F4; ++m) {
-        const float4 x = q4[m * 256 + th];
-        gacc[m].x += x.x; gacc[m].y += x.y; gacc[m].z += x.z; gacc[m].w += x.w;
-      }
-      if (zthread) {
-        const float4 x = reinterpret_cast<const float4*>(dzq + ((size_t)bh * n_q + i) * D)[th];
-        zacc.x += x.x; zacc.y += x.y; zacc.z += x.z; zacc.w += x.w;
-      }
+    for (int m = 0; m < F4; ++m) x[m] = q4[m * 256 + th];
+    if (zthread) z = reinterpret_cast<const float4*>(dzq + ((size_t)bh * n_q + i) * D)[th];
+  };
+  auto add_blk = [&](const float4 (&x)[F4], const float4& z) {
+#pragma unroll
+    for (int m = 0; m < F4; ++m) {
+      gacc[m].x = fmaf(sg, x[m].x, gacc[m].x); gacc[m].y = fmaf(sg, x[m].y, gacc[m].y);
+      gacc[m].z = fmaf(sg, x[m].z, gacc[m].z); gacc[m].w = fmaf(sg, x[m].w, gacc[m].w);
+    }
+    if (zthread) {
+      zacc.x = fmaf(sg, z.x, zacc.x); zacc.y = fmaf(sg, z.y, zacc.y);
+      zacc.z = fmaf(sg, z.z, zacc.z); zacc.w = fmaf(sg, z.w, zacc.w);
+    }
+  };
+  {
+    float4 xa[F4], xb[F4], za = make_float4(0.0f, 0.0f, 0.0f, 0.0f), zb = za;
+    int e = 0;
+    for (; e + 2 <= nb; e += 2) {
+      load_blk(e, xa, za);
+      load_blk(e + 1, xb, zb);
+      add_blk(xa, za);
+      add_blk(xb, zb);
+    }
+    if (e < nb) {
+      load_blk(e, xa, za);
+      add_blk(xa, za);
     }
   }
 #pragma unroll

@@ -12,6 +12,8 @@ namespace {
 
 // ------------------------------------------------ H_D, z_D of a query block
 constexpr int kMaxLinKeyBlocks = 4096;  // capacity of the per-row kept bitmap
+// query blocks per (b, h) of the linear branch: block_q = d >= block_k, so n_q <= n_k <= 4096
+constexpr int kMaxLinQueryBlocks = 4096;
 
 // LDS of form_hd: four stages of (phi(K)^T, V^T) tiles, the complement list
 // and the bitmap; H_D (rows of HP floats) and z_D overlay the stages at the
