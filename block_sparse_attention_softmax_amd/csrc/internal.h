@@ -185,7 +185,8 @@ struct Svg2Launch {
   int32_t *assign_q, *assign_k, *rank, *ccount, *size_q, *size_k, *off_q, *off_k, *perm_q,
       *perm_k;
   uint32_t* sbits;
-  int32_t *sidx, *scnt, *qpad_off, *kpad_off, *tile_cluster, *n_tiles, *lists, *list_cnt;
+  int32_t *sidx, *scnt, *qpad_off, *kpad_off, *tile_cluster, *n_tiles, *tile_order, *lists,
+      *list_cnt;
   uint16_t *qp, *kp, *vp, *vtp;
 };
 // everything; steps 1-3 and the gathers only; the attention only (from the workspace)

@@ -516,6 +516,140 @@ __global__ __launch_bounds__(256) void svg2_lists_kernel(const int32_t* __restri
   if (lane == 0) list_cnt[row] = padded / 4;
 }
 
+// Dispatch order of the attention's query tiles. Tiles carry very different
+// work (a query cluster keeps anywhere from one to several hundred 64-key
+// chunks), and workgroups go round-robin to the 8 XCDs, so slot i of XCD x
+// is workgroup 8 i + x (the positions xcd_remap gives). Every XCD receives a
+// contiguous, head-major range of the real tiles holding an eighth of the
+// total work (weight = chunks + kTileCost for a tile's fixed cost), clamped
+// so that no XCD gets more tiles than it has slots, and runs that range
+// heaviest tile first, so the range ends on short tiles instead of a long
+// one started late. Entries are b h * max_tiles + tile, -1 for unused slots.
+// One workgroup per XCD; thread t walks grid entries [t R, t R + R) three
+// times (weights and ranks, histogram, placement). The placement takes its
+// slots with LDS atomics, so the order among tiles of equal weight can vary
+// from call to call; every tile's output is computed the same way in any
+// order.
+constexpr int kTileCost = 3;
+constexpr int kOrderBins = 1024;
+
+__global__ __launch_bounds__(1024) void svg2_order_kernel(const int32_t* __restrict__ n_tiles,
+                                                          const int32_t* __restrict__ tile_cluster,
+                                                          const int32_t* __restrict__ list_cnt,
+                                                          int32_t* __restrict__ order, int BH,
+                                                          int Cq, int max_tiles) {
+  __shared__ long long wred[16];
+  __shared__ int cred[16];
+  __shared__ int h8[8];
+  __shared__ int bins[kOrderBins];
+  __shared__ int range[2];
+  constexpr int XCDS = 8;
+  const int x = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int total = BH * max_tiles;
+  const int R = (total + 1023) / 1024;
+  const int g0 = min(t * R, total), g1 = min(g0 + R, total);
+  auto weight = [&](int g) -> int {  // 0 for slots past a head's tiles
+    const int bh = g / max_tiles, tl = g % max_tiles;
+    if (tl >= min(n_tiles[bh], max_tiles)) return 0;
+    return max(list_cnt[(size_t)bh * Cq + tile_cluster[g]], 0) + kTileCost;
+  };
+  long long wsum = 0;
+  int vcnt = 0;
+  for (int g = g0; g < g1; ++g) {
+    const int wt = weight(g);
+    wsum += wt;
+    vcnt += wt > 0;
+  }
+  // exclusive scans of the work and of the tile count over the threads
+  long long ws = wsum;
+  int vs = vcnt;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const long long a = __shfl_up(ws, off);
+    const int b = __shfl_up(vs, off);
+    if (lane >= off) { ws += a; vs += b; }
+  }
+  if (lane == 63) { wred[w] = ws; cred[w] = vs; }
+  if (t < 8) h8[t] = 0;
+  for (int i = t; i < kOrderBins; i += 1024) bins[i] = 0;
+  __syncthreads();
+  long long wbase = 0, W = 0;
+  int rbase = 0, T = 0;
+  for (int i = 0; i < 16; ++i) {
+    wbase += i < w ? wred[i] : 0;
+    rbase += i < w ? cred[i] : 0;
+    W += wred[i];
+    T += cred[i];
+  }
+  wbase += ws - wsum;
+  rbase += vs - vcnt;
+  // tiles whose work starts in the k-th eighth of the total
+  {
+    long long p = wbase;
+    for (int g = g0; g < g1; ++g) {
+      const int wt = weight(g);
+      if (wt > 0) atomicAdd(&h8[(int)min(8 * p / max(W, 1ll), 7ll)], 1);
+      p += wt;
+    }
+  }
+  __syncthreads();
+  const int per = total / XCDS, rem = total % XCDS;
+  auto cap = [&](int y) { return per + (y < rem ? 1 : 0); };
+  if (t == 0) {
+    int s = 0, cut = 0, after = total;  // after: slots of XCDs y.. ; cut: tiles before eighth y+1
+    for (int y = 0; y < XCDS; ++y) {
+      cut += h8[y];
+      after -= cap(y);
+      const int lo = max(s, T - after), hi = min(s + cap(y), T);
+      const int e = min(max(y == XCDS - 1 ? T : cut, lo), hi);
+      if (y == x) { range[0] = s; range[1] = e; }
+      s = e;
+    }
+  }
+  __syncthreads();
+  const int s0 = range[0], s1 = range[1];
+  auto bin_of = [](int wt) { return kOrderBins - 1 - min(wt, kOrderBins - 1); };  // heaviest first
+  {
+    int r = rbase;
+    for (int g = g0; g < g1; ++g) {
+      const int wt = weight(g);
+      if (wt > 0) {
+        if (r >= s0 && r < s1) atomicAdd(&bins[bin_of(wt)], 1);
+        ++r;
+      }
+    }
+  }
+  __syncthreads();
+  {  // exclusive scan of the bins (one per thread)
+    const int v = t < kOrderBins ? bins[t] : 0;
+    int xs = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(xs, off);
+      if (lane >= off) xs += y;
+    }
+    __syncthreads();
+    if (lane == 63) cred[w] = xs;
+    __syncthreads();
+    int before = 0;
+    for (int i = 0; i < w; ++i) before += cred[i];
+    if (t < kOrderBins) bins[t] = before + xs - v;
+  }
+  __syncthreads();
+  const int base = x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per;
+  {
+    int r = rbase;
+    for (int g = g0; g < g1; ++g) {
+      const int wt = weight(g);
+      if (wt > 0) {
+        if (r >= s0 && r < s1) order[base + atomicAdd(&bins[bin_of(wt)], 1)] = g;
+        ++r;
+      }
+    }
+  }
+  for (int j = s1 - s0 + t; j < cap(x); j += 1024) order[base + j] = -1;
+}
+
 // Gather the rows of each cluster (in permuted order) into its padded slot;
 // padding rows are zero. Grid (clusters, B*H), 256 threads, 16-byte copies.
 template <int D>
@@ -548,7 +682,9 @@ __global__ __launch_bounds__(256) void svg2_gather_kernel(const uint16_t* __rest
 // only to whole 16-key groups; a query cluster's list names the groups of its
 // kept key clusters, four to a 64-key chunk. One workgroup per padded query
 // tile (BQ rows of one cluster), BQ/32 waves of 32 queries (rows past the
-// cluster's end are zero and their results are not stored). Every chunk's K rows and packed V^T slots are gathered group by group
+// cluster's end are zero and their results are not stored), taken in the
+// order svg2_order_kernel set: work-balanced XCD ranges, heaviest tile
+// first. Every chunk's K rows and packed V^T slots are gathered group by group
 // global -> LDS by direct-to-LDS copies with per-lane source addresses (K:
 // one group per copy instruction and wave; V^T: the two 16-byte halves of a
 // group's slots in every channel row), into the tile layouts of the sparse
@@ -563,7 +699,7 @@ template <int D, int BQ>
 __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void svg2_attn_kernel(
     const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp,
     const uint16_t* __restrict__ vtp, const int32_t* __restrict__ tile_cluster,
-    const int32_t* __restrict__ n_tiles, const int32_t* __restrict__ lists,
+    const int32_t* __restrict__ tile_order, const int32_t* __restrict__ lists,
     const int32_t* __restrict__ list_cnt, const int32_t* __restrict__ perm_q,
     const int32_t* __restrict__ off_q, const int32_t* __restrict__ size_q,
     const int32_t* __restrict__ qpad_off, uint16_t* __restrict__ o, int N, int NQP, int NKP,
@@ -577,9 +713,9 @@ __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void svg2_a
   unsigned char* const kbuf = smem;
   unsigned char* const vbuf = smem + 2 * T::BYTES;
 
-  const int wg = xcd_remap(blockIdx.x, (int)gridDim.x);
-  const int bh = wg / max_tiles, tile = wg % max_tiles;
-  if (tile >= n_tiles[bh]) return;
+  const int enc = tile_order[xcd_remap(blockIdx.x, (int)gridDim.x)];
+  if (enc < 0) return;
+  const int bh = enc / max_tiles, tile = enc % max_tiles;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h2 = lane >> 5, l32 = lane & 31;
@@ -892,7 +1028,7 @@ hipError_t launch_svg2_t(const Svg2Launch& a, hipStream_t s) {
   const int NQP = a.max_tiles * BQ, NKP = a.n_ktiles * BK;
   if (a.phase == kSvg2Attend) {
     hipLaunchKernelGGL((svg2_attn_kernel<D, BQ>), dim3(BH * a.max_tiles), dim3(BQ * 2), 0, s, a.qp,
-                       a.kp, a.vtp, a.tile_cluster, a.n_tiles, a.lists, a.list_cnt, a.perm_q,
+                       a.kp, a.vtp, a.tile_cluster, a.tile_order, a.lists, a.list_cnt, a.perm_q,
                        a.off_q, a.size_q, a.qpad_off, a.o, a.N, NQP, NKP, a.Cq, a.max_tiles,
                        a.max_list, a.n_ktiles, a.scale * 1.4426950408889634f);
     return hipGetLastError();
@@ -934,6 +1070,8 @@ hipError_t launch_svg2_t(const Svg2Launch& a, hipStream_t s) {
   hipLaunchKernelGGL(svg2_lists_kernel, dim3((unsigned)((lrows + 3) / 4)), dim3(256), 0, s, a.sidx,
                      a.scnt, a.kpad_off, a.size_k, a.lists, a.list_cnt, a.Cq, a.Ck, a.max_list,
                      lrows);
+  hipLaunchKernelGGL(svg2_order_kernel, dim3(8), dim3(1024), 0, s, a.n_tiles, a.tile_cluster,
+                     a.list_cnt, a.tile_order, BH, a.Cq, a.max_tiles);
   hipLaunchKernelGGL((svg2_gather_kernel<D>), dim3(a.Cq, BH), dim3(256), 0, s, a.q, a.perm_q,
                      a.off_q, a.size_q, a.qpad_off, a.qp, a.N, a.Cq, BQ, NQP);
   hipLaunchKernelGGL((svg2_gather_kernel<D>), dim3(a.Ck, BH), dim3(256), 0, s, a.k, a.perm_k,
@@ -944,7 +1082,7 @@ hipError_t launch_svg2_t(const Svg2Launch& a, hipStream_t s) {
                      nullptr, a.vtp, nullptr, NKP, a.n_ktiles, nullptr, a.H);
   if (a.phase == kSvg2Cluster) return hipGetLastError();
   hipLaunchKernelGGL((svg2_attn_kernel<D, BQ>), dim3(BH * a.max_tiles), dim3(BQ * 2), 0, s, a.qp,
-                     a.kp, a.vtp, a.tile_cluster, a.n_tiles, a.lists, a.list_cnt, a.perm_q,
+                     a.kp, a.vtp, a.tile_cluster, a.tile_order, a.lists, a.list_cnt, a.perm_q,
                      a.off_q, a.size_q, a.qpad_off, a.o, a.N, NQP, NKP, a.Cq, a.max_tiles,
                      a.max_list, a.n_ktiles, a.scale * 1.4426950408889634f);
   return hipGetLastError();
@@ -996,6 +1134,7 @@ size_t svg2_layout(Svg2Launch& a, unsigned char* w) {
   a.kpad_off = reinterpret_cast<int32_t*>(take(BH * a.Ck * 4));
   a.tile_cluster = reinterpret_cast<int32_t*>(take(BH * a.max_tiles * 4));
   a.n_tiles = reinterpret_cast<int32_t*>(take(BH * 4));
+  a.tile_order = reinterpret_cast<int32_t*>(take(BH * a.max_tiles * 4));
   a.lists = reinterpret_cast<int32_t*>(take(BH * a.Cq * a.max_list * 4));
   a.list_cnt = reinterpret_cast<int32_t*>(take(BH * a.Cq * 4));
   a.qp = reinterpret_cast<uint16_t*>(take(BH * NQP * d * 2));
