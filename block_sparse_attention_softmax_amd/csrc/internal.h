@@ -181,7 +181,12 @@ struct Svg2Launch {
   // 64-key chunks); packed 64-slot V^T tiles
   int max_tiles, max_groups, max_list, n_ktiles;
   // workspace (svg2_layout)
-  double *xq, *xk, *centq, *centk, *normq, *normk, *clog;
+  double *centq, *centk, *normq, *normk, *clog;
+  // the assignment's bf16 filter: centroid planes, |c|^2 in float32, per (b, h)
+  // cmax bits and listed-token counts (kaux), and the listed tokens
+  uint16_t *chi, *clo;
+  float* cnf;
+  int32_t *kaux, *kflags;
   int32_t *assign_q, *assign_k, *rank, *ccount, *size_q, *size_k, *off_q, *off_k, *perm_q,
       *perm_k;
   uint32_t* sbits;

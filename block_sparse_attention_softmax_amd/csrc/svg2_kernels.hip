@@ -30,11 +30,15 @@
 namespace sparge {
 namespace {
 
-// x (bf16) -> float64, elementwise.
-__global__ __launch_bounds__(256) void to_f64_kernel(const uint16_t* __restrict__ x,
-                                                     double* __restrict__ y, size_t n) {
-  for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (size_t)gridDim.x * 256)
-    y[e] = (double)__uint_as_float((uint32_t)x[e] << 16);
+// bf16 bits -> float64 (exact)
+__device__ __forceinline__ double bf16_f64(uint16_t u) {
+  return (double)__uint_as_float((uint32_t)u << 16);
+}
+
+// float -> bf16 bits, round to nearest even (finite inputs)
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
 __global__ __launch_bounds__(256) void fill_i32_zero_kernel(int32_t* __restrict__ p, size_t n) {
@@ -56,15 +60,17 @@ __device__ __forceinline__ double block_sum(double v, double* red) {
 }
 
 // ------------------------------------------------------------- k-means
-// centroid c = token floor(c N / C); |c|^2. Grid (C, B*H), D threads.
+// The tokens are read as bf16 and widened exactly, so every float64 value is
+// the token's own. centroid c = token floor(c N / C); |c|^2. Grid (C, B*H),
+// D threads.
 template <int D>
-__global__ __launch_bounds__(D) void km_init_kernel(const double* __restrict__ x,
+__global__ __launch_bounds__(D) void km_init_kernel(const uint16_t* __restrict__ x,
                                                     double* __restrict__ cent,
                                                     double* __restrict__ cnorm, int N, int C) {
   __shared__ double red[2];
   const int c = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
   const size_t tok = (size_t)c * N / C;
-  const double v = x[((size_t)bh * N + tok) * D + t];
+  const double v = bf16_f64(x[((size_t)bh * N + tok) * D + t]);
   cent[((size_t)bh * C + c) * D + t] = v;
   const double s = block_sum<D>(v * v, red);
   if (t == 0) cnorm[(size_t)bh * C + c] = s;
@@ -72,189 +78,274 @@ __global__ __launch_bounds__(D) void km_init_kernel(const double* __restrict__ x
 
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
-// assign[t] = argmin_c (|c|^2 - 2 x_t . c), ties to the lower c, without
-// storing the distances. Workgroup (64 tokens, b, h): wave w holds tokens
-// 16 w .. 16 w + 15 in registers (lane: token 16 w + lane % 16, channels
-// 8 s + 2 (lane / 16) + 0..1), the centroids stream through LDS 64 at a time
-// (rows padded by two doubles so that 16 lanes reading 16 rows hit different
-// banks), and each lane keeps the best of its column of every 16 x 16 product
-// for the 4 tokens it holds; the 16 lanes of a token group merge at the end.
-// The float64 products run in the instruction order of block_logits_kernel
-// (two 16x16x4 steps per 8 channels, per accumulator), so every distance has
-// the bits of the distance-matrix route it replaces.
+// The assignment assign[t] = argmin_c (|c|^2 - 2 x_t . c) over float64
+// distances, ties to the lower c, in two passes that give exactly the
+// float64 result:
+//  (a) km_filter_kernel: every distance on the bf16 matrix cores from the
+//      centroid split into two bf16 planes (c = hi + lo + r, |r| <= 2^-16 |c|
+//      per channel; x is bf16 already), accumulated in float32. Its error
+//      against the float64 distance is bounded by E = 1.25e-4 |x| cmax +
+//      2.5e-7 cmax^2 (cmax = the largest |c| of the head): the split residual
+//      (2^-16), float32 accumulation of 2 D exact products (at most 2 D
+//      roundings of 2^-23 each), and the float32 roundings of |c|^2 and of
+//      the difference, with about 30% to spare. A token whose best and
+//      second-best approximate distances are more than 2E apart has that
+//      best cluster as its unique float64 argmin, and it is written; any
+//      other token (and any non-finite or huge value) is listed.
+//  (b) km_exact_kernel: the listed tokens only, with the float64 products
+//      below, so a close call is decided by the float64 distances.
+
+// Per round: the centroid planes, |c|^2 in float32 and cmax per (b, h) (as
+// float bits, maxed into a zeroed word). Grid (C, B*H), D threads.
 template <int D>
-__global__ __launch_bounds__(256, 2) void km_assign_kernel(const double* __restrict__ x,
-                                                           const double* __restrict__ cent,
-                                                           const double* __restrict__ cnorm,
-                                                           int32_t* __restrict__ assign, int N,
-                                                           int C) {
-  constexpr int CT = 64, RP = D + 2;  // centroids per tile; LDS row (doubles)
-  __shared__ __align__(16) double cs[CT * RP];
-  __shared__ double cn[CT];
-  const int bh = blockIdx.y, t0 = blockIdx.x * 64;
-  const int th = threadIdx.x, lane = th & 63, wave = th >> 6;
-  const int r = lane & 15, g = lane >> 4;
-  const size_t xb = (size_t)bh * N;
-  const int tok = min(t0 + 16 * wave + r, N - 1);  // tokens past N are computed, not stored
-  double2 xr[D / 8];
-#pragma unroll
-  for (int s = 0; s < D / 8; ++s)
-    xr[s] = *reinterpret_cast<const double2*>(x + (xb + tok) * D + 8 * s + 2 * g);
-  double best[4] = {INFINITY, INFINITY, INFINITY, INFINITY};
-  int bi[4] = {C, C, C, C};
-  const double* cb0 = cent + (size_t)bh * C * D;
-  for (int cb = 0; cb < C; cb += CT) {
-    __syncthreads();  // the previous tile is consumed
-    for (int p = th; p < CT * D / 2; p += 256) {
-      const int row = p / (D / 2), c2 = p % (D / 2);
-      const int cr = min(cb + row, C - 1);
-      *reinterpret_cast<double2*>(cs + row * RP + 2 * c2) =
-          *reinterpret_cast<const double2*>(cb0 + (size_t)cr * D + 2 * c2);
-    }
-    if (th < CT) cn[th] = cnorm[(size_t)bh * C + min(cb + th, C - 1)];
-    __syncthreads();
-    f64x4 acc[4];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) acc[b] = f64x4{0.0, 0.0, 0.0, 0.0};
-#pragma unroll 4
-    for (int s = 0; s < D / 8; ++s) {
-      double2 y[4];
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-        y[b] = *reinterpret_cast<const double2*>(cs + (16 * b + r) * RP + 8 * s + 2 * g);
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-        acc[b] = __builtin_amdgcn_mfma_f64_16x16x4f64(xr[s].x, y[b].x, acc[b], 0, 0, 0);
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-        acc[b] = __builtin_amdgcn_mfma_f64_16x16x4f64(xr[s].y, y[b].y, acc[b], 0, 0, 0);
-    }
-    // lane: tokens 4 e + g of the wave's 16, centroid cb + 16 b + r (increasing)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int c = cb + 16 * b + r;
-      if (c < C) {
-        const double cnc = cn[16 * b + r];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const double v = cnc - 2.0 * acc[b][e];
-          if (v < best[e]) {
-            best[e] = v;
-            bi[e] = c;
-          }
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) {
-      const double ob = __shfl_xor(best[e], off);
-      const int oi = __shfl_xor(bi[e], off);
-      if (ob < best[e] || (ob == best[e] && oi < bi[e])) {
-        best[e] = ob;
-        bi[e] = oi;
-      }
-    }
-    const int t = t0 + 16 * wave + 4 * e + g;
-    if (r == 0 && t < N) assign[xb + t] = bi[e];
+__global__ __launch_bounds__(D) void km_planes_kernel(const double* __restrict__ cent,
+                                                      const double* __restrict__ cnorm,
+                                                      uint16_t* __restrict__ chi,
+                                                      uint16_t* __restrict__ clo,
+                                                      float* __restrict__ cnf,
+                                                      uint32_t* __restrict__ cmax_bits, int C) {
+  const int c = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+  const size_t e = ((size_t)bh * C + c) * D + t;
+  const double v = cent[e];
+  const uint16_t hi = bf16_rne((float)v);
+  const uint16_t lo = bf16_rne((float)(v - bf16_f64(hi)));
+  chi[e] = hi;
+  clo[e] = lo;
+  if (t == 0) {
+    const double cn = cnorm[(size_t)bh * C + c];
+    cnf[(size_t)bh * C + c] = (float)cn;
+    const float nrm = (float)sqrt(cn) * (1.0f + 1e-6f);  // an upper bound of |c|
+    atomicMax(&cmax_bits[bh], __float_as_uint(nrm));
   }
 }
 
-// d = 128: the same products and argmin, 256 tokens per workgroup (16 waves
-// of 16 tokens, so each centroid tile read from L2 serves four times as many
-// tokens), with the centroids in tiles of 32 double-buffered in LDS by
-// direct-to-LDS copies (one 1 KB row per copy instruction, rows padded by two
-// doubles as above): tile t + 1 is copied while tile t is multiplied. Each
-// accumulator takes its products in the order above, so the distances and
-// the assignment are bit-identical to km_assign_kernel's.
-__global__ __launch_bounds__(1024, 1) void km_assign128_kernel(const double* __restrict__ x,
-                                                              const double* __restrict__ cent,
-                                                              const double* __restrict__ cnorm,
-                                                              int32_t* __restrict__ assign, int N,
-                                                              int C) {
-  constexpr int D = 128, CT = 32, RP = D + 2;
-  __shared__ __align__(16) double cs[2 * CT * RP];
-  const int bh = blockIdx.y, t0 = blockIdx.x * 256;
+// (a) Workgroup (128 tokens, b, h), 4 waves of 32 tokens. S^T = C_tile X^T as
+// in the attention's S^T = K Q^T: the token fragments stay in registers (one
+// token per lane column), the planes of 64 centroids at a time are copied
+// global -> LDS (swizzled K-tile layout, double-buffered, rows past C repeat
+// row C - 1 and are skipped), and each lane keeps the best, its cluster and
+// the second best of its 16-row slices; the two half-waves merge at the end.
+template <int D>
+__global__ __launch_bounds__(256, 2) void km_filter_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ chi,
+    const uint16_t* __restrict__ clo, const float* __restrict__ cnf,
+    const uint32_t* __restrict__ cmax_bits, int32_t* __restrict__ assign,
+    int32_t* __restrict__ flag_list, int32_t* __restrict__ flag_cnt, int N, int C) {
+  using T = Tile<D>;
+  constexpr int NW = 4, KSTEPS = D / 16;
+  constexpr int LOADS = BK * D / 8 / 64 / NW;  // 16-byte copies per wave and plane tile
+  __shared__ __align__(16) unsigned char smem[4 * T::BYTES];  // [buffer][plane]
+  __shared__ float cns[2][BK];
+  const int bh = blockIdx.y, t0 = blockIdx.x * 128;
   const int th = threadIdx.x, lane = th & 63;
   const int wave = __builtin_amdgcn_readfirstlane(th >> 6);
-  const int r = lane & 15, g = lane >> 4;
+  const int h2 = lane >> 5, l32 = lane & 31;
   const size_t xb = (size_t)bh * N;
-  const int tok = min(t0 + 16 * wave + r, N - 1);  // tokens past N are computed, not stored
-  double2 xr[D / 8];
+  const int tok = t0 + 32 * wave + l32;
+  bf16x8 xf[KSTEPS];
+  float xx = 0.0f;
+  {
+    const uint16_t* xr = x + (xb + min(tok, N - 1)) * D + 8 * h2;
 #pragma unroll
-  for (int s = 0; s < D / 8; ++s)
-    xr[s] = *reinterpret_cast<const double2*>(x + (xb + tok) * D + 8 * s + 2 * g);
-  double best[4] = {INFINITY, INFINITY, INFINITY, INFINITY};
-  int bi[4] = {C, C, C, C};
-  const double* cb0 = cent + (size_t)bh * C * D;
-  const double* cn0 = cnorm + (size_t)bh * C;
-  const int tiles = (C + CT - 1) / CT;
-  // tile t's rows: wave w copies rows 2 w, 2 w + 1 (rows past C repeat row C - 1)
+    for (int s = 0; s < KSTEPS; ++s) {
+      xf[s] = *reinterpret_cast<const bf16x8*>(xr + 16 * s);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float f = (float)xf[s][e];
+        xx = fmaf(f, f, xx);
+      }
+    }
+  }
+  xx += __shfl_xor(xx, 32);
+  const int tiles = (C + BK - 1) / BK;
+  const uint16_t* hib = chi + (size_t)bh * C * D;
+  const uint16_t* lob = clo + (size_t)bh * C * D;
   auto issue = [&](int t) {
-    double* buf = cs + (t & 1) * CT * RP;
+    unsigned char* buf = smem + (t & 1) * 2 * T::BYTES;
 #pragma unroll
-    for (int i = 0; i < CT / 16; ++i) {
-      const int row = 2 * wave + i;
-      const int cr = min(t * CT + row, C - 1);
-      dma16(cb0 + (size_t)cr * D + 2 * lane, buf + row * RP);
+    for (int u = 0; u < LOADS; ++u) {
+      const int p = 64 * (u * NW + wave) + lane;
+      const int kr = p / T::KCPR;
+      const size_t src = (size_t)min(t * BK + kr, C - 1) * D + T::kchunk(kr, p % T::KCPR) * 8;
+      dma16(hib + src, buf + 1024 * (u * NW + wave));
+      dma16(lob + src, buf + T::BYTES + 1024 * (u * NW + wave));
     }
   };
+  int koff[KSTEPS];
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) koff[s] = l32 * T::KROWB + (T::kchunk(l32, 2 * s + h2) << 4);
+  float b1 = INFINITY, b2 = INFINITY;
+  int i1 = C;
+  float cnv = th < BK ? cnf[(size_t)bh * C + min(th, C - 1)] : 0.0f;
   issue(0);
-  double cnx[2];  // |c|^2 of this lane's two centroids of the tile
   for (int t = 0; t < tiles; ++t) {
-    const int cb = t * CT;
-#pragma unroll
-    for (int b = 0; b < 2; ++b) cnx[b] = cn0[min(cb + 16 * b + r, C - 1)];
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's rows of tile t landed
-    __syncthreads();                     // every wave's rows landed; the other buffer is free
-    if (t + 1 < tiles) issue(t + 1);
-    const double* buf = cs + (t & 1) * CT * RP;
-    f64x4 acc[2];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) acc[b] = f64x4{0.0, 0.0, 0.0, 0.0};
-#pragma unroll 4
-    for (int s = 0; s < D / 8; ++s) {
-      double2 y[2];
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-        y[b] = *reinterpret_cast<const double2*>(buf + (16 * b + r) * RP + 8 * s + 2 * g);
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-        acc[b] = __builtin_amdgcn_mfma_f64_16x16x4f64(xr[s].x, y[b].x, acc[b], 0, 0, 0);
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-        acc[b] = __builtin_amdgcn_mfma_f64_16x16x4f64(xr[s].y, y[b].y, acc[b], 0, 0, 0);
+    if (th < BK) cns[t & 1][th] = cnv;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of tile t landed
+    __syncthreads();                     // every wave's copies landed; the other buffer is free
+    if (t + 1 < tiles) {
+      cnv = th < BK ? cnf[(size_t)bh * C + min((t + 1) * BK + th, C - 1)] : 0.0f;
+      issue(t + 1);
     }
+    const unsigned char* hb = smem + (t & 1) * 2 * T::BYTES;
+    const unsigned char* lb = hb + T::BYTES;
+    floatx16 acc[2];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int c = cb + 16 * b + r;
-      if (c < C) {
+    for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const double v = cnx[b] - 2.0 * acc[b][e];
-          if (v < best[e]) {
-            best[e] = v;
-            bi[e] = c;
+      for (int r = 0; r < 16; ++r) acc[tau][r] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau) {
+        const bf16x8 a = lds_read16(hb + tau * 32 * T::KROWB + koff[s]);
+        const bf16x8 b = lds_read16(lb + tau * 32 * T::KROWB + koff[s]);
+        acc[tau] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, xf[s], acc[tau], 0, 0, 0);
+        acc[tau] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, xf[s], acc[tau], 0, 0, 0);
+      }
+    }
+    // lane: token l32, centroids t*64 + 32 tau + 8 (r / 4) + 4 h2 + r % 4
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 32 * tau + 8 * (r >> 2) + 4 * h2 + (r & 3);
+        const int c = t * BK + row;
+        const float v = fmaf(-2.0f, acc[tau][r], cns[t & 1][row]);
+        if (c < C) {
+          if (v < b1) {
+            b2 = b1;
+            b1 = v;
+            i1 = c;
+          } else {
+            b2 = fminf(b2, v);
+          }
+        }
+      }
+  }
+  {  // merge the two half-waves (the same token)
+    const float o1 = __shfl_xor(b1, 32), o2 = __shfl_xor(b2, 32);
+    const int oi = __shfl_xor(i1, 32);
+    if (o1 < b1) {
+      b2 = fminf(o2, b1);
+      b1 = o1;
+      i1 = oi;
+    } else if (o1 == b1) {
+      b2 = b1;
+      i1 = min(i1, oi);
+    } else {
+      b2 = fminf(b2, o1);
+    }
+  }
+  if (h2 == 0 && tok < N) {
+    const float cm = __uint_as_float(cmax_bits[bh]);
+    const float xn = sqrtf(xx * (1.0f + 1e-5f)) * (1.0f + 1e-6f);
+    const float E = 1.25e-4f * xn * cm + 2.5e-7f * cm * cm;
+    const bool sane = xn * cm < 1e30f && cm * cm < 1e30f && fabsf(b1) < 1e30f &&
+                      fabsf(b2) < 1e30f;
+    if (sane && b2 - b1 > 2.0f * E) {
+      assign[xb + tok] = i1;
+    } else {
+      flag_list[xb + atomicAdd(&flag_cnt[bh], 1)] = tok;
+    }
+  }
+}
+
+// (b) assign[t] for the listed tokens t of each (b, h), from float64
+// distances. Workgroup (g, b, h) takes chunks g, g + G, ... of 64 listed
+// tokens: wave w holds tokens 16 w .. 16 w + 15 of the chunk in registers
+// (lane: token 16 w + lane % 16, channels 8 s + 2 (lane / 16) + 0..1), the
+// centroids stream through LDS 64 at a time (rows padded by two doubles so
+// that 16 lanes reading 16 rows hit different banks), and each lane keeps
+// the best of its column of every 16 x 16 product for the 4 tokens it holds;
+// the 16 lanes of a token group merge at the end. Every distance comes from
+// the same float64 instruction sequence whichever tokens share its chunk.
+constexpr int kExactGroups = 16;  // workgroups per (b, h) of km_exact_kernel
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void km_exact_kernel(const uint16_t* __restrict__ x,
+                                                          const double* __restrict__ cent,
+                                                          const double* __restrict__ cnorm,
+                                                          const int32_t* __restrict__ list,
+                                                          const int32_t* __restrict__ list_cnt,
+                                                          int32_t* __restrict__ assign, int N,
+                                                          int C) {
+  constexpr int CT = 64, RP = D + 2;  // centroids per tile; LDS row (doubles)
+  __shared__ __align__(16) double cs[CT * RP];
+  __shared__ double cn[CT];
+  const int bh = blockIdx.y;
+  const int th = threadIdx.x, lane = th & 63, wave = th >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const size_t xb = (size_t)bh * N;
+  const int cnt = min(list_cnt[bh], N);
+  const int32_t* lb = list + xb;
+  const double* cb0 = cent + (size_t)bh * C * D;
+  for (int base = blockIdx.x * 64; base < cnt; base += gridDim.x * 64) {
+    const int tok = lb[min(base + 16 * wave + r, cnt - 1)];  // repeats past the count are not stored
+    double2 xr[D / 8];
+#pragma unroll
+    for (int s = 0; s < D / 8; ++s) {
+      const uint32_t two = *reinterpret_cast<const uint32_t*>(x + (xb + tok) * D + 8 * s + 2 * g);
+      xr[s] = make_double2(bf16_f64((uint16_t)(two & 0xFFFFu)), bf16_f64((uint16_t)(two >> 16)));
+    }
+    double best[4] = {INFINITY, INFINITY, INFINITY, INFINITY};
+    int bi[4] = {C, C, C, C};
+    for (int cb = 0; cb < C; cb += CT) {
+      __syncthreads();  // the previous tile is consumed
+      for (int p = th; p < CT * D / 2; p += 256) {
+        const int row = p / (D / 2), c2 = p % (D / 2);
+        const int cr = min(cb + row, C - 1);
+        *reinterpret_cast<double2*>(cs + row * RP + 2 * c2) =
+            *reinterpret_cast<const double2*>(cb0 + (size_t)cr * D + 2 * c2);
+      }
+      if (th < CT) cn[th] = cnorm[(size_t)bh * C + min(cb + th, C - 1)];
+      __syncthreads();
+      f64x4 acc[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) acc[b] = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll 4
+      for (int s = 0; s < D / 8; ++s) {
+        double2 y[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          y[b] = *reinterpret_cast<const double2*>(cs + (16 * b + r) * RP + 8 * s + 2 * g);
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          acc[b] = __builtin_amdgcn_mfma_f64_16x16x4f64(xr[s].x, y[b].x, acc[b], 0, 0, 0);
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          acc[b] = __builtin_amdgcn_mfma_f64_16x16x4f64(xr[s].y, y[b].y, acc[b], 0, 0, 0);
+      }
+      // lane: tokens 4 e + g of the wave's 16, centroid cb + 16 b + r (increasing)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int c = cb + 16 * b + r;
+        if (c < C) {
+          const double cnc = cn[16 * b + r];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const double v = cnc - 2.0 * acc[b][e];
+            if (v < best[e]) {
+              best[e] = v;
+              bi[e] = c;
+            }
           }
         }
       }
     }
-  }
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < 4; ++e) {
 #pragma unroll
-    for (int off = 1; off < 16; off <<= 1) {
-      const double ob = __shfl_xor(best[e], off);
-      const int oi = __shfl_xor(bi[e], off);
-      if (ob < best[e] || (ob == best[e] && oi < bi[e])) {
-        best[e] = ob;
-        bi[e] = oi;
+      for (int off = 1; off < 16; off <<= 1) {
+        const double ob = __shfl_xor(best[e], off);
+        const int oi = __shfl_xor(bi[e], off);
+        if (ob < best[e] || (ob == best[e] && oi < bi[e])) {
+          best[e] = ob;
+          bi[e] = oi;
+        }
       }
+      const int li = base + 16 * wave + 4 * e + g;
+      if (r == 0 && li < cnt) assign[xb + lb[li]] = bi[e];
     }
-    const int t = t0 + 16 * wave + 4 * e + g;
-    if (r == 0 && t < N) assign[xb + t] = bi[e];
   }
 }
 
@@ -370,7 +461,7 @@ __global__ __launch_bounds__(256) void km_scatter_kernel(const int32_t* __restri
 // Centroid c = the mean of its members in token order (float64); an empty
 // cluster keeps its centroid; |c|^2. Grid (C, B*H), D threads.
 template <int D>
-__global__ __launch_bounds__(D) void km_update_kernel(const double* __restrict__ x,
+__global__ __launch_bounds__(D) void km_update_kernel(const uint16_t* __restrict__ x,
                                                       const int32_t* __restrict__ perm,
                                                       const int32_t* __restrict__ size,
                                                       const int32_t* __restrict__ off,
@@ -384,17 +475,17 @@ __global__ __launch_bounds__(D) void km_update_kernel(const double* __restrict__
   if (n > 0) {
     // members in token order; eight rows in flight at a time, summed in order
     const int32_t* pm = perm + (size_t)bh * N + o0;
-    const double* xh = x + (size_t)bh * N * D + t;
+    const uint16_t* xh = x + (size_t)bh * N * D + t;
     double acc = 0.0;
     int m = 0;
     for (; m + 8 <= n; m += 8) {
-      double xv[8];
+      uint16_t xv[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) xv[e] = xh[(size_t)pm[m + e] * D];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc += xv[e];
+      for (int e = 0; e < 8; ++e) acc += bf16_f64(xv[e]);
     }
-    for (; m < n; ++m) acc += xh[(size_t)pm[m] * D];
+    for (; m < n; ++m) acc += bf16_f64(xh[(size_t)pm[m] * D]);
     v = acc / n;
     *cp = v;
   }
@@ -994,18 +1085,21 @@ __global__ __launch_bounds__(256) void svg2_pairs_kernel(
 
 // --------------------------------------------------------------- driver
 template <int D>
-hipError_t kmeans_run(const Svg2Launch& a, const double* x, int C, double* cent, double* cnorm,
+hipError_t kmeans_run(const Svg2Launch& a, const uint16_t* x, int C, double* cent, double* cnorm,
                       int32_t* assign, int32_t* size, int32_t* off, int32_t* perm, hipStream_t s) {
   const int BH = a.B * a.H, nch = (a.N + 63) / 64;
   const size_t rows = (size_t)BH * a.N, chunks = (size_t)BH * nch, cc = chunks * C;
+  uint32_t* cmax_bits = reinterpret_cast<uint32_t*>(a.kaux);
+  int32_t* flag_cnt = a.kaux + BH;
   hipLaunchKernelGGL((km_init_kernel<D>), dim3(C, BH), dim3(D), 0, s, x, cent, cnorm, a.N, C);
   for (int it = 0; it <= a.iters; ++it) {
-    if constexpr (D == 128)
-      hipLaunchKernelGGL(km_assign128_kernel, dim3((a.N + 255) / 256, BH), dim3(1024), 0, s, x,
-                         cent, cnorm, assign, a.N, C);
-    else
-      hipLaunchKernelGGL((km_assign_kernel<D>), dim3(nch, BH), dim3(256), 0, s, x, cent, cnorm,
-                         assign, a.N, C);
+    hipLaunchKernelGGL(fill_i32_zero_kernel, dim3(1), dim3(256), 0, s, a.kaux, (size_t)2 * BH);
+    hipLaunchKernelGGL((km_planes_kernel<D>), dim3(C, BH), dim3(D), 0, s, cent, cnorm, a.chi,
+                       a.clo, a.cnf, cmax_bits, C);
+    hipLaunchKernelGGL((km_filter_kernel<D>), dim3((a.N + 127) / 128, BH), dim3(256), 0, s, x,
+                       a.chi, a.clo, a.cnf, cmax_bits, assign, a.kflags, flag_cnt, a.N, C);
+    hipLaunchKernelGGL((km_exact_kernel<D>), dim3(kExactGroups, BH), dim3(256), 0, s, x, cent,
+                       cnorm, a.kflags, flag_cnt, assign, a.N, C);
     hipLaunchKernelGGL(fill_i32_zero_kernel, dim3((unsigned)std::min<size_t>((cc + 255) / 256, 4096)),
                        dim3(256), 0, s, a.ccount, cc);
     hipLaunchKernelGGL(km_rank_kernel, dim3((unsigned)((chunks + 3) / 4)), dim3(256), 0, s, assign,
@@ -1033,13 +1127,10 @@ hipError_t launch_svg2_t(const Svg2Launch& a, hipStream_t s) {
                        a.max_list, a.n_ktiles, a.scale * 1.4426950408889634f);
     return hipGetLastError();
   }
-  const size_t n = (size_t)BH * a.N * D;
-  hipLaunchKernelGGL(to_f64_kernel, dim3(4096), dim3(256), 0, s, a.q, a.xq, n);
-  hipLaunchKernelGGL(to_f64_kernel, dim3(4096), dim3(256), 0, s, a.k, a.xk, n);
-  hipError_t e = kmeans_run<D>(a, a.xq, a.Cq, a.centq, a.normq, a.assign_q, a.size_q, a.off_q,
+  hipError_t e = kmeans_run<D>(a, a.q, a.Cq, a.centq, a.normq, a.assign_q, a.size_q, a.off_q,
                                a.perm_q, s);
   if (e == hipSuccess)
-    e = kmeans_run<D>(a, a.xk, a.Ck, a.centk, a.normk, a.assign_k, a.size_k, a.off_k, a.perm_k, s);
+    e = kmeans_run<D>(a, a.k, a.Ck, a.centk, a.normk, a.assign_k, a.size_k, a.off_k, a.perm_k, s);
   if (e != hipSuccess) return e;
   // centroid Top-p
   e = launch_scores_f64(a.centq, a.centk, a.clog, BH, a.Cq, a.Ck, D, (double)a.scale, s);
@@ -1110,8 +1201,11 @@ size_t svg2_layout(Svg2Launch& a, unsigned char* w) {
     off += (bytes + 255) & ~(size_t)255;
     return p;
   };
-  a.xq = reinterpret_cast<double*>(take(BH * N * d * 8));
-  a.xk = reinterpret_cast<double*>(take(BH * N * d * 8));
+  a.chi = reinterpret_cast<uint16_t*>(take(BH * Cm * d * 2));
+  a.clo = reinterpret_cast<uint16_t*>(take(BH * Cm * d * 2));
+  a.cnf = reinterpret_cast<float*>(take(BH * Cm * 4));
+  a.kaux = reinterpret_cast<int32_t*>(take(BH * 2 * 4));
+  a.kflags = reinterpret_cast<int32_t*>(take(BH * N * 4));
   a.centq = reinterpret_cast<double*>(take(BH * a.Cq * d * 8));
   a.centk = reinterpret_cast<double*>(take(BH * a.Ck * d * 8));
   a.normq = reinterpret_cast<double*>(take(BH * a.Cq * 8));
