@@ -2,10 +2,11 @@
 //
 //  1. k-means on the query tokens (C_q clusters) and, independently, on the
 //     key tokens (C_k clusters): Lloyd's rounds in float64 from centroids at
-//     tokens floor(c N / C); distances |c|^2 - 2 x.c on the float64 matrix
-//     cores with the argmin (ties to the lower cluster) taken in the same
-//     kernel, so no distance matrix is stored; centroids the mean of their
-//     members in token order.
+//     tokens floor(c N / C); the argmin of the float64 distances
+//     |c|^2 - 2 x.c (ties to the lower cluster) found by a bf16 matrix-core
+//     filter with a proven error bound, the close calls decided by float64
+//     matrix-core products, no distance matrix stored; centroids the mean of
+//     their members in token order.
 //  2. the permutation: a stable counting sort of the tokens by cluster, so
 //     each cluster is contiguous (ranks inside 64-token chunks by lane
 //     comparisons, per-chunk counts, scans; no atomics, so the order is

@@ -392,8 +392,8 @@ int sparge_attn_fwd_lowbit_packed(const int32_t* kv_idx, const int32_t* kv_cnt, 
                                   void* lowbit_workspace, size_t lowbit_workspace_bytes,
                                   void* stream);
 
-/* Device workspace (bytes) of svg2_attn_fwd (float64 copies of Q and K, the
- * clustering, the selection and the padded permuted Q, K, V); 0 for arguments
+/* Device workspace (bytes) of svg2_attn_fwd (the clustering, the selection,
+ * the tile order and the padded permuted Q, K, V); 0 for arguments
  * svg2_attn_fwd would reject. */
 size_t svg2_attn_workspace_bytes(int B, int H, int N, int d, int block_q, int n_q_clusters,
                                  int n_k_clusters);
@@ -416,12 +416,13 @@ size_t svg2_attn_workspace_bytes(int B, int H, int N, int d, int block_q, int n_
  *     original sequence under that token-level mask.
  * q, k, v, o: bf16 [B, H, N, d], device, 16-byte aligned; block_q (64 or 128)
  * is the query tile of the attention step; at most 4096 key clusters. The
- * workspace (256-byte aligned) holds every intermediate: the float64 copies
- * of Q and K the clustering reads, the centroids, assignments, counting-sort
+ * workspace (256-byte aligned) holds every intermediate: the centroids (and
+ * their bf16 planes for the assignment's filter), assignments, counting-sort
  * counts and permutations, the centroid scores and selection, the group
- * lists, and Q, K, V and the packed V^T gathered into cluster-contiguous
- * order (query clusters padded to whole block_q tiles, key clusters only to
- * whole 16-key groups; svg2_attn_workspace_bytes gives the total). */
+ * lists, the query tiles' order, and Q, K, V and the packed V^T gathered
+ * into cluster-contiguous order (query clusters padded to whole block_q
+ * tiles, key clusters only to whole 16-key groups; svg2_attn_workspace_bytes
+ * gives the total). */
 int svg2_attn_fwd(const void* q, const void* k, const void* v, int B, int H, int N, int d,
                   int block_q, int n_q_clusters, int n_k_clusters, int iters, float p_mass,
                   float scale, void* o, void* workspace, size_t workspace_bytes, void* stream);
