@@ -97,35 +97,49 @@ typedef double f64x4 __attribute__((ext_vector_type(4)));
 //      below, so a close call is decided by the float64 distances.
 
 // Per round: the centroid planes, |c|^2 in float32 and cmax per (b, h) (as
-// float bits, maxed into a zeroed word). Grid (C, B*H), D threads.
+// float bits, maxed into a zeroed word). Workgroup (16 clusters, b, h), 256
+// threads: the planes element by element, the 16 norms and their maximum in
+// the workgroup, one atomic per workgroup.
+constexpr int kPlaneClusters = 16;
+
 template <int D>
-__global__ __launch_bounds__(D) void km_planes_kernel(const double* __restrict__ cent,
-                                                      const double* __restrict__ cnorm,
-                                                      uint16_t* __restrict__ chi,
-                                                      uint16_t* __restrict__ clo,
-                                                      float* __restrict__ cnf,
-                                                      uint32_t* __restrict__ cmax_bits, int C) {
-  const int c = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
-  const size_t e = ((size_t)bh * C + c) * D + t;
-  const double v = cent[e];
-  const uint16_t hi = bf16_rne((float)v);
-  const uint16_t lo = bf16_rne((float)(v - bf16_f64(hi)));
-  chi[e] = hi;
-  clo[e] = lo;
-  if (t == 0) {
-    const double cn = cnorm[(size_t)bh * C + c];
-    cnf[(size_t)bh * C + c] = (float)cn;
-    const float nrm = (float)sqrt(cn) * (1.0f + 1e-6f);  // an upper bound of |c|
-    atomicMax(&cmax_bits[bh], __float_as_uint(nrm));
+__global__ __launch_bounds__(256) void km_planes_kernel(const double* __restrict__ cent,
+                                                        const double* __restrict__ cnorm,
+                                                        uint16_t* __restrict__ chi,
+                                                        uint16_t* __restrict__ clo,
+                                                        float* __restrict__ cnf,
+                                                        uint32_t* __restrict__ cmax_bits, int C) {
+  const int bh = blockIdx.y, c0 = blockIdx.x * kPlaneClusters, t = threadIdx.x;
+  const int nc = min(kPlaneClusters, C - c0);
+  const size_t base = ((size_t)bh * C + c0) * D;
+  for (int e = t; e < nc * D; e += 256) {
+    const double v = cent[base + e];
+    const uint16_t hi = bf16_rne((float)v);
+    chi[base + e] = hi;
+    clo[base + e] = bf16_rne((float)(v - bf16_f64(hi)));
+  }
+  if (t < 64) {
+    float nrm = 0.0f;
+    if (t < nc) {
+      const double cn = cnorm[(size_t)bh * C + c0 + t];
+      cnf[(size_t)bh * C + c0 + t] = (float)cn;
+      nrm = (float)sqrt(cn) * (1.0f + 1e-6f);  // an upper bound of |c|
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) nrm = fmaxf(nrm, __shfl_xor(nrm, off));
+    if (t == 0) atomicMax(&cmax_bits[bh], __float_as_uint(nrm));
   }
 }
 
-// (a) Workgroup (128 tokens, b, h), 4 waves of 32 tokens. S^T = C_tile X^T as
-// in the attention's S^T = K Q^T: the token fragments stay in registers (one
-// token per lane column), the planes of 64 centroids at a time are copied
-// global -> LDS (swizzled K-tile layout, double-buffered, rows past C repeat
-// row C - 1 and are skipped), and each lane keeps the best, its cluster and
-// the second best of its 16-row slices; the two half-waves merge at the end.
+// (a) Workgroup (256 tokens, b, h), 4 waves of 64 tokens (two 32-token
+// halves). S^T = C_tile X^T as in the attention's S^T = K Q^T: the token
+// fragments stay in registers (one token per lane column and half), the
+// planes of 64 centroids at a time are copied global -> LDS (swizzled K-tile
+// layout, double-buffered, rows past C repeat row C - 1 and are skipped), each
+// plane fragment read from LDS feeds both halves, and the next k-step's
+// fragments are read while the current one multiplies. Each lane keeps the
+// best, its cluster and the second best of its 16-row slices per half; the
+// two half-waves merge at the end.
 template <int D>
 __global__ __launch_bounds__(256, 2) void km_filter_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ chi,
@@ -137,27 +151,28 @@ __global__ __launch_bounds__(256, 2) void km_filter_kernel(
   constexpr int LOADS = BK * D / 8 / 64 / NW;  // 16-byte copies per wave and plane tile
   __shared__ __align__(16) unsigned char smem[4 * T::BYTES];  // [buffer][plane]
   __shared__ float cns[2][BK];
-  const int bh = blockIdx.y, t0 = blockIdx.x * 128;
+  const int bh = blockIdx.y, t0 = blockIdx.x * 256;
   const int th = threadIdx.x, lane = th & 63;
   const int wave = __builtin_amdgcn_readfirstlane(th >> 6);
   const int h2 = lane >> 5, l32 = lane & 31;
   const size_t xb = (size_t)bh * N;
-  const int tok = t0 + 32 * wave + l32;
-  bf16x8 xf[KSTEPS];
-  float xx = 0.0f;
-  {
+  bf16x8 xf[2][KSTEPS];
+  float xx[2] = {0.0f, 0.0f};
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int tok = t0 + 64 * wave + 32 * hh + l32;
     const uint16_t* xr = x + (xb + min(tok, N - 1)) * D + 8 * h2;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
-      xf[s] = *reinterpret_cast<const bf16x8*>(xr + 16 * s);
+      xf[hh][s] = *reinterpret_cast<const bf16x8*>(xr + 16 * s);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float f = (float)xf[s][e];
-        xx = fmaf(f, f, xx);
+        const float f = (float)xf[hh][s][e];
+        xx[hh] = fmaf(f, f, xx[hh]);
       }
     }
+    xx[hh] += __shfl_xor(xx[hh], 32);
   }
-  xx += __shfl_xor(xx, 32);
   const int tiles = (C + BK - 1) / BK;
   const uint16_t* hib = chi + (size_t)bh * C * D;
   const uint16_t* lob = clo + (size_t)bh * C * D;
@@ -175,8 +190,8 @@ __global__ __launch_bounds__(256, 2) void km_filter_kernel(
   int koff[KSTEPS];
 #pragma unroll
   for (int s = 0; s < KSTEPS; ++s) koff[s] = l32 * T::KROWB + (T::kchunk(l32, 2 * s + h2) << 4);
-  float b1 = INFINITY, b2 = INFINITY;
-  int i1 = C;
+  float b1[2] = {INFINITY, INFINITY}, b2[2] = {INFINITY, INFINITY};
+  int i1[2] = {C, C};
   float cnv = th < BK ? cnf[(size_t)bh * C + min(th, C - 1)] : 0.0f;
   issue(0);
   for (int t = 0; t < tiles; ++t) {
@@ -188,77 +203,112 @@ __global__ __launch_bounds__(256, 2) void km_filter_kernel(
       issue(t + 1);
     }
     const unsigned char* hb = smem + (t & 1) * 2 * T::BYTES;
-    const unsigned char* lb = hb + T::BYTES;
-    floatx16 acc[2];
+    floatx16 acc[2][2];  // [tau][half]
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[tau][r] = 0.0f;
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[tau][hh][r] = 0.0f;
+    // fragments [plane][tau] of k-step s, the next step's read ahead
+    bf16x8 fa[2][2];
+#pragma unroll
+    for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau)
+        fa[pl][tau] = lds_read16(hb + pl * T::BYTES + tau * 32 * T::KROWB + koff[0]);
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
+      bf16x8 fn[2][2];
+      if (s + 1 < KSTEPS) {
 #pragma unroll
-      for (int tau = 0; tau < 2; ++tau) {
-        const bf16x8 a = lds_read16(hb + tau * 32 * T::KROWB + koff[s]);
-        const bf16x8 b = lds_read16(lb + tau * 32 * T::KROWB + koff[s]);
-        acc[tau] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, xf[s], acc[tau], 0, 0, 0);
-        acc[tau] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, xf[s], acc[tau], 0, 0, 0);
+        for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+          for (int tau = 0; tau < 2; ++tau)
+            fn[pl][tau] = lds_read16(hb + pl * T::BYTES + tau * 32 * T::KROWB + koff[s + 1]);
+      }
+#pragma unroll
+      for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh)
+            acc[tau][hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[pl][tau], xf[hh][s],
+                                                                    acc[tau][hh], 0, 0, 0);
+      if (s + 1 < KSTEPS) {
+#pragma unroll
+        for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+          for (int tau = 0; tau < 2; ++tau) fa[pl][tau] = fn[pl][tau];
       }
     }
-    // lane: token l32, centroids t*64 + 32 tau + 8 (r / 4) + 4 h2 + r % 4
+    // lane: token l32 of each half, centroids t*64 + 32 tau + 8 (r / 4) + 4 h2 + r % 4
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = 32 * tau + 8 * (r >> 2) + 4 * h2 + (r & 3);
         const int c = t * BK + row;
-        const float v = fmaf(-2.0f, acc[tau][r], cns[t & 1][row]);
+        const float cnc = cns[t & 1][row];
         if (c < C) {
-          if (v < b1) {
-            b2 = b1;
-            b1 = v;
-            i1 = c;
-          } else {
-            b2 = fminf(b2, v);
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const float v = fmaf(-2.0f, acc[tau][hh][r], cnc);
+            if (v < b1[hh]) {
+              b2[hh] = b1[hh];
+              b1[hh] = v;
+              i1[hh] = c;
+            } else {
+              b2[hh] = fminf(b2[hh], v);
+            }
           }
         }
       }
   }
-  {  // merge the two half-waves (the same token)
-    const float o1 = __shfl_xor(b1, 32), o2 = __shfl_xor(b2, 32);
-    const int oi = __shfl_xor(i1, 32);
-    if (o1 < b1) {
-      b2 = fminf(o2, b1);
-      b1 = o1;
-      i1 = oi;
-    } else if (o1 == b1) {
-      b2 = b1;
-      i1 = min(i1, oi);
-    } else {
-      b2 = fminf(b2, o1);
+  const float cm = __uint_as_float(cmax_bits[bh]);
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    float p1 = b1[hh], p2 = b2[hh];
+    int pi = i1[hh];
+    {  // merge the two half-waves (the same token)
+      const float o1 = __shfl_xor(p1, 32), o2 = __shfl_xor(p2, 32);
+      const int oi = __shfl_xor(pi, 32);
+      if (o1 < p1) {
+        p2 = fminf(o2, p1);
+        p1 = o1;
+        pi = oi;
+      } else if (o1 == p1) {
+        p2 = p1;
+        pi = min(pi, oi);
+      } else {
+        p2 = fminf(p2, o1);
+      }
     }
-  }
-  if (h2 == 0 && tok < N) {
-    const float cm = __uint_as_float(cmax_bits[bh]);
-    const float xn = sqrtf(xx * (1.0f + 1e-5f)) * (1.0f + 1e-6f);
-    const float E = 1.25e-4f * xn * cm + 2.5e-7f * cm * cm;
-    const bool sane = xn * cm < 1e30f && cm * cm < 1e30f && fabsf(b1) < 1e30f &&
-                      fabsf(b2) < 1e30f;
-    if (sane && b2 - b1 > 2.0f * E) {
-      assign[xb + tok] = i1;
-    } else {
-      flag_list[xb + atomicAdd(&flag_cnt[bh], 1)] = tok;
+    const int tok = t0 + 64 * wave + 32 * hh + l32;
+    if (h2 == 0 && tok < N) {
+      const float xn = sqrtf(xx[hh] * (1.0f + 1e-5f)) * (1.0f + 1e-6f);
+      const float E = 1.25e-4f * xn * cm + 2.5e-7f * cm * cm;
+      const bool sane = xn * cm < 1e30f && cm * cm < 1e30f && fabsf(p1) < 1e30f &&
+                        fabsf(p2) < 1e30f;
+      if (sane && p2 - p1 > 2.0f * E) {
+        assign[xb + tok] = pi;
+      } else {
+        flag_list[xb + atomicAdd(&flag_cnt[bh], 1)] = tok;
+      }
     }
   }
 }
 
 // (b) assign[t] for the listed tokens t of each (b, h), from float64
-// distances. Workgroup (g, b, h) takes chunks g, g + G, ... of 64 listed
-// tokens: wave w holds tokens 16 w .. 16 w + 15 of the chunk in registers
-// (lane: token 16 w + lane % 16, channels 8 s + 2 (lane / 16) + 0..1), the
-// centroids stream through LDS 64 at a time (rows padded by two doubles so
-// that 16 lanes reading 16 rows hit different banks), and each lane keeps
-// the best of its column of every 16 x 16 product for the 4 tokens it holds;
-// the 16 lanes of a token group merge at the end. Every distance comes from
+// distances. Workgroup (g, b, h) takes chunks g, g + G, ... of 16 listed
+// tokens, its 4 waves a quarter of the centroids each: a wave holds the 16
+// tokens in registers (lane: token lane % 16, channels 8 s + 2 (lane / 16) +
+// 0..1) and takes its centroids 16 at a time, each lane loading the same
+// channels of one centroid row (all its loads issued together, the next
+// tile's while the current one multiplies); each lane keeps the best of its
+// column of every 16 x 16 product for the 4 tokens it holds, the 16 lanes of
+// a token group merge, then the 4 waves through LDS, smallest (distance,
+// cluster) first, i.e. ties to the lower cluster. Every distance comes from
 // the same float64 instruction sequence whichever tokens share its chunk.
 constexpr int kExactGroups = 16;  // workgroups per (b, h) of km_exact_kernel
 
@@ -270,18 +320,30 @@ __global__ __launch_bounds__(256, 2) void km_exact_kernel(const uint16_t* __rest
                                                           const int32_t* __restrict__ list_cnt,
                                                           int32_t* __restrict__ assign, int N,
                                                           int C) {
-  constexpr int CT = 64, RP = D + 2;  // centroids per tile; LDS row (doubles)
-  __shared__ __align__(16) double cs[CT * RP];
-  __shared__ double cn[CT];
+  constexpr int CT = 16;  // centroids per step of a wave
+  __shared__ double mb[4][16];
+  __shared__ int mi[4][16];
   const int bh = blockIdx.y;
-  const int th = threadIdx.x, lane = th & 63, wave = th >> 6;
+  const int th = threadIdx.x, lane = th & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(th >> 6);
   const int r = lane & 15, g = lane >> 4;
   const size_t xb = (size_t)bh * N;
   const int cnt = min(list_cnt[bh], N);
   const int32_t* lb = list + xb;
   const double* cb0 = cent + (size_t)bh * C * D;
-  for (int base = blockIdx.x * 64; base < cnt; base += gridDim.x * 64) {
-    const int tok = lb[min(base + 16 * wave + r, cnt - 1)];  // repeats past the count are not stored
+  const double* cn0 = cnorm + (size_t)bh * C;
+  // this wave's centroids: [c_lo, c_hi), a quarter of C in whole steps
+  const int per = (C + 4 * CT - 1) / (4 * CT) * CT;
+  const int c_lo = min(wave * per, C), c_hi = min(c_lo + per, C);
+  auto load_tile = [&](int cb, double2(&y)[D / 8], double& cnc) {
+    const int cr = min(cb + r, C - 1);
+    const double* row = cb0 + (size_t)cr * D + 2 * g;
+#pragma unroll
+    for (int s = 0; s < D / 8; ++s) y[s] = *reinterpret_cast<const double2*>(row + 8 * s);
+    cnc = cn0[cr];
+  };
+  for (int base = blockIdx.x * 16; base < cnt; base += gridDim.x * 16) {
+    const int tok = lb[min(base + r, cnt - 1)];  // repeats past the count are not stored
     double2 xr[D / 8];
 #pragma unroll
     for (int s = 0; s < D / 8; ++s) {
@@ -290,45 +352,27 @@ __global__ __launch_bounds__(256, 2) void km_exact_kernel(const uint16_t* __rest
     }
     double best[4] = {INFINITY, INFINITY, INFINITY, INFINITY};
     int bi[4] = {C, C, C, C};
-    for (int cb = 0; cb < C; cb += CT) {
-      __syncthreads();  // the previous tile is consumed
-      for (int p = th; p < CT * D / 2; p += 256) {
-        const int row = p / (D / 2), c2 = p % (D / 2);
-        const int cr = min(cb + row, C - 1);
-        *reinterpret_cast<double2*>(cs + row * RP + 2 * c2) =
-            *reinterpret_cast<const double2*>(cb0 + (size_t)cr * D + 2 * c2);
-      }
-      if (th < CT) cn[th] = cnorm[(size_t)bh * C + min(cb + th, C - 1)];
-      __syncthreads();
-      f64x4 acc[4];
+    double2 y[D / 8];
+    double cnc = 0.0;
+    if (c_lo < c_hi) load_tile(c_lo, y, cnc);
+    for (int cb = c_lo; cb < c_hi; cb += CT) {
+      f64x4 acc = f64x4{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-      for (int b = 0; b < 4; ++b) acc[b] = f64x4{0.0, 0.0, 0.0, 0.0};
-#pragma unroll 4
       for (int s = 0; s < D / 8; ++s) {
-        double2 y[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-          y[b] = *reinterpret_cast<const double2*>(cs + (16 * b + r) * RP + 8 * s + 2 * g);
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-          acc[b] = __builtin_amdgcn_mfma_f64_16x16x4f64(xr[s].x, y[b].x, acc[b], 0, 0, 0);
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-          acc[b] = __builtin_amdgcn_mfma_f64_16x16x4f64(xr[s].y, y[b].y, acc[b], 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(xr[s].x, y[s].x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(xr[s].y, y[s].y, acc, 0, 0, 0);
       }
-      // lane: tokens 4 e + g of the wave's 16, centroid cb + 16 b + r (increasing)
+      const double cnu = cnc;
+      if (cb + CT < c_hi) load_tile(cb + CT, y, cnc);
+      // lane: tokens 4 e + g of the 16, centroid cb + r (increasing per lane)
+      const int c = cb + r;
+      if (c < c_hi) {
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int c = cb + 16 * b + r;
-        if (c < C) {
-          const double cnc = cn[16 * b + r];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const double v = cnc - 2.0 * acc[b][e];
-            if (v < best[e]) {
-              best[e] = v;
-              bi[e] = c;
-            }
+        for (int e = 0; e < 4; ++e) {
+          const double v = cnu - 2.0 * acc[e];
+          if (v < best[e]) {
+            best[e] = v;
+            bi[e] = c;
           }
         }
       }
@@ -344,9 +388,26 @@ __global__ __launch_bounds__(256, 2) void km_exact_kernel(const uint16_t* __rest
           bi[e] = oi;
         }
       }
-      const int li = base + 16 * wave + 4 * e + g;
-      if (r == 0 && li < cnt) assign[xb + lb[li]] = bi[e];
+      if (r == 0) {
+        mb[wave][4 * e + g] = best[e];
+        mi[wave][4 * e + g] = bi[e];
+      }
     }
+    __syncthreads();
+    if (th < 16 && base + th < cnt) {
+      double bv = mb[0][th];
+      int bc = mi[0][th];
+      for (int w = 1; w < 4; ++w) {
+        const double ov = mb[w][th];
+        const int oc = mi[w][th];
+        if (ov < bv || (ov == bv && oc < bc)) {
+          bv = ov;
+          bc = oc;
+        }
+      }
+      assign[xb + lb[base + th]] = min(bc, C - 1);  // (C only if no distance compared: NaN input)
+    }
+    __syncthreads();  // mb, mi are reused
   }
 }
 
@@ -1095,9 +1156,9 @@ hipError_t kmeans_run(const Svg2Launch& a, const uint16_t* x, int C, double* cen
   hipLaunchKernelGGL((km_init_kernel<D>), dim3(C, BH), dim3(D), 0, s, x, cent, cnorm, a.N, C);
   for (int it = 0; it <= a.iters; ++it) {
     hipLaunchKernelGGL(fill_i32_zero_kernel, dim3(1), dim3(256), 0, s, a.kaux, (size_t)2 * BH);
-    hipLaunchKernelGGL((km_planes_kernel<D>), dim3(C, BH), dim3(D), 0, s, cent, cnorm, a.chi,
-                       a.clo, a.cnf, cmax_bits, C);
-    hipLaunchKernelGGL((km_filter_kernel<D>), dim3((a.N + 127) / 128, BH), dim3(256), 0, s, x,
+    hipLaunchKernelGGL((km_planes_kernel<D>), dim3((C + kPlaneClusters - 1) / kPlaneClusters, BH),
+                       dim3(256), 0, s, cent, cnorm, a.chi, a.clo, a.cnf, cmax_bits, C);
+    hipLaunchKernelGGL((km_filter_kernel<D>), dim3((a.N + 255) / 256, BH), dim3(256), 0, s, x,
                        a.chi, a.clo, a.cnf, cmax_bits, assign, a.kflags, flag_cnt, a.N, C);
     hipLaunchKernelGGL((km_exact_kernel<D>), dim3(kExactGroups, BH), dim3(256), 0, s, x, cent,
                        cnorm, a.kflags, flag_cnt, assign, a.N, C);
