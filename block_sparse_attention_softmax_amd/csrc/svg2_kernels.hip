@@ -875,6 +875,10 @@ __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void svg2_a
   const int cq = tile_cluster[(size_t)bh * max_tiles + tile];
   const int qsz = size_q[(size_t)bh * Cq + cq];
   const int local = tile * BQ - qpad_off[(size_t)bh * Cq + cq] + wave * 32 + l32;
+  // a wave whose 32 rows all lie past the cluster's end only copies its share
+  // of the tiles and passes the barriers; its SIMD's matrix core and VALU are
+  // left to the other workgroup's wave
+  const bool idle = __builtin_amdgcn_readfirstlane(local - l32) >= qsz;
   const int prow = tile * BQ + wave * 32 + l32;  // row of the padded permuted Q
 
   bf16x8 qf[KSTEPS];
@@ -1003,7 +1007,7 @@ __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void svg2_a
     if (count > 1) stageK(e1, 1);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
-    qk(kbuf, sc, 0, KSTEPS, [](int) {});
+    if (!idle) qk(kbuf, sc, 0, KSTEPS, [](int) {});
   }
 
   // one chunk: softmax and P V of chunk it (S^T in sc), and with NEXT the
@@ -1088,16 +1092,37 @@ __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void svg2_a
     e1 = e2;
     e2 = e3;
   };
-  int it = 0;
-  for (; it + 2 < count; it += 2) {
-    step(it, std::true_type{}, sc, sn);
-    step(it + 1, std::true_type{}, sn, sc);
-  }
-  if (it + 1 < count) {
-    step(it, std::true_type{}, sc, sn);
-    step(it + 1, std::false_type{}, sn, sc);
-  } else if (it < count) {
-    step(it, std::false_type{}, sc, sn);
+  if (idle) {  // the same barriers and copies, no products
+    for (int it = 0; it < count; ++it) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+      const int e3 = load_ent(it + 3);
+      if (it + 1 < count) {
+        unsigned char* kdst = kbuf + (it & 1) * T::BYTES;
+        unsigned char* vdst = vbuf + ((it + 1) & 1) * T::BYTES;
+        const int ek = it + 2 < count ? e2 : e1;
+        const uint32_t vs = vsel(e1);
+#pragma unroll
+        for (int u = 0; u < LOADS; ++u) dma16(kh + koff_of(ek, u), kdst + 1024 * (u * NW + wave));
+#pragma unroll
+        for (int u = 0; u < LOADS; ++u) dma16(vh + voff_of(vs, u), vdst + 1024 * (u * NW + wave));
+      }
+      e0 = e1;
+      e1 = e2;
+      e2 = e3;
+    }
+  } else {
+    int it = 0;
+    for (; it + 2 < count; it += 2) {
+      step(it, std::true_type{}, sc, sn);
+      step(it + 1, std::true_type{}, sn, sc);
+    }
+    if (it + 1 < count) {
+      step(it, std::true_type{}, sc, sn);
+      step(it + 1, std::false_type{}, sn, sc);
+    } else if (it < count) {
+      step(it, std::false_type{}, sc, sn);
+    }
   }
 
   const float ltot = pair_sum(lsum);
