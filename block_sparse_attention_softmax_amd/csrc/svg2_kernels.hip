@@ -96,8 +96,9 @@ typedef double f64x4 __attribute__((ext_vector_type(4)));
 //  (b) km_exact_kernel: the listed tokens only, with the float64 products
 //      below, so a close call is decided by the float64 distances.
 
-// Per round: the centroid planes, |c|^2 in float32 and cmax per (b, h) (as
-// float bits, maxed into a zeroed word). Workgroup (16 clusters, b, h), 256
+// Per round: the centroid planes, |c|^2 in float32 (rows padded to whole
+// 64-centroid tiles with +inf) and cmax per (b, h) (as float bits, maxed into
+// a zeroed word). Workgroup (16 clusters, b, h), 256
 // threads: the planes element by element, the 16 norms and their maximum in
 // the workgroup, one atomic per workgroup.
 constexpr int kPlaneClusters = 16;
@@ -118,11 +119,14 @@ __global__ __launch_bounds__(256) void km_planes_kernel(const double* __restrict
     chi[base + e] = hi;
     clo[base + e] = bf16_rne((float)(v - bf16_f64(hi)));
   }
+  const int cpad = (C + BK - 1) / BK * BK;  // cnf rows per (b, h): whole 64-centroid tiles
+  if (c0 + kPlaneClusters >= C)  // the last workgroup of the head: +inf past C
+    for (int e = C + t; e < cpad; e += 256) cnf[(size_t)bh * cpad + e] = INFINITY;
   if (t < 64) {
     float nrm = 0.0f;
     if (t < nc) {
       const double cn = cnorm[(size_t)bh * C + c0 + t];
-      cnf[(size_t)bh * C + c0 + t] = (float)cn;
+      cnf[(size_t)bh * cpad + c0 + t] = (float)cn;
       nrm = (float)sqrt(cn) * (1.0f + 1e-6f);  // an upper bound of |c|
     }
 #pragma unroll
@@ -149,8 +153,9 @@ __global__ __launch_bounds__(256, 2) void km_filter_kernel(
   using T = Tile<D>;
   constexpr int NW = 4, KSTEPS = D / 16;
   constexpr int LOADS = BK * D / 8 / 64 / NW;  // 16-byte copies per wave and plane tile
-  __shared__ __align__(16) unsigned char smem[4 * T::BYTES];  // [buffer][plane]
-  __shared__ float cns[2][BK];
+  // [buffer][plane] tiles, then |c|^2 of the two buffers' centroids
+  __shared__ __align__(16) unsigned char smem[4 * T::BYTES + 2 * BK * 4];
+  unsigned char* const cns = smem + 4 * T::BYTES;
   const int bh = blockIdx.y, t0 = blockIdx.x * 256;
   const int th = threadIdx.x, lane = th & 63;
   const int wave = __builtin_amdgcn_readfirstlane(th >> 6);
@@ -176,6 +181,7 @@ __global__ __launch_bounds__(256, 2) void km_filter_kernel(
   const int tiles = (C + BK - 1) / BK;
   const uint16_t* hib = chi + (size_t)bh * C * D;
   const uint16_t* lob = clo + (size_t)bh * C * D;
+  const float* cnb = cnf + (size_t)bh * ((C + BK - 1) / BK * BK);
   auto issue = [&](int t) {
     unsigned char* buf = smem + (t & 1) * 2 * T::BYTES;
 #pragma unroll
@@ -186,22 +192,18 @@ __global__ __launch_bounds__(256, 2) void km_filter_kernel(
       dma16(hib + src, buf + 1024 * (u * NW + wave));
       dma16(lob + src, buf + T::BYTES + 1024 * (u * NW + wave));
     }
+    if (wave == 0 && lane < BK / 4) dma16(cnb + t * BK + 4 * lane, cns + (t & 1) * BK * 4);
   };
   int koff[KSTEPS];
 #pragma unroll
   for (int s = 0; s < KSTEPS; ++s) koff[s] = l32 * T::KROWB + (T::kchunk(l32, 2 * s + h2) << 4);
   float b1[2] = {INFINITY, INFINITY}, b2[2] = {INFINITY, INFINITY};
   int i1[2] = {C, C};
-  float cnv = th < BK ? cnf[(size_t)bh * C + min(th, C - 1)] : 0.0f;
   issue(0);
   for (int t = 0; t < tiles; ++t) {
-    if (th < BK) cns[t & 1][th] = cnv;
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of tile t landed
     __syncthreads();                     // every wave's copies landed; the other buffer is free
-    if (t + 1 < tiles) {
-      cnv = th < BK ? cnf[(size_t)bh * C + min((t + 1) * BK + th, C - 1)] : 0.0f;
-      issue(t + 1);
-    }
+    if (t + 1 < tiles) issue(t + 1);
     const unsigned char* hb = smem + (t & 1) * 2 * T::BYTES;
     floatx16 acc[2][2];  // [tau][half]
 #pragma unroll
@@ -243,24 +245,26 @@ __global__ __launch_bounds__(256, 2) void km_filter_kernel(
       }
     }
     // lane: token l32 of each half, centroids t*64 + 32 tau + 8 (r / 4) + 4 h2 + r % 4
+    // (+inf |c|^2 past C: such rows never win); the four |c|^2 of a register
+    // group are read as one 16-byte fragment
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = 32 * tau + 8 * (r >> 2) + 4 * h2 + (r & 3);
-        const int c = t * BK + row;
-        const float cnc = cns[t & 1][row];
-        if (c < C) {
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int row0 = 32 * tau + 8 * q4 + 4 * h2;
+        const float4 c4 = __builtin_bit_cast(float4, lds_read16(cns + ((t & 1) * BK + row0) * 4));
+        const float cn4[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * q4 + e, c = t * BK + row0 + e;
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
-            const float v = fmaf(-2.0f, acc[tau][hh][r], cnc);
-            if (v < b1[hh]) {
-              b2[hh] = b1[hh];
-              b1[hh] = v;
-              i1[hh] = c;
-            } else {
-              b2[hh] = fminf(b2[hh], v);
-            }
+            // best two: b2 = median of (b1, b2, v) as b1 <= b2; b1 = min
+            const float v = fmaf(-2.0f, acc[tau][hh][r], cn4[e]);
+            const bool lt = v < b1[hh];
+            b2[hh] = __builtin_amdgcn_fmed3f(b1[hh], b2[hh], v);
+            b1[hh] = lt ? v : b1[hh];
+            i1[hh] = lt ? c : i1[hh];
           }
         }
       }
@@ -1290,7 +1294,7 @@ size_t svg2_layout(Svg2Launch& a, unsigned char* w) {
   };
   a.chi = reinterpret_cast<uint16_t*>(take(BH * Cm * d * 2));
   a.clo = reinterpret_cast<uint16_t*>(take(BH * Cm * d * 2));
-  a.cnf = reinterpret_cast<float*>(take(BH * Cm * 4));
+  a.cnf = reinterpret_cast<float*>(take(BH * ((Cm + BK - 1) / BK * BK) * 4));
   a.kaux = reinterpret_cast<int32_t*>(take(BH * 2 * 4));
   a.kflags = reinterpret_cast<int32_t*>(take(BH * N * 4));
   a.centq = reinterpret_cast<double*>(take(BH * a.Cq * d * 8));
