@@ -525,80 +525,38 @@ __global__ __launch_bounds__(256) void km_scatter_kernel(const int32_t* __restri
 }
 
 // Centroid c = the mean of its members in token order (float64); an empty
-// cluster keeps its centroid; |c|^2. Workgroup (16 clusters, b, h), 256
-// threads: 16 lanes per cluster, each lane D/16 consecutive channels (one
-// 16- or 8-byte load per member row, eight rows in flight), every channel
-// summed in token order. |c|^2 is reduced in the order of a 64-thread
-// butterfly over the channel index (bits 5 .. 0, the two 64-channel halves
-// of d = 128 added last), so it has the bits of a one-channel-per-thread
-// workgroup sum.
-constexpr int kUpdateClusters = 16;
-
+// cluster keeps its centroid; |c|^2. Grid (C, B*H), D threads.
 template <int D>
-__global__ __launch_bounds__(256) void km_update_kernel(const uint16_t* __restrict__ x,
-                                                        const int32_t* __restrict__ perm,
-                                                        const int32_t* __restrict__ size,
-                                                        const int32_t* __restrict__ off,
-                                                        double* __restrict__ cent,
-                                                        double* __restrict__ cnorm, int N, int C) {
-  constexpr int CPL = D / 16;  // channels per lane: 8 (d = 128) or 4 (d = 64)
-  const int bh = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int c = blockIdx.x * kUpdateClusters + 4 * wave + (lane >> 4), sub = lane & 15;
-  const bool valid = c < C;
-  const int n = valid ? size[(size_t)bh * C + c] : 0;
-  double* cp = cent + ((size_t)bh * C + min(c, C - 1)) * D + sub * CPL;
-  double v[CPL];
+__global__ __launch_bounds__(D) void km_update_kernel(const uint16_t* __restrict__ x,
+                                                      const int32_t* __restrict__ perm,
+                                                      const int32_t* __restrict__ size,
+                                                      const int32_t* __restrict__ off,
+                                                      double* __restrict__ cent,
+                                                      double* __restrict__ cnorm, int N, int C) {
+  __shared__ double red[2];
+  const int c = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+  const int n = size[(size_t)bh * C + c], o0 = off[(size_t)bh * (C + 1) + c];
+  double* cp = cent + ((size_t)bh * C + c) * D + t;
+  double v = *cp;
   if (n > 0) {
-    const int32_t* pm = perm + (size_t)bh * N + off[(size_t)bh * (C + 1) + c];
-    const uint16_t* xh = x + (size_t)bh * N * D + sub * CPL;
-    double acc[CPL];
-#pragma unroll
-    for (int k = 0; k < CPL; ++k) acc[k] = 0.0;
-    using Row = typename std::conditional<CPL == 8, uint4, uint2>::type;
-    auto add_row = [&](const Row& w) {
-      const uint32_t* u = reinterpret_cast<const uint32_t*>(&w);
-#pragma unroll
-      for (int k = 0; k < CPL; ++k)
-        acc[k] += bf16_f64((uint16_t)(k & 1 ? u[k >> 1] >> 16 : u[k >> 1] & 0xFFFFu));
-    };
+    // members in token order; eight rows in flight at a time, summed in order
+    const int32_t* pm = perm + (size_t)bh * N + o0;
+    const uint16_t* xh = x + (size_t)bh * N * D + t;
+    double acc = 0.0;
     int m = 0;
     for (; m + 8 <= n; m += 8) {
-      Row w[8];
+      uint16_t xv[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) w[e] = *reinterpret_cast<const Row*>(xh + (size_t)pm[m + e] * D);
+      for (int e = 0; e < 8; ++e) xv[e] = xh[(size_t)pm[m + e] * D];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) add_row(w[e]);
+      for (int e = 0; e < 8; ++e) acc += bf16_f64(xv[e]);
     }
-    for (; m < n; ++m) add_row(*reinterpret_cast<const Row*>(xh + (size_t)pm[m] * D));
-#pragma unroll
-    for (int k = 0; k < CPL; ++k) v[k] = acc[k] / n;
-#pragma unroll
-    for (int k = 0; k < CPL; ++k) cp[k] = v[k];
-  } else {
-#pragma unroll
-    for (int k = 0; k < CPL; ++k) v[k] = valid ? cp[k] : 0.0;
+    for (; m < n; ++m) acc += bf16_f64(xh[(size_t)pm[m] * D]);
+    v = acc / n;
+    *cp = v;
   }
-  // channel bit b >= log2(CPL) lies in the lane (xor 2^b / CPL), lower bits in the lane's own
-  // channels
-  double q[CPL];
-#pragma unroll
-  for (int k = 0; k < CPL; ++k) q[k] = v[k] * v[k];
-#pragma unroll
-  for (int b = 5; b >= 0; --b) {
-    if ((1 << b) >= CPL) {
-#pragma unroll
-      for (int k = 0; k < CPL; ++k) q[k] += __shfl_xor(q[k], (1 << b) / CPL);
-    } else {
-      double t2[CPL];
-#pragma unroll
-      for (int k = 0; k < CPL; ++k) t2[k] = q[k] + q[k ^ (1 << b)];
-#pragma unroll
-      for (int k = 0; k < CPL; ++k) q[k] = t2[k];
-    }
-  }
-  double sq = q[0];
-  if (D == 128) sq += __shfl_xor(sq, 8);  // the two 64-channel halves
-  if (valid && sub == 0) cnorm[(size_t)bh * C + c] = sq;
+  const double s = block_sum<D>(v * v, red);
+  if (t == 0) cnorm[(size_t)bh * C + c] = s;
 }
 
 // ------------------------------------------------------- centroid Top-p
@@ -1243,9 +1201,8 @@ hipError_t kmeans_run(const Svg2Launch& a, const uint16_t* x, int C, double* cen
     hipLaunchKernelGGL(km_scatter_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s,
                        assign, a.rank, a.ccount, off, perm, a.N, C, nch, rows);
     if (it < a.iters)
-      hipLaunchKernelGGL((km_update_kernel<D>),
-                         dim3((C + kUpdateClusters - 1) / kUpdateClusters, BH), dim3(256), 0, s, x,
-                         perm, size, off, cent, cnorm, a.N, C);
+      hipLaunchKernelGGL((km_update_kernel<D>), dim3(C, BH), dim3(D), 0, s, x, perm, size, off,
+                         cent, cnorm, a.N, C);
   }
   return hipGetLastError();
 }
