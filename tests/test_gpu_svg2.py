@@ -107,3 +107,41 @@ def test_svg2_in_two_parts_equals_one_call(name, B, H, N, d, bq, Cq, Ck):
     assert_all_written(one)
     assert torch.equal(a.view(torch.int16), one.view(torch.int16))
     assert torch.equal(b.view(torch.int16), one.view(torch.int16))
+
+
+@pytest.mark.parametrize("kind,N,d,Cq,Ck", [("ties", 600, 128, 8, 12), ("ties", 520, 64, 6, 10),
+                                             ("close", 3000, 128, 16, 24)])
+def test_svg2_assignment_close_calls(kind, N, d, Cq, Ck):
+    """Tokens the bf16 filter of the assignment cannot decide: exact ties (rows
+    drawn from five distinct vectors, so equal centroids recur and their tokens
+    go to the lower cluster) and near ties (rows within 1e-3 of a few vectors,
+    most of them listed for the float64 pass, many 16-token chunks per head).
+    The clustering must still equal the oracle's: same useful pairs, same output."""
+    B, H = 1, 2
+    rng = np.random.default_rng(N + 7 * Ck)
+    base = rng.standard_normal((5, d))
+    def rows():
+        pick = base[rng.integers(0, 5, (B, H, N))]
+        if kind == "close":
+            pick = pick + 1e-3 * rng.standard_normal((B, H, N, d))
+        return f64_to_bf16_bits(pick)
+    Q, K = rows(), rows()
+    V = f64_to_bf16_bits(rng.standard_normal((B, H, N, d)))
+    print(f"\n[svg2 close calls] {kind} N={N} d={d} Cq={Cq} Ck={Ck}", flush=True)
+    q = to_gpu(Q)
+    ws = torch.empty(S.svg2_workspace_bytes(B, H, N, d, 128, Cq, Ck), dtype=torch.uint8,
+                     device="cuda")
+    o = S.svg2_attn_fwd(q, to_gpu(K), to_gpu(V), Cq, Ck, iters=3, p_mass=0.9, out=nan_like(q),
+                        workspace=ws)
+    counts = S.svg2_attn_pair_counts(q, Cq, Ck, ws).cpu().numpy()
+    torch.cuda.synchronize()
+    assert_all_written(o)
+    got = _np(o)
+    scale = S.default_scale(d)
+    for h in range(H):
+        ref, qa, ka, sel = O.svg2_attention_head(O.bf16_to_f64(Q[0, h]), O.bf16_to_f64(K[0, h]),
+                                                 O.bf16_to_f64(V[0, h]), Cq, Ck, 3, scale, 0.9)
+        mx, mean = compare_outputs(got[0, h], ref)
+        assert counts[0, h, 0] == _useful_pairs(qa, ka, sel, Cq, Ck)
+        print(f"[svg2 close calls] h={h}: clusters used q {len(np.unique(qa))} k "
+              f"{len(np.unique(ka))}, max {mx:.2e} mean {mean:.2e}", flush=True)
