@@ -737,7 +737,7 @@ size_t sparse_linear_workspace_bytes(int B, int H, int N, int d) {
   const int rc = check_shape(B, H, N, d, 128, 64);
   g_last_error = saved;
   if (rc != SPARGE_OK) return 0;
-  return sparge::linear_workspace_bytes(B, H, N, d);
+  return sparge::linear_workspace_bytes(B, H, N, d, d);
 }
 
 }  // extern "C"
@@ -756,10 +756,10 @@ int linear_impl(const char* name, int mode, const void* q, const void* k, const 
   if (!aligned(alpha, mode == sparge::kLinMix ? 16 : 4) || !aligned(workspace, 16) ||
       !aligned(lse, 4))
     return fail(SPARGE_ERR_INVALID_ARG, "alpha / workspace / lse misaligned");
-  if (workspace_bytes < sparge::linear_workspace_bytes(B, H, N, d))
-    return fail(SPARGE_ERR_INVALID_ARG, "workspace too small");
   if (block_q != d)
     return fail(SPARGE_ERR_UNSUPPORTED, "the linear branch is built for block_q == d (64 or 128)");
+  if (workspace_bytes < sparge::linear_workspace_bytes(B, H, N, d, block_q))
+    return fail(SPARGE_ERR_INVALID_ARG, "workspace too small");
   sparge::AttnLaunch a{};
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -775,17 +775,7 @@ int linear_impl(const char* name, int mode, const void* q, const void* k, const 
   a.lin_mode = mode;
   a.drop_below = drop_below;
   a.lse = lse;
-  const size_t BH = (size_t)B * H, packed = sparge::attn_workspace_bytes(B, H, N, d);
-  unsigned char* ws = static_cast<unsigned char*>(workspace);
-  a.vt = reinterpret_cast<uint16_t*>(ws);
-  a.phikt = reinterpret_cast<uint16_t*>(ws + packed);
-  float* f = reinterpret_cast<float*>(ws + 2 * packed);
-  a.lin_h = f;
-  a.lin_z = a.lin_h + BH * d * d;
-  a.part_h = a.lin_z + BH * d;
-  a.part_z = a.part_h + BH * sparge::kLinSplit * d * d;
-  a.lin_on = reinterpret_cast<int32_t*>(a.part_z + BH * sparge::kLinSplit * d);
-  a.lin_lists = a.lin_on + H;
+  sparge::linear_layout(a, static_cast<unsigned char*>(workspace), B, H, N, d, block_q);
   const hipError_t e = sparge::launch_attn(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, name);
   return SPARGE_OK;

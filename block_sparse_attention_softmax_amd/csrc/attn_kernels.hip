@@ -34,6 +34,324 @@ namespace {
 // float32 sums and bf16 products carry without loss of relative precision.
 constexpr float kRescaleLog2 = 8.0f;
 
+// ------------------------------------------------ linear branch: H_D, z_D
+// For every query block i, H_D = sum over the key blocks j it does not list
+// of phi(K_j)^T V_j and z_D = sum of phi(K_j) over the same blocks, as a
+// matrix product over the key blocks: the per-block summaries H_j, z_j are
+// formed once, with the V packing (linear_pack_kernel), the drop matrix
+// M[i][j] in {0, 1} once per mask (linear_mdrop_kernel), and [H_D, z_D]_i =
+// sum_j M[i][j] [H_j, z_j] on the matrix cores (linear_hd_kernel). The attention kernel then forms
+// O_l = phi(Q) H_D / (phi(Q) . z_D) in its epilogue.
+//
+// Summary rows: hj[bh][j][plane][D*D + D], two bf16 planes (hi = bf16(x),
+// lo = bf16(x - hi), about 16 significant bits) of H_j^T (row b = V channel,
+// column a = phi channel, at b*D + a), then of z_j (at D*D + a).
+template <int D>
+constexpr int lin_cols() { return D * D + D; }
+
+// V packing fused with the summaries: one workgroup per (key block j, b h),
+// 2*D threads (D / 32 waves). Every thread packs its piece of V_j into vt as
+// pack_kernel does; for the heads whose linear branch is evaluated (lin_on)
+// it also leaves that piece, and the same piece of bf16(phi(K_j)), in two LDS
+// tiles [D][64 slots] (rows of 128 bytes, chunks swizzled as in V^T tiles).
+// Wave w then forms rows 32 w .. 32 w + 31 of H_j^T = V_j^T phi(K_j) (the
+// 64-slot reduction pairs V and phi(K) slot by slot; keys past N are zero in
+// both) with fp32 accumulation of exact bf16 products, D / 32 output tiles
+// with phi(K) as the row operand so that each lane holds 4 consecutive
+// columns, and writes each plane of its 32-row band, which is contiguous in
+// hj, through an LDS staging area as 1 KB store instructions. Threads t < D
+// sum phi(K)^T row t over the slots in slot order for z_j.
+template <int D>
+__global__ __launch_bounds__(2 * D) void linear_pack_kernel(const uint16_t* __restrict__ v,
+                                                            const uint16_t* __restrict__ k,
+                                                            uint16_t* __restrict__ vt,
+                                                            uint16_t* __restrict__ hj, int N,
+                                                            int n_k,
+                                                            const int32_t* __restrict__ lin_on,
+                                                            int H) {
+  constexpr int DT = D / 32, COLS = lin_cols<D>(), ROWB = BK * 2, TBYTES = D * ROWB;
+  constexpr int PITCH = D * 2 + 16;  // staging row pitch: 8-byte writes by 32 rows spread out
+  constexpr int SMEM = (2 * TBYTES > DT * 32 * PITCH) ? 2 * TBYTES : DT * 32 * PITCH;
+  __shared__ __align__(16) unsigned char smem[SMEM];
+  unsigned char* const vtile = smem;
+  unsigned char* const ptile = smem + TBYTES;
+  using T = Tile<D>;
+  const int j = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+  const int q = t & 15, c = t >> 4;
+  const int slot0 = 16 * (q >> 2) + 8 * (q & 1) + 4 * ((q >> 1) & 1);
+  const bool lin = lin_on[bh % H] != 0;  // the same for the whole workgroup
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    if (w == 1 && !lin) return;
+    const uint16_t* src = (w == 0 ? v : k) + ((size_t)bh * N + (size_t)j * BK) * D + c * 8;
+    uint32_t x[4][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int key = 4 * q + r;
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (j * BK + key < N) {
+        u = *reinterpret_cast<const uint4*>(src + (size_t)key * D);
+        if (w == 1) {  // phi(K), rounded to bf16
+          uint32_t* p = &u.x;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            p[e] = f32_to_bf16_rne(elu1(bf16_lo(p[e]))) |
+                   (f32_to_bf16_rne(elu1(bf16_hi(p[e]))) << 16);
+        }
+      }
+      x[r][0] = u.x; x[r][1] = u.y; x[r][2] = u.z; x[r][3] = u.w;
+    }
+    uint16_t* dst = vt + ((size_t)bh * n_k + j) * (size_t)D * BK + (size_t)(8 * c) * BK + slot0;
+    unsigned char* tl = w == 0 ? vtile : ptile;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {  // d = 8c + 2e (low halves) and 8c + 2e + 1 (high)
+      uint2 lo, hi;
+      lo.x = (x[0][e] & 0xFFFFu) | (x[1][e] << 16);
+      lo.y = (x[2][e] & 0xFFFFu) | (x[3][e] << 16);
+      hi.x = (x[0][e] >> 16) | (x[1][e] & 0xFFFF0000u);
+      hi.y = (x[2][e] >> 16) | (x[3][e] & 0xFFFF0000u);
+      if (w == 0) {
+        *reinterpret_cast<uint2*>(dst + (size_t)(2 * e) * BK) = lo;
+        *reinterpret_cast<uint2*>(dst + (size_t)(2 * e + 1) * BK) = hi;
+      }
+      if (lin) {
+        const int r0 = 8 * c + 2 * e, r1 = r0 + 1;
+        *reinterpret_cast<uint2*>(tl + r0 * ROWB + (T::vchunk(r0, slot0 >> 3) << 4) + 2 * (slot0 & 7)) = lo;
+        *reinterpret_cast<uint2*>(tl + r1 * ROWB + (T::vchunk(r1, slot0 >> 3) << 4) + 2 * (slot0 & 7)) = hi;
+      }
+    }
+  }
+  __syncthreads();  // both tiles complete (only heads with lin get here)
+  const int lane = t & 63, wave = t >> 6, h2 = lane >> 5, l32 = lane & 31;
+  floatx16 acc[DT];
+#pragma unroll
+  for (int ta = 0; ta < DT; ++ta) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[ta][r] = 0.0f;
+    const int ra = 32 * ta + l32, rb = 32 * wave + l32;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const bf16x8 pa = lds_read16(ptile + ra * ROWB + (T::vchunk(ra, 2 * ks + h2) << 4));
+      const bf16x8 vb = lds_read16(vtile + rb * ROWB + (T::vchunk(rb, 2 * ks + h2) << 4));
+      acc[ta] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, vb, acc[ta], 0, 0, 0);
+    }
+  }
+  float z = 0.0f;
+  if (t < D) {
+#pragma unroll
+    for (int ch = 0; ch < BK / 8; ++ch) {
+      const bf16x8 p8 = lds_read16(ptile + t * ROWB + (T::vchunk(t, ch) << 4));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) z += (float)p8[e];
+    }
+  }
+  __syncthreads();  // every wave is done with the tiles before the staging reuses them
+  // lane: H^T[b = 32 wave + l32][a = 32 ta + 8 g + 4 h2 + (0..3)] = acc[ta][4 g .. 4 g + 3]
+  unsigned char* stg = smem + wave * 32 * PITCH;
+  uint16_t* out = hj + ((size_t)bh * n_k + j) * 2 * COLS + (size_t)(32 * wave) * D;
+#pragma unroll
+  for (int pl = 0; pl < 2; ++pl) {
+#pragma unroll
+    for (int ta = 0; ta < DT; ++ta)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        uint32_t w2[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float x0 = acc[ta][4 * g + 2 * e], x1 = acc[ta][4 * g + 2 * e + 1];
+          const uint32_t h0 = f32_to_bf16_rne(x0), h1 = f32_to_bf16_rne(x1);
+          w2[e] = pl == 0 ? (h0 | (h1 << 16))
+                          : (f32_to_bf16_rne(x0 - __uint_as_float(h0 << 16)) |
+                             (f32_to_bf16_rne(x1 - __uint_as_float(h1 << 16)) << 16));
+        }
+        *reinterpret_cast<uint2*>(stg + l32 * PITCH + 2 * (32 * ta + 8 * g + 4 * h2)) =
+            make_uint2(w2[0], w2[1]);
+      }
+    wave_lds_fence();
+#pragma unroll
+    for (int it = 0; it < D / 16; ++it) {  // 32 rows x D / 8 chunks, 64 per instruction
+      const int idx = 64 * it + lane, row = idx / (D / 8), ch = idx % (D / 8);
+      *reinterpret_cast<bf16x8*>(out + (size_t)pl * COLS + row * D + 8 * ch) =
+          lds_read16(stg + row * PITCH + 16 * ch);
+    }
+    wave_lds_fence();
+  }
+  if (t < D) {
+    uint16_t* zo = hj + ((size_t)bh * n_k + j) * 2 * COLS + D * D + t;
+    const uint32_t hi = f32_to_bf16_rne(z);
+    zo[0] = (uint16_t)hi;
+    zo[COLS] = (uint16_t)f32_to_bf16_rne(z - __uint_as_float(hi << 16));
+  }
+}
+
+// mdrop[bh][i][j] = bf16 1.0 where query block i does not list key block j,
+// 0 where it does and for j in [n_k, n_kp) (rows of n_kp = n_k rounded up to
+// 32). One wave per (b, h, query block): the list as a bitmap in LDS, 4096
+// key blocks at a time, then rows of 8 entries per lane.
+__global__ __launch_bounds__(256) void linear_mdrop_kernel(const int32_t* __restrict__ kv_idx,
+                                                           const int32_t* __restrict__ kv_cnt,
+                                                           uint16_t* __restrict__ mdrop, int n_k,
+                                                           int n_kp, int rows) {
+  constexpr int CH = 4096;
+  __shared__ uint32_t bits[4][CH / 32];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + wave;
+  if (row >= rows) return;
+  const int count = min(max(kv_cnt[row], 0), n_k);
+  const int32_t* ids = kv_idx + (size_t)row * n_k;
+  uint16_t* out = mdrop + (size_t)row * n_kp;
+  uint32_t* b = bits[wave];
+  for (int j0 = 0; j0 < n_kp; j0 += CH) {
+    for (int w = lane; w < CH / 32; w += 64) b[w] = 0u;
+    wave_lds_fence();
+    for (int e = lane; e < count; e += 64) {
+      const int j = min(max(ids[e], 0), n_k - 1) - j0;
+      if (j >= 0 && j < CH) atomicOr(&b[j >> 5], 1u << (j & 31));
+    }
+    wave_lds_fence();
+    for (int jj = 8 * lane; jj < min(CH, n_kp - j0); jj += 512) {
+      const uint32_t word = b[jj >> 5] >> (jj & 31);  // bits of jj .. jj + 7
+      uint32_t v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int ja = j0 + jj + 2 * e;
+        const uint32_t lo = (ja < n_k && !((word >> (2 * e)) & 1u)) ? 0x3F80u : 0u;
+        const uint32_t hi = (ja + 1 < n_k && !((word >> (2 * e + 1)) & 1u)) ? 0x3F80u : 0u;
+        v[e] = lo | (hi << 16);
+      }
+      *reinterpret_cast<uint4*>(out + j0 + jj) = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+    wave_lds_fence();
+  }
+}
+
+// [H_D, z_D]^T[col][i] = sum_j (hi_j + lo_j)[col] M[i][j]. Workgroup (128
+// columns, 256 query blocks, b h), 4 waves of 32 columns x 256 query blocks
+// (8 accumulator tiles). The key blocks go 32 at a time: the two planes' rows
+// j .. j+31 of the workgroup's columns and M's columns j .. j+31 of its rows,
+// double-buffered in one LDS array by direct-to-LDS copies (rows past n_k and
+// n_q repeat the last one; M is 0 there). The plane operand (8 consecutive key
+// blocks of one column per lane) comes from transposing LDS reads, whose 4
+// rows x 32 bytes per 16 lanes the chunk swizzle c ^ 4 (row mod 4) spreads
+// over all banks; M's 64-byte rows take the swizzle c ^ ((row / 4) mod 4).
+// Output per query block: H_D^T as two bf16 planes [2][D][D] (the same
+// hi / lo split) and z_D as float32 [D]; heads whose branch is dropped are
+// skipped.
+template <int D>
+__global__ __launch_bounds__(256, 2) void linear_hd_kernel(const uint16_t* __restrict__ hj,
+                                                           const uint16_t* __restrict__ mdrop,
+                                                           uint16_t* __restrict__ hd,
+                                                           float* __restrict__ zd, int n_q,
+                                                           int n_k, int n_kp,
+                                                           const int32_t* __restrict__ lin_on,
+                                                           int H) {
+  constexpr int COLS = lin_cols<D>(), CB = 128, IB = 256, JB = 32;
+  constexpr int HBYTES = 2 * JB * CB * 2, MBYTES = IB * JB * 2, BUF = HBYTES + MBYTES;
+  __shared__ __align__(16) unsigned char smem[2 * BUF];
+  const int bh = blockIdx.z;
+  if (!lin_on[bh % H]) return;
+  const int c0 = blockIdx.x * CB, i0 = blockIdx.y * IB;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int h2 = lane >> 5, l32 = lane & 31;
+  const uint16_t* hsrc = hj + (size_t)bh * n_k * 2 * COLS;
+  const uint16_t* msrc = mdrop + (size_t)bh * n_q * n_kp;
+  // copies of one buffer: 16 KB of plane rows (wave w, copy u: plane u / 2,
+  // rows 4 (4 (u % 2) + w) .. +3), then 16 KB of M (rows 16 (4 u + w) .. +15)
+  auto issue = [&](int jb, int b) {
+    unsigned char* buf = smem + b * BUF;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {  // lane: row r0 + lane / 16, physical chunk lane % 16
+      const int pl = u >> 1, r0 = 4 * (4 * (u & 1) + wave), r = r0 + (lane >> 4);
+      const int lc = (lane & 15) ^ ((r & 3) << 2);  // the logical chunk this slot holds
+      const int col = min(c0 + 8 * lc, COLS - 8);
+      const int jr = min(jb + r, n_k - 1);
+      dma16(hsrc + ((size_t)jr * 2 + pl) * COLS + col, buf + pl * (JB * CB * 2) + r0 * (CB * 2));
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {  // lane: row r0 + lane / 4, physical chunk lane % 4
+      const int r0 = 16 * (4 * u + wave), r = r0 + (lane >> 2);
+      const int lc = (lane & 3) ^ ((r >> 2) & 3);
+      const int ir = min(i0 + r, n_q - 1);
+      dma16(msrc + (size_t)ir * n_kp + jb + 8 * lc, buf + HBYTES + r0 * (JB * 2));
+    }
+  };
+  floatx16 acc[IB / 32];
+#pragma unroll
+  for (int ti = 0; ti < IB / 32; ++ti)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[ti][r] = 0.0f;
+  // transposing-read addresses (bytes within a plane) for k-step ks and read
+  // tt: the lane addresses row 16 ks + 8 h2 + 4 tt + (lane & 15) / 4 and the
+  // 4 columns 32 wave + 16 ((lane >> 4) & 1) + 4 (lane & 3)
+  const int g16 = lane & 15, colb = 32 * wave + 16 * ((lane >> 4) & 1) + 4 * (g16 & 3);
+  auto tr_addr = [&](int ks, int tt) {
+    const int r = 16 * ks + 8 * h2 + 4 * tt + (g16 >> 2);
+    const int lc = colb >> 3, pc = lc ^ ((r & 3) << 2);
+    return (uint32_t)(r * (CB * 2) + 16 * pc + 2 * (colb & 7));
+  };
+  const int nb = (n_kp + JB - 1) / JB;
+  issue(0, 0);
+  for (int bi = 0; bi < nb; ++bi) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of block bi landed
+    __syncthreads();                     // every wave's copies landed; the other buffer is free
+    if (bi + 1 < nb) issue((bi + 1) * JB, (bi + 1) & 1);
+    const unsigned char* buf = smem + (bi & 1) * BUF;
+    const uint32_t pbase = lds_addr(buf);
+    static_assert(JB == 32, "two k-steps per block: eight transposing reads");
+    uint32_t ad[8];
+    v4i16 fr[8];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+          ad[4 * ks + 2 * pl + tt] = pbase + pl * (JB * CB * 2) + tr_addr(ks, tt);
+    lds_read_tr<8>(fr, ad);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 ahi = join_tr(fr[4 * ks], fr[4 * ks + 1]);
+      const bf16x8 alo = join_tr(fr[4 * ks + 2], fr[4 * ks + 3]);
+#pragma unroll
+      for (int ti = 0; ti < IB / 32; ++ti) {
+        const int r = 32 * ti + l32, lc = 2 * ks + h2;
+        const bf16x8 bm = lds_read16(buf + HBYTES + r * (JB * 2) + 16 * (lc ^ ((r >> 2) & 3)));
+        acc[ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, bm, acc[ti], 0, 0, 0);
+        acc[ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, bm, acc[ti], 0, 0, 0);
+      }
+    }
+  }
+  // lane: query block i0 + 32 ti + l32, columns c0 + 32 wave + 8 (r / 4) + 4 h2 + r % 4
+#pragma unroll
+  for (int ti = 0; ti < IB / 32; ++ti) {
+    const int i = i0 + 32 * ti + l32;
+    if (i >= n_q) continue;
+    const size_t qb = (size_t)bh * n_q + i;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int col = c0 + 32 * wave + 8 * g + 4 * h2;
+      if (col + 4 <= D * D) {
+        uint32_t hw[2], lw[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float x0 = acc[ti][4 * g + 2 * e], x1 = acc[ti][4 * g + 2 * e + 1];
+          const uint32_t h0 = f32_to_bf16_rne(x0), h1 = f32_to_bf16_rne(x1);
+          hw[e] = h0 | (h1 << 16);
+          lw[e] = f32_to_bf16_rne(x0 - __uint_as_float(h0 << 16)) |
+                  (f32_to_bf16_rne(x1 - __uint_as_float(h1 << 16)) << 16);
+        }
+        uint16_t* dst = hd + qb * 2 * D * D + col;
+        *reinterpret_cast<uint2*>(dst) = make_uint2(hw[0], hw[1]);
+        *reinterpret_cast<uint2*>(dst + D * D) = make_uint2(lw[0], lw[1]);
+      } else if (col < COLS) {
+        *reinterpret_cast<float4*>(zd + qb * D + (col - D * D)) =
+            make_float4(acc[ti][4 * g], acc[ti][4 * g + 1], acc[ti][4 * g + 2], acc[ti][4 * g + 3]);
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------ attention kernel
 // Software-pipelined over the listed blocks: the S^T product of block it+1
 // is issued while the softmax and the P V product of block it run, so the
@@ -45,84 +363,44 @@ constexpr float kRescaleLog2 = 8.0f;
 // spread one per k-step over the S^T product instead of issued together,
 // so the waves of a CU do not queue behind each other's copies.
 //
-// LIN adds the linear branch over the dropped blocks with a second set of
-// BQ/32 waves in the workgroup (H waves), which pass the attention waves'
-// barriers one for one (the attention waves' loop is the plain one). Per
-// listed block, H wave w accumulates rows 32w..32w+31 of H_kept +=
-// phi(K_j)^T V_j and its share of z_kept += sum phi(K_j), from the V^T tile
-// the attention waves staged and a phi(K)^T tile the H waves copy beside it;
-// when more than half of the blocks are listed they instead sum the blocks
-// not listed (found from a bitmap of the list), copying both tiles of those
-// themselves, and H_D is that sum rather than H_tot - H_kept.
-// The H waves' matrix products fill the attention waves' softmax gaps on the
-// same SIMDs, and the attention waves carry no extra accumulator. At the end
-// the H waves form H_D (and z_D likewise) in LDS, then
-// O_l = phi(Q) H_D / (phi(Q) . z_D) for the queries of the attention wave of
-// the same index (three-term split-bf16 MFMA product, about 16 significant
-// bits per operand), and hand O_l and the scale alpha[h] / (phi(Q) . z_D)
-// over through LDS in the attention wave's own register layout; the
-// attention wave writes O = O_s + alpha[h] * O_l, or in the SLA2 mix (SLA2
-// page, section 2A) O = alpha[h][c] O_s + (1 - alpha[h][c]) O_l with the
-// scale 1 / (phi(Q) . z_D). Heads whose branch is dropped (lin_on = 0) are
-// left to a second launch of the plain kernel, which scales O_s by
-// alpha[h][c] in the mix; each launch maps its workgroups onto its own heads
-// through the lists of linear_flags_kernel.
-//
-// SEL (always with LIN) adds the head selection and the alpha scaling of the
-// epilogue; the plain kernel without it is compiled without either. LSE
-// (plain kernel only) also stores every row's log-sum-exp of its kept scores,
-// ln(sum_u exp(scale q.k_u)) of the sparse part, for the backward.
-template <int D, int BQ, bool LIN, bool SEL = LIN, bool LSE = false>
-__global__ __launch_bounds__(BQ * (LIN ? 4 : 2), (LIN || (D == 128 && BQ == 64)) ? 1 : 2) void sparse_attn_fwd_kernel(
+// LIN adds the linear branch over the dropped blocks in the epilogue: O_l =
+// phi(Q) H_D / (phi(Q) . z_D) for each wave's 32 queries, with H_D^T (two bf16
+// planes, staged in LDS) and z_D of the query block from linear_hd_kernel
+// (three-term split-bf16 product: hi hi + hi lo + lo hi, about 16 significant
+// bits per operand); the output is O = O_s + alpha[h] O_l, or in the SLA2 mix
+// (SLA2 page, section 2A) O = alpha[h][c] O_s + (1 - alpha[h][c]) O_l with the
+// scale 1 / (phi(Q) . z_D). Heads whose branch is dropped (lin_on = 0) keep
+// O_s (times alpha[h][c] in the mix). LSE also stores every row's log-sum-exp
+// of its kept scores, ln(sum_u exp(scale q.k_u)) of the sparse part, for the
+// backward.
+template <int D, int BQ, bool LIN, bool LSE = false>
+__global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void sparse_attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ vt, const int32_t* __restrict__ kv_idx,
     const int32_t* __restrict__ kv_cnt, uint16_t* __restrict__ o, int H, int N, int n_q,
     int n_k, int total, float c, const float* __restrict__ alpha,
-    const uint16_t* __restrict__ phikt, const float* __restrict__ lin_h,
-    const float* __restrict__ lin_z, const int32_t* __restrict__ sel_lists, int lin_mode,
-    float* __restrict__ lse) {
+    const uint16_t* __restrict__ hd, const float* __restrict__ zd,
+    const int32_t* __restrict__ lin_on, int lin_mode, float* __restrict__ lse) {
   constexpr int NW = BQ / 32;
   using T = Tile<D>;
   constexpr int LOADS = BK * D / 8 / 64 / NW;
   constexpr int DT = D / 32;
   constexpr int KSTEPS = D / 16;
-  static_assert(!LIN || NW == DT, "the linear branch needs one wave per 32 rows of d");
 
-  // K0 K1 V0 V1 (LIN: phi(K)^T 0, 1, the H waves' V^T 0, 1 and the kept-block
-  // bitmap); buffer b of block i is (i + ...) & 1 as below
-  __shared__ __align__(16)
-      unsigned char smem[LIN ? 8 * T::BYTES + kMaxLinKeyBlocks / 8 : 4 * T::BYTES];
+  // K0 K1 V0 V1; buffer b of block i is (i + ...) & 1 as below
+  __shared__ __align__(16) unsigned char smem[4 * T::BYTES];
   unsigned char* const kbuf = smem;
   unsigned char* const vbuf = smem + 2 * T::BYTES;
-  unsigned char* const pbuf = smem + 4 * T::BYTES;
-  unsigned char* const hvbuf = smem + 6 * T::BYTES;
-  uint32_t* const kbits = reinterpret_cast<uint32_t*>(smem + (LIN ? 8 : 4) * T::BYTES);
 
-  // with a head selection, LIN runs the (batch, head) pairs whose linear
-  // branch is on and the plain kernel the others: the first n_sel * n_q
-  // workgroups take the selected heads' query blocks, spread over the XCDs
-  // like the full grid, and the rest exit
-  int tile;
-  if constexpr (SEL) {
-    const int n_sel = sel_lists[LIN ? 0 : 1];
-    if ((int)blockIdx.x >= n_sel * n_q) return;
-    const int t2 = xcd_remap(blockIdx.x, n_sel * n_q);
-    tile = sel_lists[2 + (LIN ? 0 : total / n_q) + t2 / n_q] * n_q + t2 % n_q;
-  } else {
-    tile = xcd_remap(blockIdx.x, total);
-  }
+  const int tile = xcd_remap(blockIdx.x, total);
   const int bh = tile / n_q, qi = tile % n_q;
   const int t = threadIdx.x, lane = t & 63;
-  const int wave_id = __builtin_amdgcn_readfirstlane(t >> 6);
-  // LIN: waves NW.. are H waves (H_kept and z_kept for the d rows 32*wave..);
-  // the first NW waves run the attention itself and issue every copy
-  const bool hwave = LIN && wave_id >= NW;
-  const int wave = hwave ? wave_id - NW : wave_id;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int h2 = lane >> 5, l32 = lane & 31;
   const size_t head = (size_t)bh * N * D;
 
   const int qrow = qi * BQ + wave * 32 + l32;
-  bf16x8 qf[KSTEPS];  // (H waves load the rows of their attention wave, for phi(Q))
+  bf16x8 qf[KSTEPS];
   {
     const uint16_t* qp = q + head + (size_t)min(qrow, N - 1) * D + 8 * h2;
 #pragma unroll
@@ -134,7 +412,6 @@ __global__ __launch_bounds__(BQ * (LIN ? 4 : 2), (LIN || (D == 128 && BQ == 64))
   const uint16_t* kh = k + head;
   const size_t vtile = (size_t)D * BK;
   const uint16_t* vth = vt + (size_t)bh * n_k * vtile;
-  const uint16_t* pkh = LIN ? phikt + (size_t)bh * n_k * vtile : nullptr;
   // the list is read through two 64-entry windows held one entry per lane
   // (entries w0 .. w0+127), so the block loop issues no scalar memory loads
   auto load_win = [&](int base) { return base + lane < n_k ? ids[base + lane] : 0; };
@@ -185,31 +462,6 @@ __global__ __launch_bounds__(BQ * (LIN ? 4 : 2), (LIN || (D == 128 && BQ == 64))
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) dma16(vtt + vofs(u), vbuf + b * T::BYTES + 1024 * (u * NW + wave));
   };
-  auto stageP = [&](int j, int b) {  // phi(K)^T tile (LIN)
-    const char* ptt = reinterpret_cast<const char*>(pkh + (size_t)j * vtile);
-#pragma unroll
-    for (int u = 0; u < LOADS; ++u) dma16(ptt + vofs(u), pbuf + b * T::BYTES + 1024 * (u * NW + wave));
-  };
-
-  // LIN: the H waves sum phi(K_j)^T V_j over the listed blocks (H_D = H_tot -
-  // that sum, the listed blocks' tiles arriving with the attention's own) or,
-  // when that is the longer list, over the blocks not listed (their tiles
-  // copied by the H waves themselves). Deciding needs the number of distinct
-  // listed blocks: a bitmap of the list, built before the first barrier.
-  const bool maybe_off = LIN && count > n_k - count && n_k <= kMaxLinKeyBlocks;
-  const int words = (n_k + 31) / 32;
-  if constexpr (LIN) {
-    if (maybe_off) {  // bits past n_k count as listed
-      for (int w = t; w < words; w += BQ * 4)
-        kbits[w] = 32 * w + 32 > n_k ? ~((1u << (n_k - 32 * w)) - 1u) : 0u;
-      __syncthreads();
-      for (int e = t; e < count; e += BQ * 4) {
-        const int j = min(max(ids[e], 0), n_k - 1);
-        atomicOr(&kbits[j >> 5], 1u << (j & 31));
-      }
-    }
-  }
-
   int koff[KSTEPS];
 #pragma unroll
   for (int s = 0; s < KSTEPS; ++s) koff[s] = l32 * T::KROWB + (T::kchunk(l32, 2 * s + h2) << 4);
@@ -255,36 +507,14 @@ __global__ __launch_bounds__(BQ * (LIN ? 4 : 2), (LIN || (D == 128 && BQ == 64))
   int jcur = 0;
 
   if (count > 0) {
-    if (!hwave) {
-      jcur = jat(0);
-      stageK(jcur, 0);
-      stageV(jcur, 0);
-      if (count > 1) stageK(jat(1), 1);
-    } else if (!maybe_off) {
-      stageP(jat(0), 0);
-    }
+    jcur = jat(0);
+    stageK(jcur, 0);
+    stageV(jcur, 0);
+    if (count > 1) stageK(jat(1), 1);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
-    if (!hwave) qk(kbuf, sc, Zero{}, Full{}, [](int) {});
+    qk(kbuf, sc, Zero{}, Full{}, [](int) {});
   }
-  // hoff: the H waves take the n_off < count blocks not listed (every wave
-  // counts the bitmap's clear bits); otherwise the listed blocks, whose first
-  // phi(K)^T tile, when the route was open until now, they copy here (read
-  // after step 0's barrier)
-  int n_off = n_k;
-  bool hoff = false;
-  if constexpr (LIN) {
-    if (maybe_off) {
-      int c0 = 0;
-      for (int w = lane; w < words; w += 64) c0 += __popc(~kbits[w]);
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) c0 += __shfl_xor(c0, o);
-      n_off = __builtin_amdgcn_readfirstlane(c0);
-      hoff = n_off < count;
-    }
-    if (hwave && maybe_off && !hoff) stageP(jat(0), 0);
-  }
-
   // one listed block: softmax and P V of block `it` (S^T in sc), and with
   // NEXT the S^T of block it+1 into sn, interleaved
   auto step = [&](int it, auto next_tag, floatx16(&sc)[2], floatx16(&sn)[2]) {
@@ -400,243 +630,122 @@ __global__ __launch_bounds__(BQ * (LIN ? 4 : 2), (LIN || (D == 128 && BQ == 64))
     }
     if constexpr (NEXT) jcur = jn;
   };
-  if (hwave) {
-    // H waves: one barrier per listed block, like the attention waves' steps;
-    // H += phi(K_j)^T V_j and z += sum phi(K_j) from a (V^T, phi(K)^T) pair
-    auto h_block = [&](const unsigned char* vbh, const unsigned char* pbh) {
-#pragma unroll
-      for (int G = 0; G < 4; ++G) {
-        const bf16x8 pkf = lds_read16(pbh + wave * 32 * T::VROWB + voff[G]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) lsum += (float)pkf[e];
-#pragma unroll
-        for (int i = 0; i < DT; ++i)
-          oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              pkf, lds_read16(vbh + i * 32 * T::VROWB + voff[G]), oacc[i], 0, 0, 0);
-      }
-    };
-    if (hoff) {
-      // the blocks not listed, in increasing order: block e is copied (phi(K)^T
-      // to phi buffer e & 1, V^T to the H waves' V buffer e & 1) after barrier
-      // e and summed after barrier e + 1, so n_off < count barriers suffice
-      auto next_off = [&](int j) {  // the first block after j that is not listed
-        int w = (j + 1) >> 5;
-        uint32_t m = w < words ? ~kbits[w] & (~0u << ((j + 1) & 31)) : 0u;
-        while (m == 0u && ++w < words) m = ~kbits[w];
-        return m ? 32 * w + __builtin_ctz(m) : n_k;
-      };
-      int jo = next_off(-1);
-      for (int it = 0; it < count; ++it) {
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-        __syncthreads();
-        if (it < n_off) {
-          const char* ptt = reinterpret_cast<const char*>(pkh + (size_t)jo * vtile);
-          const char* vtt = reinterpret_cast<const char*>(vth + (size_t)jo * vtile);
-#pragma unroll
-          for (int u = 0; u < LOADS; ++u) {
-            dma16(ptt + vofs(u), pbuf + (it & 1) * T::BYTES + 1024 * (u * NW + wave));
-            dma16(vtt + vofs(u), hvbuf + (it & 1) * T::BYTES + 1024 * (u * NW + wave));
-          }
-          jo = next_off(jo);
-        }
-        if (it >= 1 && it - 1 < n_off)
-          h_block(hvbuf + ((it - 1) & 1) * T::BYTES, pbuf + ((it - 1) & 1) * T::BYTES);
-      }
-    } else {
-      // the listed blocks: V^T of block it from the attention waves' buffer
-      // it & 1, its phi(K)^T (copied by the H waves after the barrier before)
-      // from phi buffer it & 1; list entries come from the lane-held windows,
-      // slid like the attention waves' (no scalar loads next to LDS reads)
-      for (int it = 0; it < count; ++it) {
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-        __syncthreads();
-        if (it + 1 < count) {
-          if (it + 1 == w0 + 64) {
-            win0 = win1;
-            w0 += 64;
-            win1 = load_win(w0 + 64);
-          }
-          stageP(jat(it + 1), (it + 1) & 1);
-        }
-        h_block(vbuf + (it & 1) * T::BYTES, pbuf + (it & 1) * T::BYTES);
-      }
-    }
-  } else {
+  {  // two steps per iteration, the S^T arrays swapping roles
     int it = 0;
-    if constexpr (LIN) {  // (two steps per iteration need more registers than LIN has left)
-      for (; it + 1 < count; ++it) {
-        step(it, std::true_type{}, sc, sn);
-        sc[0] = sn[0];
-        sc[1] = sn[1];
-      }
-      if (count > 0) step(it, std::false_type{}, sc, sn);
-    } else {  // two steps per iteration, the S^T arrays swapping roles
-      for (; it + 2 < count; it += 2) {
-        step(it, std::true_type{}, sc, sn);
-        step(it + 1, std::true_type{}, sn, sc);
-      }
-      if (it + 1 < count) {
-        step(it, std::true_type{}, sc, sn);
-        step(it + 1, std::false_type{}, sn, sc);
-      } else if (it < count) {
-        step(it, std::false_type{}, sc, sn);
-      }
+    for (; it + 2 < count; it += 2) {
+      step(it, std::true_type{}, sc, sn);
+      step(it + 1, std::true_type{}, sn, sc);
+    }
+    if (it + 1 < count) {
+      step(it, std::true_type{}, sc, sn);
+      step(it + 1, std::false_type{}, sn, sc);
+    } else if (it < count) {
+      step(it, std::false_type{}, sc, sn);
     }
   }
 
   // ---- epilogue: O = O^T / l, with the linear branch or alpha as above; bf16, rows < N only
-  const float ltot = pair_sum(lsum);  // (H waves: their z entry 32*wave + l32)
+  const float ltot = pair_sum(lsum);
   const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
   if constexpr (LSE) {  // sum_u exp(scale s_u) = 2^(m c) * ltot; -inf for an empty row
-    if (!hwave && h2 == 0 && qrow < N)
+    if (h2 == 0 && qrow < N)
       lse[(size_t)bh * N + qrow] =
           ltot > 0.0f ? (m * c + log2f(ltot)) * 0.6931471805599453f : -INFINITY;
   }
-  // LIN: O_l for this lane's (d, query) entries, in the oacc layout, and
-  // alpha[h] / (phi(Q_t) . z_D) for its query, handed over through LDS by the
-  // H wave of the same index
-  const float4* yl = nullptr;
-  const float* ys = nullptr;
+  // LIN: O_l^T (d x 32 queries) = H_D^T phi(Q)^T for this wave's queries, in
+  // the oacc layout, and its scale (alpha[h], or 1 in the mix) / (phi(Q_t) .
+  // z_D), zero when D_i is empty (z_D = 0). The two H_D^T planes of the query
+  // block are copied into the tile buffers (rows swizzled like K tiles) once
+  // every wave is past its last block.
+  floatx16 lacc[DT];
+  float lin_scale = 0.0f;
+  bool lin = false;
   if constexpr (LIN) {
-    // the staging buffers become H_D^T [D][D+4] fp32 and z_D [D], then the
-    // per-lane O_l fragments [NW][DT*4][64 lanes] float4 and scales [NW][64]
-    constexpr int HP = D + 4;
-    float* ht = reinterpret_cast<float*>(smem);
-    float* zd = ht + D * HP;
-    static_assert(D * HP * 4 + D * 4 <= 6 * T::BYTES, "H_D must fit the staging buffers");
-    static_assert(NW * DT * 4 * 64 * 16 + NW * 64 * 4 <= 6 * T::BYTES,
-                  "O_l must fit the staging buffers");
-    float4* ylds = reinterpret_cast<float4*>(smem);
-    float* ysds = reinterpret_cast<float*>(ylds + NW * DT * 4 * 64);
-    const bool dropped = count < n_k;  // D_i is empty when every block is kept
-    __syncthreads();                   // every wave is done with the staging buffers
-    if (dropped && hwave) {  // H_D = H_tot - the listed sum, or the sum itself
-      const float* Ht = lin_h + (size_t)bh * D * D;
-      if (hoff) {
+    lin = lin_on[bh % H] != 0;  // the same for the whole workgroup
 #pragma unroll
-        for (int i = 0; i < DT; ++i)
+    for (int i = 0; i < DT; ++i)
 #pragma unroll
-          for (int g = 0; g < 4; ++g)
-            *reinterpret_cast<float4*>(ht + (32 * i + l32) * HP + 32 * wave + 8 * g + 4 * h2) =
-                make_float4(oacc[i][4 * g + 0], oacc[i][4 * g + 1], oacc[i][4 * g + 2],
-                            oacc[i][4 * g + 3]);
-        if (h2 == 0) zd[32 * wave + l32] = ltot;
-      } else {
+      for (int r = 0; r < 16; ++r) lacc[i][r] = 0.0f;
+    if (lin) {
+      constexpr int NC = 2 * D * D * 2 / 1024;  // 1 KB copies of both planes
+      static_assert(NC % NW == 0 && 2 * D * D * 2 <= 4 * T::BYTES,
+                    "the H_D^T planes must fit the tile buffers");
+      const size_t qb = (size_t)bh * n_q + qi;
+      const char* src = reinterpret_cast<const char*>(hd + qb * 2 * D * D);
+      __syncthreads();  // every wave is done with the tile buffers
 #pragma unroll
-        for (int i = 0; i < DT; ++i)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int a0 = 32 * wave + 8 * g + 4 * h2, b = 32 * i + l32;
-            float4 x;
-            x.x = Ht[(size_t)(a0 + 0) * D + b] - oacc[i][4 * g + 0];
-            x.y = Ht[(size_t)(a0 + 1) * D + b] - oacc[i][4 * g + 1];
-            x.z = Ht[(size_t)(a0 + 2) * D + b] - oacc[i][4 * g + 2];
-            x.w = Ht[(size_t)(a0 + 3) * D + b] - oacc[i][4 * g + 3];
-            *reinterpret_cast<float4*>(ht + b * HP + a0) = x;
-          }
-        if (h2 == 0) zd[32 * wave + l32] = lin_z[(size_t)bh * D + 32 * wave + l32] - ltot;
+      for (int u = 0; u < NC / NW; ++u) {
+        const int ci = u * NW + wave, p = 64 * ci + lane;
+        const int pl = p / (D * T::KCPR), b = (p / T::KCPR) % D;
+        dma16(src + ((size_t)pl * D * D + (size_t)b * D + T::kchunk(b, p % T::KCPR) * 8) * 2,
+              smem + 1024 * ci);
       }
-    }
-    __syncthreads();
-    float lin_scale = 0.0f;  // alpha[h] / (phi(Q_t) . z_D)
-    if (dropped && hwave) {
-      // O_l^T (d x 32 queries) = H_D^T phi(Q)^T; phi(Q) in the qf layout
-#pragma unroll
-      for (int i = 0; i < DT; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[i][r] = 0.0f;
+      const float* zq = zd + qb * D;
       float den = 0.0f;
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) {
-        bf16x8 qhi, qlo;
+        const float4 z0 = *reinterpret_cast<const float4*>(zq + 16 * s + 8 * h2);
+        const float4 z1 = *reinterpret_cast<const float4*>(zq + 16 * s + 8 * h2 + 4);
+        const float zv[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) den = fmaf(elu1((float)qf[s][e]), zv[e], den);
+      }
+      den = pair_sum(den);
+      lin_scale = den > 0.0f ? (lin_mode == kLinMix ? 1.0f : alpha[bh % H]) / den : 0.0f;
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's plane copies landed
+      __syncthreads();                     // and every wave's
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) {
+        bf16x8 qhi, qlo;  // phi(Q) in the qf layout, split in two bf16 terms
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float fq = elu1((float)qf[s][e]);
-          den = fmaf(fq, zd[16 * s + 8 * h2 + e], den);
           qhi[e] = (__bf16)fq;
           qlo[e] = (__bf16)(fq - (float)qhi[e]);
         }
 #pragma unroll
         for (int i = 0; i < DT; ++i) {
-          const float* hp = ht + (32 * i + l32) * HP + 16 * s + 8 * h2;
-          const float4 h0 = *reinterpret_cast<const float4*>(hp);
-          const float4 h1 = *reinterpret_cast<const float4*>(hp + 4);
-          const float hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
-          bf16x8 hhi, hlo;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            hhi[e] = (__bf16)hv[e];
-            hlo[e] = (__bf16)(hv[e] - (float)hhi[e]);
-          }
-          oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hhi, qhi, oacc[i], 0, 0, 0);
-          oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hhi, qlo, oacc[i], 0, 0, 0);
-          oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hlo, qhi, oacc[i], 0, 0, 0);
+          const int b = 32 * i + l32;
+          const int ofs = b * D * 2 + (T::kchunk(b, 2 * s + h2) << 4);
+          const bf16x8 hhi = lds_read16(smem + ofs), hlo = lds_read16(smem + D * D * 2 + ofs);
+          lacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hhi, qhi, lacc[i], 0, 0, 0);
+          lacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hhi, qlo, lacc[i], 0, 0, 0);
+          lacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hlo, qhi, lacc[i], 0, 0, 0);
         }
       }
-      den = pair_sum(den);
-      lin_scale = den > 0.0f ? (lin_mode == kLinMix ? 1.0f : alpha[bh % H]) / den : 0.0f;
-    }
-    __syncthreads();  // every H wave is done reading H_D^T
-    if (dropped && hwave) {
-#pragma unroll
-      for (int i = 0; i < DT; ++i)
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          ylds[((wave * DT + i) * 4 + g) * 64 + lane] =
-              make_float4(oacc[i][4 * g + 0], oacc[i][4 * g + 1], oacc[i][4 * g + 2],
-                          oacc[i][4 * g + 3]);
-      ysds[wave * 64 + lane] = lin_scale;
-    }
-    __syncthreads();
-    if (dropped) {
-      yl = ylds;
-      ys = ysds;
+      __syncthreads();  // every wave is done with the planes before the O tiles reuse the space
     }
   }
   // O leaves through LDS: each wave writes its 32 x D tile into its own slice
   // of buffers no wave reads any more (the K tiles, which the last block does
-  // not use; LIN: the H waves' V^T tiles, past the H_D and O_l staging), rows
-  // with their 16-byte chunks XOR-swizzled, then copies whole rows out, so
-  // that every store instruction writes 64 x 16 contiguous bytes
-  if (!hwave) {
-    static_assert(NW * 32 * D * 2 <= 2 * T::BYTES, "the O tiles must fit two staging buffers");
-    unsigned char* stg = smem + (LIN ? 6 * T::BYTES : 0) + wave * 32 * D * 2;
-    store_rows_via_lds<D>(stg, o + head, qi * BQ + wave * 32, N, lane, [&](int i, int g) {
-      const int d0 = 32 * i + 8 * g + 4 * h2;
-      float y[4];
+  // not use, or with LIN the planes' space), rows with their 16-byte chunks
+  // XOR-swizzled, then copies whole rows out, so that every store instruction
+  // writes 64 x 16 contiguous bytes
+  static_assert(NW * 32 * D * 2 <= 2 * T::BYTES, "the O tiles must fit two staging buffers");
+  unsigned char* stg = smem + wave * 32 * D * 2;
+  store_rows_via_lds<D>(stg, o + head, qi * BQ + wave * 32, N, lane, [&](int i, int g) {
+    const int d0 = 32 * i + 8 * g + 4 * h2;
+    float y[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) y[e] = oacc[i][4 * g + e] * inv;
-      // mix: alpha[h][d0..d0+3] (plain kernel: the scale of a dropped branch's alpha O_s)
-      const bool mix = SEL && (LIN ? lin_mode == kLinMix : alpha != nullptr);
-      float a[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-      if (mix) {
+    for (int e = 0; e < 4; ++e) y[e] = oacc[i][4 * g + e] * inv;
+    if constexpr (LIN) {
+      if (lin_mode == kLinMix) {  // alpha[h][d0 .. d0 + 3]
         const float4 a4 = *reinterpret_cast<const float4*>(alpha + (size_t)(bh % H) * D + d0);
-        a[0] = a4.x; a[1] = a4.y; a[2] = a4.z; a[3] = a4.w;
-      }
-      bool have_l = false;
-      float lv[4] = {0.0f, 0.0f, 0.0f, 0.0f}, sl = 0.0f;
-      if constexpr (LIN) {
-        if (yl) {
-          const float4 l = yl[((wave * DT + i) * 4 + g) * 64 + lane];
-          lv[0] = l.x; lv[1] = l.y; lv[2] = l.z; lv[3] = l.w;
-          sl = ys[wave * 64 + lane];
-          have_l = true;
-        }
-      }
-      if (mix) {
+        const float a[4] = {a4.x, a4.y, a4.z, a4.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          y[e] = have_l ? fmaf(a[e], y[e], (1.0f - a[e]) * (lv[e] * sl)) : a[e] * y[e];
-      } else if (have_l) {
+          y[e] = lin ? fmaf(a[e], y[e], (1.0f - a[e]) * (lacc[i][4 * g + e] * lin_scale))
+                     : a[e] * y[e];
+      } else if (lin) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = fmaf(lv[e], sl, y[e]);
+        for (int e = 0; e < 4; ++e) y[e] = fmaf(lacc[i][4 * g + e], lin_scale, y[e]);
       }
-      uint2 pk;
-      pk.x = pack2_bf16(y[0], y[1]);
-      pk.y = pack2_bf16(y[2], y[3]);
-      return pk;
-    });
-  }
+    }
+    uint2 pk;
+    pk.x = pack2_bf16(y[0], y[1]);
+    pk.y = pack2_bf16(y[2], y[3]);
+    return pk;
+  });
 }
 
 template <int D, int BQ, bool LIN>
@@ -648,45 +757,37 @@ hipError_t launch_sparse(const AttnLaunch& a, hipStream_t s, AttnPhase phase) {
     if constexpr (LIN)
       hipLaunchKernelGGL(linear_flags_kernel, dim3(1), dim3(kFlagThreads), 0, s, a.alpha,
                          a.lin_mode, D, a.drop_below, a.B, a.H, a.lin_on, a.lin_lists);
-    hipLaunchKernelGGL((pack_kernel<D, LIN>), dim3(a.n_k, BH), dim3(2 * D), 0, s, a.v, a.k,
-                       a.vt, a.phikt, a.N, a.n_k, a.lin_on, a.H);
-    if constexpr (LIN) {
-      hipLaunchKernelGGL((linear_total_kernel<D>), dim3(kLinSplit, BH), dim3(D * 2), 0, s,
-                         a.phikt, a.vt, a.part_h, a.part_z, a.n_k, a.lin_on, a.H);
-      hipLaunchKernelGGL((linear_reduce_kernel<D>), dim3(BH, (D * D + D + 255) / 256), dim3(256),
-                         0, s, a.part_h, a.part_z, a.lin_h, a.lin_z, a.lin_on, a.H);
-    }
+    if constexpr (LIN)
+      hipLaunchKernelGGL((linear_pack_kernel<D>), dim3(a.n_k, BH), dim3(2 * D), 0, s, a.v, a.k,
+                         a.vt, a.hj, a.N, a.n_k, a.lin_on, a.H);
+    else
+      hipLaunchKernelGGL((pack_kernel<D, false>), dim3(a.n_k, BH), dim3(2 * D), 0, s, a.v, a.k,
+                         a.vt, nullptr, a.N, a.n_k, nullptr, a.H);
   }
   if (phase != kPackOnly) {
     if constexpr (LIN) {
-      // heads whose branch is on, then (plain kernel, times alpha in the mix) the others
-      const float* mix_alpha = a.lin_mode == kLinMix ? a.alpha : nullptr;
-      if (a.lse) {
-        hipLaunchKernelGGL((sparse_attn_fwd_kernel<D, BQ, true, true, true>), dim3(total),
-                           dim3(BQ * 4), 0, s, a.q, a.k, a.vt, a.idx, a.cnt, a.o, a.H, a.N, a.n_q,
-                           a.n_k, total, c, a.alpha, a.phikt, a.lin_h, a.lin_z, a.lin_lists,
-                           a.lin_mode, a.lse);
-        hipLaunchKernelGGL((sparse_attn_fwd_kernel<D, BQ, false, true, true>), dim3(total),
-                           dim3(BQ * 2), 0, s, a.q, a.k, a.vt, a.idx, a.cnt, a.o, a.H, a.N, a.n_q,
-                           a.n_k, total, c, mix_alpha, nullptr, nullptr, nullptr, a.lin_lists,
-                           a.lin_mode, a.lse);
-      } else {
-        hipLaunchKernelGGL((sparse_attn_fwd_kernel<D, BQ, true>), dim3(total), dim3(BQ * 4), 0, s,
-                           a.q, a.k, a.vt, a.idx, a.cnt, a.o, a.H, a.N, a.n_q, a.n_k, total, c,
-                           a.alpha, a.phikt, a.lin_h, a.lin_z, a.lin_lists, a.lin_mode, nullptr);
-        hipLaunchKernelGGL((sparse_attn_fwd_kernel<D, BQ, false, true>), dim3(total), dim3(BQ * 2),
+      const int rows = BH * a.n_q, n_kp = (a.n_k + 31) / 32 * 32;
+      hipLaunchKernelGGL(linear_mdrop_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, a.idx, a.cnt,
+                         a.mdrop, a.n_k, n_kp, rows);
+      hipLaunchKernelGGL((linear_hd_kernel<D>),
+                         dim3((lin_cols<D>() + 127) / 128, (a.n_q + 255) / 256, BH), dim3(256), 0,
+                         s, a.hj, a.mdrop, a.hd, a.zd, a.n_q, a.n_k, n_kp, a.lin_on, a.H);
+      if (a.lse)
+        hipLaunchKernelGGL((sparse_attn_fwd_kernel<D, BQ, true, true>), dim3(total), dim3(BQ * 2),
                            0, s, a.q, a.k, a.vt, a.idx, a.cnt, a.o, a.H, a.N, a.n_q, a.n_k, total,
-                           c, mix_alpha, nullptr, nullptr, nullptr, a.lin_lists, a.lin_mode,
-                           nullptr);
-      }
+                           c, a.alpha, a.hd, a.zd, a.lin_on, a.lin_mode, a.lse);
+      else
+        hipLaunchKernelGGL((sparse_attn_fwd_kernel<D, BQ, true>), dim3(total), dim3(BQ * 2), 0, s,
+                           a.q, a.k, a.vt, a.idx, a.cnt, a.o, a.H, a.N, a.n_q, a.n_k, total, c,
+                           a.alpha, a.hd, a.zd, a.lin_on, a.lin_mode, nullptr);
     } else if (a.lse) {
-      hipLaunchKernelGGL((sparse_attn_fwd_kernel<D, BQ, false, false, true>), dim3(total),
-                         dim3(BQ * 2), 0, s, a.q, a.k, a.vt, a.idx, a.cnt, a.o, a.H, a.N, a.n_q,
-                         a.n_k, total, c, nullptr, nullptr, nullptr, nullptr, nullptr, 0, a.lse);
+      hipLaunchKernelGGL((sparse_attn_fwd_kernel<D, BQ, false, true>), dim3(total), dim3(BQ * 2),
+                         0, s, a.q, a.k, a.vt, a.idx, a.cnt, a.o, a.H, a.N, a.n_q, a.n_k, total,
+                         c, nullptr, nullptr, nullptr, nullptr, 0, a.lse);
     } else {
       hipLaunchKernelGGL((sparse_attn_fwd_kernel<D, BQ, false>), dim3(total), dim3(BQ * 2), 0, s,
                          a.q, a.k, a.vt, a.idx, a.cnt, a.o, a.H, a.N, a.n_q, a.n_k, total, c,
-                         nullptr, nullptr, nullptr, nullptr, nullptr, 0, nullptr);
+                         nullptr, nullptr, nullptr, nullptr, 0, nullptr);
     }
   }
   return hipGetLastError();
@@ -699,11 +800,32 @@ size_t attn_workspace_bytes(int B, int H, int N, int d) {
   return (size_t)B * H * n_k * BK * d * sizeof(uint16_t);
 }
 
-size_t linear_workspace_bytes(int B, int H, int N, int d) {
-  const size_t BH = (size_t)B * H;
-  return 2 * attn_workspace_bytes(B, H, N, d) +                // packed V, packed phi(K)
-         BH * ((size_t)d * d + d) * (1 + kLinSplit) * sizeof(float) +  // totals + partials
-         ((size_t)H + 2 + 2 * BH) * sizeof(int32_t);  // branch flags and head lists
+// Linear workspace, in order: packed V^T, the per-key-block
+// summaries (two bf16 planes of D*D + D per block), the drop matrix (bf16,
+// rows of n_k rounded up to 32), H_D^T planes and z_D per query block, the
+// branch flags and head lists; every part 256-byte aligned.
+size_t linear_layout(AttnLaunch& a, unsigned char* w, int B, int H, int N, int d, int block_q) {
+  const size_t BH = (size_t)B * H, n_k = (N + BK - 1) / BK, n_q = (N + block_q - 1) / block_q;
+  const size_t n_kp = (n_k + 31) / 32 * 32, cols = (size_t)d * d + d;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    unsigned char* p = w ? w + off : nullptr;
+    off += (bytes + 255) & ~(size_t)255;
+    return p;
+  };
+  a.vt = reinterpret_cast<uint16_t*>(take(attn_workspace_bytes(B, H, N, d)));
+  a.hj = reinterpret_cast<uint16_t*>(take(BH * n_k * 2 * cols * 2));
+  a.mdrop = reinterpret_cast<uint16_t*>(take(BH * n_q * n_kp * 2));
+  a.hd = reinterpret_cast<uint16_t*>(take(BH * n_q * 2 * (size_t)d * d * 2));
+  a.zd = reinterpret_cast<float*>(take(BH * n_q * d * 4));
+  a.lin_on = reinterpret_cast<int32_t*>(take((size_t)H * 4));
+  a.lin_lists = reinterpret_cast<int32_t*>(take((2 + 2 * BH) * 4));
+  return off;
+}
+
+size_t linear_workspace_bytes(int B, int H, int N, int d, int block_q) {
+  AttnLaunch a{};
+  return linear_layout(a, nullptr, B, H, N, d, block_q);
 }
 
 hipError_t launch_attn(const AttnLaunch& a, hipStream_t s, AttnPhase phase) {

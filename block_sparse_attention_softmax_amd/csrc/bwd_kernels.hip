@@ -222,58 +222,6 @@ __device__ __forceinline__ void dma4(const void* src, void* lds) {
   __builtin_amdgcn_global_load_lds(src, lds, 4, 0, 0);
 }
 
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-
-// 32-bit LDS address of a pointer into __shared__ memory
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)(p);
-}
-
-// NR transposing LDS reads (ds_read_b64_tr_b16; NR = 8 or 16): within each
-// group of 16 lanes, lane i receives element i & 3 of the 4-element rows that
-// lanes 4e + (i >> 2), e = 0..3, address. Written as one asm block that also
-// waits for them: as a builtin the compiler holds such a read until every
-// direct-to-LDS copy in flight has landed, the next stage's included.
-template <int NR>
-__device__ __forceinline__ void lds_read_tr(v4i16 (&r)[NR], const uint32_t (&a)[NR]) {
-  static_assert(NR == 8 || NR == 16, "8 or 16 reads");
-  if constexpr (NR == 8) {
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %8\n\tds_read_b64_tr_b16 %1, %9\n\t"
-        "ds_read_b64_tr_b16 %2, %10\n\tds_read_b64_tr_b16 %3, %11\n\t"
-        "ds_read_b64_tr_b16 %4, %12\n\tds_read_b64_tr_b16 %5, %13\n\t"
-        "ds_read_b64_tr_b16 %6, %14\n\tds_read_b64_tr_b16 %7, %15\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
-          "=&v"(r[6]), "=&v"(r[7])
-        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
-        : "memory");
-  } else {
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %16\n\tds_read_b64_tr_b16 %1, %17\n\t"
-        "ds_read_b64_tr_b16 %2, %18\n\tds_read_b64_tr_b16 %3, %19\n\t"
-        "ds_read_b64_tr_b16 %4, %20\n\tds_read_b64_tr_b16 %5, %21\n\t"
-        "ds_read_b64_tr_b16 %6, %22\n\tds_read_b64_tr_b16 %7, %23\n\t"
-        "ds_read_b64_tr_b16 %8, %24\n\tds_read_b64_tr_b16 %9, %25\n\t"
-        "ds_read_b64_tr_b16 %10, %26\n\tds_read_b64_tr_b16 %11, %27\n\t"
-        "ds_read_b64_tr_b16 %12, %28\n\tds_read_b64_tr_b16 %13, %29\n\t"
-        "ds_read_b64_tr_b16 %14, %30\n\tds_read_b64_tr_b16 %15, %31\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
-          "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]),
-          "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15])
-        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]),
-          "v"(a[8]), "v"(a[9]), "v"(a[10]), "v"(a[11]), "v"(a[12]), "v"(a[13]), "v"(a[14]),
-          "v"(a[15])
-        : "memory");
-  }
-}
-
-__device__ __forceinline__ bf16x8 join_tr(v4i16 lo, v4i16 hi) {
-  typedef short v8i16 __attribute__((ext_vector_type(8)));
-  return __builtin_bit_cast(bf16x8, (v8i16)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
 template <int D, int BQ>
 __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void sparse_attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,

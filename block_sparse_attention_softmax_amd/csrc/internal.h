@@ -105,11 +105,10 @@ struct AttnLaunch {
   float drop_below;    // a head whose linear weights are all <= this in magnitude skips the branch
   int32_t* lin_on;     // [H] 1 where the branch is evaluated
   int32_t* lin_lists;  // [2 + 2*B*H] counts, then the b*H + h with the branch on, then off
-  uint16_t* phikt;     // phi(K) packed like vt, bf16
-  float* lin_h;        // [B*H, d, d]  sum_u phi(K_u)^T V_u  (row = phi(K) index)
-  float* lin_z;        // [B*H, d]     sum_u phi(K_u)
-  float* part_h;       // [B*H, kLinSplit, d, d] split-K partials of lin_h
-  float* part_z;       // [B*H, kLinSplit, d]
+  uint16_t* hj;        // [B*H, n_k, 2, d*d + d] bf16 planes of H_j^T and z_j per key block
+  uint16_t* mdrop;     // [B*H, n_q, n_k rounded up to 32] bf16 1 where block j is dropped
+  uint16_t* hd;        // [B*H, n_q, 2, d, d] bf16 planes of H_D^T per query block
+  float* zd;           // [B*H, n_q, d] z_D per query block
 };
 constexpr int kLinSplit = 64;
 // how the linear branch meets the sparse output: O_s + alpha[h] O_l, or the
@@ -203,6 +202,8 @@ hipError_t launch_svg2_pairs(const Svg2Launch& a, unsigned long long* counts, hi
 size_t svg2_workspace_bytes(int B, int H, int N, int d, int block_q, int Cq, int Ck);
 size_t svg2_layout(Svg2Launch& a, unsigned char* workspace);  // fills pointers; returns bytes
 size_t attn_workspace_bytes(int B, int H, int N, int d);    // packed V
-size_t linear_workspace_bytes(int B, int H, int N, int d);  // packed V + linear branch
+size_t linear_workspace_bytes(int B, int H, int N, int d, int block_q);  // packed V + linear branch
+// fills the linear branch's workspace pointers of a (w may be nullptr); returns bytes
+size_t linear_layout(AttnLaunch& a, unsigned char* w, int B, int H, int N, int d, int block_q);
 
 }  // namespace sparge

@@ -273,11 +273,14 @@ int sparge_attn_bwd(const void* q, const void* k, const void* v, const void* o,
                     size_t workspace_bytes, void* stream);
 
 /* Device workspace (bytes) of sparse_linear_attn_fwd: the packed V of
- * sparge_attn_fwd, phi(K) packed the same way, and per (b, h) the float32
- * summaries sum_u phi(K_u)^T V_u (d x d) and sum_u phi(K_u) (d) with 64
- * split-K partials of each, and H + 2 + 2*B*H int32 for the per-head
- * branch flags and the lists of (batch, head) pairs by flag. Returns 0 for
- * arguments that sparse_linear_attn_fwd would reject. */
+ * sparge_attn_fwd; per (b, h) and key block
+ * the summary phi(K_j)^T V_j (d x d) and sum phi(K_j) (d) as two bf16 planes
+ * (hi and the rounded remainder); per (b, h) the drop matrix (bf16, one row
+ * per query block of the key-block count rounded up to 32); per query block
+ * the dropped-block sums as two bf16 planes of d x d and d float32; and
+ * H + 2 + 2*B*H int32 for the per-head branch flags and the lists of
+ * (batch, head) pairs by flag; each part rounded up to 256 bytes. Returns 0
+ * for arguments that sparse_linear_attn_fwd would reject. */
 size_t sparse_linear_workspace_bytes(int B, int H, int N, int d);
 
 /* Sparse attention plus a linear-attention branch over the dropped blocks
@@ -288,9 +291,11 @@ size_t sparse_linear_workspace_bytes(int B, int H, int N, int d);
  * the valid keys of the blocks NOT listed in row i,
  *   O_l,t = sum_{u in D_i} (phi(Q_t).phi(K_u)) V_u / sum_{u in D_i} phi(Q_t).phi(K_u),
  * and O_l,t = 0 when D_i is empty. phi is applied to the unscaled Q and K.
- * The linear branch accumulates in float32 from bf16-rounded phi(K) and V;
- * its final product phi(Q) . (sum over D_i) carries about 16 significant
- * bits per operand. Built for block_q == d (64 or 128); other block sizes
+ * The linear branch forms per-key-block sums in float32 from bf16-rounded
+ * phi(K) and V, carries them and their sums over D_i with about 16
+ * significant bits (two bf16 planes) and accumulates in float32; its final
+ * product phi(Q) . (sum over D_i) carries about 16 significant bits per
+ * operand. Built for block_q == d (64 or 128); other block sizes
  * return SPARGE_ERR_UNSUPPORTED.
  *
  * Post-tuning branch dropping (SALAD page): a head with |alpha[h]| <=
