@@ -736,7 +736,7 @@ size_t sparse_linear_workspace_bytes(int B, int H, int N, int d) {
   const std::string saved = g_last_error;
   const int rc = check_shape(B, H, N, d, 128, 64);
   g_last_error = saved;
-  if (rc != SPARGE_OK) return 0;
+  if (rc != SPARGE_OK || ceil_div(N, 64) > sparge::kLinMaxKeyBlocks) return 0;
   return sparge::linear_workspace_bytes(B, H, N, d, d);
 }
 
@@ -758,6 +758,8 @@ int linear_impl(const char* name, int mode, const void* q, const void* k, const 
     return fail(SPARGE_ERR_INVALID_ARG, "alpha / workspace / lse misaligned");
   if (block_q != d)
     return fail(SPARGE_ERR_UNSUPPORTED, "the linear branch is built for block_q == d (64 or 128)");
+  if (ceil_div(N, block_k) > sparge::kLinMaxKeyBlocks)
+    return fail(SPARGE_ERR_UNSUPPORTED, "the linear branch supports at most 4096 key blocks");
   if (workspace_bytes < sparge::linear_workspace_bytes(B, H, N, d, block_q))
     return fail(SPARGE_ERR_INVALID_ARG, "workspace too small");
   sparge::AttnLaunch a{};

@@ -184,70 +184,76 @@ __global__ __launch_bounds__(2 * D) void linear_pack_kernel(const uint16_t* __re
   }
 }
 
-// mdrop[bh][i][j] = bf16 1.0 where query block i does not list key block j,
-// 0 where it does and for j in [n_k, n_kp) (rows of n_kp = n_k rounded up to
-// 32). One wave per (b, h, query block): the list as a bitmap in LDS, 4096
-// key blocks at a time, then rows of 8 entries per lane.
+// mbits[bh][i][w]: bit b of word w is set where query block i does not list
+// key block j = 32 w + b (j < n_k); words of n_kw = ceil(n_k / 32) per row.
+// One wave per (b, h, query block): the list as a bitmap in LDS (n_k <=
+// kLinMaxKeyBlocks), then its complement.
 __global__ __launch_bounds__(256) void linear_mdrop_kernel(const int32_t* __restrict__ kv_idx,
                                                            const int32_t* __restrict__ kv_cnt,
-                                                           uint16_t* __restrict__ mdrop, int n_k,
-                                                           int n_kp, int rows) {
-  constexpr int CH = 4096;
-  __shared__ uint32_t bits[4][CH / 32];
+                                                           uint32_t* __restrict__ mbits, int n_k,
+                                                           int n_kw, int rows) {
+  __shared__ uint32_t bits[4][kLinMaxKeyBlocks / 32];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + wave;
   if (row >= rows) return;
   const int count = min(max(kv_cnt[row], 0), n_k);
   const int32_t* ids = kv_idx + (size_t)row * n_k;
-  uint16_t* out = mdrop + (size_t)row * n_kp;
   uint32_t* b = bits[wave];
-  for (int j0 = 0; j0 < n_kp; j0 += CH) {
-    for (int w = lane; w < CH / 32; w += 64) b[w] = 0u;
-    wave_lds_fence();
-    for (int e = lane; e < count; e += 64) {
-      const int j = min(max(ids[e], 0), n_k - 1) - j0;
-      if (j >= 0 && j < CH) atomicOr(&b[j >> 5], 1u << (j & 31));
-    }
-    wave_lds_fence();
-    for (int jj = 8 * lane; jj < min(CH, n_kp - j0); jj += 512) {
-      const uint32_t word = b[jj >> 5] >> (jj & 31);  // bits of jj .. jj + 7
-      uint32_t v[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int ja = j0 + jj + 2 * e;
-        const uint32_t lo = (ja < n_k && !((word >> (2 * e)) & 1u)) ? 0x3F80u : 0u;
-        const uint32_t hi = (ja + 1 < n_k && !((word >> (2 * e + 1)) & 1u)) ? 0x3F80u : 0u;
-        v[e] = lo | (hi << 16);
-      }
-      *reinterpret_cast<uint4*>(out + j0 + jj) = make_uint4(v[0], v[1], v[2], v[3]);
-    }
-    wave_lds_fence();
+  for (int w = lane; w < n_kw; w += 64) b[w] = 0u;
+  wave_lds_fence();
+  for (int e = lane; e < count; e += 64) {
+    const int j = min(max(ids[e], 0), n_k - 1);
+    atomicOr(&b[j >> 5], 1u << (j & 31));
   }
+  wave_lds_fence();
+  for (int w = lane; w < n_kw; w += 64) {
+    const int left = n_k - 32 * w;  // valid key blocks in this word
+    const uint32_t valid = left >= 32 ? 0xFFFFFFFFu : ((1u << left) - 1u);
+    mbits[(size_t)row * n_kw + w] = ~b[w] & valid;
+  }
+}
+
+// 8 drop flags (bits 0..7 of `byte`) as the bf16 values 0 / 1 of an MFMA
+// operand: element e of the result is bit e. `spread` has bit e at e and at
+// e + 15, so (spread >> 2t) & 0x10001 has bit 2t at 0 and bit 2t+1 at 16.
+__device__ __forceinline__ bf16x8 drop_flags_bf16(uint32_t byte) {
+  const uint32_t spread = byte | (byte << 15);
+  uint32_t w[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) w[t] = ((spread >> (2 * t)) & 0x10001u) * 0x3F80u;
+  bf16x8 r;
+  __builtin_memcpy(&r, w, 16);
+  return r;
 }
 
 // [H_D, z_D]^T[col][i] = sum_j (hi_j + lo_j)[col] M[i][j]. Workgroup (128
 // columns, 256 query blocks, b h), 4 waves of 32 columns x 256 query blocks
-// (8 accumulator tiles). The key blocks go 32 at a time: the two planes' rows
-// j .. j+31 of the workgroup's columns and M's columns j .. j+31 of its rows,
-// double-buffered in one LDS array by direct-to-LDS copies (rows past n_k and
-// n_q repeat the last one; M is 0 there). The plane operand (8 consecutive key
-// blocks of one column per lane) comes from transposing LDS reads, whose 4
-// rows x 32 bytes per 16 lanes the chunk swizzle c ^ 4 (row mod 4) spreads
-// over all banks; M's 64-byte rows take the swizzle c ^ ((row / 4) mod 4).
+// (8 accumulator tiles). The key blocks go 32 at a time in stages of the two
+// planes' rows j .. j+31 of the workgroup's columns (16 KB) and one drop-bit
+// word per query block (1 KB), in a ring of 4 stage buffers filled three
+// stages ahead by direct-to-LDS copies, so that enough bytes are in flight to
+// cover the memory latency (rows past n_k repeat the last one; their bits are
+// 0). The plane operand (8 consecutive key blocks of one column per lane)
+// comes from transposing LDS reads, whose 4 rows x 32 bytes per 16 lanes the
+// chunk swizzle c ^ 4 (row mod 4) spreads over all banks; M's operand is
+// expanded from the drop bits in registers.
 // Output per query block: H_D^T as two bf16 planes [2][D][D] (the same
-// hi / lo split) and z_D as float32 [D]; heads whose branch is dropped are
+// hi / lo split), written through LDS as whole 256-byte row pieces, and z_D
+// as float32 [D] (the last column tile); heads whose branch is dropped are
 // skipped.
 template <int D>
 __global__ __launch_bounds__(256, 2) void linear_hd_kernel(const uint16_t* __restrict__ hj,
-                                                           const uint16_t* __restrict__ mdrop,
+                                                           const uint32_t* __restrict__ mbits,
                                                            uint16_t* __restrict__ hd,
                                                            float* __restrict__ zd, int n_q,
-                                                           int n_k, int n_kp,
+                                                           int n_k, int n_kw,
                                                            const int32_t* __restrict__ lin_on,
                                                            int H) {
-  constexpr int COLS = lin_cols<D>(), CB = 128, IB = 256, JB = 32;
-  constexpr int HBYTES = 2 * JB * CB * 2, MBYTES = IB * JB * 2, BUF = HBYTES + MBYTES;
-  __shared__ __align__(16) unsigned char smem[2 * BUF];
+  constexpr int COLS = lin_cols<D>(), CB = 128, IB = 256, JB = 32, NS = 4;
+  constexpr int HBYTES = 2 * JB * CB * 2, STAGE = HBYTES + IB * 4;
+  constexpr int SP = CB * 2 + 16;  // output staging row pitch
+  static_assert(2 * 2 * 32 * SP <= NS * STAGE, "two output staging buffers fit the ring");
+  __shared__ __align__(16) unsigned char smem[NS * STAGE];
   const int bh = blockIdx.z;
   if (!lin_on[bh % H]) return;
   const int c0 = blockIdx.x * CB, i0 = blockIdx.y * IB;
@@ -255,11 +261,12 @@ __global__ __launch_bounds__(256, 2) void linear_hd_kernel(const uint16_t* __res
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int h2 = lane >> 5, l32 = lane & 31;
   const uint16_t* hsrc = hj + (size_t)bh * n_k * 2 * COLS;
-  const uint16_t* msrc = mdrop + (size_t)bh * n_q * n_kp;
-  // copies of one buffer: 16 KB of plane rows (wave w, copy u: plane u / 2,
-  // rows 4 (4 (u % 2) + w) .. +3), then 16 KB of M (rows 16 (4 u + w) .. +15)
-  auto issue = [&](int jb, int b) {
-    unsigned char* buf = smem + b * BUF;
+  const uint32_t* msrc = mbits + ((size_t)bh * n_q + min(i0 + t, n_q - 1)) * n_kw;
+  // copies of one stage, 5 per wave: 16 KB of plane rows (copy u: plane u / 2,
+  // rows 4 (4 (u % 2) + w) .. +3), then the drop word of query block i0 + t
+  auto issue = [&](int st) {
+    unsigned char* buf = smem + (st % NS) * STAGE;
+    const int jb = st * JB;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {  // lane: row r0 + lane / 16, physical chunk lane % 16
       const int pl = u >> 1, r0 = 4 * (4 * (u & 1) + wave), r = r0 + (lane >> 4);
@@ -268,13 +275,7 @@ __global__ __launch_bounds__(256, 2) void linear_hd_kernel(const uint16_t* __res
       const int jr = min(jb + r, n_k - 1);
       dma16(hsrc + ((size_t)jr * 2 + pl) * COLS + col, buf + pl * (JB * CB * 2) + r0 * (CB * 2));
     }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {  // lane: row r0 + lane / 4, physical chunk lane % 4
-      const int r0 = 16 * (4 * u + wave), r = r0 + (lane >> 2);
-      const int lc = (lane & 3) ^ ((r >> 2) & 3);
-      const int ir = min(i0 + r, n_q - 1);
-      dma16(msrc + (size_t)ir * n_kp + jb + 8 * lc, buf + HBYTES + r0 * (JB * 2));
-    }
+    dma4(msrc + st, buf + HBYTES + 256 * wave);
   };
   floatx16 acc[IB / 32];
 #pragma unroll
@@ -290,15 +291,25 @@ __global__ __launch_bounds__(256, 2) void linear_hd_kernel(const uint16_t* __res
     const int lc = colb >> 3, pc = lc ^ ((r & 3) << 2);
     return (uint32_t)(r * (CB * 2) + 16 * pc + 2 * (colb & 7));
   };
-  const int nb = (n_kp + JB - 1) / JB;
-  issue(0, 0);
+  const int nb = n_kw;  // stages of 32 key blocks
+#pragma unroll
+  for (int st = 0; st < NS - 1; ++st)
+    if (st < nb) issue(st);
   for (int bi = 0; bi < nb; ++bi) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of block bi landed
-    __syncthreads();                     // every wave's copies landed; the other buffer is free
-    if (bi + 1 < nb) issue((bi + 1) * JB, (bi + 1) & 1);
-    const unsigned char* buf = smem + (bi & 1) * BUF;
+    // this wave's copies of stage bi landed (the later stages already issued,
+    // at most NS - 2 of 5 copies each, may still be in flight) and its LDS
+    // reads of stage bi - 1 are done
+    const int later = min(nb - 1 - bi, NS - 2);
+    if (later >= 2) __builtin_amdgcn_s_waitcnt(0x007A);       // vmcnt(10) lgkmcnt(0)
+    else if (later == 1) __builtin_amdgcn_s_waitcnt(0x0075);  // vmcnt(5) lgkmcnt(0)
+    else __builtin_amdgcn_s_waitcnt(0x0070);                  // vmcnt(0) lgkmcnt(0)
+    // every wave's copies landed; the buffer of stage bi - 1 is free (a fenced
+    // barrier would wait for the later stages' copies too)
+    barrier_no_fence();
+    if (bi + NS - 1 < nb) issue(bi + NS - 1);
+    const unsigned char* buf = smem + (bi % NS) * STAGE;
     const uint32_t pbase = lds_addr(buf);
-    static_assert(JB == 32, "two k-steps per block: eight transposing reads");
+    static_assert(JB == 32, "two k-steps per stage: eight transposing reads");
     uint32_t ad[8];
     v4i16 fr[8];
 #pragma unroll
@@ -309,45 +320,67 @@ __global__ __launch_bounds__(256, 2) void linear_hd_kernel(const uint16_t* __res
         for (int tt = 0; tt < 2; ++tt)
           ad[4 * ks + 2 * pl + tt] = pbase + pl * (JB * CB * 2) + tr_addr(ks, tt);
     lds_read_tr<8>(fr, ad);
+    uint32_t mw[IB / 32];  // drop bits of query block i0 + 32 ti + l32 for this stage
+#pragma unroll
+    for (int ti = 0; ti < IB / 32; ++ti)
+      mw[ti] = *reinterpret_cast<const uint32_t*>(buf + HBYTES + 4 * (32 * ti + l32));
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const bf16x8 ahi = join_tr(fr[4 * ks], fr[4 * ks + 1]);
       const bf16x8 alo = join_tr(fr[4 * ks + 2], fr[4 * ks + 3]);
 #pragma unroll
       for (int ti = 0; ti < IB / 32; ++ti) {
-        const int r = 32 * ti + l32, lc = 2 * ks + h2;
-        const bf16x8 bm = lds_read16(buf + HBYTES + r * (JB * 2) + 16 * (lc ^ ((r >> 2) & 3)));
+        const bf16x8 bm = drop_flags_bf16((mw[ti] >> (8 * (2 * ks + h2))) & 0xFFu);
         acc[ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, bm, acc[ti], 0, 0, 0);
         acc[ti] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, bm, acc[ti], 0, 0, 0);
       }
     }
   }
   // lane: query block i0 + 32 ti + l32, columns c0 + 32 wave + 8 (r / 4) + 4 h2 + r % 4
+  if (c0 >= D * D) {  // the z_D tile: float32, straight from the accumulators
+#pragma unroll
+    for (int ti = 0; ti < IB / 32; ++ti) {
+      const int i = i0 + 32 * ti + l32;
+      if (i >= n_q) continue;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = c0 + 32 * wave + 8 * g + 4 * h2;
+        if (col < COLS)
+          *reinterpret_cast<float4*>(zd + ((size_t)bh * n_q + i) * D + (col - D * D)) =
+              make_float4(acc[ti][4 * g], acc[ti][4 * g + 1], acc[ti][4 * g + 2], acc[ti][4 * g + 3]);
+      }
+    }
+    return;
+  }
+  __syncthreads();  // every wave is done with the stage buffers
 #pragma unroll
   for (int ti = 0; ti < IB / 32; ++ti) {
-    const int i = i0 + 32 * ti + l32;
-    if (i >= n_q) continue;
-    const size_t qb = (size_t)bh * n_q + i;
+    // both planes of 32 query blocks x the workgroup's 128 columns, rows of SP bytes
+    unsigned char* stg = smem + (ti & 1) * (2 * 32 * SP);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const int col = c0 + 32 * wave + 8 * g + 4 * h2;
-      if (col + 4 <= D * D) {
-        uint32_t hw[2], lw[2];
+      uint32_t hw[2], lw[2];
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const float x0 = acc[ti][4 * g + 2 * e], x1 = acc[ti][4 * g + 2 * e + 1];
-          const uint32_t h0 = f32_to_bf16_rne(x0), h1 = f32_to_bf16_rne(x1);
-          hw[e] = h0 | (h1 << 16);
-          lw[e] = f32_to_bf16_rne(x0 - __uint_as_float(h0 << 16)) |
-                  (f32_to_bf16_rne(x1 - __uint_as_float(h1 << 16)) << 16);
-        }
-        uint16_t* dst = hd + qb * 2 * D * D + col;
-        *reinterpret_cast<uint2*>(dst) = make_uint2(hw[0], hw[1]);
-        *reinterpret_cast<uint2*>(dst + D * D) = make_uint2(lw[0], lw[1]);
-      } else if (col < COLS) {
-        *reinterpret_cast<float4*>(zd + qb * D + (col - D * D)) =
-            make_float4(acc[ti][4 * g], acc[ti][4 * g + 1], acc[ti][4 * g + 2], acc[ti][4 * g + 3]);
+      for (int e = 0; e < 2; ++e) {
+        const float x0 = acc[ti][4 * g + 2 * e], x1 = acc[ti][4 * g + 2 * e + 1];
+        const uint32_t h0 = f32_to_bf16_rne(x0), h1 = f32_to_bf16_rne(x1);
+        hw[e] = h0 | (h1 << 16);
+        lw[e] = f32_to_bf16_rne(x0 - __uint_as_float(h0 << 16)) |
+                (f32_to_bf16_rne(x1 - __uint_as_float(h1 << 16)) << 16);
       }
+      const int ofs = l32 * SP + 2 * (32 * wave + 8 * g + 4 * h2);
+      *reinterpret_cast<uint2*>(stg + ofs) = make_uint2(hw[0], hw[1]);
+      *reinterpret_cast<uint2*>(stg + 32 * SP + ofs) = make_uint2(lw[0], lw[1]);
+    }
+    __syncthreads();  // the staged rows are complete (and the other buffer's readers are done)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {  // 2 planes x 32 rows x 16 chunks, 64 chunks per copy
+      const int idx = 64 * (4 * u + wave) + lane;
+      const int pl = idx >> 9, row = (idx >> 4) & 31, ch = idx & 15;
+      const int i = i0 + 32 * ti + row;
+      if (i < n_q)
+        *reinterpret_cast<bf16x8*>(hd + (((size_t)bh * n_q + i) * 2 + pl) * D * D + c0 + 8 * ch) =
+            lds_read16(stg + pl * 32 * SP + row * SP + 16 * ch);
     }
   }
 }
@@ -766,12 +799,12 @@ hipError_t launch_sparse(const AttnLaunch& a, hipStream_t s, AttnPhase phase) {
   }
   if (phase != kPackOnly) {
     if constexpr (LIN) {
-      const int rows = BH * a.n_q, n_kp = (a.n_k + 31) / 32 * 32;
+      const int rows = BH * a.n_q, n_kw = (a.n_k + 31) / 32;
       hipLaunchKernelGGL(linear_mdrop_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, a.idx, a.cnt,
-                         a.mdrop, a.n_k, n_kp, rows);
+                         a.mbits, a.n_k, n_kw, rows);
       hipLaunchKernelGGL((linear_hd_kernel<D>),
                          dim3((lin_cols<D>() + 127) / 128, (a.n_q + 255) / 256, BH), dim3(256), 0,
-                         s, a.hj, a.mdrop, a.hd, a.zd, a.n_q, a.n_k, n_kp, a.lin_on, a.H);
+                         s, a.hj, a.mbits, a.hd, a.zd, a.n_q, a.n_k, n_kw, a.lin_on, a.H);
       if (a.lse)
         hipLaunchKernelGGL((sparse_attn_fwd_kernel<D, BQ, true, true>), dim3(total), dim3(BQ * 2),
                            0, s, a.q, a.k, a.vt, a.idx, a.cnt, a.o, a.H, a.N, a.n_q, a.n_k, total,
@@ -806,7 +839,7 @@ size_t attn_workspace_bytes(int B, int H, int N, int d) {
 // branch flags and head lists; every part 256-byte aligned.
 size_t linear_layout(AttnLaunch& a, unsigned char* w, int B, int H, int N, int d, int block_q) {
   const size_t BH = (size_t)B * H, n_k = (N + BK - 1) / BK, n_q = (N + block_q - 1) / block_q;
-  const size_t n_kp = (n_k + 31) / 32 * 32, cols = (size_t)d * d + d;
+  const size_t n_kw = (n_k + 31) / 32, cols = (size_t)d * d + d;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     unsigned char* p = w ? w + off : nullptr;
@@ -815,7 +848,7 @@ size_t linear_layout(AttnLaunch& a, unsigned char* w, int B, int H, int N, int d
   };
   a.vt = reinterpret_cast<uint16_t*>(take(attn_workspace_bytes(B, H, N, d)));
   a.hj = reinterpret_cast<uint16_t*>(take(BH * n_k * 2 * cols * 2));
-  a.mdrop = reinterpret_cast<uint16_t*>(take(BH * n_q * n_kp * 2));
+  a.mbits = reinterpret_cast<uint32_t*>(take(BH * n_q * n_kw * 4));
   a.hd = reinterpret_cast<uint16_t*>(take(BH * n_q * 2 * (size_t)d * d * 2));
   a.zd = reinterpret_cast<float*>(take(BH * n_q * d * 4));
   a.lin_on = reinterpret_cast<int32_t*>(take((size_t)H * 4));

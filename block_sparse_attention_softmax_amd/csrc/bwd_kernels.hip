@@ -218,10 +218,6 @@ struct DkdvStage {
   static constexpr int BYTES = 2 * ROWS + 2 * BQ * 4;
 };
 
-__device__ __forceinline__ void dma4(const void* src, void* lds) {
-  __builtin_amdgcn_global_load_lds(src, lds, 4, 0, 0);
-}
-
 template <int D, int BQ>
 __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void sparse_attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,

@@ -106,11 +106,12 @@ struct AttnLaunch {
   int32_t* lin_on;     // [H] 1 where the branch is evaluated
   int32_t* lin_lists;  // [2 + 2*B*H] counts, then the b*H + h with the branch on, then off
   uint16_t* hj;        // [B*H, n_k, 2, d*d + d] bf16 planes of H_j^T and z_j per key block
-  uint16_t* mdrop;     // [B*H, n_q, n_k rounded up to 32] bf16 1 where block j is dropped
+  uint32_t* mbits;     // [B*H, n_q, ceil(n_k / 32)] bit j set where block j is dropped
   uint16_t* hd;        // [B*H, n_q, 2, d, d] bf16 planes of H_D^T per query block
   float* zd;           // [B*H, n_q, d] z_D per query block
 };
 constexpr int kLinSplit = 64;
+constexpr int kLinMaxKeyBlocks = 4096;  // the linear forward's drop bitmaps (one LDS row each)
 // how the linear branch meets the sparse output: O_s + alpha[h] O_l, or the
 // per-channel mix alpha[h][c] O_s + (1 - alpha[h][c]) O_l
 enum LinMode { kLinAdd = 0, kLinMix = 1 };

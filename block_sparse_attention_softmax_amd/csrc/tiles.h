@@ -115,6 +115,11 @@ __device__ __forceinline__ bf16x8 lds_read16(const unsigned char* p) {
 __device__ __forceinline__ void dma16(const void* src, void* lds) {
   __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
 }
+// The same for 4 bytes per lane (global_load_lds_dword): lane i's word lands
+// at lds + 4 * i.
+__device__ __forceinline__ void dma4(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds(src, lds, 4, 0, 0);
+}
 
 // Orders a wave's own LDS writes before its later LDS reads of other lanes'
 // data (a wave's LDS instructions execute in order; this keeps the compiler

@@ -275,8 +275,8 @@ int sparge_attn_bwd(const void* q, const void* k, const void* v, const void* o,
 /* Device workspace (bytes) of sparse_linear_attn_fwd: the packed V of
  * sparge_attn_fwd; per (b, h) and key block
  * the summary phi(K_j)^T V_j (d x d) and sum phi(K_j) (d) as two bf16 planes
- * (hi and the rounded remainder); per (b, h) the drop matrix (bf16, one row
- * per query block of the key-block count rounded up to 32); per query block
+ * (hi and the rounded remainder); per (b, h) the drop bits (one uint32 per
+ * 32 key blocks, rounded up, per query block); per query block
  * the dropped-block sums as two bf16 planes of d x d and d float32; and
  * H + 2 + 2*B*H int32 for the per-head branch flags and the lists of
  * (batch, head) pairs by flag; each part rounded up to 256 bytes. Returns 0
@@ -295,8 +295,8 @@ size_t sparse_linear_workspace_bytes(int B, int H, int N, int d);
  * phi(K) and V, carries them and their sums over D_i with about 16
  * significant bits (two bf16 planes) and accumulates in float32; its final
  * product phi(Q) . (sum over D_i) carries about 16 significant bits per
- * operand. Built for block_q == d (64 or 128); other block sizes
- * return SPARGE_ERR_UNSUPPORTED.
+ * operand. Built for block_q == d (64 or 128) and at most 4096 key blocks
+ * (N <= 262144); other sizes return SPARGE_ERR_UNSUPPORTED.
  *
  * Post-tuning branch dropping (SALAD page): a head with |alpha[h]| <=
  * drop_below (float32 comparison) skips its linear branch entirely (no phi(K)

@@ -48,11 +48,12 @@ def test_mask_workspace_bytes():
     n_k, n_q = math.ceil(75600 / 64), math.ceil(75600 / 128)
     lin = (packed_v
            + up(40 * n_k * 2 * (128 * 128 + 128) * 2)   # per-key-block summaries, 2 bf16 planes
-           + up(40 * n_q * math.ceil(n_k / 32) * 32 * 2)  # drop matrix (bf16)
+           + up(40 * n_q * math.ceil(n_k / 32) * 4)     # drop bits
            + up(40 * n_q * 2 * 128 * 128 * 2)           # dropped-block sums, 2 bf16 planes
            + up(40 * n_q * 128 * 4)                     # their phi(K) sums, float32
            + up(40 * 4) + up((2 + 2 * 40) * 4))         # branch flags, head lists
     assert L.sparse_linear_workspace_bytes(1, 40, 75600, 128) == lin
+    assert L.sparse_linear_workspace_bytes(1, 1, 64 * 4097, 64) == 0  # > 4096 key blocks
 
 
 def _mask(**kw):
