@@ -382,6 +382,42 @@ def test_sparse_linear_small_shapes_in_full(B, H, N, d, bq):
             print(f"[linear] b={b} h={h}: max {mx:.2e} mean {mean:.2e}", flush=True)
 
 
+@pytest.mark.parametrize("N,d,sampled", [(4480, 64, False), (19217, 64, True), (38405, 128, True)])
+def test_sparse_linear_long_rows_and_many_query_blocks(N, d, sampled):
+    """Key-block counts that are not a multiple of 32 and span several stages of
+    the dropped-block product (70, 301 and 601 blocks: the last bit word is
+    partial), and 301 query blocks, so the product runs a second tile of
+    query blocks holding 45 of them. Sampled query blocks include the first and
+    last of each tile and the ragged last block."""
+    rng = np.random.default_rng(N + 3 * d)
+    from block_sparse_attention_softmax_amd.workloads import f64_to_bf16_bits
+    H = 2 if N < 10000 else 1
+    Q, K, V = (f64_to_bf16_bits(rng.standard_normal((1, H, N, d))) for _ in range(3))
+    n_q, n_k = -(-N // d), -(-N // 64)
+    kept = _random_lists(rng, 1, H, n_q, n_k)
+    idx, cnt = O.kept_to_index_list(kept)
+    alpha = rng.uniform(0.05, 0.8, size=H).astype(np.float32)
+    print(f"\n[linear long] N={N} d={d} n_q={n_q} n_k={n_k}", flush=True)
+    q = to_gpu(Q)
+    o = S.sparse_linear_attn_fwd(q, to_gpu(K), to_gpu(V), torch.from_numpy(idx).cuda(),
+                                 torch.from_numpy(cnt).cuda(), torch.from_numpy(alpha).cuda(),
+                                 d, 64, out=nan_like(q))
+    torch.cuda.synchronize()
+    assert_all_written(o)
+    got = O.bf16_to_f64(o.cpu().view(torch.uint16).numpy())
+    blocks = None
+    if sampled:
+        blocks = sorted({0, 1, 2, 255, 256, n_q - 1, *rng.choice(n_q, 3, replace=False)})
+    for h in range(H):
+        ref = O.sparse_linear_attention_head(O.bf16_to_f64(Q[0, h]), O.bf16_to_f64(K[0, h]),
+                                             O.bf16_to_f64(V[0, h]), kept[0, h], d, 64,
+                                             S.default_scale(d), float(alpha[h]),
+                                             q_blocks=blocks)
+        rows = ~np.isnan(ref[:, 0])
+        mx, mean = compare_outputs(got[0, h][rows], ref[rows])
+        print(f"[linear long] h={h} blocks={blocks}: max {mx:.2e} mean {mean:.2e}", flush=True)
+
+
 @pytest.mark.parametrize("B,H,N,d", [(1, 2, 1000, 128), (2, 1, 1500, 64)])
 def test_sparse_linear_dense_lists_sum_the_dropped_blocks(B, H, N, d):
     """Rows listing more than half of the key blocks take the branch's other
