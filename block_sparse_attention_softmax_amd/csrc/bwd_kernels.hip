@@ -819,34 +819,40 @@ __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void sparse
 // The sparse part's D_t = dO_t . O_s,t equals dO_t . O_t - G_t . O_l,t, so the
 // row kernel subtracts G . O_l from D.
 
-// Per (b, h, query block of D rows), 4 waves. First H_D, z_D on the matrix
-// cores from the packed phi(K)^T and V^T tiles of whichever list is shorter:
-// H_tot minus the listed blocks (as the forward forms it), or the sum over the
-// blocks not listed (their list is built in LDS in increasing order). The
-// tiles are copied global -> LDS by direct-to-LDS loads three blocks ahead of
-// the products (four buffers in the space the second part reuses). Then, 32
-// rows at a time in float32 on the vector units: O_l, dnum, dden, the
-// correction of D, dQ_l = dphi(Q) phi'(Q) and the block's dH_D, dz_D (written
-// for the key kernel). Rows of phi(Q) and dnum in LDS are padded by 4 floats
-// and the dQ loop takes channels part + 8 i, so that the 8 rows or channels a
-// wave reads at once fall in different banks. Heads whose branch is off and
-// blocks that dropped nothing write zeros.
+// LDS of linear_bwd_rows_kernel: H_D (rows of HP floats, row = phi(K)
+// channel), z_D, then 32 rows of phi(Q) and dnum (rows of FP floats) and dden.
+template <int D>
+struct LinRowsLds {
+  static constexpr int HP = D + 4, FP = D + 4, CH = 32;
+  static constexpr int HS = 0, ZS = HS + D * HP * 4, FQ = ZS + D * 4, DN = FQ + CH * FP * 4,
+                       DDEN = DN + CH * FP * 4, BYTES = DDEN + CH * 4;
+};
 
+// Per (b, h, query block of D rows), 4 waves. H_D comes from the two bf16
+// planes of H_D^T that the dropped-block product left for the query block
+// (summed into float32 and transposed into LDS), z_D from its float32 row.
+// Then, 32 rows at a time in float32 on the vector units: O_l, dnum, dden,
+// the correction of D, dQ_l = dphi(Q) phi'(Q) and the block's dH_D, dz_D,
+// written as two bf16 planes (hi, rounded remainder) of D*D + D columns
+// (dH_D row-major, then dz_D) for the product that sums them per key block.
+// Rows of phi(Q) and dnum in LDS are padded by 4 floats and the dQ loop takes
+// channels part + 8 i, so that the 8 rows or channels a wave reads at once
+// fall in different banks. Heads whose branch is off and blocks that dropped
+// nothing write zeros.
 template <int D>
 __global__ __launch_bounds__(256, 1) void linear_bwd_rows_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ dO,
-    const uint16_t* __restrict__ phikt, const uint16_t* __restrict__ vt,
-    const float* __restrict__ lin_h, const float* __restrict__ lin_z,
-    const int32_t* __restrict__ kv_idx, const int32_t* __restrict__ kv_cnt,
-    const int32_t* __restrict__ lin_on, const float* __restrict__ alpha, int mode,
-    float* __restrict__ dql, float* __restrict__ dHq, float* __restrict__ dzq,
-    float* __restrict__ drow, int H, int N, int n_q, int n_k, int NP, int total) {
+    const uint16_t* __restrict__ hd, const float* __restrict__ zd,
+    const int32_t* __restrict__ kv_cnt, const int32_t* __restrict__ lin_on,
+    const float* __restrict__ alpha, int mode, float* __restrict__ dql,
+    uint16_t* __restrict__ dhp, float* __restrict__ drow, int H, int N, int n_q, int n_k, int NP,
+    int total) {
   using LS = LinRowsLds<D>;
-  constexpr int HP = LS::HP, FP = LS::FP, CH = LS::CH;
+  constexpr int HP = LS::HP, FP = LS::FP, CH = LS::CH, COLS = lin_cols<D>();
   constexpr int AT = D / 16, CPT = D / 8;  // dH entries per thread per side; channels per thread
   __shared__ __align__(16) unsigned char smem[LS::BYTES];
-  const float* const Hs = reinterpret_cast<const float*>(smem + LS::HS);
-  const float* const zs = reinterpret_cast<const float*>(smem + LS::ZS);
+  float* const Hs = reinterpret_cast<float*>(smem + LS::HS);
+  float* const zs = reinterpret_cast<float*>(smem + LS::ZS);
   float* const fq = reinterpret_cast<float*>(smem + LS::FQ);
   float* const dn = reinterpret_cast<float*>(smem + LS::DN);
   float* const dden_s = reinterpret_cast<float*>(smem + LS::DDEN);
@@ -858,26 +864,36 @@ __global__ __launch_bounds__(256, 1) void linear_bwd_rows_kernel(
   const int row0 = qi * D;
   const int count = min(max(kv_cnt[tile], 0), n_k);
   const int a0 = (th / 16) * AT, c0 = (th % 16) * AT;
-  float* const dh_out = dHq + ((size_t)bh * n_q + qi) * D * D;
-  float* const dz_out = dzq + ((size_t)bh * n_q + qi) * D;
+  uint16_t* const dh_out = dhp + ((size_t)bh * n_q + qi) * 2 * COLS;
 
   if (lin_on[h] == 0 || count >= n_k) {  // no linear gradient from this block
     for (int e = th; e < CH * (D / CH) * D; e += 256) {
       const int row = row0 + e / D;
       if (row < N) dql[head + (size_t)row * D + e % D] = 0.0f;
     }
-#pragma unroll
-    for (int i = 0; i < AT; ++i)
-#pragma unroll
-      for (int j = 0; j < AT; ++j) dh_out[(size_t)(a0 + i) * D + c0 + j] = 0.0f;
-    if (th % 16 == 0)
-#pragma unroll
-      for (int i = 0; i < AT; ++i) dz_out[a0 + i] = 0.0f;
+    for (int e = th; e < 2 * COLS / 8; e += 256)
+      reinterpret_cast<uint4*>(dh_out)[e] = make_uint4(0u, 0u, 0u, 0u);
     return;
   }
 
-  // ---- H_D and z_D
-  form_hd<D>(smem, phikt, vt, lin_h, lin_z, kv_idx + (size_t)tile * n_k, count, bh, n_k);
+  // ---- H_D (Hs[a][c] = H_D^T[c][a], both planes summed) and z_D
+  {
+    const uint16_t* hsrc = hd + ((size_t)bh * n_q + qi) * 2 * D * D;
+    for (int e = th; e < D * D / 8; e += 256) {
+      const int c = 8 * e / D, a8 = 8 * e % D;
+      const uint4 hi = *reinterpret_cast<const uint4*>(hsrc + 8 * e);
+      const uint4 lo = *reinterpret_cast<const uint4*>(hsrc + D * D + 8 * e);
+      const uint32_t* wh = &hi.x;
+      const uint32_t* wl = &lo.x;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        Hs[(a8 + 2 * x) * HP + c] = bf16_lo(wh[x]) + bf16_lo(wl[x]);
+        Hs[(a8 + 2 * x + 1) * HP + c] = bf16_hi(wh[x]) + bf16_hi(wl[x]);
+      }
+    }
+    if (th < D) zs[th] = zd[((size_t)bh * n_q + qi) * D + th];
+    __syncthreads();
+  }
 
   // ---- rows, 32 at a time
   float dh[AT][AT], dzacc[AT];
@@ -1002,64 +1018,45 @@ __global__ __launch_bounds__(256, 1) void linear_bwd_rows_kernel(
     }
     __syncthreads();  // the next chunk overwrites fq, dn
   }
+  // two bf16 planes: hi = bf16(x), lo = bf16(x - hi)
 #pragma unroll
   for (int i = 0; i < AT; ++i)
 #pragma unroll
-    for (int j = 0; j < AT; ++j) dh_out[(size_t)(a0 + i) * D + c0 + j] = dh[i][j];
+    for (int j = 0; j < AT; j += 2) {
+      const uint32_t h0 = f32_to_bf16_rne(dh[i][j]), h1 = f32_to_bf16_rne(dh[i][j + 1]);
+      const uint32_t l0 = f32_to_bf16_rne(dh[i][j] - __uint_as_float(h0 << 16));
+      const uint32_t l1 = f32_to_bf16_rne(dh[i][j + 1] - __uint_as_float(h1 << 16));
+      const size_t col = (size_t)(a0 + i) * D + c0 + j;
+      *reinterpret_cast<uint32_t*>(dh_out + col) = h0 | (h1 << 16);
+      *reinterpret_cast<uint32_t*>(dh_out + COLS + col) = l0 | (l1 << 16);
+    }
   if (th % 16 == 0)
 #pragma unroll
-    for (int i = 0; i < AT; ++i) dz_out[a0 + i] = dzacc[i];
-}
-
-// dH_tot[bh] = sum over the query blocks of dH_D, dz_tot likewise, in block
-// order. Grid (B*H, chunks of 256 entries).
-template <int D>
-__global__ __launch_bounds__(256) void linear_bwd_total_kernel(const float* __restrict__ dHq,
-                                                               const float* __restrict__ dzq,
-                                                               float* __restrict__ dHt,
-                                                               float* __restrict__ dzt,
-                                                               int n_q) {
-  const int bh = blockIdx.x, e = blockIdx.y * 256 + threadIdx.x;
-  if (e >= D * D + D) return;
-  const bool hpart = e < D * D;
-  const float* src = hpart ? dHq + (size_t)bh * n_q * D * D + e
-                           : dzq + (size_t)bh * n_q * D + (e - D * D);
-  const size_t stride = hpart ? (size_t)D * D : (size_t)D;
-  float acc = 0.0f;  // in block order, eight blocks' entries loaded at a time
-  int i = 0;
-  for (; i + 8 <= n_q; i += 8) {
-    float v[8];
-#pragma unroll
-    for (int x = 0; x < 8; ++x) v[x] = src[(size_t)(i + x) * stride];
-#pragma unroll
-    for (int x = 0; x < 8; ++x) acc += v[x];
-  }
-  for (; i < n_q; ++i) acc += src[(size_t)i * stride];
-  if (hpart)
-    dHt[(size_t)bh * D * D + e] = acc;
-  else
-    dzt[(size_t)bh * D + (e - D * D)] = acc;
+    for (int i = 0; i < AT; ++i) {
+      const uint32_t hz = f32_to_bf16_rne(dzacc[i]);
+      dh_out[D * D + a0 + i] = (uint16_t)hz;
+      dh_out[COLS + D * D + a0 + i] = (uint16_t)f32_to_bf16_rne(dzacc[i] - __uint_as_float(hz << 16));
+    }
 }
 
 // Per (b, h, key block j): G_j = the sum of dH_D over the query blocks that
-// dropped j, as dH_tot minus the listing blocks or directly over the others,
-// whichever is shorter (g_j likewise), then for its 64 keys in float32
-// dV_l = phi(K) G_j and dK_l = (G_j V + g_j) phi'(K). Heads whose branch is
-// off write zeros.
+// dropped j and g_j = that of dz_D, both from the dropped-block product (two
+// bf16 planes of G_j, row-major, summed into float32 in LDS; g_j float32),
+// then for its 64 keys in float32 dV_l = phi(K) G_j and dK_l = (G_j V + g_j)
+// phi'(K). Heads whose branch is off write zeros.
 template <int D>
 __global__ __launch_bounds__(256, 1) void linear_bwd_keys_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const float* __restrict__ dHq, const float* __restrict__ dzq,
-    const float* __restrict__ dHt, const float* __restrict__ dzt,
-    const int32_t* __restrict__ cmat, const int32_t* __restrict__ colcnt,
-    const int32_t* __restrict__ coloff, const int32_t* __restrict__ collist,
+    const uint16_t* __restrict__ gp, const float* __restrict__ gz,
     const int32_t* __restrict__ lin_on, float* __restrict__ dkl, float* __restrict__ dvl,
-    int H, int N, int n_q, int n_k, int total) {
-  constexpr int HP = D + 4, F4 = D * D / 4 / 256, KPT = D / 4;  // float4 of G per thread
+    int H, int N, int n_k, int total) {
+  // G row pitch; phi(K) and V row pitch (the 16 keys a wave reads at once
+  // fall in different banks); channels per thread
+  constexpr int HP = D + 4, KP = D + 4, KPT = D / 4;
   __shared__ __align__(16) float Gs[D * HP];
   __shared__ __align__(16) float gs[D];
-  __shared__ __align__(16) float fk[BK * D];
-  __shared__ __align__(16) float vr[BK * D];
+  __shared__ __align__(16) float fk[BK * KP];
+  __shared__ __align__(16) float vr[BK * KP];
   const int tile = xcd_remap(blockIdx.x, total);
   const int bh = tile / n_k, j = tile % n_k, h = bh % H;
   const int th = threadIdx.x;
@@ -1076,90 +1073,25 @@ __global__ __launch_bounds__(256, 1) void linear_bwd_keys_kernel(
       }
     return;
   }
-  const int listed = colcnt[(size_t)bh * n_k + j];
-  const bool use_kept = listed <= n_q - listed;
-  // the query blocks to take, in increasing order: those that list j (their
-  // dH_D is subtracted from dH_tot) or those that do not (summed); the latter
-  // are gathered from the count matrix into LDS by a ballot compaction
-  __shared__ int blist[kMaxLinQueryBlocks];
-  int nb;
-  const int32_t* lsrc;
-  if (use_kept) {
-    nb = listed;
-    lsrc = collist + (size_t)bh * n_q * n_k + coloff[(size_t)bh * (n_k + 1) + j];
-  } else {
-    __shared__ int wcnt[4];
-    const int32_t* cm = cmat + ((size_t)bh * n_k + j) * n_q;
-    int base = 0;
-    for (int i0b = 0; i0b < n_q; i0b += 256) {
-      const int i = i0b + th;
-      const bool take = i < n_q && cm[i] == 0;
-      const uint64_t bal = __ballot(take);
-      const int lane = th & 63, wv = th >> 6;
-      if (lane == 0) wcnt[wv] = __popcll(bal);
-      __syncthreads();
-      int before = base;
-      for (int w = 0; w < wv; ++w) before += wcnt[w];
-      if (take) blist[before + __popcll(bal & ((1ull << lane) - 1ull))] = i;
-      base += wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
-      __syncthreads();
-    }
-    nb = base;
-    lsrc = blist;
-  }
-  float4 gacc[F4];
-  float4 zacc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  const bool zthread = th < D / 4;
-  if (use_kept) {
-    const float4* t4 = reinterpret_cast<const float4*>(dHt + (size_t)bh * D * D);
-#pragma unroll
-    for (int m = 0; m < F4; ++m) gacc[m] = t4[m * 256 + th];
-    if (zthread) zacc = reinterpret_cast<const float4*>(dzt + (size_t)bh * D)[th];
-  } else {
-#pragma unroll
-    for (int m = 0; m < F4; ++m) gacc[m] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  }
-  const float sg = use_kept ? -1.0f : 1.0f;  // exact: x * -1 and x * 1 change no bit
-  // two blocks' dH_D in flight: the loads of block e + 1 are issued before the
-  // sums of block e, which are taken in order
-  auto load_blk = [&](int e, float4 (&x)[F4], float4& z) {
-    const int i = lsrc[e];
-    const float4* q4 = reinterpret_cast<const float4*>(dHq + ((size_t)bh * n_q + i) * D * D);
-#pragma unroll
-    for (int m = 0; m < F4; ++m) x[m] = q4[m * 256 + th];
-    if (zthread) z = reinterpret_cast<const float4*>(dzq + ((size_t)bh * n_q + i) * D)[th];
-  };
-  auto add_blk = [&](const float4 (&x)[F4], const float4& z) {
-#pragma unroll
-    for (int m = 0; m < F4; ++m) {
-      gacc[m].x = fmaf(sg, x[m].x, gacc[m].x); gacc[m].y = fmaf(sg, x[m].y, gacc[m].y);
-      gacc[m].z = fmaf(sg, x[m].z, gacc[m].z); gacc[m].w = fmaf(sg, x[m].w, gacc[m].w);
-    }
-    if (zthread) {
-      zacc.x = fmaf(sg, z.x, zacc.x); zacc.y = fmaf(sg, z.y, zacc.y);
-      zacc.z = fmaf(sg, z.z, zacc.z); zacc.w = fmaf(sg, z.w, zacc.w);
-    }
-  };
   {
-    float4 xa[F4], xb[F4], za = make_float4(0.0f, 0.0f, 0.0f, 0.0f), zb = za;
-    int e = 0;
-    for (; e + 2 <= nb; e += 2) {
-      load_blk(e, xa, za);
-      load_blk(e + 1, xb, zb);
-      add_blk(xa, za);
-      add_blk(xb, zb);
-    }
-    if (e < nb) {
-      load_blk(e, xa, za);
-      add_blk(xa, za);
-    }
-  }
+    const uint16_t* gsrc = gp + ((size_t)bh * n_k + j) * 2 * D * D;
+    for (int e = th; e < D * D / 8; e += 256) {
+      const uint4 hi = *reinterpret_cast<const uint4*>(gsrc + 8 * e);
+      const uint4 lo = *reinterpret_cast<const uint4*>(gsrc + D * D + 8 * e);
+      const uint32_t* wh = &hi.x;
+      const uint32_t* wl = &lo.x;
+      float g8[8];
 #pragma unroll
-  for (int m = 0; m < F4; ++m) {
-    const int e = (m * 256 + th) * 4, a = e / D, cc = e % D;
-    *reinterpret_cast<float4*>(Gs + a * HP + cc) = gacc[m];
+      for (int x = 0; x < 4; ++x) {
+        g8[2 * x] = bf16_lo(wh[x]) + bf16_lo(wl[x]);
+        g8[2 * x + 1] = bf16_hi(wh[x]) + bf16_hi(wl[x]);
+      }
+      float* dst = Gs + (8 * e / D) * HP + 8 * e % D;
+      *reinterpret_cast<float4*>(dst) = make_float4(g8[0], g8[1], g8[2], g8[3]);
+      *reinterpret_cast<float4*>(dst + 4) = make_float4(g8[4], g8[5], g8[6], g8[7]);
+    }
+    if (th < D) gs[th] = gz[((size_t)bh * n_k + j) * D + th];
   }
-  if (zthread) *reinterpret_cast<float4*>(gs + 4 * th) = zacc;
   for (int p = th; p < BK * D / 8; p += 256) {  // phi(K) and V rows of the block, zero past N
     const int uu = p / (D / 8), c8 = (p % (D / 8)) * 8;
     float f[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
@@ -1179,8 +1111,8 @@ __global__ __launch_bounds__(256, 1) void linear_bwd_keys_kernel(
     }
 #pragma unroll
     for (int e = 0; e < 8; e += 4) {
-      *reinterpret_cast<float4*>(fk + uu * D + c8 + e) = make_float4(f[e], f[e + 1], f[e + 2], f[e + 3]);
-      *reinterpret_cast<float4*>(vr + uu * D + c8 + e) = make_float4(w8[e], w8[e + 1], w8[e + 2], w8[e + 3]);
+      *reinterpret_cast<float4*>(fk + uu * KP + c8 + e) = make_float4(f[e], f[e + 1], f[e + 2], f[e + 3]);
+      *reinterpret_cast<float4*>(vr + uu * KP + c8 + e) = make_float4(w8[e], w8[e + 1], w8[e + 2], w8[e + 3]);
     }
   }
   __syncthreads();
@@ -1190,7 +1122,7 @@ __global__ __launch_bounds__(256, 1) void linear_bwd_keys_kernel(
 #pragma unroll
   for (int cc = 0; cc < KPT; ++cc) dvv[cc] = 0.0f;
   for (int a = 0; a < D; ++a) {
-    const float f = fk[u * D + a];
+    const float f = fk[u * KP + a];
 #pragma unroll
     for (int cc = 0; cc < KPT; cc += 4) {
       const float4 gv = *reinterpret_cast<const float4*>(Gs + a * HP + cb + cc);
@@ -1210,13 +1142,13 @@ __global__ __launch_bounds__(256, 1) void linear_bwd_keys_kernel(
     float s2 = gs[a];
     for (int cc = 0; cc < D; cc += 4) {
       const float4 gv = *reinterpret_cast<const float4*>(Gs + a * HP + cc);
-      const float4 vv = *reinterpret_cast<const float4*>(vr + u * D + cc);
+      const float4 vv = *reinterpret_cast<const float4*>(vr + u * KP + cc);
       s2 = fmaf(gv.x, vv.x, s2);
       s2 = fmaf(gv.y, vv.y, s2);
       s2 = fmaf(gv.z, vv.z, s2);
       s2 = fmaf(gv.w, vv.w, s2);
     }
-    const float f = fk[u * D + a];
+    const float f = fk[u * KP + a];
     ko[a] = s2 * (f > 1.0f ? 1.0f : f);
   }
 }
@@ -1255,10 +1187,11 @@ struct BwdWs {
   float *drow, *lse2;
   int32_t *cmat, *colcnt, *coloff, *collist;
   // linear branch
-  uint16_t *vtp, *phikt, *dos;
-  float *lin_h, *lin_z, *part_h, *part_z;
+  uint16_t *vtp, *dos, *hj, *hd, *dhp, *gp;
+  uint32_t *mbits, *mtbits;
+  float *zd, *gz;
   int32_t *lin_on, *lin_lists;
-  float *dql, *dkl, *dvl, *dHq, *dzq, *dHt, *dzt;
+  float *dql, *dkl, *dvl;
 };
 
 BwdWs bwd_layout(unsigned char* w, int B, int H, int N, int d, int block_q, bool linear,
@@ -1280,22 +1213,22 @@ BwdWs bwd_layout(unsigned char* w, int B, int H, int N, int d, int block_q, bool
   r.coloff = reinterpret_cast<int32_t*>(take(BH * (n_k + 1) * 4));
   r.collist = reinterpret_cast<int32_t*>(take(BH * n_q * n_k * 4));
   if (linear) {
+    const size_t cols = (size_t)d * d + d, n_kw = (n_k + 31) / 32, n_qw = (n_q + 31) / 32;
     r.vtp = reinterpret_cast<uint16_t*>(take(packed));
-    r.phikt = reinterpret_cast<uint16_t*>(take(packed));
     r.dos = reinterpret_cast<uint16_t*>(take(rows * 2));
-    r.lin_h = reinterpret_cast<float*>(take(BH * d * d * 4));
-    r.lin_z = reinterpret_cast<float*>(take(BH * d * 4));
-    r.part_h = reinterpret_cast<float*>(take(BH * kLinSplit * d * d * 4));
-    r.part_z = reinterpret_cast<float*>(take(BH * kLinSplit * d * 4));
+    r.hj = reinterpret_cast<uint16_t*>(take(BH * n_k * 2 * cols * 2));
+    r.mbits = reinterpret_cast<uint32_t*>(take(BH * n_q * n_kw * 4));
+    r.hd = reinterpret_cast<uint16_t*>(take(BH * n_q * 2 * (size_t)d * d * 2));
+    r.zd = reinterpret_cast<float*>(take(BH * n_q * d * 4));
+    r.dhp = reinterpret_cast<uint16_t*>(take(BH * n_q * 2 * cols * 2));
+    r.mtbits = reinterpret_cast<uint32_t*>(take(BH * n_k * n_qw * 4));
+    r.gp = reinterpret_cast<uint16_t*>(take(BH * n_k * 2 * (size_t)d * d * 2));
+    r.gz = reinterpret_cast<float*>(take(BH * n_k * d * 4));
     r.lin_on = reinterpret_cast<int32_t*>(take(H * 4));
     r.lin_lists = reinterpret_cast<int32_t*>(take((2 + 2 * BH) * 4));
     r.dql = reinterpret_cast<float*>(take(rows * 4));
     r.dkl = reinterpret_cast<float*>(take(rows * 4));
     r.dvl = reinterpret_cast<float*>(take(rows * 4));
-    r.dHq = reinterpret_cast<float*>(take(BH * n_q * d * d * 4));
-    r.dzq = reinterpret_cast<float*>(take(BH * n_q * d * 4));
-    r.dHt = reinterpret_cast<float*>(take(BH * d * d * 4));
-    r.dzt = reinterpret_cast<float*>(take(BH * d * 4));
   }
   if (bytes) *bytes = off;
   return r;
@@ -1312,12 +1245,15 @@ hipError_t launch_bwd_t(const BwdLaunch& a, hipStream_t s) {
     if constexpr (D == BQ) {
       hipLaunchKernelGGL(linear_flags_kernel, dim3(1), dim3(kFlagThreads), 0, s, a.alpha,
                          a.lin_mode, D, a.drop_below, a.B, a.H, w.lin_on, w.lin_lists);
-      hipLaunchKernelGGL((pack_kernel<D, true>), dim3(a.n_k, BH), dim3(2 * D), 0, s, a.v, a.k,
-                         w.vtp, w.phikt, a.N, a.n_k, w.lin_on, a.H);
-      hipLaunchKernelGGL((linear_total_kernel<D>), dim3(kLinSplit, BH), dim3(D * 2), 0, s,
-                         w.phikt, w.vtp, w.part_h, w.part_z, a.n_k, w.lin_on, a.H);
-      hipLaunchKernelGGL((linear_reduce_kernel<D>), dim3(BH, (D * D + D + 255) / 256), dim3(256),
-                         0, s, w.part_h, w.part_z, w.lin_h, w.lin_z, w.lin_on, a.H);
+      // H_D, z_D of every query block, as the forward forms them
+      const int qrows = BH * a.n_q, n_kw = (a.n_k + 31) / 32;
+      hipLaunchKernelGGL((linear_pack_kernel<D>), dim3(a.n_k, BH), dim3(2 * D), 0, s, a.v, a.k,
+                         w.vtp, w.hj, a.N, a.n_k, w.lin_on, a.H);
+      hipLaunchKernelGGL(linear_mdrop_kernel, dim3((qrows + 3) / 4), dim3(256), 0, s, a.idx,
+                         a.cnt, w.mbits, a.n_k, n_kw, qrows);
+      hipLaunchKernelGGL((linear_hd_kernel<D>),
+                         dim3((lin_cols<D>() + 127) / 128, (a.n_q + 255) / 256, BH), dim3(256), 0,
+                         s, w.hj, w.mbits, w.hd, w.zd, a.n_q, a.n_k, n_kw, w.lin_on, a.H);
       if (a.lin_mode == kLinMix) {
         const size_t n8 = (size_t)BH * a.N * D / 8;
         hipLaunchKernelGGL((scale_do_kernel<D>), dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0,
@@ -1327,8 +1263,8 @@ hipError_t launch_bwd_t(const BwdLaunch& a, hipStream_t s) {
     }
   }
   // K^T (fp16) packed in 64-row groups like V^T
-  hipLaunchKernelGGL((pack_kernel<D, false, true>), dim3(a.n_k, BH), dim3(2 * D), 0, s, a.k,
-                     nullptr, w.kt, nullptr, a.N, a.n_k, nullptr, a.H);
+  hipLaunchKernelGGL((pack_kernel<D, true>), dim3(a.n_k, BH), dim3(2 * D), 0, s, a.k, w.kt, a.N,
+                     a.n_k);
   const int NP = a.n_q * BQ;
   const size_t rows = (size_t)BH * NP;
   constexpr int RPW = 256 / (D / 8);
@@ -1350,14 +1286,18 @@ hipError_t launch_bwd_t(const BwdLaunch& a, hipStream_t s) {
   if (linear) {
     if constexpr (D == BQ) {
       hipLaunchKernelGGL((linear_bwd_rows_kernel<D>), dim3(qrows), dim3(256), 0, s, a.q, a.dO,
-                         w.phikt, w.vtp, w.lin_h, w.lin_z, a.idx, a.cnt, w.lin_on, a.alpha,
-                         a.lin_mode, w.dql, w.dHq, w.dzq, w.drow, a.H, a.N, a.n_q, a.n_k, NP,
-                         qrows);
-      hipLaunchKernelGGL((linear_bwd_total_kernel<D>), dim3(BH, (D * D + D + 255) / 256),
-                         dim3(256), 0, s, w.dHq, w.dzq, w.dHt, w.dzt, a.n_q);
+                         w.hd, w.zd, a.cnt, w.lin_on, a.alpha, a.lin_mode, w.dql, w.dhp, w.drow,
+                         a.H, a.N, a.n_q, a.n_k, NP, qrows);
+      // G_j, g_j: the query blocks' dH_D, dz_D summed over those that dropped key block j
+      const int n_kw = (a.n_k + 31) / 32, n_qw = (a.n_q + 31) / 32;
+      const size_t words = (size_t)BH * a.n_k * n_qw;
+      hipLaunchKernelGGL(linear_mtrans_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0,
+                         s, w.mbits, w.mtbits, a.n_q, a.n_k, n_kw, n_qw, BH);
+      hipLaunchKernelGGL((linear_hd_kernel<D>),
+                         dim3((lin_cols<D>() + 127) / 128, (a.n_k + 255) / 256, BH), dim3(256), 0,
+                         s, w.dhp, w.mtbits, w.gp, w.gz, a.n_k, a.n_q, n_qw, w.lin_on, a.H);
       hipLaunchKernelGGL((linear_bwd_keys_kernel<D>), dim3(cols), dim3(256), 0, s, a.k, a.v,
-                         w.dHq, w.dzq, w.dHt, w.dzt, w.cmat, w.colcnt, w.coloff, w.collist,
-                         w.lin_on, w.dkl, w.dvl, a.H, a.N, a.n_q, a.n_k, cols);
+                         w.gp, w.gz, w.lin_on, w.dkl, w.dvl, a.H, a.N, a.n_k, cols);
     }
   }
   if constexpr (D == 128)

@@ -110,7 +110,6 @@ struct AttnLaunch {
   uint16_t* hd;        // [B*H, n_q, 2, d, d] bf16 planes of H_D^T per query block
   float* zd;           // [B*H, n_q, d] z_D per query block
 };
-constexpr int kLinSplit = 64;
 constexpr int kLinMaxKeyBlocks = 4096;  // the linear forward's drop bitmaps (one LDS row each)
 // how the linear branch meets the sparse output: O_s + alpha[h] O_l, or the
 // per-channel mix alpha[h][c] O_s + (1 - alpha[h][c]) O_l

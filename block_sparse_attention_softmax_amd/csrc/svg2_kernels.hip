@@ -1260,8 +1260,8 @@ hipError_t launch_svg2_t(const Svg2Launch& a, hipStream_t s) {
                      a.off_k, a.size_k, a.kpad_off, a.kp, a.N, a.Ck, 16, NKP);
   hipLaunchKernelGGL((svg2_gather_kernel<D>), dim3(a.Ck, BH), dim3(256), 0, s, a.v, a.perm_k,
                      a.off_k, a.size_k, a.kpad_off, a.vp, a.N, a.Ck, 16, NKP);
-  hipLaunchKernelGGL((pack_kernel<D, false>), dim3(a.n_ktiles, BH), dim3(2 * D), 0, s, a.vp,
-                     nullptr, a.vtp, nullptr, NKP, a.n_ktiles, nullptr, a.H);
+  hipLaunchKernelGGL((pack_kernel<D>), dim3(a.n_ktiles, BH), dim3(2 * D), 0, s, a.vp, a.vtp,
+                     NKP, a.n_ktiles);
   if (a.phase == kSvg2Cluster) return hipGetLastError();
   hipLaunchKernelGGL((svg2_attn_kernel<D, BQ>), dim3(BH * a.max_tiles), dim3(BQ * 2), 0, s, a.qp,
                      a.kp, a.vtp, a.tile_cluster, a.tile_order, a.lists, a.list_cnt, a.perm_q,

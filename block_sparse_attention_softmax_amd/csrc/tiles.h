@@ -23,66 +23,49 @@ __device__ __forceinline__ int packed_key(int slot) {
 // phi(x) = elu(x) + 1, the feature map of the linear branch
 __device__ __forceinline__ float elu1(float x) { return x > 0.0f ? x + 1.0f : expf(x); }
 
-// vt[bh][j][d][slot] = V[bh][64*j + packed_key(slot)][d], zero past N; with
-// LIN also phikt[...] = bf16(phi(K[...])) in the same layout, for the heads
-// whose linear branch is evaluated (lin_on).
+// vt[bh][j][d][slot] = V[bh][64*j + packed_key(slot)][d], zero past N.
 // grid (n_k, B*H), 2*D threads; one 64-key block per workgroup. Thread t
 // takes keys 4q..4q+3 (q = t % 16) at d = 8c..8c+7 (c = t / 16): four 16-byte
 // rows in, transposed in registers, eight 8-byte pieces out. The four keys
 // occupy four consecutive slots, and the 16 lanes sharing c write whole
 // 128-byte rows of the packed block.
-// F16 (without LIN) stores the values as fp16 instead: a bf16 value converts
-// to fp16 exactly when its magnitude lies in [2^-14, 65504].
-template <int D, bool LIN, bool F16 = false>
+// F16 stores the values as fp16 instead: a bf16 value converts to fp16
+// exactly when its magnitude lies in [2^-14, 65504].
+template <int D, bool F16 = false>
 __global__ __launch_bounds__(2 * D) void pack_kernel(const uint16_t* __restrict__ v,
-                                                     const uint16_t* __restrict__ k,
-                                                     uint16_t* __restrict__ vt,
-                                                     uint16_t* __restrict__ phikt, int N,
-                                                     int n_k, const int32_t* __restrict__ lin_on,
-                                                     int H) {
+                                                     uint16_t* __restrict__ vt, int N, int n_k) {
   const int j = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
   const int q = t & 15, c = t >> 4;
   // slot of key 4q: group q/4, then the inverse of packed_key within it
   const int slot0 = 16 * (q >> 2) + 8 * (q & 1) + 4 * ((q >> 1) & 1);
+  const uint16_t* src = v + ((size_t)bh * N + (size_t)j * BK) * D + c * 8;
+  uint32_t x[4][4];
 #pragma unroll
-  for (int w = 0; w < (LIN ? 2 : 1); ++w) {
-    if (w == 1 && !lin_on[bh % H]) break;  // the head's linear branch is dropped
-    const uint16_t* src = (w == 0 ? v : k) + ((size_t)bh * N + (size_t)j * BK) * D + c * 8;
-    uint32_t x[4][4];
+  for (int r = 0; r < 4; ++r) {
+    const int key = 4 * q + r;
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if (j * BK + key < N) {
+      u = *reinterpret_cast<const uint4*>(src + (size_t)key * D);
+      if constexpr (F16) {
+        uint32_t* p = &u.x;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = 4 * q + r;
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (j * BK + key < N) {
-        u = *reinterpret_cast<const uint4*>(src + (size_t)key * D);
-        if (w == 1) {  // phi(K), rounded to bf16
-          uint32_t* p = &u.x;
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            p[e] = f32_to_bf16_rne(elu1(bf16_lo(p[e]))) |
-                   (f32_to_bf16_rne(elu1(bf16_hi(p[e]))) << 16);
-        } else if constexpr (F16) {
-          uint32_t* p = &u.x;
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            p[e] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)bf16_lo(p[e])) |
-                   ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)bf16_hi(p[e])) << 16);
-        }
+        for (int e = 0; e < 4; ++e)
+          p[e] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)bf16_lo(p[e])) |
+                 ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)bf16_hi(p[e])) << 16);
       }
-      x[r][0] = u.x; x[r][1] = u.y; x[r][2] = u.z; x[r][3] = u.w;
     }
-    uint16_t* dst = (w == 0 ? vt : phikt) + ((size_t)bh * n_k + j) * (size_t)D * BK +
-                    (size_t)(8 * c) * BK + slot0;
+    x[r][0] = u.x; x[r][1] = u.y; x[r][2] = u.z; x[r][3] = u.w;
+  }
+  uint16_t* dst = vt + ((size_t)bh * n_k + j) * (size_t)D * BK + (size_t)(8 * c) * BK + slot0;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {  // d = 8c + 2e (low halves) and 8c + 2e + 1 (high)
-      uint2 lo, hi;
-      lo.x = (x[0][e] & 0xFFFFu) | (x[1][e] << 16);
-      lo.y = (x[2][e] & 0xFFFFu) | (x[3][e] << 16);
-      hi.x = (x[0][e] >> 16) | (x[1][e] & 0xFFFF0000u);
-      hi.y = (x[2][e] >> 16) | (x[3][e] & 0xFFFF0000u);
-      *reinterpret_cast<uint2*>(dst + (size_t)(2 * e) * BK) = lo;
-      *reinterpret_cast<uint2*>(dst + (size_t)(2 * e + 1) * BK) = hi;
-    }
+  for (int e = 0; e < 4; ++e) {  // d = 8c + 2e (low halves) and 8c + 2e + 1 (high)
+    uint2 lo, hi;
+    lo.x = (x[0][e] & 0xFFFFu) | (x[1][e] << 16);
+    lo.y = (x[2][e] & 0xFFFFu) | (x[3][e] << 16);
+    hi.x = (x[0][e] >> 16) | (x[1][e] & 0xFFFF0000u);
+    hi.y = (x[2][e] >> 16) | (x[3][e] & 0xFFFF0000u);
+    *reinterpret_cast<uint2*>(dst + (size_t)(2 * e) * BK) = lo;
+    *reinterpret_cast<uint2*>(dst + (size_t)(2 * e + 1) * BK) = hi;
   }
 }
 

@@ -456,9 +456,12 @@ int svg2_attn_pair_counts(int B, int H, int N, int d, int block_q, int n_q_clust
                           size_t workspace_bytes, void* stream);
 
 /* Device workspace (bytes) of sparse_linear_attn_bwd and sla2_mix_attn_bwd:
- * that of sparge_attn_bwd, plus the linear branch's packed V and phi(K), its
- * totals, the scaled dO of the mix, float32 dQ, dK, dV of the branch and one
- * float32 d x d summary per query block. Returns 0 for arguments those calls
+ * that of sparge_attn_bwd, plus the linear branch's packed V, its per-key-
+ * block summaries, drop bits and per-query-block H_D, z_D as the forward
+ * keeps them, the scaled dO of the mix, float32 dQ, dK, dV of the branch, and
+ * per query block dH_D, dz_D and per key block their sums over the query
+ * blocks that dropped it (two bf16 planes each, z parts float32 for the
+ * latter), with the transposed drop bits. Returns 0 for arguments those calls
  * would reject. */
 size_t sparse_linear_bwd_workspace_bytes(int B, int H, int N, int d);
 
@@ -471,9 +474,11 @@ size_t sparse_linear_bwd_workspace_bytes(int B, int H, int N, int d);
  *   dK_u += (dH V_u + dz) phi'(K_u),  dV_u += phi(K_u) dH  for u in D_i,
  * dH = sum_t phi(Q_t)^T dnum_t, dz = sum_t phi(Q_t) dden_t over the rows of the
  * block (the chain rule of the SLA2 page's sparse-linear output, section 1).
- * The linear part runs in float32 (H_D from bf16 phi(K) and V on the matrix
- * cores, as in the forward) and is added to the sparse part's float32
- * results before dQ, dK, dV are rounded to bf16. Heads dropped by the same
+ * The linear part runs in float32 on the vector units from H_D, z_D as the
+ * forward forms them; dH, dz of each query block are summed per key block on
+ * the matrix cores in two bf16 planes (about 16 significant bits per term,
+ * float32 accumulation). It is added to the sparse part's float32 results
+ * before dQ, dK, dV are rounded to bf16. Heads dropped by the same
  * rule as the forward (|alpha[h]| <= drop_below) pass no linear gradient.
  * Built for block_q == d and at most 4096 key blocks; deterministic.
  *
