@@ -1153,6 +1153,155 @@ __global__ __launch_bounds__(256, 1) void linear_bwd_keys_kernel(
   }
 }
 
+// The same on the matrix cores (d = 128). G_j's two planes (row-major
+// [a][c]) are copied into LDS with the 16-byte chunk c of row a stored at
+// c ^ (4 (a mod 4) + (a / 4) mod 4): 16 consecutive rows read at one chunk,
+// and the transposing reads' 4 rows x 32 bytes, both cover all banks. Wave w
+// takes keys 32 (w mod 2) .. +31 and channels 64 (w / 2) .. +63:
+//   dV_l[u][c] = sum_a phi(K_u)[a] G[a][c]: phi(K) split into two bf16 terms
+//     (in registers, from K) against G's planes read transposed (8 rows a of
+//     one column c per lane), three products (the lo x lo term left out);
+//   dK_l^T[a][u] = sum_c G[a][c] V[u][c], G's planes read directly against V
+//     (exact in bf16), two products; then + g[a] and times phi'(K[u][a]).
+template <int D>
+__global__ __launch_bounds__(256) void linear_bwd_keys_mfma_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ gp, const float* __restrict__ gz,
+    const int32_t* __restrict__ lin_on, float* __restrict__ dkl, float* __restrict__ dvl,
+    int H, int N, int n_k, int total) {
+  static_assert(D == 128, "rows of 16 chunks, two 64-channel halves");
+  constexpr int PLANE = D * D * 2, KS = D / 16, ROWB = D * 2;
+  __shared__ __align__(16) unsigned char smem[2 * PLANE + D * 4];
+  float* const gs = reinterpret_cast<float*>(smem + 2 * PLANE);
+  const int tile = xcd_remap(blockIdx.x, total);
+  const int bh = tile / n_k, j = tile % n_k, h = bh % H;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int h2 = lane >> 5, l32 = lane & 31, g16 = lane & 15;
+  const size_t head = (size_t)bh * N * D;
+  const int key0 = j * BK;
+  const int ut = wave & 1, chalf = wave >> 1;
+
+  if (lin_on[h] == 0) {
+    for (int e = t; e < BK * D / 4; e += 256) {
+      const int u = e / (D / 4), c4 = 4 * (e % (D / 4));
+      if (key0 + u < N) {
+        const size_t o = head + (size_t)(key0 + u) * D + c4;
+        *reinterpret_cast<float4*>(dkl + o) = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        *reinterpret_cast<float4*>(dvl + o) = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      }
+    }
+    return;
+  }
+  auto swz = [](int r) { return ((r & 3) << 2) | ((r >> 2) & 3); };
+  {  // 64 copies of 4 rows, 16 per wave: lane = row r0 + lane / 16, physical chunk lane % 16
+    const uint16_t* gsrc = gp + ((size_t)bh * n_k + j) * 2 * D * D;
+#pragma unroll
+    for (int u = 0; u < 2 * D / 16; ++u) {
+      const int ci = 4 * u + wave, pl = ci / (D / 4), r0 = 4 * (ci % (D / 4)), r = r0 + (lane >> 4);
+      const int lc = (lane & 15) ^ swz(r);
+      dma16(gsrc + (size_t)pl * D * D + (size_t)r * D + 8 * lc, smem + pl * PLANE + r0 * ROWB);
+    }
+  }
+  if (t < D) gs[t] = gz[((size_t)bh * n_k + j) * D + t];
+  // operands of this lane's key (32 ut + l32): phi(K) as hi + lo, V
+  const int urow = key0 + 32 * ut + l32;
+  const bool ulive = urow < N;
+  bf16x8 ph[KS], plo[KS], vb[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    uint4 kk = make_uint4(0u, 0u, 0u, 0u), vv = kk;
+    if (ulive) {
+      kk = *reinterpret_cast<const uint4*>(k + head + (size_t)urow * D + 16 * ks + 8 * h2);
+      vv = *reinterpret_cast<const uint4*>(v + head + (size_t)urow * D + 16 * ks + 8 * h2);
+    }
+    const uint32_t* wk = &kk.x;
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float f0 = ulive ? elu1(bf16_lo(wk[e])) : 0.0f;
+      const float f1 = ulive ? elu1(bf16_hi(wk[e])) : 0.0f;
+      const uint32_t a0 = f32_to_bf16_rne(f0), a1 = f32_to_bf16_rne(f1);
+      hw[e] = a0 | (a1 << 16);
+      lw[e] = f32_to_bf16_rne(f0 - __uint_as_float(a0 << 16)) |
+              (f32_to_bf16_rne(f1 - __uint_as_float(a1 << 16)) << 16);
+    }
+    __builtin_memcpy(&ph[ks], hw, 16);
+    __builtin_memcpy(&plo[ks], lw, 16);
+    __builtin_memcpy(&vb[ks], &vv, 16);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's plane copies landed
+  __syncthreads();                     // and every wave's, and g
+  floatx16 dv[2], dk[2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dv[x][r] = dk[x][r] = 0.0f;
+  const uint32_t base = lds_addr(smem);
+  const int colq = 16 * ((lane >> 4) & 1) + 4 * (g16 & 3);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    // dV: G rows 16 ks + 8 h2 .. +7 of column 32 (2 chalf + x) + l32, both planes
+    uint32_t ad[8];
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const int r = 16 * ks + 8 * h2 + 4 * tt + (g16 >> 2);
+          const int colb = 32 * (2 * chalf + x) + colq;
+          ad[4 * x + 2 * pl + tt] =
+              base + pl * PLANE + r * ROWB + 16 * ((colb >> 3) ^ swz(r)) + 2 * (colb & 7);
+        }
+    v4i16 fr[8];
+    lds_read_tr<8>(fr, ad);
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const bf16x8 gh = join_tr(fr[4 * x], fr[4 * x + 1]), gl = join_tr(fr[4 * x + 2], fr[4 * x + 3]);
+      dv[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ph[ks], gh, dv[x], 0, 0, 0);
+      dv[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(plo[ks], gh, dv[x], 0, 0, 0);
+      dv[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ph[ks], gl, dv[x], 0, 0, 0);
+    }
+    // dK^T: G row 32 (2 chalf + x) + l32, channels 16 ks + 8 h2 .. +7, both planes
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int a = 32 * (2 * chalf + x) + l32;
+      const int ofs = a * ROWB + 16 * ((2 * ks + h2) ^ swz(a));
+      const bf16x8 gh = lds_read16(smem + ofs), gl = lds_read16(smem + PLANE + ofs);
+      dk[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gh, vb[ks], dk[x], 0, 0, 0);
+      dk[x] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gl, vb[ks], dk[x], 0, 0, 0);
+    }
+  }
+  // dV: lane holds keys 32 ut + 8 (r / 4) + 4 h2 + r % 4 of column 32 (2 chalf + x) + l32
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int u = key0 + 32 * ut + 8 * (r >> 2) + 4 * h2 + (r & 3);
+      if (u < N) dvl[head + (size_t)u * D + 32 * (2 * chalf + x) + l32] = dv[x][r];
+    }
+  // dK: lane holds channels 32 (2 chalf + x) + 8 g + 4 h2 .. +3 of key urow
+  if (ulive) {
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int a0 = 32 * (2 * chalf + x) + 8 * g + 4 * h2;
+        const uint2 kk = *reinterpret_cast<const uint2*>(k + head + (size_t)urow * D + a0);
+        const float kf[4] = {bf16_lo(kk.x), bf16_hi(kk.x), bf16_lo(kk.y), bf16_hi(kk.y)};
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float f = elu1(kf[e]);
+          y[e] = (dk[x][4 * g + e] + gs[a0 + e]) * (f > 1.0f ? 1.0f : f);
+        }
+        *reinterpret_cast<float4*>(dkl + head + (size_t)urow * D + a0) =
+            make_float4(y[0], y[1], y[2], y[3]);
+      }
+  }
+}
+
 // dO_s = alpha (*) dO (the mix's sparse share), bf16; one thread per 8 values.
 template <int D>
 __global__ __launch_bounds__(256) void scale_do_kernel(const uint16_t* __restrict__ dO,
@@ -1296,8 +1445,12 @@ hipError_t launch_bwd_t(const BwdLaunch& a, hipStream_t s) {
       hipLaunchKernelGGL((linear_hd_kernel<D>),
                          dim3((lin_cols<D>() + 127) / 128, (a.n_k + 255) / 256, BH), dim3(256), 0,
                          s, w.dhp, w.mtbits, w.gp, w.gz, a.n_k, a.n_q, n_qw, w.lin_on, a.H);
-      hipLaunchKernelGGL((linear_bwd_keys_kernel<D>), dim3(cols), dim3(256), 0, s, a.k, a.v,
-                         w.gp, w.gz, w.lin_on, w.dkl, w.dvl, a.H, a.N, a.n_k, cols);
+      if constexpr (D == 128)
+        hipLaunchKernelGGL((linear_bwd_keys_mfma_kernel<D>), dim3(cols), dim3(256), 0, s, a.k,
+                           a.v, w.gp, w.gz, w.lin_on, w.dkl, w.dvl, a.H, a.N, a.n_k, cols);
+      else
+        hipLaunchKernelGGL((linear_bwd_keys_kernel<D>), dim3(cols), dim3(256), 0, s, a.k, a.v,
+                           w.gp, w.gz, w.lin_on, w.dkl, w.dvl, a.H, a.N, a.n_k, cols);
     }
   }
   if constexpr (D == 128)
