@@ -1039,6 +1039,333 @@ __global__ __launch_bounds__(256, 1) void linear_bwd_rows_kernel(
     }
 }
 
+// The same on the matrix cores (d = 128, 128-row query blocks). Wave w takes
+// rows 32 w .. 32 w + 31, one per lane, channels in the accumulator layout of
+// the forward's O^T. H_D^T's two planes are copied into LDS with the chunk
+// swizzle of linear_bwd_keys_mfma_kernel (direct row reads and 4-row
+// transposing reads both conflict-free).
+//   num^T = H_D^T phi(Q)^T: H_D^T rows read directly, phi(Q) split into hi +
+//     lo bf16 in registers; three products (lo x lo left out), as the forward.
+//   den, G = w (*) dO, corr = G . num / den, dnum = G / den, dden = -corr /
+//     den (float32, per lane), D -= corr.
+//   dQ_l^T = H_D dnum^T + z_D dden, times phi'(Q): dnum stays in its
+//     accumulator registers as the B operand, the k order of each 16-channel
+//     step being that of the registers (channels 16 p + 8 (e / 4) + 4 h2 +
+//     e % 4 of a 32-channel tile), and H_D's matching 8 rows per lane come from
+//     two 4-row transposing reads of H_D^T; three products.
+//   dH^T = dnum^T phi(Q) over the block's 128 rows: 64 rows at a time, the two
+//     waves holding them write phi(Q) and dnum as bf16 hi / lo planes into the
+//     space H_D^T used, and every wave takes 2 x 2 of the 16 output tiles from
+//     transposing reads of both (8 rows t of one channel per lane); three
+//     products. dz = sum_t phi(Q_t) dden_t by threads t < d from the same
+//     planes. dH, dz leave as two bf16 planes as in linear_bwd_rows_kernel.
+template <int D>
+__global__ __launch_bounds__(256, 2) void linear_bwd_rows_mfma_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ dO,
+    const uint16_t* __restrict__ hd, const float* __restrict__ zd,
+    const int32_t* __restrict__ kv_cnt, const int32_t* __restrict__ lin_on,
+    const float* __restrict__ alpha, int mode, float* __restrict__ dql,
+    uint16_t* __restrict__ dhp, float* __restrict__ drow, int H, int N, int n_q, int n_k, int NP,
+    int total) {
+  static_assert(D == 128, "rows of 16 chunks, four 32-row waves");
+  constexpr int PL = D * D * 2, ROWB = D * 2, KS = D / 16, DT = D / 32, COLS = lin_cols<D>();
+  constexpr int HALF = 64 * ROWB;  // one bf16 plane of 64 rows
+  constexpr int ZS = 2 * PL, DDN = ZS + D * 4, BYTES = DDN + D * 4;
+  __shared__ __align__(16) unsigned char smem[BYTES];
+  float* const zs = reinterpret_cast<float*>(smem + ZS);
+  float* const ddn = reinterpret_cast<float*>(smem + DDN);
+
+  const int tile = xcd_remap(blockIdx.x, total);
+  const int bh = tile / n_q, qi = tile % n_q, h = bh % H;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int h2 = lane >> 5, l32 = lane & 31, g16 = lane & 15;
+  const size_t head = (size_t)bh * N * D;
+  const int row0 = qi * D;
+  const int count = min(max(kv_cnt[tile], 0), n_k);
+  uint16_t* const dh_out = dhp + ((size_t)bh * n_q + qi) * 2 * COLS;
+
+  if (lin_on[h] == 0 || count >= n_k) {  // no linear gradient from this block
+    for (int e = t; e < D * D / 4; e += 256) {
+      const int row = row0 + e / (D / 4);
+      if (row < N)
+        *reinterpret_cast<float4*>(dql + head + (size_t)row * D + 4 * (e % (D / 4))) =
+            make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+    for (int e = t; e < 2 * COLS / 8; e += 256)
+      reinterpret_cast<uint4*>(dh_out)[e] = make_uint4(0u, 0u, 0u, 0u);
+    return;
+  }
+  auto swz = [](int r) { return ((r & 3) << 2) | ((r >> 2) & 3); };
+  {  // H_D^T planes: 64 copies of 4 rows, 16 per wave
+    const uint16_t* hsrc = hd + ((size_t)bh * n_q + qi) * 2 * D * D;
+#pragma unroll
+    for (int u = 0; u < 2 * D / 16; ++u) {
+      const int ci = 4 * u + wave, pl = ci / (D / 4), r0 = 4 * (ci % (D / 4)), r = r0 + (lane >> 4);
+      const int lc = (lane & 15) ^ swz(r);
+      dma16(hsrc + (size_t)pl * D * D + (size_t)r * D + 8 * lc, smem + pl * PL + r0 * ROWB);
+    }
+  }
+  if (t < D) zs[t] = zd[((size_t)bh * n_q + qi) * D + t];
+  // phi(Q) of this lane's row, channels 16 s + 8 h2 .. +7, as hi + lo (0 past
+  // N); formed again from Q where the dH planes are written, so that these
+  // registers are free during the dQ products
+  const int lrow = 32 * wave + l32, row = row0 + lrow;
+  const bool live = row < N;
+  auto phi_q = [&](int s2, bf16x8& hi, bf16x8& lo) {
+    uint4 u = make_uint4(0u, 0u, 0u, 0u);
+    if (live) u = *reinterpret_cast<const uint4*>(q + head + (size_t)row * D + 16 * s2 + 8 * h2);
+    const uint32_t* w = &u.x;
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float f0 = live ? elu1(bf16_lo(w[e])) : 0.0f;
+      const float f1 = live ? elu1(bf16_hi(w[e])) : 0.0f;
+      const uint32_t a0 = f32_to_bf16_rne(f0), a1 = f32_to_bf16_rne(f1);
+      hw[e] = a0 | (a1 << 16);
+      lw[e] = f32_to_bf16_rne(f0 - __uint_as_float(a0 << 16)) |
+              (f32_to_bf16_rne(f1 - __uint_as_float(a1 << 16)) << 16);
+    }
+    __builtin_memcpy(&hi, hw, 16);
+    __builtin_memcpy(&lo, lw, 16);
+  };
+  bf16x8 qh[KS], ql[KS];
+#pragma unroll
+  for (int s2 = 0; s2 < KS; ++s2) phi_q(s2, qh[s2], ql[s2]);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's plane copies landed
+  __syncthreads();                     // and every wave's, and z_D
+
+  // ---- num^T: acc[i][r] = num[row][32 i + 8 (r / 4) + 4 h2 + r % 4]
+  floatx16 acc[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
+#pragma unroll
+  for (int s2 = 0; s2 < KS; ++s2)
+#pragma unroll
+    for (int i = 0; i < DT; ++i) {
+      const int c = 32 * i + l32;
+      const int ofs = c * ROWB + 16 * ((2 * s2 + h2) ^ swz(c));
+      const bf16x8 hh = lds_read16(smem + ofs), hl = lds_read16(smem + PL + ofs);
+      acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hh, qh[s2], acc[i], 0, 0, 0);
+      acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hh, ql[s2], acc[i], 0, 0, 0);
+      acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hl, qh[s2], acc[i], 0, 0, 0);
+    }
+  // ---- den, G, corr; acc becomes dnum
+  float den = 0.0f;
+#pragma unroll
+  for (int s2 = 0; s2 < KS; ++s2)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      den = fmaf((float)qh[s2][e] + (float)ql[s2][e], zs[16 * s2 + 8 * h2 + e], den);
+  den = pair_sum(den);
+  const float inv_den = live ? 1.0f / den : 0.0f;
+  float gn = 0.0f;
+#pragma unroll
+  for (int i = 0; i < DT; ++i)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int c0 = 32 * i + 8 * g + 4 * h2;
+      uint2 u = make_uint2(0u, 0u);
+      if (live) u = *reinterpret_cast<const uint2*>(dO + head + (size_t)row * D + c0);
+      const float dv[4] = {bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y)};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float gv =
+            dv[e] * (mode == kLinAdd ? alpha[h] : 1.0f - alpha[(size_t)h * D + c0 + e]);
+        gn = fmaf(gv, acc[i][4 * g + e], gn);
+        acc[i][4 * g + e] = gv * inv_den;  // dnum
+      }
+    }
+  const float corr = pair_sum(gn) * inv_den;  // G . O_l
+  const float dden = -corr * inv_den;
+  if (h2 == 0) {
+    ddn[lrow] = dden;
+    if (live) drow[(size_t)bh * NP + row] -= corr;
+  }
+  // ---- dQ_l^T: dq[ta][r] at channel a = 32 ta + 8 (r / 4) + 4 h2 + r % 4
+  floatx16 dq[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[i][r] = 0.0f;
+  const uint32_t base = lds_addr(smem);
+  const int colq = 16 * ((lane >> 4) & 1) + 4 * (g16 & 3);
+#pragma unroll
+  for (int i = 0; i < DT; ++i)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      bf16x8 bh_, bl_;  // dnum of channels 32 i + 16 p + 8 (e / 4) + 4 h2 + e % 4
+      {
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x0 = acc[i][8 * p + 2 * e], x1 = acc[i][8 * p + 2 * e + 1];
+          const uint32_t a0 = f32_to_bf16_rne(x0), a1 = f32_to_bf16_rne(x1);
+          hw[e] = a0 | (a1 << 16);
+          lw[e] = f32_to_bf16_rne(x0 - __uint_as_float(a0 << 16)) |
+                  (f32_to_bf16_rne(x1 - __uint_as_float(a1 << 16)) << 16);
+        }
+        __builtin_memcpy(&bh_, hw, 16);
+        __builtin_memcpy(&bl_, lw, 16);
+      }
+#pragma unroll
+      for (int tp = 0; tp < DT / 2; ++tp) {  // two output tiles per batch of 8 reads
+        uint32_t ad[8];
+#pragma unroll
+        for (int y = 0; y < 2; ++y)
+#pragma unroll
+          for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+              const int r = 32 * i + 16 * p + 8 * tt + 4 * h2 + (g16 >> 2);
+              const int colb = 32 * (2 * tp + y) + colq;
+              ad[4 * y + 2 * pl + tt] =
+                  base + pl * PL + r * ROWB + 16 * ((colb >> 3) ^ swz(r)) + 2 * (colb & 7);
+            }
+        v4i16 fr[8];
+        lds_read_tr<8>(fr, ad);
+#pragma unroll
+        for (int y = 0; y < 2; ++y) {
+          const int ta = 2 * tp + y;
+          const bf16x8 ah = join_tr(fr[4 * y], fr[4 * y + 1]), al = join_tr(fr[4 * y + 2], fr[4 * y + 3]);
+          dq[ta] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh_, dq[ta], 0, 0, 0);
+          dq[ta] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl_, dq[ta], 0, 0, 0);
+          dq[ta] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh_, dq[ta], 0, 0, 0);
+        }
+      }
+    }
+  if (live) {
+#pragma unroll
+    for (int ta = 0; ta < DT; ++ta)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int a0 = 32 * ta + 8 * g + 4 * h2;
+        const uint2 u = *reinterpret_cast<const uint2*>(q + head + (size_t)row * D + a0);
+        const float qv[4] = {bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y)};
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float f = elu1(qv[e]);
+          y[e] = fmaf(zs[a0 + e], dden, dq[ta][4 * g + e]) * (f > 1.0f ? 1.0f : f);
+        }
+        *reinterpret_cast<float4*>(dql + head + (size_t)row * D + a0) =
+            make_float4(y[0], y[1], y[2], y[3]);
+      }
+  }
+  // ---- dH^T = dnum^T phi(Q) and dz, 64 rows at a time
+  __syncthreads();  // every wave is done with H_D^T and has written its dden
+  const int ct0 = 2 * (wave >> 1), at0 = 2 * (wave & 1);
+  floatx16 dh[4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dh[x][r] = 0.0f;
+  float dz = 0.0f;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    if ((wave >> 1) == pass) {  // planes: phi(Q) hi, lo, then dnum hi, lo; 64 rows each
+      const int lr = 32 * (wave & 1) + l32;
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2) {
+        const int ofs = lr * ROWB + 16 * ((2 * s2 + h2) ^ swz(lr));
+        bf16x8 hi, lo;
+        phi_q(s2, hi, lo);
+        *reinterpret_cast<bf16x8*>(smem + ofs) = hi;
+        *reinterpret_cast<bf16x8*>(smem + HALF + ofs) = lo;
+      }
+#pragma unroll
+      for (int i = 0; i < DT; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int c0 = 32 * i + 8 * g + 4 * h2;
+          uint32_t hw[2], lw[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const float x0 = acc[i][4 * g + 2 * e], x1 = acc[i][4 * g + 2 * e + 1];
+            const uint32_t a0 = f32_to_bf16_rne(x0), a1 = f32_to_bf16_rne(x1);
+            hw[e] = a0 | (a1 << 16);
+            lw[e] = f32_to_bf16_rne(x0 - __uint_as_float(a0 << 16)) |
+                    (f32_to_bf16_rne(x1 - __uint_as_float(a1 << 16)) << 16);
+          }
+          const int ofs = lr * ROWB + 16 * ((c0 >> 3) ^ swz(lr)) + 2 * (c0 & 7);
+          *reinterpret_cast<uint2*>(smem + 2 * HALF + ofs) = make_uint2(hw[0], hw[1]);
+          *reinterpret_cast<uint2*>(smem + 3 * HALF + ofs) = make_uint2(lw[0], lw[1]);
+        }
+    }
+    __syncthreads();  // the pass's planes are complete
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {  // 16 rows per step
+      uint32_t ad[8], bd[8];
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            const int r = 16 * ks + 8 * h2 + 4 * tt + (g16 >> 2);
+            const int ca = 32 * (ct0 + x) + colq, cb = 32 * (at0 + x) + colq;
+            ad[4 * x + 2 * pl + tt] = base + (2 + pl) * HALF + r * ROWB +
+                                      16 * ((ca >> 3) ^ swz(r)) + 2 * (ca & 7);
+            bd[4 * x + 2 * pl + tt] =
+                base + pl * HALF + r * ROWB + 16 * ((cb >> 3) ^ swz(r)) + 2 * (cb & 7);
+          }
+      v4i16 fa[8], fb[8];
+      lds_read_tr<8>(fa, ad);
+      lds_read_tr<8>(fb, bd);
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const bf16x8 dnh = join_tr(fa[4 * x], fa[4 * x + 1]), dnl = join_tr(fa[4 * x + 2], fa[4 * x + 3]);
+#pragma unroll
+        for (int y = 0; y < 2; ++y) {
+          const bf16x8 fqh = join_tr(fb[4 * y], fb[4 * y + 1]), fql = join_tr(fb[4 * y + 2], fb[4 * y + 3]);
+          floatx16& d = dh[2 * x + y];
+          d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dnh, fqh, d, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dnh, fql, d, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dnl, fqh, d, 0, 0, 0);
+        }
+      }
+    }
+    if (t < D) {  // dz[a = t] over the pass's rows, in row order
+      for (int lr = 0; lr < 64; ++lr) {
+        const int ofs = lr * ROWB + 16 * ((t >> 3) ^ swz(lr)) + 2 * (t & 7);
+        const float f = __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t*>(smem + ofs) << 16) +
+                        __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t*>(smem + HALF + ofs) << 16);
+        dz = fmaf(f, ddn[64 * pass + lr], dz);
+      }
+    }
+    __syncthreads();  // every wave is done with the pass's planes
+  }
+  // dH[a][c]: tile (ct0 + x, at0 + y) holds channels c = 32 (ct0 + x) + 8 (r / 4) + 4 h2 + r % 4 of a = 32 (at0 + y) + l32
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const floatx16& d = dh[2 * x + y];
+        const int a = 32 * (at0 + y) + l32, c0 = 32 * (ct0 + x) + 8 * g + 4 * h2;
+        uint32_t hw[2], lw[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float x0 = d[4 * g + 2 * e], x1 = d[4 * g + 2 * e + 1];
+          const uint32_t a0 = f32_to_bf16_rne(x0), a1 = f32_to_bf16_rne(x1);
+          hw[e] = a0 | (a1 << 16);
+          lw[e] = f32_to_bf16_rne(x0 - __uint_as_float(a0 << 16)) |
+                  (f32_to_bf16_rne(x1 - __uint_as_float(a1 << 16)) << 16);
+        }
+        const size_t col = (size_t)a * D + c0;
+        *reinterpret_cast<uint2*>(dh_out + col) = make_uint2(hw[0], hw[1]);
+        *reinterpret_cast<uint2*>(dh_out + COLS + col) = make_uint2(lw[0], lw[1]);
+      }
+  if (t < D) {
+    const uint32_t hz = f32_to_bf16_rne(dz);
+    dh_out[D * D + t] = (uint16_t)hz;
+    dh_out[COLS + D * D + t] = (uint16_t)f32_to_bf16_rne(dz - __uint_as_float(hz << 16));
+  }
+}
+
 // Per (b, h, key block j): G_j = the sum of dH_D over the query blocks that
 // dropped j and g_j = that of dz_D, both from the dropped-block product (two
 // bf16 planes of G_j, row-major, summed into float32 in LDS; g_j float32),
@@ -1434,9 +1761,14 @@ hipError_t launch_bwd_t(const BwdLaunch& a, hipStream_t s) {
                      w.collist, a.n_q, a.n_k, cols);
   if (linear) {
     if constexpr (D == BQ) {
-      hipLaunchKernelGGL((linear_bwd_rows_kernel<D>), dim3(qrows), dim3(256), 0, s, a.q, a.dO,
-                         w.hd, w.zd, a.cnt, w.lin_on, a.alpha, a.lin_mode, w.dql, w.dhp, w.drow,
-                         a.H, a.N, a.n_q, a.n_k, NP, qrows);
+      if constexpr (D == 128)
+        hipLaunchKernelGGL((linear_bwd_rows_mfma_kernel<D>), dim3(qrows), dim3(256), 0, s, a.q,
+                           a.dO, w.hd, w.zd, a.cnt, w.lin_on, a.alpha, a.lin_mode, w.dql, w.dhp,
+                           w.drow, a.H, a.N, a.n_q, a.n_k, NP, qrows);
+      else
+        hipLaunchKernelGGL((linear_bwd_rows_kernel<D>), dim3(qrows), dim3(256), 0, s, a.q, a.dO,
+                           w.hd, w.zd, a.cnt, w.lin_on, a.alpha, a.lin_mode, w.dql, w.dhp, w.drow,
+                           a.H, a.N, a.n_q, a.n_k, NP, qrows);
       // G_j, g_j: the query blocks' dH_D, dz_D summed over those that dropped key block j
       const int n_kw = (a.n_k + 31) / 32, n_qw = (a.n_q + 31) / 32;
       const size_t words = (size_t)BH * a.n_k * n_qw;
