@@ -83,15 +83,16 @@ __global__ __launch_bounds__(256) void quant_int8_kernel(const uint16_t* __restr
 
 // amax over the rows of each channel of V: as float bits (non-negative floats
 // order like their bits), max-combined into vmax[bh][c], which starts at 0.
-// Grid (chunks of 512 rows, b*h), 256 threads: D/8 threads cover a row with
-// 16-byte loads, 256/(D/8) rows at a time; the row lanes meet through LDS.
+// Grid (chunks of kAmaxRows rows, b*h), 256 threads: D/8 threads cover a row
+// with 16-byte loads, 256/(D/8) rows at a time; the row lanes meet through LDS.
+constexpr int kAmaxRows = 256;
 template <int D>
 __global__ __launch_bounds__(256) void v_amax_kernel(const uint16_t* __restrict__ v,
                                                      uint32_t* __restrict__ vmax, int N) {
   constexpr int CG = D / 8, RL = 256 / CG;  // channel groups, row lanes
   __shared__ float part[RL][D];
   const int bh = blockIdx.y, t = threadIdx.x, cg = t % CG, rl = t / CG;
-  const int r0 = blockIdx.x * 512, r1 = min(r0 + 512, N);
+  const int r0 = blockIdx.x * kAmaxRows, r1 = min(r0 + kAmaxRows, N);
   float mx[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
   constexpr int UNR = 8;  // rows in flight per thread (their loads issued together)
   for (int rb = r0 + rl; rb < r1; rb += RL * UNR) {
@@ -393,8 +394,8 @@ hipError_t launch_lowbit_t(const LowbitLaunch& a, hipStream_t s) {
     const size_t nv = (size_t)BH * D;
     hipLaunchKernelGGL(fill_u32_zero_kernel, dim3((unsigned)((nv + 255) / 256)), dim3(256), 0, s,
                        a.vmax, nv);
-    hipLaunchKernelGGL((v_amax_kernel<D>), dim3((a.N + 511) / 512, BH), dim3(256), 0, s, a.v,
-                       a.vmax, a.N);
+    hipLaunchKernelGGL((v_amax_kernel<D>), dim3((a.N + kAmaxRows - 1) / kAmaxRows, BH), dim3(256),
+                       0, s, a.v, a.vmax, a.N);
     hipLaunchKernelGGL((pack_v_fp8_kernel<D>), dim3(a.n_k, BH), dim3(256), 0, s, a.v, a.vmax,
                        a.vt8, a.N, a.n_k);
     if (a.phase == kLowbitPackV) return hipGetLastError();
