@@ -20,8 +20,15 @@ __device__ __forceinline__ int packed_key(int slot) {
   return 16 * g + 8 * (e >> 2) + 4 * h + (e & 3);
 }
 
-// phi(x) = elu(x) + 1, the feature map of the linear branch
-__device__ __forceinline__ float elu1(float x) { return x > 0.0f ? x + 1.0f : expf(x); }
+// phi(x) = elu(x) + 1, the feature map of the linear branch: x + 1 above 0,
+// else e^x = 2^(x log2 e) by the hardware exp2. Its relative error, about
+// |x| 2^-24 from the rounded product plus the instruction's own ulp, lies far
+// below the bf16 rounding phi goes through; both sides are computed and one
+// selected, so there is no branch per element.
+__device__ __forceinline__ float elu1(float x) {
+  const float e = __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+  return x > 0.0f ? x + 1.0f : e;
+}
 
 // vt[bh][j][d][slot] = V[bh][64*j + packed_key(slot)][d], zero past N.
 // grid (n_k, B*H), 2*D threads; one 64-key block per workgroup. Thread t
