@@ -414,10 +414,14 @@ __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void sparse
       if (lin_mode == kLinMix) {  // alpha[h][d0 .. d0 + 3]
         const float4 a4 = *reinterpret_cast<const float4*>(alpha + (size_t)(bh % H) * D + d0);
         const float a[4] = {a4.x, a4.y, a4.z, a4.w};
+        if (lin) {  // the same for the whole workgroup: one branch, not one per value
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          y[e] = lin ? fmaf(a[e], y[e], (1.0f - a[e]) * (lacc[i][4 * g + e] * lin_scale))
-                     : a[e] * y[e];
+          for (int e = 0; e < 4; ++e)
+            y[e] = fmaf(a[e], y[e], (1.0f - a[e]) * (lacc[i][4 * g + e] * lin_scale));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] = a[e] * y[e];
+        }
       } else if (lin) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) y[e] = fmaf(lacc[i][4 * g + e], lin_scale, y[e]);
