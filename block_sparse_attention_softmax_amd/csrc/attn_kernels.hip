@@ -179,8 +179,6 @@ __global__ __launch_bounds__(BQ * 2, (D == 128 && BQ == 64) ? 1 : 2) void sparse
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[i][r] = 0.0f;
   float m = -INFINITY, lsum = 0.0f;
-  // H waves accumulate H_kept (rows 32*wave..) in oacc and their share of
-  // z_kept (entry 32*wave + l32, split over the half-waves) in lsum
   floatx16 sc[2], sn[2];  // S^T of the current and the next block (roles swap each step)
 #pragma unroll
   for (int tau = 0; tau < 2; ++tau)
