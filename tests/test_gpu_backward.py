@@ -235,7 +235,7 @@ def test_forward_then_backward_on_workload_sampled():
 # (1, 2, 4480, 128): 35 query blocks and 70 key blocks, so the per-key-block sums of
 # dH_D, dz_D run two 32-block stages over the query blocks (the second partial)
 LIN_SHAPES = [(1, 3, 1000, 128), (2, 1, 777, 64), (1, 2, 300, 128), (1, 2, 2048, 128),
-              (1, 2, 4480, 128)]
+              (1, 2, 4480, 128), (2, 2, 700, 128)]
 
 
 def _lin_alpha(mode, H, d, seed):

@@ -357,7 +357,8 @@ def test_attention_long_rows_sampled():
 
 # ------------------------------------------------------------ linear branch
 @pytest.mark.parametrize("B,H,N,d,bq", [(1, 2, 1000, 128, 128), (2, 1, 777, 64, 64),
-                                         (1, 3, 300, 128, 128), (1, 1, 64, 64, 64)])
+                                         (1, 3, 300, 128, 128), (1, 1, 64, 64, 64),
+                                         (2, 2, 700, 128, 128)])
 def test_sparse_linear_small_shapes_in_full(B, H, N, d, bq):
     rng = np.random.default_rng(7 * N + d)
     from block_sparse_attention_softmax_amd.workloads import f64_to_bf16_bits
@@ -495,7 +496,7 @@ def test_sparse_linear_branch_contributes():
 
 # ------------------------------------------------------ SLA2 mix (section 2A)
 @pytest.mark.parametrize("B,H,N,d", [(1, 2, 1000, 128), (2, 1, 777, 64), (1, 3, 300, 128),
-                                     (1, 1, 64, 64)])
+                                     (1, 1, 64, 64), (2, 2, 700, 128)])
 def test_sla2_mix_small_shapes_in_full(B, H, N, d):
     rng = np.random.default_rng(11 * N + d)
     from block_sparse_attention_softmax_amd.workloads import f64_to_bf16_bits, mix_alpha
